@@ -1,0 +1,493 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for batched banded solves.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg are the only code that may load this library.
+ * The GPU library (banded_pde_solvers_amd) never calls it and shares no code,
+ * header, table or constant with it.
+ *
+ * Every routine works on ONE system at a time in the flat layout the pages'
+ * serial CPU codes use (one system per row: system s occupies
+ * p[s*n .. s*n+n-1]), in double precision, with the arithmetic written in
+ * the pages' order.  The batch drivers only loop over systems (optionally
+ * with an OpenMP parallel-for, as the pages' OpenMP baselines do).
+ *
+ * Sources (titles of the web pages this follows):
+ *   [P] "cuPentBatch - A batched pentadiagonal solver for NVIDIA GPUs":
+ *       section "Pentadiagonal solver" (factorisation steps 1-14, the
+ *       forward steps for g, the back-substitution steps for x), and the
+ *       section on the hyperdiffusion equation (periodic matrix, the
+ *       reduction of Navon: E, F, G, H blocks and eqs. (10)-(12)).
+ *   [H] "Simulating the behavior of the human brain on GPUs", section 2
+ *       "Hines algorithm", Algorithm 1.
+ *
+ * Indices are 0-based (the pages are 1-based).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int bad_pivot(double v) { return v == 0.0 || !isfinite(v); }
+
+/* ------------------------------------------------------------------------ */
+/* Threads (timing only)                                                    */
+/* ------------------------------------------------------------------------ */
+
+int orc_set_threads(int k)
+{
+#ifdef _OPENMP
+    if (k > 0) omp_set_num_threads(k);
+    return omp_get_max_threads();
+#else
+    (void)k;
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P] Pentadiagonal solver: A = L R, L g = f, R x = g                      */
+/*                                                                          */
+/* Diagonals: a_i = A[i][i-2], b_i = A[i][i-1], c_i = A[i][i],              */
+/*            d_i = A[i][i+1], e_i = A[i][i+2].                             */
+/* Entries outside the matrix (a_0, a_1, b_0, d_{n-1}, e_{n-2}, e_{n-1})    */
+/* are never read.  Requires n >= 4.                                        */
+/* Returns 0, or 1 + the first row whose pivot alpha_i is zero / non-finite */
+/* (no pivoting, as on the page; the factorisation continues regardless).   */
+/* ------------------------------------------------------------------------ */
+
+int orc_penta_factor(int64_t n, const double *a, const double *b, const double *c,
+                     const double *d, const double *e,
+                     double *alpha, double *beta, double *gamma, double *delta)
+{
+    int info = 0;
+    int64_t i;
+#define CHECK(row) do { if (!info && bad_pivot(alpha[row])) info = (int)(row) + 1; } while (0)
+    /* steps 1-3 (page row 1) */
+    alpha[0] = c[0];
+    CHECK(0);
+    gamma[0] = d[0] / alpha[0];
+    delta[0] = e[0] / alpha[0];
+    beta[0] = 0.0;
+    /* steps 4-7 (page row 2) */
+    beta[1] = b[1];
+    alpha[1] = c[1] - beta[1] * gamma[0];
+    CHECK(1);
+    gamma[1] = (d[1] - beta[1] * delta[0]) / alpha[1];
+    delta[1] = e[1] / alpha[1];
+    /* step 8: page rows 3 .. N-2 */
+    for (i = 2; i <= n - 3; ++i) {
+        beta[i] = b[i] - a[i] * gamma[i - 2];
+        alpha[i] = c[i] - a[i] * delta[i - 2] - beta[i] * gamma[i - 1];
+        CHECK(i);
+        gamma[i] = (d[i] - beta[i] * delta[i - 1]) / alpha[i];
+        delta[i] = e[i] / alpha[i];
+    }
+    /* steps 9-11: page row N-1 */
+    i = n - 2;
+    beta[i] = b[i] - a[i] * gamma[i - 2];
+    alpha[i] = c[i] - a[i] * delta[i - 2] - beta[i] * gamma[i - 1];
+    CHECK(i);
+    gamma[i] = (d[i] - beta[i] * delta[i - 1]) / alpha[i];
+    delta[i] = 0.0;
+    /* steps 12-13: page row N */
+    i = n - 1;
+    beta[i] = b[i] - a[i] * gamma[i - 2];
+    alpha[i] = c[i] - a[i] * delta[i - 2] - beta[i] * gamma[i - 1];
+    CHECK(i);
+    gamma[i] = 0.0;
+    delta[i] = 0.0;
+#undef CHECK
+    /* step 14: epsilon_i = a_i, i.e. the sub-sub-diagonal of L is a itself */
+    return info;
+}
+
+/* Forward steps: g_0 = f_0/alpha_0, g_1 = (f_1 - beta_1 g_0)/alpha_1,
+ * g_i = (f_i - eps_i g_{i-2} - beta_i g_{i-1})/alpha_i, eps_i = a_i.       */
+void orc_penta_forward(int64_t n, const double *alpha, const double *beta,
+                       const double *eps, const double *f, double *g)
+{
+    g[0] = f[0] / alpha[0];
+    g[1] = (f[1] - beta[1] * g[0]) / alpha[1];
+    for (int64_t i = 2; i < n; ++i)
+        g[i] = (f[i] - eps[i] * g[i - 2] - beta[i] * g[i - 1]) / alpha[i];
+}
+
+/* Back substitution: x_{N-1} = g_{N-1}, x_{N-2} = g_{N-2} - gamma_{N-2} x_{N-1},
+ * x_i = g_i - gamma_i x_{i+1} - delta_i x_{i+2}.                          */
+void orc_penta_backward(int64_t n, const double *gamma, const double *delta,
+                        const double *g, double *x)
+{
+    x[n - 1] = g[n - 1];
+    x[n - 2] = g[n - 2] - gamma[n - 2] * x[n - 1];
+    for (int64_t i = n - 3; i >= 0; --i)
+        x[i] = g[i] - gamma[i] * x[i + 1] - delta[i] * x[i + 2];
+}
+
+/* Factor + forward + back for one system.  x may alias f. */
+int orc_penta_solve(int64_t n, const double *a, const double *b, const double *c,
+                    const double *d, const double *e, const double *f, double *x)
+{
+    double *w = (double *)malloc(sizeof(double) * 5 * (size_t)n);
+    double *al = w, *be = w + n, *ga = w + 2 * n, *de = w + 3 * n, *g = w + 4 * n;
+    int info = orc_penta_factor(n, a, b, c, d, e, al, be, ga, de);
+    orc_penta_forward(n, al, be, a, f, g);
+    orc_penta_backward(n, ga, de, g, x);
+    free(w);
+    return info;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P] Periodic (cyclic) pentadiagonal matrix and Navon's reduction         */
+/*                                                                          */
+/* The periodic matrix has the same five diagonals, with column indices     */
+/* taken modulo N: row i holds a_i at column i-2, b_i at i-1, c_i at i,     */
+/* d_i at i+1, e_i at i+2 (mod N).  Requires N >= 6 so that the five        */
+/* columns of a row are distinct and E has at least four rows.              */
+/*                                                                          */
+/* Partition (page: E is A without its last two rows and columns):          */
+/*     A = [ E  F ]   E: (N-2)x(N-2), F: (N-2)x2                            */
+/*         [ G  H ]   G: 2x(N-2),     H: 2x2                                */
+/* Block equations (10): E X + F x_t = f_hat,  G X + H x_t = f_t.           */
+/* (11): X = E^{-1} (f_hat - F x_t).                                        */
+/* (12): x_t = (H - G E^{-1} F)^{-1} (f_t - G E^{-1} f_hat).                */
+/* The 2x2 inverse and the rows of G E^{-1} are computed once and stored;   */
+/* the rows of G E^{-1} are obtained as (E^{-1})^T applied to the rows of G */
+/* (i.e. solves with E^T), as the page states.                              */
+/* ------------------------------------------------------------------------ */
+
+/* A[i][j] of the periodic matrix, straight from its definition. */
+static double cyc_entry(int64_t n, const double *a, const double *b, const double *c,
+                        const double *d, const double *e, int64_t i, int64_t j)
+{
+    int64_t k = ((j - i) % n + n) % n;
+    if (k == 0) return c[i];
+    if (k == 1) return d[i];
+    if (k == 2) return e[i];
+    if (k == n - 1) return b[i];
+    if (k == n - 2) return a[i];
+    return 0.0;
+}
+
+typedef struct {
+    int64_t n, m;                         /* m = n - 2 rows of E              */
+    double *Ea, *Eb, *Ec, *Ed, *Ee;       /* diagonals of E                   */
+    double *al, *be, *ga, *de;            /* factors of E                     */
+    double *F0, *F1;                      /* the two columns of F (length m)  */
+    double *G0, *G1;                      /* the two rows of G (length m)     */
+    double *W0, *W1;                      /* the two rows of G E^{-1}         */
+    double H[4];                          /* H row-major                      */
+    double Sinv[4];                       /* (H - G E^{-1} F)^{-1} row-major  */
+    double *tmp;                          /* scratch of length m              */
+    double *mem;
+    int info;
+} cyc_setup;
+
+static void cyc_free(cyc_setup *s) { free(s->mem); s->mem = NULL; }
+
+static int cyc_init(cyc_setup *s, int64_t n, const double *a, const double *b,
+                    const double *c, const double *d, const double *e)
+{
+    int64_t m = n - 2, i;
+    s->n = n;
+    s->m = m;
+    s->mem = (double *)calloc((size_t)m * 18, sizeof(double));
+    double *p = s->mem;
+    s->Ea = p; p += m; s->Eb = p; p += m; s->Ec = p; p += m; s->Ed = p; p += m; s->Ee = p; p += m;
+    s->al = p; p += m; s->be = p; p += m; s->ga = p; p += m; s->de = p; p += m;
+    s->F0 = p; p += m; s->F1 = p; p += m; s->G0 = p; p += m; s->G1 = p; p += m;
+    s->W0 = p; p += m; s->W1 = p; p += m; s->tmp = p; p += m;
+    double *Zc = p; p += m;               /* a column of Z = E^{-1} F         */
+    double *gt = p; p += m;               /* forward result for E^T solves    */
+
+    /* E, F, G, H taken entry by entry from the periodic matrix. */
+    for (i = 0; i < m; ++i) {
+        s->Ea[i] = (i >= 2) ? cyc_entry(n, a, b, c, d, e, i, i - 2) : 0.0;
+        s->Eb[i] = (i >= 1) ? cyc_entry(n, a, b, c, d, e, i, i - 1) : 0.0;
+        s->Ec[i] = cyc_entry(n, a, b, c, d, e, i, i);
+        s->Ed[i] = (i + 1 < m) ? cyc_entry(n, a, b, c, d, e, i, i + 1) : 0.0;
+        s->Ee[i] = (i + 2 < m) ? cyc_entry(n, a, b, c, d, e, i, i + 2) : 0.0;
+        s->F0[i] = cyc_entry(n, a, b, c, d, e, i, m);
+        s->F1[i] = cyc_entry(n, a, b, c, d, e, i, m + 1);
+        s->G0[i] = cyc_entry(n, a, b, c, d, e, m, i);
+        s->G1[i] = cyc_entry(n, a, b, c, d, e, m + 1, i);
+    }
+    s->H[0] = cyc_entry(n, a, b, c, d, e, m, m);
+    s->H[1] = cyc_entry(n, a, b, c, d, e, m, m + 1);
+    s->H[2] = cyc_entry(n, a, b, c, d, e, m + 1, m);
+    s->H[3] = cyc_entry(n, a, b, c, d, e, m + 1, m + 1);
+
+    /* Factor E. */
+    s->info = orc_penta_factor(m, s->Ea, s->Eb, s->Ec, s->Ed, s->Ee,
+                               s->al, s->be, s->ga, s->de);
+
+    /* S = H - G Z with Z = E^{-1} F, one column of Z at a time. */
+    double S[4] = {s->H[0], s->H[1], s->H[2], s->H[3]};
+    for (int col = 0; col < 2; ++col) {
+        const double *Fc = col ? s->F1 : s->F0;
+        orc_penta_forward(m, s->al, s->be, s->Ea, Fc, s->tmp);
+        orc_penta_backward(m, s->ga, s->de, s->tmp, Zc);
+        double g0z = 0.0, g1z = 0.0;
+        for (i = 0; i < m; ++i) {
+            g0z += s->G0[i] * Zc[i];
+            g1z += s->G1[i] * Zc[i];
+        }
+        S[0 + col] -= g0z;
+        S[2 + col] -= g1z;
+    }
+    double det = S[0] * S[3] - S[1] * S[2];
+    s->Sinv[0] = S[3] / det;
+    s->Sinv[1] = -S[1] / det;
+    s->Sinv[2] = -S[2] / det;
+    s->Sinv[3] = S[0] / det;
+    if (!s->info && bad_pivot(det)) s->info = (int)m + 1;
+
+    /* Rows of G E^{-1}: solve E^T w = G_r^T.  E^T is pentadiagonal with
+     * (E^T)[i][i-2] = E[i-2][i] = Ee[i-2], (E^T)[i][i-1] = Ed[i-1],
+     * (E^T)[i][i] = Ec[i], (E^T)[i][i+1] = Eb[i+1], (E^T)[i][i+2] = Ea[i+2]. */
+    double *ta = (double *)calloc((size_t)m * 9, sizeof(double));
+    double *tb = ta + m, *tc = ta + 2 * m, *td = ta + 3 * m, *te = ta + 4 * m;
+    double *tal = ta + 5 * m, *tbe = ta + 6 * m, *tga = ta + 7 * m, *tde = ta + 8 * m;
+    for (i = 0; i < m; ++i) {
+        ta[i] = (i >= 2) ? s->Ee[i - 2] : 0.0;
+        tb[i] = (i >= 1) ? s->Ed[i - 1] : 0.0;
+        tc[i] = s->Ec[i];
+        td[i] = (i + 1 < m) ? s->Eb[i + 1] : 0.0;
+        te[i] = (i + 2 < m) ? s->Ea[i + 2] : 0.0;
+    }
+    orc_penta_factor(m, ta, tb, tc, td, te, tal, tbe, tga, tde);
+    orc_penta_forward(m, tal, tbe, ta, s->G0, gt);
+    orc_penta_backward(m, tga, tde, gt, s->W0);
+    orc_penta_forward(m, tal, tbe, ta, s->G1, gt);
+    orc_penta_backward(m, tga, tde, gt, s->W1);
+    free(ta);
+    return s->info;
+}
+
+/* One periodic solve with a prepared setup: x_t by (12) first, then the
+ * modified right-hand side and E^{-1} by (11).  x may alias f. */
+static void cyc_apply(const cyc_setup *s, const double *f, double *x)
+{
+    int64_t m = s->m, i;
+    double s0 = 0.0, s1 = 0.0;
+    for (i = 0; i < m; ++i) {
+        s0 += s->W0[i] * f[i];
+        s1 += s->W1[i] * f[i];
+    }
+    double r0 = f[m] - s0, r1 = f[m + 1] - s1;
+    double xt0 = s->Sinv[0] * r0 + s->Sinv[1] * r1;
+    double xt1 = s->Sinv[2] * r0 + s->Sinv[3] * r1;
+    for (i = 0; i < m; ++i)
+        s->tmp[i] = f[i] - s->F0[i] * xt0 - s->F1[i] * xt1;
+    double *g = (double *)malloc(sizeof(double) * (size_t)m);
+    orc_penta_forward(m, s->al, s->be, s->Ea, s->tmp, g);
+    orc_penta_backward(m, s->ga, s->de, g, x);
+    free(g);
+    x[m] = xt0;
+    x[m + 1] = xt1;
+}
+
+int orc_penta_cyclic_solve(int64_t n, const double *a, const double *b, const double *c,
+                           const double *d, const double *e, const double *f, double *x)
+{
+    cyc_setup s;
+    int info = cyc_init(&s, n, a, b, c, d, e);
+    cyc_apply(&s, f, x);
+    cyc_free(&s);
+    return info;
+}
+
+/* Exposes the setup so tests can inspect Z-free quantities directly:
+ * out = [W0 (m), W1 (m), Sinv (4)]. */
+int orc_penta_cyclic_setup(int64_t n, const double *a, const double *b, const double *c,
+                           const double *d, const double *e, double *out)
+{
+    cyc_setup s;
+    int info = cyc_init(&s, n, a, b, c, d, e);
+    memcpy(out, s.W0, sizeof(double) * (size_t)s.m);
+    memcpy(out + s.m, s.W1, sizeof(double) * (size_t)s.m);
+    memcpy(out + 2 * s.m, s.Sinv, sizeof(double) * 4);
+    cyc_free(&s);
+    return info;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Batch drivers (flat layout).  coef_stride = n: per-system diagonals;     */
+/* coef_stride = 0: one set of diagonals shared by every system, factored   */
+/* once ("constant" use on the cuPentBatch page).  x holds f on entry.      */
+/* ------------------------------------------------------------------------ */
+
+void orc_penta_solve_batch(int64_t n, int64_t batch, int64_t coef_stride,
+                           const double *a, const double *b, const double *c,
+                           const double *d, const double *e, double *x, int32_t *info)
+{
+    if (coef_stride == 0) {
+        double *w = (double *)malloc(sizeof(double) * 4 * (size_t)n);
+        double *al = w, *be = w + n, *ga = w + 2 * n, *de = w + 3 * n;
+        int inf = orc_penta_factor(n, a, b, c, d, e, al, be, ga, de);
+        #pragma omp parallel for schedule(static)
+        for (int64_t s = 0; s < batch; ++s) {
+            double *g = (double *)malloc(sizeof(double) * (size_t)n);
+            orc_penta_forward(n, al, be, a, x + s * n, g);
+            orc_penta_backward(n, ga, de, g, x + s * n);
+            free(g);
+            if (info) info[s] = inf;
+        }
+        free(w);
+        return;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < batch; ++s) {
+        int64_t o = s * coef_stride;
+        int inf = orc_penta_solve(n, a + o, b + o, c + o, d + o, e + o, x + s * n, x + s * n);
+        if (info) info[s] = inf;
+    }
+}
+
+void orc_penta_cyclic_solve_batch(int64_t n, int64_t batch, int64_t coef_stride,
+                                  const double *a, const double *b, const double *c,
+                                  const double *d, const double *e, double *x, int32_t *info)
+{
+    if (coef_stride == 0) {
+        cyc_setup s0;
+        int inf = cyc_init(&s0, n, a, b, c, d, e);
+        #pragma omp parallel
+        {
+            cyc_setup s = s0;   /* private scratch, shared read-only factors */
+            double *tmp = (double *)malloc(sizeof(double) * (size_t)s.m);
+            s.tmp = tmp;
+            #pragma omp for schedule(static)
+            for (int64_t k = 0; k < batch; ++k) {
+                cyc_apply(&s, x + k * n, x + k * n);
+                if (info) info[k] = inf;
+            }
+            free(tmp);
+        }
+        cyc_free(&s0);
+        return;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < batch; ++k) {
+        int64_t o = k * coef_stride;
+        int inf = orc_penta_cyclic_solve(n, a + o, b + o, c + o, d + o, e + o,
+                                         x + k * n, x + k * n);
+        if (info) info[k] = inf;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P] Periodic hyperdiffusion, implicit step (I + sigma D4) C^{n+1} = C^n  */
+/* with the centred fourth difference D4 = [1, -4, 6, -4, 1] and            */
+/* sigma = dt / dx^4: a = e = sigma, b = d = -4 sigma, c = 1 + 6 sigma.     */
+/* The matrix is factored once and applied nsteps times to every system.   */
+/* diag != NULL: five shared length-n diagonals [a|b|c|d|e] used instead.   */
+/* ------------------------------------------------------------------------ */
+
+int orc_hyperdiffusion(int64_t n, int64_t batch, double dt, double dx,
+                       const double *diag, double *C, int64_t nsteps)
+{
+    double *own = NULL;
+    const double *a, *b, *c, *d, *e;
+    if (diag) {
+        a = diag; b = diag + n; c = diag + 2 * n; d = diag + 3 * n; e = diag + 4 * n;
+    } else {
+        double sigma = dt / (dx * dx * dx * dx);
+        own = (double *)malloc(sizeof(double) * 5 * (size_t)n);
+        for (int64_t i = 0; i < n; ++i) {
+            own[i] = sigma;
+            own[n + i] = -4.0 * sigma;
+            own[2 * n + i] = 1.0 + 6.0 * sigma;
+            own[3 * n + i] = -4.0 * sigma;
+            own[4 * n + i] = sigma;
+        }
+        a = own; b = own + n; c = own + 2 * n; d = own + 3 * n; e = own + 4 * n;
+    }
+    cyc_setup s0;
+    int inf = cyc_init(&s0, n, a, b, c, d, e);
+    #pragma omp parallel
+    {
+        cyc_setup s = s0;
+        double *tmp = (double *)malloc(sizeof(double) * (size_t)s.m);
+        s.tmp = tmp;
+        #pragma omp for schedule(static)
+        for (int64_t k = 0; k < batch; ++k)
+            for (int64_t t = 0; t < nsteps; ++t)
+                cyc_apply(&s, C + k * n, C + k * n);
+        free(tmp);
+    }
+    cyc_free(&s0);
+    free(own);
+    return inf;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [H] Hines algorithm (Algorithm 1) for one tree-tridiagonal system.       */
+/*                                                                          */
+/* Matrix: A[i][i] = d_i, A[p_i][i] = u_i, A[i][p_i] = l_i, with p_i < i    */
+/* for i >= 1 (the numbering of Fig. 1 puts each parent first); p_0 is not  */
+/* read.  d and rhs are overwritten as in the page's code; on return rhs    */
+/* holds the solution V.  Backward sweep from the last compartment down to  */
+/* compartment 1 (the root has no parent), then the root division, then the */
+/* forward sweep from compartment 1 up.                                     */
+/* Returns 0, or 1 + the first compartment (in elimination order n-1 ... 1, */
+/* then 0) whose pivot d_i is zero / non-finite when it is divided by.      */
+/* ------------------------------------------------------------------------ */
+
+int orc_hines_solve(int64_t n, const int32_t *p, const double *u, const double *l,
+                    double *d, double *rhs)
+{
+    int info = 0;
+    int64_t i;
+    double factor;
+    for (i = n - 1; i >= 1; --i) {
+        if (!info && bad_pivot(d[i])) info = (int)i + 1;
+        factor = u[i] / d[i];
+        d[p[i]] -= factor * l[i];
+        rhs[p[i]] -= factor * rhs[i];
+    }
+    if (!info && bad_pivot(d[0])) info = 1;
+    rhs[0] /= d[0];
+    for (i = 1; i < n; ++i) {
+        rhs[i] -= l[i] * rhs[p[i]];
+        rhs[i] /= d[i];
+    }
+    return info;
+}
+
+/* One shared tree, batch neurons, flat arrays [batch][n]; d is not modified
+ * (a private copy is eliminated), rhs returns V. */
+void orc_hines_solve_batch(int64_t n, int64_t batch, const int32_t *p, const double *u,
+                           const double *l, const double *d, double *rhs, int32_t *info)
+{
+    #pragma omp parallel
+    {
+        double *dd = (double *)malloc(sizeof(double) * (size_t)n);
+        #pragma omp for schedule(static)
+        for (int64_t s = 0; s < batch; ++s) {
+            memcpy(dd, d + s * n, sizeof(double) * (size_t)n);
+            int inf = orc_hines_solve(n, p, u + s * n, l + s * n, dd, rhs + s * n);
+            if (info) info[s] = inf;
+        }
+        free(dd);
+    }
+}
+
+/* One tree per neuron: neuron s occupies [off[s], off[s+1]) of every array
+ * (parent indices local to the neuron). */
+void orc_hines_multi_batch(int64_t batch, const int64_t *off, const int32_t *p,
+                           const double *u, const double *l, const double *d,
+                           double *rhs, int32_t *info)
+{
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t s = 0; s < batch; ++s) {
+        int64_t o = off[s], n = off[s + 1] - off[s];
+        double *dd = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        memcpy(dd, d + o, sizeof(double) * (size_t)n);
+        int inf = n > 0 ? orc_hines_solve(n, p + o, u + o, l + o, dd, rhs + o) : 0;
+        if (info) info[s] = inf;
+        free(dd);
+    }
+}

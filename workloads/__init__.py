@@ -1,0 +1,284 @@
+"""Seeded synthetic inputs for the batched banded solvers.
+
+This module only draws random numbers and arranges them into arrays; it holds
+none of the solvers' arithmetic.  Both the CPU oracle (``oracle/``) and the
+GPU library (``banded_pde_solvers_amd``) are fed from here, and neither of
+them is imported by it.
+
+Layouts
+-------
+Every generator returns arrays in the *interleaved* layout the GPU library
+consumes: shape ``(rows, batch)``, C order, so element (row i, system s) sits
+at ``i * batch + s`` and the systems are the fastest-varying index (the
+interleaved layout of the cuPentBatch page, section on the batched GPU
+implementation; the Full-Interleaved layout of the Hines page, section 3).
+``to_flat`` gives the oracle's system-major layout (one system per row, as in
+the pages' serial CPU codes).
+
+Workloads
+---------
+``hyperdiffusion_modes``   periodic hyperdiffusion, initial condition a sum of
+                            seeded Fourier modes (N=256, batch=64 at full size)
+``hyperdiffusion_random``  RHS / initial state U(-1,1) (N=1024, batch=16384)
+``penta_dominant``         strictly row-dominant pentadiagonal systems with
+                            per-system coefficients (N=512, batch=65536)
+``hines_mono``             one random tree shared by every neuron
+                            (n=512, 100000 neurons)
+``hines_multi``            one random tree per neuron, n uniform in
+                            [256, 2048] (32768 neurons)
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+SEED_BASE = 20260
+
+
+def rng_for(cfg: int) -> np.random.Generator:
+    """PCG64 generator for workload number ``cfg`` (seed 20260 + cfg)."""
+    return np.random.default_rng(SEED_BASE + int(cfg))
+
+
+def to_flat(x: np.ndarray) -> np.ndarray:
+    """Interleaved (rows, batch) -> flat (batch, rows), contiguous."""
+    return np.ascontiguousarray(np.asarray(x).T)
+
+
+def to_interleaved(x: np.ndarray) -> np.ndarray:
+    """Flat (batch, rows) -> interleaved (rows, batch), contiguous."""
+    return np.ascontiguousarray(np.asarray(x).T)
+
+
+# ----------------------------------------------------------------------------
+# Periodic hyperdiffusion
+# ----------------------------------------------------------------------------
+
+@dataclass
+class ModesIC:
+    C0: np.ndarray        # (n, batch) initial state
+    k: np.ndarray         # (batch, nmodes) integer wavenumbers
+    amp: np.ndarray       # (batch, nmodes)
+    phase: np.ndarray     # (batch, nmodes)
+
+
+def hyperdiffusion_modes(n: int = 256, batch: int = 64, nmodes: int = 4,
+                         kmax: int = 16, rng: np.random.Generator | None = None,
+                         offset: float = 0.0) -> ModesIC:
+    """Initial state = sum of ``nmodes`` distinct seeded Fourier modes.
+
+    Per system: distinct integer wavenumbers k_j drawn uniformly from
+    [1, kmax], amplitudes U(-1, 1), phases U(0, 2*pi); grid x_i = i/n on the
+    unit periodic domain, C_i = offset + sum_j A_j cos(2*pi*k_j*x_i + phi_j).
+    Draw order: all wavenumbers (system by system), then amplitudes, then
+    phases.
+    """
+    rng = rng if rng is not None else rng_for(0)
+    if nmodes > kmax:
+        raise ValueError("nmodes must not exceed kmax (wavenumbers are distinct)")
+    k = np.stack([rng.choice(kmax, size=nmodes, replace=False) + 1
+                  for _ in range(batch)]).astype(np.int64)
+    amp = rng.uniform(-1.0, 1.0, size=(batch, nmodes))
+    phase = rng.uniform(0.0, 2.0 * math.pi, size=(batch, nmodes))
+    x = np.arange(n, dtype=np.float64) / n
+    # (n, batch, nmodes) -> sum over modes
+    arg = 2.0 * math.pi * x[:, None, None] * k[None, :, :] + phase[None, :, :]
+    C0 = offset + np.sum(amp[None, :, :] * np.cos(arg), axis=2)
+    return ModesIC(np.ascontiguousarray(C0), k, amp, phase)
+
+
+def hyperdiffusion_random(n: int = 1024, batch: int = 16384,
+                          rng: np.random.Generator | None = None,
+                          dtype=np.float64) -> np.ndarray:
+    """State / RHS drawn U(-1, 1) as shape (n, batch)."""
+    rng = rng if rng is not None else rng_for(1)
+    return rng.uniform(-1.0, 1.0, size=(n, batch)).astype(dtype)
+
+
+# ----------------------------------------------------------------------------
+# General pentadiagonal systems, per-system coefficients
+# ----------------------------------------------------------------------------
+
+@dataclass
+class PentaBatch:
+    a: np.ndarray   # A[i][i-2]   (n, batch)
+    b: np.ndarray   # A[i][i-1]
+    c: np.ndarray   # A[i][i]
+    d: np.ndarray   # A[i][i+1]
+    e: np.ndarray   # A[i][i+2]
+    f: np.ndarray   # right-hand side
+
+    def astype(self, dtype) -> "PentaBatch":
+        return PentaBatch(*(np.ascontiguousarray(v.astype(dtype)) for v in
+                            (self.a, self.b, self.c, self.d, self.e, self.f)))
+
+    @property
+    def diagonals(self):
+        return (self.a, self.b, self.c, self.d, self.e)
+
+
+def penta_dominant(n: int = 512, batch: int = 65536, cyclic: bool = False,
+                   rng: np.random.Generator | None = None,
+                   chunk: int = 4096) -> PentaBatch:
+    """Strictly row-dominant pentadiagonal batch.
+
+    Off-diagonals a, b, d, e ~ U(-1, 1) drawn as one (4, n, batch) block (in
+    that order); for a non-periodic system the entries that would fall
+    outside the matrix (a_0, a_1, b_0, d_{n-1}, e_{n-2}, e_{n-1}) are set to
+    zero.  Then c = 1 + |a| + |b| + |d| + |e| + U(0, 1) and f ~ U(-1, 1).
+    For a periodic (cyclic) system the wrap-around entries are kept.
+
+    The draws are made in column blocks of ``chunk`` systems so that the
+    full-size workload never holds more than one block of temporaries; the
+    result depends on ``chunk``, which is therefore fixed by default.
+    """
+    rng = rng if rng is not None else rng_for(2)
+    a = np.empty((n, batch)); b = np.empty((n, batch)); c = np.empty((n, batch))
+    d = np.empty((n, batch)); e = np.empty((n, batch)); f = np.empty((n, batch))
+    for s0 in range(0, batch, chunk):
+        s1 = min(batch, s0 + chunk)
+        w = s1 - s0
+        off = rng.uniform(-1.0, 1.0, size=(4, n, w))
+        if not cyclic:
+            off[0, 0:2, :] = 0.0          # a_0, a_1
+            off[1, 0, :] = 0.0            # b_0
+            off[2, n - 1, :] = 0.0        # d_{n-1}
+            off[3, n - 2:n, :] = 0.0      # e_{n-2}, e_{n-1}
+        a[:, s0:s1], b[:, s0:s1], d[:, s0:s1], e[:, s0:s1] = off
+        c[:, s0:s1] = 1.0 + np.abs(off).sum(axis=0) + rng.uniform(0.0, 1.0, size=(n, w))
+        f[:, s0:s1] = rng.uniform(-1.0, 1.0, size=(n, w))
+    return PentaBatch(a, b, c, d, e, f)
+
+
+# ----------------------------------------------------------------------------
+# Hines (tree-tridiagonal) systems
+# ----------------------------------------------------------------------------
+
+def random_tree(n: int, rng: np.random.Generator, window: int = 8) -> np.ndarray:
+    """Parent vector with p_0 = -1 and p_i uniform in [max(0, i-window), i-1].
+
+    Every parent precedes its child, the numbering the Hines page requires
+    (section 2, Fig. 1).
+    """
+    p = np.empty(n, dtype=np.int32)
+    p[0] = -1
+    if n > 1:
+        i = np.arange(1, n)
+        p[1:] = rng.integers(np.maximum(0, i - window), i)
+    return p
+
+
+def tree_stats(p: np.ndarray) -> dict:
+    """Branch-point / leaf fractions and depth of one parent vector."""
+    n = len(p)
+    nchild = np.bincount(p[1:], minlength=n) if n > 1 else np.zeros(1, int)
+    depth = np.zeros(n, dtype=np.int64)
+    for i in range(1, n):
+        depth[i] = depth[p[i]] + 1
+    return {"n": n,
+            "branch_frac": float(np.mean(nchild >= 2)),
+            "leaf_frac": float(np.mean(nchild == 0)),
+            "depth": int(depth.max()),
+            "max_parent_distance": int(np.max(np.arange(1, n) - p[1:])) if n > 1 else 0}
+
+
+@dataclass
+class HinesMono:
+    parent: np.ndarray   # (n,) int32, parent[0] = -1
+    u: np.ndarray        # (n, batch)  A[p_i][i]  ("a" of the workload spec)
+    l: np.ndarray        # (n, batch)  A[i][p_i]  ("b" of the workload spec)
+    d: np.ndarray        # (n, batch)  diagonal
+    rhs: np.ndarray      # (n, batch)
+
+
+def _hines_values(parent: np.ndarray, shape, rng: np.random.Generator):
+    """u, l ~ U(-1, 0) (root row zero), d row-dominant, rhs ~ U(-1, 1).
+
+    d_i = 1 + |l_i| [i > 0] + sum over children c of |u_c| + U(0, 1): strict
+    row dominance of the tree matrix (A[i][p_i] = l_i, A[i][c] = u_c).
+    """
+    n = len(parent)
+    u = rng.uniform(-1.0, 0.0, size=shape)
+    l = rng.uniform(-1.0, 0.0, size=shape)
+    u[0] = 0.0
+    l[0] = 0.0
+    d = 1.0 + np.abs(l) + rng.uniform(0.0, 1.0, size=shape)
+    for i in range(1, n):
+        d[parent[i]] += np.abs(u[i])
+    rhs = rng.uniform(-1.0, 1.0, size=shape)
+    return u, l, d, rhs
+
+
+def hines_mono(n: int = 512, batch: int = 100000,
+               rng: np.random.Generator | None = None) -> HinesMono:
+    """One seeded tree shared by all neurons; per-neuron values.
+
+    Draw order: the tree, then u, l, the U(0,1) part of d, rhs, each as one
+    (n, batch) block.
+    """
+    rng = rng if rng is not None else rng_for(3)
+    p = random_tree(n, rng)
+    u, l, d, rhs = _hines_values(p, (n, batch), rng)
+    return HinesMono(p, u, l, d, rhs)
+
+
+@dataclass
+class HinesMulti:
+    sizes: np.ndarray     # (batch,) int32 compartments per neuron
+    offsets: np.ndarray   # (batch+1,) int64 start of each neuron in the flat arrays
+    parent: np.ndarray    # (total,) int32 parent index local to its neuron
+    u: np.ndarray         # (total,) float64
+    l: np.ndarray
+    d: np.ndarray
+    rhs: np.ndarray
+
+    @property
+    def batch(self) -> int:
+        return len(self.sizes)
+
+    def neuron(self, s: int):
+        o0, o1 = self.offsets[s], self.offsets[s + 1]
+        return (self.parent[o0:o1], self.u[o0:o1], self.l[o0:o1],
+                self.d[o0:o1], self.rhs[o0:o1])
+
+
+def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
+                rng: np.random.Generator | None = None) -> HinesMulti:
+    """One seeded tree per neuron, compartment count uniform in [nmin, nmax].
+
+    The sizes are drawn first (one block), then neuron by neuron: its tree,
+    then its u, l, d, rhs exactly as ``hines_mono`` draws them for batch 1.
+    Arrays are concatenated neuron after neuron (flat, system-major).
+    """
+    rng = rng if rng is not None else rng_for(4)
+    sizes = rng.integers(nmin, nmax + 1, size=batch).astype(np.int32)
+    offsets = np.zeros(batch + 1, dtype=np.int64)
+    np.cumsum(sizes, out=offsets[1:])
+    total = int(offsets[-1])
+    parent = np.empty(total, dtype=np.int32)
+    u = np.empty(total); l = np.empty(total); d = np.empty(total); rhs = np.empty(total)
+    for s in range(batch):
+        o0, o1 = offsets[s], offsets[s + 1]
+        p = random_tree(int(sizes[s]), rng)
+        us, ls, ds, rs = _hines_values(p, (int(sizes[s]),), rng)
+        parent[o0:o1] = p
+        u[o0:o1] = us; l[o0:o1] = ls; d[o0:o1] = ds; rhs[o0:o1] = rs
+    return HinesMulti(sizes, offsets, parent, u, l, d, rhs)
+
+
+# ----------------------------------------------------------------------------
+# The five named workloads at their full sizes
+# ----------------------------------------------------------------------------
+
+WORKLOADS = {
+    0: dict(name="hyperdiffusion_modes_n256_b64_10steps", kind="hyperdiffusion",
+            n=256, batch=64, dt=1e-6, dx=1.0 / 256, nsteps=10),
+    1: dict(name="cyclic_const_n1024_b16384_100steps", kind="hyperdiffusion",
+            n=1024, batch=16384, dt=1e-6, dx=1.0 / 1024, nsteps=100),
+    2: dict(name="penta_general_n512_b65536", kind="penta", n=512, batch=65536),
+    3: dict(name="hines_mono_n512_b100000", kind="hines_mono", n=512, batch=100000),
+    4: dict(name="hines_multi_b32768_n256to2048_20steps", kind="hines_multi",
+            batch=32768, nmin=256, nmax=2048, nsteps=20),
+}
