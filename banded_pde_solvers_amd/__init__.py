@@ -1,0 +1,327 @@
+"""Python binding of libbps -- batched banded solvers for MI355X (gfx950).
+
+A thin ctypes layer over the C ABI in ``include/bps.h``: it marshals torch
+tensors (device memory, current HIP stream) into plain pointers and sizes and
+raises ``BpsError`` on a non-OK status.  Every step of every solve runs in the
+HIP kernels of ``libbps.so``; there is no Python or CPU fallback, and calling
+anything here without the built library raises ``BpsLibraryMissing``.
+
+Array conventions (see bps.h):
+  * interleaved arrays are 2-D tensors of shape (n, ld) in C order, element
+    (row i, system s) at [i, s]; the first ``batch`` columns are used
+    (batch defaults to ld);
+  * shared diagonals (BPS_SHARED_COEF) are 1-D tensors of length n;
+  * dtypes: torch.float64 (BPS_F64) or torch.float32 (BPS_F32).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "BpsError", "BpsLibraryMissing", "BPS_F32", "BPS_F64", "BPS_CYCLIC", "BPS_SHARED_COEF",
+    "library_path", "load_library", "version",
+    "bps_penta_factor_bytes", "bps_penta_work_bytes",
+    "penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
+    "penta_factor_solve_batch",
+    "hyperdiffusion_work_bytes", "hyperdiffusion_step",
+    "HinesPlan", "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
+    "hines_work_bytes", "hines_solve_batch",
+]
+
+BPS_F32 = 1
+BPS_F64 = 2
+BPS_CYCLIC = 0x1
+BPS_SHARED_COEF = 0x2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_HERE, "libbps.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class BpsError(RuntimeError):
+    """A libbps call returned a non-OK status."""
+
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+class BpsLibraryMissing(RuntimeError):
+    """libbps.so has not been built (python -m banded_pde_solvers_amd.build)."""
+
+
+class PentaDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("n", ctypes.c_int64), ("batch", ctypes.c_int64), ("ld", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIBPATH
+
+
+def load_library():
+    """Load libbps.so and declare the C signatures (raises if it is missing)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIBPATH):
+            raise BpsLibraryMissing(
+                f"{_LIBPATH} not found: build it with 'python -m banded_pde_solvers_amd.build'")
+        L = ctypes.CDLL(_LIBPATH)
+        vp, i32p, i64, st = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, ctypes.c_int
+        dp = ctypes.POINTER(PentaDesc)
+        sig = {
+            "bps_status_str": ([st], ctypes.c_char_p),
+            "bps_last_error": ([], ctypes.c_char_p),
+            "bps_version": ([], ctypes.c_int),
+            "bps_penta_factor_bytes": ([dp], ctypes.c_size_t),
+            "penta_factor_batch": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], st),
+            "penta_solve_batch": ([dp, vp, vp, vp], st),
+            "penta_cyclic_solve_batch": ([dp, vp, vp, vp], st),
+            "bps_penta_work_bytes": ([dp], ctypes.c_size_t),
+            "penta_factor_solve_batch": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp], st),
+            "hyperdiffusion_work_bytes": ([st, i64, i64], ctypes.c_size_t),
+            "hyperdiffusion_step": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double, vp, vp,
+                                     i64, vp, vp], st),
+            "hines_plan_create": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64], st),
+            "hines_plan_destroy": ([vp], st),
+            "hines_plan_elems": ([vp], i64),
+            "hines_plan_unknowns": ([vp], i64),
+            "hines_pack": ([vp, st, vp, vp, vp], st),
+            "hines_unpack": ([vp, st, vp, vp, vp], st),
+            "hines_work_bytes": ([vp, st], ctypes.c_size_t),
+            "hines_solve_batch": ([vp, st, vp, vp, vp, vp, vp, vp, vp], st),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+        return L
+
+
+def version() -> int:
+    return int(load_library().bps_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        L = load_library()
+        raise BpsError(fn, status, (L.bps_last_error() or b"").decode() or
+                       L.bps_status_str(status).decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float64:
+        return BPS_F64
+    if t.dtype == torch.float32:
+        return BPS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected (libbps runs on the GPU only)")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _desc(dtype: int, flags: int, n: int, batch: int, ld: int) -> PentaDesc:
+    return PentaDesc(int(dtype), int(flags), int(n), int(batch), int(ld))
+
+
+def _geom(x, batch):
+    if x.dim() != 2:
+        raise ValueError("interleaved tensor of shape (n, ld) expected")
+    n, ld = x.shape
+    return int(n), int(batch if batch is not None else ld), int(ld)
+
+
+# ---------------------------------------------------------------------------
+# Pentadiagonal
+# ---------------------------------------------------------------------------
+
+def bps_penta_factor_bytes(n: int, batch: int, ld: int, dtype: int = BPS_F64, flags: int = 0) -> int:
+    return int(load_library().bps_penta_factor_bytes(ctypes.byref(_desc(dtype, flags, n, batch, ld))))
+
+
+def bps_penta_work_bytes(n: int, batch: int, ld: int, dtype: int = BPS_F64) -> int:
+    return int(load_library().bps_penta_work_bytes(ctypes.byref(_desc(dtype, 0, n, batch, ld))))
+
+
+def _flags(cyclic, shared):
+    return (BPS_CYCLIC if cyclic else 0) | (BPS_SHARED_COEF if shared else 0)
+
+
+def penta_factor_batch(a, b, c, d, e, factors, info=None, *, n=None, batch=None, ld=None,
+                       cyclic=False, stream=None):
+    """Factor a batch (per-system (n, ld) diagonals, or shared 1-D diagonals).
+
+    For shared diagonals give n/batch/ld of the systems to be solved later
+    (only n matters for the factors).  factors: uint8/float device tensor of
+    at least bps_penta_factor_bytes bytes.  info: int32 device tensor or None.
+    """
+    shared = a.dim() == 1
+    if shared:
+        n = int(a.shape[0]) if n is None else int(n)
+        batch = 1 if batch is None else int(batch)
+        ld = batch if ld is None else int(ld)
+    else:
+        n, batch, ld = _geom(a, batch)
+    dsc = _desc(_dtype_code(a), _flags(cyclic, shared), n, batch, ld)
+    need = load_library().bps_penta_factor_bytes(ctypes.byref(dsc))
+    if factors.numel() * factors.element_size() < need:
+        raise ValueError(f"factors buffer too small ({need} bytes needed)")
+    _check("penta_factor_batch", load_library().penta_factor_batch(
+        ctypes.byref(dsc), _ptr(a), _ptr(b), _ptr(c), _ptr(d), _ptr(e), _ptr(factors),
+        _ptr(info), _stream(stream)))
+    return factors
+
+
+def penta_solve_batch(factors, x, *, batch=None, shared=False, stream=None):
+    """x (n, ld): right-hand sides in, solutions out (non-periodic)."""
+    n, batch, ld = _geom(x, batch)
+    dsc = _desc(_dtype_code(x), _flags(False, shared), n, batch, ld)
+    _check("penta_solve_batch", load_library().penta_solve_batch(
+        ctypes.byref(dsc), _ptr(factors), _ptr(x), _stream(stream)))
+    return x
+
+
+def penta_cyclic_solve_batch(factors, x, *, batch=None, shared=False, stream=None):
+    """x (n, ld): right-hand sides in, solutions out (periodic)."""
+    n, batch, ld = _geom(x, batch)
+    dsc = _desc(_dtype_code(x), _flags(True, shared), n, batch, ld)
+    _check("penta_cyclic_solve_batch", load_library().penta_cyclic_solve_batch(
+        ctypes.byref(dsc), _ptr(factors), _ptr(x), _stream(stream)))
+    return x
+
+
+def penta_factor_solve_batch(a, b, c, d, e, x, work, info=None, *, batch=None, stream=None):
+    """Fused factor + solve, per-system non-periodic diagonals (n, ld)."""
+    n, batch, ld = _geom(x, batch)
+    dsc = _desc(_dtype_code(x), 0, n, batch, ld)
+    need = load_library().bps_penta_work_bytes(ctypes.byref(dsc))
+    if work.numel() * work.element_size() < need:
+        raise ValueError(f"work buffer too small ({need} bytes needed)")
+    _check("penta_factor_solve_batch", load_library().penta_factor_solve_batch(
+        ctypes.byref(dsc), _ptr(a), _ptr(b), _ptr(c), _ptr(d), _ptr(e), _ptr(x), _ptr(work),
+        _ptr(info), _stream(stream)))
+    return x
+
+
+# ---------------------------------------------------------------------------
+# Hyperdiffusion
+# ---------------------------------------------------------------------------
+
+def hyperdiffusion_work_bytes(n: int, batch: int, dtype: int = BPS_F64) -> int:
+    return int(load_library().hyperdiffusion_work_bytes(int(dtype), int(n), int(batch)))
+
+
+def hyperdiffusion_step(C, dt: float, dx: float, nsteps: int, work, diagonals=None, *,
+                        batch=None, stream=None):
+    """Advance C (n, ld) by nsteps implicit periodic hyperdiffusion steps."""
+    n, batch, ld = _geom(C, batch)
+    dt_code = _dtype_code(C)
+    need = load_library().hyperdiffusion_work_bytes(dt_code, n, batch)
+    if work.numel() * work.element_size() < need:
+        raise ValueError(f"work buffer too small ({need} bytes needed)")
+    _check("hyperdiffusion_step", load_library().hyperdiffusion_step(
+        dt_code, n, batch, ld, float(dt), float(dx), _ptr(diagonals), _ptr(C), int(nsteps),
+        _ptr(work), _stream(stream)))
+    return C
+
+
+# ---------------------------------------------------------------------------
+# Hines
+# ---------------------------------------------------------------------------
+
+class HinesPlan:
+    """Owns a bps_hines_plan (destroyed on close() / garbage collection)."""
+
+    def __init__(self, handle, batch, mono):
+        self._h = handle
+        self.batch = int(batch)
+        self.mono = bool(mono)
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan already destroyed")
+        return self._h
+
+    @property
+    def elems(self) -> int:
+        return int(load_library().hines_plan_elems(self.handle))
+
+    @property
+    def unknowns(self) -> int:
+        return int(load_library().hines_plan_unknowns(self.handle))
+
+    def close(self):
+        if self._h is not None:
+            _check("hines_plan_destroy", load_library().hines_plan_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def hines_plan_create(batch: int, sizes, parent, mono: bool, ld: int = 0) -> HinesPlan:
+    """sizes / parent: host int32 arrays (numpy or sequences), see bps.h."""
+    import numpy as np
+    sz = np.ascontiguousarray(np.asarray(sizes, dtype=np.int32).reshape(-1))
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
+    h = ctypes.c_void_p()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    _check("hines_plan_create", load_library().hines_plan_create(
+        ctypes.byref(h), int(batch), sz.ctypes.data_as(i32p), par.ctypes.data_as(i32p),
+        1 if mono else 0, int(ld)))
+    return HinesPlan(h, batch, mono)
+
+
+def hines_plan_destroy(plan: HinesPlan):
+    plan.close()
+
+
+def hines_pack(plan: HinesPlan, flat, packed, stream=None):
+    _check("hines_pack", load_library().hines_pack(plan.handle, _dtype_code(flat), _ptr(flat),
+                                                   _ptr(packed), _stream(stream)))
+    return packed
+
+
+def hines_unpack(plan: HinesPlan, packed, flat, stream=None):
+    _check("hines_unpack", load_library().hines_unpack(plan.handle, _dtype_code(packed),
+                                                       _ptr(packed), _ptr(flat), _stream(stream)))
+    return flat
+
+
+def hines_work_bytes(plan: HinesPlan, dtype: int = BPS_F64) -> int:
+    return int(load_library().hines_work_bytes(plan.handle, int(dtype)))
+
+
+def hines_solve_batch(plan: HinesPlan, u, l, d, rhs, work, info=None, stream=None):
+    """rhs: right-hand sides in, voltages out (solver layout of the plan)."""
+    _check("hines_solve_batch", load_library().hines_solve_batch(
+        plan.handle, _dtype_code(rhs), _ptr(u), _ptr(l), _ptr(d), _ptr(rhs), _ptr(work),
+        _ptr(info), _stream(stream)))
+    return rhs

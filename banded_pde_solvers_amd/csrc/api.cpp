@@ -1,0 +1,306 @@
+// api.cpp -- the extern "C" entry points of libbps: argument validation on
+// the host, then kernel launches on the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace bps {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+// from hines.hip
+bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,
+                            const int32_t *parent, int mono, int64_t ld);
+bps_status hines_plan_free(bps_hines_plan *p);
+bool hines_plan_general(const bps_hines_plan *p);
+template <typename T>
+bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, void *dst,
+                           hipStream_t st);
+bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, const void *d,
+                        void *rhs, void *work, int32_t *info, hipStream_t st);
+
+// Shape of a plan, read from the opaque struct defined in hines.hip.
+int64_t hines_plan_elems_of(const bps_hines_plan *p);
+int64_t hines_plan_unknowns_of(const bps_hines_plan *p);
+int64_t hines_plan_batch_of(const bps_hines_plan *p);
+
+static const int64_t kMaxDim = int64_t(1) << 40;
+
+static bps_status check_desc(const bps_penta_desc *dsc)
+{
+    if (!dsc) BPS_FAIL(BPS_EINVAL, "desc is NULL");
+    if (dtype_size(dsc->dtype) == 0) BPS_FAIL(BPS_EINVAL, "unknown dtype %d", dsc->dtype);
+    if (dsc->flags & ~(BPS_CYCLIC | BPS_SHARED_COEF))
+        BPS_FAIL(BPS_EINVAL, "unknown flags 0x%x", dsc->flags);
+    const int64_t nmin = (dsc->flags & BPS_CYCLIC) ? 6 : 4;
+    if (dsc->n < nmin || dsc->n > kMaxDim)
+        BPS_FAIL(BPS_EINVAL, "n = %lld must be in [%lld, 2^40]", (long long)dsc->n, (long long)nmin);
+    if (dsc->batch < 1 || dsc->batch > (int64_t(1) << 31) - kWave)
+        BPS_FAIL(BPS_EINVAL, "batch = %lld must be in [1, 2^31 - 64]", (long long)dsc->batch);
+    if (dsc->ld < dsc->batch) BPS_FAIL(BPS_EINVAL, "ld = %lld < batch = %lld", (long long)dsc->ld,
+                                       (long long)dsc->batch);
+    return BPS_OK;
+}
+
+static bps_status check_ptr(const void *p, const char *name, int dtype)
+{
+    if (!p) BPS_FAIL(BPS_EINVAL, "%s is NULL", name);
+    if (!aligned(p, dtype_size(dtype))) BPS_FAIL(BPS_EINVAL, "%s is not %zu-byte aligned", name,
+                                                 dtype_size(dtype));
+    return BPS_OK;
+}
+
+#define CHECK(x)                         \
+    do {                                 \
+        bps_status s_ = (x);             \
+        if (s_ != BPS_OK) return s_;     \
+    } while (0)
+
+}  // namespace bps
+
+using namespace bps;
+
+extern "C" {
+
+const char *bps_status_str(int status)
+{
+    switch (status) {
+    case BPS_OK: return "BPS_OK";
+    case BPS_EINVAL: return "BPS_EINVAL: invalid argument";
+    case BPS_ENOTSUP: return "BPS_ENOTSUP: unsupported combination";
+    case BPS_EHIP: return "BPS_EHIP: HIP runtime error";
+    case BPS_ENOMEM: return "BPS_ENOMEM: device allocation failed";
+    default: return "unknown bps_status";
+    }
+}
+
+const char *bps_last_error(void) { return g_err; }
+
+int bps_version(void) { return 100; }
+
+size_t bps_penta_factor_bytes(const bps_penta_desc *dsc)
+{
+    if (check_desc(dsc) != BPS_OK) return 0;
+    const bool shared = dsc->flags & BPS_SHARED_COEF;
+    const int64_t ldf = shared ? 1 : dsc->ld;
+    return size_t(penta_factor_elems(dsc->n, ldf, dsc->flags & BPS_CYCLIC)) * dtype_size(dsc->dtype);
+}
+
+bps_status penta_factor_batch(const bps_penta_desc *dsc, const void *a, const void *b,
+                              const void *c, const void *d, const void *e, void *factors,
+                              int32_t *info, void *stream)
+{
+    clear_error();
+    CHECK(check_desc(dsc));
+    CHECK(check_ptr(a, "a", dsc->dtype)); CHECK(check_ptr(b, "b", dsc->dtype));
+    CHECK(check_ptr(c, "c", dsc->dtype)); CHECK(check_ptr(d, "d", dsc->dtype));
+    CHECK(check_ptr(e, "e", dsc->dtype)); CHECK(check_ptr(factors, "factors", dsc->dtype));
+    if (info && !aligned(info, 4)) BPS_FAIL(BPS_EINVAL, "info is not 4-byte aligned");
+    const bool cyc = dsc->flags & BPS_CYCLIC, sh = dsc->flags & BPS_SHARED_COEF;
+    if (dsc->dtype == BPS_F64)
+        return launch_penta_factor<double>(dsc->n, dsc->batch, dsc->ld, cyc, sh, a, b, c, d, e,
+                                           factors, info, as_stream(stream));
+    return launch_penta_factor<float>(dsc->n, dsc->batch, dsc->ld, cyc, sh, a, b, c, d, e,
+                                      factors, info, as_stream(stream));
+}
+
+bps_status penta_solve_batch(const bps_penta_desc *dsc, const void *factors, void *x, void *stream)
+{
+    clear_error();
+    CHECK(check_desc(dsc));
+    if (dsc->flags & BPS_CYCLIC)
+        BPS_FAIL(BPS_EINVAL, "penta_solve_batch: periodic desc; use penta_cyclic_solve_batch");
+    CHECK(check_ptr(factors, "factors", dsc->dtype)); CHECK(check_ptr(x, "x", dsc->dtype));
+    const bool sh = dsc->flags & BPS_SHARED_COEF;
+    if (dsc->dtype == BPS_F64)
+        return launch_penta_solve<double>(dsc->n, dsc->batch, dsc->ld, sh, factors, x, as_stream(stream));
+    return launch_penta_solve<float>(dsc->n, dsc->batch, dsc->ld, sh, factors, x, as_stream(stream));
+}
+
+bps_status penta_cyclic_solve_batch(const bps_penta_desc *dsc, const void *factors, void *x,
+                                    void *stream)
+{
+    clear_error();
+    CHECK(check_desc(dsc));
+    if (!(dsc->flags & BPS_CYCLIC))
+        BPS_FAIL(BPS_EINVAL, "penta_cyclic_solve_batch: desc lacks BPS_CYCLIC");
+    CHECK(check_ptr(factors, "factors", dsc->dtype)); CHECK(check_ptr(x, "x", dsc->dtype));
+    const bool sh = dsc->flags & BPS_SHARED_COEF;
+    if (dsc->dtype == BPS_F64)
+        return launch_penta_cyclic_solve<double>(dsc->n, dsc->batch, dsc->ld, 1, sh, factors, x,
+                                                 as_stream(stream));
+    return launch_penta_cyclic_solve<float>(dsc->n, dsc->batch, dsc->ld, 1, sh, factors, x,
+                                            as_stream(stream));
+}
+
+size_t bps_penta_work_bytes(const bps_penta_desc *dsc)
+{
+    if (check_desc(dsc) != BPS_OK) return 0;
+    return size_t(2 * dsc->n * dsc->ld) * dtype_size(dsc->dtype);
+}
+
+bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, const void *b,
+                                    const void *c, const void *d, const void *e, void *x,
+                                    void *work, int32_t *info, void *stream)
+{
+    clear_error();
+    CHECK(check_desc(dsc));
+    if (dsc->flags != 0)
+        BPS_FAIL(BPS_ENOTSUP, "penta_factor_solve_batch supports per-system non-periodic systems only");
+    CHECK(check_ptr(a, "a", dsc->dtype)); CHECK(check_ptr(b, "b", dsc->dtype));
+    CHECK(check_ptr(c, "c", dsc->dtype)); CHECK(check_ptr(d, "d", dsc->dtype));
+    CHECK(check_ptr(e, "e", dsc->dtype)); CHECK(check_ptr(x, "x", dsc->dtype));
+    CHECK(check_ptr(work, "work", dsc->dtype));
+    if (info && !aligned(info, 4)) BPS_FAIL(BPS_EINVAL, "info is not 4-byte aligned");
+    if (dsc->dtype == BPS_F64)
+        return launch_penta_fused<double>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work, info,
+                                          as_stream(stream));
+    return launch_penta_fused<float>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work, info,
+                                     as_stream(stream));
+}
+
+size_t hyperdiffusion_work_bytes(int dtype, int64_t n, int64_t batch)
+{
+    if (dtype_size(dtype) == 0 || n < 6 || n > kMaxDim || batch < 1) return 0;
+    return size_t(5 * n + penta_factor_elems(n, 1, true)) * dtype_size(dtype);
+}
+
+bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
+                               double dx, const void *diagonals, void *C, int64_t nsteps,
+                               void *work, void *stream)
+{
+    clear_error();
+    bps_penta_desc dsc{dtype, BPS_CYCLIC | BPS_SHARED_COEF, n, batch, ld};
+    CHECK(check_desc(&dsc));
+    if (nsteps < 0) BPS_FAIL(BPS_EINVAL, "nsteps = %lld < 0", (long long)nsteps);
+    if (!std::isfinite(dt) || !std::isfinite(dx) || dx == 0.0)
+        BPS_FAIL(BPS_EINVAL, "dt and dx must be finite and dx nonzero");
+    CHECK(check_ptr(C, "C", dtype));
+    CHECK(check_ptr(work, "work", dtype));
+    if (diagonals) CHECK(check_ptr(diagonals, "diagonals", dtype));
+    hipStream_t st = as_stream(stream);
+    const size_t es = dtype_size(dtype);
+    char *w = static_cast<char *>(work);
+    const void *dg = diagonals;
+    if (!dg) {
+        const double sigma = dt / (dx * dx * dx * dx);
+        if (!std::isfinite(sigma)) BPS_FAIL(BPS_EINVAL, "sigma = dt/dx^4 is not finite");
+        CHECK(dtype == BPS_F64 ? launch_hyper_diagonals<double>(n, sigma, w, st)
+                               : launch_hyper_diagonals<float>(n, sigma, w, st));
+        dg = w;
+    }
+    void *fac = w + 5 * n * es;
+    const char *D = static_cast<const char *>(dg);
+    if (dtype == BPS_F64) {
+        CHECK(launch_penta_factor<double>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
+                                          D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
+        if (nsteps == 0) return BPS_OK;
+        return launch_penta_cyclic_solve<double>(n, batch, ld, nsteps, true, fac, C, st);
+    }
+    CHECK(launch_penta_factor<float>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
+                                     D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
+    if (nsteps == 0) return BPS_OK;
+    return launch_penta_cyclic_solve<float>(n, batch, ld, nsteps, true, fac, C, st);
+}
+
+// ---- Hines ----------------------------------------------------------------------
+
+bps_status hines_plan_create(bps_hines_plan **plan, int64_t batch, const int32_t *sizes,
+                             const int32_t *parent, int mono, int64_t ld)
+{
+    clear_error();
+    if (!plan) BPS_FAIL(BPS_EINVAL, "plan is NULL");
+    *plan = nullptr;
+    if (!sizes || !parent) BPS_FAIL(BPS_EINVAL, "sizes and parent must be host arrays");
+    if (batch < 1 || batch > (int64_t(1) << 31) - kWave) BPS_FAIL(BPS_EINVAL, "batch out of range");
+    if (mono) {
+        const int64_t n = sizes[0];
+        if (n < 1 || n > (int64_t(1) << 30)) BPS_FAIL(BPS_EINVAL, "n = %lld out of range", (long long)n);
+        if (ld == 0) ld = batch;
+        if (ld < batch) BPS_FAIL(BPS_EINVAL, "ld < batch");
+        for (int64_t i = 1; i < n; ++i)
+            if (parent[i] < 0 || parent[i] >= i)
+                BPS_FAIL(BPS_EINVAL, "parent[%lld] = %d not in [0, %lld)", (long long)i, parent[i],
+                         (long long)i);
+    } else {
+        int64_t off = 0;
+        for (int64_t s = 0; s < batch; ++s) {
+            const int32_t n = sizes[s];
+            if (n < 1 || n > (1 << 30)) BPS_FAIL(BPS_EINVAL, "sizes[%lld] = %d out of range",
+                                                 (long long)s, n);
+            for (int32_t i = 1; i < n; ++i)
+                if (parent[off + i] < 0 || parent[off + i] >= i)
+                    BPS_FAIL(BPS_EINVAL, "neuron %lld: parent[%d] = %d not in [0, %d)", (long long)s,
+                             i, parent[off + i], i);
+            off += n;
+        }
+    }
+    return hines_plan_build(plan, batch, sizes, parent, mono, ld);
+}
+
+bps_status hines_plan_destroy(bps_hines_plan *plan)
+{
+    clear_error();
+    if (!plan) return BPS_OK;
+    return hines_plan_free(plan);
+}
+
+int64_t hines_plan_elems(const bps_hines_plan *plan) { return plan ? hines_plan_elems_of(plan) : 0; }
+
+int64_t hines_plan_unknowns(const bps_hines_plan *plan)
+{
+    return plan ? hines_plan_unknowns_of(plan) : 0;
+}
+
+bps_status hines_pack(const bps_hines_plan *plan, int dtype, const void *flat, void *packed,
+                      void *stream)
+{
+    clear_error();
+    if (!plan) BPS_FAIL(BPS_EINVAL, "plan is NULL");
+    CHECK(check_ptr(flat, "flat", dtype)); CHECK(check_ptr(packed, "packed", dtype));
+    if (dtype == BPS_F64) return hines_transform<double>(plan, true, flat, packed, as_stream(stream));
+    return hines_transform<float>(plan, true, flat, packed, as_stream(stream));
+}
+
+bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const void *packed, void *flat,
+                        void *stream)
+{
+    clear_error();
+    if (!plan) BPS_FAIL(BPS_EINVAL, "plan is NULL");
+    CHECK(check_ptr(flat, "flat", dtype)); CHECK(check_ptr(packed, "packed", dtype));
+    if (dtype == BPS_F64) return hines_transform<double>(plan, false, packed, flat, as_stream(stream));
+    return hines_transform<float>(plan, false, packed, flat, as_stream(stream));
+}
+
+size_t hines_work_bytes(const bps_hines_plan *plan, int dtype)
+{
+    if (!plan || dtype != BPS_F64) return 0;
+    return size_t(hines_plan_elems_of(plan)) * 8 * (hines_plan_general(plan) ? 3 : 1);
+}
+
+bps_status hines_solve_batch(const bps_hines_plan *plan, int dtype, const void *u, const void *l,
+                             const void *d, void *rhs, void *work, int32_t *info, void *stream)
+{
+    clear_error();
+    if (!plan) BPS_FAIL(BPS_EINVAL, "plan is NULL");
+    if (dtype != BPS_F64) BPS_FAIL(BPS_ENOTSUP, "hines_solve_batch supports BPS_F64 only");
+    CHECK(check_ptr(u, "u", dtype)); CHECK(check_ptr(l, "l", dtype));
+    CHECK(check_ptr(d, "d", dtype)); CHECK(check_ptr(rhs, "rhs", dtype));
+    CHECK(check_ptr(work, "work", dtype));
+    if (info && !aligned(info, 4)) BPS_FAIL(BPS_EINVAL, "info is not 4-byte aligned");
+    return hines_launch(plan, u, l, d, rhs, work, info, as_stream(stream));
+}
+
+}  // extern "C"

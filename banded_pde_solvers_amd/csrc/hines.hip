@@ -1,0 +1,343 @@
+// hines.hip -- batched Hines (tree-tridiagonal) solves for gfx950.
+//
+// Method: Algorithm 1 of "Simulating the behavior of the human brain on
+// GPUs" (section 2): eliminate from the leaves to the root (factor u_i/d_i,
+// update the parent's diagonal and right-hand side), divide at the root, then
+// substitute from the root to the leaves.  One lane per neuron (section 3).
+//
+// Layouts: mono-morphology uses the Full-Interleaved layout [n][ld] with one
+// parent vector shared by every lane (wave-uniform, scalar loads).
+// Multi-morphology (section 4) uses the Block-Interleaved layout with a block
+// of 64 neurons (one wavefront) stored [rows_b][64]; neurons are sorted by
+// size so each block's lanes have nearly equal lengths, and each lane reads
+// its own parent stream stored in the same layout.
+//
+// Between the sweeps each compartment keeps q_i = rhs'_i / d'_i (written in
+// place into rhs) and m_i = l_i / d'_i (written to work), so the second sweep
+// is V_i = q_i - m_i V_{p_i}: algebraically the page's
+// (rhs'_i - l_i V_{p_i}) / d'_i with the division done once per compartment.
+//
+// Pending parent updates (subtractions from d and rhs of the parent) are held
+// in a per-lane ring of W slots in LDS, indexed by row mod W; a parent at
+// distance <= W from its child is always inside the ring.  Trees with a larger
+// parent distance use the general variant, which sends those updates through
+// per-lane accumulators in global memory (zeroed before each solve).
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+struct bps_hines_plan {
+    int mono = 1;
+    int64_t batch = 0;
+    int64_t n = 0;           // mono: compartments per neuron
+    int64_t ld = 0;          // mono: leading dimension
+    int64_t elems = 0;       // values per array in the solver layout
+    int64_t unknowns = 0;    // real compartments
+    int32_t max_dist = 0;    // largest i - p_i
+    int64_t nblocks = 0;     // multi: number of 64-neuron blocks
+    int32_t max_rows = 0;    // multi: largest block row count
+    // device arrays
+    int32_t *parent = nullptr;     // mono [n]; multi packed [elems]
+    int64_t *blk_off = nullptr;    // multi [nblocks]
+    int32_t *blk_rows = nullptr;   // multi [nblocks]
+    int32_t *lane_n = nullptr;     // multi [nblocks*64]
+    int32_t *lane_src = nullptr;   // multi [nblocks*64] original neuron (-1 empty)
+    int64_t *src_off = nullptr;    // multi [batch+1] offsets in the flat layout
+};
+
+namespace bps {
+
+constexpr int kRing = 16;   // LDS ring slots per lane
+
+struct HinesArgs {
+    int64_t batch, n, ld;            // mono geometry
+    const int64_t *blk_off;          // multi geometry
+    const int32_t *blk_rows, *lane_n, *lane_src;
+    const int32_t *parent;
+    const double *u, *l, *d;
+    double *rhs, *mwork, *gd, *gr;
+    int32_t *info;
+};
+
+template <bool MONO, bool GEN>
+__global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
+{
+    __shared__ double ring_d[kRing][kWave];
+    __shared__ double ring_r[kRing][kWave];
+    const int k = threadIdx.x;
+    int64_t base, ld;
+    int32_t rows, my_n, src;
+    if (MONO) {
+        const int64_t s = int64_t(blockIdx.x) * kWave + k;
+        base = s; ld = A.ld; rows = int32_t(A.n);
+        my_n = s < A.batch ? rows : 0;
+        src = s < A.batch ? int32_t(s) : -1;
+    } else {
+        const int64_t b = blockIdx.x;
+        base = A.blk_off[b] + k; ld = kWave; rows = A.blk_rows[b];
+        my_n = A.lane_n[b * kWave + k];
+        src = A.lane_src[b * kWave + k];
+    }
+    const double *u = A.u + base, *l = A.l + base, *d = A.d + base;
+    double *rhs = A.rhs + base, *mw = A.mwork + base;
+    const int32_t *par = MONO ? A.parent : A.parent + base;
+    const int64_t pst = MONO ? 1 : ld;   // parent stride
+    double *gd = GEN ? A.gd + base : nullptr, *gr = GEN ? A.gr + base : nullptr;
+
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) { ring_d[j][k] = 0.0; ring_r[j][k] = 0.0; }
+
+    int32_t bad = 0;
+    // ---- leaves -> root elimination --------------------------------------
+    for (int32_t i = rows - 1; i >= 1; --i) {
+        if (i >= my_n) continue;
+        const int64_t o = int64_t(i) * ld;
+        const int slot = i % kRing;
+        double pd = ring_d[slot][k], pr = ring_r[slot][k];
+        ring_d[slot][k] = 0.0; ring_r[slot][k] = 0.0;
+        if (GEN) { pd += gd[o]; pr += gr[o]; }
+        const double dd = d[o] - pd;            // d'_i
+        const double rr = rhs[o] - pr;          // rhs'_i
+        if (!bad && bad_pivot(dd)) bad = i + 1;
+        const double rcp = 1.0 / dd;
+        const double fac = u[o] * rcp;          // factor of Algorithm 1
+        const double li = l[o];
+        rhs[o] = rr * rcp;                      // q_i
+        mw[o] = li * rcp;                       // m_i
+        const int32_t p = par[int64_t(i) * pst];
+        if (!GEN || i - p <= kRing) {
+            const int ps = p % kRing;
+            ring_d[ps][k] += fac * li;
+            ring_r[ps][k] += fac * rr;
+        } else {
+            gd[int64_t(p) * ld] += fac * li;
+            gr[int64_t(p) * ld] += fac * rr;
+        }
+    }
+    double v0 = 0.0;
+    if (my_n > 0) {
+        double pd = ring_d[0][k], pr = ring_r[0][k];
+        if (GEN) { pd += gd[0]; pr += gr[0]; }
+        const double dd = d[0] - pd;
+        if (!bad && bad_pivot(dd)) bad = 1;
+        v0 = (rhs[0] - pr) / dd;
+        rhs[0] = v0;
+    }
+    if (src >= 0 && A.info) A.info[src] = bad;
+    // ---- root -> leaves substitution -------------------------------------
+    // ring_d now holds the last kRing voltages (V of row j in slot j mod kRing)
+    ring_d[0][k] = v0;
+    for (int32_t i = 1; i < rows; ++i) {
+        if (i >= my_n) break;
+        const int64_t o = int64_t(i) * ld;
+        const int32_t p = par[int64_t(i) * pst];
+        double vp;
+        if (!GEN || i - p <= kRing) vp = ring_d[p % kRing][k];
+        else vp = rhs[int64_t(p) * ld];
+        const double v = rhs[o] - mw[o] * vp;
+        rhs[o] = v;
+        ring_d[i % kRing][k] = v;
+    }
+}
+
+__global__ void k_fill_zero(double *p, int64_t count)
+{
+    for (int64_t i = lane_id(); i < count; i += int64_t(gridDim.x) * blockDim.x) p[i] = 0.0;
+}
+
+// ---- layout transforms ---------------------------------------------------------
+
+// mono: flat [batch][n]  <->  interleaved [n][ld]
+template <typename T, bool PACK>
+__global__ void k_mono_transpose(int64_t n, int64_t batch, int64_t ld, const T *__restrict__ src,
+                                 T *__restrict__ dst)
+{
+    const int64_t total = n * batch;
+    for (int64_t e = lane_id(); e < total; e += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t i = e / batch, s = e % batch;   // interleaved order: coalesced side
+        if (PACK) dst[i * ld + s] = src[s * n + i];
+        else dst[s * n + i] = src[i * ld + s];
+    }
+}
+
+// multi: flat (neuron after neuron)  <->  block-interleaved [rows_b][64]
+template <typename T, bool PACK>
+__global__ void k_multi_pack(const int64_t *__restrict__ blk_off, const int32_t *__restrict__ blk_rows,
+                             const int32_t *__restrict__ lane_n, const int32_t *__restrict__ lane_src,
+                             const int64_t *__restrict__ src_off, const T *__restrict__ src,
+                             T *__restrict__ dst)
+{
+    const int64_t b = blockIdx.x;
+    const int64_t rows = blk_rows[b], off = blk_off[b];
+    for (int64_t e = threadIdx.x; e < rows * kWave; e += blockDim.x) {
+        const int64_t i = e / kWave;
+        const int k = int(e % kWave);
+        const int32_t s = lane_src[b * kWave + k];
+        const bool live = s >= 0 && i < lane_n[b * kWave + k];
+        if (PACK) dst[off + e] = live ? src[src_off[s] + i] : T(0);
+        else if (live) dst[src_off[s] + i] = src[off + e];
+    }
+}
+
+// ---- host side -------------------------------------------------------------------
+
+template <typename T>
+static bps_status upload(T **dptr, const std::vector<T> &h)
+{
+    if (h.empty()) { *dptr = nullptr; return BPS_OK; }
+    hipError_t e = hipMalloc((void **)dptr, h.size() * sizeof(T));
+    if (e != hipSuccess) BPS_FAIL(BPS_ENOMEM, "hipMalloc of %zu bytes failed: %s",
+                                  h.size() * sizeof(T), hipGetErrorString(e));
+    BPS_HIP(hipMemcpy(*dptr, h.data(), h.size() * sizeof(T), hipMemcpyHostToDevice));
+    return BPS_OK;
+}
+
+static void free_plan(bps_hines_plan *p)
+{
+    if (!p) return;
+    (void)hipFree(p->parent); (void)hipFree(p->blk_off); (void)hipFree(p->blk_rows);
+    (void)hipFree(p->lane_n); (void)hipFree(p->lane_src); (void)hipFree(p->src_off);
+    delete p;
+}
+
+bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,
+                            const int32_t *parent, int mono, int64_t ld)
+{
+    auto *P = new bps_hines_plan();
+    P->mono = mono ? 1 : 0;
+    P->batch = batch;
+    bps_status st = BPS_OK;
+    if (mono) {
+        const int64_t n = sizes[0];
+        P->n = n;
+        P->ld = ld;
+        P->elems = n * ld;
+        P->unknowns = n * batch;
+        std::vector<int32_t> h(parent, parent + n);
+        h[0] = 0;   // never read; keep it a valid index
+        for (int64_t i = 1; i < n; ++i) P->max_dist = std::max<int32_t>(P->max_dist, int32_t(i - h[i]));
+        st = upload(&P->parent, h);
+    } else {
+        std::vector<int64_t> off(batch + 1, 0);
+        for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];
+        P->unknowns = off[batch];
+        std::vector<int32_t> order(batch);
+        std::iota(order.begin(), order.end(), 0);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t x, int32_t y) { return sizes[x] > sizes[y]; });
+        const int64_t nb = (batch + kWave - 1) / kWave;
+        P->nblocks = nb;
+        std::vector<int64_t> boff(nb);
+        std::vector<int32_t> brows(nb), ln(nb * kWave, 0), lsrc(nb * kWave, -1);
+        int64_t acc = 0;
+        for (int64_t b = 0; b < nb; ++b) {
+            int32_t rmax = 0;
+            for (int k = 0; k < kWave; ++k) {
+                const int64_t j = b * kWave + k;
+                if (j >= batch) break;
+                const int32_t s = order[j];
+                ln[j] = sizes[s];
+                lsrc[j] = s;
+                rmax = std::max(rmax, sizes[s]);
+            }
+            boff[b] = acc;
+            brows[b] = rmax;
+            acc += int64_t(rmax) * kWave;
+            P->max_rows = std::max(P->max_rows, rmax);
+        }
+        P->elems = acc;
+        std::vector<int32_t> pk(acc, 0);
+        for (int64_t b = 0; b < nb; ++b)
+            for (int k = 0; k < kWave; ++k) {
+                const int32_t s = lsrc[b * kWave + k];
+                if (s < 0) continue;
+                for (int32_t i = 1; i < sizes[s]; ++i) {
+                    const int32_t p = parent[off[s] + i];
+                    pk[boff[b] + int64_t(i) * kWave + k] = p;
+                    P->max_dist = std::max<int32_t>(P->max_dist, i - p);
+                }
+            }
+        if ((st = upload(&P->parent, pk)) == BPS_OK && (st = upload(&P->blk_off, boff)) == BPS_OK &&
+            (st = upload(&P->blk_rows, brows)) == BPS_OK && (st = upload(&P->lane_n, ln)) == BPS_OK &&
+            (st = upload(&P->lane_src, lsrc)) == BPS_OK)
+            st = upload(&P->src_off, off);
+    }
+    if (st != BPS_OK) { free_plan(P); return st; }
+    *out = P;
+    return BPS_OK;
+}
+
+bps_status hines_plan_free(bps_hines_plan *p)
+{
+    free_plan(p);
+    return BPS_OK;
+}
+
+bool hines_plan_general(const bps_hines_plan *p) { return p->max_dist > kRing; }
+int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }
+int64_t hines_plan_unknowns_of(const bps_hines_plan *p) { return p->unknowns; }
+int64_t hines_plan_batch_of(const bps_hines_plan *p) { return p->batch; }
+
+template <typename T>
+bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, void *dst,
+                           hipStream_t st)
+{
+    if (P->mono) {
+        const int64_t total = P->n * P->batch;
+        const unsigned grid = unsigned(std::min<int64_t>((total + 255) / 256, 65536));
+        if (pack)
+            hipLaunchKernelGGL((k_mono_transpose<T, true>), dim3(grid), dim3(256), 0, st, P->n,
+                               P->batch, P->ld, (const T *)src, (T *)dst);
+        else
+            hipLaunchKernelGGL((k_mono_transpose<T, false>), dim3(grid), dim3(256), 0, st, P->n,
+                               P->batch, P->ld, (const T *)src, (T *)dst);
+    } else {
+        if (pack)
+            hipLaunchKernelGGL((k_multi_pack<T, true>), dim3(unsigned(P->nblocks)), dim3(256), 0, st,
+                               P->blk_off, P->blk_rows, P->lane_n, P->lane_src, P->src_off,
+                               (const T *)src, (T *)dst);
+        else
+            hipLaunchKernelGGL((k_multi_pack<T, false>), dim3(unsigned(P->nblocks)), dim3(256), 0, st,
+                               P->blk_off, P->blk_rows, P->lane_n, P->lane_src, P->src_off,
+                               (const T *)src, (T *)dst);
+    }
+    BPS_LAUNCHED("hines layout transform");
+    return BPS_OK;
+}
+template bps_status hines_transform<float>(const bps_hines_plan *, bool, const void *, void *, hipStream_t);
+template bps_status hines_transform<double>(const bps_hines_plan *, bool, const void *, void *, hipStream_t);
+
+bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, const void *d,
+                        void *rhs, void *work, int32_t *info, hipStream_t st)
+{
+    const bool gen = hines_plan_general(P);
+    HinesArgs A{};
+    A.batch = P->batch; A.n = P->n; A.ld = P->ld;
+    A.blk_off = P->blk_off; A.blk_rows = P->blk_rows; A.lane_n = P->lane_n; A.lane_src = P->lane_src;
+    A.parent = P->parent;
+    A.u = (const double *)u; A.l = (const double *)l; A.d = (const double *)d;
+    A.rhs = (double *)rhs;
+    A.mwork = (double *)work;
+    A.gd = gen ? A.mwork + P->elems : nullptr;
+    A.gr = gen ? A.mwork + 2 * P->elems : nullptr;
+    A.info = info;
+    if (gen) {
+        hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, A.gd, 2 * P->elems);
+        BPS_LAUNCHED("k_fill_zero");
+    }
+    const dim3 grid(unsigned(P->mono ? (P->batch + kWave - 1) / kWave : P->nblocks));
+    if (P->mono) {
+        if (gen) hipLaunchKernelGGL((k_hines<true, true>), grid, dim3(kWave), 0, st, A);
+        else hipLaunchKernelGGL((k_hines<true, false>), grid, dim3(kWave), 0, st, A);
+    } else {
+        if (gen) hipLaunchKernelGGL((k_hines<false, true>), grid, dim3(kWave), 0, st, A);
+        else hipLaunchKernelGGL((k_hines<false, false>), grid, dim3(kWave), 0, st, A);
+    }
+    BPS_LAUNCHED("k_hines");
+    return BPS_OK;
+}
+
+}  // namespace bps

@@ -1,0 +1,32 @@
+// kernels.h -- host launchers of the HIP kernels (internal to libbps).
+#pragma once
+
+#include "common.h"
+
+namespace bps {
+
+template <typename T>
+bps_status launch_penta_factor(int64_t n, int64_t batch, int64_t ld, bool cyclic, bool shared,
+                               const void *a, const void *b, const void *c, const void *d,
+                               const void *e, void *fac, int32_t *info, hipStream_t st);
+template <typename T>
+bps_status launch_penta_solve(int64_t n, int64_t batch, int64_t ld, bool shared,
+                              const void *fac, void *x, hipStream_t st);
+template <typename T>
+bps_status launch_penta_cyclic_solve(int64_t n, int64_t batch, int64_t ld, int64_t nsteps,
+                                     bool shared, const void *fac, void *x, hipStream_t st);
+template <typename T>
+bps_status launch_penta_fused(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
+                              const void *c, const void *d, const void *e, void *x, void *work,
+                              int32_t *info, hipStream_t st);
+
+// Builds the five shared diagonals of I + sigma*D4 on the device.
+template <typename T>
+bps_status launch_hyper_diagonals(int64_t n, double sigma, void *diag, hipStream_t st);
+
+// Number of values of a factor buffer.
+inline int64_t penta_factor_elems(int64_t n, int64_t ldf, bool cyclic) {
+    return cyclic ? (9 * (n - 2) + 4) * ldf : 5 * n * ldf;
+}
+
+}  // namespace bps

@@ -1,0 +1,240 @@
+/*
+ * bps.h -- batched banded solvers for PDE time stepping on AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Every array argument named "device"
+ * is a pointer to GPU memory (hipMalloc / torch tensors); "host" arrays are
+ * ordinary CPU memory.  `stream` is a hipStream_t passed as void* (NULL = the
+ * default stream); every call only ENQUEUES work on it and returns without
+ * synchronising, except hines_plan_create / hines_plan_destroy, which
+ * allocate / free device memory and synchronise.  No solve allocates memory.
+ *
+ * Sources (web-page titles; sections named as on the pages):
+ *   [P] "cuPentBatch - A batched pentadiagonal solver for NVIDIA GPUs":
+ *       section "Pentadiagonal solver" (A = L R factorisation steps, the
+ *       forward steps for g, the back-substitution steps for x, six vectors
+ *       and in-place reuse of the factors), the hyperdiffusion section
+ *       (eq. (4) on a periodic domain, the centred fourth difference, the
+ *       periodic pentadiagonal matrix and Navon's reduction eqs. (10)-(12)),
+ *       and the section on the batched GPU implementation (interleaved
+ *       layout, factorisation split from the solve: "Constant" factors once,
+ *       "Rewrite" refactors every call).
+ *   [H] "Simulating the behavior of the human brain on GPUs": section 2
+ *       (cable equation discretised on a neuron tree, the parent vector,
+ *       the Hines matrix, Algorithm 1 `solveHines(u, l, d, rhs, p, cellSize)`),
+ *       section 3 (Full-Interleaved and Block-Interleaved layouts, one thread
+ *       per system, layout transformed once up front), section 4 (batches of
+ *       neurons with different morphologies).
+ *
+ * LAYOUTS
+ *   Interleaved (the [P] and [H] layout): element (row i, system s) of an
+ *   array is at index i*ld + s, 0 <= i < n, 0 <= s < batch, ld >= batch
+ *   (elements, not bytes).  Systems are the fastest-varying index, so one
+ *   elimination step over consecutive systems is one coalesced HBM stream.
+ *
+ * PRECISION
+ *   BPS_F64 (double) everywhere; BPS_F32 (float) for the pentadiagonal and
+ *   hyperdiffusion entry points.  No pivoting (as on [P]): the solves are
+ *   meant for diagonally dominant or symmetric positive definite matrices.
+ *
+ * ERRORS
+ *   Argument checks run on the host before anything is enqueued and return
+ *   BPS_EINVAL (bad sizes, NULL or misaligned pointers, unknown dtype/flags,
+ *   a parent index not in [0, i)) or BPS_ENOTSUP (valid but not supported
+ *   combination).  A failed HIP launch returns BPS_EHIP.  bps_last_error()
+ *   gives a message for the calling thread's last failure.  Numerical
+ *   breakdown is only known on the device: when an `info` array (device,
+ *   int32[batch]) is given, info[s] = 0, or 1 + the first row whose pivot is
+ *   zero or not finite (LAPACK style); the solution of that system is then
+ *   meaningless, the others are unaffected.
+ *
+ * OWNERSHIP
+ *   The caller owns every device buffer.  Inputs are never modified; only
+ *   the arrays documented as outputs (x / rhs / C, factors, work, info) are
+ *   written.  The library allocates device memory only inside
+ *   hines_plan_create and frees it in hines_plan_destroy.  Calls on different
+ *   streams with different output buffers are independent.
+ */
+#ifndef BPS_H
+#define BPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define BPS_API __attribute__((visibility("default")))
+#else
+#define BPS_API
+#endif
+
+typedef enum bps_status {
+    BPS_OK = 0,
+    BPS_EINVAL = 1,   /* invalid argument                       */
+    BPS_ENOTSUP = 2,  /* valid but unsupported combination      */
+    BPS_EHIP = 3,     /* a HIP runtime call or launch failed    */
+    BPS_ENOMEM = 4    /* device allocation failed (plans only)  */
+} bps_status;
+
+typedef enum bps_dtype { BPS_F32 = 1, BPS_F64 = 2 } bps_dtype;
+
+/* Matrix flags for bps_penta_desc.flags */
+#define BPS_CYCLIC      0x1u  /* periodic: column indices wrap modulo n ([P], periodic matrix)  */
+#define BPS_SHARED_COEF 0x2u  /* one set of diagonals (n values each) used by every system     */
+
+/* Text for a status code (static storage). */
+BPS_API const char *bps_status_str(int status);
+/* Message describing the calling thread's most recent failure ("" if none). */
+BPS_API const char *bps_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+BPS_API int bps_version(void);
+
+/* ======================================================================== */
+/* Pentadiagonal systems  [P] "Pentadiagonal solver"                        */
+/* ======================================================================== */
+
+/* Describes a batch of pentadiagonal systems A_s x_s = f_s.
+ * Diagonals (the [P] naming): a_i = A[i][i-2], b_i = A[i][i-1], c_i = A[i][i],
+ * d_i = A[i][i+1], e_i = A[i][i+2].
+ *  - default: each system has its own diagonals, interleaved [n][ld];
+ *    the entries that fall outside the matrix (a_0, a_1, b_0, d_{n-1},
+ *    e_{n-2}, e_{n-1}) are never read.  n >= 4.
+ *  - BPS_CYCLIC: periodic matrix, column index (i+k) mod n, so every entry
+ *    is used; solved by the reduction of [P] (the last two unknowns coupled
+ *    through a 2x2 block, eqs. (10)-(12)) in an equivalent fused order.
+ *    n >= 6.
+ *  - BPS_SHARED_COEF: a..e are single vectors of n values shared by all
+ *    systems (the "Constant" use of [P]: factor once, solve many).
+ * ld: leading dimension (elements) of the interleaved x / f / per-system
+ * diagonal arrays, ld >= batch. */
+typedef struct bps_penta_desc {
+    int32_t dtype;    /* BPS_F32 or BPS_F64 */
+    uint32_t flags;   /* 0 or an OR of BPS_CYCLIC, BPS_SHARED_COEF */
+    int64_t n;        /* rows per system */
+    int64_t batch;    /* number of systems */
+    int64_t ld;       /* leading dimension of interleaved arrays, >= batch */
+} bps_penta_desc;
+
+/* Bytes of the `factors` buffer that penta_factor_batch fills for `desc`
+ * (0 if desc is invalid).  Its content is private to this library. */
+BPS_API size_t bps_penta_factor_bytes(const bps_penta_desc *desc);
+
+/* Factor every system ([P] factorisation steps 1-14; for BPS_CYCLIC also the
+ * quantities of the periodic reduction that [P] says are computed once and
+ * stored: the Schur 2x2 inverse and the coupling vectors).
+ * a..e: device, per the desc layout.  factors: device, bps_penta_factor_bytes.
+ * info: device int32[batch] (int32[1] with BPS_SHARED_COEF) or NULL.
+ * Alignment: 8 bytes (F64) / 4 bytes (F32) for every array. */
+BPS_API bps_status penta_factor_batch(const bps_penta_desc *desc,
+                              const void *a, const void *b, const void *c,
+                              const void *d, const void *e,
+                              void *factors, int32_t *info, void *stream);
+
+/* Solve with stored factors of a NON-periodic batch ([P] forward steps for g,
+ * then back substitution).  x: device interleaved [n][ld]; holds f on entry
+ * and the solution on return.  desc must equal the one used to factor. */
+BPS_API bps_status penta_solve_batch(const bps_penta_desc *desc, const void *factors,
+                             void *x, void *stream);
+
+/* Solve with stored factors of a PERIODIC batch (desc has BPS_CYCLIC).
+ * Same conventions as penta_solve_batch. */
+BPS_API bps_status penta_cyclic_solve_batch(const bps_penta_desc *desc, const void *factors,
+                                    void *x, void *stream);
+
+/* Bytes of the `work` buffer penta_factor_solve_batch needs (0 if invalid). */
+BPS_API size_t bps_penta_work_bytes(const bps_penta_desc *desc);
+
+/* Factor and solve in one pass over the data (the "Rewrite" use of [P]:
+ * a new matrix every call), non-periodic, per-system diagonals only
+ * (flags must be 0).  x: f on entry, solution on return.  work: device,
+ * bps_penta_work_bytes(desc) bytes, overwritten.  info: as above or NULL. */
+BPS_API bps_status penta_factor_solve_batch(const bps_penta_desc *desc,
+                                    const void *a, const void *b, const void *c,
+                                    const void *d, const void *e,
+                                    void *x, void *work, int32_t *info, void *stream);
+
+/* ======================================================================== */
+/* Periodic hyperdiffusion  [P] hyperdiffusion section                      */
+/* ======================================================================== */
+
+/* Bytes of `work` for hyperdiffusion_step (shared factors; 0 if invalid). */
+BPS_API size_t hyperdiffusion_work_bytes(int dtype, int64_t n, int64_t batch);
+
+/* Advance `batch` periodic 1-D fields by `nsteps` implicit steps
+ *     (I + sigma*D4) C^{k+1} = C^k,   sigma = dt / dx^4,
+ * with D4 the centred fourth difference [1, -4, 6, -4, 1] wrapping modulo n
+ * (periodic domain of length n*dx, eq. (4) with gamma = D = 1).
+ * diagonals: NULL for the operator above, or a device array of 5*n values
+ *   [a | b | c | d | e] (each n long) giving any periodic pentadiagonal
+ *   matrix shared by all systems (the "constant" use of [P]).
+ * C: device, interleaved [n][ld]; C^0 on entry, C^{nsteps} on return.
+ * work: device, hyperdiffusion_work_bytes(dtype, n, batch) bytes.
+ * The matrix is factored once per call and reused for all nsteps steps.
+ * n >= 6, batch >= 1, ld >= batch, nsteps >= 0, dt and dx finite, dx != 0. */
+BPS_API bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld,
+                               double dt, double dx, const void *diagonals,
+                               void *C, int64_t nsteps, void *work, void *stream);
+
+/* ======================================================================== */
+/* Hines tree-tridiagonal systems  [H] sections 2-4                         */
+/* ======================================================================== */
+
+/* Matrix of one neuron with n compartments ([H] section 2):
+ *   A[i][i] = d_i,  A[p_i][i] = u_i ("upper"),  A[i][p_i] = l_i ("lower"),
+ * parent p_i in [0, i) for i >= 1 (each parent numbered before its child);
+ * p_0 and u_0, l_0 are not read.  Solved by Algorithm 1 of [H] (leaves-to-
+ * root elimination, then root-to-leaves substitution). */
+typedef struct bps_hines_plan bps_hines_plan;
+
+/* Build a plan (host work + device upload; synchronises).
+ * mono != 0 (one morphology for all neurons, [H] section 3):
+ *   sizes: host int32[1] = {n}; parent: host int32[n];
+ *   solver layout: Full-Interleaved [n][ld], ld >= batch (ld = 0 means batch).
+ * mono == 0 (one morphology per neuron, [H] section 4):
+ *   sizes: host int32[batch] compartments per neuron (>= 1);
+ *   parent: host int32[sum(sizes)], each neuron's parents (local indices)
+ *   one neuron after another.  The plan sorts neurons by size and packs
+ *   them 64 per block (one wavefront), each block interleaved with its own
+ *   row count (the Block-Interleaved layout of [H] with BS = 64); ld is
+ *   ignored.  Use hines_pack / hines_unpack to convert data.
+ * Fails with BPS_EINVAL if any p_i is outside [0, i). */
+BPS_API bps_status hines_plan_create(bps_hines_plan **plan, int64_t batch, const int32_t *sizes,
+                             const int32_t *parent, int mono, int64_t ld);
+BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
+
+/* Elements of one value array (u, l, d or rhs) in the plan's solver layout. */
+BPS_API int64_t hines_plan_elems(const bps_hines_plan *plan);
+/* Real compartments (sum of sizes, or n*batch for mono). */
+BPS_API int64_t hines_plan_unknowns(const bps_hines_plan *plan);
+
+/* Layout transforms ([H] section 3: done once, off the time-stepping loop).
+ * flat: device, the neurons' values one neuron after another (sum(sizes)
+ * values; n*batch for mono, neuron-major).  packed: device,
+ * hines_plan_elems values in the solver layout.  Padding entries of the
+ * packed layout are written as 0 by hines_pack and never read by solves. */
+BPS_API bps_status hines_pack(const bps_hines_plan *plan, int dtype, const void *flat,
+                      void *packed, void *stream);
+BPS_API bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const void *packed,
+                        void *flat, void *stream);
+
+/* Bytes of `work` hines_solve_batch needs for this plan. */
+BPS_API size_t hines_work_bytes(const bps_hines_plan *plan, int dtype);
+
+/* Solve every neuron ([H] Algorithm 1), one lane per neuron.
+ * u, l, d: device, solver layout, not modified.  rhs: device, solver layout,
+ * right-hand side on entry, voltages V on return (as in [H]).  work: device,
+ * hines_work_bytes bytes.  info: device int32[batch] indexed by the ORIGINAL
+ * neuron number, or NULL; a nonzero value is 1 + the first compartment, in
+ * elimination order (n-1 down to 1, then the root 0), whose pivot is zero or
+ * not finite.  dtype must be BPS_F64. */
+BPS_API bps_status hines_solve_batch(const bps_hines_plan *plan, int dtype,
+                             const void *u, const void *l, const void *d,
+                             void *rhs, void *work, int32_t *info, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPS_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, answers size queries, and rejects invalid arguments on the
+host (BPS_EINVAL / BPS_ENOTSUP) before anything is enqueued.  No call here
+reaches a kernel launch: every case fails validation first."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import banded_pde_solvers_amd as bps
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bps.h")
+
+EINVAL, ENOTSUP = 1, 2
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"(?m)^BPS_API\s+[\w\s\*]*?\b(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bps.library_path()):
+        pytest.fail("libbps.so is not built (run __graft_entry__.build())")
+    return bps.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for required in ("penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
+                     "penta_factor_solve_batch", "hines_solve_batch", "hyperdiffusion_step",
+                     "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", bps.library_path()], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings_and_version(lib):
+    assert lib.bps_status_str(0) == b"BPS_OK"
+    assert b"invalid" in lib.bps_status_str(EINVAL)
+    assert bps.version() >= 100
+
+
+def test_size_queries(lib):
+    F64, F32 = bps.BPS_F64, bps.BPS_F32
+    assert bps.bps_penta_factor_bytes(512, 100, 128, F64) == 5 * 512 * 128 * 8
+    assert bps.bps_penta_factor_bytes(512, 100, 100, F32, bps.BPS_SHARED_COEF) == 5 * 512 * 4
+    assert bps.bps_penta_factor_bytes(10, 3, 3, F64, bps.BPS_CYCLIC) == (9 * 8 + 4) * 3 * 8
+    assert bps.bps_penta_factor_bytes(3, 1, 1, F64) == 0          # n < 4
+    assert bps.bps_penta_factor_bytes(5, 1, 1, F64, bps.BPS_CYCLIC) == 0   # periodic needs n >= 6
+    assert bps.bps_penta_work_bytes(512, 10, 16, F64) == 2 * 512 * 16 * 8
+    assert bps.hyperdiffusion_work_bytes(1024, 16384, F64) == (5 * 1024 + 9 * 1022 + 4) * 8
+    assert bps.hyperdiffusion_work_bytes(5, 1, F64) == 0
+
+
+def _desc(dtype=2, flags=0, n=8, batch=4, ld=4):
+    return ctypes.byref(bps.PentaDesc(dtype, flags, n, batch, ld))
+
+
+def _fake(k=0):
+    # an aligned non-NULL address; validation rejects these calls before use
+    return ctypes.c_void_p(4096 + 64 * k)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=3), EINVAL), (dict(batch=0), EINVAL), (dict(ld=3, batch=4), EINVAL),
+    (dict(dtype=7), EINVAL), (dict(flags=0x10), EINVAL), (dict(flags=1, n=5), EINVAL),
+])
+def test_penta_factor_rejects_bad_desc(lib, kw, code):
+    st = lib.penta_factor_batch(_desc(**kw), *(_fake(i) for i in range(6)), None, None)
+    assert st == code
+    assert lib.bps_last_error()
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    args = [_fake(i) for i in range(6)]
+    args[2] = None
+    assert lib.penta_factor_batch(_desc(), *args, None, None) == EINVAL
+    assert b"c is NULL" in lib.bps_last_error()
+    args[2] = ctypes.c_void_p(4096 + 4)     # not 8-byte aligned for F64
+    assert lib.penta_factor_batch(_desc(), *args, None, None) == EINVAL
+    assert b"aligned" in lib.bps_last_error()
+    assert lib.penta_solve_batch(_desc(), None, _fake(), None) == EINVAL
+    assert lib.penta_solve_batch(None, _fake(), _fake(), None) == EINVAL
+
+
+def test_solve_kind_mismatch_rejected(lib):
+    assert lib.penta_solve_batch(_desc(flags=1), _fake(), _fake(1), None) == EINVAL
+    assert lib.penta_cyclic_solve_batch(_desc(flags=0), _fake(), _fake(1), None) == EINVAL
+    assert lib.penta_factor_solve_batch(_desc(flags=1), *(_fake(i) for i in range(8)), None,
+                                        None) == ENOTSUP
+
+
+def test_hyperdiffusion_rejects_bad_arguments(lib):
+    f = lib.hyperdiffusion_step
+    assert f(2, 5, 4, 4, 1e-6, 0.1, None, _fake(), 1, _fake(1), None) == EINVAL   # n < 6
+    assert f(2, 16, 4, 4, 1e-6, 0.0, None, _fake(), 1, _fake(1), None) == EINVAL  # dx = 0
+    assert f(2, 16, 4, 4, float("nan"), 0.1, None, _fake(), 1, _fake(1), None) == EINVAL
+    assert f(2, 16, 4, 4, 1e-6, 0.1, None, _fake(), -1, _fake(1), None) == EINVAL
+    assert f(2, 16, 4, 3, 1e-6, 0.1, None, _fake(), 1, _fake(1), None) == EINVAL  # ld < batch
+    assert f(2, 16, 4, 4, 1e-6, 0.1, None, None, 1, _fake(1), None) == EINVAL
+
+
+def test_hines_plan_rejects_bad_parents_before_allocating(lib):
+    with pytest.raises(bps.BpsError) as ei:
+        bps.hines_plan_create(10, [4], [-1, 0, 2, 1], mono=True)      # parent[2] = 2
+    assert ei.value.status == EINVAL
+    with pytest.raises(bps.BpsError):
+        bps.hines_plan_create(2, [3, 2], [-1, 0, 0, -1, 1], mono=False)  # neuron 1: parent[1]=1
+    with pytest.raises(bps.BpsError):
+        bps.hines_plan_create(4, [0], [0], mono=True)                  # n < 1
+    with pytest.raises(bps.BpsError):
+        bps.hines_plan_create(4, [3], [-1, 0, 1], mono=True, ld=2)     # ld < batch
+
+
+def test_hines_solve_rejects_null_plan_and_dtype(lib):
+    assert lib.hines_solve_batch(None, 2, *(_fake(i) for i in range(5)), None, None) == EINVAL
+    assert lib.hines_work_bytes(None, 2) == 0

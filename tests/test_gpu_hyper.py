@@ -1,0 +1,132 @@
+"""GPU parity: periodic hyperdiffusion stepping against the oracle.
+
+Parity is per solve on identical inputs (one step from the same state,
+relative error <= 1e-10 per system); multi-step trajectories are checked
+against the oracle's trajectory with a tolerance that allows the per-step
+rounding to accumulate over the steps (the matrix has condition number
+~1.8e7 at n = 1024, sigma = dt/dx^4 ~ 1.1e6): absolute, scaled by the initial
+amplitude, where high modes decay to roundoff."""
+import numpy as np
+import pytest
+import torch
+
+import banded_pde_solvers_amd as bps
+import oracle
+import workloads as W
+from gpu_util import buf, dev, host, relerr_cols
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(C0, dt, dx, nsteps, dtype=torch.float64, diagonals=None):
+    n, batch = C0.shape
+    C = dev(C0, dtype)
+    code = bps.BPS_F64 if dtype == torch.float64 else bps.BPS_F32
+    work = buf(bps.hyperdiffusion_work_bytes(n, batch, code))
+    dg = None if diagonals is None else dev(np.concatenate(diagonals), dtype)
+    bps.hyperdiffusion_step(C, dt, dx, nsteps, work, dg)
+    return host(C)
+
+
+def _oracle(C0, dt, dx, nsteps, diagonals=None):
+    return W.to_interleaved(oracle.hyperdiffusion(W.to_flat(C0), dt, dx, nsteps, diagonals))
+
+
+def _traj_err(out, ref, C0):
+    """Per-system trajectory error relative to the initial state's norm.
+
+    Rounding differences of one solve (<= ~6e-11 relative at sigma ~ 1.1e6,
+    where the 2x2 corner block comes from a ~7e4-fold cancellation) persist in
+    the constant mode, which never decays, while the state itself shrinks
+    ~30-fold; so the accumulated difference is measured against |C^0|."""
+    return float(np.max(np.linalg.norm(out - ref, axis=0) / np.linalg.norm(C0, axis=0)))
+
+
+def test_workload0_modes_full():
+    """N = 256, 64 systems, 10 steps: the complete workload."""
+    cfg = W.WORKLOADS[0]
+    ic = W.hyperdiffusion_modes(cfg["n"], cfg["batch"])
+    out = _step(ic.C0, cfg["dt"], cfg["dx"], cfg["nsteps"])
+    ref = _oracle(ic.C0, cfg["dt"], cfg["dx"], cfg["nsteps"])
+    # trajectory: two correct orderings drift apart by ~1e-12 per step at
+    # kappa ~ 7e4; strongly damped systems make a per-system relative
+    # measure meaningless, so the bound is absolute, scaled by max|C^0|
+    assert np.max(np.abs(out - ref)) <= 1e-10 * np.max(np.abs(ic.C0))
+    # one step from the same state: per-solve parity
+    one = _step(ic.C0, cfg["dt"], cfg["dx"], 1)
+    assert relerr_cols(one, _oracle(ic.C0, cfg["dt"], cfg["dx"], 1)) <= 1e-10
+
+
+@pytest.mark.parametrize("n,batch", [(6, 1), (7, 65), (64, 130), (1024, 200)])
+def test_one_step_parity(n, batch):
+    dt, dx = 1e-6, 1.0 / n
+    C0 = np.random.default_rng(n + batch).uniform(-1, 1, (n, batch))
+    assert relerr_cols(_step(C0, dt, dx, 1), _oracle(C0, dt, dx, 1)) <= 1e-10
+
+
+def test_workload1_trajectory_reduced_batch():
+    """N = 1024, sigma ~ 1.1e6, 100 steps on 300 systems."""
+    cfg = W.WORKLOADS[1]
+    C0 = W.hyperdiffusion_random(cfg["n"], 300, rng=np.random.default_rng(11))
+    out = _step(C0, cfg["dt"], cfg["dx"], cfg["nsteps"])
+    ref = _oracle(C0, cfg["dt"], cfg["dx"], cfg["nsteps"])
+    assert _traj_err(out, ref, C0) <= 2e-9
+
+
+def test_steps_compose_bitwise_and_zero_steps():
+    n, batch, dt = 96, 70, 1e-6
+    C0 = np.random.default_rng(3).uniform(-1, 1, (n, batch))
+    a = _step(C0, dt, 1.0 / n, 10)
+    b = _step(_step(C0, dt, 1.0 / n, 4), dt, 1.0 / n, 6)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(_step(C0, dt, 1.0 / n, 0), C0)
+
+
+def test_explicit_diagonals_and_fp32():
+    n, batch, dt = 64, 100, 1e-7
+    dx = 1.0 / n
+    C0 = np.random.default_rng(4).uniform(-1, 1, (n, batch))
+    dg = oracle.hyperdiffusion_diagonals(n, dt, dx)
+    out = _step(C0, dt, dx, 3, diagonals=dg)
+    assert relerr_cols(out, _oracle(C0, dt, dx, 3, dg)) <= 1e-10
+    # a non-symmetric periodic matrix shared by all systems
+    rng = np.random.default_rng(5)
+    cy = W.penta_dominant(n, 1, cyclic=True, rng=rng)
+    dg2 = [v[:, 0].copy() for v in cy.diagonals]
+    out2 = _step(C0, dt, dx, 2, diagonals=dg2)
+    assert relerr_cols(out2, _oracle(C0, dt, dx, 2, dg2)) <= 1e-10
+    out32 = _step(C0, dt, dx, 3, dtype=torch.float32)
+    C0r = C0.astype(np.float32).astype(np.float64)
+    # fp32 arithmetic against the fp64 oracle of the fp32-rounded state; sigma ~ 1.7
+    assert relerr_cols(out32, _oracle(C0r, dt, dx, 3)) <= 1e-4
+
+
+def test_mean_and_mode_decay_on_gpu():
+    n, batch, dt = 256, 64, 1e-6
+    x = np.arange(n) / n
+    k = np.arange(1, batch + 1) % 17 + 1
+    C0 = np.cos(2 * np.pi * x[:, None] * k[None, :]) + 0.25
+    out = _step(C0, dt, 1.0 / n, 5)
+    ref = _oracle(C0, dt, 1.0 / n, 5)
+    assert np.max(np.abs(out - ref)) <= 1e-10 * np.max(np.abs(C0))
+    # the constant mode is divided by lambda_0 = a + b + c + d + e per step
+    a, b, c, d, e = oracle.hyperdiffusion_diagonals(n, dt, 1.0 / n)
+    L = np.longdouble
+    lam0 = float(L(a[0]) + L(b[0]) + L(c[0]) + L(d[0]) + L(e[0]))
+    np.testing.assert_allclose(out.sum(axis=0), C0.sum(axis=0) / lam0 ** 5, rtol=1e-11)
+
+
+@pytest.mark.slow
+def test_workload1_full_sampled():
+    """N = 1024, 16384 systems, 100 steps in one call, as benchmarked;
+    sampled systems against the oracle's trajectory, plus a per-solve check."""
+    cfg = W.WORKLOADS[1]
+    n, batch = cfg["n"], cfg["batch"]
+    print(f"full cyclic workload {n}x{batch}", flush=True)
+    C0 = W.hyperdiffusion_random(n, batch)
+    out = _step(C0, cfg["dt"], cfg["dx"], cfg["nsteps"])
+    cols = np.unique(np.r_[0, 63, 64, batch - 1, np.random.default_rng(2).integers(0, batch, 60)])
+    ref = _oracle(C0[:, cols], cfg["dt"], cfg["dx"], cfg["nsteps"])
+    assert _traj_err(out[:, cols], ref, C0[:, cols]) <= 2e-9
+    one = _step(C0, cfg["dt"], cfg["dx"], 1)
+    assert relerr_cols(one[:, cols], _oracle(C0[:, cols], cfg["dt"], cfg["dx"], 1)) <= 1e-10
