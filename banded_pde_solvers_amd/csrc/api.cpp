@@ -174,7 +174,9 @@ bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, co
 size_t hyperdiffusion_work_bytes(int dtype, int64_t n, int64_t batch)
 {
     if (dtype_size(dtype) == 0 || n < 6 || n > kMaxDim || batch < 1) return 0;
-    return size_t(5 * n + penta_factor_elems(n, 1, true)) * dtype_size(dtype);
+    const size_t stream = size_t(5 * n + penta_factor_elems(n, 1, true)) * dtype_size(dtype);
+    const size_t res = 5 * n * dtype_size(dtype) + resident_coef_bytes(n);
+    return stream > res ? stream : res;
 }
 
 bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
@@ -194,14 +196,23 @@ bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, 
     const size_t es = dtype_size(dtype);
     char *w = static_cast<char *>(work);
     const void *dg = diagonals;
+    const bool resident = !diagonals && dtype == BPS_F64 && resident_chunk(n) != 0;
     if (!dg) {
         const double sigma = dt / (dx * dx * dx * dx);
         if (!std::isfinite(sigma)) BPS_FAIL(BPS_EINVAL, "sigma = dt/dx^4 is not finite");
-        CHECK(dtype == BPS_F64 ? launch_hyper_diagonals<double>(n, sigma, w, st)
-                               : launch_hyper_diagonals<float>(n, sigma, w, st));
+        if (!resident)
+            CHECK(dtype == BPS_F64 ? launch_hyper_diagonals<double>(n, sigma, w, st)
+                                   : launch_hyper_diagonals<float>(n, sigma, w, st));
         dg = w;
     }
     void *fac = w + 5 * n * es;
+    if (resident) {
+        // the operator I + sigma*D4 with constant diagonals: every chunk of a
+        // system sees the same interior block, so the register-resident
+        // multi-step kernel applies (the diagonals built above are unused)
+        const double sigma = dt / (dx * dx * dx * dx);
+        return launch_hyper_resident(n, batch, ld, nsteps, sigma, fac, C, st);
+    }
     const char *D = static_cast<const char *>(dg);
     if (dtype == BPS_F64) {
         CHECK(launch_penta_factor<double>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,

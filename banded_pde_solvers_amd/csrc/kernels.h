@@ -24,6 +24,14 @@ bps_status launch_penta_fused(int64_t n, int64_t batch, int64_t ld, const void *
 template <typename T>
 bps_status launch_hyper_diagonals(int64_t n, double sigma, void *diag, hipStream_t st);
 
+// Register-resident multi-step solve of I + sigma*D4 (fp64): set-up kernel
+// plus the step kernel.  resident_chunk(n) is the chunk length, 0 when the
+// resident path does not apply to n.
+int resident_chunk(int64_t n);
+size_t resident_coef_bytes(int64_t n);
+bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t nsteps, double sigma,
+                                 void *coef, void *C, hipStream_t st);
+
 // Number of values of a factor buffer.
 inline int64_t penta_factor_elems(int64_t n, int64_t ldf, bool cyclic) {
     return cyclic ? (9 * (n - 2) + 4) * ldf : 5 * n * ldf;

@@ -57,7 +57,8 @@ def test_workload0_modes_full():
     assert relerr_cols(one, _oracle(ic.C0, cfg["dt"], cfg["dx"], 1)) <= 1e-10
 
 
-@pytest.mark.parametrize("n,batch", [(6, 1), (7, 65), (64, 130), (1024, 200)])
+@pytest.mark.parametrize("n,batch", [(6, 1), (7, 65), (64, 130), (128, 37), (192, 50), (256, 17),
+                                     (1024, 200)])
 def test_one_step_parity(n, batch):
     dt, dx = 1e-6, 1.0 / n
     C0 = np.random.default_rng(n + batch).uniform(-1, 1, (n, batch))
@@ -73,13 +74,27 @@ def test_workload1_trajectory_reduced_batch():
     assert _traj_err(out, ref, C0) <= 2e-9
 
 
+@pytest.mark.parametrize("n,batch", [(128, 33), (1024, 70)])
+def test_resident_and_streaming_paths_agree(n, batch):
+    """The built-in operator (register-resident chunked kernel) against the
+    same matrix given explicitly (one lane per system, streaming kernel)."""
+    dt, dx = 1e-6, 1.0 / n
+    C0 = np.random.default_rng(n).uniform(-1, 1, (n, batch))
+    dg = oracle.hyperdiffusion_diagonals(n, dt, dx)
+    for steps in (1, 7):
+        a = _step(C0, dt, dx, steps)
+        b = _step(C0, dt, dx, steps, diagonals=dg)
+        assert _traj_err(a, b, C0) <= 1e-10 * steps
+
+
 def test_steps_compose_bitwise_and_zero_steps():
-    n, batch, dt = 96, 70, 1e-6
-    C0 = np.random.default_rng(3).uniform(-1, 1, (n, batch))
-    a = _step(C0, dt, 1.0 / n, 10)
-    b = _step(_step(C0, dt, 1.0 / n, 4), dt, 1.0 / n, 6)
-    np.testing.assert_array_equal(a, b)
-    np.testing.assert_array_equal(_step(C0, dt, 1.0 / n, 0), C0)
+    for n, batch in ((96, 70), (512, 40)):     # streaming and resident kernels
+        dt = 1e-6
+        C0 = np.random.default_rng(3).uniform(-1, 1, (n, batch))
+        a = _step(C0, dt, 1.0 / n, 10)
+        b = _step(_step(C0, dt, 1.0 / n, 4), dt, 1.0 / n, 6)
+        np.testing.assert_array_equal(a, b)
+        np.testing.assert_array_equal(_step(C0, dt, 1.0 / n, 0), C0)
 
 
 def test_explicit_diagonals_and_fp32():
