@@ -196,7 +196,8 @@ bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, 
     const size_t es = dtype_size(dtype);
     char *w = static_cast<char *>(work);
     const void *dg = diagonals;
-    const bool resident = !diagonals && dtype == BPS_F64 && resident_chunk(n) != 0;
+    const bool resident = !diagonals && dtype == BPS_F64 && resident_chunk(n) != 0 &&
+                          dt / (dx * dx * dx * dx) >= 0.0;
     if (!dg) {
         const double sigma = dt / (dx * dx * dx * dx);
         if (!std::isfinite(sigma)) BPS_FAIL(BPS_EINVAL, "sigma = dt/dx^4 is not finite");

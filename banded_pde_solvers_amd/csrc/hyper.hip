@@ -96,17 +96,24 @@ constexpr int kResMaxP = 16;    // chunks per system supported by the resident k
 //   T blocks:   T_q (2x2, row-major) for q < P                   (4P doubles)
 __host__ __device__ constexpr int res_coef_elems(int M, int P) { return 8 * (M - 2) + 8 + 4 * P; }
 
-template <int M>
-__global__ void __launch_bounds__(64) k_hyper_resident_setup(int P, double sigma, double *__restrict__ coef)
+// 64-bit value of lane `lane` (uniform) of the wavefront
+__device__ __forceinline__ double read_lane(double v, int lane)
+{
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(int(b & 0xffffffffll), lane);
+    const int hi = __builtin_amdgcn_readlane(int(b >> 32), lane);
+    return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+
+template <int M, int P>
+__global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, double *__restrict__ coef)
 {
 #pragma clang fp contract(off)
-    constexpr int m = M - 2;
+    constexpr int m = M - 2, n2 = 2 * P, w = 4 * P;
     __shared__ double ra[m], be[m], ga[m], de[m];
     __shared__ double vec[8][m];        // UL0, UL1, w0, w1, ZL0, ZL1, ZR0, ZR1
     __shared__ double res[4][m];
-    __shared__ double aug[2 * kResMaxP][4 * kResMaxP];
-    __shared__ double piv[2 * kResMaxP];
-    __shared__ int pivrow;
+    __shared__ double aug[n2][w];
     const int t = threadIdx.x;
     const double a = sigma, b = -4.0 * sigma, c = 1.0 + 6.0 * sigma, d = -4.0 * sigma, e = sigma;
     auto Ea = [&](int i) { return i >= 2 ? a : 0.0; };
@@ -130,35 +137,32 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(int P, double sigma
         }
     }
     __syncthreads();
+    // triangular solves with the running values carried in registers
     auto Lsolve = [&](double *v) {           // v <- L^{-1} v
+        double p1 = 0.0, p2 = 0.0;
         for (int i = 0; i < m; ++i) {
-            double g = v[i];
-            if (i >= 2) g -= Ea(i) * v[i - 2];
-            if (i >= 1) g -= be[i] * v[i - 1];
-            v[i] = g * ra[i];
+            const double g = (v[i] - Ea(i) * p2 - be[i] * p1) * ra[i];
+            v[i] = g; p2 = p1; p1 = g;
         }
     };
     auto Rsolve = [&](double *v) {           // v <- R^{-1} v
+        double q1 = 0.0, q2 = 0.0;
         for (int i = m - 1; i >= 0; --i) {
-            double x = v[i];
-            if (i + 1 < m) x -= ga[i] * v[i + 1];
-            if (i + 2 < m) x -= de[i] * v[i + 2];
-            v[i] = x;
+            const double x = v[i] - ga[i] * q1 - de[i] * q2;
+            v[i] = x; q2 = q1; q1 = x;
         }
     };
     // ---- coupling vectors (eight independent lanes) ----
     if (t < 8) {
         double *v = vec[t];
-        for (int i = 0; i < m; ++i) {
-            const int k = t & 1;
+        const int k = t & 1;
+        for (int i = 0; i < m; ++i)
             v[i] = (t < 2 || (t >= 4 && t < 6)) ? CL(k, i) : (t >= 6) ? CR(k, i) : (i == k ? 1.0 : 0.0);
-        }
         if (t == 2 || t == 3) {              // w_k = R^{-T} e_k
+            double q1 = 0.0, q2 = 0.0;
             for (int i = 0; i < m; ++i) {
-                double y = v[i];
-                if (i >= 1) y -= ga[i - 1] * v[i - 1];
-                if (i >= 2) y -= de[i - 2] * v[i - 2];
-                v[i] = y;
+                const double y = v[i] - (i >= 1 ? ga[i - 1] : 0.0) * q1 - (i >= 2 ? de[i - 2] : 0.0) * q2;
+                v[i] = y; q2 = q1; q1 = y;
             }
         } else {
             Lsolve(v);                       // U = L^{-1} C
@@ -189,7 +193,6 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(int P, double sigma
     // ---- Schur complement S (2P x 2P), compensated, into aug = [S | I] ----
     auto ZL = [&](int q) -> const double * { return q ? vec[5] : vec[4]; };
     auto ZR = [&](int q) -> const double * { return q ? vec[7] : vec[6]; };
-    const int n2 = 2 * P, w = 4 * P;
     for (int idx = t; idx < n2 * n2; idx += blockDim.x) {
         const int row = idx / n2, col = idx % n2;
         const int J = row >> 1, r = row & 1, K = col >> 1, q = col & 1;
@@ -213,26 +216,20 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(int P, double sigma
         aug[row][n2 + col] = (row == col) ? 1.0 : 0.0;
     }
     __syncthreads();
-    // ---- Gauss-Jordan with partial pivoting; lane t owns column t of aug ----
+    // ---- Gauss-Jordan on [S | I] without pivoting (S is symmetric positive
+    // definite: a Schur complement of I + sigma*D4, sigma >= 0).  Lane t holds
+    // column t in registers; pivot column entries are broadcast by readlane.
+    double cv[n2];
+#pragma unroll
+    for (int i = 0; i < n2; ++i) cv[i] = (t < w) ? aug[i][t] : 0.0;
+#pragma unroll
     for (int k = 0; k < n2; ++k) {
-        if (t == 0) {
-            int p = k;
-            for (int i = k + 1; i < n2; ++i)
-                if (fabs(aug[i][k]) > fabs(aug[p][k])) p = i;
-            pivrow = p;
-        }
-        __syncthreads();
-        const int p = pivrow;
-        if (t < w && p != k) { const double tmp = aug[k][t]; aug[k][t] = aug[p][t]; aug[p][t] = tmp; }
-        __syncthreads();
-        if (t < n2) piv[t] = aug[t][k];
-        __syncthreads();
-        if (t < w) {
-            const double pk = aug[k][t] / piv[k];
-            for (int i = 0; i < n2; ++i)
-                aug[i][t] = (i == k) ? pk : aug[i][t] - piv[i] * pk;
-        }
-        __syncthreads();
+        double f[n2];
+#pragma unroll
+        for (int i = 0; i < n2; ++i) f[i] = read_lane(cv[i], k);
+        const double pk = cv[k] / f[k];
+#pragma unroll
+        for (int i = 0; i < n2; ++i) cv[i] = (i == k) ? pk : cv[i] - f[i] * pk;
     }
     // ---- outputs ----
     for (int idx = t; idx < m; idx += blockDim.x) {
@@ -248,50 +245,62 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(int P, double sigma
         const double URc = e * ra[m - 1];
         h[5] = URa; h[6] = URb; h[7] = URc;
     }
-    for (int idx = t; idx < 4 * P; idx += blockDim.x) {
-        const int q = idx >> 2, rr = (idx >> 1) & 1, cc = idx & 1;
-        coef[8 * m + 8 + idx] = aug[rr][n2 + 2 * q + cc];
+    // T_q = rows 0, 1 of S^{-1}, columns 2q, 2q+1 (held by lanes n2 + 2q + c)
+    if (t >= n2 && t < w) {
+        const int q = (t - n2) >> 1, cc = (t - n2) & 1;
+        coef[8 * m + 8 + 4 * q + cc] = cv[0];
+        coef[8 * m + 8 + 4 * q + 2 + cc] = cv[1];
     }
 }
 
-template <int M>
-__global__ void __launch_bounds__(kResSys * kResMaxP)
-k_hyper_resident(int P, int64_t batch, int64_t ld, int64_t nsteps,
-                 const double *__restrict__ coef, double *__restrict__ C)
+template <int M, int P>
+__global__ void __launch_bounds__(kResSys * P) __attribute__((amdgpu_waves_per_eu(2)))
+k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__restrict__ coef,
+                 double *__restrict__ C)
 {
     constexpr int m = M - 2;
     constexpr int S = kResSys;
-    __shared__ double tbuf[2][kResMaxP][S][4];
-    __shared__ double rbuf[2][kResMaxP][S][2];
+    __shared__ double tbuf[2][P][S][4];
+    __shared__ double rbuf[2][P][S][2];
+    __shared__ double Tl[P][4];       // first block row of S^{-1}
     const int tid = threadIdx.x;
+    if (tid < 4 * P) Tl[tid >> 2][tid & 3] = coef[8 * m + 8 + tid];
     const int j = tid / S, sl = tid % S;
     const int64_t s = int64_t(blockIdx.x) * S + sl;
     const bool act = s < batch;
-    double *col = C + s + int64_t(j) * M * ld;
+    // lanes past the end of the batch compute on a copy of the last system
+    // and store nothing
+    double *col = C + (act ? s : batch - 1) + int64_t(j) * M * ld;
     const double *H = coef + 8 * m;
     const double a = H[0], b = H[1], d = H[3], e = H[4];
     const double URa = H[5], URb = H[6], URc = H[7];
 
     double x[M];
 #pragma unroll
-    for (int i = 0; i < M; ++i) x[i] = act ? col[int64_t(i) * ld] : 0.0;
+    for (int i = 0; i < M; ++i) x[i] = col[int64_t(i) * ld];
 
     const int jn = (j + 1 == P) ? 0 : j + 1;
     const int jm1 = (j == 0) ? P - 1 : j - 1;
     for (int64_t step = 0; step < nsteps; ++step) {
         const int bf = int(step & 1);
-        // Re-read the per-row coefficients every step (scalar cache hits):
-        // without this the compiler hoists all 8(M-2) of them out of the
-        // step loop and spills them from scalar registers.
+        // Per-row coefficients come from the scalar cache through a pointer
+        // in the constant address space (scalar loads).  The empty asm
+        // statements re-derive that pointer every few rows with a dependence
+        // on a value computed a few rows earlier: otherwise the compiler
+        // hoists all 8(M-2) loads (out of the step loop, or to the top of
+        // the step) and spills them from scalar registers.
+        typedef const __attribute__((address_space(4))) double cdouble;
         const double *cg = coef;
         asm volatile("" : "+s"(cg));
-        // read-only for the whole launch: constant address space, scalar loads
-        const __attribute__((address_space(4))) double *cf =
-            (const __attribute__((address_space(4))) double *)cg;
+        cdouble *cf = (cdouble *)cg;
         // forward: g = L^{-1} f_interior, and y_0, y_1 = w . g
         double t0 = 0.0, t1 = 0.0;
 #pragma unroll
         for (int i = 0; i < m; ++i) {
+            if (i >= 8 && i % 4 == 0) {
+                asm volatile("" : "+s"(cg) : "v"(x[i - 4]));
+                cf = (cdouble *)cg;
+            }
             double g = x[i];
             if (i >= 2) g -= a * x[i - 2];
             if (i >= 1) g -= cf[8 * i + 1] * x[i - 1];
@@ -309,24 +318,32 @@ k_hyper_resident(int P, int64_t batch, int64_t ld, int64_t nsteps,
         rbuf[bf][j][sl][0] = x[m] - a * yR0 - b * yR1 - e * yn0;
         rbuf[bf][j][sl][1] = x[m + 1] - a * yR1 - d * yn0 - e * yn1;
         __syncthreads();
-        // interface values of the previous chunk (L) and this chunk (R)
+        // interface values of the previous chunk (l) and this chunk (r):
+        // xI_{j-1} = sum_q T_q r_{j-1+q},  xI_j = sum_q T_{q-1} r_{j-1+q}
         double l0 = 0.0, l1 = 0.0, r0 = 0.0, r1 = 0.0;
-        int jq = jm1;
+#pragma unroll 2
         for (int q = 0; q < P; ++q) {
+            int jq = jm1 + q;
+            jq = jq >= P ? jq - P : jq;
             const double R0 = rbuf[bf][jq][sl][0], R1 = rbuf[bf][jq][sl][1];
-            const auto *Tq = cf + (8 * m + 8) + 4 * q;                          // xI_{j-1}
-            const auto *Tp = cf + (8 * m + 8) + 4 * (q == 0 ? P - 1 : q - 1);   // xI_j
+            const double *Tq = Tl[q];
+            const double *Tp = Tl[q == 0 ? P - 1 : q - 1];
             l0 += Tq[0] * R0 + Tq[1] * R1;
             l1 += Tq[2] * R0 + Tq[3] * R1;
             r0 += Tp[0] * R0 + Tp[1] * R1;
             r1 += Tp[2] * R0 + Tp[3] * R1;
-            jq = (jq + 1 == P) ? 0 : jq + 1;
         }
+        asm volatile("" : "+s"(cg) : "v"(r1));
+        cf = (cdouble *)cg;
         // backward: x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j)
         x[m - 2] -= URa * r0;
         x[m - 1] -= URb * r0 + URc * r1;
 #pragma unroll
         for (int i = m - 1; i >= 0; --i) {
+            if (i <= m - 9 && i % 4 == 3) {
+                asm volatile("" : "+s"(cg) : "v"(x[i + 5]));
+                cf = (cdouble *)cg;
+            }
             double v = x[i] - cf[8 * i + 6] * l0 - cf[8 * i + 7] * l1;
             if (i + 1 < m) v -= cf[8 * i + 4] * x[i + 1];
             if (i + 2 < m) v -= cf[8 * i + 5] * x[i + 2];
@@ -336,8 +353,13 @@ k_hyper_resident(int P, int64_t batch, int64_t ld, int64_t nsteps,
         x[m + 1] = r1;
     }
     if (act) {
+        // a fresh pointer: keeps the compiler from holding the 64 load
+        // addresses in registers for the whole step loop
+        double *outg = col;
+        asm volatile("" : "+v"(outg));
+        __attribute__((address_space(1))) double *out = (__attribute__((address_space(1))) double *)outg;
 #pragma unroll
-        for (int i = 0; i < M; ++i) col[int64_t(i) * ld] = x[i];
+        for (int i = 0; i < M; ++i) out[int64_t(i) * ld] = x[i];
     }
 }
 
@@ -356,18 +378,42 @@ size_t resident_coef_bytes(int64_t n)
     return M ? size_t(res_coef_elems(M, int(n / M))) * sizeof(double) : 0;
 }
 
+template <int M, int P>
+static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, double *coef,
+                       double *C, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_hyper_resident_setup<M, P>), dim3(1), dim3(64), 0, st, sigma, coef);
+    if (nsteps == 0) return;
+    const unsigned grid = unsigned((batch + kResSys - 1) / kResSys);
+    hipLaunchKernelGGL((k_hyper_resident<M, P>), dim3(grid), dim3(kResSys * P), 0, st, batch, ld,
+                       nsteps, (const double *)coef, C);
+}
+
 bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t nsteps, double sigma,
                                  void *coef, void *C, hipStream_t st)
 {
     constexpr int M = 64;
-    if (resident_chunk(n) != M) BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16");
-    const int P = int(n / M);
-    hipLaunchKernelGGL((k_hyper_resident_setup<M>), dim3(1), dim3(64), 0, st, P, sigma, (double *)coef);
-    BPS_LAUNCHED("k_hyper_resident_setup");
-    if (nsteps == 0) return BPS_OK;
-    const unsigned grid = unsigned((batch + kResSys - 1) / kResSys);
-    hipLaunchKernelGGL((k_hyper_resident<M>), dim3(grid), dim3(kResSys * P), 0, st, P, batch, ld,
-                       nsteps, (const double *)coef, (double *)C);
+    if (resident_chunk(n) != M || !(sigma >= 0.0))
+        BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16, sigma >= 0");
+    double *cf = (double *)coef, *x = (double *)C;
+    switch (int(n / M)) {
+    case 2: launch_res<M, 2>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 3: launch_res<M, 3>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 4: launch_res<M, 4>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 5: launch_res<M, 5>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 6: launch_res<M, 6>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 7: launch_res<M, 7>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 8: launch_res<M, 8>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 9: launch_res<M, 9>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 10: launch_res<M, 10>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 11: launch_res<M, 11>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 12: launch_res<M, 12>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 13: launch_res<M, 13>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 14: launch_res<M, 14>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 15: launch_res<M, 15>(batch, ld, nsteps, sigma, cf, x, st); break;
+    case 16: launch_res<M, 16>(batch, ld, nsteps, sigma, cf, x, st); break;
+    default: BPS_FAIL(BPS_ENOTSUP, "unsupported chunk count");
+    }
     BPS_LAUNCHED("k_hyper_resident");
     return BPS_OK;
 }
