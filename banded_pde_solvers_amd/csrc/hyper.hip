@@ -261,10 +261,9 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
     constexpr int m = M - 2;
     constexpr int S = kResSys;
     __shared__ double tbuf[2][P][S][4];
-    __shared__ double rbuf[2][P][S][2];
-    __shared__ double Tl[P][4];       // first block row of S^{-1}
+    __shared__ double rbuf[2][2 * P][S][2];   // r_k stored at k and k + P
+    __shared__ double xbuf[2][P][S][2];
     const int tid = threadIdx.x;
-    if (tid < 4 * P) Tl[tid >> 2][tid & 3] = coef[8 * m + 8 + tid];
     const int j = tid / S, sl = tid % S;
     const int64_t s = int64_t(blockIdx.x) * S + sl;
     const bool act = s < batch;
@@ -315,25 +314,36 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         tb[0] = t0; tb[1] = t1; tb[2] = yR0; tb[3] = yR1;
         __syncthreads();
         const double yn0 = tbuf[bf][jn][sl][0], yn1 = tbuf[bf][jn][sl][1];
-        rbuf[bf][j][sl][0] = x[m] - a * yR0 - b * yR1 - e * yn0;
-        rbuf[bf][j][sl][1] = x[m + 1] - a * yR1 - d * yn0 - e * yn1;
+        const double rj0 = x[m] - a * yR0 - b * yR1 - e * yn0;
+        const double rj1 = x[m + 1] - a * yR1 - d * yn0 - e * yn1;
+        rbuf[bf][j][sl][0] = rj0; rbuf[bf][j][sl][1] = rj1;
+        rbuf[bf][j + P][sl][0] = rj0; rbuf[bf][j + P][sl][1] = rj1;
         __syncthreads();
-        // interface values of the previous chunk (l) and this chunk (r):
-        // xI_{j-1} = sum_q T_q r_{j-1+q},  xI_j = sum_q T_{q-1} r_{j-1+q}
-        double l0 = 0.0, l1 = 0.0, r0 = 0.0, r1 = 0.0;
-#pragma unroll 2
-        for (int q = 0; q < P; ++q) {
-            int jq = jm1 + q;
-            jq = jq >= P ? jq - P : jq;
-            const double R0 = rbuf[bf][jq][sl][0], R1 = rbuf[bf][jq][sl][1];
-            const double *Tq = Tl[q];
-            const double *Tp = Tl[q == 0 ? P - 1 : q - 1];
-            l0 += Tq[0] * R0 + Tq[1] * R1;
-            l1 += Tq[2] * R0 + Tq[3] * R1;
-            r0 += Tp[0] * R0 + Tp[1] * R1;
-            r1 += Tp[2] * R0 + Tp[3] * R1;
+        // interface values of this chunk: xI_j = sum_q T_q r_{j+q}
+        // (block-circulant S^{-1}: T_q is its first block row)
+        double r0 = 0.0, r1 = 0.0;
+        {
+            const double *tg = coef + 8 * m + 8;
+            asm volatile("" : "+s"(tg) : "v"(rj1));
+            cdouble *T = (cdouble *)tg;
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                if (q >= 4 && q % 4 == 0) {
+                    asm volatile("" : "+s"(tg) : "v"(r1));
+                    T = (cdouble *)tg;
+                }
+                const double R0 = rbuf[bf][j + q][sl][0], R1 = rbuf[bf][j + q][sl][1];
+                r0 = fma(T[4 * q + 0], R0, r0);
+                r0 = fma(T[4 * q + 1], R1, r0);
+                r1 = fma(T[4 * q + 2], R0, r1);
+                r1 = fma(T[4 * q + 3], R1, r1);
+            }
         }
-        asm volatile("" : "+s"(cg) : "v"(r1));
+        xbuf[bf][j][sl][0] = r0; xbuf[bf][j][sl][1] = r1;
+        __syncthreads();
+        // ... and of the previous chunk, from its lane
+        const double l0 = xbuf[bf][jm1][sl][0], l1 = xbuf[bf][jm1][sl][1];
+        asm volatile("" : "+s"(cg) : "v"(l1));
         cf = (cdouble *)cg;
         // backward: x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j)
         x[m - 2] -= URa * r0;
