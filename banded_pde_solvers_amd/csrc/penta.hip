@@ -199,16 +199,16 @@ k_penta_cyclic_solve(int64_t n, int64_t batch, int64_t ld, int64_t nsteps,
 // g together; gamma and delta go to `work`, g into x; then back substitution.
 // ----------------------------------------------------------------------------
 
-template <typename T>
+template <typename T, int D>
 __global__ void __launch_bounds__(kWave)
 k_penta_fused(int64_t n, int64_t batch, int64_t ld,
               const T *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
-              const T *__restrict__ D, const T *__restrict__ E, T *__restrict__ x,
+              const T *__restrict__ D_, const T *__restrict__ E, T *__restrict__ x,
               T *__restrict__ work, int32_t *__restrict__ info)
 {
     const int64_t s = lane_id();
     if (s >= batch) return;
-    A += s; B += s; C += s; D += s; E += s; x += s;
+    A += s; B += s; C += s; D_ += s; E += s; x += s;
     T *ga = work + s, *de = work + n * ld + s;
     int32_t bad = 0;
     T gam1 = 0, gam2 = 0, del1 = 0, del2 = 0, g1 = 0, g2 = 0;
@@ -217,7 +217,7 @@ k_penta_fused(int64_t n, int64_t batch, int64_t ld,
         const T alpha = C[0];
         if (bad_pivot(alpha)) bad = 1;
         const T r = T(1) / alpha;
-        gam1 = D[0] * r; del1 = E[0] * r; g1 = x[0] * r;
+        gam1 = D_[0] * r; del1 = E[0] * r; g1 = x[0] * r;
         ga[0] = gam1; de[0] = del1; x[0] = g1;
     }
     {
@@ -225,15 +225,25 @@ k_penta_fused(int64_t n, int64_t batch, int64_t ld,
         const T alpha = C[ld] - beta * gam1;
         if (!bad && bad_pivot(alpha)) bad = 2;
         const T r = T(1) / alpha;
-        const T gam = (D[ld] - beta * del1) * r, del = E[ld] * r;
+        const T gam = (D_[ld] - beta * del1) * r, del = E[ld] * r;
         const T g = (x[ld] - beta * g1) * r;
         ga[ld] = gam; de[ld] = del; x[ld] = g;
         gam2 = gam1; gam1 = gam; del2 = del1; del1 = del; g2 = g1; g1 = g;
     }
-#pragma unroll 4
-    for (int64_t i = 2; i < n - 2; ++i) {
+    // rows 2 .. n-3 with a prefetch ring: the six inputs of row i + D are
+    // loaded while row i is eliminated (one lane per system keeps only one
+    // wavefront per SIMD busy, so memory-level parallelism has to come from
+    // each lane's own look-ahead).
+    const int64_t last = n - 1;
+    auto rowp = [&](int64_t r) { return (r < last ? r : last) * ld; };
+    T qa[D], qb[D], qc[D], qd[D], qe[D], qf[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        const int64_t o = rowp(2 + k);
+        qa[k] = A[o]; qb[k] = B[o]; qc[k] = C[o]; qd[k] = D_[o]; qe[k] = E[o]; qf[k] = x[o];
+    }
+    auto fwd_row = [&](int64_t i, T ai, T bi, T ci, T di, T ei, T fi) {
         const int64_t o = i * ld;
-        const T ai = A[o], bi = B[o], ci = C[o], di = D[o], ei = E[o], fi = x[o];
         const T beta = bi - ai * gam2;
         const T alpha = ci - ai * del2 - beta * gam1;
         if (!bad && bad_pivot(alpha)) bad = int32_t(i) + 1;
@@ -243,7 +253,20 @@ k_penta_fused(int64_t n, int64_t batch, int64_t ld,
         const T g = (fi - ai * g2 - beta * g1) * r;
         ga[o] = gam; de[o] = del; x[o] = g;
         gam2 = gam1; gam1 = gam; del2 = del1; del1 = del; g2 = g1; g1 = g;
+    };
+    int64_t i = 2;
+    for (; i + D <= n - 2; i += D) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+            const T ai = qa[k], bi = qb[k], ci = qc[k], di = qd[k], ei = qe[k], fi = qf[k];
+            const int64_t o = rowp(i + k + D);
+            qa[k] = A[o]; qb[k] = B[o]; qc[k] = C[o]; qd[k] = D_[o]; qe[k] = E[o]; qf[k] = x[o];
+            fwd_row(i + k, ai, bi, ci, di, ei, fi);
+        }
     }
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+        if (i + k < n - 2) fwd_row(i + k, qa[k], qb[k], qc[k], qd[k], qe[k], qf[k]);
     // rows n-2 and n-1: d_{n-1}, e_{n-2}, e_{n-1} are outside the matrix
     T gam_n2;
     {
@@ -253,7 +276,7 @@ k_penta_fused(int64_t n, int64_t batch, int64_t ld,
         const T alpha = C[o] - ai * del2 - beta * gam1;
         if (!bad && bad_pivot(alpha)) bad = int32_t(n - 2) + 1;
         const T r = T(1) / alpha;
-        gam_n2 = (D[o] - beta * del1) * r;
+        gam_n2 = (D_[o] - beta * del1) * r;
         const T g = (x[o] - ai * g2 - beta * g1) * r;
         x[o] = g;
         gam2 = gam1; gam1 = gam_n2; del2 = del1; del1 = 0; g2 = g1; g1 = g;
@@ -270,16 +293,36 @@ k_penta_fused(int64_t n, int64_t batch, int64_t ld,
         x[o] = xl;
     }
     if (info) info[s] = bad;
-    // back substitution
+    // back substitution, rows n-3 .. 0, with the same look-ahead
     T x1 = g1 - gam_n2 * xl;                  // x_{n-2}
     x[(n - 2) * ld] = x1;
     T x2 = xl;
-#pragma unroll 4
-    for (int64_t i = n - 3; i >= 0; --i) {
-        const int64_t o = i * ld;
-        const T xi = x[o] - ga[o] * x1 - de[o] * x2;
-        x[o] = xi;
-        x2 = x1; x1 = xi;
+    auto rowb = [&](int64_t r) { return (r > 0 ? r : 0) * ld; };
+    T pg[D], pga[D], pde[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        const int64_t o = rowb(n - 3 - k);
+        pg[k] = x[o]; pga[k] = ga[o]; pde[k] = de[o];
+    }
+    int64_t r = n - 3;
+    for (; r - D >= -1; r -= D) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+            const T gi = pg[k], gai = pga[k], dei = pde[k];
+            const int64_t o = rowb(r - k - D);
+            pg[k] = x[o]; pga[k] = ga[o]; pde[k] = de[o];
+            const T xi = gi - gai * x1 - dei * x2;
+            x[(r - k) * ld] = xi;
+            x2 = x1; x1 = xi;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        if (r - k >= 0) {
+            const T xi = pg[k] - pga[k] * x1 - pde[k] * x2;
+            x[(r - k) * ld] = xi;
+            x2 = x1; x1 = xi;
+        }
     }
 }
 
@@ -341,7 +384,7 @@ bps_status launch_penta_fused(int64_t n, int64_t batch, int64_t ld, const void *
                               const void *c, const void *d, const void *e, void *x, void *work,
                               int32_t *info, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_penta_fused<T>), grid_for(batch), dim3(kWave), 0, st, n, batch, ld,
+    hipLaunchKernelGGL((k_penta_fused<T, 8>), grid_for(batch), dim3(kWave), 0, st, n, batch, ld,
                        (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
                        (T *)x, (T *)work, info);
     BPS_LAUNCHED("k_penta_fused");
