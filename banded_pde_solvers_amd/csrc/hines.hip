@@ -50,7 +50,8 @@ struct bps_hines_plan {
 
 namespace bps {
 
-constexpr int kRing = 16;   // LDS ring slots per lane
+constexpr int kRing = 16;       // LDS ring slots per lane (power of two)
+constexpr int kHinesAhead = 8;  // rows of look-ahead for the streamed inputs
 
 struct HinesArgs {
     int64_t batch, n, ld;            // mono geometry
@@ -62,7 +63,7 @@ struct HinesArgs {
     int32_t *info;
 };
 
-template <bool MONO, bool GEN>
+template <bool MONO, bool GEN, int D>
 __global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
 {
     __shared__ double ring_d[kRing][kWave];
@@ -86,35 +87,57 @@ __global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
     const int32_t *par = MONO ? A.parent : A.parent + base;
     const int64_t pst = MONO ? 1 : ld;   // parent stride
     double *gd = GEN ? A.gd + base : nullptr, *gr = GEN ? A.gr + base : nullptr;
+    auto parent_of = [&](int32_t i) { return par[int64_t(i) * pst]; };
 
 #pragma unroll
     for (int j = 0; j < kRing; ++j) { ring_d[j][k] = 0.0; ring_r[j][k] = 0.0; }
 
     int32_t bad = 0;
     // ---- leaves -> root elimination --------------------------------------
-    for (int32_t i = rows - 1; i >= 1; --i) {
-        if (i >= my_n) continue;
-        const int64_t o = int64_t(i) * ld;
-        const int slot = i % kRing;
-        double pd = ring_d[slot][k], pr = ring_r[slot][k];
-        ring_d[slot][k] = 0.0; ring_r[slot][k] = 0.0;
-        if (GEN) { pd += gd[o]; pr += gr[o]; }
-        const double dd = d[o] - pd;            // d'_i
-        const double rr = rhs[o] - pr;          // rhs'_i
-        if (!bad && bad_pivot(dd)) bad = i + 1;
-        const double rcp = 1.0 / dd;
-        const double fac = u[o] * rcp;          // factor of Algorithm 1
-        const double li = l[o];
-        rhs[o] = rr * rcp;                      // q_i
-        mw[o] = li * rcp;                       // m_i
-        const int32_t p = par[int64_t(i) * pst];
-        if (!GEN || i - p <= kRing) {
-            const int ps = p % kRing;
-            ring_d[ps][k] += fac * li;
-            ring_r[ps][k] += fac * rr;
-        } else {
-            gd[int64_t(p) * ld] += fac * li;
-            gr[int64_t(p) * ld] += fac * rr;
+    // The streamed inputs of row i - D are loaded while row i is eliminated;
+    // parent updates are accumulated with LDS atomic adds on the lane's own
+    // column (no read on the elimination chain); only the row's own pending
+    // value is read back.
+    double qu[D], ql[D], qd[D], qr[D];
+    int32_t qp[D];
+    auto load_b = [&](int j, int32_t r) {
+        const bool live = r >= 1 && r < my_n;
+        const int64_t o = int64_t(live ? r : 0) * ld;
+        qu[j] = live ? u[o] : 0.0; ql[j] = live ? l[o] : 0.0;
+        qd[j] = live ? d[o] : 1.0; qr[j] = live ? rhs[o] : 0.0;
+        if (!MONO) qp[j] = live ? par[o] : 0;
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_b(j, rows - 1 - j);
+    for (int32_t i0 = rows - 1; i0 >= 1; i0 -= D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int32_t i = i0 - j;
+            if (i < 1) break;
+            const double ui = qu[j], li = ql[j], di = qd[j], ri = qr[j];
+            const int32_t pi = MONO ? parent_of(i) : qp[j];
+            load_b(j, i - D);
+            if (i >= my_n) continue;
+            const int64_t o = int64_t(i) * ld;
+            const int slot = i & (kRing - 1);
+            double pd = ring_d[slot][k], pr = ring_r[slot][k];
+            ring_d[slot][k] = 0.0; ring_r[slot][k] = 0.0;
+            if (GEN) { pd += gd[o]; pr += gr[o]; }
+            const double dd = di - pd;               // d'_i
+            const double rr = ri - pr;               // rhs'_i
+            if (!bad && bad_pivot(dd)) bad = i + 1;
+            const double rcp = 1.0 / dd;
+            const double fac = ui * rcp;             // factor of Algorithm 1
+            rhs[o] = rr * rcp;                       // q_i
+            mw[o] = li * rcp;                        // m_i
+            if (!GEN || i - pi <= kRing) {
+                const int ps = pi & (kRing - 1);
+                unsafeAtomicAdd(&ring_d[ps][k], fac * li);
+                unsafeAtomicAdd(&ring_r[ps][k], fac * rr);
+            } else {
+                gd[int64_t(pi) * ld] += fac * li;
+                gr[int64_t(pi) * ld] += fac * rr;
+            }
         }
     }
     double v0 = 0.0;
@@ -128,18 +151,113 @@ __global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
     }
     if (src >= 0 && A.info) A.info[src] = bad;
     // ---- root -> leaves substitution -------------------------------------
-    // ring_d now holds the last kRing voltages (V of row j in slot j mod kRing)
+    // ring_d now holds the last kRing voltages (V of row j in slot j mod kRing);
+    // a parent one row up comes straight from a register.
     ring_d[0][k] = v0;
-    for (int32_t i = 1; i < rows; ++i) {
-        if (i >= my_n) break;
-        const int64_t o = int64_t(i) * ld;
-        const int32_t p = par[int64_t(i) * pst];
-        double vp;
-        if (!GEN || i - p <= kRing) vp = ring_d[p % kRing][k];
-        else vp = rhs[int64_t(p) * ld];
-        const double v = rhs[o] - mw[o] * vp;
-        rhs[o] = v;
-        ring_d[i % kRing][k] = v;
+    double vprev = v0;
+    double fq[D], fm[D];
+    int32_t fp[D];
+    auto load_f = [&](int j, int32_t r) {
+        const bool live = r < my_n;
+        const int64_t o = int64_t(live ? r : 0) * ld;
+        fq[j] = live ? rhs[o] : 0.0; fm[j] = live ? mw[o] : 0.0;
+        if (!MONO) fp[j] = live ? par[o] : 0;
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_f(j, 1 + j);
+    for (int32_t i0 = 1; i0 < rows; i0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int32_t i = i0 + j;
+            if (i >= rows) break;
+            const double qi = fq[j], mi = fm[j];
+            const int32_t pi = MONO ? parent_of(i) : fp[j];
+            load_f(j, i + D);
+            if (i >= my_n) continue;
+            double vp;
+            if (i - pi == 1) vp = vprev;
+            else if (!GEN || i - pi <= kRing) vp = ring_d[pi & (kRing - 1)][k];
+            else vp = rhs[int64_t(pi) * ld];
+            const double v = qi - mi * vp;
+            rhs[int64_t(i) * ld] = v;
+            ring_d[i & (kRing - 1)][k] = v;
+            vprev = v;
+        }
+    }
+}
+
+// One tree shared by all lanes and parents within kRing rows: the parent
+// index is wave-uniform, so the pending updates and the recent voltages stay
+// in registers, indexed by a uniform slot (relative register addressing).
+template <int D>
+__global__ void __launch_bounds__(kWave) k_hines_mono_reg(HinesArgs A)
+{
+    const int k = threadIdx.x;
+    const int64_t s = int64_t(blockIdx.x) * kWave + k;
+    const bool act = s < A.batch;
+    const int64_t ld = A.ld;
+    const int32_t n = int32_t(A.n);
+    const int64_t base = act ? s : A.batch - 1;     // tail lanes shadow the last neuron
+    const double *u = A.u + base, *l = A.l + base, *d = A.d + base;
+    double *rhs = A.rhs + base, *mw = A.mwork + base;
+    const int32_t *par = A.parent;
+    double pend_d[kRing], pend_r[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) { pend_d[j] = 0.0; pend_r[j] = 0.0; }
+    int32_t bad = 0;
+    double qu[D], ql[D], qd[D], qr[D];
+    auto load_b = [&](int j, int32_t r) {
+        const int64_t o = int64_t(r >= 1 ? r : 0) * ld;
+        qu[j] = u[o]; ql[j] = l[o]; qd[j] = d[o]; qr[j] = rhs[o];
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_b(j, n - 1 - j);
+    for (int32_t i0 = n - 1; i0 >= 1; i0 -= D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int32_t i = i0 - j;
+            if (i < 1) break;
+            const double ui = qu[j], li = ql[j], di = qd[j], ri = qr[j];
+            load_b(j, i - D);
+            const int slot = __builtin_amdgcn_readfirstlane(i & (kRing - 1));
+            const int ps = __builtin_amdgcn_readfirstlane(par[i] & (kRing - 1));
+            const double dd = di - pend_d[slot];     // d'_i
+            const double rr = ri - pend_r[slot];     // rhs'_i
+            pend_d[slot] = 0.0; pend_r[slot] = 0.0;
+            if (!bad && bad_pivot(dd)) bad = i + 1;
+            const double rcp = 1.0 / dd;
+            const double fac = ui * rcp;
+            const int64_t o = int64_t(i) * ld;
+            if (act) { rhs[o] = rr * rcp; mw[o] = li * rcp; }
+            pend_d[ps] += fac * li;
+            pend_r[ps] += fac * rr;
+        }
+    }
+    const double dd0 = d[0] - pend_d[0];
+    if (!bad && bad_pivot(dd0)) bad = 1;
+    const double v0 = (rhs[0] - pend_r[0]) / dd0;
+    if (act) { rhs[0] = v0; if (A.info) A.info[s] = bad; }
+    // substitution: recent voltages by slot (pend_d reused)
+    pend_d[0] = v0;
+    double fq[D], fm[D];
+    auto load_f = [&](int j, int32_t r) {
+        const int64_t o = int64_t(r < n ? r : n - 1) * ld;
+        fq[j] = rhs[o]; fm[j] = mw[o];
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_f(j, 1 + j);
+    for (int32_t i0 = 1; i0 < n; i0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int32_t i = i0 + j;
+            if (i >= n) break;
+            const double qi = fq[j], mi = fm[j];
+            load_f(j, i + D);
+            const int ps = __builtin_amdgcn_readfirstlane(par[i] & (kRing - 1));
+            const double v = qi - mi * pend_d[ps];
+            if (act) rhs[int64_t(i) * ld] = v;
+            pend_d[__builtin_amdgcn_readfirstlane(i & (kRing - 1))] = v;
+        }
     }
 }
 
@@ -329,12 +447,13 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
         BPS_LAUNCHED("k_fill_zero");
     }
     const dim3 grid(unsigned(P->mono ? (P->batch + kWave - 1) / kWave : P->nblocks));
+    constexpr int D = kHinesAhead;
     if (P->mono) {
-        if (gen) hipLaunchKernelGGL((k_hines<true, true>), grid, dim3(kWave), 0, st, A);
-        else hipLaunchKernelGGL((k_hines<true, false>), grid, dim3(kWave), 0, st, A);
+        if (gen) hipLaunchKernelGGL((k_hines<true, true, D>), grid, dim3(kWave), 0, st, A);
+        else hipLaunchKernelGGL((k_hines_mono_reg<D>), grid, dim3(kWave), 0, st, A);
     } else {
-        if (gen) hipLaunchKernelGGL((k_hines<false, true>), grid, dim3(kWave), 0, st, A);
-        else hipLaunchKernelGGL((k_hines<false, false>), grid, dim3(kWave), 0, st, A);
+        if (gen) hipLaunchKernelGGL((k_hines<false, true, D>), grid, dim3(kWave), 0, st, A);
+        else hipLaunchKernelGGL((k_hines<false, false, D>), grid, dim3(kWave), 0, st, A);
     }
     BPS_LAUNCHED("k_hines");
     return BPS_OK;
