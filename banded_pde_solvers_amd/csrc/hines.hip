@@ -197,7 +197,11 @@ __global__ void __launch_bounds__(kWave) k_hines_mono_reg(HinesArgs A)
     const bool act = s < A.batch;
     const int64_t ld = A.ld;
     const int32_t n = int32_t(A.n);
-    const int64_t base = act ? s : A.batch - 1;     // tail lanes shadow the last neuron
+    // Lanes past the end of the batch shadow the last neuron: they compute
+    // exactly what its own lane computes and store the same values, so the
+    // hot loops need no branches (a branch around a load or store makes the
+    // compiler drain every outstanding load at the join).
+    const int64_t base = act ? s : A.batch - 1;
     const double *u = A.u + base, *l = A.l + base, *d = A.d + base;
     double *rhs = A.rhs + base, *mw = A.mwork + base;
     const int32_t *par = A.parent;
@@ -206,59 +210,185 @@ __global__ void __launch_bounds__(kWave) k_hines_mono_reg(HinesArgs A)
     for (int j = 0; j < kRing; ++j) { pend_d[j] = 0.0; pend_r[j] = 0.0; }
     int32_t bad = 0;
     double qu[D], ql[D], qd[D], qr[D];
+    int32_t qp[D];
     auto load_b = [&](int j, int32_t r) {
-        const int64_t o = int64_t(r >= 1 ? r : 0) * ld;
+        int32_t rr = r >= 1 ? r : 1;
+        rr = rr < n ? rr : n - 1;                // n == 1: row 0 (never used)
+        const int64_t o = int64_t(rr) * ld;
         qu[j] = u[o]; ql[j] = l[o]; qd[j] = d[o]; qr[j] = rhs[o];
+        qp[j] = par[rr];
     };
 #pragma unroll
     for (int j = 0; j < D; ++j) load_b(j, n - 1 - j);
-    for (int32_t i0 = n - 1; i0 >= 1; i0 -= D) {
+    auto elim = [&](int32_t i, double ui, double li, double di, double ri, int32_t pi) {
+        const int ps = __builtin_amdgcn_readfirstlane(pi & (kRing - 1));
+        const int slot = __builtin_amdgcn_readfirstlane(i & (kRing - 1));
+        const double dd = di - pend_d[slot];     // d'_i
+        const double rr = ri - pend_r[slot];     // rhs'_i
+        pend_d[slot] = 0.0; pend_r[slot] = 0.0;
+        if (!bad && bad_pivot(dd)) bad = i + 1;
+        const double rcp = 1.0 / dd;
+        const double fac = ui * rcp;
+        const int64_t o = int64_t(i) * ld;
+        rhs[o] = rr * rcp;
+        mw[o] = li * rcp;
+        pend_d[ps] += fac * li;
+        pend_r[ps] += fac * rr;
+    };
+    // whole blocks of D rows (no exits inside: the loaded values land directly
+    // in the look-ahead registers), then the last rows without look-ahead
+    int32_t i0 = n - 1;
+    for (; i0 - D + 1 >= 1; i0 -= D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            const int32_t i = i0 - j;
-            if (i < 1) break;
             const double ui = qu[j], li = ql[j], di = qd[j], ri = qr[j];
-            load_b(j, i - D);
-            const int slot = __builtin_amdgcn_readfirstlane(i & (kRing - 1));
-            const int ps = __builtin_amdgcn_readfirstlane(par[i] & (kRing - 1));
-            const double dd = di - pend_d[slot];     // d'_i
-            const double rr = ri - pend_r[slot];     // rhs'_i
-            pend_d[slot] = 0.0; pend_r[slot] = 0.0;
-            if (!bad && bad_pivot(dd)) bad = i + 1;
-            const double rcp = 1.0 / dd;
-            const double fac = ui * rcp;
-            const int64_t o = int64_t(i) * ld;
-            if (act) { rhs[o] = rr * rcp; mw[o] = li * rcp; }
-            pend_d[ps] += fac * li;
-            pend_r[ps] += fac * rr;
+            const int32_t pi = qp[j];
+            load_b(j, i0 - j - D);
+            elim(i0 - j, ui, li, di, ri, pi);
         }
     }
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        if (i0 - j >= 1) elim(i0 - j, qu[j], ql[j], qd[j], qr[j], qp[j]);
     const double dd0 = d[0] - pend_d[0];
     if (!bad && bad_pivot(dd0)) bad = 1;
     const double v0 = (rhs[0] - pend_r[0]) / dd0;
-    if (act) { rhs[0] = v0; if (A.info) A.info[s] = bad; }
+    rhs[0] = v0;
+    if (act && A.info) A.info[s] = bad;
     // substitution: recent voltages by slot (pend_d reused)
     pend_d[0] = v0;
     double fq[D], fm[D];
+    int32_t fp[D];
     auto load_f = [&](int j, int32_t r) {
-        const int64_t o = int64_t(r < n ? r : n - 1) * ld;
-        fq[j] = rhs[o]; fm[j] = mw[o];
+        const int32_t rr = r < n ? r : n - 1;
+        const int64_t o = int64_t(rr) * ld;
+        fq[j] = rhs[o]; fm[j] = mw[o]; fp[j] = par[rr];
     };
 #pragma unroll
     for (int j = 0; j < D; ++j) load_f(j, 1 + j);
-    for (int32_t i0 = 1; i0 < n; i0 += D) {
+    auto subst = [&](int32_t i, double qi, double mi, int32_t pi) {
+        const int ps = __builtin_amdgcn_readfirstlane(pi & (kRing - 1));
+        const double v = qi - mi * pend_d[ps];
+        rhs[int64_t(i) * ld] = v;
+        pend_d[__builtin_amdgcn_readfirstlane(i & (kRing - 1))] = v;
+    };
+    int32_t f0 = 1;
+    for (; f0 + D - 1 < n; f0 += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            const int32_t i = i0 + j;
-            if (i >= n) break;
             const double qi = fq[j], mi = fm[j];
-            load_f(j, i + D);
-            const int ps = __builtin_amdgcn_readfirstlane(par[i] & (kRing - 1));
-            const double v = qi - mi * pend_d[ps];
-            if (act) rhs[int64_t(i) * ld] = v;
-            pend_d[__builtin_amdgcn_readfirstlane(i & (kRing - 1))] = v;
+            const int32_t pi = fp[j];
+            load_f(j, f0 + j + D);
+            subst(f0 + j, qi, mi, pi);
         }
     }
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        if (f0 + j < n) subst(f0 + j, fq[j], fm[j], fp[j]);
+}
+
+// Multi-morphology blocks, parents within kRing rows: branch-free loops.
+// Every lane reads and writes only its own column of its block (rows past
+// its neuron's size are padding of the packed layout); results of padding
+// rows are masked with selects and padding is written back unchanged.
+template <int D>
+__global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
+{
+    __shared__ double ring_d[kRing][kWave];
+    __shared__ double ring_r[kRing][kWave];
+    const int k = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t base = A.blk_off[b] + k;
+    const int32_t rows = A.blk_rows[b];
+    const int32_t my_n = A.lane_n[b * kWave + k];
+    const int32_t src = A.lane_src[b * kWave + k];
+    constexpr int64_t ld = kWave;
+    const double *u = A.u + base, *l = A.l + base, *d = A.d + base;
+    double *rhs = A.rhs + base, *mw = A.mwork + base;
+    const int32_t *par = A.parent + base;
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) { ring_d[j][k] = 0.0; ring_r[j][k] = 0.0; }
+    int32_t bad = 0;
+    double qu[D], ql[D], qd[D], qr[D];
+    int32_t qp[D];
+    auto load_b = [&](int j, int32_t r) {
+        const int64_t o = int64_t(r >= 1 ? r : 1 < rows ? 1 : 0) * ld;
+        qu[j] = u[o]; ql[j] = l[o]; qd[j] = d[o]; qr[j] = rhs[o]; qp[j] = par[o];
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_b(j, rows - 1 - j);
+    auto elim = [&](int32_t i, double ui, double li, double di, double ri, int32_t pi) {
+            const bool live = i < my_n;
+            const int64_t o = int64_t(i) * ld;
+            const int slot = i & (kRing - 1);
+            const double pd = ring_d[slot][k], pr = ring_r[slot][k];
+            ring_d[slot][k] = 0.0; ring_r[slot][k] = 0.0;
+            const double dd = di - pd;               // d'_i
+            const double rr = ri - pr;               // rhs'_i
+            if (live && !bad && bad_pivot(dd)) bad = i + 1;
+            const double rcp = 1.0 / dd;
+            const double fac = live ? ui * rcp : 0.0;  // factor of Algorithm 1
+            rhs[o] = live ? rr * rcp : ri;           // q_i (padding unchanged)
+            mw[o] = live ? li * rcp : 0.0;           // m_i
+            const int ps = pi & (kRing - 1);
+            unsafeAtomicAdd(&ring_d[ps][k], fac * li);
+            unsafeAtomicAdd(&ring_r[ps][k], fac * rr);
+    };
+    int32_t i0 = rows - 1;
+    for (; i0 - D + 1 >= 1; i0 -= D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const double ui = qu[j], li = ql[j], di = qd[j], ri = qr[j];
+            const int32_t pi = qp[j];
+            load_b(j, i0 - j - D);
+            elim(i0 - j, ui, li, di, ri, pi);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        if (i0 - j >= 1) elim(i0 - j, qu[j], ql[j], qd[j], qr[j], qp[j]);
+    const bool root = my_n > 0;
+    const double pd0 = ring_d[0][k], pr0 = ring_r[0][k];
+    const double dd0 = d[0] - pd0;
+    if (root && !bad && bad_pivot(dd0)) bad = 1;
+    const double r0 = rhs[0];
+    const double v0 = root ? (r0 - pr0) / dd0 : 0.0;
+    rhs[0] = root ? v0 : r0;
+    if (src >= 0 && A.info) A.info[src] = bad;
+    // root -> leaves; ring_d holds recent voltages by slot, a parent one row
+    // up comes from a register
+    ring_d[0][k] = v0;
+    double vprev = v0;
+    double fq[D], fm[D];
+    int32_t fp[D];
+    auto load_f = [&](int j, int32_t r) {
+        const int64_t o = int64_t(r < rows ? r : rows - 1) * ld;
+        fq[j] = rhs[o]; fm[j] = mw[o]; fp[j] = par[o];
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_f(j, 1 + j);
+    auto subst = [&](int32_t i, double qi, double mi, int32_t pi) {
+        const bool live = i < my_n;
+        const double vr = ring_d[pi & (kRing - 1)][k];
+        const double vp = (i - pi == 1) ? vprev : vr;
+        const double v = qi - mi * vp;
+        rhs[int64_t(i) * ld] = live ? v : qi;
+        ring_d[i & (kRing - 1)][k] = v;
+        vprev = v;
+    };
+    int32_t f0 = 1;
+    for (; f0 + D - 1 < rows; f0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const double qi = fq[j], mi = fm[j];
+            const int32_t pi = fp[j];
+            load_f(j, f0 + j + D);
+            subst(f0 + j, qi, mi, pi);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        if (f0 + j < rows) subst(f0 + j, fq[j], fm[j], fp[j]);
 }
 
 __global__ void k_fill_zero(double *p, int64_t count)
@@ -453,7 +583,7 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
         else hipLaunchKernelGGL((k_hines_mono_reg<D>), grid, dim3(kWave), 0, st, A);
     } else {
         if (gen) hipLaunchKernelGGL((k_hines<false, true, D>), grid, dim3(kWave), 0, st, A);
-        else hipLaunchKernelGGL((k_hines<false, false, D>), grid, dim3(kWave), 0, st, A);
+        else hipLaunchKernelGGL((k_hines_multi<D>), grid, dim3(kWave), 0, st, A);
     }
     BPS_LAUNCHED("k_hines");
     return BPS_OK;
