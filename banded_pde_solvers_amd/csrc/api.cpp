@@ -164,6 +164,13 @@ bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, co
     CHECK(check_ptr(e, "e", dsc->dtype)); CHECK(check_ptr(x, "x", dsc->dtype));
     CHECK(check_ptr(work, "work", dsc->dtype));
     if (info && !aligned(info, 4)) BPS_FAIL(BPS_EINVAL, "info is not 4-byte aligned");
+    if (spike_chunks(dsc->n)) {
+        if (dsc->dtype == BPS_F64)
+            return launch_penta_spike<double>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work,
+                                              info, as_stream(stream));
+        return launch_penta_spike<float>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work,
+                                         info, as_stream(stream));
+    }
     if (dsc->dtype == BPS_F64)
         return launch_penta_fused<double>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work, info,
                                           as_stream(stream));

@@ -19,6 +19,13 @@ template <typename T>
 bps_status launch_penta_fused(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
                               const void *c, const void *d, const void *e, void *x, void *work,
                               int32_t *info, hipStream_t st);
+// Chunked register-resident factor + solve (per-system, non-periodic);
+// spike_chunks(n) is the number of 16-row chunks, 0 when it does not apply.
+int spike_chunks(int64_t n);
+template <typename T>
+bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
+                              const void *c, const void *d, const void *e, void *x, void *work,
+                              int32_t *info, hipStream_t st);
 
 // Builds the five shared diagonals of I + sigma*D4 on the device.
 template <typename T>

@@ -1,0 +1,350 @@
+// penta_spike.hip -- register-resident factor + solve of batched pentadiagonal
+// systems with per-system coefficients (the "Rewrite" use of the cuPentBatch
+// page: a new matrix every call), for gfx950.
+//
+// One lane per system streams every row through global memory twice (the
+// back substitution needs gamma, delta and g of every row), so HBM sees the
+// six inputs, the result and a 24-byte-per-row round trip.  Here each system
+// is split into P chunks of M rows and one lane owns one chunk:
+//
+//   rows 0 .. M-3 of a chunk ("interior") form a pentadiagonal block E_j
+//   that couples only to the last two rows of the previous chunk
+//   ("interface" I_{j-1}, through C_L) and to its own last two rows (I_j,
+//   through C_R);  eliminating the interiors leaves a block-tridiagonal
+//   system with 2x2 blocks on the interfaces:
+//
+//     L_j xI_{j-1} + D_j xI_j + U_j xI_{j+1} = r_j,
+//     D_j = A_II - B_own Z_R,j - B_next Z_L,j+1,   L_j = -B_own Z_L,j,
+//     U_j = -B_next Z_R,j+1,   r_j = f_I - B_own y_j - B_next y_{j+1},
+//     with y = E^{-1} f and Z = E^{-1} C (only their first / last two rows
+//     are needed), and B_own / B_next the interface rows' entries on the
+//     own / next interior.
+//
+// The lane factors E_j = L R with the page's elimination steps while the
+// inputs stream in, and keeps gamma, delta, g = L^{-1} f and U_L = L^{-1} C_L
+// for its rows in registers; the first two rows of E^{-1} f and E^{-1} C come
+// from w_k = R^{-T} e_k dot products accumulated in the same sweep.  The
+// interface system is solved by block cyclic reduction (parallel, log2 P
+// steps through LDS) across the P lanes of a system, and each lane then
+// back-substitutes x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j) and writes it.
+// HBM traffic: the 5 diagonals and f read once, x written once.
+#include "common.h"
+#include "kernels.h"
+
+namespace bps {
+
+
+template <typename T>
+struct M22 {
+    T a, b, c, d;   // [[a, b], [c, d]]
+};
+
+template <typename T>
+__device__ __forceinline__ M22<T> mul(const M22<T> &x, const M22<T> &y)
+{
+    return {x.a * y.a + x.b * y.c, x.a * y.b + x.b * y.d, x.c * y.a + x.d * y.c, x.c * y.b + x.d * y.d};
+}
+
+template <typename T>
+__device__ __forceinline__ M22<T> inv(const M22<T> &x, T &det)
+{
+    det = x.a * x.d - x.b * x.c;
+    const T r = T(1) / det;
+    return {x.d * r, -x.b * r, -x.c * r, x.a * r};
+}
+
+// Sequential factor + solve of one system (the page's algorithm, one lane):
+// the fallback for a system whose chunked elimination met a zero or
+// non-finite pivot.  gamma and delta go to `work` (column s of two n x ld
+// arrays), g overwrites f in x.  Returns the 1-based first row whose pivot
+// is zero or non-finite, 0 when there is none.
+template <typename T>
+__device__ int32_t seq_penta_solve(int64_t n, int64_t ld, const T *A, const T *B, const T *C,
+                                   const T *D, const T *E, T *x, T *work)
+{
+    T *wg = work, *wd = work + n * ld;
+    T gam1 = 0, gam2 = 0, del1 = 0, del2 = 0, g1 = 0, g2 = 0;
+    int32_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t o = i * ld;
+        const T ai = i >= 2 ? A[o] : T(0), bi = i >= 1 ? B[o] : T(0);
+        const T di = i + 1 < n ? D[o] : T(0), ei = i + 2 < n ? E[o] : T(0);
+        const T beta = bi - ai * gam2;
+        const T alpha = C[o] - ai * del2 - beta * gam1;
+        if (!bad && bad_pivot(alpha)) bad = int32_t(i) + 1;
+        const T r = T(1) / alpha;
+        const T gm = (di - beta * del1) * r, dl = ei * r;
+        const T g = (x[o] - ai * g2 - beta * g1) * r;
+        wg[o] = gm; wd[o] = dl; x[o] = g;
+        gam2 = gam1; gam1 = gm; del2 = del1; del1 = dl; g2 = g1; g1 = g;
+    }
+    T x1 = 0, x2 = 0;
+    for (int64_t i = n - 1; i >= 0; --i) {
+        const int64_t o = i * ld;
+        const T v = x[o] - wg[o] * x1 - wd[o] * x2;
+        x[o] = v;
+        x2 = x1; x1 = v;
+    }
+    return bad;
+}
+
+// One workgroup holds S systems x P chunks of M rows (lane = chunk j of
+// system sl); n = P * M, P * S <= 512.  Dynamic LDS: 14 * P * S values of
+// T + S flags.
+template <typename T, int M, int S>
+__global__ void __launch_bounds__(512)
+k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
+              const T *__restrict__ C, const T *__restrict__ D, const T *__restrict__ E,
+              T *__restrict__ x, T *__restrict__ work, int32_t *__restrict__ info)
+{
+    constexpr int m = M - 2;            // interior rows of a chunk
+    constexpr int LA = 4;               // rows of look-ahead for the streamed inputs
+    extern __shared__ unsigned char lds_raw[];
+    T *buf = reinterpret_cast<T *>(lds_raw);          // [field][P][S]
+    int32_t *flag = reinterpret_cast<int32_t *>(buf + 14 * P * S);
+    const int tid = threadIdx.x;
+    if (tid < S) flag[tid] = 0;
+    const int j = tid / S, sl = tid % S;
+    const int64_t s = int64_t(blockIdx.x) * S + sl;
+    const bool act = s < batch;
+    // lanes past the end of the batch shadow the last system (identical
+    // values, identical stores, no branches around memory operations)
+    const int64_t off = (act ? s : batch - 1) + int64_t(j) * M * ld;
+    const T *pa = A + off, *pb = B + off, *pc = C + off, *pd = D + off, *pe = E + off;
+    T *px = x + off;
+    auto F = [&](int field, int jj) -> T & { return buf[(field * P + jj) * S + sl]; };
+
+    // ---- forward sweep over the interior, inputs streamed LA rows ahead ----
+    T qa[LA], qb[LA], qc[LA], qd[LA], qe[LA], qf[LA];
+#pragma unroll
+    for (int k = 0; k < LA; ++k) {
+        const int64_t o = int64_t(k) * ld;
+        qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qd[k] = pd[o]; qe[k] = pe[o]; qf[k] = px[o];
+    }
+    T gam[m], del[m], g[m], u0[m], u1[m];
+    T gam1 = 0, gam2 = 0, del1 = 0, del2 = 0;      // factors of the two previous rows
+    T w01 = 0, w02 = 0, w11 = 0, w12 = 0;          // w_0, w_1 at rows i-1, i-2
+    T t0 = 0, t1 = 0, q00 = 0, q01 = 0, q10 = 0, q11 = 0;
+    T aL0 = 0, bL0 = 0, aL1 = 0;                   // C_L entries (rows 0, 1)
+    T rcp_m2 = 0, rcp_m1 = 0, beta_m1 = 0;
+    T eC0 = 0, dC1 = 0, eC1 = 0;                   // C_R entries (rows m-2, m-1)
+    bool bad = false;
+    const bool first_chunk = (j == 0);
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+        const int k = i % LA;
+        const T a_i = qa[k], b_i = qb[k], c_i = qc[k], d_i = qd[k], e_i = qe[k], f_i = qf[k];
+        {
+            const int64_t o = int64_t(i + LA < M ? i + LA : M - 1) * ld;
+            qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qd[k] = pd[o]; qe[k] = pe[o]; qf[k] = px[o];
+        }
+        // entries of E_j; the others are couplings to the interfaces
+        const T ai = (i >= 2) ? a_i : T(0);
+        const T bi = (i >= 1) ? b_i : T(0);
+        const T di = (i + 1 < m) ? d_i : T(0);
+        const T ei = (i + 2 < m) ? e_i : T(0);
+        if (i == 0) { aL0 = first_chunk ? T(0) : a_i; bL0 = first_chunk ? T(0) : b_i; }
+        if (i == 1) aL1 = first_chunk ? T(0) : a_i;
+        if (i == m - 2) eC0 = e_i;
+        if (i == m - 1) { dC1 = d_i; eC1 = e_i; }
+        const T beta = bi - ai * gam2;
+        const T alpha = c_i - ai * del2 - beta * gam1;
+        bad |= bad_pivot(alpha);
+        const T r = T(1) / alpha;
+        const T gm = (di - beta * del1) * r;
+        const T dl = ei * r;
+        const T gi = (f_i - ai * (i >= 2 ? g[i - 2] : T(0)) - beta * (i >= 1 ? g[i - 1] : T(0))) * r;
+        // U_L = L^{-1} C_L (right-hand sides nonzero in rows 0, 1 only)
+        const T cl0 = (i == 0) ? aL0 : T(0);
+        const T cl1 = (i == 0) ? bL0 : (i == 1) ? aL1 : T(0);
+        const T ui0 = (cl0 - ai * (i >= 2 ? u0[i - 2] : T(0)) - beta * (i >= 1 ? u0[i - 1] : T(0))) * r;
+        const T ui1 = (cl1 - ai * (i >= 2 ? u1[i - 2] : T(0)) - beta * (i >= 1 ? u1[i - 1] : T(0))) * r;
+        // w_k = R^{-T} e_k: rows 0 and 1 of R^{-1}
+        const T w0 = T(i == 0 ? 1 : 0) - gam1 * w01 - del2 * w02;
+        const T w1 = T(i == 1 ? 1 : 0) - gam1 * w11 - del2 * w12;
+        t0 += w0 * gi; t1 += w1 * gi;
+        q00 += w0 * ui0; q01 += w0 * ui1; q10 += w1 * ui0; q11 += w1 * ui1;
+        gam[i] = gm; del[i] = dl; g[i] = gi; u0[i] = ui0; u1[i] = ui1;
+        if (i == m - 2) rcp_m2 = r;
+        if (i == m - 1) { rcp_m1 = r; beta_m1 = beta; }
+        gam2 = gam1; gam1 = gm; del2 = del1; del1 = dl;
+        w02 = w01; w01 = w0; w12 = w11; w11 = w1;
+    }
+    // U_R = L^{-1} C_R: nonzero in the last two rows only
+    const T urA = eC0 * rcp_m2;                    // row m-2, column 0
+    const T urB = (dC1 - beta_m1 * urA) * rcp_m1;  // row m-1, column 0
+    const T urC = eC1 * rcp_m1;                    // row m-1, column 1
+    // last two rows of y = E^{-1} f, Z_L = E^{-1} C_L, Z_R = E^{-1} C_R
+    const T yl1 = g[m - 1], yl0 = g[m - 2] - gam[m - 2] * yl1;
+    const T zl01 = u0[m - 1], zl00 = u0[m - 2] - gam[m - 2] * zl01;   // column 0, rows m-2, m-1
+    const T zl11 = u1[m - 1], zl10 = u1[m - 2] - gam[m - 2] * zl11;   // column 1
+    const T zr01 = urB, zr00 = urA - gam[m - 2] * zr01;
+    const T zr11 = urC, zr10 = -gam[m - 2] * zr11;
+    // first two rows: y_k = w_k . g, Z_L[k][c] = w_k . U_L[c], Z_R[k][c] = w_k . U_R[c]
+    const T fr00 = w02 * urA + w01 * urB, fr01 = w01 * urC;       // w_0 at rows m-2 (w02), m-1 (w01)
+    const T fr10 = w12 * urA + w11 * urB, fr11 = w11 * urC;
+    // interface rows of this chunk (local rows m, m+1)
+    const int kR0 = m % LA, kR1 = (m + 1) % LA;
+    const bool last_chunk = (j == P - 1);
+    const T aR0 = qa[kR0], bR0 = qb[kR0], cR0 = qc[kR0], dR0 = qd[kR0];
+    const T eR0 = last_chunk ? T(0) : qe[kR0], fR0 = qf[kR0];
+    const T aR1 = qa[kR1], bR1 = qb[kR1], cR1 = qc[kR1];
+    const T dR1 = last_chunk ? T(0) : qd[kR1], eR1 = last_chunk ? T(0) : qe[kR1], fR1 = qf[kR1];
+
+    // ---- publish first-row quantities; build block row j ----
+    F(0, j) = t0; F(1, j) = t1;
+    F(2, j) = q00; F(3, j) = q01; F(4, j) = q10; F(5, j) = q11;
+    F(6, j) = fr00; F(7, j) = fr01; F(8, j) = fr10; F(9, j) = fr11;
+    __syncthreads();
+    T ny0 = 0, ny1 = 0, nzl00 = 0, nzl01 = 0, nzl10 = 0, nzl11 = 0, nzr00 = 0, nzr01 = 0, nzr10 = 0, nzr11 = 0;
+    if (!last_chunk) {
+        ny0 = F(0, j + 1); ny1 = F(1, j + 1);
+        nzl00 = F(2, j + 1); nzl01 = F(3, j + 1); nzl10 = F(4, j + 1); nzl11 = F(5, j + 1);
+        nzr00 = F(6, j + 1); nzr01 = F(7, j + 1); nzr10 = F(8, j + 1); nzr11 = F(9, j + 1);
+    }
+    // B_own = [[aR0, bR0], [0, aR1]] on interior rows (m-2, m-1);
+    // B_next = [[eR0, 0], [dR1, eR1]] on the next interior rows (0, 1)
+    M22<T> Dj, Lj, Uj;
+    T rj0, rj1;
+    {
+        const M22<T> own{aR0, bR0, T(0), aR1}, nxt{eR0, T(0), dR1, eR1};
+        const M22<T> ZRl{zr00, zr10, zr01, zr11};       // rows (m-2, m-1) x columns (0, 1)
+        const M22<T> ZLl{zl00, zl10, zl01, zl11};
+        const M22<T> ZLn{nzl00, nzl01, nzl10, nzl11};   // next chunk rows (0, 1) x columns
+        const M22<T> ZRn{nzr00, nzr01, nzr10, nzr11};
+        const M22<T> p1 = mul(own, ZRl), p2 = mul(nxt, ZLn), p3 = mul(own, ZLl), p4 = mul(nxt, ZRn);
+        Dj = {cR0 - p1.a - p2.a, dR0 - p1.b - p2.b, bR1 - p1.c - p2.c, cR1 - p1.d - p2.d};
+        Lj = {-p3.a, -p3.b, -p3.c, -p3.d};
+        Uj = {-p4.a, -p4.b, -p4.c, -p4.d};
+        rj0 = fR0 - (aR0 * yl0 + bR0 * yl1) - eR0 * ny0;
+        rj1 = fR1 - aR1 * yl1 - (dR1 * ny0 + eR1 * ny1);
+    }
+    __syncthreads();
+    // ---- block cyclic reduction across the P chunks of the system ----
+    for (int h = 1; h < P; h <<= 1) {
+        T det;
+        const M22<T> Di = inv(Dj, det);
+        bad |= bad_pivot(det);
+        F(0, j) = Lj.a; F(1, j) = Lj.b; F(2, j) = Lj.c; F(3, j) = Lj.d;
+        F(4, j) = Di.a; F(5, j) = Di.b; F(6, j) = Di.c; F(7, j) = Di.d;
+        F(8, j) = Uj.a; F(9, j) = Uj.b; F(10, j) = Uj.c; F(11, j) = Uj.d;
+        F(12, j) = rj0; F(13, j) = rj1;
+        __syncthreads();
+        M22<T> nD = Dj, nL{0, 0, 0, 0}, nU{0, 0, 0, 0};
+        T nr0 = rj0, nr1 = rj1;
+        if (j - h >= 0) {
+            const int q = j - h;
+            const M22<T> Lq{F(0, q), F(1, q), F(2, q), F(3, q)};
+            const M22<T> Iq{F(4, q), F(5, q), F(6, q), F(7, q)};
+            const M22<T> Uq{F(8, q), F(9, q), F(10, q), F(11, q)};
+            const T rq0 = F(12, q), rq1 = F(13, q);
+            const M22<T> al0 = mul(Lj, Iq);
+            const M22<T> al{-al0.a, -al0.b, -al0.c, -al0.d};
+            nL = mul(al, Lq);
+            const M22<T> au = mul(al, Uq);
+            nD = {nD.a + au.a, nD.b + au.b, nD.c + au.c, nD.d + au.d};
+            nr0 += al.a * rq0 + al.b * rq1;
+            nr1 += al.c * rq0 + al.d * rq1;
+        }
+        if (j + h < P) {
+            const int q = j + h;
+            const M22<T> Lq{F(0, q), F(1, q), F(2, q), F(3, q)};
+            const M22<T> Iq{F(4, q), F(5, q), F(6, q), F(7, q)};
+            const M22<T> Uq{F(8, q), F(9, q), F(10, q), F(11, q)};
+            const T rq0 = F(12, q), rq1 = F(13, q);
+            const M22<T> ga0 = mul(Uj, Iq);
+            const M22<T> ga{-ga0.a, -ga0.b, -ga0.c, -ga0.d};
+            nU = mul(ga, Uq);
+            const M22<T> gl = mul(ga, Lq);
+            nD = {nD.a + gl.a, nD.b + gl.b, nD.c + gl.c, nD.d + gl.d};
+            nr0 += ga.a * rq0 + ga.b * rq1;
+            nr1 += ga.c * rq0 + ga.d * rq1;
+        }
+        Dj = nD; Lj = nL; Uj = nU; rj0 = nr0; rj1 = nr1;
+        __syncthreads();
+    }
+    T det;
+    const M22<T> Dinv = inv(Dj, det);
+    bad |= bad_pivot(det);
+    const T xr0 = Dinv.a * rj0 + Dinv.b * rj1, xr1 = Dinv.c * rj0 + Dinv.d * rj1;
+    F(0, j) = xr0; F(1, j) = xr1;
+    if (bad) atomicOr(&flag[sl], 1);
+    __syncthreads();
+    const T xl0 = first_chunk ? T(0) : F(0, j - 1);
+    const T xl1 = first_chunk ? T(0) : F(1, j - 1);
+    if (flag[sl]) {
+        // a chunk pivot or an interface block broke down: redo this system
+        // with the sequential elimination, which also fixes info
+        if (first_chunk && act) {
+            const int32_t r = seq_penta_solve<T>(int64_t(P) * M, ld, A + s, B + s, C + s, D + s,
+                                                 E + s, x + s, work + s);
+            if (info) info[s] = r;
+        }
+        return;
+    }
+    if (first_chunk && act && info) info[s] = 0;
+    // ---- back substitution x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j) ----
+    T x1 = 0, x2 = 0;
+#pragma unroll
+    for (int i = m - 1; i >= 0; --i) {
+        T v = g[i] - u0[i] * xl0 - u1[i] * xl1;
+        if (i == m - 2) v -= urA * xr0;
+        if (i == m - 1) v -= urB * xr0 + urC * xr1;
+        if (i + 1 < m) v -= gam[i] * x1;
+        if (i + 2 < m) v -= del[i] * x2;
+        px[int64_t(i) * ld] = v;
+        x2 = x1; x1 = v;
+    }
+    px[int64_t(m) * ld] = xr0;
+    px[int64_t(m + 1) * ld] = xr1;
+}
+
+// Chunked path applies when n = P * 16 with 2 <= P <= 64.
+int spike_chunks(int64_t n)
+{
+    if (n % 16 != 0) return 0;
+    const int64_t P = n / 16;
+    return (P >= 2 && P <= 64) ? int(P) : 0;
+}
+
+template <typename T, int S>
+static void launch_spike_s(int P, int64_t batch, int64_t ld, const void *a, const void *b,
+                           const void *c, const void *d, const void *e, void *x, void *work,
+                           int32_t *info, hipStream_t st)
+{
+    const size_t lds = size_t(14) * P * S * sizeof(T) + S * sizeof(int32_t);
+    const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
+    hipLaunchKernelGGL((k_penta_spike<T, 16, S>), grid, block, lds, st, P, batch, ld,
+                       (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
+                       (T *)x, (T *)work, info);
+}
+
+template <typename T>
+bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
+                              const void *c, const void *d, const void *e, void *x, void *work,
+                              int32_t *info, hipStream_t st)
+{
+    const int P = spike_chunks(n);
+    if (!P) BPS_FAIL(BPS_ENOTSUP, "chunked pentadiagonal solve needs n = 16 P, 2 <= P <= 64");
+    if (batch == 0) return BPS_OK;
+    // 16 systems per workgroup (one 128-byte fp64 row segment); 32 when the
+    // systems are short so that a workgroup fills a wavefront, 8 when they
+    // are long so that it stays within 1024 lanes and 64 KiB of LDS
+    if (P < 4)
+        launch_spike_s<T, 32>(P, batch, ld, a, b, c, d, e, x, work, info, st);
+    else if (P <= 32)
+        launch_spike_s<T, 16>(P, batch, ld, a, b, c, d, e, x, work, info, st);
+    else
+        launch_spike_s<T, 8>(P, batch, ld, a, b, c, d, e, x, work, info, st);
+    BPS_LAUNCHED("k_penta_spike");
+    return BPS_OK;
+}
+
+template bps_status launch_penta_spike<float>(int64_t, int64_t, int64_t, const void *, const void *,
+                                              const void *, const void *, const void *, void *,
+                                              void *, int32_t *, hipStream_t);
+template bps_status launch_penta_spike<double>(int64_t, int64_t, int64_t, const void *, const void *,
+                                               const void *, const void *, const void *, void *,
+                                               void *, int32_t *, hipStream_t);
+
+}  // namespace bps

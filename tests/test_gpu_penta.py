@@ -31,7 +31,10 @@ def _oracle(pb, dt, cols=None, cyclic=False):
 
 
 @pytest.mark.parametrize("dt", DTYPES)
-@pytest.mark.parametrize("n,batch", [(4, 1), (5, 3), (6, 64), (7, 65), (33, 129), (512, 1000)])
+@pytest.mark.parametrize("n,batch", [(4, 1), (5, 3), (6, 64), (7, 65), (33, 129), (512, 1000),
+                                     # 16-row chunks: 2, 3, 4, 31, 32, 33, 64 chunks per system
+                                     (32, 7), (48, 33), (64, 100), (496, 17), (512, 1),
+                                     (528, 50), (1024, 40), (1040, 9)])
 def test_fused_matches_oracle(dt, n, batch):
     print(f"fused n={n} batch={batch} {dt}", flush=True)
     pb = W.penta_dominant(n, batch, rng=np.random.default_rng(n * 1000 + batch))
@@ -91,8 +94,9 @@ def test_shared_coefficients(dt, cyclic):
     assert int(host(info)[0]) == 0
 
 
-def test_leading_dimension_larger_than_batch():
-    n, batch, ld = 40, 70, 96
+@pytest.mark.parametrize("n", [40, 64])
+def test_leading_dimension_larger_than_batch(n):
+    batch, ld = 70, 96
     pb = W.penta_dominant(n, ld, rng=np.random.default_rng(5))
     a, b, c, d, e = (dev(v) for v in pb.diagonals)
     x = dev(pb.f)
@@ -104,9 +108,10 @@ def test_leading_dimension_larger_than_batch():
     np.testing.assert_array_equal(out[:, batch:], pb.f[:, batch:])   # untouched columns
 
 
-def test_outside_entries_are_ignored():
+@pytest.mark.parametrize("n", [16, 32])
+def test_outside_entries_are_ignored(n):
     """a_0, a_1, b_0, d_{n-1}, e_{n-2}, e_{n-1} lie outside the matrix."""
-    n, batch = 16, 64
+    batch = 64
     pb = W.penta_dominant(n, batch, rng=np.random.default_rng(6))
     junk = [v.copy() for v in pb.diagonals]
     junk[0][:2] = 1e300; junk[1][0] = np.nan; junk[3][-1] = np.inf; junk[4][-2:] = -7.0
@@ -141,6 +146,32 @@ def test_breakdown_reported_in_info():
     ok = np.delete(np.arange(batch), [3, 10])
     ref, _ = _oracle(pb, torch.float64, cols=ok)
     assert relerr_cols(host(x)[:, ok], ref) <= 1e-10
+
+
+def test_breakdown_in_chunked_solve():
+    """n = 512 (32 chunks of 16 rows): a zero or non-finite pivot of the
+    sequential elimination is reported at its row as the oracle does; a
+    zero pivot met only by the chunked elimination (c = 0 at the first row
+    of a chunk, where the sequential pivot is nonzero) still gives the
+    oracle's solution and info 0."""
+    n, batch = 512, 70
+    pb = W.penta_dominant(n, batch, rng=np.random.default_rng(18))
+    c = pb.c.copy()
+    c[0, 3] = 0.0                          # sequential alpha_0 = 0
+    c[200, 10] = np.nan                    # non-finite pivot at row 200
+    c[32, 20] = 0.0                        # chunk-local pivot only
+    c[16 * 31, 21] = 0.0                   # first row of the last chunk
+    x = dev(pb.f)
+    info = info_buf(batch)
+    work = buf(bps.bps_penta_work_bytes(n, batch, batch))
+    bps.penta_factor_solve_batch(dev(pb.a), dev(pb.b), dev(c), dev(pb.d), dev(pb.e), x, work, info)
+    inf = host(info).astype(int)
+    pb2 = W.PentaBatch(pb.a, pb.b, c, pb.d, pb.e, pb.f)
+    ref2, rinfo = _oracle(pb2, torch.float64)
+    assert inf[3] == 1 and inf[10] == 201
+    np.testing.assert_array_equal(inf, rinfo)
+    ok = np.delete(np.arange(batch), [3, 10])
+    assert relerr_cols(host(x)[:, ok], ref2[:, ok]) <= 1e-10
 
 
 def test_deterministic_bitwise():
