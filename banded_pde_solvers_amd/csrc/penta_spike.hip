@@ -98,14 +98,19 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
               T *__restrict__ x, T *__restrict__ work, int32_t *__restrict__ info)
 {
     constexpr int m = M - 2;            // interior rows of a chunk
-    constexpr int LA = 4;               // rows of look-ahead for the streamed inputs
     extern __shared__ unsigned char lds_raw[];
     T *buf = reinterpret_cast<T *>(lds_raw);          // [field][P][S]
     int32_t *flag = reinterpret_cast<int32_t *>(buf + 14 * P * S);
     const int tid = threadIdx.x;
     if (tid < S) flag[tid] = 0;
     const int j = tid / S, sl = tid % S;
-    const int64_t s = int64_t(blockIdx.x) * S + sl;
+    // workgroups are dispatched round-robin over the 8 XCDs: give the ones
+    // that one XCD runs back to back neighbouring systems, so that a
+    // 128-byte line shared by two workgroups (row segments of 64 bytes or
+    // less) is fetched once, through one L2
+    const unsigned nb = gridDim.x, bid = blockIdx.x, full = nb & ~7u;
+    const unsigned tile = bid < full ? (bid & 7u) * (full >> 3) + (bid >> 3) : bid;
+    const int64_t s = int64_t(tile) * S + sl;
     const bool act = s < batch;
     // lanes past the end of the batch shadow the last system (identical
     // values, identical stores, no branches around memory operations)
@@ -115,6 +120,7 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     auto F = [&](int field, int jj) -> T & { return buf[(field * P + jj) * S + sl]; };
 
     // ---- forward sweep over the interior, inputs streamed LA rows ahead ----
+    constexpr int LA = 4;
     T qa[LA], qb[LA], qc[LA], qd[LA], qe[LA], qf[LA];
 #pragma unroll
     for (int k = 0; k < LA; ++k) {
@@ -184,7 +190,7 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     const T fr00 = w02 * urA + w01 * urB, fr01 = w01 * urC;       // w_0 at rows m-2 (w02), m-1 (w01)
     const T fr10 = w12 * urA + w11 * urB, fr11 = w11 * urC;
     // interface rows of this chunk (local rows m, m+1)
-    const int kR0 = m % LA, kR1 = (m + 1) % LA;
+    constexpr int kR0 = m % LA, kR1 = (m + 1) % LA;
     const bool last_chunk = (j == P - 1);
     const T aR0 = qa[kR0], bR0 = qb[kR0], cR0 = qc[kR0], dR0 = qd[kR0];
     const T eR0 = last_chunk ? T(0) : qe[kR0], fR0 = qf[kR0];
@@ -308,9 +314,9 @@ int spike_chunks(int64_t n)
 }
 
 template <typename T, int S>
-static void launch_spike_s(int P, int64_t batch, int64_t ld, const void *a, const void *b,
-                           const void *c, const void *d, const void *e, void *x, void *work,
-                           int32_t *info, hipStream_t st)
+static void launch_spike(int P, int64_t batch, int64_t ld, const void *a, const void *b,
+                         const void *c, const void *d, const void *e, void *x, void *work,
+                         int32_t *info, hipStream_t st)
 {
     const size_t lds = size_t(14) * P * S * sizeof(T) + S * sizeof(int32_t);
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
@@ -324,18 +330,17 @@ bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, const void *
                               const void *c, const void *d, const void *e, void *x, void *work,
                               int32_t *info, hipStream_t st)
 {
-    const int P = spike_chunks(n);
-    if (!P) BPS_FAIL(BPS_ENOTSUP, "chunked pentadiagonal solve needs n = 16 P, 2 <= P <= 64");
+    if (!spike_chunks(n))
+        BPS_FAIL(BPS_ENOTSUP, "chunked pentadiagonal solve needs n = 16 P, 2 <= P <= 64");
     if (batch == 0) return BPS_OK;
-    // 16 systems per workgroup (one 128-byte fp64 row segment); 32 when the
-    // systems are short so that a workgroup fills a wavefront, 8 when they
-    // are long so that it stays within 1024 lanes and 64 KiB of LDS
-    if (P < 4)
-        launch_spike_s<T, 32>(P, batch, ld, a, b, c, d, e, x, work, info, st);
-    else if (P <= 32)
-        launch_spike_s<T, 16>(P, batch, ld, a, b, c, d, e, x, work, info, st);
-    else
-        launch_spike_s<T, 8>(P, batch, ld, a, b, c, d, e, x, work, info, st);
+    // 16 systems per workgroup (a 128-byte row segment in fp64, 64 in
+    // fp32); 32 when the systems are short so that a workgroup fills a
+    // wavefront, 8 when they are long so that it stays within 512 lanes and
+    // 64 KiB of LDS
+    const int P = int(n / 16);
+    if (P < 4) launch_spike<T, 32>(P, batch, ld, a, b, c, d, e, x, work, info, st);
+    else if (P <= 32) launch_spike<T, 16>(P, batch, ld, a, b, c, d, e, x, work, info, st);
+    else launch_spike<T, 8>(P, batch, ld, a, b, c, d, e, x, work, info, st);
     BPS_LAUNCHED("k_penta_spike");
     return BPS_OK;
 }
