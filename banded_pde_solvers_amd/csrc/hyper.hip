@@ -87,8 +87,11 @@ struct Dot2 {
     __device__ double value() const { return p + s; }
 };
 
-constexpr int kResSys = 16;     // systems per workgroup (one 128-byte row segment)
 constexpr int kResMaxP = 16;    // chunks per system supported by the resident kernel
+// A workgroup of the resident kernel is one wavefront: 64 / P systems times
+// P chunks.  Its barriers then cost next to nothing, and the waves sharing a
+// SIMD hide each other's latencies without waiting on one another.
+__host__ __device__ constexpr int res_systems(int P) { return kWave / P; }
 
 // coefficient block written by the set-up kernel, read with uniform loads:
 //   rows i < m: [ralpha, beta, w0, w1, gamma, delta, UL0, UL1]   (8 doubles)
@@ -254,18 +257,23 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
 }
 
 template <int M, int P>
-__global__ void __launch_bounds__(kResSys * P) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3)))
 k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__restrict__ coef,
                  double *__restrict__ C)
 {
     constexpr int m = M - 2;
-    constexpr int S = kResSys;
+    constexpr int S = res_systems(P);
     __shared__ double tbuf[2][P][S][4];
     __shared__ double rbuf[2][2 * P][S][2];   // r_k stored at k and k + P
     __shared__ double xbuf[2][P][S][2];
     const int tid = threadIdx.x;
     const int j = tid / S, sl = tid % S;
-    const int64_t s = int64_t(blockIdx.x) * S + sl;
+    // workgroups are dispatched round-robin over the 8 XCDs: the ones one
+    // XCD runs back to back take neighbouring systems, so that row segments
+    // narrower than a 128-byte line share it through one L2
+    const unsigned nb = gridDim.x, bid = blockIdx.x, full = nb & ~7u;
+    const unsigned tile = bid < full ? (bid & 7u) * (full >> 3) + (bid >> 3) : bid;
+    const int64_t s = int64_t(tile) * S + sl;
     const bool act = s < batch;
     // lanes past the end of the batch compute on a copy of the last system
     // and store nothing
@@ -329,6 +337,7 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
 #pragma unroll
             for (int q = 0; q < P; ++q) {
                 if (q >= 4 && q % 4 == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
                     asm volatile("" : "+s"(tg) : "v"(r1));
                     T = (cdouble *)tg;
                 }
@@ -394,8 +403,9 @@ static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, 
 {
     hipLaunchKernelGGL((k_hyper_resident_setup<M, P>), dim3(1), dim3(64), 0, st, sigma, coef);
     if (nsteps == 0) return;
-    const unsigned grid = unsigned((batch + kResSys - 1) / kResSys);
-    hipLaunchKernelGGL((k_hyper_resident<M, P>), dim3(grid), dim3(kResSys * P), 0, st, batch, ld,
+    constexpr int S = res_systems(P);
+    const unsigned grid = unsigned((batch + S - 1) / S);
+    hipLaunchKernelGGL((k_hyper_resident<M, P>), dim3(grid), dim3(S * P), 0, st, batch, ld,
                        nsteps, (const double *)coef, C);
 }
 
