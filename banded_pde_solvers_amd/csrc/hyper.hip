@@ -108,6 +108,11 @@ __device__ __forceinline__ double read_lane(double v, int lane)
     return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
 }
 
+// One wavefront.  The serial recurrences run in every lane at once (lane t
+// carries coupling vector t & 7) with the running values in registers, and
+// their loops are unrolled so that the LDS reads they need are issued ahead
+// of the recurrence: the set-up is then bound by arithmetic latency rather
+// than by LDS round trips.
 template <int M, int P>
 __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, double *__restrict__ coef)
 {
@@ -116,7 +121,7 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     __shared__ double ra[m], be[m], ga[m], de[m];
     __shared__ double vec[8][m];        // UL0, UL1, w0, w1, ZL0, ZL1, ZR0, ZR1
     __shared__ double res[4][m];
-    __shared__ double aug[n2][w];
+    __shared__ double blk[3][2][2];     // blocks of S on interface offsets 0, +1, -1
     const int t = threadIdx.x;
     const double a = sigma, b = -4.0 * sigma, c = 1.0 + 6.0 * sigma, d = -4.0 * sigma, e = sigma;
     auto Ea = [&](int i) { return i >= 2 ? a : 0.0; };
@@ -127,78 +132,94 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     auto CL = [&](int k, int i) { return k == 0 ? (i == 0 ? a : 0.0) : (i == 0 ? b : i == 1 ? a : 0.0); };
     auto CR = [&](int k, int i) { return k == 0 ? (i == m - 2 ? e : i == m - 1 ? d : 0.0)
                                                 : (i == m - 1 ? e : 0.0); };
-    // ---- factor E = L R (one lane; the pentadiagonal steps of the page) ----
-    if (t == 0) {
-        double g1 = 0, g2 = 0, d1 = 0, d2 = 0;
+    // lane t < 8 builds coupling vector t (lanes 8.. repeat lane t & 7 and
+    // store nothing):
+    //   0,1  U_L = L^{-1} C_L      2,3  w_k = R^{-T} e_k
+    //   4,5  Z_L = E^{-1} C_L      6,7  Z_R = E^{-1} C_R
+    const int role = t & 7, k = role & 1;
+    const bool is_w = (role == 2 || role == 3), is_z = role >= 4, use_cr = role >= 6;
+    const bool keeper = t < 8;
+    double *my = vec[role];
+    // the right-hand side of lane t is nonzero in rows 0, 1, m-2, m-1 only
+    const double rh0 = is_w ? (k == 0 ? 1.0 : 0.0) : use_cr ? CR(k, 0) : CL(k, 0);
+    const double rh1 = is_w ? (k == 1 ? 1.0 : 0.0) : use_cr ? CR(k, 1) : CL(k, 1);
+    const double rhA = is_w ? 0.0 : use_cr ? CR(k, m - 2) : CL(k, m - 2);
+    const double rhB = is_w ? 0.0 : use_cr ? CR(k, m - 1) : CL(k, m - 1);
+    // ---- factor E = L R (the pentadiagonal steps of the page) and, in the
+    // same sweep, the forward recurrence of each lane's vector ----
+    {
+#pragma clang fp contract(fast)
+        double g1 = 0, g2 = 0, d1 = 0, d2 = 0;      // gamma, delta of rows i-1, i-2
+        double p1 = 0, p2 = 0;                      // vector values of rows i-1, i-2
+#pragma unroll
         for (int i = 0; i < m; ++i) {
             const double beta = Eb(i) - Ea(i) * g2;
             const double alpha = c - Ea(i) * d2 - beta * g1;
             const double r = 1.0 / alpha;
             const double gam = (Ed(i) - beta * d1) * r, del = Ee(i) * r;
-            ra[i] = r; be[i] = beta; ga[i] = gam; de[i] = del;
+            if (t == 0) { ra[i] = r; be[i] = beta; ga[i] = gam; de[i] = del; }
+            // L^{-1} rhs, or R^{-T} e_k (R^T is unit lower with gamma, delta)
+            const double rhs = i == 0 ? rh0 : i == 1 ? rh1 : i == m - 2 ? rhA : i == m - 1 ? rhB : 0.0;
+            const double lv = (rhs - Ea(i) * p2 - beta * p1) * r;
+            const double wv = rhs - (i >= 1 ? g1 : 0.0) * p1 - (i >= 2 ? d2 : 0.0) * p2;
+            const double x = is_w ? wv : lv;
+            if (keeper) my[i] = x;
+            p2 = p1; p1 = x;
             g2 = g1; g1 = gam; d2 = d1; d1 = del;
         }
     }
     __syncthreads();
-    // triangular solves with the running values carried in registers
-    auto Lsolve = [&](double *v) {           // v <- L^{-1} v
-        double p1 = 0.0, p2 = 0.0;
-        for (int i = 0; i < m; ++i) {
-            const double g = (v[i] - Ea(i) * p2 - be[i] * p1) * ra[i];
-            v[i] = g; p2 = p1; p1 = g;
-        }
-    };
-    auto Rsolve = [&](double *v) {           // v <- R^{-1} v
+    // ---- Z = R^{-1} U for lanes 4..7 ----
+    {
+#pragma clang fp contract(fast)
         double q1 = 0.0, q2 = 0.0;
+#pragma unroll 8
         for (int i = m - 1; i >= 0; --i) {
-            const double x = v[i] - ga[i] * q1 - de[i] * q2;
-            v[i] = x; q2 = q1; q1 = x;
-        }
-    };
-    // ---- coupling vectors (eight independent lanes) ----
-    if (t < 8) {
-        double *v = vec[t];
-        const int k = t & 1;
-        for (int i = 0; i < m; ++i)
-            v[i] = (t < 2 || (t >= 4 && t < 6)) ? CL(k, i) : (t >= 6) ? CR(k, i) : (i == k ? 1.0 : 0.0);
-        if (t == 2 || t == 3) {              // w_k = R^{-T} e_k
-            double q1 = 0.0, q2 = 0.0;
-            for (int i = 0; i < m; ++i) {
-                const double y = v[i] - (i >= 1 ? ga[i - 1] : 0.0) * q1 - (i >= 2 ? de[i - 2] : 0.0) * q2;
-                v[i] = y; q2 = q1; q1 = y;
-            }
-        } else {
-            Lsolve(v);                       // U = L^{-1} C
-            if (t >= 4) Rsolve(v);           // Z = E^{-1} C
+            const double x = my[i] - ga[i] * q1 - de[i] * q2;
+            if (keeper && is_z) my[i] = x;
+            q2 = q1; q1 = x;
         }
     }
     __syncthreads();
     // ---- one refinement step of Z: residual C - E Z with compensated sums ----
     for (int idx = t; idx < 4 * m; idx += blockDim.x) {
-        const int k = idx / m, i = idx % m;
-        const double *z = vec[4 + k];
+        const int kk = idx / m, i = idx % m;
+        const double *z = vec[4 + kk];
         Dot2 acc;
-        acc.add(k < 2 ? CL(k & 1, i) : CR(k & 1, i), 1.0);
+        acc.add(kk < 2 ? CL(kk & 1, i) : CR(kk & 1, i), 1.0);
         if (i >= 2) acc.add(-Ea(i), z[i - 2]);
         if (i >= 1) acc.add(-Eb(i), z[i - 1]);
         acc.add(-c, z[i]);
         if (i + 1 < m) acc.add(-Ed(i), z[i + 1]);
         if (i + 2 < m) acc.add(-Ee(i), z[i + 2]);
-        res[k][i] = acc.value();
+        res[kk][i] = acc.value();
     }
     __syncthreads();
     if (t < 4) {
-        Lsolve(res[t]);
-        Rsolve(res[t]);
-        for (int i = 0; i < m; ++i) vec[4 + t][i] += res[t][i];
+#pragma clang fp contract(fast)
+        // lanes 0..3 solve E dz = residual in place and correct Z
+        double *rv = res[t];
+        double p1 = 0.0, p2 = 0.0;
+#pragma unroll 8
+        for (int i = 0; i < m; ++i) {
+            const double g = (rv[i] - Ea(i) * p2 - be[i] * p1) * ra[i];
+            rv[i] = g; p2 = p1; p1 = g;
+        }
+        double q1 = 0.0, q2 = 0.0;
+#pragma unroll 8
+        for (int i = m - 1; i >= 0; --i) {
+            const double x = rv[i] - ga[i] * q1 - de[i] * q2;
+            vec[4 + t][i] += x; q2 = q1; q1 = x;
+        }
     }
     __syncthreads();
-    // ---- Schur complement S (2P x 2P), compensated, into aug = [S | I] ----
+    // ---- Schur complement S (2P x 2P, block-circulant): the three nonzero
+    // 2x2 blocks of block row 0, compensated, by lanes 0..11 ----
     auto ZL = [&](int q) -> const double * { return q ? vec[5] : vec[4]; };
     auto ZR = [&](int q) -> const double * { return q ? vec[7] : vec[6]; };
-    for (int idx = t; idx < n2 * n2; idx += blockDim.x) {
-        const int row = idx / n2, col = idx % n2;
-        const int J = row >> 1, r = row & 1, K = col >> 1, q = col & 1;
+    if (t < 12) {
+        const int bi = t >> 2, r = (t >> 1) & 1, q = t & 1;
+        const int K = bi == 0 ? 0 : bi == 1 ? 1 % P : P - 1;   // column block, row block J = 0
         Dot2 acc;
         // rows of B_own (interface j on interior j) and B_next (interface j-1 on interior j)
         auto own = [&](const double *z) {           // B_own[r] . z
@@ -209,14 +230,13 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
             if (r == 0) acc.add(-e, z[0]);
             else { acc.add(-d, z[0]); acc.add(-e, z[1]); }
         };
-        if (K == J) {
+        if (K == 0) {
             acc.add(r == 0 ? (q == 0 ? c : d) : (q == 0 ? b : c), 1.0);
             own(ZR(q)); nxt(ZL(q));
         }
-        if (K == (J + P - 1) % P) own(ZL(q));
-        if (K == (J + 1) % P) nxt(ZR(q));
-        aug[row][col] = acc.value();
-        aug[row][n2 + col] = (row == col) ? 1.0 : 0.0;
+        if (K == P - 1) own(ZL(q));
+        if (K == 1) nxt(ZR(q));
+        blk[bi][r][q] = acc.value();
     }
     __syncthreads();
     // ---- Gauss-Jordan on [S | I] without pivoting (S is symmetric positive
@@ -224,15 +244,28 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     // column t in registers; pivot column entries are broadcast by readlane.
     double cv[n2];
 #pragma unroll
-    for (int i = 0; i < n2; ++i) cv[i] = (t < w) ? aug[i][t] : 0.0;
+    for (int i = 0; i < n2; ++i) {
+        const int J = i >> 1, r = i & 1;
+        double val = 0.0;
+        if (t < n2) {
+            const int K = t >> 1, q = t & 1, off = (K - J + P) % P;
+            if (off == 0) val = blk[0][r][q];
+            else if (off == 1) val = blk[1][r][q];
+            else if (off == P - 1) val = blk[2][r][q];
+        } else if (t < w) {
+            val = (i == t - n2) ? 1.0 : 0.0;
+        }
+        cv[i] = val;
+    }
 #pragma unroll
-    for (int k = 0; k < n2; ++k) {
+    for (int kp = 0; kp < n2; ++kp) {
+#pragma clang fp contract(fast)
         double f[n2];
 #pragma unroll
-        for (int i = 0; i < n2; ++i) f[i] = read_lane(cv[i], k);
-        const double pk = cv[k] / f[k];
+        for (int i = 0; i < n2; ++i) f[i] = read_lane(cv[i], kp);
+        const double pk = cv[kp] / f[kp];
 #pragma unroll
-        for (int i = 0; i < n2; ++i) cv[i] = (i == k) ? pk : cv[i] - f[i] * pk;
+        for (int i = 0; i < n2; ++i) cv[i] = (i == kp) ? pk : cv[i] - f[i] * pk;
     }
     // ---- outputs ----
     for (int idx = t; idx < m; idx += blockDim.x) {
