@@ -323,31 +323,56 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
     const int jm1 = (j == 0) ? P - 1 : j - 1;
     for (int64_t step = 0; step < nsteps; ++step) {
         const int bf = int(step & 1);
-        // Per-row coefficients come from the scalar cache through a pointer
-        // in the constant address space (scalar loads).  The empty asm
-        // statements re-derive that pointer every few rows with a dependence
-        // on a value computed a few rows earlier: otherwise the compiler
-        // hoists all 8(M-2) loads (out of the step loop, or to the top of
-        // the step) and spills them from scalar registers.
+        // Per-row coefficients come from the scalar cache (uniform loads
+        // through a pointer in the constant address space), KB rows at a
+        // time, one batch ahead: the loads of batch k+1 are issued right after
+        // batch k has arrived and before batch k is used.  Scalar loads
+        // complete out of order, so any wait on one is a wait on all; the
+        // empty asm statements place that wait (they read batch k) before
+        // the next batch is requested, and re-derive the pointer so that the
+        // compiler neither hoists the loads out of the step loop nor sinks
+        // them to their uses.
         typedef const __attribute__((address_space(4))) double cdouble;
+        constexpr int KB = 2;
+        static_assert(m % KB == 0, "rows per chunk interior must be a multiple of the batch");
         const double *cg = coef;
         asm volatile("" : "+s"(cg));
         cdouble *cf = (cdouble *)cg;
+        double cb[2][KB][4];
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cb[0][r][q] = cf[8 * r + q];
         // forward: g = L^{-1} f_interior, and y_0, y_1 = w . g
         double t0 = 0.0, t1 = 0.0;
 #pragma unroll
-        for (int i = 0; i < m; ++i) {
-            if (i >= 8 && i % 4 == 0) {
-                asm volatile("" : "+s"(cg) : "v"(x[i - 4]));
-                cf = (cdouble *)cg;
+        for (int k = 0; k < m / KB; ++k) {
+            const int cur = k & 1;
+#pragma unroll
+            for (int r = 0; r < KB; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) asm volatile("" ::"s"(cb[cur][r][q]));
+            asm volatile("" : "+s"(cg));
+            cf = (cdouble *)cg;
+            if (k + 1 < m / KB) {
+#pragma unroll
+                for (int r = 0; r < KB; ++r)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) cb[cur ^ 1][r][q] = cf[8 * ((k + 1) * KB + r) + q];
             }
-            double g = x[i];
-            if (i >= 2) g -= a * x[i - 2];
-            if (i >= 1) g -= cf[8 * i + 1] * x[i - 1];
-            g *= cf[8 * i + 0];
-            x[i] = g;
-            t0 += cf[8 * i + 2] * g;
-            t1 += cf[8 * i + 3] * g;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < KB; ++r) {
+                const int i = k * KB + r;
+                const double *c4 = cb[cur][r];     // [1/alpha, beta, w0, w1]
+                double g = x[i];
+                if (i >= 2) g -= a * x[i - 2];
+                if (i >= 1) g -= c4[1] * x[i - 1];
+                g *= c4[0];
+                x[i] = g;
+                t0 += c4[2] * g;
+                t1 += c4[3] * g;
+            }
         }
         const double yR1 = x[m - 1];
         const double yR0 = x[m - 2] - cf[8 * (m - 2) + 4] * yR1;
@@ -387,19 +412,40 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         const double l0 = xbuf[bf][jm1][sl][0], l1 = xbuf[bf][jm1][sl][1];
         asm volatile("" : "+s"(cg) : "v"(l1));
         cf = (cdouble *)cg;
-        // backward: x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j)
+        // backward: x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j), coefficient
+        // batches of KB rows from the bottom up, loaded one batch ahead
+#pragma unroll
+        for (int r = 0; r < KB; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cb[0][r][q] = cf[8 * (m - 1 - r) + 4 + q];
         x[m - 2] -= URa * r0;
         x[m - 1] -= URb * r0 + URc * r1;
 #pragma unroll
-        for (int i = m - 1; i >= 0; --i) {
-            if (i <= m - 9 && i % 4 == 3) {
-                asm volatile("" : "+s"(cg) : "v"(x[i + 5]));
-                cf = (cdouble *)cg;
+        for (int k = 0; k < m / KB; ++k) {
+            const int cur = k & 1;
+#pragma unroll
+            for (int r = 0; r < KB; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) asm volatile("" ::"s"(cb[cur][r][q]));
+            asm volatile("" : "+s"(cg));
+            cf = (cdouble *)cg;
+            if (k + 1 < m / KB) {
+#pragma unroll
+                for (int r = 0; r < KB; ++r)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        cb[cur ^ 1][r][q] = cf[8 * (m - 1 - (k + 1) * KB - r) + 4 + q];
             }
-            double v = x[i] - cf[8 * i + 6] * l0 - cf[8 * i + 7] * l1;
-            if (i + 1 < m) v -= cf[8 * i + 4] * x[i + 1];
-            if (i + 2 < m) v -= cf[8 * i + 5] * x[i + 2];
-            x[i] = v;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < KB; ++r) {
+                const int i = m - 1 - (k * KB + r);
+                const double *c4 = cb[cur][r];     // [gamma, delta, UL0, UL1]
+                double v = x[i] - c4[2] * l0 - c4[3] * l1;
+                if (i + 1 < m) v -= c4[0] * x[i + 1];
+                if (i + 2 < m) v -= c4[1] * x[i + 2];
+                x[i] = v;
+            }
         }
         x[m] = r0;
         x[m + 1] = r1;
