@@ -88,10 +88,18 @@ struct Dot2 {
 };
 
 constexpr int kResMaxP = 16;    // chunks per system supported by the resident kernel
-// A workgroup of the resident kernel is one wavefront: 64 / P systems times
-// P chunks.  Its barriers then cost next to nothing, and the waves sharing a
-// SIMD hide each other's latencies without waiting on one another.
+// A wavefront of the resident kernel holds 64 / P systems times P chunks and
+// exchanges interface values only among its own lanes, so the waves never
+// wait on one another: the ones sharing a SIMD hide each other's latencies.
+// Where the systems of one wavefront fill less than a 128-byte row segment,
+// a workgroup gathers the wavefronts of 16 neighbouring systems, so that
+// the state is read and written in whole cache lines by one CU.
 __host__ __device__ constexpr int res_systems(int P) { return kWave / P; }
+__host__ __device__ constexpr int res_waves(int P)
+{
+    return (res_systems(P) * P == kWave && res_systems(P) < 16 && 16 % res_systems(P) == 0)
+               ? 16 / res_systems(P) : 1;
+}
 
 // coefficient block written by the set-up kernel, read with uniform loads:
 //   rows i < m: [ralpha, beta, w0, w1, gamma, delta, UL0, UL1]   (8 doubles)
@@ -290,34 +298,50 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
 }
 
 template <int M, int P>
-__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(kWave * res_waves(P)) __attribute__((amdgpu_waves_per_eu(3)))
 k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__restrict__ coef,
                  double *__restrict__ C)
 {
     constexpr int m = M - 2;
-    constexpr int S = res_systems(P);
-    __shared__ double tbuf[2][P][S][4];
-    __shared__ double rbuf[2][2 * P][S][2];   // r_k stored at k and k + P
-    __shared__ double xbuf[2][P][S][2];
-    const int tid = threadIdx.x;
-    const int j = tid / S, sl = tid % S;
+    constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;   // systems per wave, per workgroup
+    __shared__ double tbuf[2][P][SW][4];
+    __shared__ double rbuf[2][2 * P][SW][2];  // r_k stored at k and k + P
+    __shared__ double xbuf[2][P][SW][2];
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int j = lane / S, sl = wv * S + lane % S;     // chunk, system slot in the workgroup
     // workgroups are dispatched round-robin over the 8 XCDs: the ones one
     // XCD runs back to back take neighbouring systems, so that row segments
     // narrower than a 128-byte line share it through one L2
     const unsigned nb = gridDim.x, bid = blockIdx.x, full = nb & ~7u;
     const unsigned tile = bid < full ? (bid & 7u) * (full >> 3) + (bid >> 3) : bid;
-    const int64_t s = int64_t(tile) * S + sl;
+    const int64_t s = int64_t(tile) * SW + sl;
     const bool act = s < batch;
     // lanes past the end of the batch compute on a copy of the last system
     // and store nothing
     double *col = C + (act ? s : batch - 1) + int64_t(j) * M * ld;
+    // lanes of one wavefront exchange values through LDS: a fence keeps the
+    // compiler from moving the accesses across (the wavefront itself executes
+    // them in order), and no workgroup barrier is needed
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
     const double *H = coef + 8 * m;
     const double a = H[0], b = H[1], d = H[3], e = H[4];
     const double URa = H[5], URb = H[6], URc = H[7];
 
+    // the state, read in groups of 8 rows through a pointer re-derived per
+    // group, so that the compiler does not materialise all M row addresses
+    // at once (they would spill)
     double x[M];
 #pragma unroll
-    for (int i = 0; i < M; ++i) x[i] = col[int64_t(i) * ld];
+    for (int g = 0; g < M / 8; ++g) {
+        const double *pg = col + int64_t(8 * g) * ld;
+        asm volatile("" : "+v"(pg));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[8 * g + r] = pg[int64_t(r) * ld];
+    }
 
     const int jn = (j + 1 == P) ? 0 : j + 1;
     const int jm1 = (j == 0) ? P - 1 : j - 1;
@@ -378,13 +402,13 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         const double yR0 = x[m - 2] - cf[8 * (m - 2) + 4] * yR1;
         double *tb = tbuf[bf][j][sl];
         tb[0] = t0; tb[1] = t1; tb[2] = yR0; tb[3] = yR1;
-        __syncthreads();
+        wave_sync();
         const double yn0 = tbuf[bf][jn][sl][0], yn1 = tbuf[bf][jn][sl][1];
         const double rj0 = x[m] - a * yR0 - b * yR1 - e * yn0;
         const double rj1 = x[m + 1] - a * yR1 - d * yn0 - e * yn1;
         rbuf[bf][j][sl][0] = rj0; rbuf[bf][j][sl][1] = rj1;
         rbuf[bf][j + P][sl][0] = rj0; rbuf[bf][j + P][sl][1] = rj1;
-        __syncthreads();
+        wave_sync();
         // interface values of this chunk: xI_j = sum_q T_q r_{j+q}
         // (block-circulant S^{-1}: T_q is its first block row)
         double r0 = 0.0, r1 = 0.0;
@@ -407,7 +431,7 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
             }
         }
         xbuf[bf][j][sl][0] = r0; xbuf[bf][j][sl][1] = r1;
-        __syncthreads();
+        wave_sync();
         // ... and of the previous chunk, from its lane
         const double l0 = xbuf[bf][jm1][sl][0], l1 = xbuf[bf][jm1][sl][1];
         asm volatile("" : "+s"(cg) : "v"(l1));
@@ -450,14 +474,18 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         x[m] = r0;
         x[m + 1] = r1;
     }
+    // the waves of a workgroup write quarters of the same cache lines: let
+    // them store together, so that each line is whole when it leaves L2
+    if (WS > 1) __syncthreads();
     if (act) {
-        // a fresh pointer: keeps the compiler from holding the 64 load
-        // addresses in registers for the whole step loop
-        double *outg = col;
-        asm volatile("" : "+v"(outg));
-        __attribute__((address_space(1))) double *out = (__attribute__((address_space(1))) double *)outg;
 #pragma unroll
-        for (int i = 0; i < M; ++i) out[int64_t(i) * ld] = x[i];
+        for (int g = 0; g < M / 8; ++g) {
+            double *outg = col + int64_t(8 * g) * ld;
+            asm volatile("" : "+v"(outg));
+            __attribute__((address_space(1))) double *out = (__attribute__((address_space(1))) double *)outg;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) out[int64_t(r) * ld] = x[8 * g + r];
+        }
     }
 }
 
@@ -482,9 +510,10 @@ static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, 
 {
     hipLaunchKernelGGL((k_hyper_resident_setup<M, P>), dim3(1), dim3(64), 0, st, sigma, coef);
     if (nsteps == 0) return;
-    constexpr int S = res_systems(P);
-    const unsigned grid = unsigned((batch + S - 1) / S);
-    hipLaunchKernelGGL((k_hyper_resident<M, P>), dim3(grid), dim3(S * P), 0, st, batch, ld,
+    constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;
+    const unsigned grid = unsigned((batch + SW - 1) / SW);
+    const unsigned threads = WS > 1 ? unsigned(kWave * WS) : unsigned(S * P);
+    hipLaunchKernelGGL((k_hyper_resident<M, P>), dim3(grid), dim3(threads), 0, st, batch, ld,
                        nsteps, (const double *)coef, C);
 }
 

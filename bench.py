@@ -11,15 +11,17 @@ system -- the whole path on one batch of synthetic input already resident in
 device memory.
 
 Output: ONE JSON line (metric, value = unknowns solved per second, ...),
-with a "roofline" object for the dominant kernel (the multi-step periodic
-solve; algorithmic bytes = 16 per unknown per time step: read C^k, write
-C^{k+1}) and a "cpu_baseline" object (the CPU oracle, OpenMP over systems,
-timed on a bounded sample of the same workload on this host's cores).
+with a "roofline" object for the dominant kernel (the register-resident
+multi-step periodic solve, bound by fp64 vector arithmetic: 17 algorithmic
+flops per unknown per time step against the 78.6 TFLOP/s fp64 vector peak;
+HBM sees the state once in and once out per call) and a "cpu_baseline"
+object (the CPU oracle, OpenMP over systems, timed on a bounded sample of
+the same workload on this host's cores).
 
     python bench.py [--steps K] [--warmup W] [--workload {1,2,3,4}]
 
 --workload selects another workload for manual measurements
-(2: general pentadiagonal 512 x 65536 fused factor+solve; 3: Hines mono
+(2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
 512 x 100000; 4: Hines multi, 32768 neurons of 256..2048 compartments,
 20 solves per step).  Only one GPU is used; --gpus above 1 exits.
 """
@@ -294,7 +296,8 @@ def _hines_common(args, multi):
         "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
         "dtype": "f64",
         "config": {"workload": cfg["name"], "solves_per_step": nsolve, **stats},
-        "roofline": {"bound": "hbm", "kernel": "k_hines", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "k_hines_multi" if multi else "k_hines_mono_reg",
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": _traffic("hines_multi" if multi else "hines_mono"),
                      "kernel_ms": kern_ms, "bytes_per_launch": alg_bytes / nsolve},
