@@ -149,7 +149,14 @@ BPS_API size_t bps_penta_work_bytes(const bps_penta_desc *desc);
 /* Factor and solve in one pass over the data (the "Rewrite" use of [P]:
  * a new matrix every call), non-periodic, per-system diagonals only
  * (flags must be 0).  x: f on entry, solution on return.  work: device,
- * bps_penta_work_bytes(desc) bytes, overwritten.  info: as above or NULL. */
+ * bps_penta_work_bytes(desc) bytes, overwritten (scratch; contents
+ * undefined on return).  info: as above or NULL: 1 + the first row whose
+ * pivot of the page's sequential elimination is zero or non-finite.
+ * For n = 16*P with 2 <= P <= 64 the systems are solved in 16-row chunks
+ * (each eliminated with its own pivots, joined by a 2x2-block interface
+ * system); a system whose chunked elimination meets a zero or non-finite
+ * pivot is re-solved in the same launch by the sequential elimination, so
+ * info and the solution are those of the page's algorithm. */
 BPS_API bps_status penta_factor_solve_batch(const bps_penta_desc *desc,
                                     const void *a, const void *b, const void *c,
                                     const void *d, const void *e,
