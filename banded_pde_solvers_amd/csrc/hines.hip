@@ -578,11 +578,16 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
     }
     const dim3 grid(unsigned(P->mono ? (P->batch + kWave - 1) / kWave : P->nblocks));
     constexpr int D = kHinesAhead;
+    // A multi-morphology batch of at most one block per SIMD runs one wave
+    // per SIMD anyway, and its largest blocks set the time: a 32-row
+    // look-ahead (256 VGPRs, one wave per SIMD) keeps more rows in flight.
+    constexpr int kSimds = 1024;
     if (P->mono) {
         if (gen) hipLaunchKernelGGL((k_hines<true, true, D>), grid, dim3(kWave), 0, st, A);
         else hipLaunchKernelGGL((k_hines_mono_reg<D>), grid, dim3(kWave), 0, st, A);
     } else {
         if (gen) hipLaunchKernelGGL((k_hines<false, true, D>), grid, dim3(kWave), 0, st, A);
+        else if (P->nblocks <= kSimds) hipLaunchKernelGGL((k_hines_multi<32>), grid, dim3(kWave), 0, st, A);
         else hipLaunchKernelGGL((k_hines_multi<D>), grid, dim3(kWave), 0, st, A);
     }
     BPS_LAUNCHED("k_hines");
