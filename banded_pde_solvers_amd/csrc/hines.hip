@@ -287,108 +287,166 @@ __global__ void __launch_bounds__(kWave) k_hines_mono_reg(HinesArgs A)
         if (f0 + j < n) subst(f0 + j, fq[j], fm[j], fp[j]);
 }
 
+// Buffer-resource access to one block of the packed layout: a wave-uniform
+// descriptor (base, size in bytes; accesses beyond the size read zero and
+// write nothing), the lane's byte offset in a VGPR and the row's byte
+// offset in an SGPR, so that a row costs one memory instruction and no
+// address arithmetic.  Third descriptor word for gfx9 raw buffers.
+constexpr int kBufWord3 = 0x00020000;
+struct BlockBuf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ BlockBuf(const void *base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), kBufWord3)) {}
+    __device__ double ld(uint32_t lane_off, uint32_t row_off) const {
+        return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, row_off, 0));
+    }
+    __device__ int32_t ldi(uint32_t lane_off, uint32_t row_off) const {
+        return int32_t(__builtin_amdgcn_raw_buffer_load_b32(r, lane_off, row_off, 0));
+    }
+    __device__ void st(double v, uint32_t lane_off, uint32_t row_off) const {
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, lane_off, row_off, 0);
+    }
+};
+
 // Multi-morphology blocks, parents within kRing rows: branch-free loops.
 // Every lane reads and writes only its own column of its block (rows past
 // its neuron's size are padding of the packed layout); results of padding
 // rows are masked with selects and padding is written back unchanged.
+// The largest blocks set the kernel time (one wavefront per block, a serial
+// chain per lane), so the instruction count per row matters: rows go
+// through buffer descriptors (one instruction per access), the look-ahead
+// alternates between two sets of registers (no copies), and the pending
+// (d, rhs) updates of a row share one 16-byte LDS slot.
 template <int D>
 __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
 {
-    __shared__ double ring_d[kRing][kWave];
-    __shared__ double ring_r[kRing][kWave];
+    __shared__ double2 ring[kRing][kWave];
     const int k = threadIdx.x;
     const int64_t b = blockIdx.x;
-    const int64_t base = A.blk_off[b] + k;
+    const int64_t off = A.blk_off[b];
     const int32_t rows = A.blk_rows[b];
     const int32_t my_n = A.lane_n[b * kWave + k];
     const int32_t src = A.lane_src[b * kWave + k];
-    constexpr int64_t ld = kWave;
-    const double *u = A.u + base, *l = A.l + base, *d = A.d + base;
-    double *rhs = A.rhs + base, *mw = A.mwork + base;
-    const int32_t *par = A.parent + base;
+    const uint32_t nbytes = uint32_t(rows) * kWave * 8u;
+    const BlockBuf U(A.u + off, nbytes), L(A.l + off, nbytes), Dg(A.d + off, nbytes);
+    const BlockBuf R(A.rhs + off, nbytes), MW(A.mwork + off, nbytes);
+    const BlockBuf PA(A.parent + off, nbytes / 2);
+    const uint32_t lo8 = uint32_t(k) * 8u, lo4 = uint32_t(k) * 4u;   // lane byte offsets
+    auto rb8 = [](int32_t r) { return uint32_t(r) * (kWave * 8u); };  // row byte offsets
+    auto rb4 = [](int32_t r) { return uint32_t(r) * (kWave * 4u); };
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) { ring_d[j][k] = 0.0; ring_r[j][k] = 0.0; }
+    for (int j = 0; j < kRing; ++j) ring[j][k] = make_double2(0.0, 0.0);
     int32_t bad = 0;
-    double qu[D], ql[D], qd[D], qr[D];
-    int32_t qp[D];
-    auto load_b = [&](int j, int32_t r) {
-        const int64_t o = int64_t(r >= 1 ? r : 1 < rows ? 1 : 0) * ld;
-        qu[j] = u[o]; ql[j] = l[o]; qd[j] = d[o]; qr[j] = rhs[o]; qp[j] = par[o];
+
+    // ---- leaves -> root ----
+    struct BRow { double u, l, d, r; int32_t p; };
+    auto load_b = [&](BRow &q, int32_t r) {
+        const int32_t rc = r >= 1 ? r : 1 < rows ? 1 : 0;
+        q.u = U.ld(lo8, rb8(rc)); q.l = L.ld(lo8, rb8(rc)); q.d = Dg.ld(lo8, rb8(rc));
+        q.r = R.ld(lo8, rb8(rc)); q.p = PA.ldi(lo4, rb4(rc));
     };
-#pragma unroll
-    for (int j = 0; j < D; ++j) load_b(j, rows - 1 - j);
-    auto elim = [&](int32_t i, double ui, double li, double di, double ri, int32_t pi) {
-            const bool live = i < my_n;
-            const int64_t o = int64_t(i) * ld;
-            const int slot = i & (kRing - 1);
-            const double pd = ring_d[slot][k], pr = ring_r[slot][k];
-            ring_d[slot][k] = 0.0; ring_r[slot][k] = 0.0;
-            const double dd = di - pd;               // d'_i
-            const double rr = ri - pr;               // rhs'_i
-            if (live && !bad && bad_pivot(dd)) bad = i + 1;
-            const double rcp = 1.0 / dd;
-            const double fac = live ? ui * rcp : 0.0;  // factor of Algorithm 1
-            rhs[o] = live ? rr * rcp : ri;           // q_i (padding unchanged)
-            mw[o] = live ? li * rcp : 0.0;           // m_i
-            const int ps = pi & (kRing - 1);
-            unsafeAtomicAdd(&ring_d[ps][k], fac * li);
-            unsafeAtomicAdd(&ring_r[ps][k], fac * rr);
-    };
-    int32_t i0 = rows - 1;
-    for (; i0 - D + 1 >= 1; i0 -= D) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const double ui = qu[j], li = ql[j], di = qd[j], ri = qr[j];
-            const int32_t pi = qp[j];
-            load_b(j, i0 - j - D);
-            elim(i0 - j, ui, li, di, ri, pi);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-        if (i0 - j >= 1) elim(i0 - j, qu[j], ql[j], qd[j], qr[j], qp[j]);
-    const bool root = my_n > 0;
-    const double pd0 = ring_d[0][k], pr0 = ring_r[0][k];
-    const double dd0 = d[0] - pd0;
-    if (root && !bad && bad_pivot(dd0)) bad = 1;
-    const double r0 = rhs[0];
-    const double v0 = root ? (r0 - pr0) / dd0 : 0.0;
-    rhs[0] = root ? v0 : r0;
-    if (src >= 0 && A.info) A.info[src] = bad;
-    // root -> leaves; ring_d holds recent voltages by slot, a parent one row
-    // up comes from a register
-    ring_d[0][k] = v0;
-    double vprev = v0;
-    double fq[D], fm[D];
-    int32_t fp[D];
-    auto load_f = [&](int j, int32_t r) {
-        const int64_t o = int64_t(r < rows ? r : rows - 1) * ld;
-        fq[j] = rhs[o]; fm[j] = mw[o]; fp[j] = par[o];
-    };
-#pragma unroll
-    for (int j = 0; j < D; ++j) load_f(j, 1 + j);
-    auto subst = [&](int32_t i, double qi, double mi, int32_t pi) {
+    auto elim = [&](int32_t i, const BRow &q) {
         const bool live = i < my_n;
-        const double vr = ring_d[pi & (kRing - 1)][k];
-        const double vp = (i - pi == 1) ? vprev : vr;
-        const double v = qi - mi * vp;
-        rhs[int64_t(i) * ld] = live ? v : qi;
-        ring_d[i & (kRing - 1)][k] = v;
+        const int slot = i & (kRing - 1);
+        const double2 pp = ring[slot][k];
+        ring[slot][k] = make_double2(0.0, 0.0);
+        const double dd = q.d - pp.x;            // d'_i
+        const double rr = q.r - pp.y;            // rhs'_i
+        if (live && !bad && bad_pivot(dd)) bad = i + 1;
+        const double rcp = 1.0 / dd;
+        const double fac = live ? q.u * rcp : 0.0;  // factor of Algorithm 1
+        R.st(live ? rr * rcp : q.r, lo8, rb8(i));   // q_i (padding unchanged)
+        MW.st(live ? q.l * rcp : 0.0, lo8, rb8(i)); // m_i
+        const int ps = q.p & (kRing - 1);
+        unsafeAtomicAdd(&ring[ps][k].x, fac * q.l);
+        unsafeAtomicAdd(&ring[ps][k].y, fac * rr);
+    };
+    BRow qa[D], qb[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_b(qa[j], rows - 1 - j);
+    int32_t i0 = rows - 1;
+    // two groups per iteration: the group in one set is worked on while the
+    // next one arrives in the other
+    for (; i0 - 2 * D + 1 >= 1; i0 -= 2 * D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_b(qb[j], i0 - D - j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) elim(i0 - j, qa[j]);
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_b(qa[j], i0 - 2 * D - j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) elim(i0 - D - j, qb[j]);
+    }
+    if (i0 - D + 1 >= 1) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_b(qb[j], i0 - D - j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) elim(i0 - j, qa[j]);
+        i0 -= D;
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (i0 - j >= 1) elim(i0 - j, qb[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (i0 - j >= 1) elim(i0 - j, qa[j]);
+    }
+    const bool root = my_n > 0;
+    const double2 p0 = ring[0][k];
+    const double dd0 = Dg.ld(lo8, 0) - p0.x;
+    if (root && !bad && bad_pivot(dd0)) bad = 1;
+    const double r0 = R.ld(lo8, 0);
+    const double v0 = root ? (r0 - p0.y) / dd0 : 0.0;
+    R.st(root ? v0 : r0, lo8, 0);
+    if (src >= 0 && A.info) A.info[src] = bad;
+
+    // ---- root -> leaves; ring (.x) holds recent voltages by slot, a
+    // parent one row up comes from a register ----
+    ring[0][k].x = v0;
+    double vprev = v0;
+    struct FRow { double q, m; int32_t p; };
+    auto load_f = [&](FRow &f, int32_t r) {
+        const int32_t rc = r < rows ? r : rows - 1;
+        f.q = R.ld(lo8, rb8(rc)); f.m = MW.ld(lo8, rb8(rc)); f.p = PA.ldi(lo4, rb4(rc));
+    };
+    auto subst = [&](int32_t i, const FRow &f) {
+        const bool live = i < my_n;
+        const double vr = ring[f.p & (kRing - 1)][k].x;
+        const double vp = (i - f.p == 1) ? vprev : vr;
+        const double v = f.q - f.m * vp;
+        R.st(live ? v : f.q, lo8, rb8(i));
+        ring[i & (kRing - 1)][k].x = v;
         vprev = v;
     };
+    FRow fa[D], fb[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_f(fa[j], 1 + j);
     int32_t f0 = 1;
-    for (; f0 + D - 1 < rows; f0 += D) {
+    for (; f0 + 2 * D - 1 < rows; f0 += 2 * D) {
 #pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const double qi = fq[j], mi = fm[j];
-            const int32_t pi = fp[j];
-            load_f(j, f0 + j + D);
-            subst(f0 + j, qi, mi, pi);
-        }
+        for (int j = 0; j < D; ++j) load_f(fb[j], f0 + D + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) subst(f0 + j, fa[j]);
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_f(fa[j], f0 + 2 * D + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) subst(f0 + D + j, fb[j]);
     }
+    if (f0 + D - 1 < rows) {
 #pragma unroll
-    for (int j = 0; j < D; ++j)
-        if (f0 + j < rows) subst(f0 + j, fq[j], fm[j], fp[j]);
+        for (int j = 0; j < D; ++j) load_f(fb[j], f0 + D + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) subst(f0 + j, fa[j]);
+        f0 += D;
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (f0 + j < rows) subst(f0 + j, fb[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (f0 + j < rows) subst(f0 + j, fa[j]);
+    }
 }
 
 __global__ void k_fill_zero(double *p, int64_t count)
@@ -579,15 +637,15 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
     const dim3 grid(unsigned(P->mono ? (P->batch + kWave - 1) / kWave : P->nblocks));
     constexpr int D = kHinesAhead;
     // A multi-morphology batch of at most one block per SIMD runs one wave
-    // per SIMD anyway, and its largest blocks set the time: a 32-row
-    // look-ahead (256 VGPRs, one wave per SIMD) keeps more rows in flight.
+    // per SIMD anyway, and its largest blocks set the time: groups of 16
+    // rows (256 VGPRs, one wave per SIMD) keep more rows in flight.
     constexpr int kSimds = 1024;
     if (P->mono) {
         if (gen) hipLaunchKernelGGL((k_hines<true, true, D>), grid, dim3(kWave), 0, st, A);
         else hipLaunchKernelGGL((k_hines_mono_reg<D>), grid, dim3(kWave), 0, st, A);
     } else {
         if (gen) hipLaunchKernelGGL((k_hines<false, true, D>), grid, dim3(kWave), 0, st, A);
-        else if (P->nblocks <= kSimds) hipLaunchKernelGGL((k_hines_multi<32>), grid, dim3(kWave), 0, st, A);
+        else if (P->nblocks <= kSimds) hipLaunchKernelGGL((k_hines_multi<16>), grid, dim3(kWave), 0, st, A);
         else hipLaunchKernelGGL((k_hines_multi<D>), grid, dim3(kWave), 0, st, A);
     }
     BPS_LAUNCHED("k_hines");
