@@ -293,10 +293,24 @@ __global__ void __launch_bounds__(kWave) k_hines_mono_reg(HinesArgs A)
 // offset in an SGPR, so that a row costs one memory instruction and no
 // address arithmetic.  Third descriptor word for gfx9 raw buffers.
 constexpr int kBufWord3 = 0x00020000;
+// The base and size are passed through readfirstlane: a descriptor the
+// compiler cannot prove uniform would be used through a loop over the
+// distinct values in the wavefront at every access.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+    return int64_t((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ void *uniform_ptr(const void *p)
+{
+    return reinterpret_cast<void *>(uniform_i64(reinterpret_cast<int64_t>(p)));
+}
 struct BlockBuf {
     __amdgpu_buffer_rsrc_t r;
     __device__ BlockBuf(const void *base, uint32_t bytes)
-        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), kBufWord3)) {}
+        : r(__builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0,
+                                              int(__builtin_amdgcn_readfirstlane(bytes)), kBufWord3)) {}
     __device__ double ld(uint32_t lane_off, uint32_t row_off) const {
         return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, row_off, 0));
     }
@@ -324,8 +338,10 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     __shared__ double2 ring[kRing][kWave];
     const int k = threadIdx.x;
     const int64_t b = blockIdx.x;
-    const int64_t off = A.blk_off[b];
-    const int32_t rows = A.blk_rows[b];
+    // block geometry is wave-uniform: kept in scalar registers, so that row
+    // offsets can be the scalar offsets of buffer accesses
+    const int64_t off = uniform_i64(A.blk_off[b]);
+    const int32_t rows = __builtin_amdgcn_readfirstlane(A.blk_rows[b]);
     const int32_t my_n = A.lane_n[b * kWave + k];
     const int32_t src = A.lane_src[b * kWave + k];
     const uint32_t nbytes = uint32_t(rows) * kWave * 8u;
@@ -333,8 +349,9 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     const BlockBuf R(A.rhs + off, nbytes), MW(A.mwork + off, nbytes);
     const BlockBuf PA(A.parent + off, nbytes / 2);
     const uint32_t lo8 = uint32_t(k) * 8u, lo4 = uint32_t(k) * 4u;   // lane byte offsets
-    auto rb8 = [](int32_t r) { return uint32_t(r) * (kWave * 8u); };  // row byte offsets
-    auto rb4 = [](int32_t r) { return uint32_t(r) * (kWave * 4u); };
+    // row byte offsets (scalar: a buffer access takes its row offset from an SGPR)
+    auto rb8 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * (kWave * 8u)); };
+    auto rb4 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * (kWave * 4u)); };
 #pragma unroll
     for (int j = 0; j < kRing; ++j) ring[j][k] = make_double2(0.0, 0.0);
     int32_t bad = 0;
