@@ -110,7 +110,10 @@ def _run_multi(mm):
     return out, host(info).astype(int)
 
 
-@pytest.mark.parametrize("batch,nmin,nmax", [(1, 1, 1), (3, 1, 7), (70, 5, 60), (200, 256, 2048)])
+@pytest.mark.parametrize("batch,nmin,nmax", [(1, 1, 1), (3, 1, 7), (70, 5, 60), (200, 256, 2048),
+                                             # 1032 blocks: more than one per SIMD, the
+                                             # occupancy-first kernel configuration
+                                             (66000, 2, 9)])
 def test_multi_matches_oracle(batch, nmin, nmax):
     print(f"hines multi batch={batch} n in [{nmin},{nmax}]", flush=True)
     mm = W.hines_multi(batch, nmin, nmax, rng=np.random.default_rng(batch + nmax))

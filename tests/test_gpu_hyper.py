@@ -58,7 +58,9 @@ def test_workload0_modes_full():
 
 
 @pytest.mark.parametrize("n,batch", [(6, 1), (7, 65), (64, 130), (128, 37), (192, 50), (256, 17),
-                                     (1024, 200)])
+                                     (1024, 200),
+                                     # chunk counts that do not divide a wavefront
+                                     (320, 33), (448, 20), (832, 40), (960, 17)])
 def test_one_step_parity(n, batch):
     dt, dx = 1e-6, 1.0 / n
     C0 = np.random.default_rng(n + batch).uniform(-1, 1, (n, batch))
