@@ -80,6 +80,9 @@ def _load():
             lib.orc_hyperdiffusion.argtypes = [_i64, _i64, ctypes.c_double, ctypes.c_double,
                                                _D, _D, _i64]
             lib.orc_hyperdiffusion.restype = ctypes.c_int
+            lib.orc_hyperdiffusion_theta.argtypes = [_i64, _i64, ctypes.c_double, ctypes.c_double,
+                                                     ctypes.c_double, _D, _i64]
+            lib.orc_hyperdiffusion_theta.restype = ctypes.c_int
             lib.orc_hines_solve.argtypes = [_i64, _I32, _D, _D, _D, _D]
             lib.orc_hines_solve.restype = ctypes.c_int
             lib.orc_hines_solve_batch.argtypes = [_i64, _i64, _I32, _D, _D, _D, _D, _I32]
@@ -189,6 +192,28 @@ def hyperdiffusion(C0, dt: float, dx: float, nsteps: int, diagonals=None):
         dp = None
     _load().orc_hyperdiffusion(n, batch, float(dt), float(dx), dp, _ptr(C), int(nsteps))
     return C
+
+
+def hyperdiffusion_theta(C0, dt: float, dx: float, theta: float, nsteps: int):
+    """C^{nsteps} from C^0 (flat (batch, n)) by theta-scheme steps
+    (I + theta sigma D4) C' = (I - (1 - theta) sigma D4) C, sigma = dt/dx^4."""
+    C = _batch2(C0).copy()
+    batch, n = C.shape
+    if n < 6:
+        raise ValueError("periodic solve needs n >= 6")
+    _load().orc_hyperdiffusion_theta(n, batch, float(dt), float(dx), float(theta), _ptr(C),
+                                     int(nsteps))
+    return C
+
+
+def hyperdiffusion_theta_operators(n: int, dt: float, dx: float, theta: float):
+    """Stencil entries (e2, e1, e0) of I - (1-theta) sigma D4 and diagonals
+    (a, b, c, d, e) of I + theta sigma D4, rounded as the solver rounds them."""
+    sigma = dt / (dx * dx * dx * dx)
+    si, se = theta * sigma, (1.0 - theta) * sigma
+    one = np.ones(n)
+    return ((-se, 4.0 * se, 1.0 - 6.0 * se),
+            (si * one, -4.0 * si * one, (1.0 + 6.0 * si) * one, -4.0 * si * one, si * one))
 
 
 # ----------------------------------------------------------------------------

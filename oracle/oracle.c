@@ -424,6 +424,60 @@ int orc_hyperdiffusion(int64_t n, int64_t batch, double dt, double dx,
 }
 
 /* ------------------------------------------------------------------------ */
+/* [P] Periodic hyperdiffusion, theta scheme (hyperdiffusion section: the   */
+/* page steps with Crank-Nicolson, theta = 1/2, i.e. sigma_x = dt/(2dx^4)   */
+/* on both sides):                                                          */
+/*   (I + theta sigma D4) C^{k+1} = (I - (1 - theta) sigma D4) C^k,         */
+/* sigma = dt / dx^4.  The right-hand side is the five-point periodic       */
+/* stencil with entries -se, 4 se, 1 - 6 se, 4 se, -se (se = (1-theta)      */
+/* sigma), summed left to right; the implicit matrix (si = theta sigma) is  */
+/* factored once with the periodic reduction above.  theta = 1 gives the    */
+/* implicit step of orc_hyperdiffusion exactly (the stencil is C itself).   */
+/* ------------------------------------------------------------------------ */
+
+int orc_hyperdiffusion_theta(int64_t n, int64_t batch, double dt, double dx, double theta,
+                             double *C, int64_t nsteps)
+{
+    const double sigma = dt / (dx * dx * dx * dx);
+    const double si = theta * sigma, se = (1.0 - theta) * sigma;
+    const double e2 = -se, e1 = 4.0 * se, e0 = 1.0 - 6.0 * se;
+    double *dg = (double *)malloc(sizeof(double) * 5 * (size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+        dg[i] = si;
+        dg[n + i] = -4.0 * si;
+        dg[2 * n + i] = 1.0 + 6.0 * si;
+        dg[3 * n + i] = -4.0 * si;
+        dg[4 * n + i] = si;
+    }
+    cyc_setup s0;
+    int inf = cyc_init(&s0, n, dg, dg + n, dg + 2 * n, dg + 3 * n, dg + 4 * n);
+    #pragma omp parallel
+    {
+        cyc_setup s = s0;
+        double *tmp = (double *)malloc(sizeof(double) * (size_t)s.m);
+        double *rhs = (double *)malloc(sizeof(double) * (size_t)n);
+        s.tmp = tmp;
+        #pragma omp for schedule(static)
+        for (int64_t k = 0; k < batch; ++k) {
+            double *x = C + k * n;
+            for (int64_t t = 0; t < nsteps; ++t) {
+                for (int64_t i = 0; i < n; ++i) {
+                    const double xm2 = x[(i - 2 + n) % n], xm1 = x[(i - 1 + n) % n];
+                    const double xp1 = x[(i + 1) % n], xp2 = x[(i + 2) % n];
+                    rhs[i] = e2 * xm2 + e1 * xm1 + e0 * x[i] + e1 * xp1 + e2 * xp2;
+                }
+                cyc_apply(&s, rhs, x);
+            }
+        }
+        free(rhs);
+        free(tmp);
+    }
+    cyc_free(&s0);
+    free(dg);
+    return inf;
+}
+
+/* ------------------------------------------------------------------------ */
 /* [H] Hines algorithm (Algorithm 1) for one tree-tridiagonal system.       */
 /*                                                                          */
 /* Matrix: A[i][i] = d_i, A[p_i][i] = u_i, A[i][p_i] = l_i, with p_i < i    */

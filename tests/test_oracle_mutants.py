@@ -37,6 +37,12 @@ MUTANTS = {
     "F_modification_dropped": ("s->tmp[i] = f[i] - s->F0[i] * xt0 - s->F1[i] * xt1;",
                                "s->tmp[i] = f[i] - s->F0[i] * xt0;"),
     "hyperdiffusion_stencil_coefficient": ("own[2 * n + i] = 1.0 + 6.0 * sigma;", "own[2 * n + i] = 1.0 + 4.0 * sigma;"),
+    "theta_sides_swapped": ("const double si = theta * sigma, se = (1.0 - theta) * sigma;",
+                            "const double se = theta * sigma, si = (1.0 - theta) * sigma;"),
+    "theta_stencil_neighbour_sign": ("const double e2 = -se, e1 = 4.0 * se, e0 = 1.0 - 6.0 * se;",
+                                     "const double e2 = -se, e1 = -4.0 * se, e0 = 1.0 - 6.0 * se;"),
+    "theta_stencil_wrong_index": ("const double xp1 = x[(i + 1) % n], xp2 = x[(i + 2) % n];",
+                                  "const double xp1 = x[(i + 1) % n], xp2 = x[(i + 1) % n];"),
     "hines_rhs_uses_parent_value": ("rhs[p[i]] -= factor * rhs[i];", "rhs[p[i]] -= factor * rhs[p[i]];"),
     "hines_forward_u_for_l": ("rhs[i] -= l[i] * rhs[p[i]];", "rhs[i] -= u[i] * rhs[p[i]];"),
     "hines_d_update_uses_u": ("d[p[i]] -= factor * l[i];", "d[p[i]] -= factor * u[i];"),
@@ -93,6 +99,18 @@ def _checks(orc):
     g = 1 / (1 + sigma * (2 - 2 * np.cos(2 * np.pi * 3 / N)) ** 2)
     if np.max(np.abs(C - g ** 2 * C0)) > 1e-10:
         failed.append("mode_decay")
+    # theta scheme (theta != 1/2, so that the two sides differ): one step of a
+    # random state vs dense solves
+    n, dt = 9, 0.02
+    (e2, e1, e0), dgt = orc.hyperdiffusion_theta_operators(n, dt, 1.0 / n, 0.3)
+    Bt = np.zeros((n, n))
+    for i in range(n):
+        for off, v in ((-2, e2), (-1, e1), (0, e0), (1, e1), (2, e2)):
+            Bt[i, (i + off) % n] += v
+    C0 = rng.uniform(-1, 1, n)
+    got = orc.hyperdiffusion_theta(C0, dt, 1.0 / n, 0.3, 1)[0]
+    if relerr(got, np.linalg.solve(cyclic_dense(*dgt), Bt @ C0)) > 1e-12:
+        failed.append("theta_dense")
     # Hines, random tree, u != l
     from workloads import random_tree
     p = random_tree(30, rng, window=4)
