@@ -297,16 +297,20 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     }
 }
 
-template <int M, int P>
+// EX: theta scheme, each step's right-hand side is the explicit five-point
+// stencil (ex2, ex1, ex0, ex1, ex2) of the state (I - (1 - theta) sigma D4);
+// the chunks exchange their first and last two rows for it.
+template <int M, int P, bool EX>
 __global__ void __launch_bounds__(kWave * res_waves(P)) __attribute__((amdgpu_waves_per_eu(3)))
 k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__restrict__ coef,
-                 double *__restrict__ C)
+                 double *__restrict__ C, double ex0, double ex1, double ex2)
 {
     constexpr int m = M - 2;
     constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;   // systems per wave, per workgroup
     __shared__ double tbuf[2][P][SW][4];
     __shared__ double rbuf[2][2 * P][SW][2];  // r_k stored at k and k + P
     __shared__ double xbuf[2][P][SW][2];
+    __shared__ double hbuf[EX ? P : 1][SW][4];  // halo rows of the explicit stencil
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane / S, sl = wv * S + lane % S;     // chunk, system slot in the workgroup
     // workgroups are dispatched round-robin over the 8 XCDs: the ones one
@@ -347,6 +351,17 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
     const int jm1 = (j == 0) ? P - 1 : j - 1;
     for (int64_t step = 0; step < nsteps; ++step) {
         const int bf = int(step & 1);
+        // explicit half of the theta scheme: rows -2, -1 (previous chunk's
+        // last rows) and M, M+1 (next chunk's first rows) of the state
+        double xm2 = 0.0, xm1 = 0.0, xp0 = 0.0, xp1 = 0.0;
+        if constexpr (EX) {
+            double *hb = hbuf[j][sl];
+            hb[0] = x[0]; hb[1] = x[1]; hb[2] = x[m]; hb[3] = x[m + 1];
+            wave_sync();
+            xm2 = hbuf[jm1][sl][2]; xm1 = hbuf[jm1][sl][3];
+            xp0 = hbuf[jn][sl][0]; xp1 = hbuf[jn][sl][1];
+        }
+        double o1 = xm1, o2 = xm2;     // state rows i-1, i-2 before this step
         // Per-row coefficients come from the scalar cache (uniform loads
         // through a pointer in the constant address space), KB rows at a
         // time, one batch ahead: the loads of batch k+1 are issued right after
@@ -390,6 +405,15 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
                 const int i = k * KB + r;
                 const double *c4 = cb[cur][r];     // [1/alpha, beta, w0, w1]
                 double g = x[i];
+                if constexpr (EX) {
+                    const double xi = x[i];
+                    g = ex2 * o2;
+                    g = fma(ex1, o1, g);
+                    g = fma(ex0, xi, g);
+                    g = fma(ex1, x[i + 1], g);
+                    g = fma(ex2, x[i + 2], g);
+                    o2 = o1; o1 = xi;
+                }
                 if (i >= 2) g -= a * x[i - 2];
                 if (i >= 1) g -= c4[1] * x[i - 1];
                 g *= c4[0];
@@ -404,8 +428,21 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         tb[0] = t0; tb[1] = t1; tb[2] = yR0; tb[3] = yR1;
         wave_sync();
         const double yn0 = tbuf[bf][jn][sl][0], yn1 = tbuf[bf][jn][sl][1];
-        const double rj0 = x[m] - a * yR0 - b * yR1 - e * yn0;
-        const double rj1 = x[m + 1] - a * yR1 - d * yn0 - e * yn1;
+        double fI0 = x[m], fI1 = x[m + 1];     // right-hand side on the interface rows
+        if constexpr (EX) {
+            fI0 = ex2 * o2;
+            fI0 = fma(ex1, o1, fI0);
+            fI0 = fma(ex0, x[m], fI0);
+            fI0 = fma(ex1, x[m + 1], fI0);
+            fI0 = fma(ex2, xp0, fI0);
+            fI1 = ex2 * o1;
+            fI1 = fma(ex1, x[m], fI1);
+            fI1 = fma(ex0, x[m + 1], fI1);
+            fI1 = fma(ex1, xp0, fI1);
+            fI1 = fma(ex2, xp1, fI1);
+        }
+        const double rj0 = fI0 - a * yR0 - b * yR1 - e * yn0;
+        const double rj1 = fI1 - a * yR1 - d * yn0 - e * yn1;
         rbuf[bf][j][sl][0] = rj0; rbuf[bf][j][sl][1] = rj1;
         rbuf[bf][j + P][sl][0] = rj0; rbuf[bf][j + P][sl][1] = rj1;
         wave_sync();
@@ -505,45 +542,105 @@ size_t resident_coef_bytes(int64_t n)
 }
 
 template <int M, int P>
-static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, double *coef,
-                       double *C, hipStream_t st)
+static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, bool ex,
+                       double e0, double e1, double e2, double *coef, double *C, hipStream_t st)
 {
     hipLaunchKernelGGL((k_hyper_resident_setup<M, P>), dim3(1), dim3(64), 0, st, sigma, coef);
     if (nsteps == 0) return;
     constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;
     const unsigned grid = unsigned((batch + SW - 1) / SW);
     const unsigned threads = WS > 1 ? unsigned(kWave * WS) : unsigned(S * P);
-    hipLaunchKernelGGL((k_hyper_resident<M, P>), dim3(grid), dim3(threads), 0, st, batch, ld,
-                       nsteps, (const double *)coef, C);
+    if (ex)
+        hipLaunchKernelGGL((k_hyper_resident<M, P, true>), dim3(grid), dim3(threads), 0, st, batch,
+                           ld, nsteps, (const double *)coef, C, e0, e1, e2);
+    else
+        hipLaunchKernelGGL((k_hyper_resident<M, P, false>), dim3(grid), dim3(threads), 0, st, batch,
+                           ld, nsteps, (const double *)coef, C, e0, e1, e2);
 }
 
 bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t nsteps, double sigma,
-                                 void *coef, void *C, hipStream_t st)
+                                 bool ex, double e0, double e1, double e2, void *coef, void *C,
+                                 hipStream_t st)
 {
     constexpr int M = 64;
     if (resident_chunk(n) != M || !(sigma >= 0.0))
         BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16, sigma >= 0");
     double *cf = (double *)coef, *x = (double *)C;
+#define BPS_RES_CASE(PP) \
+    case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, ex, e0, e1, e2, cf, x, st); break;
     switch (int(n / M)) {
-    case 2: launch_res<M, 2>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 3: launch_res<M, 3>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 4: launch_res<M, 4>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 5: launch_res<M, 5>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 6: launch_res<M, 6>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 7: launch_res<M, 7>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 8: launch_res<M, 8>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 9: launch_res<M, 9>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 10: launch_res<M, 10>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 11: launch_res<M, 11>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 12: launch_res<M, 12>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 13: launch_res<M, 13>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 14: launch_res<M, 14>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 15: launch_res<M, 15>(batch, ld, nsteps, sigma, cf, x, st); break;
-    case 16: launch_res<M, 16>(batch, ld, nsteps, sigma, cf, x, st); break;
+    BPS_RES_CASE(2) BPS_RES_CASE(3) BPS_RES_CASE(4) BPS_RES_CASE(5) BPS_RES_CASE(6)
+    BPS_RES_CASE(7) BPS_RES_CASE(8) BPS_RES_CASE(9) BPS_RES_CASE(10) BPS_RES_CASE(11)
+    BPS_RES_CASE(12) BPS_RES_CASE(13) BPS_RES_CASE(14) BPS_RES_CASE(15) BPS_RES_CASE(16)
     default: BPS_FAIL(BPS_ENOTSUP, "unsupported chunk count");
     }
+#undef BPS_RES_CASE
     BPS_LAUNCHED("k_hyper_resident");
     return BPS_OK;
 }
+
+// ---- explicit stencil of the theta scheme (streaming path) ------------------
+
+// out[i] = e2 x[i-2] + e1 x[i-1] + e0 x[i] + e1 x[i+1] + e2 x[i+2], periodic
+// in the row index, interleaved [n][ld] arrays (separate input and output).
+template <typename T>
+__global__ void k_hyper_explicit(int64_t n, int64_t batch, int64_t ldi, int64_t ldo, T e0, T e1,
+                                 T e2, const T *__restrict__ in, T *__restrict__ out)
+{
+    const int64_t s = lane_id();
+    if (s >= batch) return;
+    const T *c = in + s;
+    T *o = out + s;
+    T xm2 = c[(n - 2) * ldi], xm1 = c[(n - 1) * ldi], x0 = c[0], xp1 = c[ldi];
+    const T first0 = x0, first1 = xp1;
+    for (int64_t i = 0; i < n; ++i) {
+        const T xp2 = i + 2 < n ? c[(i + 2) * ldi] : (i + 2 == n ? first0 : first1);
+        T f = e2 * xm2;
+        f = fma(e1, xm1, f);
+        f = fma(e0, x0, f);
+        f = fma(e1, xp1, f);
+        f = fma(e2, xp2, f);
+        o[i * ldo] = f;
+        xm2 = xm1; xm1 = x0; x0 = xp1; xp1 = xp2;
+    }
+}
+
+template <typename T>
+__global__ void k_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_t ldo,
+                                   const T *__restrict__ in, T *__restrict__ out)
+{
+    const int64_t s = lane_id();
+    if (s >= batch) return;
+    for (int64_t i = 0; i < n; ++i) out[i * ldo + s] = in[i * ldi + s];
+}
+
+template <typename T>
+bps_status launch_hyper_explicit(int64_t n, int64_t batch, int64_t ldi, int64_t ldo, double e0,
+                                 double e1, double e2, const void *in, void *out, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_hyper_explicit<T>), dim3(unsigned((batch + 255) / 256)), dim3(256), 0, st,
+                       n, batch, ldi, ldo, T(e0), T(e1), T(e2), (const T *)in, (T *)out);
+    BPS_LAUNCHED("k_hyper_explicit");
+    return BPS_OK;
+}
+
+template <typename T>
+bps_status launch_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_t ldo,
+                                   const void *in, void *out, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_copy_interleaved<T>), dim3(unsigned((batch + 255) / 256)), dim3(256), 0,
+                       st, n, batch, ldi, ldo, (const T *)in, (T *)out);
+    BPS_LAUNCHED("k_copy_interleaved");
+    return BPS_OK;
+}
+
+#define BPS_INST(T)                                                                             \
+    template bps_status launch_hyper_explicit<T>(int64_t, int64_t, int64_t, int64_t, double,     \
+                                                 double, double, const void *, void *, hipStream_t); \
+    template bps_status launch_copy_interleaved<T>(int64_t, int64_t, int64_t, int64_t,          \
+                                                   const void *, void *, hipStream_t);
+BPS_INST(float)
+BPS_INST(double)
+#undef BPS_INST
 
 }  // namespace bps

@@ -184,6 +184,27 @@ BPS_API bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int6
                                double dt, double dx, const void *diagonals,
                                void *C, int64_t nsteps, void *work, void *stream);
 
+/* Bytes of `work` for hyperdiffusion_theta_step (0 if invalid). */
+BPS_API size_t hyperdiffusion_theta_work_bytes(int dtype, int64_t n, int64_t batch);
+
+/* Advance `batch` periodic 1-D fields by `nsteps` theta-scheme steps
+ *     (I + theta*sigma*D4) C^{k+1} = (I - (1 - theta)*sigma*D4) C^k,
+ * sigma = dt / dx^4, D4 as above ([P] hyperdiffusion section: the page's
+ * Crank-Nicolson scheme is theta = 1/2, i.e. sigma_x = dt/(2 dx^4) on both
+ * sides; theta = 1 is hyperdiffusion_step with the built-in operator, with
+ * identical results).  The right-hand side is the explicit five-point
+ * stencil with entries -se, 4 se, 1 - 6 se, 4 se, -se (se = (1-theta)*sigma);
+ * the implicit matrix (a = e = si, b = d = -4 si, c = 1 + 6 si, si =
+ * theta*sigma) is factored once per call.  The scheme is unconditionally
+ * stable for theta >= 1/2 only; smaller theta is computed as asked.
+ * C: device, interleaved [n][ld]; C^0 on entry, C^{nsteps} on return.
+ * work: device, hyperdiffusion_theta_work_bytes(dtype, n, batch) bytes.
+ * n >= 6, batch >= 1, ld >= batch, nsteps >= 0, dt and dx finite, dx != 0,
+ * 0 <= theta <= 1 (else BPS_EINVAL). */
+BPS_API bps_status hyperdiffusion_theta_step(int dtype, int64_t n, int64_t batch, int64_t ld,
+                                     double dt, double dx, double theta, void *C,
+                                     int64_t nsteps, void *work, void *stream);
+
 /* ======================================================================== */
 /* Hines tree-tridiagonal systems  [H] sections 2-4                         */
 /* ======================================================================== */

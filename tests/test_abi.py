@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for required in ("penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
                      "penta_factor_solve_batch", "hines_solve_batch", "hyperdiffusion_step",
+                     "hyperdiffusion_theta_step",
                      "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack"):
         assert required in names
 
@@ -111,6 +112,19 @@ def test_hyperdiffusion_rejects_bad_arguments(lib):
     assert f(2, 16, 4, 4, 1e-6, 0.1, None, _fake(), -1, _fake(1), None) == EINVAL
     assert f(2, 16, 4, 3, 1e-6, 0.1, None, _fake(), 1, _fake(1), None) == EINVAL  # ld < batch
     assert f(2, 16, 4, 4, 1e-6, 0.1, None, None, 1, _fake(1), None) == EINVAL
+
+
+def test_theta_step_rejects_bad_arguments(lib):
+    f = lib.hyperdiffusion_theta_step
+    assert f(2, 16, 4, 4, 1e-6, 0.1, -0.1, _fake(), 1, _fake(1), None) == EINVAL   # theta < 0
+    assert f(2, 16, 4, 4, 1e-6, 0.1, 1.5, _fake(), 1, _fake(1), None) == EINVAL    # theta > 1
+    assert f(2, 16, 4, 4, 1e-6, 0.1, float("nan"), _fake(), 1, _fake(1), None) == EINVAL
+    assert f(2, 5, 4, 4, 1e-6, 0.1, 0.5, _fake(), 1, _fake(1), None) == EINVAL     # n < 6
+    assert f(2, 16, 4, 4, 1e-6, 0.0, 0.5, _fake(), 1, _fake(1), None) == EINVAL    # dx = 0
+    assert f(2, 16, 4, 4, 1e-6, 0.1, 0.5, _fake(), -1, _fake(1), None) == EINVAL   # nsteps < 0
+    assert lib.hyperdiffusion_theta_work_bytes(2, 1024, 100) == (
+        lib.hyperdiffusion_work_bytes(2, 1024, 100) + 1024 * 100 * 8)
+    assert lib.hyperdiffusion_theta_work_bytes(2, 5, 1) == 0
 
 
 def test_hines_plan_rejects_bad_parents_before_allocating(lib):
