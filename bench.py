@@ -18,12 +18,14 @@ HBM sees the state once in and once out per call) and a "cpu_baseline"
 object (the CPU oracle, OpenMP over systems, timed on a bounded sample of
 the same workload on this host's cores).
 
-    python bench.py [--steps K] [--warmup W] [--workload {1,2,3,4}]
+    python bench.py [--steps K] [--warmup W] [--workload {1,2,3,4,5}]
 
 --workload selects another workload for manual measurements
 (2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
 512 x 100000; 4: Hines multi, 32768 neurons of 256..2048 compartments,
-20 solves per step).  Only one GPU is used; --gpus above 1 exits.
+20 solves per step; 5: the default shape time-stepped with Crank-Nicolson,
+theta = 1/2, 24 algorithmic flops per unknown per time step).  Only one GPU
+is used; --gpus above 1 exits.
 """
 import argparse
 import json
@@ -149,20 +151,26 @@ def _cpu_baseline(run_sample, unknowns_per_system, label, seconds):
 # Workloads
 # ---------------------------------------------------------------------------
 
-def bench_hyperdiffusion(args):
+def bench_hyperdiffusion(args, which=1):
     import numpy as np
     import torch
     import banded_pde_solvers_amd as bps
     import workloads as W
 
-    cfg = W.WORKLOADS[1]
+    cfg = W.WORKLOADS[which]
     n, batch, nsteps, dt, dx = cfg["n"], cfg["batch"], cfg["nsteps"], cfg["dt"], cfg["dx"]
+    theta = cfg.get("theta")
     C = torch.as_tensor(W.hyperdiffusion_random(n, batch), device="cuda:0")
-    work = torch.empty(bps.hyperdiffusion_work_bytes(n, batch), dtype=torch.uint8, device="cuda:0")
-    step = lambda: bps.hyperdiffusion_step(C, dt, dx, nsteps, work)
-    wall, per = _time_loop(step, args.steps, args.warmup)
+    if theta is None:
+        work = torch.empty(bps.hyperdiffusion_work_bytes(n, batch), dtype=torch.uint8, device="cuda:0")
+        run = lambda k: bps.hyperdiffusion_step(C, dt, dx, k, work)
+    else:
+        work = torch.empty(bps.hyperdiffusion_theta_work_bytes(n, batch), dtype=torch.uint8,
+                           device="cuda:0")
+        run = lambda k: bps.hyperdiffusion_theta_step(C, dt, dx, theta, k, work)
+    wall, per = _time_loop(lambda: run(nsteps), args.steps, args.warmup)
     # the operator set-up alone (diagonals + shared factorisation), same stream
-    _, setup = _time_loop(lambda: bps.hyperdiffusion_step(C, dt, dx, 0, work), 10, 2)
+    _, setup = _time_loop(lambda: run(0), 10, 2)
     ms_step = wall * 1e3 / args.steps
     kern_ms = max(statistics.mean(per) - statistics.median(setup), 1e-6)
     unknowns = n * batch * nsteps
@@ -171,22 +179,29 @@ def bench_hyperdiffusion(args):
     # fp64 vector arithmetic.  Algorithmic flops per unknown per time step of
     # the periodic LU solve: forward 2 FMA + 1 MUL, corner dot products 2 FMA,
     # back substitution 2 FMA, rank-2 corner correction 2 FMA = 17 flops.
-    alg_flops = 17.0 * unknowns
+    # The theta scheme adds the explicit stencil, at least 7 flops in its
+    # symmetric form e0 x_i + e1 (x_i-1 + x_i+1) + e2 (x_i-2 + x_i+2).
+    flops_per = 17.0 if theta is None else 24.0
+    alg_flops = flops_per * unknowns
     achieved = alg_flops / (kern_ms * 1e-3) / 1e12
     hbm_bytes = 16.0 * n * batch                     # C read once, written once
+    scheme = "implicit" if theta is None else f"theta = {theta}"
     line = {
-        "metric": "unknowns solved/s (fp64), periodic hyperdiffusion implicit steps",
+        "metric": "unknowns solved/s (fp64), periodic hyperdiffusion " +
+                  ("implicit steps" if theta is None else "Crank-Nicolson steps"),
         "value": unknowns / (ms_step * 1e-3),
         "unit": "unknowns/s",
         "ms_per_step": ms_step,
         "dtype": "f64",
         "config": {"workload": cfg["name"], "n": n, "batch": batch, "time_steps_per_step": nsteps,
-                   "dt": dt, "dx": dx, "sigma": dt / dx ** 4, "coefficients": "constant (factor once)"},
+                   "dt": dt, "dx": dx, "sigma": dt / dx ** 4, "scheme": scheme,
+                   "coefficients": "constant (factor once)"},
         "roofline": {"bound": "alu", "kernel": "k_hyper_resident<64,16>",
                      "achieved": achieved, "peak": FP64_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP64_VALU_PEAK_TFLOPS,
-                     "traffic": _traffic("hyperdiffusion"),
+                     "traffic": _traffic("hyperdiffusion" if theta is None else "hyperdiffusion_theta"),
                      "kernel_ms": kern_ms, "setup_ms": statistics.median(setup),
+                     "flops_per_unknown_step": flops_per,
                      "flops_per_launch": alg_flops, "hbm_bytes_per_launch": hbm_bytes,
                      "effective_gbs_16B_per_unknown_step": 16.0 * unknowns / (kern_ms * 1e-3) / 1e9},
     }
@@ -198,7 +213,11 @@ def bench_hyperdiffusion(args):
             reps = (k + 2047) // 2048
             for r in range(reps):
                 kk = min(2048, k - r * 2048)
-                oracle.hyperdiffusion(W.to_flat(C0[:, :kk]), dt, dx, nsteps)
+                x = W.to_flat(C0[:, :kk])
+                if theta is None:
+                    oracle.hyperdiffusion(x, dt, dx, nsteps)
+                else:
+                    oracle.hyperdiffusion_theta(x, dt, dx, theta, nsteps)
         line["cpu_baseline"] = _cpu_baseline(sample, n * nsteps, f"systems x {nsteps} steps",
                                              args.cpu_seconds)
     return line
@@ -347,7 +366,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workload 2 only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -366,9 +385,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py measures one GPU only: the solver batches are independent and "
-                  "this build runs on a single MI355X (see DESIGN.md for how the batch would "
-                  "shard); rerun with --gpus 1.", file=sys.stderr, flush=True)
+            print("bench.py measures one GPU only: the systems of a batch are independent, "
+                  "so a multi-GPU run would split the batch by columns and add nothing to "
+                  "measure per GPU; rerun with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -380,7 +399,7 @@ def main():
     import banded_pde_solvers_amd as bps
     bps.load_library()
     fn = {1: bench_hyperdiffusion, 2: bench_penta, 3: lambda a: _hines_common(a, False),
-          4: lambda a: _hines_common(a, True)}[args.workload]
+          4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5)}[args.workload]
     line = fn(args)
     out = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"),
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -129,3 +129,21 @@ def test_invalid_theta():
     for th in (-0.1, 1.5, float("nan")):
         with pytest.raises(bps.BpsError):
             bps.hyperdiffusion_theta_step(C, 1e-6, 1.0 / 64, th, 1, work)
+
+
+@pytest.mark.slow
+def test_crank_nicolson_full_sampled():
+    """N = 1024, 16384 systems, 100 Crank-Nicolson steps in one call, as
+    benchmarked: sampled systems against the oracle's trajectory (per-step
+    error bound times the step count), plus a one-step check."""
+    cfg = W.WORKLOADS[5]
+    n, batch, dt, dx, theta = cfg["n"], cfg["batch"], cfg["dt"], cfg["dx"], cfg["theta"]
+    print(f"full Crank-Nicolson workload {n}x{batch}", flush=True)
+    C0 = W.hyperdiffusion_random(n, batch)
+    out = _run(C0, dt, dx, theta, cfg["nsteps"])
+    cols = np.unique(np.r_[0, 15, 16, batch - 1, np.random.default_rng(5).integers(0, batch, 40)])
+    ref = _oracle(C0[:, cols], dt, dx, theta, cfg["nsteps"])
+    err = np.linalg.norm(out[:, cols] - ref, axis=0) / np.linalg.norm(C0[:, cols], axis=0)
+    assert np.max(err) <= cfg["nsteps"] * _tol(n, dt, dx, theta)
+    one = _run(C0, dt, dx, theta, 1)
+    assert relerr_cols(one[:, cols], _oracle(C0[:, cols], dt, dx, theta, 1)) <= _tol(n, dt, dx, theta)

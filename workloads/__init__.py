@@ -269,7 +269,8 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
 
 
 # ----------------------------------------------------------------------------
-# The five named workloads at their full sizes
+# The named workloads at their full sizes (5: the headline shape time-stepped
+# with Crank-Nicolson instead of backward Euler)
 # ----------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -281,4 +282,6 @@ WORKLOADS = {
     3: dict(name="hines_mono_n512_b100000", kind="hines_mono", n=512, batch=100000),
     4: dict(name="hines_multi_b32768_n256to2048_20steps", kind="hines_multi",
             batch=32768, nmin=256, nmax=2048, nsteps=20),
+    5: dict(name="cn_theta0.5_n1024_b16384_100steps", kind="hyperdiffusion_theta",
+            n=1024, batch=16384, dt=1e-6, dx=1.0 / 1024, nsteps=100, theta=0.5),
 }
