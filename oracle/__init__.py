@@ -19,6 +19,11 @@ Functions and the passages they follow:
                             matrix and Navon's reduction, eqs. (10)-(12)
   hyperdiffusion         -- cuPentBatch page, eqs. (4)-(7) with the implicit
                             step (I + sigma D4) C^{n+1} = C^n, sigma = dt/dx^4
+  hyperdiffusion_theta   -- cuPentBatch page, hyperdiffusion section: the
+                            Crank-Nicolson step generalised to the theta family
+  cahn_hilliard          -- cuPentBatch page, introduction: the Cahn-Hilliard
+                            equation with the phase-separation term at the old
+                            time level and the fourth-order term implicit
   hines_solve            -- Hines page, section 2, Algorithm 1
   hines_multi_solve      -- Algorithm 1 per neuron, one tree per neuron
 """
@@ -83,6 +88,10 @@ def _load():
             lib.orc_hyperdiffusion_theta.argtypes = [_i64, _i64, ctypes.c_double, ctypes.c_double,
                                                      ctypes.c_double, _D, _i64]
             lib.orc_hyperdiffusion_theta.restype = ctypes.c_int
+            lib.orc_cahn_hilliard.argtypes = [_i64, _i64, ctypes.c_double, ctypes.c_double,
+                                              ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                              _D, _i64]
+            lib.orc_cahn_hilliard.restype = ctypes.c_int
             lib.orc_hines_solve.argtypes = [_i64, _I32, _D, _D, _D, _D]
             lib.orc_hines_solve.restype = ctypes.c_int
             lib.orc_hines_solve_batch.argtypes = [_i64, _i64, _I32, _D, _D, _D, _D, _I32]
@@ -213,6 +222,33 @@ def hyperdiffusion_theta_operators(n: int, dt: float, dx: float, theta: float):
     si, se = theta * sigma, (1.0 - theta) * sigma
     one = np.ones(n)
     return ((-se, 4.0 * se, 1.0 - 6.0 * se),
+            (si * one, -4.0 * si * one, (1.0 + 6.0 * si) * one, -4.0 * si * one, si * one))
+
+
+def cahn_hilliard(C0, dt: float, dx: float, gamma: float, mobility: float, theta: float,
+                  nsteps: int):
+    """C^{nsteps} from C^0 (flat (batch, n)) by semi-implicit Cahn-Hilliard
+    steps (I + theta sigma D4) C' = (I - (1-theta) sigma D4) C + r D2 (C^3 - C),
+    r = mobility dt / dx^2, sigma = gamma r / dx^2 (theta = 1: the linear
+    fourth-order term fully implicit)."""
+    C = _batch2(C0).copy()
+    batch, n = C.shape
+    if n < 6:
+        raise ValueError("periodic solve needs n >= 6")
+    _load().orc_cahn_hilliard(n, batch, float(dt), float(dx), float(gamma), float(mobility),
+                              float(theta), _ptr(C), int(nsteps))
+    return C
+
+
+def cahn_hilliard_operators(n: int, dt: float, dx: float, gamma: float, mobility: float,
+                            theta: float):
+    """(e2, e1, e0), r and the implicit diagonals (a, b, c, d, e) of the
+    Cahn-Hilliard step, rounded as the solver rounds them."""
+    r = mobility * dt / (dx * dx)
+    sigma = gamma * r / (dx * dx)
+    si, se = theta * sigma, (1.0 - theta) * sigma
+    one = np.ones(n)
+    return ((-se, 4.0 * se, 1.0 - 6.0 * se), r,
             (si * one, -4.0 * si * one, (1.0 + 6.0 * si) * one, -4.0 * si * one, si * one))
 
 

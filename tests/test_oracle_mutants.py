@@ -37,12 +37,18 @@ MUTANTS = {
     "F_modification_dropped": ("s->tmp[i] = f[i] - s->F0[i] * xt0 - s->F1[i] * xt1;",
                                "s->tmp[i] = f[i] - s->F0[i] * xt0;"),
     "hyperdiffusion_stencil_coefficient": ("own[2 * n + i] = 1.0 + 6.0 * sigma;", "own[2 * n + i] = 1.0 + 4.0 * sigma;"),
-    "theta_sides_swapped": ("const double si = theta * sigma, se = (1.0 - theta) * sigma;",
-                            "const double se = theta * sigma, si = (1.0 - theta) * sigma;"),
-    "theta_stencil_neighbour_sign": ("const double e2 = -se, e1 = 4.0 * se, e0 = 1.0 - 6.0 * se;",
-                                     "const double e2 = -se, e1 = -4.0 * se, e0 = 1.0 - 6.0 * se;"),
+    "theta_sides_swapped": ("(dx * dx * dx * dx);\n    const double si = theta * sigma, se = (1.0 - theta) * sigma;",
+                            "(dx * dx * dx * dx);\n    const double se = theta * sigma, si = (1.0 - theta) * sigma;"),
+    "theta_stencil_neighbour_sign": ("(dx * dx * dx * dx);\n    const double si = theta * sigma, se = (1.0 - theta) * sigma;\n    const double e2 = -se, e1 = 4.0 * se,",
+                                     "(dx * dx * dx * dx);\n    const double si = theta * sigma, se = (1.0 - theta) * sigma;\n    const double e2 = -se, e1 = -4.0 * se,"),
     "theta_stencil_wrong_index": ("const double xp1 = x[(i + 1) % n], xp2 = x[(i + 2) % n];",
                                   "const double xp1 = x[(i + 1) % n], xp2 = x[(i + 1) % n];"),
+    "ch_phase_term_sign": ("rhs[i] = lin + r * lap;", "rhs[i] = lin - r * lap;"),
+    "ch_square_for_cube": ("phi[i] = x[i] * x[i] * x[i] - x[i];", "phi[i] = x[i] * x[i] - x[i];"),
+    "ch_laplacian_centre": ("const double lap = phi[im1] - 2.0 * phi[i] + phi[ip1];",
+                            "const double lap = phi[im1] - 2.0 * phi[i] + phi[ip2];"),
+    "ch_r_uses_dx4": ("const double r = mobility * dt / (dx * dx);",
+                      "const double r = mobility * dt / (dx * dx * dx * dx);"),
     "hines_rhs_uses_parent_value": ("rhs[p[i]] -= factor * rhs[i];", "rhs[p[i]] -= factor * rhs[p[i]];"),
     "hines_forward_u_for_l": ("rhs[i] -= l[i] * rhs[p[i]];", "rhs[i] -= u[i] * rhs[p[i]];"),
     "hines_d_update_uses_u": ("d[p[i]] -= factor * l[i];", "d[p[i]] -= factor * u[i];"),
@@ -111,6 +117,20 @@ def _checks(orc):
     got = orc.hyperdiffusion_theta(C0, dt, 1.0 / n, 0.3, 1)[0]
     if relerr(got, np.linalg.solve(cyclic_dense(*dgt), Bt @ C0)) > 1e-12:
         failed.append("theta_dense")
+    # Cahn-Hilliard: one step vs dense solves with the phase-separation term
+    n, dt, dx, gm, mob = 9, 2e-3, 1.0 / 9, 0.05, 1.3
+    (e2, e1, e0), r, dgc = orc.cahn_hilliard_operators(n, dt, dx, gm, mob, 0.5)
+    Bc = np.zeros((n, n)); L2 = np.zeros((n, n))
+    for i in range(n):
+        for off, v in ((-2, e2), (-1, e1), (0, e0), (1, e1), (2, e2)):
+            Bc[i, (i + off) % n] += v
+        for off, v in ((-1, 1.0), (0, -2.0), (1, 1.0)):
+            L2[i, (i + off) % n] += v
+    C0 = rng.uniform(-1, 1, n)
+    got = orc.cahn_hilliard(C0, dt, dx, gm, mob, 0.5, 1)[0]
+    ref = np.linalg.solve(cyclic_dense(*dgc), Bc @ C0 + r * (L2 @ (C0 ** 3 - C0)))
+    if relerr(got, ref) > 1e-12:
+        failed.append("ch_dense")
     # Hines, random tree, u != l
     from workloads import random_tree
     p = random_tree(30, rng, window=4)
