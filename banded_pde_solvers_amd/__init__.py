@@ -27,6 +27,7 @@ __all__ = [
     "penta_factor_solve_batch",
     "hyperdiffusion_work_bytes", "hyperdiffusion_step",
     "hyperdiffusion_theta_work_bytes", "hyperdiffusion_theta_step",
+    "cahn_hilliard_work_bytes", "cahn_hilliard_step",
     "HinesPlan", "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
     "hines_work_bytes", "hines_solve_batch",
 ]
@@ -91,6 +92,10 @@ def load_library():
             "hyperdiffusion_theta_work_bytes": ([st, i64, i64], ctypes.c_size_t),
             "hyperdiffusion_theta_step": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double,
                                            ctypes.c_double, vp, i64, vp, vp], st),
+            "cahn_hilliard_work_bytes": ([st, i64, i64], ctypes.c_size_t),
+            "cahn_hilliard_step": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double,
+                                    ctypes.c_double, ctypes.c_double, ctypes.c_double, vp, i64,
+                                    vp, vp], st),
             "hines_plan_create": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64], st),
             "hines_plan_destroy": ([vp], st),
             "hines_plan_elems": ([vp], i64),
@@ -267,6 +272,24 @@ def hyperdiffusion_theta_step(C, dt: float, dx: float, theta: float, nsteps: int
     _check("hyperdiffusion_theta_step", load_library().hyperdiffusion_theta_step(
         dt_code, n, batch, ld, float(dt), float(dx), float(theta), _ptr(C), int(nsteps),
         _ptr(work), _stream(stream)))
+    return C
+
+
+def cahn_hilliard_work_bytes(n: int, batch: int, dtype: int = BPS_F64) -> int:
+    return int(load_library().cahn_hilliard_work_bytes(int(dtype), int(n), int(batch)))
+
+
+def cahn_hilliard_step(C, dt: float, dx: float, gamma: float, mobility: float, theta: float,
+                       nsteps: int, work, *, batch=None, stream=None):
+    """Advance C (n, ld) by nsteps semi-implicit periodic Cahn-Hilliard steps."""
+    n, batch, ld = _geom(C, batch)
+    dt_code = _dtype_code(C)
+    need = load_library().cahn_hilliard_work_bytes(dt_code, n, batch)
+    if work.numel() * work.element_size() < need:
+        raise ValueError(f"work buffer too small ({need} bytes needed)")
+    _check("cahn_hilliard_step", load_library().cahn_hilliard_step(
+        dt_code, n, batch, ld, float(dt), float(dx), float(gamma), float(mobility), float(theta),
+        _ptr(C), int(nsteps), _ptr(work), _stream(stream)))
     return C
 
 

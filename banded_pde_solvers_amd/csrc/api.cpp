@@ -220,7 +220,8 @@ bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, 
         // system sees the same interior block, so the register-resident
         // multi-step kernel applies (the diagonals built above are unused)
         const double sigma = dt / (dx * dx * dx * dx);
-        return launch_hyper_resident(n, batch, ld, nsteps, sigma, false, 1.0, 0.0, 0.0, fac, C, st);
+        return launch_hyper_resident(n, batch, ld, nsteps, sigma, 0, 1.0, 0.0, 0.0, 0.0, fac, C,
+                                     st);
     }
     const char *D = static_cast<const char *>(dg);
     if (dtype == BPS_F64) {
@@ -244,6 +245,56 @@ size_t hyperdiffusion_theta_work_bytes(int dtype, int64_t n, int64_t batch)
     return base + size_t(n) * size_t(batch) * dtype_size(dtype);   // + the right-hand sides
 }
 
+// Steps (I + si D4) C' = S C (+ rr D2 (C^3 - C) with kResPhase), S the
+// stencil (e2, e1, e0, e1, e2) with kResStencil, else the identity;
+// arguments already validated.
+static bps_status explicit_implicit_steps(int dtype, int64_t n, int64_t batch, int64_t ld, double si,
+                                          double e0, double e1, double e2, double rr, int mode,
+                                          void *C, int64_t nsteps, void *work, hipStream_t st)
+{
+    const size_t es = dtype_size(dtype);
+    char *w = static_cast<char *>(work);
+    void *fac = w + 5 * n * es;
+    if (dtype == BPS_F64 && resident_chunk(n) != 0 && si >= 0.0)
+        return launch_hyper_resident(n, batch, ld, nsteps, si, mode, e0, e1, e2, rr, fac, C, st);
+    // streaming: factor I + si D4 once, then per step the right-hand side
+    // into a separate array and a solve in place, alternating between C and
+    // that array (the result is copied back when it ends in the array)
+    void *R = w + hyperdiffusion_work_bytes(dtype, n, batch);
+    if (dtype == BPS_F64) CHECK(launch_hyper_diagonals<double>(n, si, w, st));
+    else CHECK(launch_hyper_diagonals<float>(n, si, w, st));
+    const char *D = w;
+    if (dtype == BPS_F64)
+        CHECK(launch_penta_factor<double>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
+                                          D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
+    else
+        CHECK(launch_penta_factor<float>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
+                                         D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
+    if (mode == 0) {
+        if (nsteps == 0) return BPS_OK;
+        return dtype == BPS_F64 ? launch_penta_cyclic_solve<double>(n, batch, ld, nsteps, true, fac, C, st)
+                                : launch_penta_cyclic_solve<float>(n, batch, ld, nsteps, true, fac, C, st);
+    }
+    const bool ch = (mode & kResPhase) != 0;
+    void *cur = C, *nxt = R;
+    int64_t lcur = ld, lnxt = batch;
+    for (int64_t t = 0; t < nsteps; ++t) {
+        if (dtype == BPS_F64) {
+            CHECK(launch_hyper_explicit<double>(n, batch, lcur, lnxt, e0, e1, e2, rr, ch, cur, nxt, st));
+            CHECK(launch_penta_cyclic_solve<double>(n, batch, lnxt, 1, true, fac, nxt, st));
+        } else {
+            CHECK(launch_hyper_explicit<float>(n, batch, lcur, lnxt, e0, e1, e2, rr, ch, cur, nxt, st));
+            CHECK(launch_penta_cyclic_solve<float>(n, batch, lnxt, 1, true, fac, nxt, st));
+        }
+        std::swap(cur, nxt);
+        std::swap(lcur, lnxt);
+    }
+    if (cur != C)
+        return dtype == BPS_F64 ? launch_copy_interleaved<double>(n, batch, lcur, ld, cur, C, st)
+                                : launch_copy_interleaved<float>(n, batch, lcur, ld, cur, C, st);
+    return BPS_OK;
+}
+
 bps_status hyperdiffusion_theta_step(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
                                      double dx, double theta, void *C, int64_t nsteps, void *work,
                                      void *stream)
@@ -263,48 +314,41 @@ bps_status hyperdiffusion_theta_step(int dtype, int64_t n, int64_t batch, int64_
     // I + si D4, explicit stencil (-se, 4 se, 1 - 6 se, 4 se, -se)
     const double si = theta * sigma, se = (1.0 - theta) * sigma;
     const double e2 = -se, e1 = 4.0 * se, e0 = 1.0 - 6.0 * se;
-    const bool ex = theta != 1.0;
-    hipStream_t st = as_stream(stream);
-    const size_t es = dtype_size(dtype);
-    char *w = static_cast<char *>(work);
-    void *fac = w + 5 * n * es;
-    if (dtype == BPS_F64 && resident_chunk(n) != 0 && si >= 0.0)
-        return launch_hyper_resident(n, batch, ld, nsteps, si, ex, e0, e1, e2, fac, C, st);
-    // streaming: factor I + si D4 once, then per step the stencil into the
-    // right-hand-side array and a solve in place, alternating between C and
-    // that array (the result is copied back when it ends in the array)
-    void *R = w + hyperdiffusion_work_bytes(dtype, n, batch);
-    if (dtype == BPS_F64) CHECK(launch_hyper_diagonals<double>(n, si, w, st));
-    else CHECK(launch_hyper_diagonals<float>(n, si, w, st));
-    const char *D = w;
-    if (dtype == BPS_F64)
-        CHECK(launch_penta_factor<double>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
-                                          D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
-    else
-        CHECK(launch_penta_factor<float>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
-                                         D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
-    if (!ex) {
-        if (nsteps == 0) return BPS_OK;
-        return dtype == BPS_F64 ? launch_penta_cyclic_solve<double>(n, batch, ld, nsteps, true, fac, C, st)
-                                : launch_penta_cyclic_solve<float>(n, batch, ld, nsteps, true, fac, C, st);
-    }
-    void *cur = C, *nxt = R;
-    int64_t lcur = ld, lnxt = batch;
-    for (int64_t t = 0; t < nsteps; ++t) {
-        if (dtype == BPS_F64) {
-            CHECK(launch_hyper_explicit<double>(n, batch, lcur, lnxt, e0, e1, e2, cur, nxt, st));
-            CHECK(launch_penta_cyclic_solve<double>(n, batch, lnxt, 1, true, fac, nxt, st));
-        } else {
-            CHECK(launch_hyper_explicit<float>(n, batch, lcur, lnxt, e0, e1, e2, cur, nxt, st));
-            CHECK(launch_penta_cyclic_solve<float>(n, batch, lnxt, 1, true, fac, nxt, st));
-        }
-        std::swap(cur, nxt);
-        std::swap(lcur, lnxt);
-    }
-    if (cur != C)
-        return dtype == BPS_F64 ? launch_copy_interleaved<double>(n, batch, lcur, ld, cur, C, st)
-                                : launch_copy_interleaved<float>(n, batch, lcur, ld, cur, C, st);
-    return BPS_OK;
+    return explicit_implicit_steps(dtype, n, batch, ld, si, e0, e1, e2, 0.0,
+                                   theta != 1.0 ? kResStencil : 0, C, nsteps, work,
+                                   as_stream(stream));
+}
+
+size_t cahn_hilliard_work_bytes(int dtype, int64_t n, int64_t batch)
+{
+    return hyperdiffusion_theta_work_bytes(dtype, n, batch);
+}
+
+bps_status cahn_hilliard_step(int dtype, int64_t n, int64_t batch, int64_t ld, double dt, double dx,
+                              double gamma, double mobility, double theta, void *C, int64_t nsteps,
+                              void *work, void *stream)
+{
+    clear_error();
+    bps_penta_desc dsc{dtype, BPS_CYCLIC | BPS_SHARED_COEF, n, batch, ld};
+    CHECK(check_desc(&dsc));
+    if (nsteps < 0) BPS_FAIL(BPS_EINVAL, "nsteps = %lld < 0", (long long)nsteps);
+    if (!std::isfinite(dt) || !std::isfinite(dx) || dx == 0.0)
+        BPS_FAIL(BPS_EINVAL, "dt and dx must be finite and dx nonzero");
+    if (!(gamma >= 0.0) || !std::isfinite(gamma) || !(mobility >= 0.0) || !std::isfinite(mobility))
+        BPS_FAIL(BPS_EINVAL, "gamma and the mobility must be finite and >= 0");
+    if (!(theta >= 0.0 && theta <= 1.0)) BPS_FAIL(BPS_EINVAL, "theta = %g not in [0, 1]", theta);
+    CHECK(check_ptr(C, "C", dtype));
+    CHECK(check_ptr(work, "work", dtype));
+    const double r = mobility * dt / (dx * dx);
+    const double sigma = gamma * r / (dx * dx);
+    if (!std::isfinite(r) || !std::isfinite(sigma))
+        BPS_FAIL(BPS_EINVAL, "D dt/dx^2 or gamma D dt/dx^4 is not finite");
+    const double si = theta * sigma, se = (1.0 - theta) * sigma;
+    const double e2 = -se, e1 = 4.0 * se, e0 = 1.0 - 6.0 * se;
+    // theta = 1: the stencil is the identity and is left out
+    const int mode = kResPhase | (theta != 1.0 ? kResStencil : 0);
+    return explicit_implicit_steps(dtype, n, batch, ld, si, e0, e1, e2, r, mode, C, nsteps, work,
+                                   as_stream(stream));
 }
 
 // ---- Hines ----------------------------------------------------------------------

@@ -297,20 +297,24 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     }
 }
 
-// EX: theta scheme, each step's right-hand side is the explicit five-point
-// stencil (ex2, ex1, ex0, ex1, ex2) of the state (I - (1 - theta) sigma D4);
-// the chunks exchange their first and last two rows for it.
-template <int M, int P, bool EX>
+// Right-hand side of each step, by the bits of EX:
+//   kResStencil  the explicit five-point stencil (ex2, ex1, ex0, ex1, ex2)
+//                of the state, (I - (1 - theta) sigma D4) C, instead of C;
+//   kResPhase    plus rr D2 (C^3 - C), the phase-separation term of the
+//                Cahn-Hilliard equation at the old time level.
+// With either bit the chunks exchange their first and last two rows.
+template <int M, int P, int EX>
 __global__ void __launch_bounds__(kWave * res_waves(P)) __attribute__((amdgpu_waves_per_eu(3)))
 k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__restrict__ coef,
-                 double *__restrict__ C, double ex0, double ex1, double ex2)
+                 double *__restrict__ C, double ex0, double ex1, double ex2, double rr)
 {
     constexpr int m = M - 2;
     constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;   // systems per wave, per workgroup
     __shared__ double tbuf[2][P][SW][4];
     __shared__ double rbuf[2][2 * P][SW][2];  // r_k stored at k and k + P
     __shared__ double xbuf[2][P][SW][2];
-    __shared__ double hbuf[EX ? P : 1][SW][4];  // halo rows of the explicit stencil
+    constexpr bool LIN = (EX & kResStencil) != 0, PHI = (EX & kResPhase) != 0;
+    __shared__ double hbuf[EX != 0 ? P : 1][SW][4];  // halo rows of the explicit side
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane / S, sl = wv * S + lane % S;     // chunk, system slot in the workgroup
     // workgroups are dispatched round-robin over the 8 XCDs: the ones one
@@ -354,7 +358,7 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         // explicit half of the theta scheme: rows -2, -1 (previous chunk's
         // last rows) and M, M+1 (next chunk's first rows) of the state
         double xm2 = 0.0, xm1 = 0.0, xp0 = 0.0, xp1 = 0.0;
-        if constexpr (EX) {
+        if constexpr (EX != 0) {
             double *hb = hbuf[j][sl];
             hb[0] = x[0]; hb[1] = x[1]; hb[2] = x[m]; hb[3] = x[m + 1];
             wave_sync();
@@ -362,6 +366,12 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
             xp0 = hbuf[jn][sl][0]; xp1 = hbuf[jn][sl][1];
         }
         double o1 = xm1, o2 = xm2;     // state rows i-1, i-2 before this step
+        // phase-separation term phi = C^3 - C of rows i-1 and i before this step
+        double qa = 0.0, qb = 0.0;
+        if constexpr (PHI) {
+            qa = fma(xm1 * xm1, xm1, -xm1);
+            qb = fma(x[0] * x[0], x[0], -x[0]);
+        }
         // Per-row coefficients come from the scalar cache (uniform loads
         // through a pointer in the constant address space), KB rows at a
         // time, one batch ahead: the loads of batch k+1 are issued right after
@@ -405,7 +415,7 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
                 const int i = k * KB + r;
                 const double *c4 = cb[cur][r];     // [1/alpha, beta, w0, w1]
                 double g = x[i];
-                if constexpr (EX) {
+                if constexpr (LIN) {
                     const double xi = x[i];
                     g = ex2 * o2;
                     g = fma(ex1, o1, g);
@@ -413,6 +423,12 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
                     g = fma(ex1, x[i + 1], g);
                     g = fma(ex2, x[i + 2], g);
                     o2 = o1; o1 = xi;
+                }
+                if constexpr (PHI) {
+                    const double xn = x[i + 1];
+                    const double qc = fma(xn * xn, xn, -xn);
+                    g = fma(rr, fma(-2.0, qb, qa + qc), g);
+                    qa = qb; qb = qc;
                 }
                 if (i >= 2) g -= a * x[i - 2];
                 if (i >= 1) g -= c4[1] * x[i - 1];
@@ -429,7 +445,7 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         wave_sync();
         const double yn0 = tbuf[bf][jn][sl][0], yn1 = tbuf[bf][jn][sl][1];
         double fI0 = x[m], fI1 = x[m + 1];     // right-hand side on the interface rows
-        if constexpr (EX) {
+        if constexpr (LIN) {
             fI0 = ex2 * o2;
             fI0 = fma(ex1, o1, fI0);
             fI0 = fma(ex0, x[m], fI0);
@@ -440,6 +456,14 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
             fI1 = fma(ex0, x[m + 1], fI1);
             fI1 = fma(ex1, xp0, fI1);
             fI1 = fma(ex2, xp1, fI1);
+        }
+        if constexpr (PHI) {
+            // qa, qb: phi of rows m-1, m
+            const double xn = x[m + 1];
+            const double qc = fma(xn * xn, xn, -xn);
+            const double qd = fma(xp0 * xp0, xp0, -xp0);
+            fI0 = fma(rr, fma(-2.0, qb, qa + qc), fI0);
+            fI1 = fma(rr, fma(-2.0, qc, qb + qd), fI1);
         }
         const double rj0 = fI0 - a * yR0 - b * yR1 - e * yn0;
         const double rj1 = fI1 - a * yR1 - d * yn0 - e * yn1;
@@ -542,32 +566,45 @@ size_t resident_coef_bytes(int64_t n)
 }
 
 template <int M, int P>
-static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, bool ex,
-                       double e0, double e1, double e2, double *coef, double *C, hipStream_t st)
+static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, int mode,
+                       double e0, double e1, double e2, double rr, double *coef, double *C,
+                       hipStream_t st)
 {
     hipLaunchKernelGGL((k_hyper_resident_setup<M, P>), dim3(1), dim3(64), 0, st, sigma, coef);
     if (nsteps == 0) return;
     constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;
     const unsigned grid = unsigned((batch + SW - 1) / SW);
     const unsigned threads = WS > 1 ? unsigned(kWave * WS) : unsigned(S * P);
-    if (ex)
-        hipLaunchKernelGGL((k_hyper_resident<M, P, true>), dim3(grid), dim3(threads), 0, st, batch,
-                           ld, nsteps, (const double *)coef, C, e0, e1, e2);
-    else
-        hipLaunchKernelGGL((k_hyper_resident<M, P, false>), dim3(grid), dim3(threads), 0, st, batch,
-                           ld, nsteps, (const double *)coef, C, e0, e1, e2);
+    const double *cf = coef;
+    switch (mode) {
+    case kResStencil:
+        hipLaunchKernelGGL((k_hyper_resident<M, P, kResStencil>), dim3(grid), dim3(threads), 0, st,
+                           batch, ld, nsteps, cf, C, e0, e1, e2, rr);
+        break;
+    case kResPhase:
+        hipLaunchKernelGGL((k_hyper_resident<M, P, kResPhase>), dim3(grid), dim3(threads), 0, st,
+                           batch, ld, nsteps, cf, C, e0, e1, e2, rr);
+        break;
+    case kResStencil | kResPhase:
+        hipLaunchKernelGGL((k_hyper_resident<M, P, kResStencil | kResPhase>), dim3(grid),
+                           dim3(threads), 0, st, batch, ld, nsteps, cf, C, e0, e1, e2, rr);
+        break;
+    default:
+        hipLaunchKernelGGL((k_hyper_resident<M, P, 0>), dim3(grid), dim3(threads), 0, st, batch, ld,
+                           nsteps, cf, C, e0, e1, e2, rr);
+    }
 }
 
 bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t nsteps, double sigma,
-                                 bool ex, double e0, double e1, double e2, void *coef, void *C,
-                                 hipStream_t st)
+                                 int mode, double e0, double e1, double e2, double rr, void *coef,
+                                 void *C, hipStream_t st)
 {
     constexpr int M = 64;
     if (resident_chunk(n) != M || !(sigma >= 0.0))
         BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16, sigma >= 0");
     double *cf = (double *)coef, *x = (double *)C;
 #define BPS_RES_CASE(PP) \
-    case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, ex, e0, e1, e2, cf, x, st); break;
+    case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, st); break;
     switch (int(n / M)) {
     BPS_RES_CASE(2) BPS_RES_CASE(3) BPS_RES_CASE(4) BPS_RES_CASE(5) BPS_RES_CASE(6)
     BPS_RES_CASE(7) BPS_RES_CASE(8) BPS_RES_CASE(9) BPS_RES_CASE(10) BPS_RES_CASE(11)
@@ -581,11 +618,13 @@ bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t n
 
 // ---- explicit stencil of the theta scheme (streaming path) ------------------
 
-// out[i] = e2 x[i-2] + e1 x[i-1] + e0 x[i] + e1 x[i+1] + e2 x[i+2], periodic
-// in the row index, interleaved [n][ld] arrays (separate input and output).
-template <typename T>
+// out[i] = e2 x[i-2] + e1 x[i-1] + e0 x[i] + e1 x[i+1] + e2 x[i+2]
+//          (+ rr (phi[i-1] - 2 phi[i] + phi[i+1]), phi = x^3 - x, when CH),
+// periodic in the row index, interleaved [n][ld] arrays (separate input and
+// output).
+template <typename T, bool CH>
 __global__ void k_hyper_explicit(int64_t n, int64_t batch, int64_t ldi, int64_t ldo, T e0, T e1,
-                                 T e2, const T *__restrict__ in, T *__restrict__ out)
+                                 T e2, T rr, const T *__restrict__ in, T *__restrict__ out)
 {
     const int64_t s = lane_id();
     if (s >= batch) return;
@@ -593,6 +632,11 @@ __global__ void k_hyper_explicit(int64_t n, int64_t batch, int64_t ldi, int64_t 
     T *o = out + s;
     T xm2 = c[(n - 2) * ldi], xm1 = c[(n - 1) * ldi], x0 = c[0], xp1 = c[ldi];
     const T first0 = x0, first1 = xp1;
+    T qa = T(0), qb = T(0);     // phi of rows i-1, i
+    if constexpr (CH) {
+        qa = fma(xm1 * xm1, xm1, -xm1);
+        qb = fma(x0 * x0, x0, -x0);
+    }
     for (int64_t i = 0; i < n; ++i) {
         const T xp2 = i + 2 < n ? c[(i + 2) * ldi] : (i + 2 == n ? first0 : first1);
         T f = e2 * xm2;
@@ -600,6 +644,11 @@ __global__ void k_hyper_explicit(int64_t n, int64_t batch, int64_t ldi, int64_t 
         f = fma(e0, x0, f);
         f = fma(e1, xp1, f);
         f = fma(e2, xp2, f);
+        if constexpr (CH) {
+            const T qc = fma(xp1 * xp1, xp1, -xp1);
+            f = fma(rr, fma(T(-2), qb, qa + qc), f);
+            qa = qb; qb = qc;
+        }
         o[i * ldo] = f;
         xm2 = xm1; xm1 = x0; x0 = xp1; xp1 = xp2;
     }
@@ -616,10 +665,16 @@ __global__ void k_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_
 
 template <typename T>
 bps_status launch_hyper_explicit(int64_t n, int64_t batch, int64_t ldi, int64_t ldo, double e0,
-                                 double e1, double e2, const void *in, void *out, hipStream_t st)
+                                 double e1, double e2, double rr, bool ch, const void *in,
+                                 void *out, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_hyper_explicit<T>), dim3(unsigned((batch + 255) / 256)), dim3(256), 0, st,
-                       n, batch, ldi, ldo, T(e0), T(e1), T(e2), (const T *)in, (T *)out);
+    const dim3 grid(unsigned((batch + 255) / 256)), block(256);
+    if (ch)
+        hipLaunchKernelGGL((k_hyper_explicit<T, true>), grid, block, 0, st, n, batch, ldi, ldo,
+                           T(e0), T(e1), T(e2), T(rr), (const T *)in, (T *)out);
+    else
+        hipLaunchKernelGGL((k_hyper_explicit<T, false>), grid, block, 0, st, n, batch, ldi, ldo,
+                           T(e0), T(e1), T(e2), T(rr), (const T *)in, (T *)out);
     BPS_LAUNCHED("k_hyper_explicit");
     return BPS_OK;
 }
@@ -636,7 +691,8 @@ bps_status launch_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_
 
 #define BPS_INST(T)                                                                             \
     template bps_status launch_hyper_explicit<T>(int64_t, int64_t, int64_t, int64_t, double,     \
-                                                 double, double, const void *, void *, hipStream_t); \
+                                                 double, double, double, bool, const void *,     \
+                                                 void *, hipStream_t);                            \
     template bps_status launch_copy_interleaved<T>(int64_t, int64_t, int64_t, int64_t,          \
                                                    const void *, void *, hipStream_t);
 BPS_INST(float)

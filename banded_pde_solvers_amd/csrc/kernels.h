@@ -36,16 +36,21 @@ bps_status launch_hyper_diagonals(int64_t n, double sigma, void *diag, hipStream
 // resident path does not apply to n.
 int resident_chunk(int64_t n);
 size_t resident_coef_bytes(int64_t n);
-// ex: theta scheme, the right-hand side of every step is the explicit
-// stencil (e2, e1, e0, e1, e2) of the state; sigma is then theta * sigma.
+// Right-hand side of every step of the resident kernel (mode bits): the
+// state (0: implicit step), or the explicit stencil (e2, e1, e0, e1, e2) of
+// the state (kResStencil: theta scheme; sigma is then theta * sigma), plus
+// rr D2 (C^3 - C) with kResPhase (Cahn-Hilliard).
+enum { kResStencil = 1, kResPhase = 2 };
 bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t nsteps, double sigma,
-                                 bool ex, double e0, double e1, double e2, void *coef, void *C,
-                                 hipStream_t st);
-// Streaming theta scheme: the explicit stencil into a separate array, and a
-// strided copy between interleaved arrays.
+                                 int mode, double e0, double e1, double e2, double rr, void *coef,
+                                 void *C, hipStream_t st);
+// Streaming theta / Cahn-Hilliard right-hand side: the explicit stencil
+// (+ rr D2 (C^3 - C) when ch) into a separate array, and a strided copy
+// between interleaved arrays.
 template <typename T>
 bps_status launch_hyper_explicit(int64_t n, int64_t batch, int64_t ldi, int64_t ldo, double e0,
-                                 double e1, double e2, const void *in, void *out, hipStream_t st);
+                                 double e1, double e2, double rr, bool ch, const void *in,
+                                 void *out, hipStream_t st);
 template <typename T>
 bps_status launch_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_t ldo,
                                    const void *in, void *out, hipStream_t st);

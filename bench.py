@@ -18,14 +18,15 @@ HBM sees the state once in and once out per call) and a "cpu_baseline"
 object (the CPU oracle, OpenMP over systems, timed on a bounded sample of
 the same workload on this host's cores).
 
-    python bench.py [--steps K] [--warmup W] [--workload {1,2,3,4,5}]
+    python bench.py [--steps K] [--warmup W] [--workload {1,2,3,4,5,6}]
 
 --workload selects another workload for manual measurements
 (2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
 512 x 100000; 4: Hines multi, 32768 neurons of 256..2048 compartments,
 20 solves per step; 5: the default shape time-stepped with Crank-Nicolson,
-theta = 1/2, 24 algorithmic flops per unknown per time step).  Only one GPU
-is used; --gpus above 1 exits.
+theta = 1/2, 24 algorithmic flops per unknown per time step; 6: the same grid
+and batch for the Cahn-Hilliard equation, semi-implicit, 25 flops).  Only one
+GPU is used; --gpus above 1 exits.
 """
 import argparse
 import json
@@ -152,22 +153,31 @@ def _cpu_baseline(run_sample, unknowns_per_system, label, seconds):
 # ---------------------------------------------------------------------------
 
 def bench_hyperdiffusion(args, which=1):
+    """Workloads 1 (implicit), 5 (Crank-Nicolson) and 6 (Cahn-Hilliard): the
+    register-resident periodic solver with the matching right-hand side."""
     import numpy as np
     import torch
     import banded_pde_solvers_amd as bps
     import workloads as W
 
     cfg = W.WORKLOADS[which]
+    kind = cfg["kind"]
     n, batch, nsteps, dt, dx = cfg["n"], cfg["batch"], cfg["nsteps"], cfg["dt"], cfg["dx"]
     theta = cfg.get("theta")
-    C = torch.as_tensor(W.hyperdiffusion_random(n, batch), device="cuda:0")
-    if theta is None:
-        work = torch.empty(bps.hyperdiffusion_work_bytes(n, batch), dtype=torch.uint8, device="cuda:0")
+    dev = "cuda:0"
+    if kind == "hyperdiffusion":
+        C = torch.as_tensor(W.hyperdiffusion_random(n, batch), device=dev)
+        work = torch.empty(bps.hyperdiffusion_work_bytes(n, batch), dtype=torch.uint8, device=dev)
         run = lambda k: bps.hyperdiffusion_step(C, dt, dx, k, work)
-    else:
-        work = torch.empty(bps.hyperdiffusion_theta_work_bytes(n, batch), dtype=torch.uint8,
-                           device="cuda:0")
+    elif kind == "hyperdiffusion_theta":
+        C = torch.as_tensor(W.hyperdiffusion_random(n, batch), device=dev)
+        work = torch.empty(bps.hyperdiffusion_theta_work_bytes(n, batch), dtype=torch.uint8, device=dev)
         run = lambda k: bps.hyperdiffusion_theta_step(C, dt, dx, theta, k, work)
+    else:
+        gamma, mob = cfg["gamma"], cfg["mobility"]
+        C = torch.as_tensor(W.cahn_hilliard_quench(n, batch), device=dev)
+        work = torch.empty(bps.cahn_hilliard_work_bytes(n, batch), dtype=torch.uint8, device=dev)
+        run = lambda k: bps.cahn_hilliard_step(C, dt, dx, gamma, mob, theta, k, work)
     wall, per = _time_loop(lambda: run(nsteps), args.steps, args.warmup)
     # the operator set-up alone (diagonals + shared factorisation), same stream
     _, setup = _time_loop(lambda: run(0), 10, 2)
@@ -179,27 +189,43 @@ def bench_hyperdiffusion(args, which=1):
     # fp64 vector arithmetic.  Algorithmic flops per unknown per time step of
     # the periodic LU solve: forward 2 FMA + 1 MUL, corner dot products 2 FMA,
     # back substitution 2 FMA, rank-2 corner correction 2 FMA = 17 flops.
-    # The theta scheme adds the explicit stencil, at least 7 flops in its
-    # symmetric form e0 x_i + e1 (x_i-1 + x_i+1) + e2 (x_i-2 + x_i+2).
-    flops_per = 17.0 if theta is None else 24.0
+    # A theta < 1 right-hand side adds the explicit stencil, at least 7 flops
+    # in its symmetric form e0 x_i + e1 (x_i-1 + x_i+1) + e2 (x_i-2 + x_i+2);
+    # the Cahn-Hilliard term r (phi_i-1 - 2 phi_i + phi_i+1), phi = x^3 - x
+    # (x (x x - 1): 3 flops per row), adds 3 + 3 + 2 = 8.
+    flops_per = 17.0
+    if theta is not None and theta != 1.0:
+        flops_per += 7.0
+    if kind == "cahn_hilliard":
+        flops_per += 8.0
     alg_flops = flops_per * unknowns
     achieved = alg_flops / (kern_ms * 1e-3) / 1e12
     hbm_bytes = 16.0 * n * batch                     # C read once, written once
-    scheme = "implicit" if theta is None else f"theta = {theta}"
+    label = {"hyperdiffusion": "periodic hyperdiffusion implicit steps",
+             "hyperdiffusion_theta": "periodic hyperdiffusion Crank-Nicolson steps",
+             "cahn_hilliard": "periodic Cahn-Hilliard semi-implicit steps"}[kind]
+    config = {"workload": cfg["name"], "n": n, "batch": batch, "time_steps_per_step": nsteps,
+              "dt": dt, "dx": dx}
+    if kind == "cahn_hilliard":
+        r = cfg["mobility"] * dt / dx ** 2
+        config.update(gamma=cfg["gamma"], mobility=cfg["mobility"], theta=theta, r=r,
+                      sigma=cfg["gamma"] * r / dx ** 2)
+    else:
+        config.update(sigma=dt / dx ** 4, scheme="implicit" if theta is None else f"theta = {theta}")
+    config["coefficients"] = "constant (factor once)"
     line = {
-        "metric": "unknowns solved/s (fp64), periodic hyperdiffusion " +
-                  ("implicit steps" if theta is None else "Crank-Nicolson steps"),
+        "metric": "unknowns solved/s (fp64), " + label,
         "value": unknowns / (ms_step * 1e-3),
         "unit": "unknowns/s",
         "ms_per_step": ms_step,
         "dtype": "f64",
-        "config": {"workload": cfg["name"], "n": n, "batch": batch, "time_steps_per_step": nsteps,
-                   "dt": dt, "dx": dx, "sigma": dt / dx ** 4, "scheme": scheme,
-                   "coefficients": "constant (factor once)"},
+        "config": config,
         "roofline": {"bound": "alu", "kernel": "k_hyper_resident<64,16>",
                      "achieved": achieved, "peak": FP64_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP64_VALU_PEAK_TFLOPS,
-                     "traffic": _traffic("hyperdiffusion" if theta is None else "hyperdiffusion_theta"),
+                     "traffic": _traffic({"hyperdiffusion": "hyperdiffusion",
+                                          "hyperdiffusion_theta": "hyperdiffusion_theta",
+                                          "cahn_hilliard": "cahn_hilliard"}[kind]),
                      "kernel_ms": kern_ms, "setup_ms": statistics.median(setup),
                      "flops_per_unknown_step": flops_per,
                      "flops_per_launch": alg_flops, "hbm_bytes_per_launch": hbm_bytes,
@@ -207,17 +233,22 @@ def bench_hyperdiffusion(args, which=1):
     }
     if not args.no_cpu_baseline:
         import oracle
-        C0 = W.hyperdiffusion_random(n, 2048, rng=np.random.default_rng(77))
+        if kind == "cahn_hilliard":
+            C0 = W.cahn_hilliard_quench(n, 2048, rng=np.random.default_rng(77))
+        else:
+            C0 = W.hyperdiffusion_random(n, 2048, rng=np.random.default_rng(77))
 
         def sample(k):
             reps = (k + 2047) // 2048
             for r in range(reps):
                 kk = min(2048, k - r * 2048)
                 x = W.to_flat(C0[:, :kk])
-                if theta is None:
+                if kind == "hyperdiffusion":
                     oracle.hyperdiffusion(x, dt, dx, nsteps)
-                else:
+                elif kind == "hyperdiffusion_theta":
                     oracle.hyperdiffusion_theta(x, dt, dx, theta, nsteps)
+                else:
+                    oracle.cahn_hilliard(x, dt, dx, cfg["gamma"], cfg["mobility"], theta, nsteps)
         line["cpu_baseline"] = _cpu_baseline(sample, n * nsteps, f"systems x {nsteps} steps",
                                              args.cpu_seconds)
     return line
@@ -366,7 +397,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workload 2 only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -399,7 +430,8 @@ def main():
     import banded_pde_solvers_amd as bps
     bps.load_library()
     fn = {1: bench_hyperdiffusion, 2: bench_penta, 3: lambda a: _hines_common(a, False),
-          4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5)}[args.workload]
+          4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5),
+          6: lambda a: bench_hyperdiffusion(a, 6)}[args.workload]
     line = fn(args)
     out = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"),
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

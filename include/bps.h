@@ -206,6 +206,35 @@ BPS_API bps_status hyperdiffusion_theta_step(int dtype, int64_t n, int64_t batch
                                      int64_t nsteps, void *work, void *stream);
 
 /* ======================================================================== */
+/* Cahn-Hilliard  [P] introduction (model equation and its time scheme)     */
+/* ======================================================================== */
+
+/* Bytes of `work` for cahn_hilliard_step (0 if invalid). */
+BPS_API size_t cahn_hilliard_work_bytes(int dtype, int64_t n, int64_t batch);
+
+/* Advance `batch` periodic 1-D concentration fields of the Cahn-Hilliard
+ * equation dC/dt = D d_xx (C^3 - C - gamma d_xx C) by `nsteps` steps of the
+ * semi-implicit scheme: the phase-separation term at the old time level,
+ * the fourth-order term with the theta family,
+ *     (I + theta*sigma*D4) C^{k+1} = (I - (1 - theta)*sigma*D4) C^k
+ *                                    + r * D2 ((C^k)^3 - C^k),
+ * r = mobility*dt/(dx*dx), sigma = gamma*r/(dx*dx), D2 = [1, -2, 1] and D4 =
+ * [1, -4, 6, -4, 1] wrapping modulo n.  theta = 1 is the semi-implicit scheme
+ * (fourth-order term fully implicit); theta = 1/2 treats it like the page's
+ * Crank-Nicolson hyperdiffusion step.  The implicit matrix is factored once
+ * per call; the explicit side is the stencil of hyperdiffusion_theta_step
+ * plus the phase-separation term.  Stability of the explicit term is the
+ * caller's concern (steps are computed as asked).
+ * C: device, interleaved [n][ld]; C^0 on entry, C^{nsteps} on return.
+ * work: device, cahn_hilliard_work_bytes(dtype, n, batch) bytes.
+ * n >= 6, batch >= 1, ld >= batch, nsteps >= 0, dt and dx finite, dx != 0,
+ * gamma and mobility finite and >= 0, 0 <= theta <= 1 (else BPS_EINVAL). */
+BPS_API bps_status cahn_hilliard_step(int dtype, int64_t n, int64_t batch, int64_t ld,
+                              double dt, double dx, double gamma, double mobility,
+                              double theta, void *C, int64_t nsteps, void *work,
+                              void *stream);
+
+/* ======================================================================== */
 /* Hines tree-tridiagonal systems  [H] sections 2-4                         */
 /* ======================================================================== */
 

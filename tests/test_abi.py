@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for required in ("penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
                      "penta_factor_solve_batch", "hines_solve_batch", "hyperdiffusion_step",
-                     "hyperdiffusion_theta_step",
+                     "hyperdiffusion_theta_step", "cahn_hilliard_step",
                      "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack"):
         assert required in names
 
@@ -112,6 +112,27 @@ def test_hyperdiffusion_rejects_bad_arguments(lib):
     assert f(2, 16, 4, 4, 1e-6, 0.1, None, _fake(), -1, _fake(1), None) == EINVAL
     assert f(2, 16, 4, 3, 1e-6, 0.1, None, _fake(), 1, _fake(1), None) == EINVAL  # ld < batch
     assert f(2, 16, 4, 4, 1e-6, 0.1, None, None, 1, _fake(1), None) == EINVAL
+
+
+def test_cahn_hilliard_rejects_bad_arguments(lib):
+    f = lib.cahn_hilliard_step
+    ok = (2, 16, 4, 4, 1e-6, 0.1, 1e-4, 1.0, 1.0, _fake(), 1, _fake(1), None)
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[{"n": 1, "dx": 5, "gamma": 6, "mob": 7, "theta": 8, "nsteps": 10}[k]] = v
+        return f(*args)
+    assert call(gamma=-1e-4) == EINVAL
+    assert call(gamma=float("inf")) == EINVAL
+    assert call(mob=float("nan")) == EINVAL
+    assert call(mob=-1.0) == EINVAL
+    assert call(theta=1.01) == EINVAL
+    assert call(n=5) == EINVAL
+    assert call(dx=0.0) == EINVAL
+    assert call(nsteps=-2) == EINVAL
+    assert lib.cahn_hilliard_work_bytes(2, 1024, 100) == lib.hyperdiffusion_theta_work_bytes(2, 1024, 100)
+    assert lib.cahn_hilliard_work_bytes(1, 4, 3) == 0
 
 
 def test_theta_step_rejects_bad_arguments(lib):

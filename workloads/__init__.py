@@ -97,6 +97,13 @@ def hyperdiffusion_random(n: int = 1024, batch: int = 16384,
     return rng.uniform(-1.0, 1.0, size=(n, batch)).astype(dtype)
 
 
+def cahn_hilliard_quench(n: int = 1024, batch: int = 16384, amp: float = 0.1,
+                         rng: np.random.Generator | None = None) -> np.ndarray:
+    """A quench from the well-mixed state: C ~ U(-amp, amp) as shape (n, batch)."""
+    rng = rng if rng is not None else rng_for(6)
+    return rng.uniform(-amp, amp, size=(n, batch))
+
+
 # ----------------------------------------------------------------------------
 # General pentadiagonal systems, per-system coefficients
 # ----------------------------------------------------------------------------
@@ -270,7 +277,8 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
 
 # ----------------------------------------------------------------------------
 # The named workloads at their full sizes (5: the headline shape time-stepped
-# with Crank-Nicolson instead of backward Euler)
+# with Crank-Nicolson instead of backward Euler; 6: the same grid and batch
+# for the Cahn-Hilliard equation)
 # ----------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -284,4 +292,8 @@ WORKLOADS = {
             batch=32768, nmin=256, nmax=2048, nsteps=20),
     5: dict(name="cn_theta0.5_n1024_b16384_100steps", kind="hyperdiffusion_theta",
             n=1024, batch=16384, dt=1e-6, dx=1.0 / 1024, nsteps=100, theta=0.5),
+    # semi-implicit Cahn-Hilliard quench: interface width sqrt(gamma) = 10 dx
+    6: dict(name="cahn_hilliard_n1024_b16384_100steps", kind="cahn_hilliard",
+            n=1024, batch=16384, dt=1e-6, dx=1.0 / 1024, gamma=1e-4, mobility=1.0, theta=1.0,
+            nsteps=100),
 }
