@@ -24,6 +24,8 @@ Functions and the passages they follow:
   cahn_hilliard          -- cuPentBatch page, introduction: the Cahn-Hilliard
                             equation with the phase-separation term at the old
                             time level and the fourth-order term implicit
+  thomas_solve           -- Hines page, section 4.1: Thomas algorithm for
+                            tridiagonal systems (cuThomasBatch's method)
   hines_solve            -- Hines page, section 2, Algorithm 1
   hines_multi_solve      -- Algorithm 1 per neuron, one tree per neuron
 """
@@ -92,6 +94,8 @@ def _load():
                                               ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                               _D, _i64]
             lib.orc_cahn_hilliard.restype = ctypes.c_int
+            lib.orc_thomas_solve_batch.argtypes = [_i64, _i64, _D, _D, _D, _D, _I32]
+            lib.orc_thomas_solve_batch.restype = None
             lib.orc_hines_solve.argtypes = [_i64, _I32, _D, _D, _D, _D]
             lib.orc_hines_solve.restype = ctypes.c_int
             lib.orc_hines_solve_batch.argtypes = [_i64, _i64, _I32, _D, _D, _D, _D, _I32]
@@ -255,6 +259,25 @@ def cahn_hilliard_operators(n: int, dt: float, dx: float, gamma: float, mobility
 # ----------------------------------------------------------------------------
 # Hines
 # ----------------------------------------------------------------------------
+
+def thomas_solve(a, b, c, y):
+    """Thomas algorithm for a batch of tridiagonal systems (flat layout).
+
+    a (sub-diagonal, a[:, 0] ignored), b (diagonal), c (super-diagonal,
+    c[:, -1] ignored), y (right-hand side): (batch, n) or (n,).
+    Returns (u, info)."""
+    u = _batch2(y).copy()
+    batch, n = u.shape
+    a, b, c = (_batch2(v) for v in (a, b, c))
+    for v in (a, b, c):
+        if v.shape != (batch, n):
+            raise ValueError("a, b, c must match y")
+    if n < 1:
+        raise ValueError("n >= 1 needed")
+    info = np.zeros(batch, dtype=np.int32)
+    _load().orc_thomas_solve_batch(n, batch, _ptr(a), _ptr(b), _ptr(c), _ptr(u), _ptr(info, _I32))
+    return u, info
+
 
 def hines_solve(parent, u, l, d, rhs):
     """Algorithm 1 for a batch of neurons sharing one tree (flat layout).

@@ -540,6 +540,52 @@ int orc_cahn_hilliard(int64_t n, int64_t batch, double dt, double dx, double gam
 }
 
 /* ------------------------------------------------------------------------ */
+/* [H] Thomas algorithm for one tridiagonal system (section 4.1, the         */
+/* forward elimination of the lower diagonal and the backward substitution, */
+/* written 0-based): row i holds a_i (column i-1), b_i (diagonal) and c_i    */
+/* (column i+1); a_0 and c_{n-1} lie outside the matrix and are ignored.     */
+/*   c'_0 = c_0 / b_0,            y'_0 = y_0 / b_0,                            */
+/*   c'_i = c_i / (b_i - c'_{i-1} a_i),                                        */
+/*   y'_i = (y_i - y'_{i-1} a_i) / (b_i - c'_{i-1} a_i),     i = 1 .. n-1,      */
+/*   u_{n-1} = y'_{n-1},          u_i = y'_i - c'_i u_{i+1}, i = n-2 .. 0.      */
+/* cp is caller scratch (n values); y returns u.  Returns 0, or 1 + the      */
+/* first row whose pivot is zero or not finite (no pivoting, as the page).  */
+/* ------------------------------------------------------------------------ */
+
+int orc_thomas_solve(int64_t n, const double *a, const double *b, const double *c, double *y,
+                     double *cp)
+{
+    int info = 0;
+    if (bad_pivot(b[0])) info = 1;
+    cp[0] = c[0] / b[0];
+    y[0] = y[0] / b[0];
+    for (int64_t i = 1; i < n; ++i) {
+        const double den = b[i] - cp[i - 1] * a[i];
+        if (!info && bad_pivot(den)) info = (int)i + 1;
+        cp[i] = c[i] / den;
+        y[i] = (y[i] - y[i - 1] * a[i]) / den;
+    }
+    for (int64_t i = n - 2; i >= 0; --i) y[i] = y[i] - cp[i] * y[i + 1];
+    return info;
+}
+
+/* batch systems, flat arrays [batch][n]; y returns the solutions. */
+void orc_thomas_solve_batch(int64_t n, int64_t batch, const double *a, const double *b,
+                            const double *c, double *y, int32_t *info)
+{
+    #pragma omp parallel
+    {
+        double *cp = (double *)malloc(sizeof(double) * (size_t)n);
+        #pragma omp for schedule(static)
+        for (int64_t s = 0; s < batch; ++s) {
+            int inf = orc_thomas_solve(n, a + s * n, b + s * n, c + s * n, y + s * n, cp);
+            if (info) info[s] = inf;
+        }
+        free(cp);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* [H] Hines algorithm (Algorithm 1) for one tree-tridiagonal system.       */
 /*                                                                          */
 /* Matrix: A[i][i] = d_i, A[p_i][i] = u_i, A[i][p_i] = l_i, with p_i < i    */

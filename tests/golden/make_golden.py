@@ -8,6 +8,7 @@ on the pages:
   penta  -- cuPentBatch page, "Pentadiagonal solver" (five diagonals a..e)
   cyclic -- cuPentBatch page, hyperdiffusion section (periodic wrap mod n)
   hines  -- Hines page, section 2 (A[i][i]=d_i, A[p_i][i]=u_i, A[i][p_i]=l_i)
+  tri    -- Hines page, section 4.1 (row i: a_i, b_i, c_i at columns i-1, i, i+1)
 """
 import json
 import os
@@ -78,12 +79,29 @@ def main():
             x = solve_exact(dense_hines(p, u, l, d), f)
             hines.append({"n": n, "parent": p, "u": u, "l": l, "d": d, "f": f,
                           "x": [str(v) for v in x]})
+    tri = []
+    for n in (1, 2, 3, 4, 7, 10):
+        for _ in range(3):
+            a = [0] + [int(v) for v in rng.integers(-6, 7, n - 1)]
+            c = [int(v) for v in rng.integers(-6, 7, n - 1)] + [0]
+            b = [int(v) * (1 if rng.random() < .5 else -1) for v in rng.integers(13, 30, n)]
+            f = [int(v) for v in rng.integers(-9, 10, n)]
+            A = [[0] * n for _ in range(n)]
+            for i in range(n):
+                A[i][i] = b[i]
+                if i > 0:
+                    A[i][i - 1] = a[i]
+                if i < n - 1:
+                    A[i][i + 1] = c[i]
+            x = solve_exact(A, f)
+            tri.append({"n": n, "a": a, "b": b, "c": c, "f": f, "x": [str(v) for v in x]})
     hdr = ("Exact solutions (fractions) of small integer systems, written by "
            "tests/golden/make_golden.py with oracle.referee.solve_exact.")
     for name, cases, cite in (
             ("exact_penta.json", penta, "cuPentBatch page, section 'Pentadiagonal solver'"),
             ("exact_cyclic.json", cyclic, "cuPentBatch page, hyperdiffusion section, periodic matrix"),
-            ("exact_hines.json", hines, "Hines page, section 2, Hines matrix")):
+            ("exact_hines.json", hines, "Hines page, section 2, Hines matrix"),
+            ("exact_tri.json", tri, "Hines page, section 4.1, tridiagonal matrix")):
         with open(os.path.join(HERE, name), "w") as fh:
             json.dump({"about": hdr, "matrix": cite, "cases": cases}, fh, indent=0)
             fh.write("\n")

@@ -49,6 +49,12 @@ MUTANTS = {
                             "const double lap = phi[im1] - 2.0 * phi[i] + phi[ip2];"),
     "ch_r_uses_dx4": ("const double r = mobility * dt / (dx * dx);",
                       "const double r = mobility * dt / (dx * dx * dx * dx);"),
+    "thomas_pivot_drops_coupling": ("const double den = b[i] - cp[i - 1] * a[i];",
+                                    "const double den = b[i];"),
+    "thomas_rhs_wrong_index": ("y[i] = (y[i] - y[i - 1] * a[i]) / den;",
+                               "y[i] = (y[i] - y[i - 1] * a[i - 1]) / den;"),
+    "thomas_back_sign": ("for (int64_t i = n - 2; i >= 0; --i) y[i] = y[i] - cp[i] * y[i + 1];",
+                         "for (int64_t i = n - 2; i >= 0; --i) y[i] = y[i] + cp[i] * y[i + 1];"),
     "hines_rhs_uses_parent_value": ("rhs[p[i]] -= factor * rhs[i];", "rhs[p[i]] -= factor * rhs[p[i]];"),
     "hines_forward_u_for_l": ("rhs[i] -= l[i] * rhs[p[i]];", "rhs[i] -= u[i] * rhs[p[i]];"),
     "hines_d_update_uses_u": ("d[p[i]] -= factor * l[i];", "d[p[i]] -= factor * u[i];"),
@@ -131,6 +137,16 @@ def _checks(orc):
     ref = np.linalg.solve(cyclic_dense(*dgc), Bc @ C0 + r * (L2 @ (C0 ** 3 - C0)))
     if relerr(got, ref) > 1e-12:
         failed.append("ch_dense")
+    # Thomas, random dominant tridiagonal
+    n = 10
+    ta, tc = rng.uniform(-1, 1, (2, n))
+    ta[0] = tc[-1] = 0
+    tbd = 1 + np.abs(ta) + np.abs(tc) + rng.uniform(0, 1, n)
+    ty = rng.uniform(-1, 1, n)
+    u, _ = orc.thomas_solve(ta, tbd, tc, ty)
+    A = np.diag(tbd) + np.diag(ta[1:], -1) + np.diag(tc[:-1], 1)
+    if relerr(u[0], np.linalg.solve(A, ty)) > 1e-12:
+        failed.append("thomas_dense")
     # Hines, random tree, u != l
     from workloads import random_tree
     p = random_tree(30, rng, window=4)

@@ -57,3 +57,12 @@ def test_modes_distinct_wavenumbers():
     assert ic.C0.shape == (256, 64)
     for row in ic.k:
         assert len(set(row.tolist())) == 4 and row.min() >= 1 and row.max() <= 16
+
+
+def test_tri_dominance_and_outside_zeros():
+    tb = W.tri_dominant(33, 20, rng=np.random.default_rng(1), chunk=8)
+    assert np.all(tb.a[0] == 0) and np.all(tb.c[-1] == 0)
+    assert np.all(tb.b > np.abs(tb.a) + np.abs(tb.c) + 1)
+    assert np.all(tb.b < np.abs(tb.a) + np.abs(tb.c) + 2)
+    again = W.tri_dominant(33, 20, rng=np.random.default_rng(1), chunk=8)
+    np.testing.assert_array_equal(tb.y, again.y)

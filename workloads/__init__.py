@@ -160,6 +160,46 @@ def penta_dominant(n: int = 512, batch: int = 65536, cyclic: bool = False,
 
 
 # ----------------------------------------------------------------------------
+# Tridiagonal systems, per-system coefficients
+# ----------------------------------------------------------------------------
+
+@dataclass
+class TriBatch:
+    a: np.ndarray   # A[i][i-1]   (n, batch); a[0] = 0
+    b: np.ndarray   # A[i][i]
+    c: np.ndarray   # A[i][i+1];  c[n-1] = 0
+    y: np.ndarray   # right-hand side
+
+    def astype(self, dtype) -> "TriBatch":
+        return TriBatch(*(np.ascontiguousarray(v.astype(dtype)) for v in
+                          (self.a, self.b, self.c, self.y)))
+
+
+def tri_dominant(n: int = 512, batch: int = 256000, rng: np.random.Generator | None = None,
+                 chunk: int = 8192) -> TriBatch:
+    """Strictly row-dominant tridiagonal batch (the Hines page's tridiagonal
+    test systems are random with |b_i| > |a_i| + |c_i|).
+
+    a, c ~ U(-1, 1) drawn as one (2, n, batch) block (in that order), with the
+    entries outside the matrix (a_0, c_{n-1}) set to zero; then
+    b = 1 + |a| + |c| + U(0, 1) and y ~ U(-1, 1), in column blocks of
+    ``chunk`` systems (fixed, as the draws depend on it)."""
+    rng = rng if rng is not None else rng_for(7)
+    a = np.empty((n, batch)); b = np.empty((n, batch)); c = np.empty((n, batch))
+    y = np.empty((n, batch))
+    for s0 in range(0, batch, chunk):
+        s1 = min(batch, s0 + chunk)
+        w = s1 - s0
+        off = rng.uniform(-1.0, 1.0, size=(2, n, w))
+        off[0, 0, :] = 0.0
+        off[1, n - 1, :] = 0.0
+        a[:, s0:s1], c[:, s0:s1] = off
+        b[:, s0:s1] = 1.0 + np.abs(off).sum(axis=0) + rng.uniform(0.0, 1.0, size=(n, w))
+        y[:, s0:s1] = rng.uniform(-1.0, 1.0, size=(n, w))
+    return TriBatch(a, b, c, y)
+
+
+# ----------------------------------------------------------------------------
 # Hines (tree-tridiagonal) systems
 # ----------------------------------------------------------------------------
 
