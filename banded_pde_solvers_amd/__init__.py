@@ -28,6 +28,7 @@ __all__ = [
     "hyperdiffusion_work_bytes", "hyperdiffusion_step",
     "hyperdiffusion_theta_work_bytes", "hyperdiffusion_theta_step",
     "cahn_hilliard_work_bytes", "cahn_hilliard_step",
+    "tri_work_bytes", "tri_solve_batch",
     "HinesPlan", "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
     "hines_work_bytes", "hines_solve_batch",
 ]
@@ -96,6 +97,8 @@ def load_library():
             "cahn_hilliard_step": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, ctypes.c_double, vp, i64,
                                     vp, vp], st),
+            "tri_work_bytes": ([st, i64, i64], ctypes.c_size_t),
+            "tri_solve_batch": ([st, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp], st),
             "hines_plan_create": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64], st),
             "hines_plan_destroy": ([vp], st),
             "hines_plan_elems": ([vp], i64),
@@ -291,6 +294,31 @@ def cahn_hilliard_step(C, dt: float, dx: float, gamma: float, mobility: float, t
         dt_code, n, batch, ld, float(dt), float(dx), float(gamma), float(mobility), float(theta),
         _ptr(C), int(nsteps), _ptr(work), _stream(stream)))
     return C
+
+
+# ---------------------------------------------------------------------------
+# Tridiagonal
+# ---------------------------------------------------------------------------
+
+def tri_work_bytes(n: int, ld: int, dtype: int = BPS_F64) -> int:
+    return int(load_library().tri_work_bytes(int(dtype), int(n), int(ld)))
+
+
+def tri_solve_batch(a, b, c, y, work, info=None, *, batch=None, stream=None):
+    """Solve the tridiagonal systems (a, b, c) u = y in place of y; all
+    arrays interleaved (n, ld) on the device, a[0] and c[n-1] ignored."""
+    n, batch, ld = _geom(y, batch)
+    code = _dtype_code(y)
+    for name, v in (("a", a), ("b", b), ("c", c)):
+        if tuple(v.shape) != tuple(y.shape) or v.dtype != y.dtype or v.stride() != y.stride():
+            raise ValueError(f"{name} must have the shape, dtype and layout of y")
+    need = load_library().tri_work_bytes(code, n, ld)
+    if work.numel() * work.element_size() < need:
+        raise ValueError(f"work buffer too small ({need} bytes needed)")
+    _check("tri_solve_batch", load_library().tri_solve_batch(
+        code, n, batch, ld, _ptr(a), _ptr(b), _ptr(c), _ptr(y), _ptr(work), _ptr(info),
+        _stream(stream)))
+    return y
 
 
 # ---------------------------------------------------------------------------

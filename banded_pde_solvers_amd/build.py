@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbps.so")
-SOURCES = ["api.cpp", "penta.hip", "penta_spike.hip", "hyper.hip", "hines.hip"]
+SOURCES = ["api.cpp", "penta.hip", "penta_spike.hip", "hyper.hip", "hines.hip", "tri.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

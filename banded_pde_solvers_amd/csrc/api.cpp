@@ -351,6 +351,36 @@ bps_status cahn_hilliard_step(int dtype, int64_t n, int64_t batch, int64_t ld, d
                                    as_stream(stream));
 }
 
+// ---- tridiagonal ----------------------------------------------------------------
+
+size_t tri_work_bytes(int dtype, int64_t n, int64_t ld)
+{
+    if (dtype_size(dtype) == 0 || n < 1 || n > kMaxDim || ld < 1 || ld > kMaxDim) return 0;
+    return size_t(n) * size_t(ld) * dtype_size(dtype);
+}
+
+bps_status tri_solve_batch(int dtype, int64_t n, int64_t batch, int64_t ld, const void *a,
+                           const void *b, const void *c, void *y, void *work, int32_t *info,
+                           void *stream)
+{
+    clear_error();
+    if (dtype_size(dtype) == 0) BPS_FAIL(BPS_EINVAL, "unknown dtype %d", dtype);
+    if (n < 1 || n > kMaxDim) BPS_FAIL(BPS_EINVAL, "n = %lld must be in [1, 2^40]", (long long)n);
+    if (batch < 1 || batch > (int64_t(1) << 31) - kWave)
+        BPS_FAIL(BPS_EINVAL, "batch = %lld must be in [1, 2^31 - 64]", (long long)batch);
+    if (ld < batch) BPS_FAIL(BPS_EINVAL, "ld = %lld < batch = %lld", (long long)ld, (long long)batch);
+    if (n > kMaxDim / ld) BPS_FAIL(BPS_EINVAL, "n * ld too large");
+    CHECK(check_ptr(a, "a", dtype));
+    CHECK(check_ptr(b, "b", dtype));
+    CHECK(check_ptr(c, "c", dtype));
+    CHECK(check_ptr(y, "y", dtype));
+    CHECK(check_ptr(work, "work", dtype));
+    if (info && !aligned(info, 4)) BPS_FAIL(BPS_EINVAL, "info is not 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    return dtype == BPS_F64 ? launch_tri_solve<double>(n, batch, ld, a, b, c, y, work, info, st)
+                            : launch_tri_solve<float>(n, batch, ld, a, b, c, y, work, info, st);
+}
+
 // ---- Hines ----------------------------------------------------------------------
 
 bps_status hines_plan_create(bps_hines_plan **plan, int64_t batch, const int32_t *sizes,

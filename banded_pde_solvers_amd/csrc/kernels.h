@@ -55,6 +55,13 @@ template <typename T>
 bps_status launch_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_t ldo,
                                    const void *in, void *out, hipStream_t st);
 
+// Batched tridiagonal solve (chunked for n = 16 P, 2 <= P <= 64, else one
+// lane per system); work holds n x ld values.  tri_chunks(n) is P, or 0.
+int tri_chunks(int64_t n);
+template <typename T>
+bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
+                            const void *c, void *y, void *work, int32_t *info, hipStream_t st);
+
 // Number of values of a factor buffer.
 inline int64_t penta_factor_elems(int64_t n, int64_t ldf, bool cyclic) {
     return cyclic ? (9 * (n - 2) + 4) * ldf : 5 * n * ldf;

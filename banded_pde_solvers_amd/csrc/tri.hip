@@ -1,0 +1,254 @@
+// tri.hip -- batched tridiagonal systems with per-system coefficients
+// (the Hines page, section 4.1: the Thomas algorithm and cuThomasBatch, one
+// system per thread on the interleaved layout), for gfx950.
+//
+// Thomas on one lane per system must write c' of every row and read it back
+// (a 16-byte-per-row round trip in fp64 on top of the 32 bytes in and 8 out),
+// and a batch of a few thousand systems fills only a few percent of the
+// chip.  For n = 16 P (2 <= P <= 64) each system is instead split into P
+// chunks of 16 rows, one lane per chunk:
+//
+//   rows 0 .. 14 of a chunk ("interior") form a tridiagonal block E_j that
+//   couples to the previous chunk's last row (the interface unknown
+//   xI_{j-1}, through its row 0 entry a_0) and to its own last row (xI_j,
+//   through its row 14 entry c_14).  With the Thomas factors of E_j,
+//     y = R^{-1} (g - xI_{j-1} gv) with y_15 = xI_j,   g = L^{-1} f,
+//     gv = L^{-1} (a_0 e_0),  R unit upper bidiagonal with c'_i above,
+//   the last interior row is y_14 = g_14 - xI_{j-1} gv_14 - c'_14 xI_j and
+//   the first is y_0 = z0 - xI_{j-1} p0 - xI_j q0 with z0 = w . g,
+//   p0 = w . gv, q0 = w_14 c'_14, w = R^{-T} e_0 (w_0 = 1,
+//   w_i = -c'_{i-1} w_{i-1}).  Each interface row then reads
+//     L_j xI_{j-1} + D_j xI_j + U_j xI_{j+1} = R_j,
+//     L_j = -a gv_14,  D_j = b - a c'_14 - c p0_{j+1},  U_j = -c q0_{j+1},
+//     R_j = f - a g_14 - c z0_{j+1}   (a, b, c, f of the interface row),
+//   a scalar tridiagonal system over the chunks, solved by parallel cyclic
+//   reduction through LDS (ceil(log2 P) steps).  Each lane keeps c', g and
+//   gv of its rows in registers and back-substitutes once xI is known: the
+//   four inputs are read once and the solution written once.
+// A system whose chunked elimination meets a zero or non-finite pivot is
+// re-solved in the same launch by the sequential Thomas algorithm, so info
+// and the result are those of the page's method.
+#include "common.h"
+#include "kernels.h"
+
+namespace bps {
+
+// Thomas on one system (column s already applied to the pointers): c' to
+// work (n x ld), y' then the solution in place of y.  Returns 1 + the first
+// row whose pivot is zero or not finite, 0 when there is none.  a_0 and
+// c_{n-1} lie outside the matrix and are not read.
+template <typename T>
+__device__ int32_t seq_thomas(int64_t n, int64_t ld, const T *A, const T *B, const T *C, T *Y,
+                              T *work)
+{
+    int32_t bad = 0;
+    T cpp = 0, yp = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t o = i * ld;
+        const T ai = i > 0 ? A[o] : T(0);
+        const T ci = i + 1 < n ? C[o] : T(0);
+        const T den = B[o] - cpp * ai;
+        if (!bad && bad_pivot(den)) bad = int32_t(i) + 1;
+        const T r = T(1) / den;
+        const T cp = ci * r;
+        const T yv = (Y[o] - yp * ai) * r;
+        work[o] = cp;
+        Y[o] = yv;
+        cpp = cp; yp = yv;
+    }
+    T un = 0;
+    for (int64_t i = n - 1; i >= 0; --i) {
+        const int64_t o = i * ld;
+        const T v = (i + 1 < n) ? Y[o] - work[o] * un : Y[o];
+        Y[o] = v;
+        un = v;
+    }
+    return bad;
+}
+
+// cuThomasBatch: one lane per system on the interleaved layout.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_tri_thomas(int64_t n, int64_t batch, int64_t ld, const T *__restrict__ A,
+             const T *__restrict__ B, const T *__restrict__ C, T *__restrict__ Y,
+             T *__restrict__ work, int32_t *__restrict__ info)
+{
+    const int64_t s = lane_id();
+    if (s >= batch) return;
+    const int32_t r = seq_thomas<T>(n, ld, A + s, B + s, C + s, Y + s, work + s);
+    if (info) info[s] = r;
+}
+
+// One workgroup holds S systems x P chunks of M rows (lane = chunk j of
+// system sl); n = P * M, P * S <= 512.  Dynamic LDS: 4 * P * S values of T
+// + S flags.
+template <typename T, int M, int S>
+__global__ void __launch_bounds__(512)
+k_tri_chunk(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
+            const T *__restrict__ C, T *__restrict__ Y, T *__restrict__ work,
+            int32_t *__restrict__ info)
+{
+    constexpr int m = M - 1;            // interior rows of a chunk
+    extern __shared__ unsigned char lds_raw[];
+    T *buf = reinterpret_cast<T *>(lds_raw);          // [field][P][S]
+    int32_t *flag = reinterpret_cast<int32_t *>(buf + 4 * P * S);
+    const int tid = threadIdx.x;
+    if (tid < S) flag[tid] = 0;
+    const int j = tid / S, sl = tid % S;
+    // workgroups are dispatched round-robin over the 8 XCDs: the ones one
+    // XCD runs back to back take neighbouring systems, so that a 128-byte
+    // line shared by two workgroups is fetched once, through one L2
+    const unsigned nb = gridDim.x, bid = blockIdx.x, full = nb & ~7u;
+    const unsigned tile = bid < full ? (bid & 7u) * (full >> 3) + (bid >> 3) : bid;
+    const int64_t s = int64_t(tile) * S + sl;
+    const bool act = s < batch;
+    // lanes past the end of the batch shadow the last system (identical
+    // values, identical stores, no branches around memory operations)
+    const int64_t off = (act ? s : batch - 1) + int64_t(j) * M * ld;
+    const T *pa = A + off, *pb = B + off, *pc = C + off;
+    T *py = Y + off;
+    auto F = [&](int field, int jj) -> T & { return buf[(field * P + jj) * S + sl]; };
+    const bool first_chunk = (j == 0), last_chunk = (j == P - 1);
+
+    // ---- forward sweep over the interior, inputs streamed LA rows ahead ----
+    constexpr int LA = 4;
+    T qa[LA], qb[LA], qc[LA], qy[LA];
+#pragma unroll
+    for (int k = 0; k < LA; ++k) {
+        const int64_t o = int64_t(k) * ld;
+        qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qy[k] = py[o];
+    }
+    T cp[m], g[m], gv[m];
+    T cpp = 0, gp = 0, gvp = 0, w = 1, z0 = 0, p0 = 0;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+        const int k = i % LA;
+        const T a_i = qa[k], b_i = qb[k], c_i = qc[k], f_i = qy[k];
+        {
+            const int64_t o = int64_t(i + LA < M ? i + LA : M - 1) * ld;
+            qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qy[k] = py[o];
+        }
+        const T ai = (i > 0) ? a_i : T(0);                         // entry of E_j
+        const T al = (i == 0 && !first_chunk) ? a_i : T(0);         // coupling to xI_{j-1}
+        const T den = b_i - cpp * ai;
+        bad |= bad_pivot(den);
+        const T r = T(1) / den;
+        const T cpi = c_i * r;          // row m-1: the coupling to xI_j
+        const T gi = (f_i - ai * gp) * r;
+        const T gvi = (al - ai * gvp) * r;
+        if (i > 0) w = -cpp * w;
+        z0 += w * gi;
+        p0 += w * gvi;
+        cp[i] = cpi; g[i] = gi; gv[i] = gvi;
+        cpp = cpi; gp = gi; gvp = gvi;
+    }
+    const T q0 = w * cp[m - 1];
+    constexpr int kI = m % LA;          // the interface row (local row m)
+    const T aI = qa[kI], bI = qb[kI], cI = last_chunk ? T(0) : qc[kI], fI = qy[kI];
+
+    // ---- publish first-row quantities; build interface row j ----
+    F(0, j) = z0; F(1, j) = p0; F(2, j) = q0;
+    __syncthreads();
+    T nz0 = 0, np0 = 0, nq0 = 0;
+    if (!last_chunk) { nz0 = F(0, j + 1); np0 = F(1, j + 1); nq0 = F(2, j + 1); }
+    T Lj = -aI * gv[m - 1];
+    T Dj = bI - aI * cp[m - 1] - cI * np0;
+    T Uj = -cI * nq0;
+    T Rj = fI - aI * g[m - 1] - cI * nz0;
+    __syncthreads();
+    // ---- parallel cyclic reduction across the P chunks of the system ----
+    for (int h = 1; h < P; h <<= 1) {
+        bad |= bad_pivot(Dj);
+        F(0, j) = Lj; F(1, j) = T(1) / Dj; F(2, j) = Uj; F(3, j) = Rj;
+        __syncthreads();
+        T nL = 0, nU = 0, nD = Dj, nR = Rj;
+        if (j - h >= 0) {
+            const int q = j - h;
+            const T al = -Lj * F(1, q);
+            nL = al * F(0, q);
+            nD += al * F(2, q);
+            nR += al * F(3, q);
+        }
+        if (j + h < P) {
+            const int q = j + h;
+            const T be = -Uj * F(1, q);
+            nU = be * F(2, q);
+            nD += be * F(0, q);
+            nR += be * F(3, q);
+        }
+        Lj = nL; Uj = nU; Dj = nD; Rj = nR;
+        __syncthreads();
+    }
+    bad |= bad_pivot(Dj);
+    const T xI = Rj / Dj;
+    F(0, j) = xI;
+    if (bad) atomicOr(&flag[sl], 1);
+    __syncthreads();
+    const T xL = first_chunk ? T(0) : F(0, j - 1);
+    if (flag[sl]) {
+        // an interior pivot or a reduced diagonal broke down: redo this
+        // system with the sequential algorithm, which also sets info
+        if (first_chunk && act) {
+            const int32_t r = seq_thomas<T>(int64_t(P) * M, ld, A + s, B + s, C + s, Y + s, work + s);
+            if (info) info[s] = r;
+        }
+        return;
+    }
+    if (first_chunk && act && info) info[s] = 0;
+    // ---- back substitution y_i = g_i - xI_{j-1} gv_i - c'_i y_{i+1} ----
+    T yn = xI;
+#pragma unroll
+    for (int i = m - 1; i >= 0; --i) {
+        const T v = g[i] - gv[i] * xL - cp[i] * yn;
+        py[int64_t(i) * ld] = v;
+        yn = v;
+    }
+    py[int64_t(m) * ld] = xI;
+}
+
+// Chunked path applies when n = P * 16 with 2 <= P <= 64.
+int tri_chunks(int64_t n)
+{
+    if (n % 16 != 0) return 0;
+    const int64_t P = n / 16;
+    return (P >= 2 && P <= 64) ? int(P) : 0;
+}
+
+template <typename T, int S>
+static void launch_chunk(int P, int64_t batch, int64_t ld, const void *a, const void *b,
+                         const void *c, void *y, void *work, int32_t *info, hipStream_t st)
+{
+    const size_t lds = size_t(4) * P * S * sizeof(T) + S * sizeof(int32_t);
+    const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
+    hipLaunchKernelGGL((k_tri_chunk<T, 16, S>), grid, block, lds, st, P, batch, ld, (const T *)a,
+                       (const T *)b, (const T *)c, (T *)y, (T *)work, info);
+}
+
+template <typename T>
+bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
+                            const void *c, void *y, void *work, int32_t *info, hipStream_t st)
+{
+    if (batch == 0) return BPS_OK;
+    if (const int P = tri_chunks(n)) {
+        // 16 systems per workgroup (a 128-byte row segment in fp64), 32 for
+        // short systems so that a workgroup fills a wavefront, 8 for long
+        // ones so that it stays within 512 lanes
+        if (P < 4) launch_chunk<T, 32>(P, batch, ld, a, b, c, y, work, info, st);
+        else if (P <= 32) launch_chunk<T, 16>(P, batch, ld, a, b, c, y, work, info, st);
+        else launch_chunk<T, 8>(P, batch, ld, a, b, c, y, work, info, st);
+        BPS_LAUNCHED("k_tri_chunk");
+        return BPS_OK;
+    }
+    hipLaunchKernelGGL((k_tri_thomas<T>), dim3(unsigned((batch + 255) / 256)), dim3(256), 0, st, n,
+                       batch, ld, (const T *)a, (const T *)b, (const T *)c, (T *)y, (T *)work, info);
+    BPS_LAUNCHED("k_tri_thomas");
+    return BPS_OK;
+}
+
+template bps_status launch_tri_solve<float>(int64_t, int64_t, int64_t, const void *, const void *,
+                                            const void *, void *, void *, int32_t *, hipStream_t);
+template bps_status launch_tri_solve<double>(int64_t, int64_t, int64_t, const void *, const void *,
+                                             const void *, void *, void *, int32_t *, hipStream_t);
+
+}  // namespace bps

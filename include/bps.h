@@ -235,6 +235,34 @@ BPS_API bps_status cahn_hilliard_step(int dtype, int64_t n, int64_t batch, int64
                               void *stream);
 
 /* ======================================================================== */
+/* Tridiagonal systems  [H] section 4.1 (Thomas algorithm, cuThomasBatch)   */
+/* ======================================================================== */
+
+/* Bytes of `work` for tri_solve_batch with this n and ld (n*ld values;
+ * 0 if invalid). */
+BPS_API size_t tri_work_bytes(int dtype, int64_t n, int64_t ld);
+
+/* Solve `batch` independent tridiagonal systems A u = y, row i of system s
+ * holding a_i (column i-1), b_i (diagonal) and c_i (column i+1); a_0 and
+ * c_{n-1} lie outside the matrix and are ignored.
+ * a, b, c, y: device, interleaved [n][ld] (element (i, s) at i*ld + s);
+ * a, b, c are not modified; y holds the right-hand sides on entry and the
+ * solutions on return.  work: device, tri_work_bytes(dtype, n, ld) bytes,
+ * scratch (contents undefined on return).  info: device int32[batch] or
+ * NULL: 0, or 1 + the first row whose pivot of the page's Thomas
+ * elimination (no pivoting) is zero or non-finite.
+ * For n = 16*P with 2 <= P <= 64 the systems are solved in 16-row chunks
+ * (each eliminated with its own pivots, joined by a scalar tridiagonal
+ * interface system); a system whose chunked elimination meets a zero or
+ * non-finite pivot is re-solved in the same launch by the sequential Thomas
+ * algorithm, so info and the solution are those of the page's method.
+ * Other n: one lane per system (cuThomasBatch).
+ * n >= 1, 1 <= batch <= 2^31 - 64, ld >= batch (else BPS_EINVAL). */
+BPS_API bps_status tri_solve_batch(int dtype, int64_t n, int64_t batch, int64_t ld,
+                           const void *a, const void *b, const void *c, void *y,
+                           void *work, int32_t *info, void *stream);
+
+/* ======================================================================== */
 /* Hines tree-tridiagonal systems  [H] sections 2-4                         */
 /* ======================================================================== */
 

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for required in ("penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
                      "penta_factor_solve_batch", "hines_solve_batch", "hyperdiffusion_step",
-                     "hyperdiffusion_theta_step", "cahn_hilliard_step",
+                     "hyperdiffusion_theta_step", "cahn_hilliard_step", "tri_solve_batch",
                      "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack"):
         assert required in names
 
@@ -112,6 +112,21 @@ def test_hyperdiffusion_rejects_bad_arguments(lib):
     assert f(2, 16, 4, 4, 1e-6, 0.1, None, _fake(), -1, _fake(1), None) == EINVAL
     assert f(2, 16, 4, 3, 1e-6, 0.1, None, _fake(), 1, _fake(1), None) == EINVAL  # ld < batch
     assert f(2, 16, 4, 4, 1e-6, 0.1, None, None, 1, _fake(1), None) == EINVAL
+
+
+def test_tri_rejects_bad_arguments(lib):
+    f = lib.tri_solve_batch
+    p = [_fake(i) for i in range(5)]
+    assert f(3, 16, 4, 4, *p, None, None) == EINVAL          # dtype
+    assert f(2, 0, 4, 4, *p, None, None) == EINVAL           # n < 1
+    assert f(2, 16, 0, 4, *p, None, None) == EINVAL          # batch < 1
+    assert f(2, 16, 5, 4, *p, None, None) == EINVAL          # ld < batch
+    assert f(2, 16, 4, 4, None, *p[1:], None, None) == EINVAL
+    assert f(2, 16, 4, 4, *p[:4], None, None, None) == EINVAL   # work
+    assert f(2, 16, 4, 4, ctypes.c_void_p(12), *p[1:], None, None) == EINVAL   # misaligned
+    assert lib.tri_work_bytes(2, 100, 37) == 100 * 37 * 8
+    assert lib.tri_work_bytes(1, 100, 37) == 100 * 37 * 4
+    assert lib.tri_work_bytes(2, 0, 37) == 0
 
 
 def test_cahn_hilliard_rejects_bad_arguments(lib):

@@ -1,0 +1,128 @@
+"""GPU parity: batched tridiagonal solves (tri_solve_batch) against the
+oracle's Thomas algorithm (Hines page, section 4.1), through the C-ABI.
+
+Per system on identical inputs: normwise relative error <= 1e-10 (fp64) /
+1e-4 (fp32 against the fp64 oracle of the fp32-rounded inputs); the test
+matrices are row-dominant with margin >= 1, so both eliminations are
+backward stable and well conditioned.  info is compared exactly."""
+import numpy as np
+import pytest
+import torch
+
+import banded_pde_solvers_amd as bps
+import oracle
+import workloads as W
+from gpu_util import TOL, buf, dev, host, relerr_cols, rounded
+
+pytestmark = pytest.mark.gpu
+
+
+def _solve(tb, dtype=torch.float64, batch=None, with_info=True):
+    n, ld = tb.y.shape
+    b_ = ld if batch is None else batch
+    a, b, c, y = (dev(v, dtype) for v in (tb.a, tb.b, tb.c, tb.y))
+    code = bps.BPS_F64 if dtype == torch.float64 else bps.BPS_F32
+    work = buf(bps.tri_work_bytes(n, ld, code))
+    info = torch.full((b_,), -7, dtype=torch.int32, device=y.device) if with_info else None
+    bps.tri_solve_batch(a, b, c, y, work, info, batch=batch)
+    return host(y), (info.cpu().numpy() if with_info else None), (a, b, c)
+
+
+def _oracle(tb, dtype=torch.float64, cols=None):
+    arrs = [rounded(v if cols is None else v[:, cols], dtype) for v in (tb.a, tb.b, tb.c, tb.y)]
+    u, info = oracle.thomas_solve(*(W.to_flat(v) for v in arrs))
+    return u.T, info
+
+
+@pytest.mark.parametrize("n,batch", [(32, 37), (48, 100), (64, 20), (80, 33), (256, 50),
+                                     (512, 17), (1024, 9),                 # chunked
+                                     (1, 70), (2, 5), (3, 64), (17, 65), (100, 33), (2048, 10)])
+def test_parity_fp64(n, batch):
+    print(f"tri n={n} batch={batch}", flush=True)
+    tb = W.tri_dominant(n, batch, rng=np.random.default_rng(n * 7 + batch))
+    got, info, _ = _solve(tb)
+    ref, rinfo = _oracle(tb)
+    assert np.all(info == 0) and np.all(rinfo == 0)
+    assert relerr_cols(got, ref) <= TOL[torch.float64]
+
+
+@pytest.mark.parametrize("n,batch", [(64, 100), (512, 40), (1024, 16), (100, 30)])
+def test_parity_fp32(n, batch):
+    tb = W.tri_dominant(n, batch, rng=np.random.default_rng(n + 1))
+    got, info, _ = _solve(tb, torch.float32)
+    ref, _ = _oracle(tb, torch.float32)
+    assert np.all(info == 0)
+    assert relerr_cols(got, ref) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("n", [256, 100])
+def test_leading_dimension_inputs_untouched(n):
+    batch, ld = 30, 48
+    tb = W.tri_dominant(n, ld, rng=np.random.default_rng(3))
+    got, info, (a, b, c) = _solve(tb, batch=batch)
+    ref, _ = _oracle(tb, cols=slice(0, batch))
+    assert relerr_cols(got[:, :batch], ref) <= TOL[torch.float64]
+    np.testing.assert_array_equal(got[:, batch:], tb.y[:, batch:])
+    for d, h in ((a, tb.a), (b, tb.b), (c, tb.c)):
+        np.testing.assert_array_equal(host(d), h)
+    assert np.all(info == 0)
+
+
+@pytest.mark.parametrize("n", [256, 96])
+def test_breakdown_info_and_sequential_rescue(n):
+    """System 3: b_0 = 0 (the page's elimination stops at row 1: info 1).
+    System 5: b_16 = 0 but a_16 c_15 != 0, so the sequential pivot of row 16
+    is nonzero while the chunked elimination (chunk 1 starts at row 16) meets
+    a zero pivot: it must fall back and still match the oracle.  System 8:
+    an exactly zero pivot deep inside (a_40 = b_40 = 0: info 41 whatever
+    the rounding of the earlier factors)."""
+    batch = 12
+    tb = W.tri_dominant(n, batch, rng=np.random.default_rng(11))
+    tb.b[0, 3] = 0.0
+    tb.b[16, 5] = 0.0
+    tb.a[40, 8] = 0.0
+    tb.b[40, 8] = 0.0
+    got, info, _ = _solve(tb)
+    ref, rinfo = _oracle(tb)
+    assert info[3] == rinfo[3] == 1
+    assert info[8] == rinfo[8] == 41
+    assert info[5] == rinfo[5] == 0
+    ok = [s for s in range(batch) if s not in (3, 8)]
+    assert relerr_cols(got[:, ok], ref[:, ok]) <= TOL[torch.float64]
+
+
+def test_info_optional():
+    tb = W.tri_dominant(512, 40, rng=np.random.default_rng(5))
+    got, _, _ = _solve(tb, with_info=False)
+    ref, _ = _oracle(tb)
+    assert relerr_cols(got, ref) <= TOL[torch.float64]
+
+
+def test_chunked_and_sequential_agree():
+    """The same systems through the chunked path (n = 512) and, embedded in a
+    system one row longer with a decoupled extra row, through the one-lane
+    path: the first 512 rows of both solutions agree to 1e-13."""
+    n, batch = 512, 64
+    tb = W.tri_dominant(n, batch, rng=np.random.default_rng(21))
+    got, _, _ = _solve(tb)
+    big = W.TriBatch(*(np.vstack([v, np.ones((1, batch))]) for v in (tb.a, tb.b, tb.c, tb.y)))
+    big.a[n] = 0.0
+    big.c[n - 1] = 0.0
+    got2, _, _ = _solve(big)
+    assert relerr_cols(got, got2[:n]) <= 1e-13
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("which", [7, 8])
+def test_page_sizes_sampled(which):
+    """The page's largest tridiagonal cases, as benchmarked: sampled systems
+    against the oracle."""
+    cfg = W.WORKLOADS[which]
+    n, batch = cfg["n"], cfg["batch"]
+    print(f"tri workload {n}x{batch}", flush=True)
+    tb = W.tri_dominant(n, batch)
+    got, info, _ = _solve(tb)
+    cols = np.unique(np.r_[0, 15, 16, batch - 1, np.random.default_rng(7).integers(0, batch, 40)])
+    ref, rinfo = _oracle(tb, cols=cols)
+    assert np.all(info == 0)
+    assert relerr_cols(got[:, cols], ref) <= TOL[torch.float64]

@@ -318,7 +318,7 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
 # ----------------------------------------------------------------------------
 # The named workloads at their full sizes (5: the headline shape time-stepped
 # with Crank-Nicolson instead of backward Euler; 6: the same grid and batch
-# for the Cahn-Hilliard equation)
+# for the Cahn-Hilliard equation; 7, 8: batched tridiagonal systems)
 # ----------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -336,4 +336,8 @@ WORKLOADS = {
     6: dict(name="cahn_hilliard_n1024_b16384_100steps", kind="cahn_hilliard",
             n=1024, batch=16384, dt=1e-6, dx=1.0 / 1024, gamma=1e-4, mobility=1.0, theta=1.0,
             nsteps=100),
+    # the Hines page's tridiagonal test cases: the largest of the "small"
+    # systems and of the long ones
+    7: dict(name="tri_n512_b256000", kind="tri", n=512, batch=256000),
+    8: dict(name="tri_n8192_b20000", kind="tri", n=8192, batch=20000),
 }
