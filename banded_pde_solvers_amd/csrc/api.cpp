@@ -356,7 +356,7 @@ bps_status cahn_hilliard_step(int dtype, int64_t n, int64_t batch, int64_t ld, d
 size_t tri_work_bytes(int dtype, int64_t n, int64_t ld)
 {
     if (dtype_size(dtype) == 0 || n < 1 || n > kMaxDim || ld < 1 || ld > kMaxDim) return 0;
-    return size_t(n) * size_t(ld) * dtype_size(dtype);
+    return tri_work_bytes_es(n, ld, dtype_size(dtype));
 }
 
 bps_status tri_solve_batch(int dtype, int64_t n, int64_t batch, int64_t ld, const void *a,

@@ -55,9 +55,13 @@ template <typename T>
 bps_status launch_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_t ldo,
                                    const void *in, void *out, hipStream_t st);
 
-// Batched tridiagonal solve (chunked for n = 16 P, 2 <= P <= 64, else one
-// lane per system); work holds n x ld values.  tri_chunks(n) is P, or 0.
+// Batched tridiagonal solve: register-resident chunks for n = 16 P,
+// 2 <= P <= 64 (tri_chunks(n) is P, or 0); chunks spread over workgroups for
+// n = 16 P, 64 < P <= 65535 (tri_part_chunks); else one lane per system.
+// Work: tri_work_bytes_es(n, ld, sizeof(T)) bytes.
 int tri_chunks(int64_t n);
+int tri_part_chunks(int64_t n);
+size_t tri_work_bytes_es(int64_t n, int64_t ld, size_t es);
 template <typename T>
 bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
                             const void *c, void *y, void *work, int32_t *info, hipStream_t st);

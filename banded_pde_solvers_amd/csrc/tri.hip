@@ -215,6 +215,168 @@ int tri_chunks(int64_t n)
     return (P >= 2 && P <= 64) ? int(P) : 0;
 }
 
+// ---- partitioned path for long systems (n = 16 P, P > 64) ------------------
+//
+// The same chunk algebra as k_tri_chunk, with the chunks of a system spread
+// over many workgroups (a wavefront holds 64 neighbouring systems at the same
+// chunk, so every row access is a contiguous 512-byte segment):
+//   1. k_tri_part_fwd: Thomas over each chunk interior, writing six numbers
+//      per chunk: g, gv, c' of the last interior row and z0, p0, q0;
+//   2. k_tri_part_iface: the interface rows (L_j, D_j, U_j, R_j) from them;
+//   3. the interface system (P unknowns per system) by launch_tri_solve;
+//   4. k_tri_part_back: each chunk's forward sweep again, now with the left
+//      interface value known, and its back substitution;
+//   5. k_tri_part_rescue: the sequential algorithm for systems whose chunk
+//      or interface elimination met a bad pivot (it also writes info).
+// HBM: the four inputs twice, the solution once, about 10 values per chunk.
+constexpr int kPartM = 16;
+
+int tri_part_chunks(int64_t n)
+{
+    if (n % kPartM != 0) return 0;
+    const int64_t P = n / kPartM;
+    return (P > 64 && P <= 65535) ? int(P) : 0;    // the chunk index is blockIdx.y
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_tri_part_fwd(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
+               const T *__restrict__ C, const T *__restrict__ Y, T *__restrict__ summ,
+               int32_t *__restrict__ flag)
+{
+    constexpr int M = kPartM, m = M - 1;
+    const int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int j = int(blockIdx.y);
+    if (s >= batch) return;
+    const int64_t off = s + int64_t(j) * M * ld;
+    const T *pa = A + off, *pb = B + off, *pc = C + off, *py = Y + off;
+    T cpp = 0, gp = 0, gvp = 0, w = 1, z0 = 0, p0 = 0;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+        const int64_t o = int64_t(i) * ld;
+        const T a_i = pa[o], b_i = pb[o], c_i = pc[o], f_i = py[o];
+        const T ai = (i > 0) ? a_i : T(0);
+        const T al = (i == 0 && j > 0) ? a_i : T(0);
+        const T den = b_i - cpp * ai;
+        bad |= bad_pivot(den);
+        const T r = T(1) / den;
+        const T cpi = c_i * r;
+        const T gi = (f_i - ai * gp) * r;
+        const T gvi = (al - ai * gvp) * r;
+        if (i > 0) w = -cpp * w;
+        z0 += w * gi;
+        p0 += w * gvi;
+        cpp = cpi; gp = gi; gvp = gvi;
+    }
+    const int64_t so = int64_t(P) * ld;
+    T *o = summ + int64_t(j) * ld + s;
+    o[0] = gp; o[so] = gvp; o[2 * so] = cpp; o[3 * so] = z0; o[4 * so] = p0; o[5 * so] = w * cpp;
+    if (bad) flag[s] = 1;
+}
+
+// Interface row j: L_j = -a gv, D_j = b - a c' - c p0_{j+1},
+// U_j = -c q0_{j+1}, R_j = f - a g - c z0_{j+1} into the arrays lo, di, up,
+// rh ([P][ld] each).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_tri_part_iface(int P, int64_t batch, int64_t ld, const T *__restrict__ A,
+                 const T *__restrict__ B, const T *__restrict__ C, const T *__restrict__ Y,
+                 const T *__restrict__ summ, T *__restrict__ lo, T *__restrict__ di,
+                 T *__restrict__ up, T *__restrict__ rh)
+{
+    const int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int j = int(blockIdx.y);
+    if (s >= batch) return;
+    const int64_t row = (int64_t(j) * kPartM + kPartM - 1) * ld + s;
+    const T aI = A[row], bI = B[row], fI = Y[row];
+    const bool last = (j == P - 1);
+    const T cI = last ? T(0) : C[row];
+    const int64_t so = int64_t(P) * ld;
+    const T *own = summ + int64_t(j) * ld + s;
+    const T G = own[0], V = own[so], cpm = own[2 * so];
+    T nz0 = 0, np0 = 0, nq0 = 0;
+    if (!last) {
+        const T *nx = own + ld;
+        nz0 = nx[3 * so]; np0 = nx[4 * so]; nq0 = nx[5 * so];
+    }
+    const int64_t o = int64_t(j) * ld + s;
+    lo[o] = -aI * V;
+    di[o] = bI - aI * cpm - cI * np0;
+    up[o] = -cI * nq0;
+    rh[o] = fI - aI * G - cI * nz0;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_tri_part_back(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
+                const T *__restrict__ C, T *__restrict__ Y, const T *__restrict__ xI,
+                const int32_t *__restrict__ flag, const int32_t *__restrict__ info2)
+{
+    constexpr int M = kPartM, m = M - 1;
+    const int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int j = int(blockIdx.y);
+    if (s >= batch) return;
+    if (flag[s] || info2[s]) return;          // left to the sequential rescue
+    const T xL = j > 0 ? xI[int64_t(j - 1) * ld + s] : T(0);
+    const T xR = xI[int64_t(j) * ld + s];
+    const int64_t off = s + int64_t(j) * M * ld;
+    const T *pa = A + off, *pb = B + off, *pc = C + off;
+    T *py = Y + off;
+    T cp[m], g[m];
+    T cpp = 0, gp = 0;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+        const int64_t o = int64_t(i) * ld;
+        const T a_i = pa[o], b_i = pb[o], c_i = pc[o], f_i = py[o];
+        const T ai = (i > 0) ? a_i : T(0);
+        const T fi = (i == 0 && j > 0) ? f_i - a_i * xL : f_i;
+        const T r = T(1) / (b_i - cpp * ai);
+        cp[i] = c_i * r;
+        g[i] = (fi - ai * gp) * r;
+        cpp = cp[i]; gp = g[i];
+    }
+    T yn = xR;
+#pragma unroll
+    for (int i = m - 1; i >= 0; --i) {
+        yn = g[i] - cp[i] * yn;
+        py[int64_t(i) * ld] = yn;
+    }
+    py[int64_t(m) * ld] = xR;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_tri_part_rescue(int64_t n, int64_t batch, int64_t ld, const T *__restrict__ A,
+                  const T *__restrict__ B, const T *__restrict__ C, T *__restrict__ Y,
+                  T *__restrict__ work, const int32_t *__restrict__ flag,
+                  const int32_t *__restrict__ info2, int32_t *__restrict__ info)
+{
+    const int64_t s = lane_id();
+    if (s >= batch) return;
+    int32_t r = 0;
+    if (flag[s] || info2[s]) r = seq_thomas<T>(n, ld, A + s, B + s, C + s, Y + s, work + s);
+    if (info) info[s] = r;
+}
+
+__global__ void k_tri_fill_zero(int64_t count, int32_t *__restrict__ p)
+{
+    const int64_t i = lane_id();
+    if (i < count) p[i] = 0;
+}
+
+// Work of a solve of n rows (bytes).  Partitioned path (values of T unless
+// noted): [n ld: c' of the rescue] [6 P ld: chunk summaries] [4 P ld:
+// interface rows] [ld int32: flags] [ld int32: info of the interface solve]
+// [the work of the interface solve, P rows]; other paths: n ld values.
+size_t tri_work_bytes_es(int64_t n, int64_t ld, size_t es)
+{
+    if (const int P = tri_part_chunks(n))
+        return size_t(n + 10 * int64_t(P)) * size_t(ld) * es + 2 * size_t(ld) * sizeof(int32_t) +
+               tri_work_bytes_es(P, ld, es);
+    return size_t(n) * size_t(ld) * es;
+}
+
 template <typename T, int S>
 static void launch_chunk(int P, int64_t batch, int64_t ld, const void *a, const void *b,
                          const void *c, void *y, void *work, int32_t *info, hipStream_t st)
@@ -226,10 +388,40 @@ static void launch_chunk(int P, int64_t batch, int64_t ld, const void *a, const 
 }
 
 template <typename T>
+static bps_status launch_tri_part(int P, int64_t batch, int64_t ld, const T *a, const T *b,
+                                  const T *c, T *y, void *work, int32_t *info, hipStream_t st)
+{
+    const int64_t n = int64_t(P) * kPartM, pl = int64_t(P) * ld;
+    T *w0 = static_cast<T *>(work);
+    T *summ = w0 + n * ld;
+    T *lo = summ + 6 * pl, *di = lo + pl, *up = di + pl, *rh = up + pl;
+    int32_t *flag = reinterpret_cast<int32_t *>(rh + pl);
+    int32_t *info2 = flag + ld;
+    void *iw = info2 + ld;          // 8-byte aligned: 2 ld int32 above
+    const dim3 blk(256), grid2(unsigned((batch + 255) / 256), unsigned(P));
+    const dim3 grid1(unsigned((batch + 255) / 256));
+    hipLaunchKernelGGL(k_tri_fill_zero, grid1, blk, 0, st, batch, flag);
+    hipLaunchKernelGGL((k_tri_part_fwd<T>), grid2, blk, 0, st, P, batch, ld, a, b, c, y, summ, flag);
+    hipLaunchKernelGGL((k_tri_part_iface<T>), grid2, blk, 0, st, P, batch, ld, a, b, c, y, summ, lo,
+                       di, up, rh);
+    bps_status r = launch_tri_solve<T>(P, batch, ld, lo, di, up, rh, iw, info2, st);
+    if (r != BPS_OK) return r;
+    hipLaunchKernelGGL((k_tri_part_back<T>), grid2, blk, 0, st, P, batch, ld, a, b, c, y, rh, flag,
+                       info2);
+    hipLaunchKernelGGL((k_tri_part_rescue<T>), grid1, blk, 0, st, n, batch, ld, a, b, c, y, w0,
+                       flag, info2, info);
+    BPS_LAUNCHED("k_tri_part");
+    return BPS_OK;
+}
+
+template <typename T>
 bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
                             const void *c, void *y, void *work, int32_t *info, hipStream_t st)
 {
     if (batch == 0) return BPS_OK;
+    if (const int P = tri_part_chunks(n))
+        return launch_tri_part<T>(P, batch, ld, (const T *)a, (const T *)b, (const T *)c, (T *)y,
+                                  work, info, st);
     if (const int P = tri_chunks(n)) {
         // 16 systems per workgroup (a 128-byte row segment in fp64), 32 for
         // short systems so that a workgroup fills a wavefront, 8 for long

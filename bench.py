@@ -18,15 +18,16 @@ HBM sees the state once in and once out per call) and a "cpu_baseline"
 object (the CPU oracle, OpenMP over systems, timed on a bounded sample of
 the same workload on this host's cores).
 
-    python bench.py [--steps K] [--warmup W] [--workload {1,2,3,4,5,6}]
+    python bench.py [--steps K] [--warmup W] [--workload {1,...,8}]
 
 --workload selects another workload for manual measurements
 (2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
 512 x 100000; 4: Hines multi, 32768 neurons of 256..2048 compartments,
 20 solves per step; 5: the default shape time-stepped with Crank-Nicolson,
 theta = 1/2, 24 algorithmic flops per unknown per time step; 6: the same grid
-and batch for the Cahn-Hilliard equation, semi-implicit, 25 flops).  Only one
-GPU is used; --gpus above 1 exits.
+and batch for the Cahn-Hilliard equation, semi-implicit, 25 flops; 7, 8:
+batched tridiagonal solves, 512 x 256000 and 8192 x 20000, --dtype f64|f32).
+Only one GPU is used; --gpus above 1 exits.
 """
 import argparse
 import json
@@ -305,6 +306,62 @@ def bench_penta(args):
     return line
 
 
+def bench_tri(args, which):
+    """Workloads 7, 8: batched tridiagonal solves (the Hines page's
+    cuThomasBatch test cases), per-system coefficients, fp64 or fp32."""
+    import numpy as np
+    import torch
+    import banded_pde_solvers_amd as bps
+    import workloads as W
+
+    cfg = W.WORKLOADS[which]
+    n, batch = cfg["n"], cfg["batch"]
+    dt = torch.float32 if args.dtype == "f32" else torch.float64
+    tb = W.tri_dominant(n, batch)
+    a, b, c, y = (torch.as_tensor(v, device="cuda:0").to(dt) for v in (tb.a, tb.b, tb.c, tb.y))
+    del tb
+    code = bps.BPS_F32 if dt == torch.float32 else bps.BPS_F64
+    work = torch.empty(bps.tri_work_bytes(n, batch, code), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        bps.tri_solve_batch(a, b, c, y, work)
+    wall, per = _time_loop(step, args.steps, args.warmup)
+    ms_step = wall * 1e3 / args.steps
+    if n % 16 == 0 and 2 <= n // 16 <= 64:
+        kname = "k_tri_chunk"
+    elif n % 16 == 0 and 64 < n // 16 <= 65535:
+        kname = "k_tri_part"        # five kernels per call: timed as a whole
+    else:
+        kname = "k_tri_thomas"
+    es = 4 if dt == torch.float32 else 8
+    unknowns = n * batch
+    alg_bytes = 5.0 * es * unknowns                  # a, b, c, y in, u out
+    kern_ms = statistics.mean(per)
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    line = {
+        "metric": f"unknowns solved/s ({args.dtype}), batched tridiagonal solve",
+        "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
+        "dtype": args.dtype,
+        "config": {"workload": cfg["name"], "n": n, "batch": batch, "coefficients": "per system"},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": _traffic(f"{kname[2:]}_n{n}_{args.dtype}"), "kernel_ms": kern_ms,
+                     "bytes_per_launch": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        k0 = max(1, min(batch, (1 << 22) // n))
+        small = W.tri_dominant(n, k0, rng=np.random.default_rng(9))
+        fl = [W.to_flat(v) for v in (small.a, small.b, small.c, small.y)]
+
+        def sample(k):
+            for r in range((k + k0 - 1) // k0):
+                kk = min(k0, k - r * k0)
+                oracle.thomas_solve(*(v[:kk] for v in fl))
+        line["cpu_baseline"] = _cpu_baseline(sample, n, "systems", args.cpu_seconds)
+    return line
+
+
 def _hines_common(args, multi):
     import numpy as np
     import torch
@@ -397,8 +454,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6])
-    ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workload 2 only")
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -431,7 +488,8 @@ def main():
     bps.load_library()
     fn = {1: bench_hyperdiffusion, 2: bench_penta, 3: lambda a: _hines_common(a, False),
           4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5),
-          6: lambda a: bench_hyperdiffusion(a, 6)}[args.workload]
+          6: lambda a: bench_hyperdiffusion(a, 6), 7: lambda a: bench_tri(a, 7),
+          8: lambda a: bench_tri(a, 8)}[args.workload]
     line = fn(args)
     out = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"),
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

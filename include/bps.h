@@ -238,8 +238,8 @@ BPS_API bps_status cahn_hilliard_step(int dtype, int64_t n, int64_t batch, int64
 /* Tridiagonal systems  [H] section 4.1 (Thomas algorithm, cuThomasBatch)   */
 /* ======================================================================== */
 
-/* Bytes of `work` for tri_solve_batch with this n and ld (n*ld values;
- * 0 if invalid). */
+/* Bytes of `work` for tri_solve_batch with this n and ld (n*ld values, a
+ * little more for n = 16*P with P > 64; 0 if invalid). */
 BPS_API size_t tri_work_bytes(int dtype, int64_t n, int64_t ld);
 
 /* Solve `batch` independent tridiagonal systems A u = y, row i of system s
@@ -256,7 +256,10 @@ BPS_API size_t tri_work_bytes(int dtype, int64_t n, int64_t ld);
  * interface system); a system whose chunked elimination meets a zero or
  * non-finite pivot is re-solved in the same launch by the sequential Thomas
  * algorithm, so info and the solution are those of the page's method.
- * Other n: one lane per system (cuThomasBatch).
+ * For n = 16*P with 64 < P <= 65535 the chunks of a system are spread
+ * over many workgroups (per-chunk elimination, the interface system solved
+ * by this same routine, then each chunk's substitution), with the same
+ * sequential rescue.  Other n: one lane per system (cuThomasBatch).
  * n >= 1, 1 <= batch <= 2^31 - 64, ld >= batch (else BPS_EINVAL). */
 BPS_API bps_status tri_solve_batch(int dtype, int64_t n, int64_t batch, int64_t ld,
                            const void *a, const void *b, const void *c, void *y,

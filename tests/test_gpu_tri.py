@@ -36,7 +36,9 @@ def _oracle(tb, dtype=torch.float64, cols=None):
 
 @pytest.mark.parametrize("n,batch", [(32, 37), (48, 100), (64, 20), (80, 33), (256, 50),
                                      (512, 17), (1024, 9),                 # chunked
-                                     (1, 70), (2, 5), (3, 64), (17, 65), (100, 33), (2048, 10)])
+                                     (1040, 21), (2048, 10), (4096, 300),  # partitioned
+                                     (16640, 3),                           # two levels
+                                     (1, 70), (2, 5), (3, 64), (17, 65), (100, 33), (1000, 7)])
 def test_parity_fp64(n, batch):
     print(f"tri n={n} batch={batch}", flush=True)
     tb = W.tri_dominant(n, batch, rng=np.random.default_rng(n * 7 + batch))
@@ -46,7 +48,7 @@ def test_parity_fp64(n, batch):
     assert relerr_cols(got, ref) <= TOL[torch.float64]
 
 
-@pytest.mark.parametrize("n,batch", [(64, 100), (512, 40), (1024, 16), (100, 30)])
+@pytest.mark.parametrize("n,batch", [(64, 100), (512, 40), (1024, 16), (100, 30), (2048, 20)])
 def test_parity_fp32(n, batch):
     tb = W.tri_dominant(n, batch, rng=np.random.default_rng(n + 1))
     got, info, _ = _solve(tb, torch.float32)
@@ -55,7 +57,7 @@ def test_parity_fp32(n, batch):
     assert relerr_cols(got, ref) <= TOL[torch.float32]
 
 
-@pytest.mark.parametrize("n", [256, 100])
+@pytest.mark.parametrize("n", [256, 100, 2048])
 def test_leading_dimension_inputs_untouched(n):
     batch, ld = 30, 48
     tb = W.tri_dominant(n, ld, rng=np.random.default_rng(3))
@@ -68,7 +70,7 @@ def test_leading_dimension_inputs_untouched(n):
     assert np.all(info == 0)
 
 
-@pytest.mark.parametrize("n", [256, 96])
+@pytest.mark.parametrize("n", [256, 96, 2048])
 def test_breakdown_info_and_sequential_rescue(n):
     """System 3: b_0 = 0 (the page's elimination stops at row 1: info 1).
     System 5: b_16 = 0 but a_16 c_15 != 0, so the sequential pivot of row 16
@@ -126,3 +128,28 @@ def test_page_sizes_sampled(which):
     ref, rinfo = _oracle(tb, cols=cols)
     assert np.all(info == 0)
     assert relerr_cols(got[:, cols], ref) <= TOL[torch.float64]
+
+
+def test_partitioned_and_sequential_agree():
+    """n = 2048 through the partitioned path and, embedded in a system one row
+    longer with a decoupled extra row, through the one-lane path."""
+    n, batch = 2048, 40
+    tb = W.tri_dominant(n, batch, rng=np.random.default_rng(23))
+    got, _, _ = _solve(tb)
+    big = W.TriBatch(*(np.vstack([v, np.ones((1, batch))]) for v in (tb.a, tb.b, tb.c, tb.y)))
+    big.a[n] = 0.0
+    big.c[n - 1] = 0.0
+    got2, _, _ = _solve(big)
+    assert relerr_cols(got, got2[:n]) <= 1e-13
+
+
+def test_partitioned_interface_breakdown_rescued():
+    """A zero pivot that only the partitioned elimination meets, at the first
+    row of a chunk far from the start (row 16 * 70 = 1120), is rescued."""
+    n, batch = 2048, 8
+    tb = W.tri_dominant(n, batch, rng=np.random.default_rng(29))
+    tb.b[1120, 2] = 0.0
+    got, info, _ = _solve(tb)
+    ref, rinfo = _oracle(tb)
+    assert np.all(info == 0) and np.all(rinfo == 0)
+    assert relerr_cols(got, ref) <= TOL[torch.float64]
