@@ -425,9 +425,12 @@ bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a,
     if (const int P = tri_chunks(n)) {
         // 16 systems per workgroup (a 128-byte row segment in fp64), 32 for
         // short systems so that a workgroup fills a wavefront, 8 for long
-        // ones so that it stays within 512 lanes
+        // ones so that it stays within 512 lanes.  fp64 at 32 chunks: 8
+        // systems (256 lanes, three workgroups per CU at 168 VGPRs instead
+        // of one of 512) measured 4% faster; fp32 loses with 32-byte rows.
         if (P < 4) launch_chunk<T, 32>(P, batch, ld, a, b, c, y, work, info, st);
-        else if (P <= 32) launch_chunk<T, 16>(P, batch, ld, a, b, c, y, work, info, st);
+        else if (P < 32 || (P == 32 && sizeof(T) == 4))
+            launch_chunk<T, 16>(P, batch, ld, a, b, c, y, work, info, st);
         else launch_chunk<T, 8>(P, batch, ld, a, b, c, y, work, info, st);
         BPS_LAUNCHED("k_tri_chunk");
         return BPS_OK;

@@ -108,8 +108,21 @@ def pmc_summary(args):
     f_copy, _ = mean_of(cfetch, args.copy_match)
     w_copy, _ = mean_of(cwrite, args.copy_match)
     f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
-    f_k, nf = mean_of(fetch, args.pmc_match)
-    w_k, nw = mean_of(write, args.pmc_match)
+    if args.pmc_calls_match:
+        # a call of several kernels: all matching dispatches summed, divided
+        # by the number of calls (dispatches of the one kernel named here)
+        def per_call(path):
+            rows = list(csv.DictReader(open(path)))
+            tot = sum(float(r["Counter_Value"]) for r in rows if args.pmc_match in r["Kernel_Name"])
+            calls = sum(1 for r in rows if args.pmc_calls_match in r["Kernel_Name"])
+            if not calls:
+                raise SystemExit(f"no dispatch of {args.pmc_calls_match!r} in {path}")
+            return tot / calls, calls
+        f_k, nf = per_call(fetch)
+        w_k, nw = per_call(write)
+    else:
+        f_k, nf = mean_of(fetch, args.pmc_match)
+        w_k, nw = mean_of(write, args.pmc_match)
     fb, wb = f_k * f_scale * 1024, w_k * w_scale * 1024
     ent = {"kernel": args.pmc_match, "bytes_per_launch": fb + wb, "fetch_bytes": fb,
            "write_bytes": wb, "fetch_scale": f_scale, "write_scale": w_scale,
@@ -466,6 +479,8 @@ def main():
     ap.add_argument("--pmc-match", default="k_hyper_resident<")
     ap.add_argument("--pmc-source", default="banded_pde_solvers_amd/csrc/hyper.hip")
     ap.add_argument("--copy-match", default="copyBuffer")
+    ap.add_argument("--pmc-calls-match", default=None,
+                    help="sum the --pmc-match dispatches per call of this kernel")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)
