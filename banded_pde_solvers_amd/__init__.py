@@ -174,8 +174,10 @@ def bps_penta_factor_bytes(n: int, batch: int, ld: int, dtype: int = BPS_F64, fl
     return int(load_library().bps_penta_factor_bytes(ctypes.byref(_desc(dtype, flags, n, batch, ld))))
 
 
-def bps_penta_work_bytes(n: int, batch: int, ld: int, dtype: int = BPS_F64) -> int:
-    return int(load_library().bps_penta_work_bytes(ctypes.byref(_desc(dtype, 0, n, batch, ld))))
+def bps_penta_work_bytes(n: int, batch: int, ld: int, dtype: int = BPS_F64,
+                         cyclic: bool = False) -> int:
+    return int(load_library().bps_penta_work_bytes(
+        ctypes.byref(_desc(dtype, BPS_CYCLIC if cyclic else 0, n, batch, ld))))
 
 
 def _flags(cyclic, shared):
@@ -225,10 +227,11 @@ def penta_cyclic_solve_batch(factors, x, *, batch=None, shared=False, stream=Non
     return x
 
 
-def penta_factor_solve_batch(a, b, c, d, e, x, work, info=None, *, batch=None, stream=None):
-    """Fused factor + solve, per-system non-periodic diagonals (n, ld)."""
+def penta_factor_solve_batch(a, b, c, d, e, x, work, info=None, *, batch=None, cyclic=False,
+                             stream=None):
+    """Fused factor + solve, per-system diagonals (n, ld); cyclic: periodic."""
     n, batch, ld = _geom(x, batch)
-    dsc = _desc(_dtype_code(x), 0, n, batch, ld)
+    dsc = _desc(_dtype_code(x), BPS_CYCLIC if cyclic else 0, n, batch, ld)
     need = load_library().bps_penta_work_bytes(ctypes.byref(dsc))
     if work.numel() * work.element_size() < need:
         raise ValueError(f"work buffer too small ({need} bytes needed)")

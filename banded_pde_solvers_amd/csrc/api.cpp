@@ -149,7 +149,10 @@ bps_status penta_cyclic_solve_batch(const bps_penta_desc *dsc, const void *facto
 size_t bps_penta_work_bytes(const bps_penta_desc *dsc)
 {
     if (check_desc(dsc) != BPS_OK) return 0;
-    return size_t(2 * dsc->n * dsc->ld) * dtype_size(dsc->dtype);
+    const size_t es = dtype_size(dsc->dtype);
+    if (dsc->flags & BPS_CYCLIC)     // periodic factors, then a mask of int32[ld]
+        return size_t(penta_factor_elems(dsc->n, dsc->ld, true)) * es + size_t(dsc->ld) * 4;
+    return size_t(2 * dsc->n * dsc->ld) * es;
 }
 
 bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, const void *b,
@@ -158,19 +161,39 @@ bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, co
 {
     clear_error();
     CHECK(check_desc(dsc));
-    if (dsc->flags != 0)
-        BPS_FAIL(BPS_ENOTSUP, "penta_factor_solve_batch supports per-system non-periodic systems only");
+    if (dsc->flags & BPS_SHARED_COEF)
+        BPS_FAIL(BPS_ENOTSUP, "penta_factor_solve_batch takes per-system coefficients only");
     CHECK(check_ptr(a, "a", dsc->dtype)); CHECK(check_ptr(b, "b", dsc->dtype));
     CHECK(check_ptr(c, "c", dsc->dtype)); CHECK(check_ptr(d, "d", dsc->dtype));
     CHECK(check_ptr(e, "e", dsc->dtype)); CHECK(check_ptr(x, "x", dsc->dtype));
     CHECK(check_ptr(work, "work", dsc->dtype));
     if (info && !aligned(info, 4)) BPS_FAIL(BPS_EINVAL, "info is not 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    const int64_t n = dsc->n, batch = dsc->batch, ld = dsc->ld;
+    if (dsc->flags & BPS_CYCLIC) {
+        // periodic, per system: the chunked kernel where it applies; systems
+        // it leaves (breakdown) and other n take the periodic factor + solve
+        const bool f64 = dsc->dtype == BPS_F64;
+        void *fac = work;
+        int32_t *mask = reinterpret_cast<int32_t *>(
+            static_cast<char *>(work) + size_t(penta_factor_elems(n, ld, true)) * dtype_size(dsc->dtype));
+        if (spike_cyclic_chunks(n)) {
+            CHECK(f64 ? launch_penta_spike<double>(n, batch, ld, true, a, b, c, d, e, x, fac, info, mask, st)
+                      : launch_penta_spike<float>(n, batch, ld, true, a, b, c, d, e, x, fac, info, mask, st));
+        } else {
+            mask = nullptr;
+        }
+        CHECK(f64 ? launch_penta_factor<double>(n, batch, ld, true, false, a, b, c, d, e, fac, info, st, mask)
+                  : launch_penta_factor<float>(n, batch, ld, true, false, a, b, c, d, e, fac, info, st, mask));
+        return f64 ? launch_penta_cyclic_solve<double>(n, batch, ld, 1, false, fac, x, st, mask)
+                   : launch_penta_cyclic_solve<float>(n, batch, ld, 1, false, fac, x, st, mask);
+    }
     if (spike_chunks(dsc->n)) {
         if (dsc->dtype == BPS_F64)
-            return launch_penta_spike<double>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work,
-                                              info, as_stream(stream));
-        return launch_penta_spike<float>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work,
-                                         info, as_stream(stream));
+            return launch_penta_spike<double>(n, batch, ld, false, a, b, c, d, e, x, work, info,
+                                              nullptr, st);
+        return launch_penta_spike<float>(n, batch, ld, false, a, b, c, d, e, x, work, info, nullptr,
+                                         st);
     }
     if (dsc->dtype == BPS_F64)
         return launch_penta_fused<double>(dsc->n, dsc->batch, dsc->ld, a, b, c, d, e, x, work, info,

@@ -6,26 +6,34 @@
 namespace bps {
 
 template <typename T>
+// mask (device int32[batch] or NULL): only systems with mask[s] != 0.
 bps_status launch_penta_factor(int64_t n, int64_t batch, int64_t ld, bool cyclic, bool shared,
                                const void *a, const void *b, const void *c, const void *d,
-                               const void *e, void *fac, int32_t *info, hipStream_t st);
+                               const void *e, void *fac, int32_t *info, hipStream_t st,
+                               const int32_t *mask = nullptr);
 template <typename T>
 bps_status launch_penta_solve(int64_t n, int64_t batch, int64_t ld, bool shared,
                               const void *fac, void *x, hipStream_t st);
 template <typename T>
 bps_status launch_penta_cyclic_solve(int64_t n, int64_t batch, int64_t ld, int64_t nsteps,
-                                     bool shared, const void *fac, void *x, hipStream_t st);
+                                     bool shared, const void *fac, void *x, hipStream_t st,
+                                     const int32_t *mask = nullptr);
 template <typename T>
 bps_status launch_penta_fused(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
                               const void *c, const void *d, const void *e, void *x, void *work,
                               int32_t *info, hipStream_t st);
-// Chunked register-resident factor + solve (per-system, non-periodic);
-// spike_chunks(n) is the number of 16-row chunks, 0 when it does not apply.
+// Chunked register-resident factor + solve (per-system); spike_chunks(n)
+// is the number of 16-row chunks, 0 when it does not apply (periodic:
+// spike_cyclic_chunks, a power of two).  Non-periodic: work holds 2 n ld
+// values for the sequential fallback.  Periodic: systems whose chunked
+// elimination breaks down are left untouched and marked in mask
+// (int32[batch], every entry written) for a second pass.
 int spike_chunks(int64_t n);
+int spike_cyclic_chunks(int64_t n);
 template <typename T>
-bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
-                              const void *c, const void *d, const void *e, void *x, void *work,
-                              int32_t *info, hipStream_t st);
+bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, bool cyclic, const void *a,
+                              const void *b, const void *c, const void *d, const void *e, void *x,
+                              void *work, int32_t *info, int32_t *mask, hipStream_t st);
 
 // Builds the five shared diagonals of I + sigma*D4 on the device.
 template <typename T>

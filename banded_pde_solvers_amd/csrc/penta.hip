@@ -41,10 +41,11 @@ __global__ void __launch_bounds__(kWave)
 k_penta_factor(int64_t n, int64_t batch, int64_t ld, int64_t ldf,
                const T *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
                const T *__restrict__ D, const T *__restrict__ E, T *__restrict__ fac,
-               int32_t *__restrict__ info)
+               int32_t *__restrict__ info, const int32_t *__restrict__ mask)
 {
     const int64_t s = lane_id();
     if (s >= batch) return;
+    if (mask && !mask[s]) return;       // only the systems marked in mask
     A += s; B += s; C += s; D += s; E += s;
     const int64_t rows = CYC ? n - 2 : n;     // rows of the factored block
     const int64_t arr = rows * ldf;           // stride between factor arrays
@@ -155,10 +156,11 @@ k_penta_solve(int64_t n, int64_t batch, int64_t ld, const T *__restrict__ fac, T
 template <typename T, bool SH>
 __global__ void __launch_bounds__(kWave)
 k_penta_cyclic_solve(int64_t n, int64_t batch, int64_t ld, int64_t nsteps,
-                     const T *__restrict__ fac, T *__restrict__ x)
+                     const T *__restrict__ fac, T *__restrict__ x, const int32_t *__restrict__ mask)
 {
     const int64_t s = lane_id();
     if (s >= batch) return;
+    if (mask && !mask[s]) return;       // only the systems marked in mask
     const int64_t m = n - 2;
     const int64_t ldf = SH ? 1 : ld;
     const T *f0 = fac + (SH ? 0 : s);
@@ -335,7 +337,8 @@ static inline dim3 grid_for(int64_t lanes) { return dim3(unsigned((lanes + kWave
 template <typename T>
 bps_status launch_penta_factor(int64_t n, int64_t batch, int64_t ld, bool cyclic, bool shared,
                                const void *a, const void *b, const void *c, const void *d,
-                               const void *e, void *fac, int32_t *info, hipStream_t st)
+                               const void *e, void *fac, int32_t *info, hipStream_t st,
+                               const int32_t *mask)
 {
     const int64_t lanes = shared ? 1 : batch;
     const int64_t ldin = shared ? 1 : ld;
@@ -343,7 +346,7 @@ bps_status launch_penta_factor(int64_t n, int64_t batch, int64_t ld, bool cyclic
     auto args = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid_for(lanes), dim3(kWave), 0, st, n, lanes, ldin, ldf,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
-                           (T *)fac, info);
+                           (T *)fac, info, mask);
     };
     if (cyclic) args(k_penta_factor<T, true>);
     else args(k_penta_factor<T, false>);
@@ -367,14 +370,15 @@ bps_status launch_penta_solve(int64_t n, int64_t batch, int64_t ld, bool shared,
 
 template <typename T>
 bps_status launch_penta_cyclic_solve(int64_t n, int64_t batch, int64_t ld, int64_t nsteps,
-                                     bool shared, const void *fac, void *x, hipStream_t st)
+                                     bool shared, const void *fac, void *x, hipStream_t st,
+                                     const int32_t *mask)
 {
     if (shared)
         hipLaunchKernelGGL((k_penta_cyclic_solve<T, true>), grid_for(batch), dim3(kWave), 0, st,
-                           n, batch, ld, nsteps, (const T *)fac, (T *)x);
+                           n, batch, ld, nsteps, (const T *)fac, (T *)x, mask);
     else
         hipLaunchKernelGGL((k_penta_cyclic_solve<T, false>), grid_for(batch), dim3(kWave), 0, st,
-                           n, batch, ld, nsteps, (const T *)fac, (T *)x);
+                           n, batch, ld, nsteps, (const T *)fac, (T *)x, mask);
     BPS_LAUNCHED("k_penta_cyclic_solve");
     return BPS_OK;
 }
@@ -395,11 +399,12 @@ bps_status launch_penta_fused(int64_t n, int64_t batch, int64_t ld, const void *
     template bps_status launch_penta_factor<T>(int64_t, int64_t, int64_t, bool, bool,        \
                                                const void *, const void *, const void *,     \
                                                const void *, const void *, void *, int32_t *, \
-                                               hipStream_t);                                 \
+                                               hipStream_t, const int32_t *);                \
     template bps_status launch_penta_solve<T>(int64_t, int64_t, int64_t, bool, const void *, \
                                               void *, hipStream_t);                          \
     template bps_status launch_penta_cyclic_solve<T>(int64_t, int64_t, int64_t, int64_t,     \
-                                                     bool, const void *, void *, hipStream_t); \
+                                                     bool, const void *, void *, hipStream_t, \
+                                                     const int32_t *);                       \
     template bps_status launch_penta_fused<T>(int64_t, int64_t, int64_t, const void *,       \
                                               const void *, const void *, const void *,      \
                                               const void *, void *, void *, int32_t *,       \

@@ -28,6 +28,15 @@
 // steps through LDS) across the P lanes of a system, and each lane then
 // back-substitutes x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j) and writes it.
 // HBM traffic: the 5 diagonals and f read once, x written once.
+//
+// Periodic systems (CYC): the wrap entries of rows 0 and 1 (a_0, b_0, a_1)
+// couple chunk 0's interior to the last chunk's interface, and those of rows
+// n-2 and n-1 (e_{n-2}, d_{n-1}, e_{n-1}) couple the last interface to chunk
+// 0's interior: the same C_L / B_next roles as between neighbouring chunks,
+// with chunk indices taken modulo P.  The interface system is then block
+// tridiagonal and periodic; block cyclic reduction with indices modulo P
+// (P a power of two) leaves after log2 P steps each unknown coupled only to
+// itself through L_j, D_j and U_j, so xI_j = (L_j + D_j + U_j)^{-1} r_j.
 #include "common.h"
 #include "kernels.h"
 
@@ -91,11 +100,12 @@ __device__ int32_t seq_penta_solve(int64_t n, int64_t ld, const T *A, const T *B
 // One workgroup holds S systems x P chunks of M rows (lane = chunk j of
 // system sl); n = P * M, P * S <= 512.  Dynamic LDS: 14 * P * S values of
 // T + S flags.
-template <typename T, int M, int S>
+template <typename T, int M, int S, bool CYC>
 __global__ void __launch_bounds__(512)
 k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
               const T *__restrict__ C, const T *__restrict__ D, const T *__restrict__ E,
-              T *__restrict__ x, T *__restrict__ work, int32_t *__restrict__ info)
+              T *__restrict__ x, T *__restrict__ work, int32_t *__restrict__ info,
+              int32_t *__restrict__ mask)
 {
     constexpr int m = M - 2;            // interior rows of a chunk
     extern __shared__ unsigned char lds_raw[];
@@ -135,7 +145,8 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     T rcp_m2 = 0, rcp_m1 = 0, beta_m1 = 0;
     T eC0 = 0, dC1 = 0, eC1 = 0;                   // C_R entries (rows m-2, m-1)
     bool bad = false;
-    const bool first_chunk = (j == 0);
+    // the chunk before the first one is the last one for a periodic system
+    const bool first_chunk = (j == 0) && !CYC;
 #pragma unroll
     for (int i = 0; i < m; ++i) {
         const int k = i % LA;
@@ -191,7 +202,8 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     const T fr10 = w12 * urA + w11 * urB, fr11 = w11 * urC;
     // interface rows of this chunk (local rows m, m+1)
     constexpr int kR0 = m % LA, kR1 = (m + 1) % LA;
-    const bool last_chunk = (j == P - 1);
+    const bool last_chunk = (j == P - 1) && !CYC;
+    const int jn = (j + 1 == P) ? 0 : j + 1, jp = (j == 0) ? P - 1 : j - 1;
     const T aR0 = qa[kR0], bR0 = qb[kR0], cR0 = qc[kR0], dR0 = qd[kR0];
     const T eR0 = last_chunk ? T(0) : qe[kR0], fR0 = qf[kR0];
     const T aR1 = qa[kR1], bR1 = qb[kR1], cR1 = qc[kR1];
@@ -204,9 +216,9 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     __syncthreads();
     T ny0 = 0, ny1 = 0, nzl00 = 0, nzl01 = 0, nzl10 = 0, nzl11 = 0, nzr00 = 0, nzr01 = 0, nzr10 = 0, nzr11 = 0;
     if (!last_chunk) {
-        ny0 = F(0, j + 1); ny1 = F(1, j + 1);
-        nzl00 = F(2, j + 1); nzl01 = F(3, j + 1); nzl10 = F(4, j + 1); nzl11 = F(5, j + 1);
-        nzr00 = F(6, j + 1); nzr01 = F(7, j + 1); nzr10 = F(8, j + 1); nzr11 = F(9, j + 1);
+        ny0 = F(0, jn); ny1 = F(1, jn);
+        nzl00 = F(2, jn); nzl01 = F(3, jn); nzl10 = F(4, jn); nzl11 = F(5, jn);
+        nzr00 = F(6, jn); nzr01 = F(7, jn); nzr10 = F(8, jn); nzr11 = F(9, jn);
     }
     // B_own = [[aR0, bR0], [0, aR1]] on interior rows (m-2, m-1);
     // B_next = [[eR0, 0], [dR1, eR1]] on the next interior rows (0, 1)
@@ -238,8 +250,8 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
         __syncthreads();
         M22<T> nD = Dj, nL{0, 0, 0, 0}, nU{0, 0, 0, 0};
         T nr0 = rj0, nr1 = rj1;
-        if (j - h >= 0) {
-            const int q = j - h;
+        if (CYC || j - h >= 0) {
+            const int q = (j - h) & (CYC ? P - 1 : -1);
             const M22<T> Lq{F(0, q), F(1, q), F(2, q), F(3, q)};
             const M22<T> Iq{F(4, q), F(5, q), F(6, q), F(7, q)};
             const M22<T> Uq{F(8, q), F(9, q), F(10, q), F(11, q)};
@@ -252,8 +264,8 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
             nr0 += al.a * rq0 + al.b * rq1;
             nr1 += al.c * rq0 + al.d * rq1;
         }
-        if (j + h < P) {
-            const int q = j + h;
+        if (CYC || j + h < P) {
+            const int q = (j + h) & (CYC ? P - 1 : -1);
             const M22<T> Lq{F(0, q), F(1, q), F(2, q), F(3, q)};
             const M22<T> Iq{F(4, q), F(5, q), F(6, q), F(7, q)};
             const M22<T> Uq{F(8, q), F(9, q), F(10, q), F(11, q)};
@@ -269,6 +281,10 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
         Dj = nD; Lj = nL; Uj = nU; rj0 = nr0; rj1 = nr1;
         __syncthreads();
     }
+    if (CYC) {
+        // both remaining couplings refer to this chunk's own interface
+        Dj = {Dj.a + Lj.a + Uj.a, Dj.b + Lj.b + Uj.b, Dj.c + Lj.c + Uj.c, Dj.d + Lj.d + Uj.d};
+    }
     T det;
     const M22<T> Dinv = inv(Dj, det);
     bad |= bad_pivot(det);
@@ -276,9 +292,13 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     F(0, j) = xr0; F(1, j) = xr1;
     if (bad) atomicOr(&flag[sl], 1);
     __syncthreads();
-    const T xl0 = first_chunk ? T(0) : F(0, j - 1);
-    const T xl1 = first_chunk ? T(0) : F(1, j - 1);
-    if (flag[sl]) {
+    const T xl0 = first_chunk ? T(0) : F(0, jp);
+    const T xl1 = first_chunk ? T(0) : F(1, jp);
+    if (CYC) {
+        // a breakdown leaves the system to the periodic factor + solve pass
+        if (j == 0 && act) mask[s] = flag[sl];
+        if (flag[sl]) return;
+    } else if (flag[sl]) {
         // a chunk pivot or an interface block broke down: redo this system
         // with the sequential elimination, which also fixes info
         if (first_chunk && act) {
@@ -288,7 +308,7 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
         }
         return;
     }
-    if (first_chunk && act && info) info[s] = 0;
+    if (j == 0 && act && info) info[s] = 0;
     // ---- back substitution x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j) ----
     T x1 = 0, x2 = 0;
 #pragma unroll
@@ -305,7 +325,8 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     px[int64_t(m + 1) * ld] = xr1;
 }
 
-// Chunked path applies when n = P * 16 with 2 <= P <= 64.
+// Chunked path applies when n = P * 16 with 2 <= P <= 64; for periodic
+// systems P must also be a power of two.
 int spike_chunks(int64_t n)
 {
     if (n % 16 != 0) return 0;
@@ -313,43 +334,58 @@ int spike_chunks(int64_t n)
     return (P >= 2 && P <= 64) ? int(P) : 0;
 }
 
+int spike_cyclic_chunks(int64_t n)
+{
+    const int P = spike_chunks(n);
+    return (P & (P - 1)) == 0 ? P : 0;
+}
+
 template <typename T, int S>
-static void launch_spike(int P, int64_t batch, int64_t ld, const void *a, const void *b,
-                         const void *c, const void *d, const void *e, void *x, void *work,
-                         int32_t *info, hipStream_t st)
+static void launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
+                         const void *b, const void *c, const void *d, const void *e, void *x,
+                         void *work, int32_t *info, int32_t *mask, hipStream_t st)
 {
     const size_t lds = size_t(14) * P * S * sizeof(T) + S * sizeof(int32_t);
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
-    hipLaunchKernelGGL((k_penta_spike<T, 16, S>), grid, block, lds, st, P, batch, ld,
-                       (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
-                       (T *)x, (T *)work, info);
+    if (cyclic)
+        hipLaunchKernelGGL((k_penta_spike<T, 16, S, true>), grid, block, lds, st, P, batch, ld,
+                           (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
+                           (T *)x, (T *)work, info, mask);
+    else
+        hipLaunchKernelGGL((k_penta_spike<T, 16, S, false>), grid, block, lds, st, P, batch, ld,
+                           (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
+                           (T *)x, (T *)work, info, mask);
 }
 
 template <typename T>
-bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
-                              const void *c, const void *d, const void *e, void *x, void *work,
-                              int32_t *info, hipStream_t st)
+bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, bool cyclic, const void *a,
+                              const void *b, const void *c, const void *d, const void *e, void *x,
+                              void *work, int32_t *info, int32_t *mask, hipStream_t st)
 {
-    if (!spike_chunks(n))
-        BPS_FAIL(BPS_ENOTSUP, "chunked pentadiagonal solve needs n = 16 P, 2 <= P <= 64");
+    if (!(cyclic ? spike_cyclic_chunks(n) : spike_chunks(n)))
+        BPS_FAIL(BPS_ENOTSUP, "chunked pentadiagonal solve needs n = 16 P, 2 <= P <= 64 "
+                              "(a power of two for periodic systems)");
+    if (cyclic && !mask) BPS_FAIL(BPS_EINVAL, "periodic chunked solve needs a mask array");
     if (batch == 0) return BPS_OK;
     // 16 systems per workgroup (a 128-byte row segment in fp64, 64 in
     // fp32); 32 when the systems are short so that a workgroup fills a
     // wavefront, 8 when they are long so that it stays within 512 lanes and
     // 64 KiB of LDS
     const int P = int(n / 16);
-    if (P < 4) launch_spike<T, 32>(P, batch, ld, a, b, c, d, e, x, work, info, st);
-    else if (P <= 32) launch_spike<T, 16>(P, batch, ld, a, b, c, d, e, x, work, info, st);
-    else launch_spike<T, 8>(P, batch, ld, a, b, c, d, e, x, work, info, st);
+    if (P < 4) launch_spike<T, 32>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    else if (P <= 32) launch_spike<T, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    else launch_spike<T, 8>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
     BPS_LAUNCHED("k_penta_spike");
     return BPS_OK;
 }
 
-template bps_status launch_penta_spike<float>(int64_t, int64_t, int64_t, const void *, const void *,
-                                              const void *, const void *, const void *, void *,
-                                              void *, int32_t *, hipStream_t);
-template bps_status launch_penta_spike<double>(int64_t, int64_t, int64_t, const void *, const void *,
-                                               const void *, const void *, const void *, void *,
-                                               void *, int32_t *, hipStream_t);
+template bps_status launch_penta_spike<float>(int64_t, int64_t, int64_t, bool, const void *,
+                                              const void *, const void *, const void *,
+                                              const void *, void *, void *, int32_t *, int32_t *,
+                                              hipStream_t);
+template bps_status launch_penta_spike<double>(int64_t, int64_t, int64_t, bool, const void *,
+                                               const void *, const void *, const void *,
+                                               const void *, void *, void *, int32_t *, int32_t *,
+                                               hipStream_t);
 
 }  // namespace bps

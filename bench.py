@@ -18,7 +18,7 @@ HBM sees the state once in and once out per call) and a "cpu_baseline"
 object (the CPU oracle, OpenMP over systems, timed on a bounded sample of
 the same workload on this host's cores).
 
-    python bench.py [--steps K] [--warmup W] [--workload {1,...,8}]
+    python bench.py [--steps K] [--warmup W] [--workload {1,...,9}]
 
 --workload selects another workload for manual measurements
 (2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
@@ -26,7 +26,9 @@ the same workload on this host's cores).
 20 solves per step; 5: the default shape time-stepped with Crank-Nicolson,
 theta = 1/2, 24 algorithmic flops per unknown per time step; 6: the same grid
 and batch for the Cahn-Hilliard equation, semi-implicit, 25 flops; 7, 8:
-batched tridiagonal solves, 512 x 256000 and 8192 x 20000, --dtype f64|f32).
+batched tridiagonal solves, 512 x 256000 and 8192 x 20000, --dtype f64|f32;
+9: periodic pentadiagonal 512 x 65536 with per-system coefficients, fused
+factor+solve, --dtype f64|f32).
 Only one GPU is used; --gpus above 1 exits.
 """
 import argparse
@@ -268,26 +270,29 @@ def bench_hyperdiffusion(args, which=1):
     return line
 
 
-def bench_penta(args):
+def bench_penta(args, which=2):
+    """Workloads 2 (non-periodic) and 9 (periodic): fused factor + solve of
+    pentadiagonal systems with per-system coefficients."""
     import numpy as np
     import torch
     import banded_pde_solvers_amd as bps
     import workloads as W
 
-    cfg = W.WORKLOADS[2]
+    cfg = W.WORKLOADS[which]
+    cyclic = cfg["kind"] == "penta_cyclic"
     n, batch = cfg["n"], cfg["batch"]
     dt = torch.float32 if args.dtype == "f32" else torch.float64
-    pb = W.penta_dominant(n, batch)
+    pb = W.penta_dominant(n, batch, cyclic=cyclic, rng=W.rng_for(which))
     dg = [torch.as_tensor(v, device="cuda:0").to(dt) for v in pb.diagonals]
     f0 = torch.as_tensor(pb.f, device="cuda:0").to(dt)
     x = f0.clone()
     code = bps.BPS_F32 if dt == torch.float32 else bps.BPS_F64
-    work = torch.empty(bps.bps_penta_work_bytes(n, batch, batch, code), dtype=torch.uint8,
-                       device="cuda:0")
+    work = torch.empty(bps.bps_penta_work_bytes(n, batch, batch, code, cyclic=cyclic),
+                       dtype=torch.uint8, device="cuda:0")
     del pb
 
     def step():
-        bps.penta_factor_solve_batch(*dg, x, work)
+        bps.penta_factor_solve_batch(*dg, x, work, cyclic=cyclic)
     wall, per = _time_loop(step, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
     kname = "k_penta_spike" if n % 16 == 0 and 2 <= n // 16 <= 64 else "k_penta_fused"
@@ -297,24 +302,27 @@ def bench_penta(args):
     kern_ms = statistics.mean(per)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     line = {
-        "metric": f"unknowns solved/s ({args.dtype}), general pentadiagonal factor+solve",
+        "metric": f"unknowns solved/s ({args.dtype}), " +
+                  ("periodic" if cyclic else "general") + " pentadiagonal factor+solve",
         "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
         "dtype": args.dtype,
-        "config": {"workload": cfg["name"], "n": n, "batch": batch, "coefficients": "per system"},
+        "config": {"workload": cfg["name"], "n": n, "batch": batch, "coefficients": "per system",
+                   "periodic": cyclic},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": _traffic(kname[2:] + "_" + args.dtype), "kernel_ms": kern_ms,
+                     "traffic": _traffic(kname[2:] + ("_cyclic_" if cyclic else "_") + args.dtype),
+                     "kernel_ms": kern_ms,
                      "bytes_per_launch": alg_bytes},
     }
     if not args.no_cpu_baseline:
         import oracle
-        small = W.penta_dominant(n, 4096, rng=np.random.default_rng(5))
+        small = W.penta_dominant(n, 4096, cyclic=cyclic, rng=np.random.default_rng(5))
         fl = [W.to_flat(v) for v in (*small.diagonals, small.f)]
 
         def sample(k):
             for r in range((k + 4095) // 4096):
                 kk = min(4096, k - r * 4096)
-                oracle.penta_solve(*(v[:kk] for v in fl))
+                oracle.penta_solve(*(v[:kk] for v in fl), cyclic=cyclic)
         line["cpu_baseline"] = _cpu_baseline(sample, n, "systems", args.cpu_seconds)
     return line
 
@@ -467,8 +475,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7, 8])
-    ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8")
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
+    ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -504,7 +512,7 @@ def main():
     fn = {1: bench_hyperdiffusion, 2: bench_penta, 3: lambda a: _hines_common(a, False),
           4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5),
           6: lambda a: bench_hyperdiffusion(a, 6), 7: lambda a: bench_tri(a, 7),
-          8: lambda a: bench_tri(a, 8)}[args.workload]
+          8: lambda a: bench_tri(a, 8), 9: lambda a: bench_penta(a, 9)}[args.workload]
     line = fn(args)
     out = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"),
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -143,20 +143,30 @@ BPS_API bps_status penta_solve_batch(const bps_penta_desc *desc, const void *fac
 BPS_API bps_status penta_cyclic_solve_batch(const bps_penta_desc *desc, const void *factors,
                                     void *x, void *stream);
 
-/* Bytes of the `work` buffer penta_factor_solve_batch needs (0 if invalid). */
+/* Bytes of the `work` buffer penta_factor_solve_batch needs (0 if invalid):
+ * 2*n*ld values, or for BPS_CYCLIC the periodic factors of every system
+ * plus ld int32. */
 BPS_API size_t bps_penta_work_bytes(const bps_penta_desc *desc);
 
 /* Factor and solve in one pass over the data (the "Rewrite" use of [P]:
- * a new matrix every call), non-periodic, per-system diagonals only
- * (flags must be 0).  x: f on entry, solution on return.  work: device,
- * bps_penta_work_bytes(desc) bytes, overwritten (scratch; contents
- * undefined on return).  info: as above or NULL: 1 + the first row whose
- * pivot of the page's sequential elimination is zero or non-finite.
- * For n = 16*P with 2 <= P <= 64 the systems are solved in 16-row chunks
- * (each eliminated with its own pivots, joined by a 2x2-block interface
- * system); a system whose chunked elimination meets a zero or non-finite
- * pivot is re-solved in the same launch by the sequential elimination, so
- * info and the solution are those of the page's algorithm. */
+ * a new matrix every call), per-system diagonals only (flags 0 or
+ * BPS_CYCLIC; BPS_SHARED_COEF gives BPS_ENOTSUP).  x: f on entry, solution
+ * on return.  work: device, bps_penta_work_bytes(desc) bytes, overwritten
+ * (scratch; contents undefined on return).  info: as above or NULL.
+ * Non-periodic: 1 + the first row whose pivot of the page's sequential
+ * elimination is zero or non-finite.  For n = 16*P with 2 <= P <= 64 the
+ * systems are solved in 16-row chunks (each eliminated with its own pivots,
+ * joined by a 2x2-block interface system); a system whose chunked
+ * elimination meets a zero or non-finite pivot is re-solved in the same
+ * launch by the sequential elimination, so info and the solution are those
+ * of the page's algorithm.
+ * Periodic (BPS_CYCLIC, [P] hyperdiffusion section: Navon's reduction with
+ * per-system coupling vectors): info as penta_factor_batch (1 + first bad
+ * pivot of the leading n-2 block, n - 1 for a singular 2x2 corner system).
+ * For n = 16*P with P in {2, 4, ..., 64} the chunked solve applies with the
+ * chunks joined periodically (the wrap entries couple the first and last
+ * chunks); systems whose chunked elimination breaks down, and other n, are
+ * factored and solved by the page's periodic reduction in a second pass. */
 BPS_API bps_status penta_factor_solve_batch(const bps_penta_desc *desc,
                                     const void *a, const void *b, const void *c,
                                     const void *d, const void *e,

@@ -100,8 +100,9 @@ def test_null_and_misaligned_pointers_rejected(lib):
 def test_solve_kind_mismatch_rejected(lib):
     assert lib.penta_solve_batch(_desc(flags=1), _fake(), _fake(1), None) == EINVAL
     assert lib.penta_cyclic_solve_batch(_desc(flags=0), _fake(), _fake(1), None) == EINVAL
-    assert lib.penta_factor_solve_batch(_desc(flags=1), *(_fake(i) for i in range(8)), None,
-                                        None) == ENOTSUP
+    for flags in (2, 3):           # shared coefficients: not a fused use
+        assert lib.penta_factor_solve_batch(_desc(flags=flags), *(_fake(i) for i in range(8)),
+                                            None, None) == ENOTSUP
 
 
 def test_hyperdiffusion_rejects_bad_arguments(lib):

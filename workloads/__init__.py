@@ -318,7 +318,8 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
 # ----------------------------------------------------------------------------
 # The named workloads at their full sizes (5: the headline shape time-stepped
 # with Crank-Nicolson instead of backward Euler; 6: the same grid and batch
-# for the Cahn-Hilliard equation; 7, 8: batched tridiagonal systems)
+# for the Cahn-Hilliard equation; 7, 8: batched tridiagonal systems; 9: periodic
+# pentadiagonal systems with per-system coefficients)
 # ----------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -340,4 +341,8 @@ WORKLOADS = {
     # systems and of the long ones
     7: dict(name="tri_n512_b256000", kind="tri", n=512, batch=256000),
     8: dict(name="tri_n8192_b20000", kind="tri", n=8192, batch=20000),
+    # periodic pentadiagonal systems with per-system coefficients (the
+    # periodic matrix of the hyperdiffusion section, any entries), shape of
+    # workload 2
+    9: dict(name="penta_cyclic_n512_b65536", kind="penta_cyclic", n=512, batch=65536),
 }
