@@ -30,13 +30,17 @@ __all__ = [
     "cahn_hilliard_work_bytes", "cahn_hilliard_step",
     "tri_work_bytes", "tri_solve_batch",
     "HinesPlan", "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
-    "hines_work_bytes", "hines_solve_batch",
+    "hines_work_bytes", "hines_solve_batch", "BPS_HINES_AUTO", "BPS_HINES_LANES",
+    "BPS_HINES_LEVELS",
 ]
 
 BPS_F32 = 1
 BPS_F64 = 2
 BPS_CYCLIC = 0x1
 BPS_SHARED_COEF = 0x2
+BPS_HINES_AUTO = 0
+BPS_HINES_LANES = 1
+BPS_HINES_LEVELS = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "libbps.so")
@@ -100,6 +104,8 @@ def load_library():
             "tri_work_bytes": ([st, i64, i64], ctypes.c_size_t),
             "tri_solve_batch": ([st, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp], st),
             "hines_plan_create": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64], st),
+            "hines_plan_create_sched": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64, st], st),
+            "hines_plan_uses_levels": ([vp], st),
             "hines_plan_destroy": ([vp], st),
             "hines_plan_elems": ([vp], i64),
             "hines_plan_unknowns": ([vp], i64),
@@ -350,6 +356,10 @@ class HinesPlan:
     def unknowns(self) -> int:
         return int(load_library().hines_plan_unknowns(self.handle))
 
+    @property
+    def uses_levels(self) -> bool:
+        return bool(load_library().hines_plan_uses_levels(self.handle))
+
     def close(self):
         if self._h is not None:
             _check("hines_plan_destroy", load_library().hines_plan_destroy(self._h))
@@ -362,16 +372,17 @@ class HinesPlan:
             pass
 
 
-def hines_plan_create(batch: int, sizes, parent, mono: bool, ld: int = 0) -> HinesPlan:
+def hines_plan_create(batch: int, sizes, parent, mono: bool, ld: int = 0,
+                      schedule: int = BPS_HINES_AUTO) -> HinesPlan:
     """sizes / parent: host int32 arrays (numpy or sequences), see bps.h."""
     import numpy as np
     sz = np.ascontiguousarray(np.asarray(sizes, dtype=np.int32).reshape(-1))
     par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
     h = ctypes.c_void_p()
     i32p = ctypes.POINTER(ctypes.c_int32)
-    _check("hines_plan_create", load_library().hines_plan_create(
+    _check("hines_plan_create_sched", load_library().hines_plan_create_sched(
         ctypes.byref(h), int(batch), sz.ctypes.data_as(i32p), par.ctypes.data_as(i32p),
-        1 if mono else 0, int(ld)))
+        1 if mono else 0, int(ld), int(schedule)))
     return HinesPlan(h, batch, mono)
 
 

@@ -23,9 +23,10 @@ void clear_error() { g_err[0] = '\0'; }
 
 // from hines.hip
 bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,
-                            const int32_t *parent, int mono, int64_t ld);
+                            const int32_t *parent, int mono, int64_t ld, int sched);
 bps_status hines_plan_free(bps_hines_plan *p);
 bool hines_plan_general(const bps_hines_plan *p);
+bool hines_plan_levels(const bps_hines_plan *p);
 template <typename T>
 bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, void *dst,
                            hipStream_t st);
@@ -409,6 +410,14 @@ bps_status tri_solve_batch(int dtype, int64_t n, int64_t batch, int64_t ld, cons
 bps_status hines_plan_create(bps_hines_plan **plan, int64_t batch, const int32_t *sizes,
                              const int32_t *parent, int mono, int64_t ld)
 {
+    return hines_plan_create_sched(plan, batch, sizes, parent, mono, ld, BPS_HINES_AUTO);
+}
+
+int hines_plan_uses_levels(const bps_hines_plan *plan) { return plan && hines_plan_levels(plan); }
+
+bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch, const int32_t *sizes,
+                                   const int32_t *parent, int mono, int64_t ld, int schedule)
+{
     clear_error();
     if (!plan) BPS_FAIL(BPS_EINVAL, "plan is NULL");
     *plan = nullptr;
@@ -436,7 +445,9 @@ bps_status hines_plan_create(bps_hines_plan **plan, int64_t batch, const int32_t
             off += n;
         }
     }
-    return hines_plan_build(plan, batch, sizes, parent, mono, ld);
+    if (schedule != BPS_HINES_AUTO && schedule != BPS_HINES_LANES && schedule != BPS_HINES_LEVELS)
+        BPS_FAIL(BPS_EINVAL, "unknown schedule %d", schedule);
+    return hines_plan_build(plan, batch, sizes, parent, mono, ld, schedule);
 }
 
 bps_status hines_plan_destroy(bps_hines_plan *plan)

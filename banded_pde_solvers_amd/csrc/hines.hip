@@ -46,11 +46,27 @@ struct bps_hines_plan {
     int32_t *lane_n = nullptr;     // multi [nblocks*64]
     int32_t *lane_src = nullptr;   // multi [nblocks*64] original neuron (-1 empty)
     int64_t *src_off = nullptr;    // multi [batch+1] offsets in the flat layout
+    // level schedule (one wavefront per neuron, sections of each tree by
+    // level; see k_hines_levels): built when the plan may use it
+    int sched = 0;                 // BPS_HINES_AUTO / _LANES / _LEVELS as created
+    bool use_levels = false;       // the schedule hines_launch takes
+    int32_t lv_maxn = 0;           // largest tree of the batch
+    int32_t *lv_perm = nullptr;    // per tree: new index -> compartment
+    int32_t *lv_sec = nullptr;     // per tree: section start (new index), nsec + 1 entries
+    int32_t *lv_spar = nullptr;    // per tree: parent (new index) of each section head, -1 root
+    int32_t *lv_lev = nullptr;     // per tree: section ranges per level, nlev + 1 entries
+    int64_t *lv_tree = nullptr;    // per tree: perm base, sec base, lev base, nlev, n, data base
 };
 
 namespace bps {
 
 constexpr int kRing = 16;       // LDS ring slots per lane (power of two)
+constexpr int kLevelMaxN = 4096;        // tree size limit of the level schedule (LDS)
+// auto: the level schedule up to this many compartments in the batch.
+// Measured (one solve): trees of 512, 16 .. 1024 neurons: 77 .. 107 us with
+// levels, 147 us with one lane per neuron; 2048: 135 vs 151; 4096: 259 vs 158.
+// Trees of 256 .. 2048: 256 neurons 308 vs 513 us, 1024 neurons 584 vs 513.
+constexpr int64_t kLevelAutoUnknowns = 786432;
 constexpr int kHinesAhead = 8;  // rows of look-ahead for the streamed inputs
 
 struct HinesArgs {
@@ -466,6 +482,166 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     }
 }
 
+// ---- level schedule -----------------------------------------------------------
+//
+// For batches of few neurons one lane per neuron leaves most of the chip
+// idle.  Here one wavefront takes one neuron and parallelises inside its tree
+// (the per-branch, per-level decomposition of section 4 of the Hines page):
+// the tree is cut into sections (maximal unbranched paths: a node starts a
+// section when it is the root or its parent has several children), nodes
+// are renumbered so that each section is a contiguous range head -> tail,
+// and a section's level is one more than the highest level of the sections
+// hanging from its tail (leaf sections: 0).  The neuron's u, l, d, rhs are
+// gathered into LDS in that order; the elimination runs level by level, one
+// section per lane, from the tail to the head (the parent of every node but
+// the head is the node before it, so the update is carried in registers);
+// the head's update to its parent (the tail of a higher-level section) is an
+// LDS atomic add.  Substitution runs the levels in reverse, head to tail.
+// Between the sweeps the LDS copies of d and rhs hold m_i = l_i / d'_i and
+// q_i = rhs'_i / d'_i, as in the one-lane-per-neuron kernels.  info = 1 + the
+// largest index of a bad pivot, the first one Algorithm 1's order meets.
+struct LevelArgs {
+    int64_t ld;
+    int mono;
+    const int64_t *tree;
+    const int32_t *perm, *sec, *spar, *lev;
+    const double *u, *l, *d;
+    double *rhs;
+    int32_t *info;
+};
+
+__global__ void __launch_bounds__(kWave) k_hines_levels(LevelArgs A)
+{
+    extern __shared__ double lv_lds[];
+    __shared__ int32_t bad;
+    const int64_t s = blockIdx.x;
+    const int k = threadIdx.x;
+    const int64_t *t = A.tree + (A.mono ? 0 : 6 * s);
+    const int32_t *perm = A.perm + t[0], *sec = A.sec + t[1], *spar = A.spar + t[1];
+    const int32_t *lev = A.lev + t[2];
+    const int32_t nlev = int32_t(t[3]), n = int32_t(t[4]);
+    const int64_t base = A.mono ? s : t[5];
+    const int64_t stride = A.mono ? A.ld : kWave;
+    double *dd = lv_lds, *rr = lv_lds + n, *uu = lv_lds + 2 * n, *ll = lv_lds + 3 * n;
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    };
+    if (k == 0) bad = 0;
+    for (int32_t j = k; j < n; j += kWave) {
+        const int64_t o = base + int64_t(perm[j]) * stride;
+        dd[j] = A.d[o];
+        rr[j] = A.rhs[o];
+        const bool root = perm[j] == 0;   // no coupling above the root
+        uu[j] = root ? 0.0 : A.u[o];
+        ll[j] = root ? 0.0 : A.l[o];
+    }
+    wave_sync();
+    int32_t mybad = 0;
+    // ---- leaves -> root, level by level ----
+    for (int32_t L = 0; L < nlev; ++L) {
+        for (int32_t q = lev[L] + k; q < lev[L + 1]; q += kWave) {
+            const int32_t s0 = sec[q], s1 = sec[q + 1];
+            double cd = 0.0, cr = 0.0;
+            for (int32_t j = s1 - 1; j >= s0; --j) {
+                const double dj = dd[j] - cd, rj = rr[j] - cr;
+                if (bad_pivot(dj)) mybad = max(mybad, perm[j] + 1);
+                const double rc = 1.0 / dj;
+                const double fac = uu[j] * rc;
+                dd[j] = ll[j] * rc;        // m_j
+                rr[j] = rj * rc;           // q_j
+                cd = fac * ll[j];
+                cr = fac * rj;
+            }
+            const int32_t ph = spar[q];
+            if (ph >= 0) {
+                unsafeAtomicAdd(&dd[ph], -cd);
+                unsafeAtomicAdd(&rr[ph], -cr);
+            }
+        }
+        wave_sync();
+    }
+    // ---- root -> leaves ----
+    for (int32_t L = nlev - 1; L >= 0; --L) {
+        for (int32_t q = lev[L] + k; q < lev[L + 1]; q += kWave) {
+            const int32_t s0 = sec[q], s1 = sec[q + 1], ph = spar[q];
+            double vp = ph >= 0 ? rr[ph] : 0.0;
+            for (int32_t j = s0; j < s1; ++j) {
+                const double v = rr[j] - dd[j] * vp;
+                rr[j] = v;
+                vp = v;
+            }
+        }
+        wave_sync();
+    }
+    if (mybad) atomicMax(&bad, mybad);
+    for (int32_t j = k; j < n; j += kWave) A.rhs[base + int64_t(perm[j]) * stride] = rr[j];
+    wave_sync();
+    if (k == 0 && A.info) A.info[s] = bad;
+}
+
+// Sections of one tree (parent[0] ignored), renumbered and ordered by level.
+struct LevelTree {
+    std::vector<int32_t> perm, sec, spar, lev;
+};
+
+static void build_level_tree(int32_t n, const int32_t *p, LevelTree &T)
+{
+    std::vector<int32_t> nch(n, 0), only(n, -1);
+    for (int32_t i = 1; i < n; ++i) nch[p[i]]++;
+    for (int32_t i = 1; i < n; ++i)
+        if (nch[p[i]] == 1) only[p[i]] = i;
+    std::vector<int32_t> heads;
+    for (int32_t i = 0; i < n; ++i)
+        if (i == 0 || nch[p[i]] != 1) heads.push_back(i);
+    const int32_t ns = int32_t(heads.size());
+    std::vector<int32_t> sec_of(n, -1), len(ns, 0), level(ns, 0);
+    for (int32_t h = 0; h < ns; ++h) {
+        int32_t c = heads[h];
+        while (true) {
+            sec_of[c] = h;
+            ++len[h];
+            if (nch[c] != 1) break;
+            c = only[c];
+        }
+    }
+    // a child section's head has a larger index than every node of its
+    // parent section's head, so decreasing head order visits children first
+    for (int32_t h = ns - 1; h >= 1; --h) {
+        const int32_t ps = sec_of[p[heads[h]]];
+        level[ps] = std::max(level[ps], level[h] + 1);
+    }
+    std::vector<int32_t> ord(ns);
+    std::iota(ord.begin(), ord.end(), 0);
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) {
+        return level[x] != level[y] ? level[x] < level[y] : len[x] > len[y];
+    });
+    T.perm.assign(n, 0);
+    T.sec.assign(ns + 1, n);
+    T.spar.assign(ns + 1, -1);
+    std::vector<int32_t> newidx(n, 0);
+    int32_t pos = 0;
+    for (int32_t q = 0; q < ns; ++q) {
+        T.sec[q] = pos;
+        int32_t c = heads[ord[q]];
+        while (true) {
+            T.perm[pos] = c;
+            newidx[c] = pos++;
+            if (nch[c] != 1) break;
+            c = only[c];
+        }
+    }
+    for (int32_t q = 0; q < ns; ++q) {
+        const int32_t hd = heads[ord[q]];
+        T.spar[q] = hd == 0 ? -1 : newidx[p[hd]];
+    }
+    const int32_t nlev = level[ord[ns - 1]] + 1;
+    T.lev.assign(nlev + 1, 0);
+    for (int32_t q = 0; q < ns; ++q) T.lev[level[ord[q]] + 1]++;
+    for (int32_t L = 0; L < nlev; ++L) T.lev[L + 1] += T.lev[L];
+}
+
 __global__ void k_fill_zero(double *p, int64_t count)
 {
     for (int64_t i = lane_id(); i < count; i += int64_t(gridDim.x) * blockDim.x) p[i] = 0.0;
@@ -523,15 +699,62 @@ static void free_plan(bps_hines_plan *p)
     if (!p) return;
     (void)hipFree(p->parent); (void)hipFree(p->blk_off); (void)hipFree(p->blk_rows);
     (void)hipFree(p->lane_n); (void)hipFree(p->lane_src); (void)hipFree(p->src_off);
+    (void)hipFree(p->lv_perm); (void)hipFree(p->lv_sec); (void)hipFree(p->lv_spar);
+    (void)hipFree(p->lv_lev); (void)hipFree(p->lv_tree);
     delete p;
 }
 
+// Level schedules of the batch's trees (one for a shared tree), uploaded.
+// data_base: per tree, where its values start in the solver layout (multi).
+static bps_status build_levels(bps_hines_plan *P, int64_t ntrees, const int32_t *sizes,
+                               const int32_t *parent, const std::vector<int64_t> &data_base)
+{
+    std::vector<int32_t> perm, sec, spar, lev;
+    std::vector<int64_t> tree(6 * ntrees);
+    int64_t off = 0;
+    LevelTree T;
+    for (int64_t s = 0; s < ntrees; ++s) {
+        const int32_t n = sizes[s];
+        build_level_tree(n, parent + off, T);
+        int64_t *d = &tree[6 * s];
+        d[0] = int64_t(perm.size()); d[1] = int64_t(sec.size()); d[2] = int64_t(lev.size());
+        d[3] = int64_t(T.lev.size()) - 1; d[4] = n; d[5] = data_base.empty() ? 0 : data_base[s];
+        perm.insert(perm.end(), T.perm.begin(), T.perm.end());
+        sec.insert(sec.end(), T.sec.begin(), T.sec.end());
+        spar.insert(spar.end(), T.spar.begin(), T.spar.end());
+        lev.insert(lev.end(), T.lev.begin(), T.lev.end());
+        P->lv_maxn = std::max(P->lv_maxn, n);
+        off += n;
+    }
+    bps_status st;
+    if ((st = upload(&P->lv_perm, perm)) != BPS_OK) return st;
+    if ((st = upload(&P->lv_sec, sec)) != BPS_OK) return st;
+    if ((st = upload(&P->lv_spar, spar)) != BPS_OK) return st;
+    if ((st = upload(&P->lv_lev, lev)) != BPS_OK) return st;
+    return upload(&P->lv_tree, tree);
+}
+
 bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,
-                            const int32_t *parent, int mono, int64_t ld)
+                            const int32_t *parent, int mono, int64_t ld, int sched)
 {
     auto *P = new bps_hines_plan();
     P->mono = mono ? 1 : 0;
     P->batch = batch;
+    P->sched = sched;
+    int32_t nmax = 0;
+    int64_t total = 0;
+    for (int64_t s = 0; s < (mono ? 1 : batch); ++s) {
+        nmax = std::max(nmax, sizes[s]);
+        total += sizes[s];
+    }
+    if (mono) total *= batch;
+    const bool lv_fit = nmax <= kLevelMaxN;
+    if (sched == BPS_HINES_LEVELS && !lv_fit) {
+        delete P;
+        BPS_FAIL(BPS_ENOTSUP, "level schedule needs trees of at most %d compartments", kLevelMaxN);
+    }
+    P->use_levels = sched == BPS_HINES_LEVELS ||
+                    (sched == BPS_HINES_AUTO && lv_fit && total <= kLevelAutoUnknowns);
     bps_status st = BPS_OK;
     if (mono) {
         const int64_t n = sizes[0];
@@ -543,6 +766,7 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         h[0] = 0;   // never read; keep it a valid index
         for (int64_t i = 1; i < n; ++i) P->max_dist = std::max<int32_t>(P->max_dist, int32_t(i - h[i]));
         st = upload(&P->parent, h);
+        if (st == BPS_OK && P->use_levels) st = build_levels(P, 1, sizes, parent, {});
     } else {
         std::vector<int64_t> off(batch + 1, 0);
         for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];
@@ -587,6 +811,14 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
             (st = upload(&P->blk_rows, brows)) == BPS_OK && (st = upload(&P->lane_n, ln)) == BPS_OK &&
             (st = upload(&P->lane_src, lsrc)) == BPS_OK)
             st = upload(&P->src_off, off);
+        if (st == BPS_OK && P->use_levels) {
+            // neuron s sits at lane k of block b: its values start at boff[b] + k
+            std::vector<int64_t> dbase(batch, 0);
+            for (int64_t b = 0; b < nb; ++b)
+                for (int k = 0; k < kWave; ++k)
+                    if (lsrc[b * kWave + k] >= 0) dbase[lsrc[b * kWave + k]] = boff[b] + k;
+            st = build_levels(P, batch, sizes, parent, dbase);
+        }
     }
     if (st != BPS_OK) { free_plan(P); return st; }
     *out = P;
@@ -600,6 +832,7 @@ bps_status hines_plan_free(bps_hines_plan *p)
 }
 
 bool hines_plan_general(const bps_hines_plan *p) { return p->max_dist > kRing; }
+bool hines_plan_levels(const bps_hines_plan *p) { return p->use_levels; }
 int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }
 int64_t hines_plan_unknowns_of(const bps_hines_plan *p) { return p->unknowns; }
 int64_t hines_plan_batch_of(const bps_hines_plan *p) { return p->batch; }
@@ -636,6 +869,19 @@ template bps_status hines_transform<double>(const bps_hines_plan *, bool, const 
 bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, const void *d,
                         void *rhs, void *work, int32_t *info, hipStream_t st)
 {
+    if (P->use_levels) {
+        LevelArgs L{};
+        L.ld = P->ld; L.mono = P->mono; L.tree = P->lv_tree;
+        L.perm = P->lv_perm; L.sec = P->lv_sec; L.spar = P->lv_spar; L.lev = P->lv_lev;
+        L.u = (const double *)u; L.l = (const double *)l; L.d = (const double *)d;
+        L.rhs = (double *)rhs; L.info = info;
+        const size_t lds = size_t(4) * P->lv_maxn * sizeof(double);
+        BPS_HIP(hipFuncSetAttribute((const void *)k_hines_levels,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
+        hipLaunchKernelGGL(k_hines_levels, dim3(unsigned(P->batch)), dim3(kWave), lds, st, L);
+        BPS_LAUNCHED("k_hines_levels");
+        return BPS_OK;
+    }
     const bool gen = hines_plan_general(P);
     HinesArgs A{};
     A.batch = P->batch; A.n = P->n; A.ld = P->ld;

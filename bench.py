@@ -18,7 +18,7 @@ HBM sees the state once in and once out per call) and a "cpu_baseline"
 object (the CPU oracle, OpenMP over systems, timed on a bounded sample of
 the same workload on this host's cores).
 
-    python bench.py [--steps K] [--warmup W] [--workload {1,...,9}]
+    python bench.py [--steps K] [--warmup W] [--workload {1,...,10}]
 
 --workload selects another workload for manual measurements
 (2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
@@ -28,7 +28,8 @@ theta = 1/2, 24 algorithmic flops per unknown per time step; 6: the same grid
 and batch for the Cahn-Hilliard equation, semi-implicit, 25 flops; 7, 8:
 batched tridiagonal solves, 512 x 256000 and 8192 x 20000, --dtype f64|f32;
 9: periodic pentadiagonal 512 x 65536 with per-system coefficients, fused
-factor+solve, --dtype f64|f32).
+factor+solve, --dtype f64|f32; 10: Hines mono 512 x 256, a batch too small
+for one lane per neuron, solved with the per-level section schedule).
 Only one GPU is used; --gpus above 1 exits.
 """
 import argparse
@@ -383,13 +384,13 @@ def bench_tri(args, which):
     return line
 
 
-def _hines_common(args, multi):
+def _hines_common(args, multi, which=None):
     import numpy as np
     import torch
     import banded_pde_solvers_amd as bps
     import workloads as W
 
-    cfg = W.WORKLOADS[4 if multi else 3]
+    cfg = W.WORKLOADS[which if which is not None else (4 if multi else 3)]
     if multi:
         mm = W.hines_multi(cfg["batch"], cfg["nmin"], cfg["nmax"])
         plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
@@ -401,7 +402,7 @@ def _hines_common(args, multi):
         nsolve = cfg["nsteps"]
         stats = {"mean_n": float(mm.sizes.mean()), "padded_elems": plan.elems}
     else:
-        hm = W.hines_mono(cfg["n"], cfg["batch"])
+        hm = W.hines_mono(cfg["n"], cfg["batch"], rng=W.rng_for(which if which is not None else 3))
         plan = bps.hines_plan_create(cfg["batch"], [cfg["n"]], hm.parent, mono=True)
         arrs = [torch.as_tensor(v, device="cuda:0") for v in (hm.u, hm.l, hm.d, hm.rhs)]
         nsolve = 1
@@ -424,10 +425,13 @@ def _hines_common(args, multi):
         "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
         "dtype": "f64",
         "config": {"workload": cfg["name"], "solves_per_step": nsolve, **stats},
-        "roofline": {"bound": "hbm", "kernel": "k_hines_multi" if multi else "k_hines_mono_reg",
+        "roofline": {"bound": "hbm", "kernel": "k_hines_levels" if plan.uses_levels else
+                     ("k_hines_multi" if multi else "k_hines_mono_reg"),
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": _traffic("hines_multi" if multi else "hines_mono"),
+                     "traffic": _traffic("hines_levels" if plan.uses_levels else
+                                         ("hines_multi" if multi else "hines_mono")),
+                     "schedule": "levels" if plan.uses_levels else "one lane per neuron",
                      "kernel_ms": kern_ms, "bytes_per_launch": alg_bytes / nsolve},
     }
     if not args.no_cpu_baseline:
@@ -475,7 +479,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
+    ap.add_argument("--workload", type=int, default=1, choices=list(range(1, 11)))
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -512,7 +516,8 @@ def main():
     fn = {1: bench_hyperdiffusion, 2: bench_penta, 3: lambda a: _hines_common(a, False),
           4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5),
           6: lambda a: bench_hyperdiffusion(a, 6), 7: lambda a: bench_tri(a, 7),
-          8: lambda a: bench_tri(a, 8), 9: lambda a: bench_penta(a, 9)}[args.workload]
+          8: lambda a: bench_tri(a, 8), 9: lambda a: bench_penta(a, 9),
+          10: lambda a: _hines_common(a, False, 10)}[args.workload]
     line = fn(args)
     out = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"),
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -302,6 +302,31 @@ BPS_API bps_status hines_plan_create(bps_hines_plan **plan, int64_t batch, const
                              const int32_t *parent, int mono, int64_t ld);
 BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
 
+/* Schedules of hines_solve_batch ([H] sections 3 and 4):
+ *   BPS_HINES_LANES   one lane per neuron over the whole tree (the page's
+ *                     Full-/Block-Interleaved kernels);
+ *   BPS_HINES_LEVELS  one wavefront per neuron: the tree cut into its
+ *                     unbranched sections, grouped by level (the page's
+ *                     per-branch / per-level decomposition of section 4),
+ *                     one section per lane and level, with the neuron held
+ *                     in LDS; for batches too small to fill the GPU with one
+ *                     lane per neuron.  Trees of at most 4096 compartments;
+ *   BPS_HINES_AUTO    LEVELS for batches of at most 786432 compartments in
+ *                     all whose trees fit, else LANES (what hines_plan_create
+ *                     chooses).
+ * The solver layout and every other argument are the same for both. */
+enum { BPS_HINES_AUTO = 0, BPS_HINES_LANES = 1, BPS_HINES_LEVELS = 2 };
+
+/* hines_plan_create with an explicit schedule.  BPS_ENOTSUP for
+ * BPS_HINES_LEVELS with a tree above 4096 compartments; BPS_EINVAL for an
+ * unknown schedule. */
+BPS_API bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch,
+                                   const int32_t *sizes, const int32_t *parent, int mono,
+                                   int64_t ld, int schedule);
+
+/* 1 if the plan solves with the level schedule, else 0. */
+BPS_API int hines_plan_uses_levels(const bps_hines_plan *plan);
+
 /* Elements of one value array (u, l, d or rhs) in the plan's solver layout. */
 BPS_API int64_t hines_plan_elems(const bps_hines_plan *plan);
 /* Real compartments (sum of sizes, or n*batch for mono). */

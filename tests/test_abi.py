@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for required in ("penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
                      "penta_factor_solve_batch", "hines_solve_batch", "hyperdiffusion_step",
                      "hyperdiffusion_theta_step", "cahn_hilliard_step", "tri_solve_batch",
-                     "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack"):
+                     "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
+                     "hines_plan_create_sched", "hines_plan_uses_levels"):
         assert required in names
 
 
@@ -174,6 +175,12 @@ def test_hines_plan_rejects_bad_parents_before_allocating(lib):
         bps.hines_plan_create(4, [0], [0], mono=True)                  # n < 1
     with pytest.raises(bps.BpsError):
         bps.hines_plan_create(4, [3], [-1, 0, 1], mono=True, ld=2)     # ld < batch
+
+
+def test_hines_plan_rejects_unknown_schedule(lib):
+    with pytest.raises(bps.BpsError):
+        bps.hines_plan_create(4, [3], [-1, 0, 1], mono=True, schedule=3)
+    assert lib.hines_plan_uses_levels(None) == 0
 
 
 def test_hines_solve_rejects_null_plan_and_dtype(lib):

@@ -4,7 +4,9 @@ Per-neuron normwise relative error <= 1e-10 on identical inputs, through the
 C-ABI (plan, pack, solve, unpack).  Covers ragged batches, a single
 compartment, chain trees, trees whose parent distance exceeds the on-chip
 window (general variant), breakdown reporting, and sampled neurons of the
-full mono (100000 x 512) and multi (32768 neurons of 256..2048) workloads."""
+full mono (100000 x 512) and multi (32768 neurons of 256..2048) workloads.
+The small-batch cases run both schedules (one lane per neuron, and the
+per-level section schedule that the automatic choice takes for them)."""
 import numpy as np
 import pytest
 import torch
@@ -25,9 +27,14 @@ def _rel_per_neuron(x, y, off):
     return float(np.max(errs))
 
 
-def _solve_mono(hm, ld=0):
+SCHEDULES = [bps.BPS_HINES_LANES, bps.BPS_HINES_LEVELS]
+
+
+def _solve_mono(hm, ld=0, schedule=bps.BPS_HINES_AUTO):
     n, batch = hm.u.shape
-    plan = bps.hines_plan_create(batch, [n], hm.parent, mono=True, ld=ld)
+    plan = bps.hines_plan_create(batch, [n], hm.parent, mono=True, ld=ld, schedule=schedule)
+    if schedule != bps.BPS_HINES_AUTO:
+        assert plan.uses_levels == (schedule == bps.BPS_HINES_LEVELS)
     ldd = ld or batch
     pad = lambda v: np.pad(v, ((0, 0), (0, ldd - batch)))
     u, l, d, r = (dev(pad(v)) for v in (hm.u, hm.l, hm.d, hm.rhs))
@@ -49,17 +56,19 @@ def _cols_err(x, y):
     return float(np.max(np.linalg.norm(x - y, axis=0) / np.linalg.norm(y, axis=0)))
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("n,batch", [(1, 5), (2, 64), (9, 65), (100, 129), (512, 1000)])
-def test_mono_matches_oracle(n, batch):
-    print(f"hines mono n={n} batch={batch}", flush=True)
+def test_mono_matches_oracle(n, batch, schedule):
+    print(f"hines mono n={n} batch={batch} schedule={schedule}", flush=True)
     hm = W.hines_mono(n, batch, rng=np.random.default_rng(n + 17 * batch))
-    out, info = _solve_mono(hm)
+    out, info = _solve_mono(hm, schedule=schedule)
     ref, rinfo = _oracle_mono(hm)
     assert _cols_err(out, ref) <= 1e-10
     np.testing.assert_array_equal(info, rinfo)
 
 
-def test_mono_ld_and_chain_tree():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_mono_ld_and_chain_tree(schedule):
     rng = np.random.default_rng(4)
     hm = W.hines_mono(300, 70, rng=rng)
     hm.parent = np.arange(-1, 299, dtype=np.int32)          # chain: tridiagonal (Thomas)
@@ -67,12 +76,13 @@ def test_mono_ld_and_chain_tree():
     for i in range(1, 300):
         acc[hm.parent[i]] += np.abs(hm.u[i])
     hm.d = acc + 1.0 + rng.uniform(0, 1, hm.d.shape)
-    out, _ = _solve_mono(hm, ld=128)
+    out, _ = _solve_mono(hm, ld=128, schedule=schedule)
     ref, _ = _oracle_mono(hm)
     assert _cols_err(out, ref) <= 1e-10
 
 
-def test_mono_long_parent_distance_general_variant():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_mono_long_parent_distance_general_variant(schedule):
     """Parents up to 200 rows away (beyond the 16-slot on-chip window)."""
     rng = np.random.default_rng(5)
     n, batch = 400, 130
@@ -84,14 +94,16 @@ def test_mono_long_parent_distance_general_variant():
         acc[hm.parent[j]] += np.abs(hm.u[j])
     hm.d = acc + 1.0 + rng.uniform(0, 1, hm.d.shape)
     assert W.tree_stats(hm.parent)["max_parent_distance"] > 16
-    out, info = _solve_mono(hm)
+    out, info = _solve_mono(hm, schedule=schedule)
     ref, _ = _oracle_mono(hm)
     assert _cols_err(out, ref) <= 1e-10
     assert np.all(info == 0)
 
 
-def _run_multi(mm):
-    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
+def _run_multi(mm, schedule=bps.BPS_HINES_AUTO):
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=schedule)
+    if schedule != bps.BPS_HINES_AUTO:
+        assert plan.uses_levels == (schedule == bps.BPS_HINES_LEVELS)
     E = plan.elems
     packed = [torch.empty(E, dtype=torch.float64, device="cuda:0") for _ in range(4)]
     for src, dst in zip((mm.u, mm.l, mm.d, mm.rhs), packed):
@@ -110,20 +122,23 @@ def _run_multi(mm):
     return out, host(info).astype(int)
 
 
-@pytest.mark.parametrize("batch,nmin,nmax", [(1, 1, 1), (3, 1, 7), (70, 5, 60), (200, 256, 2048),
-                                             # 1032 blocks: more than one per SIMD, the
-                                             # occupancy-first kernel configuration
-                                             (66000, 2, 9)])
-def test_multi_matches_oracle(batch, nmin, nmax):
-    print(f"hines multi batch={batch} n in [{nmin},{nmax}]", flush=True)
+@pytest.mark.parametrize("batch,nmin,nmax,schedule",
+                         [(1, 1, 1, 1), (3, 1, 7, 1), (70, 5, 60, 1), (200, 256, 2048, 1),
+                          (1, 1, 1, 2), (3, 1, 7, 2), (70, 5, 60, 2), (200, 256, 2048, 2),
+                          # 1032 blocks: more than one per SIMD, the occupancy-first
+                          # kernel configuration; the automatic choice
+                          (66000, 2, 9, 0)])
+def test_multi_matches_oracle(batch, nmin, nmax, schedule):
+    print(f"hines multi batch={batch} n in [{nmin},{nmax}] schedule={schedule}", flush=True)
     mm = W.hines_multi(batch, nmin, nmax, rng=np.random.default_rng(batch + nmax))
-    out, info = _run_multi(mm)
+    out, info = _run_multi(mm, schedule)
     ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
     assert _rel_per_neuron(out, ref, mm.offsets) <= 1e-10
     np.testing.assert_array_equal(info, rinfo)
 
 
-def test_multi_general_variant_and_breakdown():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_multi_general_variant_and_breakdown(schedule):
     rng = np.random.default_rng(6)
     mm = W.hines_multi(90, 20, 120, rng=rng)
     # give neuron 7 long-range parents, and a zero pivot to neuron 11
@@ -136,7 +151,7 @@ def test_multi_general_variant_and_breakdown():
     mm.d[o0:o1] = acc + 1.0
     z = mm.offsets[11] + mm.sizes[11] - 1
     mm.d[z] = 0.0
-    out, info = _run_multi(mm)
+    out, info = _run_multi(mm, schedule)
     ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
     np.testing.assert_array_equal(info, rinfo)
     assert info[11] == mm.sizes[11]
@@ -147,15 +162,16 @@ def test_multi_general_variant_and_breakdown():
     assert max(errs) <= 1e-10
 
 
-def test_mono_as_multi_agree():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_mono_as_multi_agree(schedule):
     hm = W.hines_mono(64, 100, rng=np.random.default_rng(8))
-    out_mono, _ = _solve_mono(hm)
+    out_mono, _ = _solve_mono(hm, schedule=schedule)
     sizes = np.full(100, 64, dtype=np.int32)
     off = np.arange(101, dtype=np.int64) * 64
     flat = lambda v: W.to_flat(v).reshape(-1)
     mm = W.HinesMulti(sizes, off, np.tile(hm.parent, 100), flat(hm.u), flat(hm.l), flat(hm.d),
                       flat(hm.rhs))
-    out_multi, _ = _run_multi(mm)
+    out_multi, _ = _run_multi(mm, schedule)
     np.testing.assert_allclose(out_multi, flat(out_mono), rtol=1e-13, atol=1e-15)
 
 
@@ -186,3 +202,87 @@ def test_multi_full_workload_sampled():
         V, _ = oracle.hines_solve(p, u, l, d, r)
         got = out[mm.offsets[s]:mm.offsets[s + 1]]
         assert np.linalg.norm(got - V[0]) / np.linalg.norm(V[0]) <= 1e-10
+
+
+# ---- the level schedule ---------------------------------------------------------
+
+def _tree_values(p, batch, rng):
+    n = len(p)
+    u = rng.uniform(-1, 0, (n, batch)); l = rng.uniform(-1, 0, (n, batch))
+    u[0] = l[0] = 0.0
+    d = 1.0 + np.abs(l) + rng.uniform(0, 1, (n, batch))
+    for i in range(1, n):
+        d[p[i]] += np.abs(u[i])
+    return W.HinesMono(np.asarray(p, dtype=np.int32), u, l, d, rng.uniform(-1, 1, (n, batch)))
+
+
+@pytest.mark.parametrize("shape", ["star", "uniform", "deep_binary", "big"])
+def test_levels_tree_shapes(shape):
+    """Shapes that stress the section decomposition: a star (n - 1 sections of
+    one node, all updating the root at once), uniformly random parents (long
+    distances, few levels), a deep tree of long sections, and a tree of 4096
+    compartments (128 KiB of LDS).  Both schedules against the oracle and
+    each other."""
+    rng = np.random.default_rng(77)
+    if shape == "star":
+        p = np.r_[-1, np.zeros(299, dtype=int)]
+    elif shape == "uniform":
+        p = np.r_[-1, rng.integers(0, np.arange(1, 800))]
+    elif shape == "deep_binary":
+        # sections of 40 nodes; every section's tail has two children
+        p = [-1]
+        for i in range(1, 1200):
+            p.append(i - 1 if i % 40 else (i // 40 - 1) // 2 * 40 + 39 if i >= 80 else 39)
+        p = np.array(p)
+    else:
+        p = W.random_tree(4096, rng, window=8)
+    batch = 9 if shape == "big" else 40
+    hm = _tree_values(p, batch, rng)
+    ref, rinfo = _oracle_mono(hm)
+    lv, linfo = _solve_mono(hm, schedule=bps.BPS_HINES_LEVELS)
+    ln, _ = _solve_mono(hm, schedule=bps.BPS_HINES_LANES)
+    assert _cols_err(lv, ref) <= 1e-10
+    assert _cols_err(lv, ln) <= 1e-12
+    np.testing.assert_array_equal(linfo, rinfo)
+
+
+def test_levels_breakdown_info():
+    """info of the level schedule: 1 + the largest index with a zero pivot,
+    the first one Algorithm 1 meets; a zero root pivot alone gives 1."""
+    rng = np.random.default_rng(12)
+    hm = W.hines_mono(200, 6, rng=rng)
+    hm.d[150, 1] = 0.0          # a node's own pivot (if it is a leaf, d'_150 = d_150)
+    hm.d[150, 2] = 0.0
+    hm.d[40, 2] = 0.0
+    hm.u[1:, 4] = 0.0           # decoupled: every pivot is d itself
+    hm.d[0, 4] = 0.0            # the root
+    _, info = _solve_mono(hm, schedule=bps.BPS_HINES_LEVELS)
+    _, rinfo = _oracle_mono(hm)
+    np.testing.assert_array_equal(info, rinfo)
+    assert info[4] == 1 and info[0] == 0
+
+
+def test_levels_auto_choice_and_limits():
+    rng = np.random.default_rng(13)
+    p = W.random_tree(300, rng)
+    # automatic choice: at most 786432 compartments in the batch
+    assert bps.hines_plan_create(2621, [300], p, mono=True).uses_levels
+    assert not bps.hines_plan_create(2622, [300], p, mono=True).uses_levels
+    big = W.random_tree(5000, rng)
+    assert not bps.hines_plan_create(10, [5000], big, mono=True).uses_levels
+    with pytest.raises(bps.BpsError):
+        bps.hines_plan_create(10, [5000], big, mono=True, schedule=bps.BPS_HINES_LEVELS)
+
+
+def test_small_batch_workload_full():
+    """The benchmarked small batch (512 compartments, 256 neurons): the
+    automatic choice is the level schedule; every neuron against the oracle."""
+    cfg = W.WORKLOADS[10]
+    hm = W.hines_mono(cfg["n"], cfg["batch"], rng=W.rng_for(10))
+    plan = bps.hines_plan_create(cfg["batch"], [cfg["n"]], hm.parent, mono=True)
+    assert plan.uses_levels
+    plan.close()
+    out, info = _solve_mono(hm)
+    ref, _ = _oracle_mono(hm)
+    assert _cols_err(out, ref) <= 1e-10
+    assert np.all(info == 0)

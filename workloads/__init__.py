@@ -319,7 +319,7 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
 # The named workloads at their full sizes (5: the headline shape time-stepped
 # with Crank-Nicolson instead of backward Euler; 6: the same grid and batch
 # for the Cahn-Hilliard equation; 7, 8: batched tridiagonal systems; 9: periodic
-# pentadiagonal systems with per-system coefficients)
+# pentadiagonal systems with per-system coefficients; 10: a small Hines batch)
 # ----------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -345,4 +345,7 @@ WORKLOADS = {
     # periodic matrix of the hyperdiffusion section, any entries), shape of
     # workload 2
     9: dict(name="penta_cyclic_n512_b65536", kind="penta_cyclic", n=512, batch=65536),
+    # Hines mono with few neurons (the page measures batches from 256): the
+    # level schedule's regime
+    10: dict(name="hines_mono_n512_b256", kind="hines_mono", n=512, batch=256),
 }
