@@ -30,7 +30,10 @@ batched tridiagonal solves, 512 x 256000 and 8192 x 20000, --dtype f64|f32;
 9: periodic pentadiagonal 512 x 65536 with per-system coefficients, fused
 factor+solve, --dtype f64|f32; 10: Hines mono 512 x 256, a batch too small
 for one lane per neuron, solved with the per-level section schedule).
-Only one GPU is used; --gpus above 1 exits.
+HBM-bound workloads also report the measured bandwidth of a plain 1 GiB
+device copy (copy_gbs) and the kernel's fraction of it (frac_of_copy): a
+stream that writes cannot exceed it.  Only one GPU is used; --gpus above 1
+exits.
 """
 import argparse
 import json
@@ -461,6 +464,19 @@ def _hines_common(args, multi, which=None):
     return line
 
 
+def _copy_gbs():
+    """Measured device-copy bandwidth (1 GiB read + 1 GiB written, median of
+    5): the practical ceiling of a stream that writes, beside the 8 TB/s
+    peak."""
+    import torch
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 8, dtype=torch.float64, device="cuda:0")
+    dst = torch.empty_like(src)
+    _, per = _time_loop(lambda: dst.copy_(src), 5, 2)
+    del src, dst
+    return 2 * nbytes / (statistics.median(per) * 1e-3) / 1e9
+
+
 def calibrate_copy(args):
     """A plain device-to-device copy of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
@@ -519,6 +535,10 @@ def main():
           8: lambda a: bench_tri(a, 8), 9: lambda a: bench_penta(a, 9),
           10: lambda a: _hines_common(a, False, 10)}[args.workload]
     line = fn(args)
+    roof = line.get("roofline")
+    if roof and roof.get("bound") == "hbm":
+        roof["copy_gbs"] = _copy_gbs()
+        roof["frac_of_copy"] = roof["achieved"] / roof["copy_gbs"]
     out = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"),
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
