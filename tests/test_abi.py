@@ -186,3 +186,19 @@ def test_hines_plan_rejects_unknown_schedule(lib):
 def test_hines_solve_rejects_null_plan_and_dtype(lib):
     assert lib.hines_solve_batch(None, 2, *(_fake(i) for i in range(5)), None, None) == EINVAL
     assert lib.hines_work_bytes(None, 2) == 0
+
+
+def test_binding_rejects_undersized_work_before_any_call():
+    """The Python wrappers compare the work buffer with the library's size
+    query and raise before the C call (the C ABI cannot see buffer sizes)."""
+    import torch
+    small = torch.empty(8, dtype=torch.uint8)
+    C = torch.zeros(64, 4, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        bps.hyperdiffusion_theta_step(C, 1e-6, 1 / 64, 0.5, 1, small)
+    with pytest.raises(ValueError):
+        bps.cahn_hilliard_step(C, 1e-6, 1 / 64, 1e-4, 1.0, 1.0, 1, small)
+    with pytest.raises(ValueError):
+        bps.tri_solve_batch(C, C, C, C, small)
+    with pytest.raises(ValueError):
+        bps.penta_factor_solve_batch(C, C, C, C, C, C, small, cyclic=True)
