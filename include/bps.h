@@ -5,8 +5,9 @@
  * is a pointer to GPU memory (hipMalloc / torch tensors); "host" arrays are
  * ordinary CPU memory.  `stream` is a hipStream_t passed as void* (NULL = the
  * default stream); every call only ENQUEUES work on it and returns without
- * synchronising, except hines_plan_create / hines_plan_destroy, which
- * allocate / free device memory and synchronise.  No solve allocates memory.
+ * synchronising, except hines_plan_create / hines_plan_create_sched /
+ * hines_plan_destroy, which allocate / free device memory and synchronise.
+ * No solve allocates memory.
  *
  * Sources (web-page titles; sections named as on the pages):
  *   [P] "cuPentBatch - A batched pentadiagonal solver for NVIDIA GPUs":
@@ -23,7 +24,10 @@
  *       the Hines matrix, Algorithm 1 `solveHines(u, l, d, rhs, p, cellSize)`),
  *       section 3 (Full-Interleaved and Block-Interleaved layouts, one thread
  *       per system, layout transformed once up front), section 4 (batches of
- *       neurons with different morphologies).
+ *       neurons with different morphologies, the per-branch / per-level
+ *       decomposition, and tridiagonal systems: the Thomas algorithm of
+ *       cuThomasBatch, section 4.1).  The cuPentBatch page's introduction
+ *       also gives the Cahn-Hilliard model and its semi-implicit scheme.
  *
  * LAYOUTS
  *   Interleaved (the [P] and [H] layout): element (row i, system s) of an
@@ -51,7 +55,8 @@
  *   The caller owns every device buffer.  Inputs are never modified; only
  *   the arrays documented as outputs (x / rhs / C, factors, work, info) are
  *   written.  The library allocates device memory only inside
- *   hines_plan_create and frees it in hines_plan_destroy.  Calls on different
+ *   hines_plan_create / hines_plan_create_sched and frees it in
+ *   hines_plan_destroy.  Calls on different
  *   streams with different output buffers are independent.
  */
 #ifndef BPS_H
