@@ -295,11 +295,28 @@ def bench_penta(args, which=2):
                        dtype=torch.uint8, device="cuda:0")
     del pb
 
-    def step():
-        bps.penta_factor_solve_batch(*dg, x, work, cyclic=cyclic)
+    if args.split:
+        # the page's two calls: factor (the factors of every system written
+        # out), then solve with them
+        fac = torch.empty(bps.bps_penta_factor_bytes(n, batch, batch, code,
+                                                     bps.BPS_CYCLIC if cyclic else 0),
+                          dtype=torch.uint8, device="cuda:0")
+        solve = bps.penta_cyclic_solve_batch if cyclic else bps.penta_solve_batch
+
+        def step():
+            bps.penta_factor_batch(*dg, fac, cyclic=cyclic)
+            solve(fac, x)
+    else:
+        def step():
+            bps.penta_factor_solve_batch(*dg, x, work, cyclic=cyclic)
     wall, per = _time_loop(step, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
-    kname = "k_penta_spike" if n % 16 == 0 and 2 <= n // 16 <= 64 else "k_penta_fused"
+    if args.split:
+        kname = "k_penta_factor + " + ("k_penta_cyclic_solve" if cyclic else "k_penta_solve")
+    elif n % 16 == 0 and 2 <= n // 16 <= 64 and (not cyclic or (n // 16) & (n // 16 - 1) == 0):
+        kname = "k_penta_spike"
+    else:
+        kname = "k_penta_fused"
     es = 4 if dt == torch.float32 else 8
     unknowns = n * batch
     alg_bytes = 7.0 * es * unknowns                  # 5 diagonals + f in, x out
@@ -311,10 +328,11 @@ def bench_penta(args, which=2):
         "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
         "dtype": args.dtype,
         "config": {"workload": cfg["name"], "n": n, "batch": batch, "coefficients": "per system",
-                   "periodic": cyclic},
+                   "periodic": cyclic, "calls": "factor, then solve" if args.split else "fused"},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": _traffic(kname[2:] + ("_cyclic_" if cyclic else "_") + args.dtype),
+                     "traffic": None if args.split else
+                     _traffic(kname[2:] + ("_cyclic_" if cyclic else "_") + args.dtype),
                      "kernel_ms": kern_ms,
                      "bytes_per_launch": alg_bytes},
     }
@@ -497,6 +515,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1, choices=list(range(1, 11)))
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
+    ap.add_argument("--split", action="store_true",
+                    help="workloads 2, 9: time the separate factor and solve calls instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
