@@ -23,6 +23,7 @@
 // parent distance use the general variant, which sends those updates through
 // per-lane accumulators in global memory (zeroed before each solve).
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -726,6 +727,18 @@ static bps_status build_levels(bps_hines_plan *P, int64_t ntrees, const int32_t 
         P->lv_maxn = std::max(P->lv_maxn, n);
         off += n;
     }
+    // the kernel's dynamic LDS may exceed the default limit: raise it once,
+    // to the largest any plan uses, here at plan time (not in the solve,
+    // which may be captured into a graph)
+    static std::once_flag lds_once;
+    static hipError_t lds_err = hipSuccess;
+    std::call_once(lds_once, [] {
+        lds_err = hipFuncSetAttribute((const void *)k_hines_levels,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      int(4 * kLevelMaxN * sizeof(double)));
+    });
+    if (lds_err != hipSuccess)
+        BPS_FAIL(BPS_EHIP, "hipFuncSetAttribute failed: %s", hipGetErrorString(lds_err));
     bps_status st;
     if ((st = upload(&P->lv_perm, perm)) != BPS_OK) return st;
     if ((st = upload(&P->lv_sec, sec)) != BPS_OK) return st;
@@ -876,8 +889,6 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
         L.u = (const double *)u; L.l = (const double *)l; L.d = (const double *)d;
         L.rhs = (double *)rhs; L.info = info;
         const size_t lds = size_t(4) * P->lv_maxn * sizeof(double);
-        BPS_HIP(hipFuncSetAttribute((const void *)k_hines_levels,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
         hipLaunchKernelGGL(k_hines_levels, dim3(unsigned(P->batch)), dim3(kWave), lds, st, L);
         BPS_LAUNCHED("k_hines_levels");
         return BPS_OK;

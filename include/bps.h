@@ -7,7 +7,9 @@
  * default stream); every call only ENQUEUES work on it and returns without
  * synchronising, except hines_plan_create / hines_plan_create_sched /
  * hines_plan_destroy, which allocate / free device memory and synchronise.
- * No solve allocates memory.
+ * No solve allocates memory.  Solve, pack and unpack calls enqueue kernels
+ * only (no allocation, copy, memset or synchronisation), so a sequence of
+ * them can be captured into a HIP graph and replayed.
  *
  * Sources (web-page titles; sections named as on the pages):
  *   [P] "cuPentBatch - A batched pentadiagonal solver for NVIDIA GPUs":
