@@ -502,8 +502,9 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
 // q_i = rhs'_i / d'_i, as in the one-lane-per-neuron kernels.  info = 1 + the
 // largest index of a bad pivot, the first one Algorithm 1's order meets.
 struct LevelArgs {
-    int64_t ld;
+    int64_t ld, nwg;
     int mono;
+    const int32_t *lane_src;     // multi: neuron at each position of the packed layout
     const int64_t *tree;
     const int32_t *perm, *sec, *spar, *lev;
     const double *u, *l, *d;
@@ -515,7 +516,15 @@ __global__ void __launch_bounds__(kWave) k_hines_levels(LevelArgs A)
 {
     extern __shared__ double lv_lds[];
     __shared__ int32_t bad;
-    const int64_t s = blockIdx.x;
+    // A neuron's values share cache lines with its neighbours in the solver
+    // layout (16 per 128-byte row segment mono, 64 per block row multi).
+    // Workgroups are dispatched round-robin over the 8 XCDs, each with its
+    // own L2: give the workgroups one XCD runs neighbouring positions, so
+    // that a line is fetched once instead of once per XCD.
+    const int64_t nb = A.nwg, bid = blockIdx.x, full = nb & ~int64_t(7);
+    const int64_t pos = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
+    const int64_t s = A.mono ? pos : A.lane_src[pos];
+    if (s < 0) return;               // an empty lane of the last block
     const int k = threadIdx.x;
     const int64_t *t = A.tree + (A.mono ? 0 : 6 * s);
     const int32_t *perm = A.perm + t[0], *sec = A.sec + t[1], *spar = A.spar + t[1];
@@ -884,12 +893,13 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
 {
     if (P->use_levels) {
         LevelArgs L{};
-        L.ld = P->ld; L.mono = P->mono; L.tree = P->lv_tree;
+        L.ld = P->ld; L.mono = P->mono; L.tree = P->lv_tree; L.lane_src = P->lane_src;
+        L.nwg = P->mono ? P->batch : P->nblocks * kWave;
         L.perm = P->lv_perm; L.sec = P->lv_sec; L.spar = P->lv_spar; L.lev = P->lv_lev;
         L.u = (const double *)u; L.l = (const double *)l; L.d = (const double *)d;
         L.rhs = (double *)rhs; L.info = info;
         const size_t lds = size_t(4) * P->lv_maxn * sizeof(double);
-        hipLaunchKernelGGL(k_hines_levels, dim3(unsigned(P->batch)), dim3(kWave), lds, st, L);
+        hipLaunchKernelGGL(k_hines_levels, dim3(unsigned(L.nwg)), dim3(kWave), lds, st, L);
         BPS_LAUNCHED("k_hines_levels");
         return BPS_OK;
     }
