@@ -31,7 +31,8 @@ __all__ = [
     "tri_work_bytes", "tri_solve_batch",
     "HinesPlan", "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
     "hines_work_bytes", "hines_solve_batch", "BPS_HINES_AUTO", "BPS_HINES_LANES",
-    "BPS_HINES_LEVELS",
+    "BPS_HINES_LEVELS", "hines_plan_create_sched", "hines_plan_elems", "hines_plan_unknowns",
+    "hines_plan_uses_levels", "bps_version", "bps_status_str", "bps_last_error", "PentaDesc",
 ]
 
 BPS_F32 = 1
@@ -124,6 +125,19 @@ def load_library():
 
 def version() -> int:
     return int(load_library().bps_version())
+
+
+def bps_version() -> int:
+    return version()
+
+
+def bps_status_str(status: int) -> str:
+    return (load_library().bps_status_str(int(status)) or b"").decode()
+
+
+def bps_last_error() -> str:
+    """Message of the last failed call on this thread ('' if none)."""
+    return (load_library().bps_last_error() or b"").decode()
 
 
 def _check(fn: str, status: int):
@@ -384,6 +398,24 @@ def hines_plan_create(batch: int, sizes, parent, mono: bool, ld: int = 0,
         ctypes.byref(h), int(batch), sz.ctypes.data_as(i32p), par.ctypes.data_as(i32p),
         1 if mono else 0, int(ld), int(schedule)))
     return HinesPlan(h, batch, mono)
+
+
+def hines_plan_create_sched(batch: int, sizes, parent, mono: bool, ld: int = 0,
+                            schedule: int = BPS_HINES_AUTO) -> HinesPlan:
+    """hines_plan_create with an explicit schedule (BPS_HINES_*)."""
+    return hines_plan_create(batch, sizes, parent, mono, ld, schedule)
+
+
+def hines_plan_elems(plan: HinesPlan) -> int:
+    return plan.elems
+
+
+def hines_plan_unknowns(plan: HinesPlan) -> int:
+    return plan.unknowns
+
+
+def hines_plan_uses_levels(plan: HinesPlan) -> bool:
+    return plan.uses_levels
 
 
 def hines_plan_destroy(plan: HinesPlan):

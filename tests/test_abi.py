@@ -202,3 +202,12 @@ def test_binding_rejects_undersized_work_before_any_call():
         bps.tri_solve_batch(C, C, C, C, small)
     with pytest.raises(ValueError):
         bps.penta_factor_solve_batch(C, C, C, C, C, C, small, cyclic=True)
+
+
+def test_binding_has_every_declared_entry_point():
+    """The Python binding exposes each C entry point of bps.h under its name."""
+    names = _declared()
+    missing = sorted(n for n in names if not hasattr(bps, n))
+    assert not missing, missing
+    assert bps.bps_status_str(1).startswith("BPS_EINVAL")
+    assert bps.bps_version() == bps.version()
