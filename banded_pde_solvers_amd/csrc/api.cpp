@@ -178,7 +178,7 @@ bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, co
         void *fac = work;
         int32_t *mask = reinterpret_cast<int32_t *>(
             static_cast<char *>(work) + size_t(penta_factor_elems(n, ld, true)) * dtype_size(dsc->dtype));
-        if (spike_cyclic_chunks(n)) {
+        if (spike_rows(n, true)) {
             CHECK(f64 ? launch_penta_spike<double>(n, batch, ld, true, a, b, c, d, e, x, fac, info, mask, st)
                       : launch_penta_spike<float>(n, batch, ld, true, a, b, c, d, e, x, fac, info, mask, st));
         } else {
@@ -189,7 +189,7 @@ bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, co
         return f64 ? launch_penta_cyclic_solve<double>(n, batch, ld, 1, false, fac, x, st, mask)
                    : launch_penta_cyclic_solve<float>(n, batch, ld, 1, false, fac, x, st, mask);
     }
-    if (spike_chunks(dsc->n)) {
+    if (spike_rows(n, false)) {
         if (dsc->dtype == BPS_F64)
             return launch_penta_spike<double>(n, batch, ld, false, a, b, c, d, e, x, work, info,
                                               nullptr, st);

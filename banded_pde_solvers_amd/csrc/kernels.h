@@ -22,14 +22,13 @@ template <typename T>
 bps_status launch_penta_fused(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
                               const void *c, const void *d, const void *e, void *x, void *work,
                               int32_t *info, hipStream_t st);
-// Chunked register-resident factor + solve (per-system); spike_chunks(n)
-// is the number of 16-row chunks, 0 when it does not apply (periodic:
-// spike_cyclic_chunks, a power of two).  Non-periodic: work holds 2 n ld
-// values for the sequential fallback.  Periodic: systems whose chunked
-// elimination breaks down are left untouched and marked in mask
-// (int32[batch], every entry written) for a second pass.
-int spike_chunks(int64_t n);
-int spike_cyclic_chunks(int64_t n);
+// Chunked register-resident factor + solve (per-system); spike_rows(n,
+// cyclic) is the chunk length (16 or 12), 0 when the path does not apply.
+// Non-periodic: work holds 2 n ld values for the sequential fallback.
+// Periodic: systems whose chunked elimination breaks down are left
+// untouched and marked in mask (int32[batch], every entry written) for a
+// second pass.
+int spike_rows(int64_t n, bool cyclic);
 template <typename T>
 bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, bool cyclic, const void *a,
                               const void *b, const void *c, const void *d, const void *e, void *x,
@@ -63,11 +62,11 @@ template <typename T>
 bps_status launch_copy_interleaved(int64_t n, int64_t batch, int64_t ldi, int64_t ldo,
                                    const void *in, void *out, hipStream_t st);
 
-// Batched tridiagonal solve: register-resident chunks for n = 16 P,
-// 2 <= P <= 64 (tri_chunks(n) is P, or 0); chunks spread over workgroups for
-// n = 16 P, 64 < P <= 65535 (tri_part_chunks); else one lane per system.
-// Work: tri_work_bytes_es(n, ld, sizeof(T)) bytes.
-int tri_chunks(int64_t n);
+// Batched tridiagonal solve: register-resident chunks for n = M P, M = 16
+// (else 12), 2 <= P <= 64 (tri_rows(n) is M, or 0); chunks spread over
+// workgroups for n = 16 P, 64 < P <= 65535 (tri_part_chunks); else one lane
+// per system.  Work: tri_work_bytes_es(n, ld, sizeof(T)) bytes.
+int tri_rows(int64_t n);
 int tri_part_chunks(int64_t n);
 size_t tri_work_bytes_es(int64_t n, int64_t ld, size_t es);
 template <typename T>

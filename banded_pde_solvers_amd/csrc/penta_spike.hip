@@ -29,6 +29,8 @@
 // back-substitutes x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j) and writes it.
 // HBM traffic: the 5 diagonals and f read once, x written once.
 //
+// Chunks are M = 16 rows where n allows, else 12 (template parameter M).
+//
 // Periodic systems (CYC): the wrap entries of rows 0 and 1 (a_0, b_0, a_1)
 // couple chunk 0's interior to the last chunk's interface, and those of rows
 // n-2 and n-1 (e_{n-2}, d_{n-1}, e_{n-1}) couple the last interface to chunk
@@ -325,22 +327,20 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     px[int64_t(m + 1) * ld] = xr1;
 }
 
-// Chunked path applies when n = P * 16 with 2 <= P <= 64; for periodic
-// systems P must also be a power of two.
-int spike_chunks(int64_t n)
+// Rows per chunk of the chunked path, 0 when it does not apply: n = P * M
+// with M = 16 (else 12) and 2 <= P <= 64; for periodic systems P must also
+// be a power of two.
+int spike_rows(int64_t n, bool cyclic)
 {
-    if (n % 16 != 0) return 0;
-    const int64_t P = n / 16;
-    return (P >= 2 && P <= 64) ? int(P) : 0;
+    for (const int M : {16, 12}) {
+        if (n % M != 0) continue;
+        const int64_t P = n / M;
+        if (P >= 2 && P <= 64 && (!cyclic || (P & (P - 1)) == 0)) return M;
+    }
+    return 0;
 }
 
-int spike_cyclic_chunks(int64_t n)
-{
-    const int P = spike_chunks(n);
-    return (P & (P - 1)) == 0 ? P : 0;
-}
-
-template <typename T, int S>
+template <typename T, int M, int S>
 static void launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
                          const void *b, const void *c, const void *d, const void *e, void *x,
                          void *work, int32_t *info, int32_t *mask, hipStream_t st)
@@ -348,13 +348,27 @@ static void launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const vo
     const size_t lds = size_t(14) * P * S * sizeof(T) + S * sizeof(int32_t);
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
     if (cyclic)
-        hipLaunchKernelGGL((k_penta_spike<T, 16, S, true>), grid, block, lds, st, P, batch, ld,
+        hipLaunchKernelGGL((k_penta_spike<T, M, S, true>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
                            (T *)x, (T *)work, info, mask);
     else
-        hipLaunchKernelGGL((k_penta_spike<T, 16, S, false>), grid, block, lds, st, P, batch, ld,
+        hipLaunchKernelGGL((k_penta_spike<T, M, S, false>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
                            (T *)x, (T *)work, info, mask);
+}
+
+template <typename T, int M>
+static void launch_spike_m(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
+                           const void *b, const void *c, const void *d, const void *e, void *x,
+                           void *work, int32_t *info, int32_t *mask, hipStream_t st)
+{
+    // 16 systems per workgroup (a 128-byte row segment in fp64, 64 in
+    // fp32); 32 when the systems are short so that a workgroup fills a
+    // wavefront, 8 when they are long so that it stays within 512 lanes and
+    // 64 KiB of LDS
+    if (P < 4) launch_spike<T, M, 32>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    else if (P <= 32) launch_spike<T, M, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    else launch_spike<T, M, 8>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
 }
 
 template <typename T>
@@ -362,19 +376,15 @@ bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, bool cyclic,
                               const void *b, const void *c, const void *d, const void *e, void *x,
                               void *work, int32_t *info, int32_t *mask, hipStream_t st)
 {
-    if (!(cyclic ? spike_cyclic_chunks(n) : spike_chunks(n)))
-        BPS_FAIL(BPS_ENOTSUP, "chunked pentadiagonal solve needs n = 16 P, 2 <= P <= 64 "
+    const int M = spike_rows(n, cyclic);
+    if (!M)
+        BPS_FAIL(BPS_ENOTSUP, "chunked pentadiagonal solve needs n = 16 P or 12 P, 2 <= P <= 64 "
                               "(a power of two for periodic systems)");
     if (cyclic && !mask) BPS_FAIL(BPS_EINVAL, "periodic chunked solve needs a mask array");
     if (batch == 0) return BPS_OK;
-    // 16 systems per workgroup (a 128-byte row segment in fp64, 64 in
-    // fp32); 32 when the systems are short so that a workgroup fills a
-    // wavefront, 8 when they are long so that it stays within 512 lanes and
-    // 64 KiB of LDS
-    const int P = int(n / 16);
-    if (P < 4) launch_spike<T, 32>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
-    else if (P <= 32) launch_spike<T, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
-    else launch_spike<T, 8>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    const int P = int(n / M);
+    if (M == 16) launch_spike_m<T, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    else launch_spike_m<T, 12>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
     BPS_LAUNCHED("k_penta_spike");
     return BPS_OK;
 }

@@ -207,12 +207,13 @@ k_tri_chunk(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *
     py[int64_t(m) * ld] = xI;
 }
 
-// Chunked path applies when n = P * 16 with 2 <= P <= 64.
-int tri_chunks(int64_t n)
+// Rows per chunk of the chunked path, 0 when it does not apply: n = P * M
+// with M = 16 (else 12) and 2 <= P <= 64.
+int tri_rows(int64_t n)
 {
-    if (n % 16 != 0) return 0;
-    const int64_t P = n / 16;
-    return (P >= 2 && P <= 64) ? int(P) : 0;
+    for (const int M : {16, 12})
+        if (n % M == 0 && n / M >= 2 && n / M <= 64) return M;
+    return 0;
 }
 
 // ---- partitioned path for long systems (n = 16 P, P > 64) ------------------
@@ -377,14 +378,29 @@ size_t tri_work_bytes_es(int64_t n, int64_t ld, size_t es)
     return size_t(n) * size_t(ld) * es;
 }
 
-template <typename T, int S>
+template <typename T, int M, int S>
 static void launch_chunk(int P, int64_t batch, int64_t ld, const void *a, const void *b,
                          const void *c, void *y, void *work, int32_t *info, hipStream_t st)
 {
     const size_t lds = size_t(4) * P * S * sizeof(T) + S * sizeof(int32_t);
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
-    hipLaunchKernelGGL((k_tri_chunk<T, 16, S>), grid, block, lds, st, P, batch, ld, (const T *)a,
+    hipLaunchKernelGGL((k_tri_chunk<T, M, S>), grid, block, lds, st, P, batch, ld, (const T *)a,
                        (const T *)b, (const T *)c, (T *)y, (T *)work, info);
+}
+
+template <typename T, int M>
+static void launch_chunk_m(int P, int64_t batch, int64_t ld, const void *a, const void *b,
+                           const void *c, void *y, void *work, int32_t *info, hipStream_t st)
+{
+    // 16 systems per workgroup (a 128-byte row segment in fp64), 32 for
+    // short systems so that a workgroup fills a wavefront, 8 for long ones
+    // so that it stays within 512 lanes.  fp64 at 32 chunks: 8 systems (256
+    // lanes, three workgroups per CU at 168 VGPRs instead of one of 512)
+    // measured 4% faster; fp32 loses with 32-byte rows.
+    if (P < 4) launch_chunk<T, M, 32>(P, batch, ld, a, b, c, y, work, info, st);
+    else if (P < 32 || (P == 32 && sizeof(T) == 4))
+        launch_chunk<T, M, 16>(P, batch, ld, a, b, c, y, work, info, st);
+    else launch_chunk<T, M, 8>(P, batch, ld, a, b, c, y, work, info, st);
 }
 
 template <typename T>
@@ -422,16 +438,10 @@ bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a,
     if (const int P = tri_part_chunks(n))
         return launch_tri_part<T>(P, batch, ld, (const T *)a, (const T *)b, (const T *)c, (T *)y,
                                   work, info, st);
-    if (const int P = tri_chunks(n)) {
-        // 16 systems per workgroup (a 128-byte row segment in fp64), 32 for
-        // short systems so that a workgroup fills a wavefront, 8 for long
-        // ones so that it stays within 512 lanes.  fp64 at 32 chunks: 8
-        // systems (256 lanes, three workgroups per CU at 168 VGPRs instead
-        // of one of 512) measured 4% faster; fp32 loses with 32-byte rows.
-        if (P < 4) launch_chunk<T, 32>(P, batch, ld, a, b, c, y, work, info, st);
-        else if (P < 32 || (P == 32 && sizeof(T) == 4))
-            launch_chunk<T, 16>(P, batch, ld, a, b, c, y, work, info, st);
-        else launch_chunk<T, 8>(P, batch, ld, a, b, c, y, work, info, st);
+    if (const int M = tri_rows(n)) {
+        const int P = int(n / M);
+        if (M == 16) launch_chunk_m<T, 16>(P, batch, ld, a, b, c, y, work, info, st);
+        else launch_chunk_m<T, 12>(P, batch, ld, a, b, c, y, work, info, st);
         BPS_LAUNCHED("k_tri_chunk");
         return BPS_OK;
     }

@@ -161,19 +161,20 @@ BPS_API size_t bps_penta_work_bytes(const bps_penta_desc *desc);
  * on return.  work: device, bps_penta_work_bytes(desc) bytes, overwritten
  * (scratch; contents undefined on return).  info: as above or NULL.
  * Non-periodic: 1 + the first row whose pivot of the page's sequential
- * elimination is zero or non-finite.  For n = 16*P with 2 <= P <= 64 the
- * systems are solved in 16-row chunks (each eliminated with its own pivots,
- * joined by a 2x2-block interface system); a system whose chunked
- * elimination meets a zero or non-finite pivot is re-solved in the same
- * launch by the sequential elimination, so info and the solution are those
- * of the page's algorithm.
+ * elimination is zero or non-finite.  For n = M*P with M = 16 (else 12)
+ * and 2 <= P <= 64 the systems are solved in M-row chunks (each eliminated
+ * with its own pivots, joined by a 2x2-block interface system); a system
+ * whose chunked elimination meets a zero or non-finite pivot is re-solved
+ * in the same launch by the sequential elimination, so info and the
+ * solution are those of the page's algorithm.
  * Periodic (BPS_CYCLIC, [P] hyperdiffusion section: Navon's reduction with
  * per-system coupling vectors): info as penta_factor_batch (1 + first bad
  * pivot of the leading n-2 block, n - 1 for a singular 2x2 corner system).
- * For n = 16*P with P in {2, 4, ..., 64} the chunked solve applies with the
- * chunks joined periodically (the wrap entries couple the first and last
- * chunks); systems whose chunked elimination breaks down, and other n, are
- * factored and solved by the page's periodic reduction in a second pass. */
+ * For n = M*P, M = 16 (else 12), P in {2, 4, ..., 64}, the chunked solve
+ * applies with the chunks joined periodically (the wrap entries couple the
+ * first and last chunks); systems whose chunked elimination breaks down,
+ * and other n, are factored and solved by the page's periodic reduction in
+ * a second pass. */
 BPS_API bps_status penta_factor_solve_batch(const bps_penta_desc *desc,
                                     const void *a, const void *b, const void *c,
                                     const void *d, const void *e,
@@ -268,11 +269,12 @@ BPS_API size_t tri_work_bytes(int dtype, int64_t n, int64_t ld);
  * scratch (contents undefined on return).  info: device int32[batch] or
  * NULL: 0, or 1 + the first row whose pivot of the page's Thomas
  * elimination (no pivoting) is zero or non-finite.
- * For n = 16*P with 2 <= P <= 64 the systems are solved in 16-row chunks
- * (each eliminated with its own pivots, joined by a scalar tridiagonal
- * interface system); a system whose chunked elimination meets a zero or
- * non-finite pivot is re-solved in the same launch by the sequential Thomas
- * algorithm, so info and the solution are those of the page's method.
+ * For n = M*P with M = 16 (else 12) and 2 <= P <= 64 the systems are solved
+ * in M-row chunks (each eliminated with its own pivots, joined by a scalar
+ * tridiagonal interface system); a system whose chunked elimination meets a
+ * zero or non-finite pivot is re-solved in the same launch by the
+ * sequential Thomas algorithm, so info and the solution are those of the
+ * page's method.
  * For n = 16*P with 64 < P <= 65535 the chunks of a system are spread
  * over many workgroups (per-chunk elimination, the interface system solved
  * by this same routine, then each chunk's substitution), with the same

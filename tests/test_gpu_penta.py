@@ -34,7 +34,9 @@ def _oracle(pb, dt, cols=None, cyclic=False):
 @pytest.mark.parametrize("n,batch", [(4, 1), (5, 3), (6, 64), (7, 65), (33, 129), (512, 1000),
                                      # 16-row chunks: 2, 3, 4, 31, 32, 33, 64 chunks per system
                                      (32, 7), (48, 33), (64, 100), (496, 17), (512, 1),
-                                     (528, 50), (1024, 40), (1040, 9)])
+                                     (528, 50), (1024, 40), (1040, 9),
+                                     # 12-row chunks: 2, 5, 45, 63 chunks per system
+                                     (24, 40), (60, 33), (540, 20), (756, 9)])
 def test_fused_matches_oracle(dt, n, batch):
     print(f"fused n={n} batch={batch} {dt}", flush=True)
     pb = W.penta_dominant(n, batch, rng=np.random.default_rng(n * 1000 + batch))

@@ -46,8 +46,10 @@ def _oracle(pb, dt=torch.float64, cols=None):
 
 @pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("n,batch", [(32, 37), (64, 100), (128, 33), (256, 20), (512, 17),
-                                     (1024, 9),                            # chunked, P = 2 .. 64
-                                     (48, 40), (96, 21), (6, 64), (7, 65), (100, 30)])  # second pass
+                                     (1024, 9),                  # 16-row chunks, P = 2 .. 64
+                                     (24, 33), (48, 40), (96, 21), (384, 20),
+                                     (768, 9),                   # 12-row chunks, P = 2 .. 64
+                                     (40, 40), (72, 21), (6, 64), (7, 65), (100, 30)])  # second pass
 def test_matches_oracle(dt, n, batch):
     print(f"cyclic fused n={n} batch={batch} {dt}", flush=True)
     pb = W.penta_dominant(n, batch, cyclic=True, rng=np.random.default_rng(n * 31 + batch))
@@ -82,17 +84,18 @@ def test_per_system_hyperdiffusion_operators(n):
     assert np.all(err <= np.maximum(1e-10, 4 * (1 + 16 * sig2) * u))
 
 
-@pytest.mark.parametrize("n", [256, 96])
-def test_breakdown_info_and_rescue(n):
-    """System 3: c_0 = 0 (the periodic reduction's first pivot: info 1).
-    System 20: c_32 = 0, a zero pivot only the chunked elimination meets
-    (chunk 2 starts at row 32): solved by the second pass, info 0.
-    System 21: the same at the first row of the last chunk."""
+@pytest.mark.parametrize("n,m", [(256, 16), (96, 12), (100, 16)])
+def test_breakdown_info_and_rescue(n, m):
+    """Chunks of m rows (n = 100: no chunked pass).  System 3: c_0 = 0 (the
+    periodic reduction's first pivot: info 1).  System 20: c = 0 at the
+    first row of chunk 2, a zero pivot only the chunked elimination meets:
+    solved by the second pass, info 0.  System 21: the same at the first row
+    of the last chunk."""
     batch = 30
     pb = W.penta_dominant(n, batch, cyclic=True, rng=np.random.default_rng(41))
     pb.c[0, 3] = 0.0
-    pb.c[32, 20] = 0.0
-    pb.c[n - 16, 21] = 0.0
+    pb.c[2 * m, 20] = 0.0
+    pb.c[n - m, 21] = 0.0
     got, info = _solve(pb)
     ref, rinfo = _oracle(pb)
     assert info[3] == rinfo[3] == 1

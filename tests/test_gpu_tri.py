@@ -35,7 +35,8 @@ def _oracle(tb, dtype=torch.float64, cols=None):
 
 
 @pytest.mark.parametrize("n,batch", [(32, 37), (48, 100), (64, 20), (80, 33), (256, 50),
-                                     (512, 17), (1024, 9),                 # chunked
+                                     (512, 17), (1024, 9),                 # 16-row chunks
+                                     (24, 40), (36, 50), (180, 21), (540, 11),  # 12-row chunks
                                      (1040, 21), (2048, 10), (4096, 300),  # partitioned
                                      (16640, 3),                           # two levels
                                      (1, 70), (2, 5), (3, 64), (17, 65), (100, 33), (1000, 7)])
@@ -48,7 +49,8 @@ def test_parity_fp64(n, batch):
     assert relerr_cols(got, ref) <= TOL[torch.float64]
 
 
-@pytest.mark.parametrize("n,batch", [(64, 100), (512, 40), (1024, 16), (100, 30), (2048, 20)])
+@pytest.mark.parametrize("n,batch", [(64, 100), (512, 40), (1024, 16), (180, 25), (100, 30),
+                                     (2048, 20)])
 def test_parity_fp32(n, batch):
     tb = W.tri_dominant(n, batch, rng=np.random.default_rng(n + 1))
     got, info, _ = _solve(tb, torch.float32)
@@ -70,18 +72,19 @@ def test_leading_dimension_inputs_untouched(n):
     assert np.all(info == 0)
 
 
-@pytest.mark.parametrize("n", [256, 96, 2048])
-def test_breakdown_info_and_sequential_rescue(n):
-    """System 3: b_0 = 0 (the page's elimination stops at row 1: info 1).
-    System 5: b_16 = 0 but a_16 c_15 != 0, so the sequential pivot of row 16
-    is nonzero while the chunked elimination (chunk 1 starts at row 16) meets
-    a zero pivot: it must fall back and still match the oracle.  System 8:
-    an exactly zero pivot deep inside (a_40 = b_40 = 0: info 41 whatever
-    the rounding of the earlier factors)."""
+@pytest.mark.parametrize("n,m", [(256, 16), (96, 12), (2048, 16), (100, 16)])
+def test_breakdown_info_and_sequential_rescue(n, m):
+    """Chunks of m rows (n = 100: one lane per system).  System 3: b_0 = 0
+    (the page's elimination stops at row 1: info 1).  System 5: b_m = 0 but
+    a_m c_{m-1} != 0, so the sequential pivot of row m is nonzero while the
+    chunked elimination (chunk 1 starts at row m) meets a zero pivot: it
+    must fall back and still match the oracle.  System 8: an exactly zero
+    pivot deep inside (a_40 = b_40 = 0: info 41 whatever the rounding of the
+    earlier factors)."""
     batch = 12
     tb = W.tri_dominant(n, batch, rng=np.random.default_rng(11))
     tb.b[0, 3] = 0.0
-    tb.b[16, 5] = 0.0
+    tb.b[m, 5] = 0.0
     tb.a[40, 8] = 0.0
     tb.b[40, 8] = 0.0
     got, info, _ = _solve(tb)
