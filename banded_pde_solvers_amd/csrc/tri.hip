@@ -79,14 +79,25 @@ k_tri_thomas(int64_t n, int64_t batch, int64_t ld, const T *__restrict__ A,
     if (info) info[s] = r;
 }
 
+// Rows of an interface system assembled on load (the partitioned path's
+// partial interface rows, see k_tri_part_fwd): with Lp, Dp, cI, Rp of row r
+// in A, B, C, Y and z0, p0, q0 of the next chunk in Z0, P0, Q0 (row r + 1),
+//   a_r = Lp,  b_r = Dp - cI p0,  c_r = -cI q0,  f_r = Rp - cI z0.
+template <typename T>
+struct TriAssemble {
+    const T *Z0, *P0, *Q0;
+};
+
 // One workgroup holds S systems x P chunks of M rows (lane = chunk j of
 // system sl); n = P * M, P * S <= 512.  Dynamic LDS: 4 * P * S values of T
-// + S flags.
-template <typename T, int M, int S>
+// + S flags.  ASM: the rows are assembled on load (TriAssemble); a system
+// whose chunked elimination breaks down is then only reported (info 1), for
+// the caller to re-solve from its own inputs.
+template <typename T, int M, int S, bool ASM>
 __global__ void __launch_bounds__(512)
 k_tri_chunk(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
             const T *__restrict__ C, T *__restrict__ Y, T *__restrict__ work,
-            int32_t *__restrict__ info)
+            int32_t *__restrict__ info, TriAssemble<T> asmb)
 {
     constexpr int m = M - 1;            // interior rows of a chunk
     extern __shared__ unsigned char lds_raw[];
@@ -113,22 +124,41 @@ k_tri_chunk(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *
     // ---- forward sweep over the interior, inputs streamed LA rows ahead ----
     constexpr int LA = 4;
     T qa[LA], qb[LA], qc[LA], qy[LA];
-#pragma unroll
-    for (int k = 0; k < LA; ++k) {
-        const int64_t o = int64_t(k) * ld;
-        qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qy[k] = py[o];
+    // ASM: z0, p0, q0 of the row after each ring row (the last row of the
+    // system has none: its cI is zero, and its own values stand in)
+    T qz[ASM ? LA : 1], qp[ASM ? LA : 1], qq[ASM ? LA : 1];
+    const T *pz = nullptr, *pp = nullptr, *pq = nullptr;
+    if constexpr (ASM) {
+        const int64_t noff = off + ld;
+        pz = asmb.Z0 + noff; pp = asmb.P0 + noff; pq = asmb.Q0 + noff;
     }
+    auto load_row = [&](int k, int i) {
+        const int64_t o = int64_t(i) * ld;
+        qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qy[k] = py[o];
+        if constexpr (ASM) {
+            const int64_t on = (last_chunk && i == M - 1) ? o - ld : o;
+            qz[k] = pz[on]; qp[k] = pp[on]; qq[k] = pq[on];
+        }
+    };
+    // row entries a, b, c, f of ring slot k
+    auto row = [&](int k, T &a, T &b, T &c, T &f) {
+        if constexpr (ASM) {
+            a = qa[k]; b = qb[k] - qc[k] * qp[k]; c = -qc[k] * qq[k]; f = qy[k] - qc[k] * qz[k];
+        } else {
+            a = qa[k]; b = qb[k]; c = qc[k]; f = qy[k];
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < LA; ++k) load_row(k, k);
     T cp[m], g[m], gv[m];
     T cpp = 0, gp = 0, gvp = 0, w = 1, z0 = 0, p0 = 0;
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < m; ++i) {
         const int k = i % LA;
-        const T a_i = qa[k], b_i = qb[k], c_i = qc[k], f_i = qy[k];
-        {
-            const int64_t o = int64_t(i + LA < M ? i + LA : M - 1) * ld;
-            qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qy[k] = py[o];
-        }
+        T a_i, b_i, c_i, f_i;
+        row(k, a_i, b_i, c_i, f_i);
+        load_row(k, i + LA < M ? i + LA : M - 1);
         const T ai = (i > 0) ? a_i : T(0);                         // entry of E_j
         const T al = (i == 0 && !first_chunk) ? a_i : T(0);         // coupling to xI_{j-1}
         const T den = b_i - cpp * ai;
@@ -145,7 +175,9 @@ k_tri_chunk(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *
     }
     const T q0 = w * cp[m - 1];
     constexpr int kI = m % LA;          // the interface row (local row m)
-    const T aI = qa[kI], bI = qb[kI], cI = last_chunk ? T(0) : qc[kI], fI = qy[kI];
+    T aI, bI, cI, fI;
+    row(kI, aI, bI, cI, fI);
+    if (last_chunk) cI = T(0);
 
     // ---- publish first-row quantities; build interface row j ----
     F(0, j) = z0; F(1, j) = p0; F(2, j) = q0;
@@ -188,10 +220,15 @@ k_tri_chunk(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *
     const T xL = first_chunk ? T(0) : F(0, j - 1);
     if (flag[sl]) {
         // an interior pivot or a reduced diagonal broke down: redo this
-        // system with the sequential algorithm, which also sets info
+        // system with the sequential algorithm, which also sets info (ASM:
+        // report it; the caller redoes the system it came from)
         if (first_chunk && act) {
-            const int32_t r = seq_thomas<T>(int64_t(P) * M, ld, A + s, B + s, C + s, Y + s, work + s);
-            if (info) info[s] = r;
+            if constexpr (ASM) {
+                info[s] = 1;
+            } else {
+                const int32_t r = seq_thomas<T>(int64_t(P) * M, ld, A + s, B + s, C + s, Y + s, work + s);
+                if (info) info[s] = r;
+            }
         }
         return;
     }
@@ -239,10 +276,15 @@ int tri_part_chunks(int64_t n)
     return (P > 64 && P <= 65535) ? int(P) : 0;    // the chunk index is blockIdx.y
 }
 
+// Per chunk: Thomas over the interior, then the interface row's partial
+// entries Lp = -a gv, Dp = b - a c', Rp = f - a g and its c (cI, zero for
+// the last chunk) into lo, di, rh, up, and the first-row quantities z0, p0,
+// q0 into summ ([3][P][ld]); the next chunk's z0, p0, q0 complete the row.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_tri_part_fwd(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
                const T *__restrict__ C, const T *__restrict__ Y, T *__restrict__ summ,
+               T *__restrict__ lo, T *__restrict__ di, T *__restrict__ up, T *__restrict__ rh,
                int32_t *__restrict__ flag)
 {
     constexpr int M = kPartM, m = M - 1;
@@ -270,42 +312,38 @@ k_tri_part_fwd(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const 
         p0 += w * gvi;
         cpp = cpi; gp = gi; gvp = gvi;
     }
-    const int64_t so = int64_t(P) * ld;
-    T *o = summ + int64_t(j) * ld + s;
-    o[0] = gp; o[so] = gvp; o[2 * so] = cpp; o[3 * so] = z0; o[4 * so] = p0; o[5 * so] = w * cpp;
+    const int64_t mo = int64_t(m) * ld;
+    const T aI = pa[mo], bI = pb[mo], fI = py[mo];
+    const T cI = (j == P - 1) ? T(0) : pc[mo];
+    const int64_t so = int64_t(P) * ld, o = int64_t(j) * ld + s;
+    lo[o] = -aI * gvp;
+    di[o] = bI - aI * cpp;
+    rh[o] = fI - aI * gp;
+    up[o] = cI;
+    summ[o] = z0; summ[so + o] = p0; summ[2 * so + o] = w * cpp;
     if (bad) flag[s] = 1;
 }
 
-// Interface row j: L_j = -a gv, D_j = b - a c' - c p0_{j+1},
-// U_j = -c q0_{j+1}, R_j = f - a g - c z0_{j+1} into the arrays lo, di, up,
-// rh ([P][ld] each).
+// Completes interface row j in place (when the interface system is not
+// solved by the assembling chunk kernel): D_j = Dp - cI p0_{j+1},
+// U_j = -cI q0_{j+1}, R_j = Rp - cI z0_{j+1}; L_j = Lp is final already.
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_tri_part_iface(int P, int64_t batch, int64_t ld, const T *__restrict__ A,
-                 const T *__restrict__ B, const T *__restrict__ C, const T *__restrict__ Y,
-                 const T *__restrict__ summ, T *__restrict__ lo, T *__restrict__ di,
-                 T *__restrict__ up, T *__restrict__ rh)
+k_tri_part_iface(int P, int64_t batch, int64_t ld, const T *__restrict__ summ,
+                 T *__restrict__ di, T *__restrict__ up, T *__restrict__ rh)
 {
     const int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int j = int(blockIdx.y);
     if (s >= batch) return;
-    const int64_t row = (int64_t(j) * kPartM + kPartM - 1) * ld + s;
-    const T aI = A[row], bI = B[row], fI = Y[row];
-    const bool last = (j == P - 1);
-    const T cI = last ? T(0) : C[row];
-    const int64_t so = int64_t(P) * ld;
-    const T *own = summ + int64_t(j) * ld + s;
-    const T G = own[0], V = own[so], cpm = own[2 * so];
+    const int64_t so = int64_t(P) * ld, o = int64_t(j) * ld + s;
+    const T cI = up[o];
     T nz0 = 0, np0 = 0, nq0 = 0;
-    if (!last) {
-        const T *nx = own + ld;
-        nz0 = nx[3 * so]; np0 = nx[4 * so]; nq0 = nx[5 * so];
+    if (j < P - 1) {
+        nz0 = summ[o + ld]; np0 = summ[so + o + ld]; nq0 = summ[2 * so + o + ld];
     }
-    const int64_t o = int64_t(j) * ld + s;
-    lo[o] = -aI * V;
-    di[o] = bI - aI * cpm - cI * np0;
+    di[o] = di[o] - cI * np0;
     up[o] = -cI * nq0;
-    rh[o] = fI - aI * G - cI * nz0;
+    rh[o] = rh[o] - cI * nz0;
 }
 
 template <typename T>
@@ -367,40 +405,43 @@ __global__ void k_tri_fill_zero(int64_t count, int32_t *__restrict__ p)
 }
 
 // Work of a solve of n rows (bytes).  Partitioned path (values of T unless
-// noted): [n ld: c' of the rescue] [6 P ld: chunk summaries] [4 P ld:
-// interface rows] [ld int32: flags] [ld int32: info of the interface solve]
-// [the work of the interface solve, P rows]; other paths: n ld values.
+// noted): [n ld: c' of the rescue] [3 P ld: z0, p0, q0 of the chunks]
+// [4 P ld: interface rows] [ld int32: flags] [ld int32: info of the
+// interface solve] [the work of the interface solve, P rows]; other paths:
+// n ld values.
 size_t tri_work_bytes_es(int64_t n, int64_t ld, size_t es)
 {
     if (const int P = tri_part_chunks(n))
-        return size_t(n + 10 * int64_t(P)) * size_t(ld) * es + 2 * size_t(ld) * sizeof(int32_t) +
+        return size_t(n + 7 * int64_t(P)) * size_t(ld) * es + 2 * size_t(ld) * sizeof(int32_t) +
                tri_work_bytes_es(P, ld, es);
     return size_t(n) * size_t(ld) * es;
 }
 
-template <typename T, int M, int S>
+template <typename T, int M, int S, bool ASM>
 static void launch_chunk(int P, int64_t batch, int64_t ld, const void *a, const void *b,
-                         const void *c, void *y, void *work, int32_t *info, hipStream_t st)
+                         const void *c, void *y, void *work, int32_t *info, TriAssemble<T> asmb,
+                         hipStream_t st)
 {
     const size_t lds = size_t(4) * P * S * sizeof(T) + S * sizeof(int32_t);
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
-    hipLaunchKernelGGL((k_tri_chunk<T, M, S>), grid, block, lds, st, P, batch, ld, (const T *)a,
-                       (const T *)b, (const T *)c, (T *)y, (T *)work, info);
+    hipLaunchKernelGGL((k_tri_chunk<T, M, S, ASM>), grid, block, lds, st, P, batch, ld,
+                       (const T *)a, (const T *)b, (const T *)c, (T *)y, (T *)work, info, asmb);
 }
 
-template <typename T, int M>
+template <typename T, int M, bool ASM = false>
 static void launch_chunk_m(int P, int64_t batch, int64_t ld, const void *a, const void *b,
-                           const void *c, void *y, void *work, int32_t *info, hipStream_t st)
+                           const void *c, void *y, void *work, int32_t *info, hipStream_t st,
+                           TriAssemble<T> asmb = {})
 {
     // 16 systems per workgroup (a 128-byte row segment in fp64), 32 for
     // short systems so that a workgroup fills a wavefront, 8 for long ones
     // so that it stays within 512 lanes.  fp64 at 32 chunks: 8 systems (256
     // lanes, three workgroups per CU at 168 VGPRs instead of one of 512)
     // measured 4% faster; fp32 loses with 32-byte rows.
-    if (P < 4) launch_chunk<T, M, 32>(P, batch, ld, a, b, c, y, work, info, st);
+    if (P < 4) launch_chunk<T, M, 32, ASM>(P, batch, ld, a, b, c, y, work, info, asmb, st);
     else if (P < 32 || (P == 32 && sizeof(T) == 4))
-        launch_chunk<T, M, 16>(P, batch, ld, a, b, c, y, work, info, st);
-    else launch_chunk<T, M, 8>(P, batch, ld, a, b, c, y, work, info, st);
+        launch_chunk<T, M, 16, ASM>(P, batch, ld, a, b, c, y, work, info, asmb, st);
+    else launch_chunk<T, M, 8, ASM>(P, batch, ld, a, b, c, y, work, info, asmb, st);
 }
 
 template <typename T>
@@ -410,18 +451,27 @@ static bps_status launch_tri_part(int P, int64_t batch, int64_t ld, const T *a, 
     const int64_t n = int64_t(P) * kPartM, pl = int64_t(P) * ld;
     T *w0 = static_cast<T *>(work);
     T *summ = w0 + n * ld;
-    T *lo = summ + 6 * pl, *di = lo + pl, *up = di + pl, *rh = up + pl;
+    T *lo = summ + 3 * pl, *di = lo + pl, *up = di + pl, *rh = up + pl;
     int32_t *flag = reinterpret_cast<int32_t *>(rh + pl);
     int32_t *info2 = flag + ld;
     void *iw = info2 + ld;          // 8-byte aligned: 2 ld int32 above
     const dim3 blk(256), grid2(unsigned((batch + 255) / 256), unsigned(P));
     const dim3 grid1(unsigned((batch + 255) / 256));
     hipLaunchKernelGGL(k_tri_fill_zero, grid1, blk, 0, st, batch, flag);
-    hipLaunchKernelGGL((k_tri_part_fwd<T>), grid2, blk, 0, st, P, batch, ld, a, b, c, y, summ, flag);
-    hipLaunchKernelGGL((k_tri_part_iface<T>), grid2, blk, 0, st, P, batch, ld, a, b, c, y, summ, lo,
-                       di, up, rh);
-    bps_status r = launch_tri_solve<T>(P, batch, ld, lo, di, up, rh, iw, info2, st);
-    if (r != BPS_OK) return r;
+    hipLaunchKernelGGL((k_tri_part_fwd<T>), grid2, blk, 0, st, P, batch, ld, a, b, c, y, summ, lo,
+                       di, up, rh, flag);
+    if (const int MI = tri_rows(P)) {
+        // the interface system goes to the chunk kernel, which completes its
+        // rows as it loads them; a breakdown there re-solves the whole system
+        // below (info2 = 1)
+        const TriAssemble<T> asmb{summ, summ + pl, summ + 2 * pl};
+        if (MI == 16) launch_chunk_m<T, 16, true>(P / 16, batch, ld, lo, di, up, rh, iw, info2, st, asmb);
+        else launch_chunk_m<T, 12, true>(P / 12, batch, ld, lo, di, up, rh, iw, info2, st, asmb);
+    } else {
+        hipLaunchKernelGGL((k_tri_part_iface<T>), grid2, blk, 0, st, P, batch, ld, summ, di, up, rh);
+        bps_status r = launch_tri_solve<T>(P, batch, ld, lo, di, up, rh, iw, info2, st);
+        if (r != BPS_OK) return r;
+    }
     hipLaunchKernelGGL((k_tri_part_back<T>), grid2, blk, 0, st, P, batch, ld, a, b, c, y, rh, flag,
                        info2);
     hipLaunchKernelGGL((k_tri_part_rescue<T>), grid1, blk, 0, st, n, batch, ld, a, b, c, y, w0,
