@@ -258,15 +258,18 @@ int tri_rows(int64_t n)
 // The same chunk algebra as k_tri_chunk, with the chunks of a system spread
 // over many workgroups (a wavefront holds 64 neighbouring systems at the same
 // chunk, so every row access is a contiguous 512-byte segment):
-//   1. k_tri_part_fwd: Thomas over each chunk interior, writing six numbers
-//      per chunk: g, gv, c' of the last interior row and z0, p0, q0;
-//   2. k_tri_part_iface: the interface rows (L_j, D_j, U_j, R_j) from them;
-//   3. the interface system (P unknowns per system) by launch_tri_solve;
-//   4. k_tri_part_back: each chunk's forward sweep again, now with the left
+//   1. k_tri_part_fwd: Thomas over each chunk interior, then the chunk's
+//      interface row as far as the chunk itself determines it (L_j and the
+//      parts of D_j, R_j without the next chunk, and its c), and z0, p0, q0;
+//   2. the interface system (P unknowns per system): by k_tri_chunk, which
+//      adds the next chunk's terms to each row as it loads it, when P suits
+//      it; otherwise k_tri_part_iface completes the rows in place and
+//      launch_tri_solve solves them (recursively for long interfaces);
+//   3. k_tri_part_back: each chunk's forward sweep again, now with the left
 //      interface value known, and its back substitution;
-//   5. k_tri_part_rescue: the sequential algorithm for systems whose chunk
+//   4. k_tri_part_rescue: the sequential algorithm for systems whose chunk
 //      or interface elimination met a bad pivot (it also writes info).
-// HBM: the four inputs twice, the solution once, about 10 values per chunk.
+// HBM: the four inputs twice, the solution once, about 11 values per chunk.
 constexpr int kPartM = 16;
 
 int tri_part_chunks(int64_t n)
