@@ -156,3 +156,22 @@ def test_partitioned_interface_breakdown_rescued():
     ref, rinfo = _oracle(tb)
     assert np.all(info == 0) and np.all(rinfo == 0)
     assert relerr_cols(got, ref) <= TOL[torch.float64]
+
+
+def test_interface_chunk_breakdown_goes_to_sequential_rescue():
+    """n = 2048: 128 outer chunks, so the 128-unknown interface system is
+    solved in 8 chunks of 16 rows.  Zeroing row 16 * 32 + 15 = 527 (an outer
+    interface row) makes that interface row exactly zero, the first pivot of
+    the interface system's chunk 2; the system then goes to the sequential
+    elimination, which meets the same zero pivot: info 528 as the oracle's,
+    the other systems solved as usual."""
+    n, batch = 2048, 6
+    tb = W.tri_dominant(n, batch, rng=np.random.default_rng(31))
+    r = 16 * 32 + 15
+    tb.a[r, 4] = tb.b[r, 4] = tb.c[r, 4] = 0.0
+    got, info, _ = _solve(tb)
+    ref, rinfo = _oracle(tb)
+    assert info[4] == rinfo[4] == r + 1
+    np.testing.assert_array_equal(info, rinfo)
+    ok = [s for s in range(batch) if s != 4]
+    assert relerr_cols(got[:, ok], ref[:, ok]) <= TOL[torch.float64]
