@@ -117,6 +117,19 @@ __device__ __forceinline__ double read_lane(double v, int lane)
     return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
 }
 
+// 64-bit value of another lane of the same 16-lane row (DPP row rotation, a
+// VALU move: no LDS round trip).  ROR = 1: the lane before (lane 0 of the
+// row takes lane 15); ROR = 15: the lane after (lane 15 takes lane 0).
+template <int ROR>
+__device__ __forceinline__ double row_rotate(double v)
+{
+    static_assert(ROR >= 1 && ROR <= 15, "row rotation by 1 .. 15 lanes");
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, int(b & 0xffffffffll), 0x120 + ROR, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, int(b >> 32), 0x120 + ROR, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+
 // One wavefront.  The serial recurrences run in every lane at once (lane t
 // carries coupling vector t & 7) with the running values in registers, and
 // their loops are unrolled so that the LDS reads they need are issued ahead
@@ -311,13 +324,26 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
 {
     constexpr int m = M - 2;
     constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;   // systems per wave, per workgroup
-    __shared__ double tbuf[2][P][SW][4];
-    __shared__ double rbuf[2][2 * P][SW][2];  // r_k stored at k and k + P
-    __shared__ double xbuf[2][P][SW][2];
+    // 16 chunks: a system is one 16-lane row (lane = chunk), and the values
+    // of the neighbouring chunks come by row rotation; otherwise lane =
+    // chunk * S + system and every exchange goes through LDS
+    constexpr bool ROW = (P == 16);
+    constexpr int PL = ROW ? 1 : P;          // LDS slots of the neighbour exchanges
+    __shared__ double tbuf[2][PL][SW][2];
+    // r_k stored at k and k + P; the index that varies fastest across lanes
+    // varies fastest in LDS (the chunk for ROW, else the system), so that
+    // the 16 lanes of a 128-bit access hit distinct banks
+    __shared__ double rbuf[2][ROW ? SW : 2 * P][ROW ? 2 * P : SW][2];
+    __shared__ double xbuf[2][PL][SW][2];
     constexpr bool LIN = (EX & kResStencil) != 0, PHI = (EX & kResPhase) != 0;
-    __shared__ double hbuf[EX != 0 ? P : 1][SW][4];  // halo rows of the explicit side
+    __shared__ double hbuf[EX != 0 ? PL : 1][SW][4];  // halo rows of the explicit side
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int j = lane / S, sl = wv * S + lane % S;     // chunk, system slot in the workgroup
+    // chunk, system slot in the workgroup
+    const int j = ROW ? (lane & 15) : lane / S, sl = wv * S + (ROW ? lane >> 4 : lane % S);
+    auto R = [&](int b, int k) -> double * {
+        if constexpr (ROW) return rbuf[b][sl][k];
+        else return rbuf[b][k][sl];
+    };
     // workgroups are dispatched round-robin over the 8 XCDs: the ones one
     // XCD runs back to back take neighbouring systems, so that row segments
     // narrower than a 128-byte line share it through one L2
@@ -359,7 +385,10 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         // explicit half of the theta scheme: rows -2, -1 (previous chunk's
         // last rows) and M, M+1 (next chunk's first rows) of the state
         double xm2 = 0.0, xm1 = 0.0, xp0 = 0.0, xp1 = 0.0;
-        if constexpr (EX != 0) {
+        if constexpr (EX != 0 && ROW) {
+            xm2 = row_rotate<1>(x[m]); xm1 = row_rotate<1>(x[m + 1]);
+            xp0 = row_rotate<15>(x[0]); xp1 = row_rotate<15>(x[1]);
+        } else if constexpr (EX != 0) {
             double *hb = hbuf[j][sl];
             hb[0] = x[0]; hb[1] = x[1]; hb[2] = x[m]; hb[3] = x[m + 1];
             wave_sync();
@@ -444,10 +473,15 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         }
         const double yR1 = x[m - 1];
         const double yR0 = x[m - 2] - cf[4 * m + 4 * (m - 2)] * yR1;
-        double *tb = tbuf[bf][j][sl];
-        tb[0] = t0; tb[1] = t1; tb[2] = yR0; tb[3] = yR1;
-        wave_sync();
-        const double yn0 = tbuf[bf][jn][sl][0], yn1 = tbuf[bf][jn][sl][1];
+        // y_0, y_1 of the next chunk
+        double yn0, yn1;
+        if constexpr (ROW) {
+            yn0 = row_rotate<15>(t0); yn1 = row_rotate<15>(t1);
+        } else {
+            tbuf[bf][j][sl][0] = t0; tbuf[bf][j][sl][1] = t1;
+            wave_sync();
+            yn0 = tbuf[bf][jn][sl][0]; yn1 = tbuf[bf][jn][sl][1];
+        }
         double fI0 = x[m], fI1 = x[m + 1];     // right-hand side on the interface rows
         if constexpr (LIN) {
             fI0 = ex2 * o2;
@@ -471,8 +505,8 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         }
         const double rj0 = fI0 - a * yR0 - b * yR1 - e * yn0;
         const double rj1 = fI1 - a * yR1 - d * yn0 - e * yn1;
-        rbuf[bf][j][sl][0] = rj0; rbuf[bf][j][sl][1] = rj1;
-        rbuf[bf][j + P][sl][0] = rj0; rbuf[bf][j + P][sl][1] = rj1;
+        R(bf, j)[0] = rj0; R(bf, j)[1] = rj1;
+        R(bf, j + P)[0] = rj0; R(bf, j + P)[1] = rj1;
         wave_sync();
         // interface values of this chunk: xI_j = sum_q T_q r_{j+q}
         // (block-circulant S^{-1}: T_q is its first block row)
@@ -488,17 +522,22 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
                     asm volatile("" : "+s"(tg) : "v"(r1));
                     T = (cdouble *)tg;
                 }
-                const double R0 = rbuf[bf][j + q][sl][0], R1 = rbuf[bf][j + q][sl][1];
+                const double R0 = R(bf, j + q)[0], R1 = R(bf, j + q)[1];
                 r0 = fma(T[4 * q + 0], R0, r0);
                 r0 = fma(T[4 * q + 1], R1, r0);
                 r1 = fma(T[4 * q + 2], R0, r1);
                 r1 = fma(T[4 * q + 3], R1, r1);
             }
         }
-        xbuf[bf][j][sl][0] = r0; xbuf[bf][j][sl][1] = r1;
-        wave_sync();
         // ... and of the previous chunk, from its lane
-        const double l0 = xbuf[bf][jm1][sl][0], l1 = xbuf[bf][jm1][sl][1];
+        double l0, l1;
+        if constexpr (ROW) {
+            l0 = row_rotate<1>(r0); l1 = row_rotate<1>(r1);
+        } else {
+            xbuf[bf][j][sl][0] = r0; xbuf[bf][j][sl][1] = r1;
+            wave_sync();
+            l0 = xbuf[bf][jm1][sl][0]; l1 = xbuf[bf][jm1][sl][1];
+        }
         asm volatile("" : "+s"(cg) : "v"(l1));
         cf = (cdouble *)cg;
         // backward: x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j), coefficient
