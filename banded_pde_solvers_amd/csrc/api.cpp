@@ -53,6 +53,8 @@ static bps_status check_desc(const bps_penta_desc *dsc)
         BPS_FAIL(BPS_EINVAL, "batch = %lld must be in [1, 2^31 - 64]", (long long)dsc->batch);
     if (dsc->ld < dsc->batch) BPS_FAIL(BPS_EINVAL, "ld = %lld < batch = %lld", (long long)dsc->ld,
                                        (long long)dsc->batch);
+    // element offsets (and their byte sizes) stay far inside int64
+    if (dsc->n > kMaxDim / dsc->ld) BPS_FAIL(BPS_EINVAL, "n * ld exceeds 2^40 elements");
     return BPS_OK;
 }
 
@@ -428,6 +430,7 @@ bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch, const i
         if (n < 1 || n > (int64_t(1) << 30)) BPS_FAIL(BPS_EINVAL, "n = %lld out of range", (long long)n);
         if (ld == 0) ld = batch;
         if (ld < batch) BPS_FAIL(BPS_EINVAL, "ld < batch");
+        if (n > kMaxDim / ld) BPS_FAIL(BPS_EINVAL, "n * ld exceeds 2^40 elements");
         for (int64_t i = 1; i < n; ++i)
             if (parent[i] < 0 || parent[i] >= i)
                 BPS_FAIL(BPS_EINVAL, "parent[%lld] = %d not in [0, %lld)", (long long)i, parent[i],

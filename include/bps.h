@@ -34,8 +34,9 @@
  * LAYOUTS
  *   Interleaved (the [P] and [H] layout): element (row i, system s) of an
  *   array is at index i*ld + s, 0 <= i < n, 0 <= s < batch, ld >= batch
- *   (elements, not bytes).  Systems are the fastest-varying index, so one
- *   elimination step over consecutive systems is one coalesced HBM stream.
+ *   (elements, not bytes), n * ld <= 2^40.  Systems are the fastest-varying
+ *   index, so one elimination step over consecutive systems is one
+ *   coalesced HBM stream.
  *
  * PRECISION
  *   BPS_F64 (double) everywhere; BPS_F32 (float) for the pentadiagonal and

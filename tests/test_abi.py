@@ -79,6 +79,8 @@ def _fake(k=0):
 @pytest.mark.parametrize("kw,code", [
     (dict(n=3), EINVAL), (dict(batch=0), EINVAL), (dict(ld=3, batch=4), EINVAL),
     (dict(dtype=7), EINVAL), (dict(flags=0x10), EINVAL), (dict(flags=1, n=5), EINVAL),
+    (dict(n=1 << 20, ld=1 << 21), EINVAL),          # n * ld above 2^40 elements
+    (dict(n=8, ld=1 << 62), EINVAL),                # and no overflow on the way
 ])
 def test_penta_factor_rejects_bad_desc(lib, kw, code):
     st = lib.penta_factor_batch(_desc(**kw), *(_fake(i) for i in range(6)), None, None)
