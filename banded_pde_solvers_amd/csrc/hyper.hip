@@ -105,8 +105,14 @@ __host__ __device__ constexpr int res_waves(int P)
 //   forward rows i < m:  [ralpha, beta, w0, w1]                  (4 doubles)
 //   backward rows i < m: [gamma, delta, UL0, UL1]                (4 doubles)
 //   header:     [a, b, c, d, e, URa, URb, URc]                   (8 doubles)
+//   16 chunks:  the interface step by periodic block cyclic reduction:
+//               per level h = 1, 2, 4, 8 the 2x2 blocks alpha_h, gamma_h
+//               (row-major), then (L + D + U)^{-1} of the last level
+//               (36 doubles, in the space of the T blocks)
 //   T blocks:   T_q (2x2, row-major) for q < P                   (4P doubles)
 __host__ __device__ constexpr int res_coef_elems(int M, int P) { return 8 * (M - 2) + 8 + 4 * P; }
+// 16 chunks: one system per 16-lane row, interface step by PCR (see below)
+__host__ __device__ constexpr bool res_row(int P) { return P == 16; }
 
 // 64-bit value of lane `lane` (uniform) of the wavefront
 __device__ __forceinline__ double read_lane(double v, int lane)
@@ -261,9 +267,49 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
         blk[bi][r][q] = acc.value();
     }
     __syncthreads();
-    // ---- Gauss-Jordan on [S | I] without pivoting (S is symmetric positive
-    // definite: a Schur complement of I + sigma*D4, sigma >= 0).  Lane t holds
-    // column t in registers; pivot column entries are broadcast by readlane.
+    // ---- 16 chunks: coefficients of periodic block cyclic reduction on the
+    // interface system S xI = r (all block rows alike: L = S_{j,j-1},
+    // D = S_{j,j}, U = S_{j,j+1}).  Level h: alpha = -L D^{-1},
+    // gamma = -U D^{-1}; r_j += alpha r_{j-h} + gamma r_{j+h}; L, D, U of the
+    // next level alpha L, D + alpha U + gamma L, gamma U.  After the level
+    // h = P/2, j - P and j + P are j itself: xI_j = (L + D + U)^{-1} r_j.
+    // (S is a Schur complement of the SPD I + sigma D4, hence SPD; the
+    // reduction is block elimination in another order.)
+    if constexpr (res_row(P)) {
+        if (t == 0) {
+            struct B2 { double a, b, c, d; };
+            auto mul = [](B2 x, B2 y) {
+                return B2{x.a * y.a + x.b * y.c, x.a * y.b + x.b * y.d,
+                          x.c * y.a + x.d * y.c, x.c * y.b + x.d * y.d};
+            };
+            auto add = [](B2 x, B2 y) { return B2{x.a + y.a, x.b + y.b, x.c + y.c, x.d + y.d}; };
+            auto neg = [](B2 x) { return B2{-x.a, -x.b, -x.c, -x.d}; };
+            auto inv = [](B2 x) {
+                const double r = 1.0 / (x.a * x.d - x.b * x.c);
+                return B2{x.d * r, -x.b * r, -x.c * r, x.a * r};
+            };
+            B2 L{blk[2][0][0], blk[2][0][1], blk[2][1][0], blk[2][1][1]};
+            B2 D{blk[0][0][0], blk[0][0][1], blk[0][1][0], blk[0][1][1]};
+            B2 U{blk[1][0][0], blk[1][0][1], blk[1][1][0], blk[1][1][1]};
+            double *pc = coef + 8 * m + 8;
+            for (int h = 1; h < P; h <<= 1, pc += 8) {
+                const B2 Di = inv(D);
+                const B2 al = neg(mul(L, Di)), ga = neg(mul(U, Di));
+                pc[0] = al.a; pc[1] = al.b; pc[2] = al.c; pc[3] = al.d;
+                pc[4] = ga.a; pc[5] = ga.b; pc[6] = ga.c; pc[7] = ga.d;
+                const B2 nL = mul(al, L), nU = mul(ga, U);
+                D = add(D, add(mul(al, U), mul(ga, L)));
+                L = nL; U = nU;
+            }
+            const B2 Mi = inv(add(L, add(D, U)));
+            pc[0] = Mi.a; pc[1] = Mi.b; pc[2] = Mi.c; pc[3] = Mi.d;
+        }
+    }
+    // ---- other chunk counts: Gauss-Jordan on [S | I] without pivoting (S is
+    // symmetric positive definite: a Schur complement of I + sigma*D4,
+    // sigma >= 0).  Lane t holds column t in registers; pivot column entries
+    // are broadcast by readlane.
+    if constexpr (!res_row(P)) {
     double cv[n2];
 #pragma unroll
     for (int i = 0; i < n2; ++i) {
@@ -289,6 +335,13 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
 #pragma unroll
         for (int i = 0; i < n2; ++i) cv[i] = (i == kp) ? pk : cv[i] - f[i] * pk;
     }
+    // T_q = rows 0, 1 of S^{-1}, columns 2q, 2q+1 (held by lanes n2 + 2q + c)
+    if (t >= n2 && t < w) {
+        const int q = (t - n2) >> 1, cc = (t - n2) & 1;
+        coef[8 * m + 8 + 4 * q + cc] = cv[0];
+        coef[8 * m + 8 + 4 * q + 2 + cc] = cv[1];
+    }
+    }
     // ---- outputs ----
     for (int idx = t; idx < m; idx += blockDim.x) {
         double *fw = coef + 4 * idx, *bw = coef + 4 * m + 4 * idx;
@@ -302,12 +355,6 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
         const double URb = (d - be[m - 1] * URa) * ra[m - 1];
         const double URc = e * ra[m - 1];
         h[5] = URa; h[6] = URb; h[7] = URc;
-    }
-    // T_q = rows 0, 1 of S^{-1}, columns 2q, 2q+1 (held by lanes n2 + 2q + c)
-    if (t >= n2 && t < w) {
-        const int q = (t - n2) >> 1, cc = (t - n2) & 1;
-        coef[8 * m + 8 + 4 * q + cc] = cv[0];
-        coef[8 * m + 8 + 4 * q + 2 + cc] = cv[1];
     }
 }
 
@@ -327,23 +374,18 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
     // 16 chunks: a system is one 16-lane row (lane = chunk), and the values
     // of the neighbouring chunks come by row rotation; otherwise lane =
     // chunk * S + system and every exchange goes through LDS
-    constexpr bool ROW = (P == 16);
+    constexpr bool ROW = res_row(P);
     constexpr int PL = ROW ? 1 : P;          // LDS slots of the neighbour exchanges
     __shared__ double tbuf[2][PL][SW][2];
-    // r_k stored at k and k + P; the index that varies fastest across lanes
-    // varies fastest in LDS (the chunk for ROW, else the system), so that
-    // the 16 lanes of a 128-bit access hit distinct banks
-    __shared__ double rbuf[2][ROW ? SW : 2 * P][ROW ? 2 * P : SW][2];
+    // r_k stored at k and k + P (the dense interface step; ROW uses none)
+    __shared__ double rbuf[2][ROW ? 1 : 2 * P][SW][2];
     __shared__ double xbuf[2][PL][SW][2];
     constexpr bool LIN = (EX & kResStencil) != 0, PHI = (EX & kResPhase) != 0;
     __shared__ double hbuf[EX != 0 ? PL : 1][SW][4];  // halo rows of the explicit side
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     // chunk, system slot in the workgroup
     const int j = ROW ? (lane & 15) : lane / S, sl = wv * S + (ROW ? lane >> 4 : lane % S);
-    auto R = [&](int b, int k) -> double * {
-        if constexpr (ROW) return rbuf[b][sl][k];
-        else return rbuf[b][k][sl];
-    };
+    auto R = [&](int b, int k) -> double * { return rbuf[b][k][sl]; };
     // workgroups are dispatched round-robin over the 8 XCDs: the ones one
     // XCD runs back to back take neighbouring systems, so that row segments
     // narrower than a 128-byte line share it through one L2
@@ -505,13 +547,40 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         }
         const double rj0 = fI0 - a * yR0 - b * yR1 - e * yn0;
         const double rj1 = fI1 - a * yR1 - d * yn0 - e * yn1;
+        double r0 = 0.0, r1 = 0.0;
+        if constexpr (ROW) {
+            // interface values by periodic block cyclic reduction across the
+            // row's 16 lanes: four levels of neighbours 1, 2, 4, 8 lanes away
+            // (row rotations), then (L + D + U)^{-1}
+            const double *pg = coef + 8 * m + 8;
+            asm volatile("" : "+s"(pg) : "v"(rj1));
+            cdouble *pc = (cdouble *)pg;
+            double q0 = rj0, q1 = rj1;
+            auto level = [&](double m0, double m1, double p0, double p1, int lv) {
+                cdouble *c8 = pc + 8 * lv;       // [alpha (2x2), gamma (2x2)]
+                double n0 = q0, n1 = q1;
+                n0 = fma(c8[0], m0, n0); n0 = fma(c8[1], m1, n0);
+                n0 = fma(c8[4], p0, n0); n0 = fma(c8[5], p1, n0);
+                n1 = fma(c8[2], m0, n1); n1 = fma(c8[3], m1, n1);
+                n1 = fma(c8[6], p0, n1); n1 = fma(c8[7], p1, n1);
+                q0 = n0; q1 = n1;
+            };
+            level(row_rotate<1>(q0), row_rotate<1>(q1), row_rotate<15>(q0), row_rotate<15>(q1), 0);
+            level(row_rotate<2>(q0), row_rotate<2>(q1), row_rotate<14>(q0), row_rotate<14>(q1), 1);
+            level(row_rotate<4>(q0), row_rotate<4>(q1), row_rotate<12>(q0), row_rotate<12>(q1), 2);
+            {
+                const double h0 = row_rotate<8>(q0), h1 = row_rotate<8>(q1);   // j - 8 = j + 8
+                level(h0, h1, h0, h1, 3);
+            }
+            cdouble *mi = pc + 32;
+            r0 = mi[0] * q0; r0 = fma(mi[1], q1, r0);
+            r1 = mi[2] * q0; r1 = fma(mi[3], q1, r1);
+        } else {
         R(bf, j)[0] = rj0; R(bf, j)[1] = rj1;
         R(bf, j + P)[0] = rj0; R(bf, j + P)[1] = rj1;
         wave_sync();
         // interface values of this chunk: xI_j = sum_q T_q r_{j+q}
         // (block-circulant S^{-1}: T_q is its first block row)
-        double r0 = 0.0, r1 = 0.0;
-        {
             const double *tg = coef + 8 * m + 8;
             asm volatile("" : "+s"(tg) : "v"(rj1));
             cdouble *T = (cdouble *)tg;
