@@ -54,13 +54,16 @@ template bps_status launch_hyper_diagonals<double>(int64_t, double, void *, hipS
 //   interfaces:   S xI = r,  r_j = fI_j - B_own y_j - B_next y_{j+1},  y = E^{-1} f
 //
 // One lane owns one chunk of one system and keeps its M values in registers
-// for all time steps; the chunks of a system exchange four numbers per step
-// through LDS.  Per step and lane:
+// for all time steps; the chunks of a system exchange a few numbers per step
+// (through LDS, or by DPP row rotations when a system fills a 16-lane row).
+// Per step and lane:
 //   forward  g = L^{-1} f (E = L R), with y_0, y_1 accumulated as w_k . g,
 //            w_k = R^{-T} e_k, and y_{m-1}, y_{m-2} from the last two g;
 //   exchange r_j (needs y_0, y_1 of the next chunk), then
 //            xI_j = sum_q T_q r_{j+q} with T_q the first block row of S^{-1}
-//            (S is block-circulant because every chunk is identical);
+//            (S is block-circulant because every chunk is identical), or,
+//            for 16 chunks (one system per 16-lane row), periodic block
+//            cyclic reduction across the row's lanes;
 //   backward x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j), U = L^{-1} C.
 // HBM sees the state twice per call (load, store) instead of twice per step.
 //
