@@ -244,7 +244,7 @@ bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, 
     if (resident) {
         // the operator I + sigma*D4 with constant diagonals: every chunk of a
         // system sees the same interior block, so the register-resident
-        // multi-step kernel applies (the diagonals built above are unused)
+        // multi-step kernel applies (it needs no diagonal arrays)
         const double sigma = dt / (dx * dx * dx * dx);
         return launch_hyper_resident(n, batch, ld, nsteps, sigma, 0, 1.0, 0.0, 0.0, 0.0, fac, C,
                                      st);
