@@ -147,3 +147,15 @@ def test_workload1_full_sampled():
     assert _traj_err(out[:, cols], ref, C0[:, cols]) <= 2e-9
     one = _step(C0, cfg["dt"], cfg["dx"], 1)
     assert relerr_cols(one[:, cols], _oracle(C0[:, cols], cfg["dt"], cfg["dx"], 1)) <= 1e-10
+
+
+@pytest.mark.parametrize("n", [1024, 256, 832, 100])
+def test_zero_time_step_is_identity(n):
+    """dt = 0 gives sigma = 0 and the operator I: the state comes back
+    unchanged (to rounding) on every path — the resident kernel with the
+    cyclic-reduction interface (n = 1024), with the dense interface (256,
+    832), and the streaming kernel (100)."""
+    C0 = np.random.default_rng(n).uniform(-1, 1, (n, 40))
+    out = _step(C0, 0.0, 1.0 / n, 7)
+    np.testing.assert_allclose(out, C0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out, _oracle(C0, 0.0, 1.0 / n, 7), rtol=0, atol=1e-15)

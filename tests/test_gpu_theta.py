@@ -147,3 +147,13 @@ def test_crank_nicolson_full_sampled():
     assert np.max(err) <= cfg["nsteps"] * _tol(n, dt, dx, theta)
     one = _run(C0, dt, dx, theta, 1)
     assert relerr_cols(one[:, cols], _oracle(C0[:, cols], dt, dx, theta, 1)) <= _tol(n, dt, dx, theta)
+
+
+@pytest.mark.parametrize("n", [1024, 96])
+def test_theta_zero_time_step_is_identity(n):
+    """dt = 0: both sides of the theta scheme are I."""
+    C0 = np.random.default_rng(n + 3).uniform(-1, 1, (n, 24))
+    C = dev(C0)
+    work = buf(bps.hyperdiffusion_theta_work_bytes(n, 24))
+    bps.hyperdiffusion_theta_step(C, 0.0, 1.0 / n, 0.5, 5, work)
+    np.testing.assert_allclose(host(C), C0, rtol=0, atol=1e-15)
