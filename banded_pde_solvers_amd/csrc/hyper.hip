@@ -90,7 +90,7 @@ struct Dot2 {
     __device__ double value() const { return p + s; }
 };
 
-constexpr int kResMaxP = 16;    // chunks per system supported by the resident kernel
+constexpr int kResMaxP = 16;    // chunks per system supported by the resident kernel (and 32)
 // A wavefront of the resident kernel holds 64 / P systems times P chunks and
 // exchanges interface values only among its own lanes, so the waves never
 // wait on one another: the ones sharing a SIMD hide each other's latencies.
@@ -100,20 +100,25 @@ constexpr int kResMaxP = 16;    // chunks per system supported by the resident k
 __host__ __device__ constexpr int res_systems(int P) { return kWave / P; }
 __host__ __device__ constexpr int res_waves(int P)
 {
+    // (at most 4 wavefronts: with 32 chunks a workgroup of 8 systems still
+    // leaves room for three per CU)
     return (res_systems(P) * P == kWave && res_systems(P) < 16 && 16 % res_systems(P) == 0)
-               ? 16 / res_systems(P) : 1;
+               ? (16 / res_systems(P) < 4 ? 16 / res_systems(P) : 4) : 1;
 }
 
 // coefficient block written by the set-up kernel, read with uniform loads:
 //   forward rows i < m:  [ralpha, beta, w0, w1]                  (4 doubles)
 //   backward rows i < m: [gamma, delta, UL0, UL1]                (4 doubles)
 //   header:     [a, b, c, d, e, URa, URb, URc]                   (8 doubles)
-//   16 chunks:  the interface step by periodic block cyclic reduction:
-//               per level h = 1, 2, 4, 8 the 2x2 blocks alpha_h, gamma_h
-//               (row-major), then (L + D + U)^{-1} of the last level
-//               (36 doubles, in the space of the T blocks)
+//   P a power of two (after the T blocks): periodic block cyclic
+//               reduction on the interface system: per level h = 1, 2, ...,
+//               P/2 the 2x2 blocks alpha_h, gamma_h (row-major), then
+//               (L + D + U)^{-1} of the last level (8 log2 P + 4 doubles);
+//               16 chunks use them in the time step, the T blocks of other
+//               powers of two are computed from them
 //   T blocks:   T_q (2x2, row-major) for q < P                   (4P doubles)
-__host__ __device__ constexpr int res_coef_elems(int M, int P) { return 8 * (M - 2) + 8 + 4 * P; }
+__host__ __device__ constexpr int res_coef_elems(int M, int P) { return 8 * (M - 2) + 8 + 4 * P + 44; }
+__host__ __device__ constexpr bool res_pow2(int P) { return (P & (P - 1)) == 0; }
 // 16 chunks: one system per 16-lane row, interface step by PCR (see below)
 __host__ __device__ constexpr bool res_row(int P) { return P == 16; }
 
@@ -270,7 +275,7 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
         blk[bi][r][q] = acc.value();
     }
     __syncthreads();
-    // ---- 16 chunks: coefficients of periodic block cyclic reduction on the
+    // ---- P a power of two: coefficients of periodic block cyclic reduction on the
     // interface system S xI = r (all block rows alike: L = S_{j,j-1},
     // D = S_{j,j}, U = S_{j,j+1}).  Level h: alpha = -L D^{-1},
     // gamma = -U D^{-1}; r_j += alpha r_{j-h} + gamma r_{j+h}; L, D, U of the
@@ -278,7 +283,8 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     // h = P/2, j - P and j + P are j itself: xI_j = (L + D + U)^{-1} r_j.
     // (S is a Schur complement of the SPD I + sigma D4, hence SPD; the
     // reduction is block elimination in another order.)
-    if constexpr (res_row(P)) {
+    __shared__ double pcr[res_pow2(P) ? 44 : 1];
+    if constexpr (res_pow2(P)) {
         if (t == 0) {
             struct B2 { double a, b, c, d; };
             auto mul = [](B2 x, B2 y) {
@@ -293,8 +299,11 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
             };
             B2 L{blk[2][0][0], blk[2][0][1], blk[2][1][0], blk[2][1][1]};
             B2 D{blk[0][0][0], blk[0][0][1], blk[0][1][0], blk[0][1][1]};
-            B2 U{blk[1][0][0], blk[1][0][1], blk[1][1][0], blk[1][1][1]};
-            double *pc = coef + 8 * m + 8;
+            // with 2 chunks both neighbours are the other chunk, and blk[1] and
+            // blk[2] each hold its whole coupling: count it once
+            B2 U = P == 2 ? B2{0.0, 0.0, 0.0, 0.0}
+                          : B2{blk[1][0][0], blk[1][0][1], blk[1][1][0], blk[1][1][1]};
+            double *pc = pcr;
             for (int h = 1; h < P; h <<= 1, pc += 8) {
                 const B2 Di = inv(D);
                 const B2 al = neg(mul(L, Di)), ga = neg(mul(U, Di));
@@ -307,12 +316,56 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
             const B2 Mi = inv(add(L, add(D, U)));
             pc[0] = Mi.a; pc[1] = Mi.b; pc[2] = Mi.c; pc[3] = Mi.d;
         }
+        __syncthreads();
+        for (int i = t; i < 44; i += blockDim.x) coef[8 * m + 8 + 4 * P + i] = pcr[i];
+    }
+    // ---- other powers of two: T_q, the first block row of S^{-1}, by the
+    // same reduction applied to the block column E_0 = [I; 0; ...; 0]
+    // (S X = E_0, lane j < P holds the 2x2 block row j of X; S is symmetric,
+    // so T_q = X_q^T)
+    if constexpr (res_pow2(P) && !res_row(P)) {
+        __shared__ double xr[2][P][4];
+        double x4[4] = {t == 0 ? 1.0 : 0.0, 0.0, 0.0, t == 0 ? 1.0 : 0.0};
+        int cur = 0;
+        if (t < P) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xr[0][t][e] = x4[e];
+        }
+        __syncthreads();
+        int lv = 0;
+        for (int h = 1; h < P; h <<= 1, ++lv) {
+            if (t < P) {
+                const double *al = pcr + 8 * lv, *ga = al + 4;
+                const double *xm = xr[cur][(t - h + P) % P], *xp = xr[cur][(t + h) % P];
+                // x4 += alpha xm + gamma xp (2x2 blocks, row-major)
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        x4[2 * r + c] += al[2 * r] * xm[c] + al[2 * r + 1] * xm[2 + c] +
+                                         ga[2 * r] * xp[c] + ga[2 * r + 1] * xp[2 + c];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xr[cur ^ 1][t][e] = x4[e];
+            }
+            cur ^= 1;
+            __syncthreads();
+        }
+        if (t < P) {
+            const double *mi = pcr + 8 * lv;
+            double xq[4];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) xq[2 * r + c] = mi[2 * r] * x4[c] + mi[2 * r + 1] * x4[2 + c];
+            double *T = coef + 8 * m + 8 + 4 * t;
+            T[0] = xq[0]; T[1] = xq[2]; T[2] = xq[1]; T[3] = xq[3];     // X_q^T
+        }
     }
     // ---- other chunk counts: Gauss-Jordan on [S | I] without pivoting (S is
     // symmetric positive definite: a Schur complement of I + sigma*D4,
     // sigma >= 0).  Lane t holds column t in registers; pivot column entries
     // are broadcast by readlane.
-    if constexpr (!res_row(P)) {
+    if constexpr (!res_pow2(P)) {
     double cv[n2];
 #pragma unroll
     for (int i = 0; i < n2; ++i) {
@@ -555,7 +608,7 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
             // interface values by periodic block cyclic reduction across the
             // row's 16 lanes: four levels of neighbours 1, 2, 4, 8 lanes away
             // (row rotations), then (L + D + U)^{-1}
-            const double *pg = coef + 8 * m + 8;
+            const double *pg = coef + 8 * m + 8 + 4 * P;
             asm volatile("" : "+s"(pg) : "v"(rj1));
             cdouble *pc = (cdouble *)pg;
             double q0 = rj0, q1 = rj1;
@@ -671,7 +724,7 @@ int resident_chunk(int64_t n)
     constexpr int M = 64;
     if (n % M != 0) return 0;
     const int64_t P = n / M;
-    return (P >= 2 && P <= kResMaxP) ? M : 0;
+    return ((P >= 2 && P <= kResMaxP) || P == 32) ? M : 0;
 }
 
 size_t resident_coef_bytes(int64_t n)
@@ -716,7 +769,7 @@ bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t n
 {
     constexpr int M = 64;
     if (resident_chunk(n) != M || !(sigma >= 0.0))
-        BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16, sigma >= 0");
+        BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16 or P = 32, sigma >= 0");
     double *cf = (double *)coef, *x = (double *)C;
 #define BPS_RES_CASE(PP) \
     case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, st); break;
@@ -724,6 +777,7 @@ bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t n
     BPS_RES_CASE(2) BPS_RES_CASE(3) BPS_RES_CASE(4) BPS_RES_CASE(5) BPS_RES_CASE(6)
     BPS_RES_CASE(7) BPS_RES_CASE(8) BPS_RES_CASE(9) BPS_RES_CASE(10) BPS_RES_CASE(11)
     BPS_RES_CASE(12) BPS_RES_CASE(13) BPS_RES_CASE(14) BPS_RES_CASE(15) BPS_RES_CASE(16)
+    BPS_RES_CASE(32)
     default: BPS_FAIL(BPS_ENOTSUP, "unsupported chunk count");
     }
 #undef BPS_RES_CASE

@@ -32,6 +32,13 @@ def _oracle(C0, dt, dx, nsteps, diagonals=None):
     return W.to_interleaved(oracle.hyperdiffusion(W.to_flat(C0), dt, dx, nsteps, diagonals))
 
 
+def _dt(n):
+    """1e-6, or for n > 1024 the step that keeps sigma = dt/dx^4 at its
+    n = 1024 value (1.1e6), so that the bounds below, set for that
+    conditioning, apply to the 32-chunk kernel as well."""
+    return 1e-6 * min(1.0, (1024.0 / n) ** 4)
+
+
 def _traj_err(out, ref, C0):
     """Per-system trajectory error relative to the initial state's norm.
 
@@ -58,11 +65,11 @@ def test_workload0_modes_full():
 
 
 @pytest.mark.parametrize("n,batch", [(6, 1), (7, 65), (64, 130), (128, 37), (192, 50), (256, 17),
-                                     (1024, 200),
+                                     (1024, 200), (2048, 40),
                                      # chunk counts that do not divide a wavefront
                                      (320, 33), (448, 20), (832, 40), (960, 17)])
 def test_one_step_parity(n, batch):
-    dt, dx = 1e-6, 1.0 / n
+    dt, dx = _dt(n), 1.0 / n
     C0 = np.random.default_rng(n + batch).uniform(-1, 1, (n, batch))
     assert relerr_cols(_step(C0, dt, dx, 1), _oracle(C0, dt, dx, 1)) <= 1e-10
 
@@ -76,11 +83,11 @@ def test_workload1_trajectory_reduced_batch():
     assert _traj_err(out, ref, C0) <= 2e-9
 
 
-@pytest.mark.parametrize("n,batch", [(128, 33), (1024, 70)])
+@pytest.mark.parametrize("n,batch", [(128, 33), (1024, 70), (2048, 20)])
 def test_resident_and_streaming_paths_agree(n, batch):
     """The built-in operator (register-resident chunked kernel) against the
     same matrix given explicitly (one lane per system, streaming kernel)."""
-    dt, dx = 1e-6, 1.0 / n
+    dt, dx = _dt(n), 1.0 / n
     C0 = np.random.default_rng(n).uniform(-1, 1, (n, batch))
     dg = oracle.hyperdiffusion_diagonals(n, dt, dx)
     for steps in (1, 7):
@@ -159,3 +166,15 @@ def test_zero_time_step_is_identity(n):
     out = _step(C0, 0.0, 1.0 / n, 7)
     np.testing.assert_allclose(out, C0, rtol=0, atol=1e-15)
     np.testing.assert_allclose(out, _oracle(C0, 0.0, 1.0 / n, 7), rtol=0, atol=1e-15)
+
+
+def test_32_chunk_trajectory():
+    """N = 2048 (32 chunks of 64 rows: dense interface step, T from the
+    cyclic-reduction coefficients), 30 steps on 90 systems against the
+    oracle's trajectory."""
+    n = 2048
+    dt, dx = _dt(n), 1.0 / n
+    C0 = W.hyperdiffusion_random(n, 90, rng=np.random.default_rng(13))
+    out = _step(C0, dt, dx, 30)
+    ref = _oracle(C0, dt, dx, 30)
+    assert _traj_err(out, ref, C0) <= 2e-9
