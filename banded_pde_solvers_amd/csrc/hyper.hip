@@ -90,7 +90,7 @@ struct Dot2 {
     __device__ double value() const { return p + s; }
 };
 
-constexpr int kResMaxP = 16;    // chunks per system supported by the resident kernel (and 32)
+constexpr int kResMaxP = 16;    // chunks per system supported by the resident kernel (and 32, 64)
 // A wavefront of the resident kernel holds 64 / P systems times P chunks and
 // exchanges interface values only among its own lanes, so the waves never
 // wait on one another: the ones sharing a SIMD hide each other's latencies.
@@ -100,8 +100,8 @@ constexpr int kResMaxP = 16;    // chunks per system supported by the resident k
 __host__ __device__ constexpr int res_systems(int P) { return kWave / P; }
 __host__ __device__ constexpr int res_waves(int P)
 {
-    // (at most 4 wavefronts: with 32 chunks a workgroup of 8 systems still
-    // leaves room for three per CU)
+    // (at most 4 wavefronts: with 32 or 64 chunks a workgroup of 8 or 4
+    // systems still leaves room for three per CU)
     return (res_systems(P) * P == kWave && res_systems(P) < 16 && 16 % res_systems(P) == 0)
                ? (16 / res_systems(P) < 4 ? 16 / res_systems(P) : 4) : 1;
 }
@@ -113,11 +113,11 @@ __host__ __device__ constexpr int res_waves(int P)
 //   P a power of two (after the T blocks): periodic block cyclic
 //               reduction on the interface system: per level h = 1, 2, ...,
 //               P/2 the 2x2 blocks alpha_h, gamma_h (row-major), then
-//               (L + D + U)^{-1} of the last level (8 log2 P + 4 doubles);
+//               (L + D + U)^{-1} of the last level (8 log2 P + 4 <= 52 doubles);
 //               16 chunks use them in the time step, the T blocks of other
 //               powers of two are computed from them
 //   T blocks:   T_q (2x2, row-major) for q < P                   (4P doubles)
-__host__ __device__ constexpr int res_coef_elems(int M, int P) { return 8 * (M - 2) + 8 + 4 * P + 44; }
+__host__ __device__ constexpr int res_coef_elems(int M, int P) { return 8 * (M - 2) + 8 + 4 * P + 52; }
 __host__ __device__ constexpr bool res_pow2(int P) { return (P & (P - 1)) == 0; }
 // 16 chunks: one system per 16-lane row, interface step by PCR (see below)
 __host__ __device__ constexpr bool res_row(int P) { return P == 16; }
@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     // h = P/2, j - P and j + P are j itself: xI_j = (L + D + U)^{-1} r_j.
     // (S is a Schur complement of the SPD I + sigma D4, hence SPD; the
     // reduction is block elimination in another order.)
-    __shared__ double pcr[res_pow2(P) ? 44 : 1];
+    __shared__ double pcr[res_pow2(P) ? 52 : 1];
     if constexpr (res_pow2(P)) {
         if (t == 0) {
             struct B2 { double a, b, c, d; };
@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
             pc[0] = Mi.a; pc[1] = Mi.b; pc[2] = Mi.c; pc[3] = Mi.d;
         }
         __syncthreads();
-        for (int i = t; i < 44; i += blockDim.x) coef[8 * m + 8 + 4 * P + i] = pcr[i];
+        for (int i = t; i < 52; i += blockDim.x) coef[8 * m + 8 + 4 * P + i] = pcr[i];
     }
     // ---- other powers of two: T_q, the first block row of S^{-1}, by the
     // same reduction applied to the block column E_0 = [I; 0; ...; 0]
@@ -724,7 +724,7 @@ int resident_chunk(int64_t n)
     constexpr int M = 64;
     if (n % M != 0) return 0;
     const int64_t P = n / M;
-    return ((P >= 2 && P <= kResMaxP) || P == 32) ? M : 0;
+    return ((P >= 2 && P <= kResMaxP) || P == 32 || P == 64) ? M : 0;
 }
 
 size_t resident_coef_bytes(int64_t n)
@@ -769,7 +769,7 @@ bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t n
 {
     constexpr int M = 64;
     if (resident_chunk(n) != M || !(sigma >= 0.0))
-        BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16 or P = 32, sigma >= 0");
+        BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16 or P = 32, 64, sigma >= 0");
     double *cf = (double *)coef, *x = (double *)C;
 #define BPS_RES_CASE(PP) \
     case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, st); break;
@@ -777,7 +777,7 @@ bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t n
     BPS_RES_CASE(2) BPS_RES_CASE(3) BPS_RES_CASE(4) BPS_RES_CASE(5) BPS_RES_CASE(6)
     BPS_RES_CASE(7) BPS_RES_CASE(8) BPS_RES_CASE(9) BPS_RES_CASE(10) BPS_RES_CASE(11)
     BPS_RES_CASE(12) BPS_RES_CASE(13) BPS_RES_CASE(14) BPS_RES_CASE(15) BPS_RES_CASE(16)
-    BPS_RES_CASE(32)
+    BPS_RES_CASE(32) BPS_RES_CASE(64)
     default: BPS_FAIL(BPS_ENOTSUP, "unsupported chunk count");
     }
 #undef BPS_RES_CASE
