@@ -61,9 +61,11 @@ template bps_status launch_hyper_diagonals<double>(int64_t, double, void *, hipS
 //            w_k = R^{-T} e_k, and y_{m-1}, y_{m-2} from the last two g;
 //   exchange r_j (needs y_0, y_1 of the next chunk), then
 //            xI_j = sum_q T_q r_{j+q} with T_q the first block row of S^{-1}
-//            (S is block-circulant because every chunk is identical), or,
-//            for 16 chunks (one system per 16-lane row), periodic block
-//            cyclic reduction across the row's lanes;
+//            (S is block-circulant because every chunk is identical; the
+//            set-up gets T by Gauss-Jordan, or for a power-of-two P from the
+//            coefficients of periodic block cyclic reduction), or, for 16
+//            chunks (one system per 16-lane row), that cyclic reduction
+//            itself across the row's lanes;
 //   backward x = R^{-1}(g - U_L xI_{j-1} - U_R xI_j), U = L^{-1} C.
 // HBM sees the state twice per call (load, store) instead of twice per step.
 //
@@ -95,8 +97,9 @@ constexpr int kResMaxP = 16;    // chunks per system supported by the resident k
 // exchanges interface values only among its own lanes, so the waves never
 // wait on one another: the ones sharing a SIMD hide each other's latencies.
 // Where the systems of one wavefront fill less than a 128-byte row segment,
-// a workgroup gathers the wavefronts of 16 neighbouring systems, so that
-// the state is read and written in whole cache lines by one CU.
+// a workgroup gathers the wavefronts of up to 16 neighbouring systems (at
+// most 4 wavefronts), so that the state is read and written in whole or
+// half cache lines by one CU.
 __host__ __device__ constexpr int res_systems(int P) { return kWave / P; }
 __host__ __device__ constexpr int res_waves(int P)
 {
