@@ -39,6 +39,8 @@
 // tridiagonal and periodic; block cyclic reduction with indices modulo P
 // (P a power of two) leaves after log2 P steps each unknown coupled only to
 // itself through L_j, D_j and U_j, so xI_j = (L_j + D_j + U_j)^{-1} r_j.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -100,10 +102,18 @@ __device__ int32_t seq_penta_solve(int64_t n, int64_t ld, const T *A, const T *B
 }
 
 // One workgroup holds S systems x P chunks of M rows (lane = chunk j of
-// system sl); n = P * M, P * S <= 512.  Dynamic LDS: 14 * P * S values of
-// T + S flags.
+// system sl); n = P * M, P * S <= 512.  Dynamic LDS: two buffers of
+// kSpikeFields * P * S values of T (successive exchange stages alternate
+// between them, so one barrier separates a stage's writes from its reads
+// and none is needed after the reads) + S flags.
+constexpr int kSpikeFields = 10;
+
+// fp32: registers capped for four waves per SIMD (two 512-lane workgroups
+// per CU, so that one workgroup's loads overlap the other's reduction), at
+// the cost of a few spilled values; fp64 needs about twice the registers
+// and runs two waves per SIMD.
 template <typename T, int M, int S, bool CYC>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 4 : 2)))
 k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
               const T *__restrict__ C, const T *__restrict__ D, const T *__restrict__ E,
               T *__restrict__ x, T *__restrict__ work, int32_t *__restrict__ info,
@@ -111,8 +121,8 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
 {
     constexpr int m = M - 2;            // interior rows of a chunk
     extern __shared__ unsigned char lds_raw[];
-    T *buf = reinterpret_cast<T *>(lds_raw);          // [field][P][S]
-    int32_t *flag = reinterpret_cast<int32_t *>(buf + 14 * P * S);
+    T *buf = reinterpret_cast<T *>(lds_raw);          // [2][field][P][S]
+    int32_t *flag = reinterpret_cast<int32_t *>(buf + 2 * kSpikeFields * P * S);
     const int tid = threadIdx.x;
     if (tid < S) flag[tid] = 0;
     const int j = tid / S, sl = tid % S;
@@ -129,7 +139,9 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     const int64_t off = (act ? s : batch - 1) + int64_t(j) * M * ld;
     const T *pa = A + off, *pb = B + off, *pc = C + off, *pd = D + off, *pe = E + off;
     T *px = x + off;
-    auto F = [&](int field, int jj) -> T & { return buf[(field * P + jj) * S + sl]; };
+    auto F = [&](int bb, int field, int jj) -> T & {
+        return buf[((bb * kSpikeFields + field) * P + jj) * S + sl];
+    };
 
     // ---- forward sweep over the interior, inputs streamed LA rows ahead ----
     constexpr int LA = 4;
@@ -212,15 +224,15 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     const T dR1 = last_chunk ? T(0) : qd[kR1], eR1 = last_chunk ? T(0) : qe[kR1], fR1 = qf[kR1];
 
     // ---- publish first-row quantities; build block row j ----
-    F(0, j) = t0; F(1, j) = t1;
-    F(2, j) = q00; F(3, j) = q01; F(4, j) = q10; F(5, j) = q11;
-    F(6, j) = fr00; F(7, j) = fr01; F(8, j) = fr10; F(9, j) = fr11;
+    F(0, 0, j) = t0; F(0, 1, j) = t1;
+    F(0, 2, j) = q00; F(0, 3, j) = q01; F(0, 4, j) = q10; F(0, 5, j) = q11;
+    F(0, 6, j) = fr00; F(0, 7, j) = fr01; F(0, 8, j) = fr10; F(0, 9, j) = fr11;
     __syncthreads();
     T ny0 = 0, ny1 = 0, nzl00 = 0, nzl01 = 0, nzl10 = 0, nzl11 = 0, nzr00 = 0, nzr01 = 0, nzr10 = 0, nzr11 = 0;
     if (!last_chunk) {
-        ny0 = F(0, jn); ny1 = F(1, jn);
-        nzl00 = F(2, jn); nzl01 = F(3, jn); nzl10 = F(4, jn); nzl11 = F(5, jn);
-        nzr00 = F(6, jn); nzr01 = F(7, jn); nzr10 = F(8, jn); nzr11 = F(9, jn);
+        ny0 = F(0, 0, jn); ny1 = F(0, 1, jn);
+        nzl00 = F(0, 2, jn); nzl01 = F(0, 3, jn); nzl10 = F(0, 4, jn); nzl11 = F(0, 5, jn);
+        nzr00 = F(0, 6, jn); nzr01 = F(0, 7, jn); nzr10 = F(0, 8, jn); nzr11 = F(0, 9, jn);
     }
     // B_own = [[aR0, bR0], [0, aR1]] on interior rows (m-2, m-1);
     // B_next = [[eR0, 0], [dR1, eR1]] on the next interior rows (0, 1)
@@ -239,49 +251,48 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
         rj0 = fR0 - (aR0 * yl0 + bR0 * yl1) - eR0 * ny0;
         rj1 = fR1 - aR1 * yl1 - (dR1 * ny0 + eR1 * ny1);
     }
-    __syncthreads();
     // ---- block cyclic reduction across the P chunks of the system ----
-    for (int h = 1; h < P; h <<= 1) {
+    // Each lane publishes D_j^{-1} L_j, D_j^{-1} U_j and D_j^{-1} r_j; with
+    // alpha = -L_j D_q^{-1} from the chunk q = j - h and gamma = -U_j D_q^{-1}
+    // from q = j + h the reduced row is
+    //   L' = -L_j (D^{-1}L)_{j-h},  U' = -U_j (D^{-1}U)_{j+h},
+    //   D' = D_j - L_j (D^{-1}U)_{j-h} - U_j (D^{-1}L)_{j+h},
+    //   r' = r_j - L_j (D^{-1}r)_{j-h} - U_j (D^{-1}r)_{j+h}.
+    int bb = 1;                                    // stage buffer (0 held the first rows)
+    for (int h = 1; h < P; h <<= 1, bb ^= 1) {
         T det;
         const M22<T> Di = inv(Dj, det);
         bad |= bad_pivot(det);
-        F(0, j) = Lj.a; F(1, j) = Lj.b; F(2, j) = Lj.c; F(3, j) = Lj.d;
-        F(4, j) = Di.a; F(5, j) = Di.b; F(6, j) = Di.c; F(7, j) = Di.d;
-        F(8, j) = Uj.a; F(9, j) = Uj.b; F(10, j) = Uj.c; F(11, j) = Uj.d;
-        F(12, j) = rj0; F(13, j) = rj1;
+        const M22<T> IL = mul(Di, Lj), IU = mul(Di, Uj);
+        F(bb, 0, j) = IL.a; F(bb, 1, j) = IL.b; F(bb, 2, j) = IL.c; F(bb, 3, j) = IL.d;
+        F(bb, 4, j) = IU.a; F(bb, 5, j) = IU.b; F(bb, 6, j) = IU.c; F(bb, 7, j) = IU.d;
+        F(bb, 8, j) = Di.a * rj0 + Di.b * rj1; F(bb, 9, j) = Di.c * rj0 + Di.d * rj1;
         __syncthreads();
         M22<T> nD = Dj, nL{0, 0, 0, 0}, nU{0, 0, 0, 0};
         T nr0 = rj0, nr1 = rj1;
         if (CYC || j - h >= 0) {
             const int q = (j - h) & (CYC ? P - 1 : -1);
-            const M22<T> Lq{F(0, q), F(1, q), F(2, q), F(3, q)};
-            const M22<T> Iq{F(4, q), F(5, q), F(6, q), F(7, q)};
-            const M22<T> Uq{F(8, q), F(9, q), F(10, q), F(11, q)};
-            const T rq0 = F(12, q), rq1 = F(13, q);
-            const M22<T> al0 = mul(Lj, Iq);
-            const M22<T> al{-al0.a, -al0.b, -al0.c, -al0.d};
-            nL = mul(al, Lq);
-            const M22<T> au = mul(al, Uq);
-            nD = {nD.a + au.a, nD.b + au.b, nD.c + au.c, nD.d + au.d};
-            nr0 += al.a * rq0 + al.b * rq1;
-            nr1 += al.c * rq0 + al.d * rq1;
+            const M22<T> ILq{F(bb, 0, q), F(bb, 1, q), F(bb, 2, q), F(bb, 3, q)};
+            const M22<T> IUq{F(bb, 4, q), F(bb, 5, q), F(bb, 6, q), F(bb, 7, q)};
+            const T iq0 = F(bb, 8, q), iq1 = F(bb, 9, q);
+            const M22<T> l1 = mul(Lj, ILq), l2 = mul(Lj, IUq);
+            nL = {-l1.a, -l1.b, -l1.c, -l1.d};
+            nD = {nD.a - l2.a, nD.b - l2.b, nD.c - l2.c, nD.d - l2.d};
+            nr0 -= Lj.a * iq0 + Lj.b * iq1;
+            nr1 -= Lj.c * iq0 + Lj.d * iq1;
         }
         if (CYC || j + h < P) {
             const int q = (j + h) & (CYC ? P - 1 : -1);
-            const M22<T> Lq{F(0, q), F(1, q), F(2, q), F(3, q)};
-            const M22<T> Iq{F(4, q), F(5, q), F(6, q), F(7, q)};
-            const M22<T> Uq{F(8, q), F(9, q), F(10, q), F(11, q)};
-            const T rq0 = F(12, q), rq1 = F(13, q);
-            const M22<T> ga0 = mul(Uj, Iq);
-            const M22<T> ga{-ga0.a, -ga0.b, -ga0.c, -ga0.d};
-            nU = mul(ga, Uq);
-            const M22<T> gl = mul(ga, Lq);
-            nD = {nD.a + gl.a, nD.b + gl.b, nD.c + gl.c, nD.d + gl.d};
-            nr0 += ga.a * rq0 + ga.b * rq1;
-            nr1 += ga.c * rq0 + ga.d * rq1;
+            const M22<T> ILq{F(bb, 0, q), F(bb, 1, q), F(bb, 2, q), F(bb, 3, q)};
+            const M22<T> IUq{F(bb, 4, q), F(bb, 5, q), F(bb, 6, q), F(bb, 7, q)};
+            const T iq0 = F(bb, 8, q), iq1 = F(bb, 9, q);
+            const M22<T> u1 = mul(Uj, IUq), u2 = mul(Uj, ILq);
+            nU = {-u1.a, -u1.b, -u1.c, -u1.d};
+            nD = {nD.a - u2.a, nD.b - u2.b, nD.c - u2.c, nD.d - u2.d};
+            nr0 -= Uj.a * iq0 + Uj.b * iq1;
+            nr1 -= Uj.c * iq0 + Uj.d * iq1;
         }
         Dj = nD; Lj = nL; Uj = nU; rj0 = nr0; rj1 = nr1;
-        __syncthreads();
     }
     if (CYC) {
         // both remaining couplings refer to this chunk's own interface
@@ -291,11 +302,11 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     const M22<T> Dinv = inv(Dj, det);
     bad |= bad_pivot(det);
     const T xr0 = Dinv.a * rj0 + Dinv.b * rj1, xr1 = Dinv.c * rj0 + Dinv.d * rj1;
-    F(0, j) = xr0; F(1, j) = xr1;
+    F(bb, 0, j) = xr0; F(bb, 1, j) = xr1;
     if (bad) atomicOr(&flag[sl], 1);
     __syncthreads();
-    const T xl0 = first_chunk ? T(0) : F(0, jp);
-    const T xl1 = first_chunk ? T(0) : F(1, jp);
+    const T xl0 = first_chunk ? T(0) : F(bb, 0, jp);
+    const T xl1 = first_chunk ? T(0) : F(bb, 1, jp);
     if (CYC) {
         // a breakdown leaves the system to the periodic factor + solve pass
         if (j == 0 && act) mask[s] = flag[sl];
@@ -341,12 +352,27 @@ int spike_rows(int64_t n, bool cyclic)
 }
 
 template <typename T, int M, int S>
-static void launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
+static hipError_t launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
                          const void *b, const void *c, const void *d, const void *e, void *x,
                          void *work, int32_t *info, int32_t *mask, hipStream_t st)
 {
-    const size_t lds = size_t(14) * P * S * sizeof(T) + S * sizeof(int32_t);
+    const size_t lds = size_t(2 * kSpikeFields) * P * S * sizeof(T) + S * sizeof(int32_t);
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
+    // past 64 KiB of dynamic LDS the kernel must be allowed more, once per
+    // instantiation, for the largest workgroup (512 lanes)
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        const int most = int(2 * kSpikeFields * 512 * sizeof(T) + S * sizeof(int32_t));
+        if (most > 65536) {
+            attr = hipFuncSetAttribute((const void *)k_penta_spike<T, M, S, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
+            if (attr == hipSuccess)
+                attr = hipFuncSetAttribute((const void *)k_penta_spike<T, M, S, false>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        }
+    });
+    if (attr != hipSuccess) return attr;
     if (cyclic)
         hipLaunchKernelGGL((k_penta_spike<T, M, S, true>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
@@ -355,10 +381,11 @@ static void launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const vo
         hipLaunchKernelGGL((k_penta_spike<T, M, S, false>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
                            (T *)x, (T *)work, info, mask);
+    return hipSuccess;
 }
 
 template <typename T, int M>
-static void launch_spike_m(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
+static hipError_t launch_spike_m(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
                            const void *b, const void *c, const void *d, const void *e, void *x,
                            void *work, int32_t *info, int32_t *mask, hipStream_t st)
 {
@@ -366,9 +393,9 @@ static void launch_spike_m(int P, int64_t batch, int64_t ld, bool cyclic, const 
     // fp32); 32 when the systems are short so that a workgroup fills a
     // wavefront, 8 when they are long so that it stays within 512 lanes and
     // 64 KiB of LDS
-    if (P < 4) launch_spike<T, M, 32>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
-    else if (P <= 32) launch_spike<T, M, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
-    else launch_spike<T, M, 8>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    if (P < 4) return launch_spike<T, M, 32>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    if (P <= 32) return launch_spike<T, M, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    return launch_spike<T, M, 8>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
 }
 
 template <typename T>
@@ -383,8 +410,11 @@ bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, bool cyclic,
     if (cyclic && !mask) BPS_FAIL(BPS_EINVAL, "periodic chunked solve needs a mask array");
     if (batch == 0) return BPS_OK;
     const int P = int(n / M);
-    if (M == 16) launch_spike_m<T, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
-    else launch_spike_m<T, 12>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    const hipError_t err = M == 16
+        ? launch_spike_m<T, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st)
+        : launch_spike_m<T, 12>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    if (err != hipSuccess)
+        BPS_FAIL(BPS_EHIP, "hipFuncSetAttribute failed: %s", hipGetErrorString(err));
     BPS_LAUNCHED("k_penta_spike");
     return BPS_OK;
 }
