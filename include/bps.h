@@ -9,7 +9,10 @@
  * hines_plan_destroy, which allocate / free device memory and synchronise.
  * No solve allocates memory.  Solve, pack and unpack calls enqueue kernels
  * only (no allocation, copy, memset or synchronisation), so a sequence of
- * them can be captured into a HIP graph and replayed.
+ * them can be captured into a HIP graph and replayed.  The first chunked
+ * pentadiagonal solve of a precision (penta_factor_solve_batch) also raises
+ * its kernels' dynamic-LDS limit once (hipFuncSetAttribute, a host-side
+ * setting): make that first call outside a capture.
  *
  * Sources (web-page titles; sections named as on the pages):
  *   [P] "cuPentBatch - A batched pentadiagonal solver for NVIDIA GPUs":
