@@ -1,8 +1,10 @@
 // api.cpp -- the extern "C" entry points of libbps: argument validation on
 // the host, then kernel launches on the caller's stream.
 #include <cmath>
-#include <utility>
 #include <cstring>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -20,6 +22,20 @@ void set_error(const char *fmt, ...)
 }
 
 void clear_error() { g_err[0] = '\0'; }
+
+hipError_t allow_lds(const void *kernel, int bytes)
+{
+    static std::mutex mu;
+    static std::set<std::pair<const void *, int>> done;    // (kernel, device)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({kernel, dev})) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.insert({kernel, dev});
+    return e;
+}
 
 // from hines.hip
 bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,

@@ -38,6 +38,11 @@ void clear_error();
             BPS_FAIL(BPS_EHIP, "launch of %s failed: %s", name, hipGetErrorString(e_)); \
     } while (0)
 
+// Allow `kernel` up to `bytes` of dynamic LDS on the current device (past
+// the 64 KiB default): done once per kernel and device, since the setting
+// belongs to the device it is made on.  Host-side only (no stream work).
+hipError_t allow_lds(const void *kernel, int bytes);
+
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline bool aligned(const void *p, size_t a) {

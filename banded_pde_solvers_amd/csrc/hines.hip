@@ -23,7 +23,6 @@
 // parent distance use the general variant, which sends those updates through
 // per-lane accumulators in global memory (zeroed before each solve).
 #include <algorithm>
-#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -736,16 +735,11 @@ static bps_status build_levels(bps_hines_plan *P, int64_t ntrees, const int32_t 
         P->lv_maxn = std::max(P->lv_maxn, n);
         off += n;
     }
-    // the kernel's dynamic LDS may exceed the default limit: raise it once,
-    // to the largest any plan uses, here at plan time (not in the solve,
-    // which may be captured into a graph)
-    static std::once_flag lds_once;
-    static hipError_t lds_err = hipSuccess;
-    std::call_once(lds_once, [] {
-        lds_err = hipFuncSetAttribute((const void *)k_hines_levels,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      int(4 * kLevelMaxN * sizeof(double)));
-    });
+    // the kernel's dynamic LDS may exceed the default limit: raise it on this
+    // device, to the largest any plan uses, here at plan time (not in the
+    // solve, which may be captured into a graph)
+    const hipError_t lds_err = allow_lds((const void *)k_hines_levels,
+                                         int(4 * kLevelMaxN * sizeof(double)));
     if (lds_err != hipSuccess)
         BPS_FAIL(BPS_EHIP, "hipFuncSetAttribute failed: %s", hipGetErrorString(lds_err));
     bps_status st;

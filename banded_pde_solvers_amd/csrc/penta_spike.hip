@@ -39,8 +39,6 @@
 // tridiagonal and periodic; block cyclic reduction with indices modulo P
 // (P a power of two) leaves after log2 P steps each unknown coupled only to
 // itself through L_j, D_j and U_j, so xI_j = (L_j + D_j + U_j)^{-1} r_j.
-#include <mutex>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -358,21 +356,13 @@ static hipError_t launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, co
 {
     const size_t lds = size_t(2 * kSpikeFields) * P * S * sizeof(T) + S * sizeof(int32_t);
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
-    // past 64 KiB of dynamic LDS the kernel must be allowed more, once per
-    // instantiation, for the largest workgroup (512 lanes)
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    std::call_once(once, [] {
-        const int most = int(2 * kSpikeFields * 512 * sizeof(T) + S * sizeof(int32_t));
-        if (most > 65536) {
-            attr = hipFuncSetAttribute((const void *)k_penta_spike<T, M, S, true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
-            if (attr == hipSuccess)
-                attr = hipFuncSetAttribute((const void *)k_penta_spike<T, M, S, false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, most);
-        }
-    });
-    if (attr != hipSuccess) return attr;
+    // past 64 KiB of dynamic LDS the kernel must be allowed more
+    if (lds > 65536) {
+        const hipError_t e = cyclic
+            ? allow_lds((const void *)k_penta_spike<T, M, S, true>, int(lds))
+            : allow_lds((const void *)k_penta_spike<T, M, S, false>, int(lds));
+        if (e != hipSuccess) return e;
+    }
     if (cyclic)
         hipLaunchKernelGGL((k_penta_spike<T, M, S, true>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,

@@ -10,9 +10,9 @@
  * No solve allocates memory.  Solve, pack and unpack calls enqueue kernels
  * only (no allocation, copy, memset or synchronisation), so a sequence of
  * them can be captured into a HIP graph and replayed.  The first chunked
- * pentadiagonal solve of a precision (penta_factor_solve_batch) also raises
- * its kernels' dynamic-LDS limit once (hipFuncSetAttribute, a host-side
- * setting): make that first call outside a capture.
+ * pentadiagonal solve of a precision on a device (penta_factor_solve_batch)
+ * also raises its kernels' dynamic-LDS limit there (hipFuncSetAttribute, a
+ * host-side setting): make that first call outside a capture.
  *
  * Sources (web-page titles; sections named as on the pages):
  *   [P] "cuPentBatch - A batched pentadiagonal solver for NVIDIA GPUs":
