@@ -381,8 +381,7 @@ static hipError_t launch_spike_m(int P, int64_t batch, int64_t ld, bool cyclic, 
 {
     // 16 systems per workgroup (a 128-byte row segment in fp64, 64 in
     // fp32); 32 when the systems are short so that a workgroup fills a
-    // wavefront, 8 when they are long so that it stays within 512 lanes and
-    // 64 KiB of LDS
+    // wavefront, 8 when they are long so that it stays within 512 lanes
     if (P < 4) return launch_spike<T, M, 32>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
     if (P <= 32) return launch_spike<T, M, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
     return launch_spike<T, M, 8>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
