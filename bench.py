@@ -153,10 +153,13 @@ def pmc_summary(args):
     print(json.dumps({args.pmc_key: ent}), flush=True)
 
 
+_CPU_THREADS = 0      # oracle threads for the CPU baseline (0: OpenMP's default)
+
+
 def _cpu_baseline(run_sample, unknowns_per_system, label, seconds):
     """Time the oracle on a growing sample until it takes ~`seconds`."""
     import oracle
-    cores = oracle.set_threads(0)
+    cores = oracle.set_threads(_CPU_THREADS)
     k = 8
     t = 0.0
     while True:
@@ -597,6 +600,8 @@ def main():
                     help="workloads 2, 9: time the separate factor and solve calls instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads for cpu_baseline (default: OpenMP's, i.e. all cores)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYFETCH", "COPYWRITE"),
@@ -608,6 +613,8 @@ def main():
     ap.add_argument("--pmc-calls-match", default=None,
                     help="sum the --pmc-match dispatches per call of this kernel")
     args = ap.parse_args()
+    global _CPU_THREADS
+    _CPU_THREADS = max(0, args.cpu_threads)
     if args.pmc_summary:
         pmc_summary(args)
         return
