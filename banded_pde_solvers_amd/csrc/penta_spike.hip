@@ -106,11 +106,41 @@ __device__ int32_t seq_penta_solve(int64_t n, int64_t ld, const T *A, const T *B
 // and none is needed after the reads) + S flags.
 constexpr int kSpikeFields = 10;
 
+// Two consecutive values of the interleaved layout (two neighbouring
+// systems of one row) as one vector access.
+template <typename T> struct Pair2;
+template <> struct Pair2<double> { using type = double2; };
+template <> struct Pair2<float> { using type = float2; };
+
+// Value of the other lane of this lane's pair (lanes 2k and 2k+1; DPP quad
+// permutation 1, 0, 3, 2: a VALU move, no LDS).
+__device__ __forceinline__ int pair_swap(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float pair_swap(float v)
+{
+    return __int_as_float(pair_swap(__float_as_int(v)));
+}
+__device__ __forceinline__ double pair_swap(double v)
+{
+    const long long b = __double_as_longlong(v);
+    const int lo = pair_swap(int(b & 0xffffffffll)), hi = pair_swap(int(b >> 32));
+    return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+
 // fp32: registers capped for four waves per SIMD (two 512-lane workgroups
 // per CU, so that one workgroup's loads overlap the other's reduction), at
 // the cost of a few spilled values; fp64 needs about twice the registers
 // and runs two waves per SIMD.
-template <typename T, int M, int S, bool CYC>
+//
+// PAIR (ld even, arrays aligned to two values): the two lanes of a pair
+// (neighbouring systems, same chunk) read rows r and r + 1 of both their
+// systems with one vector access each and swap one value, so a row pair of
+// an input costs one wavefront access of 2 x 8 (fp64) bytes per lane
+// instead of two of 8: half the accesses through the address units, which
+// the 8-byte-per-lane pattern keeps busy.
+template <typename T, int M, int S, bool CYC, bool PAIR>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 4 : 2)))
 k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T *__restrict__ B,
               const T *__restrict__ C, const T *__restrict__ D, const T *__restrict__ E,
@@ -134,9 +164,24 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     const bool act = s < batch;
     // lanes past the end of the batch shadow the last system (identical
     // values, identical stores, no branches around memory operations)
-    const int64_t off = (act ? s : batch - 1) + int64_t(j) * M * ld;
+    const int64_t se = act ? s : batch - 1;
+    const int64_t off = se + int64_t(j) * M * ld;
     const T *pa = A + off, *pb = B + off, *pc = C + off, *pd = D + off, *pe = E + off;
     T *px = x + off;
+    // pair access: this lane reads row r + (sl & 1) of the column pair that
+    // holds its system and keeps the value of its own column (cp) of both
+    // rows; a shadow lane keeps the column of the system it shadows
+    using T2 = typename Pair2<T>::type;
+    const int par = sl & 1, cp = int(se & 1);
+    const int cpp = PAIR ? pair_swap(cp) : 0;            // the other lane's column
+    const int64_t off2 = (se & ~int64_t(1)) + (int64_t(j) * M + par) * ld;
+    auto pair_row = [&](const T *base, int r0, T &v0, T &v1) {
+        const T2 v = *reinterpret_cast<const T2 *>(base + off2 + int64_t(r0) * ld);
+        const T recv = pair_swap(cpp ? v.y : v.x);
+        const T mine = cp ? v.y : v.x;
+        v0 = par ? recv : mine;                          // row r0
+        v1 = par ? mine : recv;                          // row r0 + 1
+    };
     auto F = [&](int bb, int field, int jj) -> T & {
         return buf[((bb * kSpikeFields + field) * P + jj) * S + sl];
     };
@@ -144,10 +189,22 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     // ---- forward sweep over the interior, inputs streamed LA rows ahead ----
     constexpr int LA = 4;
     T qa[LA], qb[LA], qc[LA], qd[LA], qe[LA], qf[LA];
+    // rows r0, r0 + 1 (r0 even) into their ring slots
+    auto load_pair = [&](int r0) {
+        const int k0 = r0 % LA, k1 = (r0 + 1) % LA;
+        pair_row(A, r0, qa[k0], qa[k1]); pair_row(B, r0, qb[k0], qb[k1]);
+        pair_row(C, r0, qc[k0], qc[k1]); pair_row(D, r0, qd[k0], qd[k1]);
+        pair_row(E, r0, qe[k0], qe[k1]); pair_row(x, r0, qf[k0], qf[k1]);
+    };
+    if constexpr (PAIR) {
+        load_pair(0);
+        load_pair(2);
+    } else {
 #pragma unroll
-    for (int k = 0; k < LA; ++k) {
-        const int64_t o = int64_t(k) * ld;
-        qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qd[k] = pd[o]; qe[k] = pe[o]; qf[k] = px[o];
+        for (int k = 0; k < LA; ++k) {
+            const int64_t o = int64_t(k) * ld;
+            qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qd[k] = pd[o]; qe[k] = pe[o]; qf[k] = px[o];
+        }
     }
     T gam[m], del[m], g[m], u0[m], u1[m];
     T gam1 = 0, gam2 = 0, del1 = 0, del2 = 0;      // factors of the two previous rows
@@ -163,7 +220,10 @@ k_penta_spike(int P, int64_t batch, int64_t ld, const T *__restrict__ A, const T
     for (int i = 0; i < m; ++i) {
         const int k = i % LA;
         const T a_i = qa[k], b_i = qb[k], c_i = qc[k], d_i = qd[k], e_i = qe[k], f_i = qf[k];
-        {
+        if constexpr (PAIR) {
+            // both rows of the slot pair consumed: fetch the pair LA rows on
+            if ((i & 1) && i - 1 + LA < M) load_pair(i - 1 + LA);
+        } else {
             const int64_t o = int64_t(i + LA < M ? i + LA : M - 1) * ld;
             qa[k] = pa[o]; qb[k] = pb[o]; qc[k] = pc[o]; qd[k] = pd[o]; qe[k] = pe[o]; qf[k] = px[o];
         }
@@ -349,7 +409,7 @@ int spike_rows(int64_t n, bool cyclic)
     return 0;
 }
 
-template <typename T, int M, int S>
+template <typename T, int M, int S, bool PAIR>
 static hipError_t launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
                          const void *b, const void *c, const void *d, const void *e, void *x,
                          void *work, int32_t *info, int32_t *mask, hipStream_t st)
@@ -359,16 +419,16 @@ static hipError_t launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, co
     // past 64 KiB of dynamic LDS the kernel must be allowed more
     if (lds > 65536) {
         const hipError_t e = cyclic
-            ? allow_lds((const void *)k_penta_spike<T, M, S, true>, int(lds))
-            : allow_lds((const void *)k_penta_spike<T, M, S, false>, int(lds));
+            ? allow_lds((const void *)k_penta_spike<T, M, S, true, PAIR>, int(lds))
+            : allow_lds((const void *)k_penta_spike<T, M, S, false, PAIR>, int(lds));
         if (e != hipSuccess) return e;
     }
     if (cyclic)
-        hipLaunchKernelGGL((k_penta_spike<T, M, S, true>), grid, block, lds, st, P, batch, ld,
+        hipLaunchKernelGGL((k_penta_spike<T, M, S, true, PAIR>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
                            (T *)x, (T *)work, info, mask);
     else
-        hipLaunchKernelGGL((k_penta_spike<T, M, S, false>), grid, block, lds, st, P, batch, ld,
+        hipLaunchKernelGGL((k_penta_spike<T, M, S, false, PAIR>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
                            (T *)x, (T *)work, info, mask);
     return hipSuccess;
@@ -381,10 +441,20 @@ static hipError_t launch_spike_m(int P, int64_t batch, int64_t ld, bool cyclic, 
 {
     // 16 systems per workgroup (a 128-byte row segment in fp64, 64 in
     // fp32); 32 when the systems are short so that a workgroup fills a
-    // wavefront, 8 when they are long so that it stays within 512 lanes
-    if (P < 4) return launch_spike<T, M, 32>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
-    if (P <= 32) return launch_spike<T, M, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
-    return launch_spike<T, M, 8>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
+    // wavefront, 8 when they are long so that it stays within 512 lanes.
+    // Pair accesses need ld even and every input aligned to two values.
+    const size_t al = 2 * sizeof(T);
+    const bool pair = ld % 2 == 0 && aligned(a, al) && aligned(b, al) && aligned(c, al) &&
+                      aligned(d, al) && aligned(e, al) && aligned(x, al);
+#define BPS_SPIKE_S(SS)                                                                            \
+    return pair ? launch_spike<T, M, SS, true>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info,  \
+                                               mask, st)                                           \
+                : launch_spike<T, M, SS, false>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, \
+                                                mask, st)
+    if (P < 4) BPS_SPIKE_S(32);
+    if (P <= 32) BPS_SPIKE_S(16);
+    BPS_SPIKE_S(8);
+#undef BPS_SPIKE_S
 }
 
 template <typename T>

@@ -110,6 +110,29 @@ def test_leading_dimension_larger_than_batch(n):
     np.testing.assert_array_equal(out[:, batch:], pb.f[:, batch:])   # untouched columns
 
 
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("cyclic", [False, True])
+@pytest.mark.parametrize("n,batch,ld", [(128, 37, 38), (96, 37, 38), (128, 65, 66), (128, 37, 37),
+                                        (96, 64, 65)])
+def test_chunked_paired_and_single_accesses(dt, cyclic, n, batch, ld):
+    """Chunked kernel: with ld even, the two lanes of a pair read neighbouring
+    systems together, and the last pair of an odd batch reads (never writes)
+    the padding column; with ld odd each lane reads its own values."""
+    print(f"chunked accesses n={n} batch={batch} ld={ld} cyclic={cyclic} {dt}", flush=True)
+    pb = W.penta_dominant(n, ld, cyclic=cyclic, rng=np.random.default_rng(n + batch + ld))
+    a, b, c, d, e = (dev(v, dt) for v in pb.diagonals)
+    x = dev(pb.f, dt)
+    before = host(x)
+    work = buf(bps.bps_penta_work_bytes(n, batch, ld, _code(dt), cyclic=cyclic))
+    info = info_buf(batch)
+    bps.penta_factor_solve_batch(a, b, c, d, e, x, work, info, batch=batch, cyclic=cyclic)
+    ref, rinfo = _oracle(pb, dt, cols=slice(0, batch), cyclic=cyclic)
+    out = host(x)
+    assert relerr_cols(out[:, :batch], ref) <= TOL[dt]
+    np.testing.assert_array_equal(out[:, batch:], before[:, batch:])   # padding untouched
+    np.testing.assert_array_equal(host(info).astype(int), rinfo)
+
+
 @pytest.mark.parametrize("n", [16, 32])
 def test_outside_entries_are_ignored(n):
     """a_0, a_1, b_0, d_{n-1}, e_{n-2}, e_{n-1} lie outside the matrix."""
