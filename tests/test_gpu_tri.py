@@ -49,6 +49,21 @@ def test_parity_fp64(n, batch):
     assert relerr_cols(got, ref) <= TOL[torch.float64]
 
 
+@pytest.mark.parametrize("dt", [torch.float64, torch.float32])
+@pytest.mark.parametrize("n,batch,ld", [(128, 37, 38), (96, 37, 38), (512, 65, 66), (128, 37, 37),
+                                        (96, 64, 65)])
+def test_chunked_leading_dimension_and_padding(dt, n, batch, ld):
+    """Chunked kernel with ld > batch (even or odd) and odd or even batches:
+    the solution of the batch's systems, padding columns left untouched."""
+    print(f"tri chunked n={n} batch={batch} ld={ld} {dt}", flush=True)
+    tb = W.tri_dominant(n, ld, rng=np.random.default_rng(n + batch + ld))
+    got, info, _ = _solve(tb, dt, batch=batch)
+    ref, rinfo = _oracle(tb, dt, cols=slice(0, batch))
+    assert np.all(info == 0) and np.all(rinfo == 0)
+    assert relerr_cols(got[:, :batch], ref) <= TOL[dt]
+    np.testing.assert_array_equal(got[:, batch:], rounded(tb.y[:, batch:], dt))   # padding untouched
+
+
 @pytest.mark.parametrize("n,batch", [(64, 100), (512, 40), (1024, 16), (180, 25), (100, 30),
                                      (2048, 20)])
 def test_parity_fp32(n, batch):
