@@ -32,7 +32,7 @@ __all__ = [
     "HinesPlan", "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
     "hines_work_bytes", "hines_solve_batch", "BPS_HINES_AUTO", "BPS_HINES_LANES",
     "BPS_HINES_LEVELS", "hines_plan_create_sched", "hines_plan_elems", "hines_plan_unknowns",
-    "hines_plan_uses_levels", "bps_version", "bps_status_str", "bps_last_error", "PentaDesc",
+    "hines_plan_uses_levels", "bps_version", "bps_init", "bps_status_str", "bps_last_error", "PentaDesc",
 ]
 
 BPS_F32 = 1
@@ -86,6 +86,7 @@ def load_library():
             "bps_status_str": ([st], ctypes.c_char_p),
             "bps_last_error": ([], ctypes.c_char_p),
             "bps_version": ([], ctypes.c_int),
+            "bps_init": ([], st),
             "bps_penta_factor_bytes": ([dp], ctypes.c_size_t),
             "penta_factor_batch": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], st),
             "penta_solve_batch": ([dp, vp, vp, vp], st),
@@ -129,6 +130,11 @@ def version() -> int:
 
 def bps_version() -> int:
     return version()
+
+
+def bps_init():
+    """Prepare the current device (kernel attributes; optional, see bps.h)."""
+    _check("bps_init", load_library().bps_init())
 
 
 def bps_status_str(status: int) -> str:
@@ -422,13 +428,24 @@ def hines_plan_destroy(plan: HinesPlan):
     plan.close()
 
 
+def _hines_sizes(plan, flat, packed):
+    if flat.numel() < plan.unknowns:
+        raise ValueError(f"flat array too small ({plan.unknowns} values needed)")
+    if packed.numel() < plan.elems:
+        raise ValueError(f"packed array too small ({plan.elems} values needed)")
+    if flat.dtype != packed.dtype:
+        raise ValueError("flat and packed arrays must have the same dtype")
+
+
 def hines_pack(plan: HinesPlan, flat, packed, stream=None):
+    _hines_sizes(plan, flat, packed)
     _check("hines_pack", load_library().hines_pack(plan.handle, _dtype_code(flat), _ptr(flat),
                                                    _ptr(packed), _stream(stream)))
     return packed
 
 
 def hines_unpack(plan: HinesPlan, packed, flat, stream=None):
+    _hines_sizes(plan, flat, packed)
     _check("hines_unpack", load_library().hines_unpack(plan.handle, _dtype_code(packed),
                                                        _ptr(packed), _ptr(flat), _stream(stream)))
     return flat

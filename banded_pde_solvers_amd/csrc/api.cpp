@@ -23,18 +23,18 @@ void set_error(const char *fmt, ...)
 
 void clear_error() { g_err[0] = '\0'; }
 
-hipError_t allow_lds(const void *kernel, int bytes)
+bps_status prepare_device()
 {
     static std::mutex mu;
-    static std::set<std::pair<const void *, int>> done;    // (kernel, device)
+    static std::set<int> done;
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
+    BPS_HIP(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lock(mu);
-    if (done.count({kernel, dev})) return hipSuccess;
-    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess) done.insert({kernel, dev});
-    return e;
+    if (done.count(dev)) return BPS_OK;
+    BPS_HIP(spike_prepare_device());
+    BPS_HIP(hines_prepare_device());
+    done.insert(dev);
+    return BPS_OK;
 }
 
 // from hines.hip
@@ -108,7 +108,13 @@ const char *bps_status_str(int status)
 
 const char *bps_last_error(void) { return g_err; }
 
-int bps_version(void) { return 100; }
+int bps_version(void) { return 101; }
+
+bps_status bps_init(void)
+{
+    clear_error();
+    return prepare_device();
+}
 
 size_t bps_penta_factor_bytes(const bps_penta_desc *dsc)
 {
@@ -187,6 +193,7 @@ bps_status penta_factor_solve_batch(const bps_penta_desc *dsc, const void *a, co
     CHECK(check_ptr(e, "e", dsc->dtype)); CHECK(check_ptr(x, "x", dsc->dtype));
     CHECK(check_ptr(work, "work", dsc->dtype));
     if (info && !aligned(info, 4)) BPS_FAIL(BPS_EINVAL, "info is not 4-byte aligned");
+    CHECK(prepare_device());
     hipStream_t st = as_stream(stream);
     const int64_t n = dsc->n, batch = dsc->batch, ld = dsc->ld;
     if (dsc->flags & BPS_CYCLIC) {
@@ -466,6 +473,7 @@ bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch, const i
     }
     if (schedule != BPS_HINES_AUTO && schedule != BPS_HINES_LANES && schedule != BPS_HINES_LEVELS)
         BPS_FAIL(BPS_EINVAL, "unknown schedule %d", schedule);
+    CHECK(prepare_device());
     return hines_plan_build(plan, batch, sizes, parent, mono, ld, schedule);
 }
 

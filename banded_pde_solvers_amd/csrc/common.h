@@ -38,10 +38,13 @@ void clear_error();
             BPS_FAIL(BPS_EHIP, "launch of %s failed: %s", name, hipGetErrorString(e_)); \
     } while (0)
 
-// Allow `kernel` up to `bytes` of dynamic LDS on the current device (past
-// the 64 KiB default): done once per kernel and device, since the setting
-// belongs to the device it is made on.  Host-side only (no stream work).
-hipError_t allow_lds(const void *kernel, int bytes);
+// Kernel attributes of the current device, set once per device by the first
+// call that needs them: every kernel whose launches may use more than the
+// default 64 KiB of dynamic LDS is allowed its largest launch.  Host-side
+// only (no stream work, no allocation), so it may run inside a graph capture.
+bps_status prepare_device();
+hipError_t spike_prepare_device();     // penta_spike.hip
+hipError_t hines_prepare_device();     // hines.hip
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 

@@ -658,15 +658,18 @@ __global__ void k_fill_zero(double *p, int64_t count)
 
 // ---- layout transforms ---------------------------------------------------------
 
-// mono: flat [batch][n]  <->  interleaved [n][ld]
+// mono: flat [batch][n]  <->  interleaved [n][ld].  Packing walks every
+// element of the interleaved array, padding columns (s >= batch) included,
+// and writes those as 0; unpacking reads the batch real columns only.
 template <typename T, bool PACK>
 __global__ void k_mono_transpose(int64_t n, int64_t batch, int64_t ld, const T *__restrict__ src,
                                  T *__restrict__ dst)
 {
-    const int64_t total = n * batch;
+    const int64_t cols = PACK ? ld : batch;
+    const int64_t total = n * cols;
     for (int64_t e = lane_id(); e < total; e += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t i = e / batch, s = e % batch;   // interleaved order: coalesced side
-        if (PACK) dst[i * ld + s] = src[s * n + i];
+        const int64_t i = e / cols, s = e % cols;     // interleaved order: coalesced side
+        if (PACK) dst[i * ld + s] = s < batch ? src[s * n + i] : T(0);
         else dst[s * n + i] = src[i * ld + s];
     }
 }
@@ -735,13 +738,6 @@ static bps_status build_levels(bps_hines_plan *P, int64_t ntrees, const int32_t 
         P->lv_maxn = std::max(P->lv_maxn, n);
         off += n;
     }
-    // the kernel's dynamic LDS may exceed the default limit: raise it on this
-    // device, to the largest any plan uses, here at plan time (not in the
-    // solve, which may be captured into a graph)
-    const hipError_t lds_err = allow_lds((const void *)k_hines_levels,
-                                         int(4 * kLevelMaxN * sizeof(double)));
-    if (lds_err != hipSuccess)
-        BPS_FAIL(BPS_EHIP, "hipFuncSetAttribute failed: %s", hipGetErrorString(lds_err));
     bps_status st;
     if ((st = upload(&P->lv_perm, perm)) != BPS_OK) return st;
     if ((st = upload(&P->lv_sec, sec)) != BPS_OK) return st;
@@ -847,6 +843,16 @@ bps_status hines_plan_free(bps_hines_plan *p)
     return BPS_OK;
 }
 
+// The level schedule's dynamic LDS (four values per compartment of the
+// largest tree) may exceed the default 64 KiB: allowed its largest amount on
+// the current device.
+hipError_t hines_prepare_device()
+{
+    return hipFuncSetAttribute((const void *)k_hines_levels,
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               int(4 * kLevelMaxN * sizeof(double)));
+}
+
 bool hines_plan_general(const bps_hines_plan *p) { return p->max_dist > kRing; }
 bool hines_plan_levels(const bps_hines_plan *p) { return p->use_levels; }
 int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }
@@ -858,7 +864,7 @@ bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, 
                            hipStream_t st)
 {
     if (P->mono) {
-        const int64_t total = P->n * P->batch;
+        const int64_t total = P->n * (pack ? P->ld : P->batch);
         const unsigned grid = unsigned(std::min<int64_t>((total + 255) / 256, 65536));
         if (pack)
             hipLaunchKernelGGL((k_mono_transpose<T, true>), dim3(grid), dim3(256), 0, st, P->n,

@@ -409,20 +409,64 @@ int spike_rows(int64_t n, bool cyclic)
     return 0;
 }
 
+// Dynamic LDS of one launch: the two exchange buffers of kSpikeFields * P * S
+// values each, and S int32 flags.
+template <typename T, int S>
+constexpr size_t spike_lds(int P)
+{
+    return size_t(2 * kSpikeFields) * P * S * sizeof(T) + S * sizeof(int32_t);
+}
+// Largest chunk count launched with S systems per workgroup (launch_spike_m).
+constexpr int spike_pmax(int S) { return S == 32 ? 3 : S == 16 ? 32 : 64; }
+
+template <typename T, int M, int S, bool CYC, bool PAIR>
+static hipError_t spike_raise()
+{
+    constexpr size_t lds = spike_lds<T, S>(spike_pmax(S));
+    if (lds <= 65536) return hipSuccess;
+    return hipFuncSetAttribute((const void *)k_penta_spike<T, M, S, CYC, PAIR>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+}
+
+template <typename T, int M, int S>
+static hipError_t spike_raise_s()
+{
+    hipError_t e;
+    if ((e = spike_raise<T, M, S, false, false>()) != hipSuccess) return e;
+    if ((e = spike_raise<T, M, S, false, true>()) != hipSuccess) return e;
+    if ((e = spike_raise<T, M, S, true, false>()) != hipSuccess) return e;
+    return spike_raise<T, M, S, true, true>();
+}
+
+template <typename T, int M>
+static hipError_t spike_raise_m()
+{
+    hipError_t e;
+    if ((e = spike_raise_s<T, M, 32>()) != hipSuccess) return e;
+    if ((e = spike_raise_s<T, M, 16>()) != hipSuccess) return e;
+    return spike_raise_s<T, M, 8>();
+}
+
+// Every instantiation whose largest launch needs more than the default 64 KiB
+// of dynamic LDS is allowed that largest amount on the current device.
+hipError_t spike_prepare_device()
+{
+    hipError_t e;
+    if ((e = spike_raise_m<double, 16>()) != hipSuccess) return e;
+    if ((e = spike_raise_m<double, 12>()) != hipSuccess) return e;
+    if ((e = spike_raise_m<float, 16>()) != hipSuccess) return e;
+    return spike_raise_m<float, 12>();
+}
+
 template <typename T, int M, int S, bool PAIR>
 static hipError_t launch_spike(int P, int64_t batch, int64_t ld, bool cyclic, const void *a,
                          const void *b, const void *c, const void *d, const void *e, void *x,
                          void *work, int32_t *info, int32_t *mask, hipStream_t st)
 {
-    const size_t lds = size_t(2 * kSpikeFields) * P * S * sizeof(T) + S * sizeof(int32_t);
+    // within the limit spike_prepare_device set for this instantiation
+    const size_t lds = spike_lds<T, S>(P);
+    if (P > spike_pmax(S)) return hipErrorInvalidConfiguration;
     const dim3 grid(unsigned((batch + S - 1) / S)), block(unsigned(P * S));
-    // past 64 KiB of dynamic LDS the kernel must be allowed more
-    if (lds > 65536) {
-        const hipError_t e = cyclic
-            ? allow_lds((const void *)k_penta_spike<T, M, S, true, PAIR>, int(lds))
-            : allow_lds((const void *)k_penta_spike<T, M, S, false, PAIR>, int(lds));
-        if (e != hipSuccess) return e;
-    }
     if (cyclic)
         hipLaunchKernelGGL((k_penta_spike<T, M, S, true, PAIR>), grid, block, lds, st, P, batch, ld,
                            (const T *)a, (const T *)b, (const T *)c, (const T *)d, (const T *)e,
@@ -473,7 +517,7 @@ bps_status launch_penta_spike(int64_t n, int64_t batch, int64_t ld, bool cyclic,
         ? launch_spike_m<T, 16>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st)
         : launch_spike_m<T, 12>(P, batch, ld, cyclic, a, b, c, d, e, x, work, info, mask, st);
     if (err != hipSuccess)
-        BPS_FAIL(BPS_EHIP, "hipFuncSetAttribute failed: %s", hipGetErrorString(err));
+        BPS_FAIL(BPS_EHIP, "k_penta_spike: %s", hipGetErrorString(err));
     BPS_LAUNCHED("k_penta_spike");
     return BPS_OK;
 }

@@ -298,8 +298,7 @@ def bench_penta(args, which=2):
     dt = torch.float32 if args.dtype == "f32" else torch.float64
     pb = W.penta_dominant(n, batch, cyclic=cyclic, rng=W.rng_for(which))
     dg = [torch.as_tensor(v, device="cuda:0").to(dt) for v in pb.diagonals]
-    f0 = torch.as_tensor(pb.f, device="cuda:0").to(dt)
-    x = f0.clone()
+    x = torch.as_tensor(pb.f, device="cuda:0").to(dt)
     code = bps.BPS_F32 if dt == torch.float32 else bps.BPS_F64
     work = torch.empty(bps.bps_penta_work_bytes(n, batch, batch, code, cyclic=cyclic),
                        dtype=torch.uint8, device="cuda:0")
@@ -346,14 +345,6 @@ def bench_penta(args, which=2):
                      "kernel_ms": kern_ms,
                      "bytes_per_launch": alg_bytes},
     }
-    if args.compare_rocsparse and not cyclic:
-        # our solution of the original right-hand side, then the library's
-        xo = f0.clone()
-        bps.penta_factor_solve_batch(*dg, xo, work)
-        cmp_ = _rocsparse_compare("penta", dt, dg, f0, xo, args.steps)
-        cmp_["ours_ms"] = kern_ms
-        cmp_["speedup_of_ours"] = cmp_["ms"] / kern_ms
-        line["comparison"] = cmp_
     if not args.no_cpu_baseline:
         import oracle
         small = W.penta_dominant(n, 4096, cyclic=cyclic, rng=np.random.default_rng(5))
@@ -380,7 +371,6 @@ def bench_tri(args, which):
     dt = torch.float32 if args.dtype == "f32" else torch.float64
     tb = W.tri_dominant(n, batch)
     a, b, c, y = (torch.as_tensor(v, device="cuda:0").to(dt) for v in (tb.a, tb.b, tb.c, tb.y))
-    y0 = y.clone()
     del tb
     code = bps.BPS_F32 if dt == torch.float32 else bps.BPS_F64
     work = torch.empty(bps.tri_work_bytes(n, batch, code), dtype=torch.uint8, device="cuda:0")
@@ -410,13 +400,6 @@ def bench_tri(args, which):
                      "traffic": _traffic(f"{kname[2:]}_n{n}_{args.dtype}"), "kernel_ms": kern_ms,
                      "bytes_per_launch": alg_bytes},
     }
-    if args.compare_rocsparse:
-        yo = y0.clone()
-        bps.tri_solve_batch(a, b, c, yo, work)
-        cmp_ = _rocsparse_compare("tri", dt, (a, b, c), y0, yo, args.steps)
-        cmp_["ours_ms"] = kern_ms
-        cmp_["speedup_of_ours"] = cmp_["ms"] / kern_ms
-        line["comparison"] = cmp_
     if not args.no_cpu_baseline:
         import oracle
         k0 = max(1, min(batch, (1 << 22) // n))
@@ -521,58 +504,6 @@ def _copy_gbs():
     return 2 * nbytes / (statistics.median(per) * 1e-3) / 1e9
 
 
-def _rocsparse_compare(kind, dt, diags, rhs, ours_x, steps):
-    """Context only: the vendor library's interleaved batched solver on the
-    same systems, as the pages compare their kernels with cuSPARSE's
-    (gpsvInterleavedBatch: QR; the tridiagonal case: rocSPARSE's Thomas
-    variant, the cuThomasBatch algorithm).  The library overwrites its
-    matrix, so each timed call gets fresh copies made outside the timed
-    region.  Returns timing and the largest per-system difference from our
-    solution."""
-    import ctypes
-    import torch
-    L = ctypes.CDLL(os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib", "librocsparse.so"))
-    vp, i32 = ctypes.c_void_p, ctypes.c_int32
-    h = vp()
-    if L.rocsparse_create_handle(ctypes.byref(h)) != 0:
-        raise RuntimeError("rocsparse_create_handle failed")
-    L.rocsparse_set_stream(h, vp(torch.cuda.current_stream().cuda_stream))
-    n, batch = rhs.shape
-    pre = "d" if dt == torch.float64 else "s"
-    if kind == "penta":
-        name, alg, nd = f"rocsparse_{pre}gpsv_interleaved_batch", 0, 5
-    else:
-        name, alg, nd = f"rocsparse_{pre}gtsv_interleaved_batch", 1, 3   # Thomas
-    work = [d.clone() for d in diags] + [rhs.clone()]
-    size = ctypes.c_size_t()
-    fb = getattr(L, name + "_buffer_size")
-    st = fb(h, i32(alg), i32(n), *(vp(t.data_ptr()) for t in work), i32(batch), i32(batch),
-            ctypes.byref(size))
-    if st != 0:
-        raise RuntimeError(f"{name}_buffer_size: status {st}")
-    tmp = torch.empty(max(1, size.value), dtype=torch.uint8, device="cuda:0")
-    f = getattr(L, name)
-    times = []
-    for k in range(steps + 2):
-        for dst, src in zip(work, list(diags) + [rhs]):
-            dst.copy_(src)
-        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        st = f(h, i32(alg), i32(n), *(vp(t.data_ptr()) for t in work), i32(batch), i32(batch),
-               vp(tmp.data_ptr()))
-        b.record()
-        if st != 0:
-            raise RuntimeError(f"{name}: status {st}")
-        torch.cuda.synchronize()
-        if k >= 2:
-            times.append(a.elapsed_time(b))
-    x = work[-1]
-    diff = ((x - ours_x).norm(dim=0) / ours_x.norm(dim=0)).max().item()
-    L.rocsparse_destroy_handle(h)
-    return {"library": name + (" (QR)" if kind == "penta" else " (Thomas)"),
-            "ms": statistics.median(times), "max_rel_diff_vs_ours": diff}
-
-
 def calibrate_copy(args):
     """A plain device-to-device copy of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
@@ -593,9 +524,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1, choices=list(range(1, 11)))
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
-    ap.add_argument("--compare-rocsparse", action="store_true",
-                    help="workloads 2, 7, 8: also time rocSPARSE's interleaved batched solver "
-                         "on the same systems (context, as the pages compare with cuSPARSE)")
     ap.add_argument("--split", action="store_true",
                     help="workloads 2, 9: time the separate factor and solve calls instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -9,10 +9,11 @@
  * hines_plan_destroy, which allocate / free device memory and synchronise.
  * No solve allocates memory.  Solve, pack and unpack calls enqueue kernels
  * only (no allocation, copy, memset or synchronisation), so a sequence of
- * them can be captured into a HIP graph and replayed.  The first chunked
- * pentadiagonal solve of a precision on a device (penta_factor_solve_batch)
- * also raises its kernels' dynamic-LDS limit there (hipFuncSetAttribute, a
- * host-side setting): make that first call outside a capture.
+ * them can be captured into a HIP graph and replayed.  The first call on a
+ * device that needs them (bps_init, penta_factor_solve_batch,
+ * hines_plan_create*) also sets the dynamic-LDS limits of the kernels that
+ * use more than 64 KiB there: a host-side kernel attribute, with no stream
+ * work, so that first call may itself be inside a capture.
  *
  * Sources (web-page titles; sections named as on the pages):
  *   [P] "cuPentBatch - A batched pentadiagonal solver for NVIDIA GPUs":
@@ -101,6 +102,13 @@ BPS_API const char *bps_status_str(int status);
 BPS_API const char *bps_last_error(void);
 /* Library version, major*10000 + minor*100 + patch. */
 BPS_API int bps_version(void);
+/* Prepare the current device: sets, once per device, the dynamic-LDS limits
+ * of the kernels whose launches may use more than 64 KiB (the chunked
+ * pentadiagonal solves, the Hines level schedule) to their largest launch.
+ * Host-side only (no allocation, no stream work); idempotent and
+ * thread-safe.  The entry points that launch those kernels call it
+ * themselves, so calling it is optional.  BPS_EHIP if the runtime refuses. */
+BPS_API bps_status bps_init(void);
 
 /* ======================================================================== */
 /* Pentadiagonal systems  [P] "Pentadiagonal solver"                        */

@@ -6,6 +6,10 @@ captured into a HIP graph and replayed -- the way to amortise launches for
 small, launch-bound batches.  Each replay is checked bit for bit against the
 eager result, with eager work and synchronisation between replays.  Calls on
 two streams with separate buffers give the results of sequential calls."""
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -102,3 +106,15 @@ def test_two_streams_match_sequential():
     for got_a, got_b, want in zip(A.outputs(), B.outputs(), ref):
         np.testing.assert_array_equal(got_a, want)
         np.testing.assert_array_equal(got_b, want)
+
+
+def test_first_call_inside_capture():
+    """The first library call of a process may be captured: the kernel
+    attributes it sets on the device are host-side (tests/graph_first_call.py,
+    run as a child process so that nothing before it has touched the
+    library)."""
+    script = os.path.join(os.path.dirname(os.path.abspath(__file__)), "graph_first_call.py")
+    r = subprocess.run([sys.executable, "-u", script], capture_output=True, text=True, timeout=240)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0
+    assert "FIRST_CALL_CAPTURE_OK" in r.stdout

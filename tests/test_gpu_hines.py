@@ -100,6 +100,92 @@ def test_mono_long_parent_distance_general_variant(schedule):
     assert np.all(info == 0)
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("n,batch,ld", [(300, 70, 128), (33, 1, 3), (512, 1000, 1024)])
+def test_mono_pack_solve_unpack(n, batch, ld, schedule):
+    """The mono layout transform of the Hines page (section 3, done once):
+    flat neuron-after-neuron values -> Full-Interleaved [n][ld] with ld >
+    batch -> solve -> flat.  The padding columns of every packed array read
+    0 (the packed buffers start as NaN), the round trip of an array is
+    exact, and every neuron matches the oracle."""
+    print(f"hines mono pack n={n} batch={batch} ld={ld} schedule={schedule}", flush=True)
+    hm = W.hines_mono(n, batch, rng=np.random.default_rng(n + 3 * ld))
+    plan = bps.hines_plan_create(batch, [n], hm.parent, mono=True, ld=ld, schedule=schedule)
+    assert plan.elems == n * ld
+    flats = [dev(W.to_flat(v).reshape(-1)) for v in (hm.u, hm.l, hm.d, hm.rhs)]
+    packed = [torch.full((n, ld), float("nan"), dtype=torch.float64, device="cuda:0")
+              for _ in range(4)]
+    for f, q in zip(flats, packed):
+        bps.hines_pack(plan, f, q)
+    for q, v in zip(packed, (hm.u, hm.l, hm.d, hm.rhs)):
+        h = host(q)
+        np.testing.assert_array_equal(h[:, :batch], v)
+        assert np.all(h[:, batch:] == 0.0)
+    back = torch.full_like(flats[2], float("nan"))
+    bps.hines_unpack(plan, packed[2], back)
+    np.testing.assert_array_equal(host(back), host(flats[2]))
+    work = buf(bps.hines_work_bytes(plan))
+    info = info_buf(batch)
+    bps.hines_solve_batch(plan, *packed, work, info)
+    out = torch.full_like(flats[3], float("nan"))
+    bps.hines_unpack(plan, packed[3], out)
+    got = host(out).reshape(batch, n).T
+    ref, rinfo = _oracle_mono(hm)
+    assert _cols_err(got, ref) <= 1e-10
+    np.testing.assert_array_equal(host(info).astype(int), rinfo)
+    plan.close()
+
+
+def _tree_at_distance(n, dist, rng):
+    """Parents in the window of 8 rows, with every 29th node's parent planted
+    exactly `dist` rows up: the largest parent distance is `dist`."""
+    p = W.random_tree(n, rng)
+    p[dist::29] = np.arange(dist, n, 29) - dist
+    assert W.tree_stats(p)["max_parent_distance"] == dist
+    return p
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("dist", [16, 17])
+def test_mono_parent_distance_window_edge(dist, schedule):
+    """Largest parent distance 16 (the last one the 16-slot on-chip window
+    of pending updates and recent voltages holds: the child's slot is the
+    parent's) and 17 (the first one sent to the global accumulators)."""
+    print(f"hines mono window edge dist={dist} schedule={schedule}", flush=True)
+    rng = np.random.default_rng(100 + dist)
+    hm = _tree_values(_tree_at_distance(200, dist, rng), 130, rng)
+    out, info = _solve_mono(hm, schedule=schedule)
+    ref, rinfo = _oracle_mono(hm)
+    assert _cols_err(out, ref) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("dist", [16, 17])
+def test_multi_parent_distance_window_edge(dist, schedule):
+    """As the mono case, for blocks of different trees: every neuron with
+    more than `dist` compartments carries parents at exactly `dist`."""
+    print(f"hines multi window edge dist={dist} schedule={schedule}", flush=True)
+    rng = np.random.default_rng(200 + dist)
+    mm = W.hines_multi(150, 10, 90, rng=rng)
+    for s in range(mm.batch):
+        n = int(mm.sizes[s])
+        if n <= dist:
+            continue
+        o0, o1 = mm.offsets[s], mm.offsets[s + 1]
+        p = _tree_at_distance(n, dist, rng)
+        mm.parent[o0:o1] = p
+        u = mm.u[o0:o1]
+        d = 1.0 + np.abs(mm.l[o0:o1]) + rng.uniform(0, 1, n)   # l of the root is 0
+        for j in range(1, n):
+            d[p[j]] += abs(u[j])
+        mm.d[o0:o1] = d
+    out, info = _run_multi(mm, schedule)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    assert _rel_per_neuron(out, ref, mm.offsets) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+
+
 def _run_multi(mm, schedule=bps.BPS_HINES_AUTO):
     plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=schedule)
     if schedule != bps.BPS_HINES_AUTO:
