@@ -25,7 +25,8 @@ __all__ = [
     "bps_penta_factor_bytes", "bps_penta_work_bytes",
     "penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
     "penta_factor_solve_batch",
-    "hyperdiffusion_work_bytes", "hyperdiffusion_step",
+    "hyperdiffusion_work_bytes", "hyperdiffusion_step", "hyperdiffusion_step_noalloc",
+    "BPS_NOALLOC_SCRATCH_BYTES",
     "hyperdiffusion_theta_work_bytes", "hyperdiffusion_theta_step",
     "cahn_hilliard_work_bytes", "cahn_hilliard_step",
     "tri_work_bytes", "tri_solve_batch",
@@ -96,6 +97,8 @@ def load_library():
             "hyperdiffusion_work_bytes": ([st, i64, i64], ctypes.c_size_t),
             "hyperdiffusion_step": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double, vp, vp,
                                      i64, vp, vp], st),
+            "hyperdiffusion_step_noalloc": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double,
+                                             vp, vp, i64, vp], st),
             "hyperdiffusion_theta_work_bytes": ([st, i64, i64], ctypes.c_size_t),
             "hyperdiffusion_theta_step": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double,
                                            ctypes.c_double, vp, i64, vp, vp], st),
@@ -286,6 +289,21 @@ def hyperdiffusion_step(C, dt: float, dx: float, nsteps: int, work, diagonals=No
     _check("hyperdiffusion_step", load_library().hyperdiffusion_step(
         dt_code, n, batch, ld, float(dt), float(dx), _ptr(diagonals), _ptr(C), int(nsteps),
         _ptr(work), _stream(stream)))
+    return C
+
+
+BPS_NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024
+
+
+def hyperdiffusion_step_noalloc(C, dt: float, dx: float, nsteps: int, diagonals=None, *,
+                                batch=None, stream=None):
+    """hyperdiffusion_step with the library's per-GPU scratch array as work
+    memory: allocates nothing (see bps.h for the size limit and the sharing
+    of the array between calls on one GPU)."""
+    n, batch, ld = _geom(C, batch)
+    _check("hyperdiffusion_step_noalloc", load_library().hyperdiffusion_step_noalloc(
+        _dtype_code(C), n, batch, ld, float(dt), float(dx), _ptr(diagonals), _ptr(C),
+        int(nsteps), _stream(stream)))
     return C
 
 

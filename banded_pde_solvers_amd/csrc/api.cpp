@@ -2,8 +2,8 @@
 // the host, then kernel launches on the caller's stream.
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <mutex>
-#include <set>
 #include <utility>
 
 #include "common.h"
@@ -23,17 +23,30 @@ void set_error(const char *fmt, ...)
 
 void clear_error() { g_err[0] = '\0'; }
 
-bps_status prepare_device()
+// Work memory of hyperdiffusion_step_noalloc: one array per GPU (each device
+// that loads the library holds its own copy until the process ends).  In host
+// code the name `scratch` is only a host-side stand-in: the device address is
+// taken with hipGetSymbolAddress, once per device, and used everywhere the
+// host needs the array.
+static __device__ __align__(256) unsigned char scratch[BPS_NOALLOC_SCRATCH_BYTES];
+
+bps_status prepare_device(void **scratch_dev)
 {
     static std::mutex mu;
-    static std::set<int> done;
+    static std::map<int, void *> done;     // device -> address of its scratch
     int dev = 0;
     BPS_HIP(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lock(mu);
-    if (done.count(dev)) return BPS_OK;
-    BPS_HIP(spike_prepare_device());
-    BPS_HIP(hines_prepare_device());
-    done.insert(dev);
+    auto it = done.find(dev);
+    if (it == done.end()) {
+        BPS_HIP(spike_prepare_device());
+        BPS_HIP(hines_prepare_device());
+        void *ptr = nullptr;
+        BPS_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) BPS_FAIL(BPS_EHIP, "hipGetSymbolAddress gave no address for the scratch array");
+        it = done.emplace(dev, ptr).first;
+    }
+    if (scratch_dev) *scratch_dev = it->second;
     return BPS_OK;
 }
 
@@ -236,20 +249,28 @@ size_t hyperdiffusion_work_bytes(int dtype, int64_t n, int64_t batch)
     return stream > res ? stream : res;
 }
 
-bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
-                               double dx, const void *diagonals, void *C, int64_t nsteps,
-                               void *work, void *stream)
+// Checks every argument of hyperdiffusion_step but `work`.
+static bps_status check_hyper_args(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
+                                   double dx, const void *diagonals, void *C, int64_t nsteps)
 {
-    clear_error();
     bps_penta_desc dsc{dtype, BPS_CYCLIC | BPS_SHARED_COEF, n, batch, ld};
     CHECK(check_desc(&dsc));
     if (nsteps < 0) BPS_FAIL(BPS_EINVAL, "nsteps = %lld < 0", (long long)nsteps);
     if (!std::isfinite(dt) || !std::isfinite(dx) || dx == 0.0)
         BPS_FAIL(BPS_EINVAL, "dt and dx must be finite and dx nonzero");
     CHECK(check_ptr(C, "C", dtype));
-    CHECK(check_ptr(work, "work", dtype));
     if (diagonals) CHECK(check_ptr(diagonals, "diagonals", dtype));
-    hipStream_t st = as_stream(stream);
+    if (!diagonals && !std::isfinite(dt / (dx * dx * dx * dx)))
+        BPS_FAIL(BPS_EINVAL, "sigma = dt/dx^4 is not finite");
+    return BPS_OK;
+}
+
+// The steps of hyperdiffusion_step with validated arguments and a work
+// buffer of hyperdiffusion_work_bytes(dtype, n, batch) bytes.
+static bps_status hyper_steps(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
+                              double dx, const void *diagonals, void *C, int64_t nsteps,
+                              void *work, hipStream_t st)
+{
     const size_t es = dtype_size(dtype);
     char *w = static_cast<char *>(work);
     const void *dg = diagonals;
@@ -257,7 +278,6 @@ bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, 
                           dt / (dx * dx * dx * dx) >= 0.0;
     if (!dg) {
         const double sigma = dt / (dx * dx * dx * dx);
-        if (!std::isfinite(sigma)) BPS_FAIL(BPS_EINVAL, "sigma = dt/dx^4 is not finite");
         if (!resident)
             CHECK(dtype == BPS_F64 ? launch_hyper_diagonals<double>(n, sigma, w, st)
                                    : launch_hyper_diagonals<float>(n, sigma, w, st));
@@ -283,6 +303,33 @@ bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, 
                                      D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
     if (nsteps == 0) return BPS_OK;
     return launch_penta_cyclic_solve<float>(n, batch, ld, nsteps, true, fac, C, st);
+}
+
+bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
+                               double dx, const void *diagonals, void *C, int64_t nsteps,
+                               void *work, void *stream)
+{
+    clear_error();
+    CHECK(check_hyper_args(dtype, n, batch, ld, dt, dx, diagonals, C, nsteps));
+    CHECK(check_ptr(work, "work", dtype));
+    return hyper_steps(dtype, n, batch, ld, dt, dx, diagonals, C, nsteps, work,
+                       as_stream(stream));
+}
+
+bps_status hyperdiffusion_step_noalloc(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
+                                       double dx, const void *diagonals, void *C, int64_t nsteps,
+                                       void *stream)
+{
+    clear_error();
+    CHECK(check_hyper_args(dtype, n, batch, ld, dt, dx, diagonals, C, nsteps));
+    const size_t need = hyperdiffusion_work_bytes(dtype, n, batch);
+    if (need > size_t(BPS_NOALLOC_SCRATCH_BYTES))
+        BPS_FAIL(BPS_EINVAL, "hyperdiffusion_step_noalloc: n = %lld needs %zu bytes of work, more "
+                 "than the %zu-byte scratch array", (long long)n, need,
+                 size_t(BPS_NOALLOC_SCRATCH_BYTES));
+    void *work = nullptr;
+    CHECK(prepare_device(&work));
+    return hyper_steps(dtype, n, batch, ld, dt, dx, diagonals, C, nsteps, work, as_stream(stream));
 }
 
 // ---- theta scheme -------------------------------------------------------------------

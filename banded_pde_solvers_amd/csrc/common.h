@@ -42,7 +42,9 @@ void clear_error();
 // call that needs them: every kernel whose launches may use more than the
 // default 64 KiB of dynamic LDS is allowed its largest launch.  Host-side
 // only (no stream work, no allocation), so it may run inside a graph capture.
-bps_status prepare_device();
+// Also gives the device address of the current device's scratch array (the
+// work memory of the allocation-free entry point) when scratch_dev is set.
+bps_status prepare_device(void **scratch_dev = nullptr);
 hipError_t spike_prepare_device();     // penta_spike.hip
 hipError_t hines_prepare_device();     // hines.hip
 

@@ -214,6 +214,27 @@ BPS_API bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int6
                                double dt, double dx, const void *diagonals,
                                void *C, int64_t nsteps, void *work, void *stream);
 
+/* Size of the per-GPU scratch array of hyperdiffusion_step_noalloc. */
+#define BPS_NOALLOC_SCRATCH_BYTES (2u * 1024u * 1024u)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * hyperdiffusion_step without the `work` argument: same operation, other
+ * arguments, checks and results.  Its work memory is a device array of
+ * BPS_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU, which that GPU
+ * holds from the library's first use on it until the process ends.  The
+ * call allocates nothing (no hipMalloc / hipFree, no allocating library
+ * routine).  BPS_EINVAL when hyperdiffusion_work_bytes(dtype, n, batch)
+ * exceeds the array (n above 18725 in fp64, 37450 in fp32).  Every call on a
+ * GPU uses that GPU's array, which keeps the last call's contents (each call
+ * writes all the work memory it reads before reading it, so nothing needs
+ * clearing): calls on one stream are ordered, but calls that overlap on one
+ * GPU (on streams not ordered with each other, or from several threads at
+ * once) race and give undefined results. */
+BPS_API bps_status hyperdiffusion_step_noalloc(int dtype, int64_t n, int64_t batch, int64_t ld,
+                                       double dt, double dx, const void *diagonals, void *C,
+                                       int64_t nsteps, void *stream);
+
 /* Bytes of `work` for hyperdiffusion_theta_step (0 if invalid). */
 BPS_API size_t hyperdiffusion_theta_work_bytes(int dtype, int64_t n, int64_t batch);
 
