@@ -26,6 +26,7 @@ __all__ = [
     "penta_factor_batch", "penta_solve_batch", "penta_cyclic_solve_batch",
     "penta_factor_solve_batch",
     "hyperdiffusion_work_bytes", "hyperdiffusion_step", "hyperdiffusion_step_noalloc",
+    "hyperdiffusion_factor", "hyperdiffusion_solve",
     "BPS_NOALLOC_SCRATCH_BYTES",
     "hyperdiffusion_theta_work_bytes", "hyperdiffusion_theta_step",
     "cahn_hilliard_work_bytes", "cahn_hilliard_step",
@@ -97,6 +98,9 @@ def load_library():
             "hyperdiffusion_work_bytes": ([st, i64, i64], ctypes.c_size_t),
             "hyperdiffusion_step": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double, vp, vp,
                                      i64, vp, vp], st),
+            "hyperdiffusion_factor": ([st, i64, ctypes.c_double, ctypes.c_double, vp, vp, vp], st),
+            "hyperdiffusion_solve": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double, vp, vp,
+                                      i64, vp, vp], st),
             "hyperdiffusion_step_noalloc": ([st, i64, i64, i64, ctypes.c_double, ctypes.c_double,
                                              vp, vp, i64, vp], st),
             "hyperdiffusion_theta_work_bytes": ([st, i64, i64], ctypes.c_size_t),
@@ -287,6 +291,33 @@ def hyperdiffusion_step(C, dt: float, dx: float, nsteps: int, work, diagonals=No
     if work.numel() * work.element_size() < need:
         raise ValueError(f"work buffer too small ({need} bytes needed)")
     _check("hyperdiffusion_step", load_library().hyperdiffusion_step(
+        dt_code, n, batch, ld, float(dt), float(dx), _ptr(diagonals), _ptr(C), int(nsteps),
+        _ptr(work), _stream(stream)))
+    return C
+
+
+def hyperdiffusion_factor(n: int, dt: float, dx: float, work, diagonals=None, *,
+                          dtype: int = BPS_F64, stream=None):
+    """Factor the periodic operator (I + sigma D4, or the given diagonals)
+    once into work; hyperdiffusion_solve then reuses it."""
+    need = load_library().hyperdiffusion_work_bytes(int(dtype), int(n), 1)
+    if work.numel() * work.element_size() < need:
+        raise ValueError(f"work buffer too small ({need} bytes needed)")
+    _check("hyperdiffusion_factor", load_library().hyperdiffusion_factor(
+        int(dtype), int(n), float(dt), float(dx), _ptr(diagonals), _ptr(work), _stream(stream)))
+    return work
+
+
+def hyperdiffusion_solve(C, dt: float, dx: float, nsteps: int, work, diagonals=None, *,
+                         batch=None, stream=None):
+    """Advance C (n, ld) by nsteps steps with the factors of
+    hyperdiffusion_factor (same dt, dx, diagonals and dtype)."""
+    n, batch, ld = _geom(C, batch)
+    dt_code = _dtype_code(C)
+    need = load_library().hyperdiffusion_work_bytes(dt_code, n, 1)
+    if work.numel() * work.element_size() < need:
+        raise ValueError(f"work buffer too small ({need} bytes needed)")
+    _check("hyperdiffusion_solve", load_library().hyperdiffusion_solve(
         dt_code, n, batch, ld, float(dt), float(dx), _ptr(diagonals), _ptr(C), int(nsteps),
         _ptr(work), _stream(stream)))
     return C

@@ -265,44 +265,87 @@ static bps_status check_hyper_args(int dtype, int64_t n, int64_t batch, int64_t 
     return BPS_OK;
 }
 
-// The steps of hyperdiffusion_step with validated arguments and a work
-// buffer of hyperdiffusion_work_bytes(dtype, n, batch) bytes.
+// The register-resident multi-step kernel applies to the built-in operator
+// I + sigma*D4 in fp64 for the chunkable n: every chunk of a system then sees
+// the same interior block, and no diagonal arrays are needed.
+static bool hyper_resident(int dtype, int64_t n, double dt, double dx, const void *diagonals)
+{
+    return !diagonals && dtype == BPS_F64 && resident_chunk(n) != 0 && dt / (dx * dx * dx * dx) >= 0.0;
+}
+
+// The factor half of hyperdiffusion_step (validated arguments; work of
+// hyperdiffusion_work_bytes): the resident kernel's coefficients, or the
+// operator's diagonals (built unless given) and their periodic factors.
+static bps_status hyper_factor(int dtype, int64_t n, double dt, double dx, const void *diagonals,
+                               void *work, hipStream_t st)
+{
+    const size_t es = dtype_size(dtype);
+    char *w = static_cast<char *>(work);
+    void *fac = w + 5 * n * es;
+    if (hyper_resident(dtype, n, dt, dx, diagonals))
+        return launch_hyper_resident(n, 1, 1, 0, dt / (dx * dx * dx * dx), 0, 1.0, 0.0, 0.0, 0.0,
+                                     fac, nullptr, st, kResSetup);
+    const void *dg = diagonals;
+    if (!dg) {
+        const double sigma = dt / (dx * dx * dx * dx);
+        CHECK(dtype == BPS_F64 ? launch_hyper_diagonals<double>(n, sigma, w, st)
+                               : launch_hyper_diagonals<float>(n, sigma, w, st));
+        dg = w;
+    }
+    const char *D = static_cast<const char *>(dg);
+    if (dtype == BPS_F64)
+        return launch_penta_factor<double>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
+                                           D + 3 * n * es, D + 4 * n * es, fac, nullptr, st);
+    return launch_penta_factor<float>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
+                                      D + 3 * n * es, D + 4 * n * es, fac, nullptr, st);
+}
+
+// The solve half: nsteps steps with the factors hyper_factor left in work.
+static bps_status hyper_solve(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
+                              double dx, const void *diagonals, void *C, int64_t nsteps,
+                              const void *work, hipStream_t st)
+{
+    const size_t es = dtype_size(dtype);
+    void *fac = const_cast<char *>(static_cast<const char *>(work)) + 5 * n * es;
+    if (nsteps == 0) return BPS_OK;
+    if (hyper_resident(dtype, n, dt, dx, diagonals))
+        return launch_hyper_resident(n, batch, ld, nsteps, dt / (dx * dx * dx * dx), 0, 1.0, 0.0,
+                                     0.0, 0.0, fac, C, st, kResSteps);
+    return dtype == BPS_F64 ? launch_penta_cyclic_solve<double>(n, batch, ld, nsteps, true, fac, C, st)
+                            : launch_penta_cyclic_solve<float>(n, batch, ld, nsteps, true, fac, C, st);
+}
+
 static bps_status hyper_steps(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
                               double dx, const void *diagonals, void *C, int64_t nsteps,
                               void *work, hipStream_t st)
 {
-    const size_t es = dtype_size(dtype);
-    char *w = static_cast<char *>(work);
-    const void *dg = diagonals;
-    const bool resident = !diagonals && dtype == BPS_F64 && resident_chunk(n) != 0 &&
-                          dt / (dx * dx * dx * dx) >= 0.0;
-    if (!dg) {
-        const double sigma = dt / (dx * dx * dx * dx);
-        if (!resident)
-            CHECK(dtype == BPS_F64 ? launch_hyper_diagonals<double>(n, sigma, w, st)
-                                   : launch_hyper_diagonals<float>(n, sigma, w, st));
-        dg = w;
-    }
-    void *fac = w + 5 * n * es;
-    if (resident) {
-        // the operator I + sigma*D4 with constant diagonals: every chunk of a
-        // system sees the same interior block, so the register-resident
-        // multi-step kernel applies (it needs no diagonal arrays)
-        const double sigma = dt / (dx * dx * dx * dx);
-        return launch_hyper_resident(n, batch, ld, nsteps, sigma, 0, 1.0, 0.0, 0.0, 0.0, fac, C,
-                                     st);
-    }
-    const char *D = static_cast<const char *>(dg);
-    if (dtype == BPS_F64) {
-        CHECK(launch_penta_factor<double>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
-                                          D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
-        if (nsteps == 0) return BPS_OK;
-        return launch_penta_cyclic_solve<double>(n, batch, ld, nsteps, true, fac, C, st);
-    }
-    CHECK(launch_penta_factor<float>(n, 1, 1, true, true, D, D + n * es, D + 2 * n * es,
-                                     D + 3 * n * es, D + 4 * n * es, fac, nullptr, st));
-    if (nsteps == 0) return BPS_OK;
-    return launch_penta_cyclic_solve<float>(n, batch, ld, nsteps, true, fac, C, st);
+    CHECK(hyper_factor(dtype, n, dt, dx, diagonals, work, st));
+    return hyper_solve(dtype, n, batch, ld, dt, dx, diagonals, C, nsteps, work, st);
+}
+
+bps_status hyperdiffusion_factor(int dtype, int64_t n, double dt, double dx, const void *diagonals,
+                                 void *work, void *stream)
+{
+    clear_error();
+    bps_penta_desc dsc{dtype, BPS_CYCLIC | BPS_SHARED_COEF, n, 1, 1};
+    CHECK(check_desc(&dsc));
+    if (!std::isfinite(dt) || !std::isfinite(dx) || dx == 0.0)
+        BPS_FAIL(BPS_EINVAL, "dt and dx must be finite and dx nonzero");
+    if (diagonals) CHECK(check_ptr(diagonals, "diagonals", dtype));
+    if (!diagonals && !std::isfinite(dt / (dx * dx * dx * dx)))
+        BPS_FAIL(BPS_EINVAL, "sigma = dt/dx^4 is not finite");
+    CHECK(check_ptr(work, "work", dtype));
+    return hyper_factor(dtype, n, dt, dx, diagonals, work, as_stream(stream));
+}
+
+bps_status hyperdiffusion_solve(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,
+                                double dx, const void *diagonals, void *C, int64_t nsteps,
+                                const void *work, void *stream)
+{
+    clear_error();
+    CHECK(check_hyper_args(dtype, n, batch, ld, dt, dx, diagonals, C, nsteps));
+    CHECK(check_ptr(work, "work", dtype));
+    return hyper_solve(dtype, n, batch, ld, dt, dx, diagonals, C, nsteps, work, as_stream(stream));
 }
 
 bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int64_t ld, double dt,

@@ -739,10 +739,11 @@ size_t resident_coef_bytes(int64_t n)
 template <int M, int P>
 static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, int mode,
                        double e0, double e1, double e2, double rr, double *coef, double *C,
-                       hipStream_t st)
+                       int parts, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_hyper_resident_setup<M, P>), dim3(1), dim3(64), 0, st, sigma, coef);
-    if (nsteps == 0) return;
+    if (parts & kResSetup)
+        hipLaunchKernelGGL((k_hyper_resident_setup<M, P>), dim3(1), dim3(64), 0, st, sigma, coef);
+    if (nsteps == 0 || !(parts & kResSteps)) return;
     constexpr int S = res_systems(P), WS = res_waves(P), SW = S * WS;
     const unsigned grid = unsigned((batch + SW - 1) / SW);
     const unsigned threads = WS > 1 ? unsigned(kWave * WS) : unsigned(S * P);
@@ -768,14 +769,14 @@ static void launch_res(int64_t batch, int64_t ld, int64_t nsteps, double sigma, 
 
 bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t nsteps, double sigma,
                                  int mode, double e0, double e1, double e2, double rr, void *coef,
-                                 void *C, hipStream_t st)
+                                 void *C, hipStream_t st, int parts)
 {
     constexpr int M = 64;
     if (resident_chunk(n) != M || !(sigma >= 0.0))
         BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16 or P = 32, 64, sigma >= 0");
     double *cf = (double *)coef, *x = (double *)C;
 #define BPS_RES_CASE(PP) \
-    case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, st); break;
+    case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st); break;
     switch (int(n / M)) {
     BPS_RES_CASE(2) BPS_RES_CASE(3) BPS_RES_CASE(4) BPS_RES_CASE(5) BPS_RES_CASE(6)
     BPS_RES_CASE(7) BPS_RES_CASE(8) BPS_RES_CASE(9) BPS_RES_CASE(10) BPS_RES_CASE(11)

@@ -48,9 +48,12 @@ size_t resident_coef_bytes(int64_t n);
 // the state (kResStencil: theta scheme; sigma is then theta * sigma), plus
 // rr D2 (C^3 - C) with kResPhase (Cahn-Hilliard).
 enum { kResStencil = 1, kResPhase = 2 };
+// parts: the set-up kernel (coefficients into coef), the step kernel (reads
+// them), or both in that order.
+enum { kResSetup = 1, kResSteps = 2, kResBoth = 3 };
 bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t nsteps, double sigma,
                                  int mode, double e0, double e1, double e2, double rr, void *coef,
-                                 void *C, hipStream_t st);
+                                 void *C, hipStream_t st, int parts = kResBoth);
 // Streaming theta / Cahn-Hilliard right-hand side: the explicit stencil
 // (+ rr D2 (C^3 - C) when ch) into a separate array, and a strided copy
 // between interleaved arrays.

@@ -4,19 +4,31 @@
 Default workload (the headline): periodic hyperdiffusion with constant
 coefficients, N = 1024 unknowns per system, 16384 systems, fp64,
 sigma = dt/dx^4 with dt = 1e-6, dx = 1/1024, 100 implicit time steps per
-benchmark step.  One benchmark step is one hyperdiffusion_step call: build
-the operator, factor it once (with the periodic-reduction quantities), and
-run all 100 solves (forward sweep, corner solve, backward sweep) on every
-system -- the whole path on one batch of synthetic input already resident in
-device memory.
+benchmark step.  One benchmark step is the whole path on one batch already
+resident in device memory: hyperdiffusion_factor (build the operator, factor
+it once with the periodic-reduction quantities) then hyperdiffusion_solve
+(all 100 solves -- forward sweep, corner/interface solve, backward sweep --
+on every system); together they are exactly hyperdiffusion_step.
+
+Timing protocol: W untimed warm-up steps, then exactly K timed steps
+bracketed by torch.cuda.synchronize(); `value` is the whole-job throughput
+(unknowns of the K steps over the wall time).  Every call is also bracketed
+by HIP events on the stream the library launches on, giving per-call medians
+with p10 / p90 (`timing`); for the headline the event pair around
+hyperdiffusion_solve times the register-resident step kernel alone (one
+launch), which is what the roofline uses.  After the timed region the same
+call is made on the initial state and a sample of systems is compared with
+the oracle (`parity`).
 
 Output: ONE JSON line (metric, value = unknowns solved per second, ...),
-with a "roofline" object for the dominant kernel (the register-resident
-multi-step periodic solve, bound by fp64 vector arithmetic: 17 algorithmic
-flops per unknown per time step against the 78.6 TFLOP/s fp64 vector peak;
-HBM sees the state once in and once out per call) and a "cpu_baseline"
-object (the CPU oracle, OpenMP over systems, timed on a bounded sample of
-the same workload on this host's cores).
+with "timing", "parity", a "roofline" object for the dominant kernel (the
+headline's is bound by fp64 vector arithmetic: 17 algorithmic flops per
+unknown per time step against the 78.6 TFLOP/s fp64 vector peak; its "hbm"
+part gives the state's algorithmic bytes per launch and the measured
+counter bytes over the kernel time) and a "cpu_baseline" object (the
+oracle, built with gcc -O3 -march=native -fopenmp on this host, timed on a
+bounded sample of the same workload with all of this host's cores and with
+one thread, median of 3 runs each, CPU model and core counts stated).
 
     python bench.py [--steps K] [--warmup W] [--workload {1,...,10}]
 
@@ -55,23 +67,45 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def _time_loop(fn, steps, warmup):
-    """Warm up, then time exactly `steps` calls bracketed by synchronisation;
-    also record each call with HIP events on the current stream."""
+def _stats(xs):
+    """Median, 10th and 90th percentile of a list of times (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=float)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def _time_steps(segments, steps, warmup):
+    """Warm up, then time exactly `steps` steps bracketed by synchronisation.
+
+    A step runs the callables in `segments` in order; HIP events on the
+    current stream (the one the library launches on) are recorded before the
+    first and after each, so that every segment of every step is timed on
+    the device.  Returns the wall time of the timed steps and, per segment,
+    the list of its per-step times in ms."""
     import torch
     for _ in range(warmup):
-        fn()
+        for f in segments:
+            f()
     torch.cuda.synchronize()
-    evs = [_events() for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(segments) + 1)]
+           for _ in range(steps)]
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
+    for ev in evs:
+        ev[0].record()
+        for k, f in enumerate(segments):
+            f()
+            ev[k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in evs]
+    per = [[ev[k].elapsed_time(ev[k + 1]) for ev in evs] for k in range(len(segments))]
     return wall, per
+
+
+def _time_loop(fn, steps, warmup):
+    """One-segment _time_steps: (wall, per-step ms)."""
+    wall, per = _time_steps([fn], steps, warmup)
+    return wall, per[0]
 
 
 def _source_hash(relpath):
@@ -153,29 +187,63 @@ def pmc_summary(args):
     print(json.dumps({args.pmc_key: ent}), flush=True)
 
 
-_CPU_THREADS = 0      # oracle threads for the CPU baseline (0: OpenMP's default)
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _cpu_baseline(run_sample, unknowns_per_system, label, seconds):
-    """Time the oracle on a growing sample until it takes ~`seconds`."""
+    """The oracle as it stands, timed on this host: built here with gcc -O3
+    -march=native -fopenmp (oracle.TIMING_CFLAGS), run on a sample of the
+    workload sized so that one run takes about seconds / 8, three runs with
+    all the threads OpenMP gives it and three with one thread, medians
+    reported (about `seconds` of CPU work in all)."""
+    import tempfile
     import oracle
-    cores = oracle.set_threads(_CPU_THREADS)
-    k = 8
-    t = 0.0
-    while True:
-        t0 = time.perf_counter()
-        run_sample(k)
-        t = time.perf_counter() - t0
-        if t >= seconds / 4 or k >= 1 << 20:
-            break
-        k = int(k * min(16.0, max(2.0, seconds / 4 / max(t, 1e-4))))
-    # final timed sample sized to ~seconds
-    k = max(1, int(k * seconds / max(t, 1e-6) / 2))
-    t0 = time.perf_counter()
-    run_sample(k)
-    t = time.perf_counter() - t0
-    return {"value": k * unknowns_per_system / t, "unit": "unknowns/s", "cores": cores,
-            "kind": "oracle", "sample": f"{k} {label} in {t:.2f} s"}
+    oracle.use_library(oracle.build_timing(tempfile.mkdtemp(prefix="orc_timing_")))
+    legs = {}
+    for key, req in (("all", 0), ("one", 1)):
+        used = oracle.set_threads(req)
+        k, t = 4, 0.0
+        while True:
+            t0 = time.perf_counter()
+            run_sample(k)
+            t = time.perf_counter() - t0
+            if t >= seconds / 40 or k >= 1 << 20:
+                break
+            k = int(k * min(16.0, max(2.0, seconds / 40 / max(t, 1e-4))))
+        k = max(1, int(k * seconds / 8 / max(t, 1e-6)))
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            run_sample(k)
+            runs.append(time.perf_counter() - t0)
+        med = statistics.median(runs)
+        legs[key] = {"value": k * unknowns_per_system / med, "systems_per_s": k / med,
+                     "threads": used, "sample": f"{k} {label}", "runs_s": [round(r, 3) for r in runs]}
+    a = legs["all"]
+    return {"value": a["value"], "unit": "unknowns/s", "cores": a["threads"], "kind": "oracle",
+            "sample": f"{a['sample']}, median of 3 runs of {statistics.median(a['runs_s']):.2f} s",
+            "systems_per_s": a["systems_per_s"],
+            "one_thread": {"value": legs["one"]["value"], "systems_per_s": legs["one"]["systems_per_s"],
+                           "sample": f"{legs['one']['sample']}, median of 3 runs",
+                           "runs_s": legs["one"]["runs_s"]},
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)),
+            "build": "gcc " + " ".join(oracle.TIMING_CFLAGS)}
+
+
+def _max_col_err(got, ref, scale=None):
+    """Largest per-system normwise relative error of (n, k) arrays."""
+    import numpy as np
+    den = np.linalg.norm(ref if scale is None else scale, axis=0)
+    return float(np.max(np.linalg.norm(got - ref, axis=0) / den))
 
 
 # ---------------------------------------------------------------------------
@@ -195,24 +263,30 @@ def bench_hyperdiffusion(args, which=1):
     n, batch, nsteps, dt, dx = cfg["n"], cfg["batch"], cfg["nsteps"], cfg["dt"], cfg["dx"]
     theta = cfg.get("theta")
     dev = "cuda:0"
+    if kind == "cahn_hilliard":
+        C0 = torch.as_tensor(W.cahn_hilliard_quench(n, batch), device=dev)
+    else:
+        C0 = torch.as_tensor(W.hyperdiffusion_random(n, batch), device=dev)
+    C = C0.clone()
     if kind == "hyperdiffusion":
-        C = torch.as_tensor(W.hyperdiffusion_random(n, batch), device=dev)
+        # the headline: factor once, then the 100 steps (one kernel launch)
         work = torch.empty(bps.hyperdiffusion_work_bytes(n, batch), dtype=torch.uint8, device=dev)
-        run = lambda k: bps.hyperdiffusion_step(C, dt, dx, k, work)
+        segs = [lambda: bps.hyperdiffusion_factor(n, dt, dx, work),
+                lambda: bps.hyperdiffusion_solve(C, dt, dx, nsteps, work)]
+        run = lambda: [f() for f in segs]
     elif kind == "hyperdiffusion_theta":
-        C = torch.as_tensor(W.hyperdiffusion_random(n, batch), device=dev)
         work = torch.empty(bps.hyperdiffusion_theta_work_bytes(n, batch), dtype=torch.uint8, device=dev)
-        run = lambda k: bps.hyperdiffusion_theta_step(C, dt, dx, theta, k, work)
+        run = lambda: bps.hyperdiffusion_theta_step(C, dt, dx, theta, nsteps, work)
+        segs = [run]
     else:
         gamma, mob = cfg["gamma"], cfg["mobility"]
-        C = torch.as_tensor(W.cahn_hilliard_quench(n, batch), device=dev)
         work = torch.empty(bps.cahn_hilliard_work_bytes(n, batch), dtype=torch.uint8, device=dev)
-        run = lambda k: bps.cahn_hilliard_step(C, dt, dx, gamma, mob, theta, k, work)
-    wall, per = _time_loop(lambda: run(nsteps), args.steps, args.warmup)
-    # the operator set-up alone (diagonals + shared factorisation), same stream
-    _, setup = _time_loop(lambda: run(0), 10, 2)
+        run = lambda: bps.cahn_hilliard_step(C, dt, dx, gamma, mob, theta, nsteps, work)
+        segs = [run]
+    wall, per = _time_steps(segs, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
-    kern_ms = max(statistics.mean(per) - statistics.median(setup), 1e-6)
+    call = [sum(x) for x in zip(*per)]
+    kern = per[-1]            # the step kernel alone (headline), else the whole call
     unknowns = n * batch * nsteps
     # The solve keeps every system in registers for all time steps, so HBM
     # sees the state once in and once out per call: the kernel is bound by
@@ -228,9 +302,12 @@ def bench_hyperdiffusion(args, which=1):
         flops_per += 7.0
     if kind == "cahn_hilliard":
         flops_per += 8.0
+    kern_ms = _stats(kern)["median"]
     alg_flops = flops_per * unknowns
     achieved = alg_flops / (kern_ms * 1e-3) / 1e12
     hbm_bytes = 16.0 * n * batch                     # C read once, written once
+    traffic = _traffic({"hyperdiffusion": "hyperdiffusion", "hyperdiffusion_theta": "hyperdiffusion_theta",
+                        "cahn_hilliard": "cahn_hilliard"}[kind])
     label = {"hyperdiffusion": "periodic hyperdiffusion implicit steps",
              "hyperdiffusion_theta": "periodic hyperdiffusion Crank-Nicolson steps",
              "cahn_hilliard": "periodic Cahn-Hilliard semi-implicit steps"}[kind]
@@ -243,36 +320,68 @@ def bench_hyperdiffusion(args, which=1):
     else:
         config.update(sigma=dt / dx ** 4, scheme="implicit" if theta is None else f"theta = {theta}")
     config["coefficients"] = "constant (factor once)"
+    timing = {"call_ms": _stats(call), "systems_per_s": batch * args.steps / wall,
+              "time_steps_per_s": nsteps * args.steps / wall}
+    if kind == "hyperdiffusion":
+        timing["factor_ms"] = _stats(per[0])
+        timing["solve_kernel_ms"] = _stats(kern)
+        timed = "k_hyper_resident<64,16,0> alone (HIP events around hyperdiffusion_solve)"
+    else:
+        timed = "whole call (set-up kernel included)"
     line = {
         "metric": "unknowns solved/s (fp64), " + label,
-        "value": unknowns / (ms_step * 1e-3),
+        "value": unknowns * args.steps / wall,
         "unit": "unknowns/s",
         "ms_per_step": ms_step,
         "dtype": "f64",
         "config": config,
-        "roofline": {"bound": "alu", "kernel": "k_hyper_resident<64,16>",
+        "timing": timing,
+        "roofline": {"bound": "alu", "kernel": "k_hyper_resident<64,16," +
+                     {"hyperdiffusion": "0", "hyperdiffusion_theta": "1",
+                      "cahn_hilliard": "2"}[kind] + ">",
                      "achieved": achieved, "peak": FP64_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP64_VALU_PEAK_TFLOPS,
-                     "traffic": _traffic({"hyperdiffusion": "hyperdiffusion",
-                                          "hyperdiffusion_theta": "hyperdiffusion_theta",
-                                          "cahn_hilliard": "cahn_hilliard"}[kind]),
-                     "kernel_ms": kern_ms, "setup_ms": statistics.median(setup),
-                     "flops_per_unknown_step": flops_per,
-                     "flops_per_launch": alg_flops, "hbm_bytes_per_launch": hbm_bytes,
-                     "effective_gbs_16B_per_unknown_step": 16.0 * unknowns / (kern_ms * 1e-3) / 1e9},
+                     "frac": achieved / FP64_VALU_PEAK_TFLOPS, "traffic": traffic,
+                     "kernel_ms": kern_ms, "timed": timed,
+                     "flops_per_unknown_step": flops_per, "flops_per_launch": alg_flops,
+                     "hbm": {"algorithmic_bytes_per_launch": hbm_bytes,
+                             "counter_bytes_per_launch": traffic,
+                             "achieved_gbs": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9,
+                             "frac_of_peak": None if traffic is None else
+                             traffic / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                     "model_gbs_if_state_streamed_every_step":
+                         16.0 * unknowns / (kern_ms * 1e-3) / 1e9},
     }
+    # parity on a sample of systems, outside the timed region: the call on
+    # the initial state against the oracle's trajectory (R12: relative to
+    # the norm of C0, <= 2e-9 after 100 steps)
+    import oracle
+    cols = np.unique(np.r_[0, batch - 1, np.random.default_rng(11).integers(0, batch, 14)])
+    C.copy_(C0)
+    run()
+    torch.cuda.synchronize()
+    got = C[:, cols].cpu().numpy()
+    c0 = C0[:, cols].cpu().numpy()
+    if kind == "hyperdiffusion":
+        ref = oracle.hyperdiffusion(W.to_flat(c0), dt, dx, nsteps).T
+    elif kind == "hyperdiffusion_theta":
+        ref = oracle.hyperdiffusion_theta(W.to_flat(c0), dt, dx, theta, nsteps).T
+    else:
+        ref = oracle.cahn_hilliard(W.to_flat(c0), dt, dx, cfg["gamma"], cfg["mobility"], theta, nsteps).T
+    line["parity"] = {"systems_checked": int(len(cols)),
+                      "max_rel_err_vs_oracle": _max_col_err(got, ref, scale=c0),
+                      "norm": "||C_gpu - C_oracle|| / ||C0|| per system, after the call's "
+                              f"{nsteps} steps"}
     if not args.no_cpu_baseline:
-        import oracle
         if kind == "cahn_hilliard":
-            C0 = W.cahn_hilliard_quench(n, 2048, rng=np.random.default_rng(77))
+            Cs = W.cahn_hilliard_quench(n, 2048, rng=np.random.default_rng(77))
         else:
-            C0 = W.hyperdiffusion_random(n, 2048, rng=np.random.default_rng(77))
+            Cs = W.hyperdiffusion_random(n, 2048, rng=np.random.default_rng(77))
 
         def sample(k):
             reps = (k + 2047) // 2048
             for r in range(reps):
                 kk = min(2048, k - r * 2048)
-                x = W.to_flat(C0[:, :kk])
+                x = W.to_flat(Cs[:, :kk])
                 if kind == "hyperdiffusion":
                     oracle.hyperdiffusion(x, dt, dx, nsteps)
                 elif kind == "hyperdiffusion_theta":
@@ -297,8 +406,11 @@ def bench_penta(args, which=2):
     n, batch = cfg["n"], cfg["batch"]
     dt = torch.float32 if args.dtype == "f32" else torch.float64
     pb = W.penta_dominant(n, batch, cyclic=cyclic, rng=W.rng_for(which))
+    cols = np.unique(np.r_[0, batch - 1, np.random.default_rng(12).integers(0, batch, 62)])
+    sample_in = [v[:, cols].copy() for v in (*pb.diagonals, pb.f)]
     dg = [torch.as_tensor(v, device="cuda:0").to(dt) for v in pb.diagonals]
-    x = torch.as_tensor(pb.f, device="cuda:0").to(dt)
+    f0 = torch.as_tensor(pb.f, device="cuda:0").to(dt)
+    x = f0.clone()
     code = bps.BPS_F32 if dt == torch.float32 else bps.BPS_F64
     work = torch.empty(bps.bps_penta_work_bytes(n, batch, batch, code, cyclic=cyclic),
                        dtype=torch.uint8, device="cuda:0")
@@ -329,24 +441,37 @@ def bench_penta(args, which=2):
     es = 4 if dt == torch.float32 else 8
     unknowns = n * batch
     alg_bytes = 7.0 * es * unknowns                  # 5 diagonals + f in, x out
-    kern_ms = statistics.mean(per)
+    kern_ms = _stats(per)["median"]
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = None if args.split else _traffic(kname[2:] + ("_cyclic_" if cyclic else "_") + args.dtype)
     line = {
         "metric": f"unknowns solved/s ({args.dtype}), " +
                   ("periodic" if cyclic else "general") + " pentadiagonal factor+solve",
-        "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
+        "value": unknowns * args.steps / wall, "unit": "unknowns/s", "ms_per_step": ms_step,
         "dtype": args.dtype,
         "config": {"workload": cfg["name"], "n": n, "batch": batch, "coefficients": "per system",
                    "periodic": cyclic, "calls": "factor, then solve" if args.split else "fused"},
+        "timing": {"call_ms": _stats(per), "systems_per_s": batch * args.steps / wall},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if args.split else
-                     _traffic(kname[2:] + ("_cyclic_" if cyclic else "_") + args.dtype),
-                     "kernel_ms": kern_ms,
-                     "bytes_per_launch": alg_bytes},
+                     "traffic": traffic, "kernel_ms": kern_ms,
+                     "timed": "whole call" + (" (the chunked kernel, then the masked second pass)"
+                                              if cyclic and not args.split else ""),
+                     "bytes_per_launch": alg_bytes,
+                     "counter_gbs": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9},
     }
+    import oracle
+    x.copy_(f0)
+    step()
+    torch.cuda.synchronize()
+    got = x[:, cols].cpu().double().numpy()
+    rin = [v.astype(np.float32).astype(np.float64) if es == 4 else v for v in sample_in]
+    ref, _ = oracle.penta_solve(*(W.to_flat(v) for v in rin), cyclic=cyclic)
+    line["parity"] = {"systems_checked": int(len(cols)),
+                      "max_rel_err_vs_oracle": _max_col_err(got, W.to_interleaved(ref)),
+                      "norm": "||x_gpu - x_oracle|| / ||x_oracle|| per system (fp32: the fp64 "
+                              "oracle of the fp32-rounded inputs)"}
     if not args.no_cpu_baseline:
-        import oracle
         small = W.penta_dominant(n, 4096, cyclic=cyclic, rng=np.random.default_rng(5))
         fl = [W.to_flat(v) for v in (*small.diagonals, small.f)]
 
@@ -370,7 +495,10 @@ def bench_tri(args, which):
     n, batch = cfg["n"], cfg["batch"]
     dt = torch.float32 if args.dtype == "f32" else torch.float64
     tb = W.tri_dominant(n, batch)
+    cols = np.unique(np.r_[0, batch - 1, np.random.default_rng(13).integers(0, batch, 62)])
+    sample_in = [v[:, cols].copy() for v in (tb.a, tb.b, tb.c, tb.y)]
     a, b, c, y = (torch.as_tensor(v, device="cuda:0").to(dt) for v in (tb.a, tb.b, tb.c, tb.y))
+    y0 = y.clone()
     del tb
     code = bps.BPS_F32 if dt == torch.float32 else bps.BPS_F64
     work = torch.empty(bps.tri_work_bytes(n, batch, code), dtype=torch.uint8, device="cuda:0")
@@ -388,20 +516,32 @@ def bench_tri(args, which):
     es = 4 if dt == torch.float32 else 8
     unknowns = n * batch
     alg_bytes = 5.0 * es * unknowns                  # a, b, c, y in, u out
-    kern_ms = statistics.mean(per)
+    kern_ms = _stats(per)["median"]
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = _traffic(f"{kname[2:]}_n{n}_{args.dtype}")
     line = {
         "metric": f"unknowns solved/s ({args.dtype}), batched tridiagonal solve",
-        "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
+        "value": unknowns * args.steps / wall, "unit": "unknowns/s", "ms_per_step": ms_step,
         "dtype": args.dtype,
         "config": {"workload": cfg["name"], "n": n, "batch": batch, "coefficients": "per system"},
+        "timing": {"call_ms": _stats(per), "systems_per_s": batch * args.steps / wall},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": _traffic(f"{kname[2:]}_n{n}_{args.dtype}"), "kernel_ms": kern_ms,
-                     "bytes_per_launch": alg_bytes},
+                     "traffic": traffic, "kernel_ms": kern_ms, "timed": "whole call",
+                     "bytes_per_launch": alg_bytes,
+                     "counter_gbs": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9},
     }
+    import oracle
+    y.copy_(y0)
+    step()
+    torch.cuda.synchronize()
+    got = y[:, cols].cpu().double().numpy()
+    rin = [v.astype(np.float32).astype(np.float64) if es == 4 else v for v in sample_in]
+    ref, _ = oracle.thomas_solve(*(W.to_flat(v) for v in rin))
+    line["parity"] = {"systems_checked": int(len(cols)),
+                      "max_rel_err_vs_oracle": _max_col_err(got, W.to_interleaved(ref)),
+                      "norm": "||u_gpu - u_oracle|| / ||u_oracle|| per system"}
     if not args.no_cpu_baseline:
-        import oracle
         k0 = max(1, min(batch, (1 << 22) // n))
         small = W.tri_dominant(n, k0, rng=np.random.default_rng(9))
         fl = [W.to_flat(v) for v in (small.a, small.b, small.c, small.y)]
@@ -438,34 +578,60 @@ def _hines_common(args, multi, which=None):
         nsolve = 1
         stats = W.tree_stats(hm.parent)
     u, l, d, rhs = arrs
+    r0 = rhs.clone()
     work = torch.empty(bps.hines_work_bytes(plan), dtype=torch.uint8, device="cuda:0")
 
-    def step():
-        for _ in range(nsolve):          # rhs_{k+1} = V_k, d restored (kept constant)
-            bps.hines_solve_batch(plan, u, l, d, rhs, work)
-    wall, per = _time_loop(step, args.steps, args.warmup)
+    # one step: nsolve solves, rhs_{k+1} = V_k, d restored (kept constant);
+    # each solve is one segment, timed by its own events
+    solve = lambda: bps.hines_solve_batch(plan, u, l, d, rhs, work)
+    wall, per = _time_steps([solve] * nsolve, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
+    per_solve = [t for seg in per for t in seg]
     unknowns = plan.unknowns * nsolve
     per_unknown = 44.0 if multi else 40.0            # u, l, d, rhs in, V out (+ parent)
-    alg_bytes = per_unknown * unknowns
-    kern_ms = statistics.mean(per) / nsolve
-    achieved = per_unknown * plan.unknowns / (kern_ms * 1e-3) / 1e9
+    kern_ms = _stats(per_solve)["median"]
+    alg_bytes = per_unknown * plan.unknowns
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    kname = "k_hines_levels" if plan.uses_levels else ("k_hines_multi" if multi else "k_hines_mono_reg")
+    traffic = _traffic("hines_levels" if plan.uses_levels else ("hines_multi" if multi else "hines_mono"))
     line = {
         "metric": "unknowns solved/s (fp64), Hines " + ("multi" if multi else "mono"),
-        "value": unknowns / (ms_step * 1e-3), "unit": "unknowns/s", "ms_per_step": ms_step,
+        "value": unknowns * args.steps / wall, "unit": "unknowns/s", "ms_per_step": ms_step,
         "dtype": "f64",
         "config": {"workload": cfg["name"], "solves_per_step": nsolve, **stats},
-        "roofline": {"bound": "hbm", "kernel": "k_hines_levels" if plan.uses_levels else
-                     ("k_hines_multi" if multi else "k_hines_mono_reg"),
-                     "achieved": achieved,
+        "timing": {"solve_ms": _stats(per_solve), "systems_per_s": plan.batch * nsolve * args.steps / wall},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": _traffic("hines_levels" if plan.uses_levels else
-                                         ("hines_multi" if multi else "hines_mono")),
+                     "traffic": traffic,
                      "schedule": "levels" if plan.uses_levels else "one lane per neuron",
-                     "kernel_ms": kern_ms, "bytes_per_launch": alg_bytes / nsolve},
+                     "kernel_ms": kern_ms, "timed": "one solve call", "bytes_per_launch": alg_bytes,
+                     "counter_gbs": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9},
     }
+    import oracle
+    rhs.copy_(r0)
+    solve()
+    torch.cuda.synchronize()
+    errs = []
+    if multi:
+        flat = torch.empty(plan.unknowns, dtype=torch.float64, device="cuda:0")
+        bps.hines_unpack(plan, rhs, flat)
+        out = flat.cpu().numpy()
+        pick = np.unique(np.r_[0, mm.batch - 1, np.random.default_rng(14).integers(0, mm.batch, 30)])
+        for s_ in pick:
+            p_, u_, l_, d_, r_ = mm.neuron(s_)
+            V, _ = oracle.hines_solve(p_, u_, l_, d_, r_)
+            got = out[mm.offsets[s_]:mm.offsets[s_ + 1]]
+            errs.append(np.linalg.norm(got - V[0]) / np.linalg.norm(V[0]))
+    else:
+        cols = np.unique(np.r_[0, cfg["batch"] - 1,
+                               np.random.default_rng(14).integers(0, cfg["batch"], 62)])
+        got = rhs[:, cols].cpu().numpy()
+        V, _ = oracle.hines_solve(hm.parent, *(W.to_flat(v[:, cols]) for v in (hm.u, hm.l, hm.d, hm.rhs)))
+        errs.append(_max_col_err(got, W.to_interleaved(V)))
+        pick = cols
+    line["parity"] = {"systems_checked": int(len(pick)), "max_rel_err_vs_oracle": float(max(errs)),
+                      "norm": "||V_gpu - V_oracle|| / ||V_oracle|| per neuron, one solve"}
     if not args.no_cpu_baseline:
-        import oracle
         if multi:
             small = W.hines_multi(2048, cfg["nmin"], cfg["nmax"], rng=np.random.default_rng(9))
 
@@ -528,8 +694,6 @@ def main():
                     help="workloads 2, 9: time the separate factor and solve calls instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--cpu-threads", type=int, default=0,
-                    help="oracle threads for cpu_baseline (default: OpenMP's, i.e. all cores)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYFETCH", "COPYWRITE"),
@@ -541,8 +705,6 @@ def main():
     ap.add_argument("--pmc-calls-match", default=None,
                     help="sum the --pmc-match dispatches per call of this kernel")
     args = ap.parse_args()
-    global _CPU_THREADS
-    _CPU_THREADS = max(0, args.cpu_threads)
     if args.pmc_summary:
         pmc_summary(args)
         return

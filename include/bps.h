@@ -214,6 +214,24 @@ BPS_API bps_status hyperdiffusion_step(int dtype, int64_t n, int64_t batch, int6
                                double dt, double dx, const void *diagonals,
                                void *C, int64_t nsteps, void *work, void *stream);
 
+/* The two halves of hyperdiffusion_step, for the "Constant" use of [P]
+ * (the matrix factored once at the start, its factors reused by every
+ * solve): hyperdiffusion_factor writes the factors of the operator (with the
+ * quantities of the periodic reduction) into `work`; hyperdiffusion_solve
+ * advances C by nsteps steps with them.  hyperdiffusion_step is the factor
+ * call followed by the solve call with the same arguments.  The factors
+ * depend on dtype, n, dt, dx and diagonals only: every solve call must be
+ * given those exactly as the factor call was (they also select the solver),
+ * with any batch, ld and nsteps; `work` (hyperdiffusion_work_bytes(dtype, n,
+ * 1) bytes or more, device) is read, not written, by the solve, so one
+ * factorisation serves any number of solves, on any stream ordered after
+ * the factor call.  Checks as hyperdiffusion_step. */
+BPS_API bps_status hyperdiffusion_factor(int dtype, int64_t n, double dt, double dx,
+                                 const void *diagonals, void *work, void *stream);
+BPS_API bps_status hyperdiffusion_solve(int dtype, int64_t n, int64_t batch, int64_t ld,
+                                double dt, double dx, const void *diagonals, void *C,
+                                int64_t nsteps, const void *work, void *stream);
+
 /* Size of the per-GPU scratch array of hyperdiffusion_step_noalloc. */
 #define BPS_NOALLOC_SCRATCH_BYTES (2u * 1024u * 1024u)
 

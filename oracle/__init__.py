@@ -48,6 +48,13 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off"
           "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
 
+# The CPU-baseline timing build: the same source with the flags of a tuned
+# CPU build.  -march=native targets the host that compiles it, so it is built
+# on the machine that runs the timing (build_timing), never shipped.
+TIMING_CFLAGS = ["-O3", "-march=native", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                 "-ffp-contract=off", "-fno-fast-math"]
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liborc.so with gcc (plain -O2, no -march)."""
     if force or not os.path.exists(_LIB):
@@ -55,6 +62,27 @@ def build(force: bool = True) -> str:
         subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_timing(outdir: str) -> str:
+    """Compile oracle.c with TIMING_CFLAGS into outdir/liborc_timing.so."""
+    out = os.path.join(outdir, "liborc_timing.so")
+    subprocess.check_call(["gcc", *TIMING_CFLAGS, _SRC, "-o", out, "-lm"])
+    return out
+
+
+def use_library(path: str) -> None:
+    """Route every wrapper below through the build at `path` (the timing
+    build, or the checker's liborc.so again); the thread count set by
+    set_threads applies to the build loaded when it is called."""
+    global _LIB_ACTIVE, _lib
+    with _lock:
+        if _LIB_ACTIVE != path:
+            _lib = None
+        _LIB_ACTIVE = path
+
+
+_LIB_ACTIVE = _LIB
 
 
 _D = ctypes.POINTER(ctypes.c_double)
@@ -67,9 +95,10 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            if _LIB_ACTIVE == _LIB and (not os.path.exists(_LIB) or
+                                        os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
                 build()
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(_LIB_ACTIVE)
             lib.orc_set_threads.argtypes = [ctypes.c_int]
             lib.orc_set_threads.restype = ctypes.c_int
             lib.orc_penta_factor.argtypes = [_i64] + [_D] * 9

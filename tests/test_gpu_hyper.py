@@ -178,3 +178,32 @@ def test_32_chunk_trajectory():
     out = _step(C0, dt, dx, 30)
     ref = _oracle(C0, dt, dx, 30)
     assert _traj_err(out, ref, C0) <= 2e-9
+
+
+@pytest.mark.parametrize("n,dtype,explicit", [(1024, torch.float64, False), (256, torch.float64, False),
+                                              (100, torch.float64, False), (96, torch.float32, False),
+                                              (512, torch.float64, True), (4096, torch.float64, False)])
+def test_factor_once_solve_many(n, dtype, explicit):
+    """hyperdiffusion_factor once, then hyperdiffusion_solve three times (other
+    batch, ld and step counts, the factors reused): each equals
+    hyperdiffusion_step on the same input bit for bit."""
+    print(f"factor once n={n} {dtype} explicit={explicit}", flush=True)
+    rng = np.random.default_rng(n + 5)
+    dt, dx = 1e-6, 1.0 / n
+    code = bps.BPS_F64 if dtype == torch.float64 else bps.BPS_F32
+    dg = None
+    if explicit:
+        a, b, c, d, e = oracle.hyperdiffusion_diagonals(n, dt, dx)
+        dg = dev(np.concatenate([a[0] * np.ones(n), b[0] * np.ones(n), c[0] * np.ones(n),
+                                 d[0] * np.ones(n), e[0] * np.ones(n)]), dtype)
+    fac = buf(bps.hyperdiffusion_work_bytes(n, 1, code))
+    bps.hyperdiffusion_factor(n, dt, dx, fac, dg, dtype=code)
+    for batch, ld, nsteps in ((70, 70, 5), (33, 40, 1), (129, 130, 3)):
+        C0 = dev(rng.uniform(-1, 1, (n, ld)), dtype)
+        C = C0.clone()
+        bps.hyperdiffusion_solve(C, dt, dx, nsteps, fac, dg, batch=batch)
+        R = C0.clone()
+        bps.hyperdiffusion_step(R, dt, dx, nsteps, buf(bps.hyperdiffusion_work_bytes(n, batch, code)),
+                                dg, batch=batch)
+        np.testing.assert_array_equal(host(C), host(R))
+        np.testing.assert_array_equal(host(C)[:, batch:], host(C0)[:, batch:])
