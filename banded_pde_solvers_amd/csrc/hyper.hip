@@ -93,6 +93,10 @@ struct Dot2 {
 };
 
 constexpr int kResMaxP = 16;    // chunks per system supported by the resident kernel (and 32, 64)
+#ifndef BPS_RES_BATCH
+#define BPS_RES_BATCH 3
+#endif
+constexpr int kResBatch = BPS_RES_BATCH;   // coefficient rows per scalar-load batch
 // A wavefront of the resident kernel holds 64 / P systems times P chunks and
 // exchanges interface values only among its own lanes, so the waves never
 // wait on one another: the ones sharing a SIMD hide each other's latencies.
@@ -142,8 +146,8 @@ __device__ __forceinline__ double row_rotate(double v)
 {
     static_assert(ROR >= 1 && ROR <= 15, "row rotation by 1 .. 15 lanes");
     const long long b = __double_as_longlong(v);
-    const int lo = __builtin_amdgcn_update_dpp(0, int(b & 0xffffffffll), 0x120 + ROR, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, int(b >> 32), 0x120 + ROR, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_mov_dpp(int(b & 0xffffffffll), 0x120 + ROR, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(int(b >> 32), 0x120 + ROR, 0xF, 0xF, false);
     return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
 }
 
@@ -516,8 +520,9 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
         // their size, is what the waits cost (two 32-byte loads per batch
         // measured 7% slower over the whole solve).
         typedef const __attribute__((address_space(4))) double cdouble;
-        constexpr int KB = 2;
-        static_assert(m % KB == 0, "rows per chunk interior must be a multiple of the batch");
+        // KB rows per batch (the last batch may be shorter): a lone wave per
+        // SIMD stalls at every wait, so fewer, larger batches keep it issuing
+        constexpr int KB = kResBatch, NB = (m + KB - 1) / KB;
         const double *cg = coef;
         asm volatile("" : "+s"(cg));
         cdouble *cf = (cdouble *)cg;
@@ -525,28 +530,31 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
 #pragma unroll
         for (int r = 0; r < KB; ++r)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) cb[0][r][q] = cf[4 * r + q];
+            for (int q = 0; q < 4; ++q) cb[0][r][q] = r < m ? cf[4 * r + q] : 0.0;
         // forward: g = L^{-1} f_interior, and y_0, y_1 = w . g
         double t0 = 0.0, t1 = 0.0;
 #pragma unroll
-        for (int k = 0; k < m / KB; ++k) {
+        for (int k = 0; k < NB; ++k) {
             const int cur = k & 1;
 #pragma unroll
             for (int r = 0; r < KB; ++r)
+                if (k * KB + r < m)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) asm volatile("" ::"s"(cb[cur][r][q]));
+                    for (int q = 0; q < 4; ++q) asm volatile("" ::"s"(cb[cur][r][q]));
             asm volatile("" : "+s"(cg));
             cf = (cdouble *)cg;
-            if (k + 1 < m / KB) {
+            if (k + 1 < NB) {
 #pragma unroll
                 for (int r = 0; r < KB; ++r)
+                    if ((k + 1) * KB + r < m)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) cb[cur ^ 1][r][q] = cf[4 * ((k + 1) * KB + r) + q];
+                        for (int q = 0; q < 4; ++q) cb[cur ^ 1][r][q] = cf[4 * ((k + 1) * KB + r) + q];
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < KB; ++r) {
                 const int i = k * KB + r;
+                if (i >= m) break;
                 const double *c4 = cb[cur][r];     // [1/alpha, beta, w0, w1]
                 double g = x[i];
                 if constexpr (LIN) {
@@ -673,28 +681,31 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
 #pragma unroll
         for (int r = 0; r < KB; ++r)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) cb[0][r][q] = cf[4 * m + 4 * (m - 1 - r) + q];
+            for (int q = 0; q < 4; ++q) cb[0][r][q] = r < m ? cf[4 * m + 4 * (m - 1 - r) + q] : 0.0;
         x[m - 2] -= URa * r0;
         x[m - 1] -= URb * r0 + URc * r1;
 #pragma unroll
-        for (int k = 0; k < m / KB; ++k) {
+        for (int k = 0; k < NB; ++k) {
             const int cur = k & 1;
 #pragma unroll
             for (int r = 0; r < KB; ++r)
+                if (k * KB + r < m)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) asm volatile("" ::"s"(cb[cur][r][q]));
+                    for (int q = 0; q < 4; ++q) asm volatile("" ::"s"(cb[cur][r][q]));
             asm volatile("" : "+s"(cg));
             cf = (cdouble *)cg;
-            if (k + 1 < m / KB) {
+            if (k + 1 < NB) {
 #pragma unroll
                 for (int r = 0; r < KB; ++r)
+                    if ((k + 1) * KB + r < m)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        cb[cur ^ 1][r][q] = cf[4 * m + 4 * (m - 1 - (k + 1) * KB - r) + q];
+                        for (int q = 0; q < 4; ++q)
+                            cb[cur ^ 1][r][q] = cf[4 * m + 4 * (m - 1 - (k + 1) * KB - r) + q];
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < KB; ++r) {
+                if (k * KB + r >= m) break;
                 const int i = m - 1 - (k * KB + r);
                 const double *c4 = cb[cur][r];     // [gamma, delta, UL0, UL1]
                 double v = x[i] - c4[2] * l0 - c4[3] * l1;

@@ -116,7 +116,7 @@ template <> struct Pair2<float> { using type = float2; };
 // permutation 1, 0, 3, 2: a VALU move, no LDS).
 __device__ __forceinline__ int pair_swap(int v)
 {
-    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
 }
 __device__ __forceinline__ float pair_swap(float v)
 {
