@@ -41,6 +41,8 @@ struct bps_hines_plan {
     int32_t max_rows = 0;    // multi: largest block row count
     // device arrays
     int32_t *parent = nullptr;     // mono [n]; multi packed [elems]
+    uint8_t *dist8 = nullptr;      // multi packed [elems]: i - p_i (0 for roots and padding),
+                                   // when every parent is within kRing rows
     int64_t *blk_off = nullptr;    // multi [nblocks]
     int32_t *blk_rows = nullptr;   // multi [nblocks]
     int32_t *lane_n = nullptr;     // multi [nblocks*64]
@@ -74,6 +76,7 @@ struct HinesArgs {
     const int64_t *blk_off;          // multi geometry
     const int32_t *blk_rows, *lane_n, *lane_src;
     const int32_t *parent;
+    const uint8_t *dist8;
     const double *u, *l, *d;
     double *rhs, *mwork, *gd, *gr;
     int32_t *info;
@@ -333,6 +336,9 @@ struct BlockBuf {
     __device__ int32_t ldi(uint32_t lane_off, uint32_t row_off) const {
         return int32_t(__builtin_amdgcn_raw_buffer_load_b32(r, lane_off, row_off, 0));
     }
+    __device__ int32_t ldb(uint32_t lane_off, uint32_t row_off) const {
+        return int32_t(__builtin_amdgcn_raw_buffer_load_b8(r, lane_off, row_off, 0));
+    }
     __device__ void st(double v, uint32_t lane_off, uint32_t row_off) const {
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, lane_off, row_off, 0);
@@ -363,21 +369,23 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     const uint32_t nbytes = uint32_t(rows) * kWave * 8u;
     const BlockBuf U(A.u + off, nbytes), L(A.l + off, nbytes), Dg(A.d + off, nbytes);
     const BlockBuf R(A.rhs + off, nbytes), MW(A.mwork + off, nbytes);
-    const BlockBuf PA(A.parent + off, nbytes / 2);
-    const uint32_t lo8 = uint32_t(k) * 8u, lo4 = uint32_t(k) * 4u;   // lane byte offsets
+    // parents as one-byte distances i - p_i (the window holds them): a
+    // quarter of the bytes of int32 indices in both sweeps
+    const BlockBuf PD(A.dist8 + off, nbytes / 8);
+    const uint32_t lo8 = uint32_t(k) * 8u, lo1 = uint32_t(k);   // lane byte offsets
     // row byte offsets (scalar: a buffer access takes its row offset from an SGPR)
     auto rb8 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * (kWave * 8u)); };
-    auto rb4 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * (kWave * 4u)); };
+    auto rb1 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * uint32_t(kWave)); };
 #pragma unroll
     for (int j = 0; j < kRing; ++j) ring[j][k] = make_double2(0.0, 0.0);
     int32_t bad = 0;
 
     // ---- leaves -> root ----
-    struct BRow { double u, l, d, r; int32_t p; };
+    struct BRow { double u, l, d, r; int32_t p; };   // p: distance to the parent
     auto load_b = [&](BRow &q, int32_t r) {
         const int32_t rc = r >= 1 ? r : 1 < rows ? 1 : 0;
         q.u = U.ld(lo8, rb8(rc)); q.l = L.ld(lo8, rb8(rc)); q.d = Dg.ld(lo8, rb8(rc));
-        q.r = R.ld(lo8, rb8(rc)); q.p = PA.ldi(lo4, rb4(rc));
+        q.r = R.ld(lo8, rb8(rc)); q.p = PD.ldb(lo1, rb1(rc));
     };
     auto elim = [&](int32_t i, const BRow &q) {
         const bool live = i < my_n;
@@ -391,7 +399,7 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
         const double fac = live ? q.u * rcp : 0.0;  // factor of Algorithm 1
         R.st(live ? rr * rcp : q.r, lo8, rb8(i));   // q_i (padding unchanged)
         MW.st(live ? q.l * rcp : 0.0, lo8, rb8(i)); // m_i
-        const int ps = q.p & (kRing - 1);
+        const int ps = (i - q.p) & (kRing - 1);
         unsafeAtomicAdd(&ring[ps][k].x, fac * q.l);
         unsafeAtomicAdd(&ring[ps][k].y, fac * rr);
     };
@@ -438,15 +446,15 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     // parent one row up comes from a register ----
     ring[0][k].x = v0;
     double vprev = v0;
-    struct FRow { double q, m; int32_t p; };
+    struct FRow { double q, m; int32_t p; };         // p: distance to the parent
     auto load_f = [&](FRow &f, int32_t r) {
         const int32_t rc = r < rows ? r : rows - 1;
-        f.q = R.ld(lo8, rb8(rc)); f.m = MW.ld(lo8, rb8(rc)); f.p = PA.ldi(lo4, rb4(rc));
+        f.q = R.ld(lo8, rb8(rc)); f.m = MW.ld(lo8, rb8(rc)); f.p = PD.ldb(lo1, rb1(rc));
     };
     auto subst = [&](int32_t i, const FRow &f) {
         const bool live = i < my_n;
-        const double vr = ring[f.p & (kRing - 1)][k].x;
-        const double vp = (i - f.p == 1) ? vprev : vr;
+        const double vr = ring[(i - f.p) & (kRing - 1)][k].x;
+        const double vp = (f.p == 1) ? vprev : vr;
         const double v = f.q - f.m * vp;
         R.st(live ? v : f.q, lo8, rb8(i));
         ring[i & (kRing - 1)][k].x = v;
@@ -709,7 +717,8 @@ static bps_status upload(T **dptr, const std::vector<T> &h)
 static void free_plan(bps_hines_plan *p)
 {
     if (!p) return;
-    (void)hipFree(p->parent); (void)hipFree(p->blk_off); (void)hipFree(p->blk_rows);
+    (void)hipFree(p->parent); (void)hipFree(p->dist8); (void)hipFree(p->blk_off);
+    (void)hipFree(p->blk_rows);
     (void)hipFree(p->lane_n); (void)hipFree(p->lane_src); (void)hipFree(p->src_off);
     (void)hipFree(p->lv_perm); (void)hipFree(p->lv_sec); (void)hipFree(p->lv_spar);
     (void)hipFree(p->lv_lev); (void)hipFree(p->lv_tree);
@@ -809,6 +818,7 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         }
         P->elems = acc;
         std::vector<int32_t> pk(acc, 0);
+        std::vector<uint8_t> d8(acc, 0);
         for (int64_t b = 0; b < nb; ++b)
             for (int k = 0; k < kWave; ++k) {
                 const int32_t s = lsrc[b * kWave + k];
@@ -816,10 +826,12 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
                 for (int32_t i = 1; i < sizes[s]; ++i) {
                     const int32_t p = parent[off[s] + i];
                     pk[boff[b] + int64_t(i) * kWave + k] = p;
+                    d8[boff[b] + int64_t(i) * kWave + k] = uint8_t(std::min(i - p, 255));
                     P->max_dist = std::max<int32_t>(P->max_dist, i - p);
                 }
             }
-        if ((st = upload(&P->parent, pk)) == BPS_OK && (st = upload(&P->blk_off, boff)) == BPS_OK &&
+        if (P->max_dist <= kRing) st = upload(&P->dist8, d8);
+        if (st == BPS_OK && (st = upload(&P->parent, pk)) == BPS_OK && (st = upload(&P->blk_off, boff)) == BPS_OK &&
             (st = upload(&P->blk_rows, brows)) == BPS_OK && (st = upload(&P->lane_n, ln)) == BPS_OK &&
             (st = upload(&P->lane_src, lsrc)) == BPS_OK)
             st = upload(&P->src_off, off);
@@ -908,6 +920,7 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
     A.batch = P->batch; A.n = P->n; A.ld = P->ld;
     A.blk_off = P->blk_off; A.blk_rows = P->blk_rows; A.lane_n = P->lane_n; A.lane_src = P->lane_src;
     A.parent = P->parent;
+    A.dist8 = P->dist8;
     A.u = (const double *)u; A.l = (const double *)l; A.d = (const double *)d;
     A.rhs = (double *)rhs;
     A.mwork = (double *)work;
