@@ -33,7 +33,8 @@ one thread, median of 3 runs each, CPU model and core counts stated).
     python bench.py [--steps K] [--warmup W] [--workload {1,...,10}]
 
 --workload selects another workload for manual measurements
-(2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
+(0: the small periodic case, N = 256, 64 systems, 10 steps from seeded Fourier
+modes -- latency-bound, reported for completeness; 2: general pentadiagonal 512 x 65536 factor+solve, --dtype f64|f32; 3: Hines mono
 512 x 100000; 4: Hines multi, 32768 neurons of 256..2048 compartments,
 20 solves per step; 5: the default shape time-stepped with Crank-Nicolson,
 theta = 1/2, 24 algorithmic flops per unknown per time step; 6: the same grid
@@ -265,6 +266,8 @@ def bench_hyperdiffusion(args, which=1):
     dev = "cuda:0"
     if kind == "cahn_hilliard":
         C0 = torch.as_tensor(W.cahn_hilliard_quench(n, batch), device=dev)
+    elif which == 0:
+        C0 = torch.as_tensor(W.hyperdiffusion_modes(n, batch).C0, device=dev)
     else:
         C0 = torch.as_tensor(W.hyperdiffusion_random(n, batch), device=dev)
     C = C0.clone()
@@ -306,8 +309,9 @@ def bench_hyperdiffusion(args, which=1):
     alg_flops = flops_per * unknowns
     achieved = alg_flops / (kern_ms * 1e-3) / 1e12
     hbm_bytes = 16.0 * n * batch                     # C read once, written once
+    # counter traffic was taken on the N = 1024 x 16384 workloads only
     traffic = _traffic({"hyperdiffusion": "hyperdiffusion", "hyperdiffusion_theta": "hyperdiffusion_theta",
-                        "cahn_hilliard": "cahn_hilliard"}[kind])
+                        "cahn_hilliard": "cahn_hilliard"}[kind]) if which in (1, 5, 6) else None
     label = {"hyperdiffusion": "periodic hyperdiffusion implicit steps",
              "hyperdiffusion_theta": "periodic hyperdiffusion Crank-Nicolson steps",
              "cahn_hilliard": "periodic Cahn-Hilliard semi-implicit steps"}[kind]
@@ -325,7 +329,7 @@ def bench_hyperdiffusion(args, which=1):
     if kind == "hyperdiffusion":
         timing["factor_ms"] = _stats(per[0])
         timing["solve_kernel_ms"] = _stats(kern)
-        timed = "k_hyper_resident<64,16,0> alone (HIP events around hyperdiffusion_solve)"
+        timed = f"k_hyper_resident<64,{n // 64},0> alone (HIP events around hyperdiffusion_solve)"
     else:
         timed = "whole call (set-up kernel included)"
     line = {
@@ -336,7 +340,7 @@ def bench_hyperdiffusion(args, which=1):
         "dtype": "f64",
         "config": config,
         "timing": timing,
-        "roofline": {"bound": "alu", "kernel": "k_hyper_resident<64,16," +
+        "roofline": {"bound": "alu", "kernel": f"k_hyper_resident<64,{n // 64}," +
                      {"hyperdiffusion": "0", "hyperdiffusion_theta": "1",
                       "cahn_hilliard": "2"}[kind] + ">",
                      "achieved": achieved, "peak": FP64_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -688,7 +692,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=list(range(1, 11)))
+    ap.add_argument("--workload", type=int, default=1, choices=list(range(0, 11)))
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
     ap.add_argument("--split", action="store_true",
                     help="workloads 2, 9: time the separate factor and solve calls instead")
@@ -724,7 +728,7 @@ def main():
         return
     import banded_pde_solvers_amd as bps
     bps.load_library()
-    fn = {1: bench_hyperdiffusion, 2: bench_penta, 3: lambda a: _hines_common(a, False),
+    fn = {0: lambda a: bench_hyperdiffusion(a, 0), 1: bench_hyperdiffusion, 2: bench_penta, 3: lambda a: _hines_common(a, False),
           4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5),
           6: lambda a: bench_hyperdiffusion(a, 6), 7: lambda a: bench_tri(a, 7),
           8: lambda a: bench_tri(a, 8), 9: lambda a: bench_penta(a, 9),
