@@ -28,9 +28,9 @@ part gives the state's algorithmic bytes per launch and the measured
 counter bytes over the kernel time) and a "cpu_baseline" object (the
 oracle, built with gcc -O3 -march=native -fopenmp on this host, timed on a
 bounded sample of the same workload with all of this host's cores and with
-one thread, median of 3 runs each, CPU model and core counts stated).
+one thread, median of 5 runs each, CPU model and core counts stated).
 
-    python bench.py [--steps K] [--warmup W] [--workload {1,...,10}]
+    python bench.py [--steps K] [--warmup W] [--workload {0,...,10}]
 
 --workload selects another workload for manual measurements
 (0: the small periodic case, N = 256, 64 systems, 10 steps from seeded Fourier
@@ -202,8 +202,8 @@ def _cpu_model():
 def _cpu_baseline(run_sample, unknowns_per_system, label, seconds):
     """The oracle as it stands, timed on this host: built here with gcc -O3
     -march=native -fopenmp (oracle.TIMING_CFLAGS), run on a sample of the
-    workload sized so that one run takes about seconds / 8, three runs with
-    all the threads OpenMP gives it and three with one thread, medians
+    workload sized so that one run takes about seconds / 12, five runs with
+    all the threads OpenMP gives it and five with one thread, medians
     reported (about `seconds` of CPU work in all)."""
     import tempfile
     import oracle
@@ -219,9 +219,9 @@ def _cpu_baseline(run_sample, unknowns_per_system, label, seconds):
             if t >= seconds / 40 or k >= 1 << 20:
                 break
             k = int(k * min(16.0, max(2.0, seconds / 40 / max(t, 1e-4))))
-        k = max(1, int(k * seconds / 8 / max(t, 1e-6)))
+        k = max(1, int(k * seconds / 12 / max(t, 1e-6)))
         runs = []
-        for _ in range(3):
+        for _ in range(5):
             t0 = time.perf_counter()
             run_sample(k)
             runs.append(time.perf_counter() - t0)
@@ -230,10 +230,10 @@ def _cpu_baseline(run_sample, unknowns_per_system, label, seconds):
                      "threads": used, "sample": f"{k} {label}", "runs_s": [round(r, 3) for r in runs]}
     a = legs["all"]
     return {"value": a["value"], "unit": "unknowns/s", "cores": a["threads"], "kind": "oracle",
-            "sample": f"{a['sample']}, median of 3 runs of {statistics.median(a['runs_s']):.2f} s",
+            "sample": f"{a['sample']}, median of 5 runs of {statistics.median(a['runs_s']):.2f} s",
             "systems_per_s": a["systems_per_s"],
             "one_thread": {"value": legs["one"]["value"], "systems_per_s": legs["one"]["systems_per_s"],
-                           "sample": f"{legs['one']['sample']}, median of 3 runs",
+                           "sample": f"{legs['one']['sample']}, median of 5 runs",
                            "runs_s": legs["one"]["runs_s"]},
             "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
             "affinity": len(os.sched_getaffinity(0)),
