@@ -371,10 +371,20 @@ def bench_hyperdiffusion(args, which=1):
         ref = oracle.hyperdiffusion_theta(W.to_flat(c0), dt, dx, theta, nsteps).T
     else:
         ref = oracle.cahn_hilliard(W.to_flat(c0), dt, dx, cfg["gamma"], cfg["mobility"], theta, nsteps).T
-    line["parity"] = {"systems_checked": int(len(cols)),
-                      "max_rel_err_vs_oracle": _max_col_err(got, ref, scale=c0),
-                      "norm": "||C_gpu - C_oracle|| / ||C0|| per system, after the call's "
-                              f"{nsteps} steps"}
+    par = {"systems_checked": int(len(cols)),
+           "max_rel_err_vs_oracle": _max_col_err(got, ref, scale=c0),
+           "norm": "||C_gpu - C_oracle|| / ||C0|| per system, after the call's "
+                   f"{nsteps} steps"}
+    if kind == "hyperdiffusion":
+        # one implicit step (one solve per system) with the same factors: the
+        # per-solve error, relative to the oracle's solution
+        C.copy_(C0)
+        bps.hyperdiffusion_solve(C, dt, dx, 1, work)
+        torch.cuda.synchronize()
+        ref1 = oracle.hyperdiffusion(W.to_flat(c0), dt, dx, 1).T
+        par["per_solve_max_rel_err_vs_oracle"] = _max_col_err(C[:, cols].cpu().numpy(), ref1)
+        par["per_solve_norm"] = "||x_gpu - x_oracle|| / ||x_oracle|| per system, one step"
+    line["parity"] = par
     if not args.no_cpu_baseline:
         if kind == "cahn_hilliard":
             Cs = W.cahn_hilliard_quench(n, 2048, rng=np.random.default_rng(77))
