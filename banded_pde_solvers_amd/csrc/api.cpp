@@ -2,6 +2,7 @@
 // the host, then kernel launches on the caller's stream.
 #include <cmath>
 #include <cstring>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -32,10 +33,21 @@ static __device__ __align__(256) unsigned char scratch[BPS_NOALLOC_SCRATCH_BYTES
 
 bps_status prepare_device(void **scratch_dev)
 {
+    // after a device's first call: one atomic load, no lock (devices past
+    // kFastDevices take the locked path every time)
+    constexpr int kFastDevices = 64;
+    static std::atomic<void *> ready[kFastDevices];
     static std::mutex mu;
     static std::map<int, void *> done;     // device -> address of its scratch
     int dev = 0;
     BPS_HIP(hipGetDevice(&dev));
+    if (dev >= 0 && dev < kFastDevices) {
+        void *ptr = ready[dev].load(std::memory_order_acquire);
+        if (ptr) {
+            if (scratch_dev) *scratch_dev = ptr;
+            return BPS_OK;
+        }
+    }
     std::lock_guard<std::mutex> lock(mu);
     auto it = done.find(dev);
     if (it == done.end()) {
@@ -45,6 +57,7 @@ bps_status prepare_device(void **scratch_dev)
         BPS_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
         if (!ptr) BPS_FAIL(BPS_EHIP, "hipGetSymbolAddress gave no address for the scratch array");
         it = done.emplace(dev, ptr).first;
+        if (dev >= 0 && dev < kFastDevices) ready[dev].store(ptr, std::memory_order_release);
     }
     if (scratch_dev) *scratch_dev = it->second;
     return BPS_OK;
