@@ -213,3 +213,35 @@ def test_binding_has_every_declared_entry_point():
     assert not missing, missing
     assert bps.bps_status_str(1).startswith("BPS_EINVAL")
     assert bps.bps_version() == bps.version()
+
+
+def test_hyperdiffusion_factor_solve_and_noalloc_reject_bad_arguments(lib):
+    """The two halves of hyperdiffusion_step and its allocation-free variant
+    validate like the step itself; the allocation-free call rejects sizes
+    whose work exceeds its scratch array before touching the device."""
+    fa, so, na = lib.hyperdiffusion_factor, lib.hyperdiffusion_solve, lib.hyperdiffusion_step_noalloc
+    assert fa(2, 5, 1e-6, 0.1, None, _fake(), None) == EINVAL            # n < 6
+    assert fa(2, 16, 1e-6, 0.0, None, _fake(), None) == EINVAL           # dx = 0
+    assert fa(2, 16, float("inf"), 0.1, None, _fake(), None) == EINVAL
+    assert fa(2, 16, 1e-6, 0.1, None, None, None) == EINVAL              # work
+    assert fa(3, 16, 1e-6, 0.1, None, _fake(), None) == EINVAL           # dtype
+    assert fa(2, 16, 1e-6, 0.1, ctypes.c_void_p(4096 + 4), _fake(), None) == EINVAL
+    assert so(2, 16, 4, 3, 1e-6, 0.1, None, _fake(), 1, _fake(1), None) == EINVAL   # ld
+    assert so(2, 16, 4, 4, 1e-6, 0.1, None, _fake(), -2, _fake(1), None) == EINVAL  # nsteps
+    assert so(2, 16, 4, 4, 1e-6, 0.1, None, _fake(), 1, None, None) == EINVAL       # work
+    assert so(2, 16, 4, 4, 1e-6, 0.1, None, None, 1, _fake(1), None) == EINVAL      # C
+    assert na(2, 5, 4, 4, 1e-6, 0.1, None, _fake(), 1, None) == EINVAL              # n < 6
+    assert na(2, 16, 4, 4, 1e-6, 0.1, None, None, 1, None) == EINVAL                # C
+    for dtype, n in ((2, 18726), (1, 37451)):
+        assert na(dtype, n, 2, 2, 1e-6, 1.0 / n, None, _fake(), 1, None) == EINVAL
+        assert b"scratch" in lib.bps_last_error()
+    # the largest sizes fit the array
+    assert bps.hyperdiffusion_work_bytes(18725, 1, 2) <= bps.BPS_NOALLOC_SCRATCH_BYTES
+    assert bps.hyperdiffusion_work_bytes(37450, 1, 1) <= bps.BPS_NOALLOC_SCRATCH_BYTES
+    assert bps.hyperdiffusion_work_bytes(18726, 1, 2) > bps.BPS_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define BPS_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", text)
+    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == bps.BPS_NOALLOC_SCRATCH_BYTES
