@@ -151,6 +151,25 @@ __device__ __forceinline__ double row_rotate(double v)
     return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
 }
 
+// Backward sweep x = R^{-1} src of the set-up (R unit upper with gamma,
+// delta), into dst; the arrays are distinct, so the LDS reads of later rows
+// may be issued ahead of the stores of earlier ones.
+template <int m>
+__device__ __forceinline__ void setup_back_sweep(const double *__restrict__ src,
+                                                 const double *__restrict__ ga,
+                                                 const double *__restrict__ de,
+                                                 double *__restrict__ dst)
+{
+#pragma clang fp contract(fast)
+    double q1 = 0.0, q2 = 0.0;
+#pragma unroll
+    for (int i = m - 1; i >= 0; --i) {
+        const double x = src[i] - ga[i] * q1 - de[i] * q2;
+        dst[i] = x;
+        q2 = q1; q1 = x;
+    }
+}
+
 // One wavefront.  The serial recurrences run in every lane at once (lane t
 // carries coupling vector t & 7) with the running values in registers, and
 // their loops are unrolled so that the LDS reads they need are issued ahead
@@ -175,14 +194,17 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
     auto CL = [&](int k, int i) { return k == 0 ? (i == 0 ? a : 0.0) : (i == 0 ? b : i == 1 ? a : 0.0); };
     auto CR = [&](int k, int i) { return k == 0 ? (i == m - 2 ? e : i == m - 1 ? d : 0.0)
                                                 : (i == m - 1 ? e : 0.0); };
-    // lane t < 8 builds coupling vector t (lanes 8.. repeat lane t & 7 and
-    // store nothing):
+    // lane t builds coupling vector t & 7 (lanes t and t & 7 compute and
+    // store equal values):
     //   0,1  U_L = L^{-1} C_L      2,3  w_k = R^{-T} e_k
     //   4,5  Z_L = E^{-1} C_L      6,7  Z_R = E^{-1} C_R
     const int role = t & 7, k = role & 1;
     const bool is_w = (role == 2 || role == 3), is_z = role >= 4, use_cr = role >= 6;
-    const bool keeper = t < 8;
     double *my = vec[role];
+    // the forward results of Z_L, Z_R go to `tmpz` (the backward sweep then
+    // reads and writes different arrays)
+    __shared__ double tmpz[4][m], dump[m];
+    double *fw_out = is_z ? tmpz[role - 4] : my;
     // the right-hand side of lane t is nonzero in rows 0, 1, m-2, m-1 only
     const double rh0 = is_w ? (k == 0 ? 1.0 : 0.0) : use_cr ? CR(k, 0) : CL(k, 0);
     const double rh1 = is_w ? (k == 1 ? 1.0 : 0.0) : use_cr ? CR(k, 1) : CL(k, 1);
@@ -198,60 +220,69 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
         for (int i = 0; i < m; ++i) {
             const double beta = Eb(i) - Ea(i) * g2;
             const double alpha = c - Ea(i) * d2 - beta * g1;
-            const double r = 1.0 / alpha;
+            // 1/alpha: hardware estimate and two Newton steps, five
+            // instructions on the recurrence's critical path where the
+            // correctly rounded quotient takes eleven.  alpha, a pivot of the
+            // SPD interior block (not below I), lies in [1, 1 + 6 sigma], so
+            // no scaling is needed; the result is within an ulp of 1/alpha
+            double r = __builtin_amdgcn_rcp(alpha);
+            r = fma(fma(-alpha, r, 1.0), r, r);
+            r = fma(fma(-alpha, r, 1.0), r, r);
             const double gam = (Ed(i) - beta * d1) * r, del = Ee(i) * r;
-            if (t == 0) { ra[i] = r; be[i] = beta; ga[i] = gam; de[i] = del; }
+            // every lane stores (the lanes hold equal values): no branch in
+            // the unrolled sweep, so its LDS traffic overlaps the recurrence
+            ra[i] = r; be[i] = beta; ga[i] = gam; de[i] = del;
             // L^{-1} rhs, or R^{-T} e_k (R^T is unit lower with gamma, delta)
             const double rhs = i == 0 ? rh0 : i == 1 ? rh1 : i == m - 2 ? rhA : i == m - 1 ? rhB : 0.0;
             const double lv = (rhs - Ea(i) * p2 - beta * p1) * r;
             const double wv = rhs - (i >= 1 ? g1 : 0.0) * p1 - (i >= 2 ? d2 : 0.0) * p2;
             const double x = is_w ? wv : lv;
-            if (keeper) my[i] = x;
+            fw_out[i] = x;                  // lanes t and t & 7 store equal values
             p2 = p1; p1 = x;
             g2 = g1; g1 = gam; d2 = d1; d1 = del;
         }
     }
     __syncthreads();
-    // ---- Z = R^{-1} U for lanes 4..7 ----
-    {
-#pragma clang fp contract(fast)
-        double q1 = 0.0, q2 = 0.0;
-#pragma unroll 8
-        for (int i = m - 1; i >= 0; --i) {
-            const double x = my[i] - ga[i] * q1 - de[i] * q2;
-            if (keeper && is_z) my[i] = x;
-            q2 = q1; q1 = x;
-        }
-    }
+    // ---- Z = R^{-1} U for lanes 4..7 (the other lanes store into `dump`,
+    // so that the unrolled sweep has no branch) ----
+    setup_back_sweep<m>(fw_out, ga, de, is_z ? my : dump);
     __syncthreads();
-    // ---- one refinement step of Z: residual C - E Z with compensated sums ----
-    for (int idx = t; idx < 4 * m; idx += blockDim.x) {
+    // ---- one refinement step of Z: residual C - E Z with compensated sums
+    // (4m entries over the wavefront's lanes; past the end a lane repeats
+    // the last entry and stores it into `dump`) ----
+    constexpr int kResid = (4 * m + kWave - 1) / kWave;
+#pragma unroll
+    for (int it = 0; it < kResid; ++it) {
+        const int idx0 = t + kWave * it, idx = idx0 < 4 * m ? idx0 : 4 * m - 1;
         const int kk = idx / m, i = idx % m;
         const double *z = vec[4 + kk];
+        // terms outside the block have a zero coefficient (an exact zero
+        // product leaves the compensated sum unchanged), their index clamped
         Dot2 acc;
         acc.add(kk < 2 ? CL(kk & 1, i) : CR(kk & 1, i), 1.0);
-        if (i >= 2) acc.add(-Ea(i), z[i - 2]);
-        if (i >= 1) acc.add(-Eb(i), z[i - 1]);
+        acc.add(-Ea(i), z[i >= 2 ? i - 2 : 0]);
+        acc.add(-Eb(i), z[i >= 1 ? i - 1 : 0]);
         acc.add(-c, z[i]);
-        if (i + 1 < m) acc.add(-Ed(i), z[i + 1]);
-        if (i + 2 < m) acc.add(-Ee(i), z[i + 2]);
-        res[kk][i] = acc.value();
+        acc.add(-Ed(i), z[i + 1 < m ? i + 1 : m - 1]);
+        acc.add(-Ee(i), z[i + 2 < m ? i + 2 : m - 1]);
+        (idx0 < 4 * m ? &res[kk][i] : &dump[0])[0] = acc.value();
     }
     __syncthreads();
     if (t < 4) {
 #pragma clang fp contract(fast)
-        // lanes 0..3 solve E dz = residual in place and correct Z
-        double *rv = res[t];
+        // lanes 0..3 solve E dz = residual (g in registers) and correct Z
+        const double *rv = res[t];
+        double gv[m];
         double p1 = 0.0, p2 = 0.0;
-#pragma unroll 8
+#pragma unroll
         for (int i = 0; i < m; ++i) {
             const double g = (rv[i] - Ea(i) * p2 - be[i] * p1) * ra[i];
-            rv[i] = g; p2 = p1; p1 = g;
+            gv[i] = g; p2 = p1; p1 = g;
         }
         double q1 = 0.0, q2 = 0.0;
-#pragma unroll 8
+#pragma unroll
         for (int i = m - 1; i >= 0; --i) {
-            const double x = rv[i] - ga[i] * q1 - de[i] * q2;
+            const double x = gv[i] - ga[i] * q1 - de[i] * q2;
             vec[4 + t][i] += x; q2 = q1; q1 = x;
         }
     }
@@ -324,7 +355,9 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
             pc[0] = Mi.a; pc[1] = Mi.b; pc[2] = Mi.c; pc[3] = Mi.d;
         }
         __syncthreads();
-        for (int i = t; i < 52; i += blockDim.x) coef[8 * m + 8 + 4 * P + i] = pcr[i];
+        // 8 log2 P + 4 of the 52 entries are set; the rest are written as 0
+        constexpr int npcr = 8 * (P >= 64 ? 6 : P >= 32 ? 5 : P >= 16 ? 4 : P >= 8 ? 3 : P >= 4 ? 2 : 1) + 4;
+        for (int i = t; i < 52; i += blockDim.x) coef[8 * m + 8 + 4 * P + i] = i < npcr ? pcr[i] : 0.0;
     }
     // ---- other powers of two: T_q, the first block row of S^{-1}, by the
     // same reduction applied to the block column E_0 = [I; 0; ...; 0]
