@@ -33,8 +33,9 @@ __all__ = [
     "tri_work_bytes", "tri_solve_batch",
     "HinesPlan", "hines_plan_create", "hines_plan_destroy", "hines_pack", "hines_unpack",
     "hines_work_bytes", "hines_solve_batch", "BPS_HINES_AUTO", "BPS_HINES_LANES",
-    "BPS_HINES_LEVELS", "hines_plan_create_sched", "hines_plan_elems", "hines_plan_unknowns",
-    "hines_plan_uses_levels", "bps_version", "bps_init", "bps_status_str", "bps_last_error", "PentaDesc",
+    "BPS_HINES_LEVELS", "BPS_HINES_SPLIT", "hines_plan_create_sched", "hines_plan_elems",
+    "hines_plan_unknowns", "hines_plan_uses_levels", "hines_plan_split", "hines_split_schedule",
+    "bps_version", "bps_init", "bps_status_str", "bps_last_error", "PentaDesc",
 ]
 
 BPS_F32 = 1
@@ -44,6 +45,7 @@ BPS_SHARED_COEF = 0x2
 BPS_HINES_AUTO = 0
 BPS_HINES_LANES = 1
 BPS_HINES_LEVELS = 2
+BPS_HINES_SPLIT = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "libbps.so")
@@ -115,6 +117,9 @@ def load_library():
             "hines_plan_create": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64], st),
             "hines_plan_create_sched": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64, st], st),
             "hines_plan_uses_levels": ([vp], st),
+            "hines_plan_split": ([vp], i64),
+            "hines_split_schedule": ([ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_int32],
+                                     ctypes.c_int32),
             "hines_plan_destroy": ([vp], st),
             "hines_plan_elems": ([vp], i64),
             "hines_plan_unknowns": ([vp], i64),
@@ -429,6 +434,11 @@ class HinesPlan:
     def uses_levels(self) -> bool:
         return bool(load_library().hines_plan_uses_levels(self.handle))
 
+    @property
+    def split(self) -> int:
+        """Number of trees solved on two lanes."""
+        return int(load_library().hines_plan_split(self.handle))
+
     def close(self):
         if self._h is not None:
             _check("hines_plan_destroy", load_library().hines_plan_destroy(self._h))
@@ -467,6 +477,30 @@ def hines_plan_elems(plan: HinesPlan) -> int:
 
 def hines_plan_unknowns(plan: HinesPlan) -> int:
     return plan.unknowns
+
+
+def hines_plan_split(plan: HinesPlan) -> int:
+    return plan.split
+
+
+def hines_split_schedule(parent):
+    """Host-only two-lane schedule of one tree (see bps.h): (node, code), each
+    of shape (2, rows), or None when the tree stays on one lane."""
+    import numpy as np
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
+    n = len(par)
+    cap = 2 * n + 80
+    node = np.empty(2 * cap, dtype=np.int32)
+    code = np.empty(2 * cap, dtype=np.uint16)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L = load_library()
+    m = L.hines_split_schedule(n, par.ctypes.data_as(i32p), node.ctypes.data_as(i32p),
+                               code.ctypes.data_as(ctypes.c_void_p), cap)
+    if m < 0:
+        raise BpsError("hines_split_schedule", 1, (L.bps_last_error() or b"").decode())
+    if m == 0:
+        return None
+    return node.reshape(2, cap)[:, :m].copy(), code.reshape(2, cap)[:, :m].copy()
 
 
 def hines_plan_uses_levels(plan: HinesPlan) -> bool:

@@ -79,6 +79,8 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
 int64_t hines_plan_elems_of(const bps_hines_plan *p);
 int64_t hines_plan_unknowns_of(const bps_hines_plan *p);
 int64_t hines_plan_batch_of(const bps_hines_plan *p);
+int64_t hines_plan_split_of(const bps_hines_plan *p);
+int32_t hines_split_rows(int32_t n, const int32_t *parent, int32_t *node, uint16_t *code, int32_t cap);
 
 static const int64_t kMaxDim = int64_t(1) << 40;
 
@@ -543,6 +545,33 @@ bps_status hines_plan_create(bps_hines_plan **plan, int64_t batch, const int32_t
 
 int hines_plan_uses_levels(const bps_hines_plan *plan) { return plan && hines_plan_levels(plan); }
 
+int64_t hines_plan_split(const bps_hines_plan *plan) { return plan ? hines_plan_split_of(plan) : 0; }
+
+int32_t hines_split_schedule(int32_t n, const int32_t *parent, int32_t *node, uint16_t *code,
+                             int32_t cap)
+{
+    clear_error();
+    if (!parent || !node || !code || cap < 0) {
+        set_error("hines_split_schedule: NULL array or negative cap");
+        return -1;
+    }
+    if (n < 1 || n > (1 << 30)) {
+        set_error("hines_split_schedule: n = %d out of range", n);
+        return -1;
+    }
+    for (int32_t i = 1; i < n; ++i)
+        if (parent[i] < 0 || parent[i] >= i) {
+            set_error("hines_split_schedule: parent[%d] = %d not in [0, %d)", i, parent[i], i);
+            return -1;
+        }
+    const int32_t m = hines_split_rows(n, parent, node, code, cap);
+    if (m < 0) {
+        set_error("hines_split_schedule: %d rows do not fit cap = %d", -m, cap);
+        return -1;
+    }
+    return m;
+}
+
 bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch, const int32_t *sizes,
                                    const int32_t *parent, int mono, int64_t ld, int schedule)
 {
@@ -574,7 +603,8 @@ bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch, const i
             off += n;
         }
     }
-    if (schedule != BPS_HINES_AUTO && schedule != BPS_HINES_LANES && schedule != BPS_HINES_LEVELS)
+    if (schedule != BPS_HINES_AUTO && schedule != BPS_HINES_LANES && schedule != BPS_HINES_LEVELS &&
+        schedule != BPS_HINES_SPLIT)
         BPS_FAIL(BPS_EINVAL, "unknown schedule %d", schedule);
     CHECK(prepare_device());
     return hines_plan_build(plan, batch, sizes, parent, mono, ld, schedule);

@@ -47,6 +47,11 @@ struct bps_hines_plan {
     int32_t *blk_rows = nullptr;   // multi [nblocks]
     int32_t *lane_n = nullptr;     // multi [nblocks*64]
     int32_t *lane_src = nullptr;   // multi [nblocks*64] original neuron (-1 empty)
+    // two lanes per neuron for the largest trees (k_hines_split): built when
+    // at least one tree is split; then lane_n holds each lane's branch rows
+    int64_t nsplit = 0;            // neurons on two lanes
+    uint16_t *code16 = nullptr;    // multi packed [elems]: row codes
+    int32_t *comp = nullptr;       // multi packed [elems]: compartment of the row, -1 padding
     int64_t *src_off = nullptr;    // multi [batch+1] offsets in the flat layout
     // level schedule (one wavefront per neuron, sections of each tree by
     // level; see k_hines_levels): built when the plan may use it
@@ -70,6 +75,24 @@ constexpr int kLevelMaxN = 4096;        // tree size limit of the level schedule
 // Trees of 256 .. 2048: 256 neurons 308 vs 513 us, 1024 neurons 584 vs 513.
 constexpr int64_t kLevelAutoUnknowns = 786432;
 constexpr int kHinesAhead = 8;  // rows of look-ahead for the streamed inputs
+constexpr int kSimds = 1024;    // SIMDs of the GPU (256 CUs x 4)
+constexpr int kSplitMin = 32;   // smallest tree put on two lanes
+// Row codes of the two-lane kernel (see build_split), 16 bits: the row's
+// own slot (bits 0-5), its parent's slot (bits 6-11), live (bit 12),
+// whether the parent's voltage is that of the lane's previous live row in
+// the substitution (bit 13, then it is in a register), and whether the
+// parent's slot is in the column of the pair's even lane (bit 14: a branch
+// root of the odd lane, whose parent is on the trunk).  Slot ids: 0..15 the
+// lane's ring, 16..31 the pair's trunk ring (kept in the even lane's column,
+// the lane that takes the trunk), 32 the lane's sink (the own slot of
+// padding and waiting rows, the parent slot of roots and those).
+constexpr int kSlotTrunk = 16, kSlotSink = 32, kSlots = 33;
+constexpr uint16_t kCodeLive = 1u << 12, kCodeVreg = 1u << 13, kCodeEven = 1u << 14;
+__host__ __device__ constexpr uint16_t row_code(int own, int par, bool live, bool vreg, bool even = false)
+{
+    return uint16_t(own | (par << 6) | (live ? kCodeLive : 0) | (vreg ? kCodeVreg : 0) |
+                    (even ? kCodeEven : 0));
+}
 
 struct HinesArgs {
     int64_t batch, n, ld;            // mono geometry
@@ -77,6 +100,8 @@ struct HinesArgs {
     const int32_t *blk_rows, *lane_n, *lane_src;
     const int32_t *parent;
     const uint8_t *dist8;
+    const uint16_t *code16;          // two-lane plans: row codes
+    const int32_t *comp;             // two-lane plans: compartment of each row
     const double *u, *l, *d;
     double *rhs, *mwork, *gd, *gr;
     int32_t *info;
@@ -339,6 +364,9 @@ struct BlockBuf {
     __device__ int32_t ldb(uint32_t lane_off, uint32_t row_off) const {
         return int32_t(__builtin_amdgcn_raw_buffer_load_b8(r, lane_off, row_off, 0));
     }
+    __device__ uint32_t ldh(uint32_t lane_off, uint32_t row_off) const {
+        return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, lane_off, row_off, 0));
+    }
     __device__ void st(double v, uint32_t lane_off, uint32_t row_off) const {
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, lane_off, row_off, 0);
@@ -464,6 +492,145 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
 #pragma unroll
     for (int j = 0; j < D; ++j) load_f(fa[j], 1 + j);
     int32_t f0 = 1;
+    for (; f0 + 2 * D - 1 < rows; f0 += 2 * D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_f(fb[j], f0 + D + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) subst(f0 + j, fa[j]);
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_f(fa[j], f0 + 2 * D + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) subst(f0 + D + j, fb[j]);
+    }
+    if (f0 + D - 1 < rows) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_f(fb[j], f0 + D + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) subst(f0 + j, fa[j]);
+        f0 += D;
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (f0 + j < rows) subst(f0 + j, fb[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (f0 + j < rows) subst(f0 + j, fa[j]);
+    }
+}
+
+// Multi-morphology blocks in which some trees run on two lanes (an aligned
+// pair; the plan's schedule, see build_split) and the others on one.  Each
+// row's code names its own slot and its parent's (a lane ring, the pair's
+// trunk ring, or the lane's sink), so the kernel keeps no counters and no
+// row branches on its kind: padding and waiting rows read, clear and feed
+// the sink, and what they store in rhs and work is never read.  Everything
+// else follows k_hines_multi.
+template <int D>
+__global__ void __launch_bounds__(kWave) k_hines_split(HinesArgs A)
+{
+    // slot id s of lane k: ring[s][k]; the odd lane of a pair reaches the
+    // trunk slots in the even lane's column (code bit 14)
+    __shared__ double2 ring[kSlots][kWave];
+    const int k = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t off = uniform_i64(A.blk_off[b]);
+    const int32_t rows = __builtin_amdgcn_readfirstlane(A.blk_rows[b]);
+    const int32_t src = A.lane_src[b * kWave + k];
+    const uint32_t nbytes = uint32_t(rows) * kWave * 8u;
+    const BlockBuf U(A.u + off, nbytes), L(A.l + off, nbytes), Dg(A.d + off, nbytes);
+    const BlockBuf R(A.rhs + off, nbytes), MW(A.mwork + off, nbytes);
+    const BlockBuf PC(A.code16 + off, nbytes / 4);
+    const uint32_t lo8 = uint32_t(k) * 8u, lo2 = uint32_t(k) * 2u;
+    auto rb8 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * (kWave * 8u)); };
+    auto rb2 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * (kWave * 2u)); };
+    const uint32_t kl = uint32_t(k);
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) ring[j][k] = make_double2(0.0, 0.0);
+    // (the plan writes no slot id above 32; LDS accesses past the block's
+    // allocation would be dropped by the hardware in any case)
+    auto own_slot = [&](uint32_t c) -> double2 & { return ring[c & 63u][kl]; };
+    auto parent_slot = [&](uint32_t c) -> double2 & { return ring[(c >> 6) & 63u][kl & ~((c >> 14) & 1u)]; };
+    int32_t bad = 0;
+
+    // ---- leaves -> root ----
+    struct BRow { double u, l, d, r; uint32_t c; };
+    auto load_b = [&](BRow &q, int32_t r) {
+        const int32_t rc = r >= 0 ? r : 0;
+        q.u = U.ld(lo8, rb8(rc)); q.l = L.ld(lo8, rb8(rc)); q.d = Dg.ld(lo8, rb8(rc));
+        q.r = R.ld(lo8, rb8(rc)); q.c = PC.ldh(lo2, rb2(rc));
+    };
+    auto elim = [&](int32_t i, const BRow &q) {
+        const bool live = q.c & kCodeLive;
+        double2 &own = own_slot(q.c);
+        const double2 pp = own;
+        own = make_double2(0.0, 0.0);
+        const double dd = q.d - pp.x;            // d'_i
+        const double rr = q.r - pp.y;            // rhs'_i
+        if (live & bad_pivot(dd)) bad = max(bad, 1 + A.comp[off + int64_t(i) * kWave + k]);
+        const double rcp = 1.0 / dd;
+        const double fac = q.u * rcp;            // factor of Algorithm 1
+        R.st(rr * rcp, lo8, rb8(i));             // q_i (padding: unspecified)
+        MW.st(q.l * rcp, lo8, rb8(i));           // m_i
+        double2 &par = parent_slot(q.c);
+        unsafeAtomicAdd(&par.x, fac * q.l);
+        unsafeAtomicAdd(&par.y, fac * rr);
+    };
+    BRow qa[D], qb[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_b(qa[j], rows - 1 - j);
+    int32_t i0 = rows - 1;
+    for (; i0 - 2 * D + 1 >= 0; i0 -= 2 * D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_b(qb[j], i0 - D - j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) elim(i0 - j, qa[j]);
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_b(qa[j], i0 - 2 * D - j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) elim(i0 - D - j, qb[j]);
+    }
+    if (i0 - D + 1 >= 0) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_b(qb[j], i0 - D - j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) elim(i0 - j, qa[j]);
+        i0 -= D;
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (i0 - j >= 0) elim(i0 - j, qb[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (i0 - j >= 0) elim(i0 - j, qa[j]);
+    }
+    // a tree's info: 1 + the largest index of a bad pivot over its lanes
+    const int32_t other_src = __builtin_amdgcn_mov_dpp(src, 0xB1, 0xF, 0xF, false);
+    const int32_t other_bad = __builtin_amdgcn_mov_dpp(bad, 0xB1, 0xF, 0xF, false);
+    const bool paired = src >= 0 && other_src == src;
+    if (src >= 0 && A.info && (!paired || (k & 1) == 0)) A.info[src] = paired ? max(bad, other_bad) : bad;
+
+    // ---- root -> leaves: a slot holds the voltage its row stored last.  The
+    // sink starts at 0: a root (the first live row of its lanes here) reads
+    // it as its parent's voltage ----
+    ring[kSlotSink][k] = make_double2(0.0, 0.0);
+    double vprev = 0.0;
+    struct FRow { double q, m; uint32_t c; };
+    auto load_f = [&](FRow &f, int32_t r) {
+        const int32_t rc = r < rows ? r : rows - 1;
+        f.q = R.ld(lo8, rb8(rc)); f.m = MW.ld(lo8, rb8(rc)); f.c = PC.ldh(lo2, rb2(rc));
+    };
+    auto subst = [&](int32_t i, const FRow &f) {
+        const bool live = f.c & kCodeLive;
+        const double vr = parent_slot(f.c).x;
+        const double v = f.q - f.m * ((f.c & kCodeVreg) ? vprev : vr);
+        R.st(v, lo8, rb8(i));
+        own_slot(f.c).x = v;
+        vprev = live ? v : vprev;
+    };
+    FRow fa[D], fb[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_f(fa[j], j);
+    int32_t f0 = 0;
     for (; f0 + 2 * D - 1 < rows; f0 += 2 * D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) load_f(fb[j], f0 + D + j);
@@ -701,6 +868,27 @@ __global__ void k_multi_pack(const int64_t *__restrict__ blk_off, const int32_t 
     }
 }
 
+// multi with trees on two lanes: the compartment of each packed element is
+// listed (comp, -1 for padding), since a split tree's rows are in schedule
+// order
+template <typename T, bool PACK>
+__global__ void k_multi_pack_map(const int64_t *__restrict__ blk_off, const int32_t *__restrict__ blk_rows,
+                                 const int32_t *__restrict__ lane_src, const int32_t *__restrict__ comp,
+                                 const int64_t *__restrict__ src_off, const T *__restrict__ src,
+                                 T *__restrict__ dst)
+{
+    const int64_t b = blockIdx.x;
+    const int64_t rows = blk_rows[b], off = blk_off[b];
+    for (int64_t e = threadIdx.x; e < rows * kWave; e += blockDim.x) {
+        const int k = int(e % kWave);
+        const int32_t s = lane_src[b * kWave + k];
+        const int32_t c = comp[off + e];
+        const bool live = s >= 0 && c >= 0;
+        if (PACK) dst[off + e] = live ? src[src_off[s] + c] : T(0);
+        else if (live) dst[src_off[s] + c] = src[off + e];
+    }
+}
+
 // ---- host side -------------------------------------------------------------------
 
 template <typename T>
@@ -722,6 +910,7 @@ static void free_plan(bps_hines_plan *p)
     (void)hipFree(p->lane_n); (void)hipFree(p->lane_src); (void)hipFree(p->src_off);
     (void)hipFree(p->lv_perm); (void)hipFree(p->lv_sec); (void)hipFree(p->lv_spar);
     (void)hipFree(p->lv_lev); (void)hipFree(p->lv_tree);
+    (void)hipFree(p->code16); (void)hipFree(p->comp);
     delete p;
 }
 
@@ -753,6 +942,314 @@ static bps_status build_levels(bps_hines_plan *P, int64_t ntrees, const int32_t 
     if ((st = upload(&P->lv_spar, spar)) != BPS_OK) return st;
     if ((st = upload(&P->lv_lev, lev)) != BPS_OK) return st;
     return upload(&P->lv_tree, tree);
+}
+
+// ---- two lanes per neuron (multi-morphology) ----------------------------------
+//
+// With one lane per neuron the largest trees of a batch set the time of the
+// launch: their lanes run a serial chain of n rows while the rest of the
+// GPU has finished.  Such a tree is split over two lanes of its wavefront
+// (the per-branch decomposition of section 4 of the Hines page, done inside
+// one wavefront): the trunk (the path from the root that always descends
+// into the largest subtree) and the side branches hanging from it.  Lane 0
+// eliminates the trunk from its deepest node upwards as each trunk node's
+// branches are done; both lanes eliminate side branches, deepest attachment
+// first, each branch in decreasing index order.  A trunk node's pending
+// update lives in a ring of 16 slots shared by the pair (slot = its position
+// on the trunk mod 16); a branch node's in the lane's own ring (slot = the
+// lane's count of branch rows mod 16).  The schedule is lockstep (one row
+// per lane and step, bubbles where a lane waits), and is checked here by
+// replaying both sweeps' slot traffic; a tree that fails stays on one lane.
+//
+// Row code (one byte per row and lane): bit 7 live, bit 6 trunk row,
+// bits 4-5 where the parent's pending update / voltage is (0 the lane's
+// ring, 2 the trunk ring, 3 no parent), bits 0-3 the slot (a trunk row: its
+// own slot; its parent is the trunk slot before it).
+namespace {
+
+struct SplitLane {
+    std::vector<int32_t> node;   // per step (first sweep order): compartment, -1 waiting
+    std::vector<uint16_t> code;  // per step: row_code
+};
+
+// Replays both sweeps of k_hines_split on the slot level for one tree on a
+// lane pair: every pending update reaches its parent's slot before the
+// parent reads it, and every parent voltage read finds the parent's.
+bool split_check(int32_t n, const int32_t *p, const SplitLane lane[2])
+{
+    const int32_t rows = int32_t(lane[0].node.size());
+    std::vector<int32_t> nch(n, 0);
+    for (int32_t i = 1; i < n; ++i) ++nch[p[i]];
+    struct Slot { int32_t tag = -1, count = 0; };
+    // [lane][slot id]: a row's own slot in its lane's column, its parent's in
+    // the even lane's when the code says so
+    Slot sl[2][kSlots];
+    auto at = [&](int j, int id) -> Slot & { return sl[j][id]; };
+    int32_t seen = 0;
+    for (int32_t s = 0; s < rows; ++s) {
+        for (int j = 0; j < 2; ++j) {            // read and clear the own slot
+            const uint16_t c = lane[j].code[s];
+            const int own = c & 63, par = (c >> 6) & 63;
+            if (own >= kSlots || par >= kSlots) return false;
+            if (!(c & kCodeLive)) { if (own != kSlotSink || par != kSlotSink) return false; continue; }
+            const int32_t x = lane[j].node[s];
+            if (own == kSlotSink) return false;
+            Slot &o = at(j, own);
+            if (o.count != nch[x] || (nch[x] && o.tag != x)) return false;
+            o = Slot{};
+            ++seen;
+        }
+        for (int j = 0; j < 2; ++j) {            // add to the parent's slot
+            const uint16_t c = lane[j].code[s];
+            if (!(c & kCodeLive)) continue;
+            const int32_t x = lane[j].node[s];
+            const int par = (c >> 6) & 63;
+            if ((par == kSlotSink) != (x == 0)) return false;
+            if (x == 0) continue;
+            Slot &q = at((c & kCodeEven) ? 0 : j, par);
+            if (q.count && q.tag != p[x]) return false;
+            q.tag = p[x];
+            ++q.count;
+        }
+    }
+    if (seen != n) return false;
+    // substitution: steps in reverse; a slot holds the last voltage stored
+    int32_t vs[2][kSlots], vprev[2] = {-1, -1};
+    std::fill(&vs[0][0], &vs[0][0] + 2 * kSlots, -1);
+    auto vat = [&](int j, int id) -> int32_t & { return vs[j][id]; };
+    bool root_done = false;
+    for (int32_t s = rows - 1; s >= 0; --s) {
+        int32_t got[2] = {-2, -2};
+        for (int j = 0; j < 2; ++j) {            // read the parent's voltage
+            const uint16_t c = lane[j].code[s];
+            if (!(c & kCodeLive)) continue;
+            const int32_t x = lane[j].node[s];
+            const int par = (c >> 6) & 63;
+            if (x == 0) {                        // the root reads the zeroed sink, first
+                if (root_done || s != rows - 1 || j != 0 || (c & kCodeVreg)) return false;
+                root_done = true;
+                continue;
+            }
+            got[j] = (c & kCodeVreg) ? vprev[j] : vat((c & kCodeEven) ? 0 : j, par);
+            if (got[j] != p[x]) return false;
+        }
+        for (int j = 0; j < 2; ++j) {            // store the own voltage
+            const uint16_t c = lane[j].code[s];
+            if (!(c & kCodeLive)) continue;
+            const int32_t x = lane[j].node[s];
+            vat(j, c & 63) = x;
+            vprev[j] = x;
+        }
+    }
+    return root_done;
+}
+
+// The two-lane schedule of one tree (parents p, p_0 ignored); false when
+// the greedy schedule does not close or fails the replay.
+bool split_schedule(int32_t n, const int32_t *p, SplitLane lane[2])
+{
+    if (n < 2) return false;
+    std::vector<int32_t> sz(n, 1), first(n + 1, 0), kids(n > 1 ? n - 1 : 0);
+    for (int32_t i = n - 1; i >= 1; --i) sz[p[i]] += sz[i];
+    for (int32_t i = 1; i < n; ++i) ++first[p[i] + 1];
+    for (int32_t i = 0; i < n; ++i) first[i + 1] += first[i];
+    {
+        std::vector<int32_t> fill(first.begin(), first.end() - 1);
+        for (int32_t i = 1; i < n; ++i) kids[fill[p[i]]++] = i;     // children in increasing index
+    }
+    std::vector<int32_t> trunk, tpos(n, -1);
+    for (int32_t v = 0;;) {
+        tpos[v] = int32_t(trunk.size());
+        trunk.push_back(v);
+        int32_t best = -1;
+        for (int32_t e = first[v]; e < first[v + 1]; ++e)
+            if (best < 0 || sz[kids[e]] > sz[best]) best = kids[e];
+        if (best < 0) break;
+        v = best;
+    }
+    const int32_t L = int32_t(trunk.size());
+    // side branches, deepest attachment first, each in decreasing index order
+    struct Branch { int32_t attach, begin, end; };
+    std::vector<Branch> br;
+    std::vector<int32_t> bn, stack, pending(L, 0);
+    bn.reserve(n);
+    for (int32_t k = L - 1; k >= 0; --k) {
+        const int32_t t = trunk[k];
+        for (int32_t e = first[t]; e < first[t + 1]; ++e) {
+            const int32_t c = kids[e];
+            if (tpos[c] >= 0) continue;
+            const int32_t b0 = int32_t(bn.size());
+            stack.assign(1, c);
+            while (!stack.empty()) {
+                const int32_t x = stack.back();
+                stack.pop_back();
+                bn.push_back(x);
+                for (int32_t f = first[x]; f < first[x + 1]; ++f) stack.push_back(kids[f]);
+            }
+            std::sort(bn.begin() + b0, bn.end(), std::greater<int32_t>());
+            br.push_back({k, b0, int32_t(bn.size())});
+            ++pending[k];
+        }
+    }
+    std::vector<int32_t> tstep(L, -1), cnt_of(n, -1), lane_of(n, -1);
+    int32_t nextk = L - 1, cnt[2] = {0, 0}, cur[2] = {-1, -1}, pos[2] = {0, 0};
+    size_t qi = 0;
+    for (int j = 0; j < 2; ++j) { lane[j].node.clear(); lane[j].code.clear(); }
+    for (int32_t step = 0; nextk >= 0; ++step) {
+        if (step > 2 * n + 4 * kRing) return false;
+        const bool ready = pending[nextk] == 0 && (nextk == L - 1 || tstep[nextk + 1] >= 0);
+        for (int j = 0; j < 2; ++j) {
+            if (j == 0 && ready) {
+                lane[0].node.push_back(trunk[nextk]);
+                tstep[nextk] = step;
+                lane_of[trunk[nextk]] = 0;
+                --nextk;
+                continue;
+            }
+            if (cur[j] < 0 && qi < br.size()) { cur[j] = int32_t(qi++); pos[j] = br[cur[j]].begin; }
+            if (cur[j] < 0) { lane[j].node.push_back(-1); continue; }
+            const Branch &B = br[cur[j]];
+            // a branch root's update goes to trunk slot (attach mod 16): the
+            // trunk node 16 positions deeper must have taken its own first
+            if (pos[j] + 1 == B.end && B.attach + kRing < L && tstep[B.attach + kRing] < 0) {
+                lane[j].node.push_back(-1);
+                continue;
+            }
+            const int32_t x = bn[pos[j]];
+            lane[j].node.push_back(x);
+            cnt_of[x] = cnt[j]++;
+            lane_of[x] = j;
+            if (++pos[j] == B.end) { --pending[B.attach]; cur[j] = -1; }
+        }
+    }
+    if (qi != br.size() || cur[0] >= 0 || cur[1] >= 0) return false;
+    // a tree whose trunk is most of it (a chain) gains too little from a
+    // second lane to pay for the lane
+    if (5 * int64_t(lane[0].node.size()) > 4 * int64_t(n)) return false;
+    // slot ids: a branch row's is its count mod 16 in its lane, a trunk row's
+    // 16 + its trunk position mod 16; the voltage register serves a parent
+    // that is the lane's previous live row in the substitution
+    auto slot_of = [&](int32_t x) {
+        return tpos[x] >= 0 ? kSlotTrunk + (tpos[x] & (kRing - 1)) : cnt_of[x] & (kRing - 1);
+    };
+    for (int j = 0; j < 2; ++j) {
+        const size_t m = lane[j].node.size();
+        lane[j].code.assign(m, row_code(kSlotSink, kSlotSink, false, false));
+        int32_t prev = -1;                       // previous live row, substitution order
+        for (size_t t = m; t-- > 0;) {
+            const int32_t x = lane[j].node[t];
+            if (x < 0) continue;
+            if (x != 0 && tpos[p[x]] < 0 && lane_of[p[x]] != j) return false;
+            if (j == 1 && tpos[x] >= 0) return false;         // the trunk is lane 0's
+            const int par = x == 0 ? kSlotSink : slot_of(p[x]);
+            lane[j].code[t] = row_code(slot_of(x), par, true, x != 0 && p[x] == prev,
+                                       j == 1 && par >= kSlotTrunk && par < kSlotSink);
+            prev = x;
+        }
+    }
+    return split_check(n, p, lane);
+}
+
+}  // namespace
+
+// Multi-morphology plan with up to `want` trees on two lanes: the largest
+// of at least kSplitMin compartments whose schedules close.  Units (a tree on one lane, or a
+// split tree on an aligned pair of lanes) are sorted by their row count and
+// dealt 64 lanes per block; a unit of m rows occupies rows m-1 .. 0 of its
+// block (first sweep from the top), the rows above are padding.  Leaves
+// P->nsplit = 0 and builds nothing when no tree splits.
+static bps_status build_split(bps_hines_plan *P, int64_t batch, const int32_t *sizes,
+                              const int32_t *parent, const std::vector<int64_t> &off, int64_t want)
+{
+    std::vector<SplitLane> lanes;          // two per split tree
+    std::vector<int32_t> split_of(batch, -1), by_size(batch);
+    std::iota(by_size.begin(), by_size.end(), 0);
+    std::stable_sort(by_size.begin(), by_size.end(), [&](int32_t x, int32_t y) { return sizes[x] > sizes[y]; });
+    for (int32_t s : by_size) {
+        if (int64_t(lanes.size() / 2) >= want || sizes[s] < kSplitMin) break;
+        SplitLane two[2];
+        if (!split_schedule(sizes[s], parent + off[s], two)) continue;
+        split_of[s] = int32_t(lanes.size() / 2);
+        lanes.push_back(std::move(two[0]));
+        lanes.push_back(std::move(two[1]));
+    }
+    P->nsplit = int64_t(lanes.size() / 2);
+    if (P->nsplit == 0) return BPS_OK;
+    auto rows_of = [&](int32_t s) {
+        return split_of[s] >= 0 ? int32_t(lanes[2 * split_of[s]].node.size()) : sizes[s];
+    };
+    std::vector<int32_t> pairs, singles;
+    for (int32_t s = 0; s < int32_t(batch); ++s) (split_of[s] >= 0 ? pairs : singles).push_back(s);
+    auto by_rows = [&](int32_t x, int32_t y) { return rows_of(x) > rows_of(y); };
+    std::stable_sort(pairs.begin(), pairs.end(), by_rows);
+    std::stable_sort(singles.begin(), singles.end(), by_rows);
+    // lane assignment: longest first; a pair starts at an even lane (an odd
+    // lane takes the next single, or stays empty)
+    std::vector<int32_t> lsrc;
+    size_t ip = 0, is = 0;
+    while (ip < pairs.size() || is < singles.size()) {
+        const bool odd = lsrc.size() & 1;
+        const bool take_pair = ip < pairs.size() &&
+                               (is == singles.size() || rows_of(pairs[ip]) >= rows_of(singles[is]));
+        if (take_pair && !odd) { lsrc.push_back(pairs[ip]); lsrc.push_back(pairs[ip]); ++ip; }
+        else if (is < singles.size()) lsrc.push_back(singles[is++]);
+        else lsrc.push_back(-1);
+    }
+    const int64_t nb = int64_t((lsrc.size() + kWave - 1) / kWave);
+    lsrc.resize(size_t(nb * kWave), -1);
+    std::vector<int64_t> boff(nb);
+    std::vector<int32_t> brows(nb), ln(nb * kWave, 0);
+    int64_t acc = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+        int32_t rmax = 1;
+        for (int k = 0; k < kWave; ++k)
+            if (lsrc[b * kWave + k] >= 0) rmax = std::max(rmax, rows_of(lsrc[b * kWave + k]));
+        boff[b] = acc;
+        brows[b] = rmax;
+        acc += int64_t(rmax) * kWave;
+        P->max_rows = std::max(P->max_rows, rmax);
+    }
+    P->nblocks = nb;
+    P->elems = acc;
+    std::vector<uint16_t> code(acc, row_code(kSlotSink, kSlotSink, false, false));
+    std::vector<int32_t> comp(acc, -1);
+    for (int64_t b = 0; b < nb; ++b)
+        for (int k = 0; k < kWave; ++k) {
+            const int32_t s = lsrc[b * kWave + k];
+            if (s < 0) continue;
+            const int64_t base = boff[b] + k;
+            if (split_of[s] >= 0) {
+                const SplitLane &SL = lanes[2 * split_of[s] + (k & 1)];
+                const int32_t m = int32_t(SL.node.size());
+                int32_t live = 0;
+                for (int32_t t = 0; t < m; ++t) {
+                    const int64_t e = base + int64_t(m - 1 - t) * kWave;
+                    code[e] = SL.code[t];
+                    comp[e] = SL.node[t];
+                    live += SL.node[t] >= 0;
+                }
+                ln[b * kWave + k] = live;
+            } else {
+                // one lane: row i is compartment i; its slot is its count
+                // (n-1-i: the first sweep runs from row n-1 down) mod 16
+                const int32_t n = sizes[s];
+                const int32_t *ps = parent + off[s];
+                for (int32_t i = 0; i < n; ++i) {
+                    const int64_t e = base + int64_t(i) * kWave;
+                    code[e] = i == 0 ? row_code((n - 1) & (kRing - 1), kSlotSink, true, false)
+                                     : row_code((n - 1 - i) & (kRing - 1), (n - 1 - ps[i]) & (kRing - 1),
+                                                true, ps[i] == i - 1);
+                    comp[e] = i;
+                }
+                ln[b * kWave + k] = n;
+            }
+        }
+    bps_status st;
+    if ((st = upload(&P->code16, code)) != BPS_OK || (st = upload(&P->comp, comp)) != BPS_OK ||
+        (st = upload(&P->blk_off, boff)) != BPS_OK || (st = upload(&P->blk_rows, brows)) != BPS_OK ||
+        (st = upload(&P->lane_n, ln)) != BPS_OK || (st = upload(&P->lane_src, lsrc)) != BPS_OK)
+        return st;
+    return upload(&P->src_off, off);
 }
 
 bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,
@@ -792,6 +1289,23 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         std::vector<int64_t> off(batch + 1, 0);
         for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];
         P->unknowns = off[batch];
+        if (!P->use_levels && sched != BPS_HINES_LANES) {
+            int32_t dmax = 0;
+            for (int64_t s = 0; s < batch; ++s)
+                for (int32_t i = 1; i < sizes[s]; ++i) dmax = std::max(dmax, i - parent[off[s] + i]);
+            // how many trees go on two lanes: every one when asked for; by
+            // default, when one lane per neuron leaves SIMDs without a
+            // wavefront, the largest, until the lanes (nearly) fill one
+            // wavefront per SIMD
+            const int64_t want = sched == BPS_HINES_SPLIT ? batch
+                               : (batch + kWave - 1) / kWave < kSimds ? int64_t(kSimds) * kWave - batch - 2 * kWave
+                                                                     : 0;
+            if (dmax <= kRing && want > 0) {
+                st = build_split(P, batch, sizes, parent, off, want);
+                if (st != BPS_OK) { free_plan(P); return st; }
+                if (P->nsplit > 0) { P->max_dist = dmax; *out = P; return BPS_OK; }
+            }
+        }
         std::vector<int32_t> order(batch);
         std::iota(order.begin(), order.end(), 0);
         std::stable_sort(order.begin(), order.end(),
@@ -870,6 +1384,20 @@ bool hines_plan_levels(const bps_hines_plan *p) { return p->use_levels; }
 int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }
 int64_t hines_plan_unknowns_of(const bps_hines_plan *p) { return p->unknowns; }
 int64_t hines_plan_batch_of(const bps_hines_plan *p) { return p->batch; }
+int64_t hines_plan_split_of(const bps_hines_plan *p) { return p->nsplit; }
+
+int32_t hines_split_rows(int32_t n, const int32_t *parent, int32_t *node, uint16_t *code, int32_t cap)
+{
+    SplitLane two[2];
+    if (!split_schedule(n, parent, two)) return 0;
+    const int32_t m = int32_t(two[0].node.size());
+    if (m > cap) return -m;
+    for (int j = 0; j < 2; ++j) {
+        std::copy(two[j].node.begin(), two[j].node.end(), node + int64_t(j) * cap);
+        std::copy(two[j].code.begin(), two[j].code.end(), code + int64_t(j) * cap);
+    }
+    return m;
+}
 
 template <typename T>
 bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, void *dst,
@@ -884,6 +1412,15 @@ bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, 
         else
             hipLaunchKernelGGL((k_mono_transpose<T, false>), dim3(grid), dim3(256), 0, st, P->n,
                                P->batch, P->ld, (const T *)src, (T *)dst);
+    } else if (P->nsplit > 0) {
+        if (pack)
+            hipLaunchKernelGGL((k_multi_pack_map<T, true>), dim3(unsigned(P->nblocks)), dim3(256), 0, st,
+                               P->blk_off, P->blk_rows, P->lane_src, P->comp, P->src_off,
+                               (const T *)src, (T *)dst);
+        else
+            hipLaunchKernelGGL((k_multi_pack_map<T, false>), dim3(unsigned(P->nblocks)), dim3(256), 0, st,
+                               P->blk_off, P->blk_rows, P->lane_src, P->comp, P->src_off,
+                               (const T *)src, (T *)dst);
     } else {
         if (pack)
             hipLaunchKernelGGL((k_multi_pack<T, true>), dim3(unsigned(P->nblocks)), dim3(256), 0, st,
@@ -921,6 +1458,8 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
     A.blk_off = P->blk_off; A.blk_rows = P->blk_rows; A.lane_n = P->lane_n; A.lane_src = P->lane_src;
     A.parent = P->parent;
     A.dist8 = P->dist8;
+    A.code16 = P->code16;
+    A.comp = P->comp;
     A.u = (const double *)u; A.l = (const double *)l; A.d = (const double *)d;
     A.rhs = (double *)rhs;
     A.mwork = (double *)work;
@@ -936,12 +1475,14 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
     // A multi-morphology batch of at most one block per SIMD runs one wave
     // per SIMD anyway, and its largest blocks set the time: groups of 16
     // rows (256 VGPRs, one wave per SIMD) keep more rows in flight.
-    constexpr int kSimds = 1024;
     if (P->mono) {
         if (gen) hipLaunchKernelGGL((k_hines<true, true, D>), grid, dim3(kWave), 0, st, A);
         else hipLaunchKernelGGL((k_hines_mono_reg<D>), grid, dim3(kWave), 0, st, A);
     } else {
         if (gen) hipLaunchKernelGGL((k_hines<false, true, D>), grid, dim3(kWave), 0, st, A);
+        else if (P->nsplit > 0 && P->nblocks <= kSimds)
+            hipLaunchKernelGGL((k_hines_split<16>), grid, dim3(kWave), 0, st, A);
+        else if (P->nsplit > 0) hipLaunchKernelGGL((k_hines_split<D>), grid, dim3(kWave), 0, st, A);
         else if (P->nblocks <= kSimds) hipLaunchKernelGGL((k_hines_multi<16>), grid, dim3(kWave), 0, st, A);
         else hipLaunchKernelGGL((k_hines_multi<D>), grid, dim3(kWave), 0, st, A);
     }

@@ -365,6 +365,16 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
 /* Schedules of hines_solve_batch ([H] sections 3 and 4):
  *   BPS_HINES_LANES   one lane per neuron over the whole tree (the page's
  *                     Full-/Block-Interleaved kernels);
+ *   BPS_HINES_SPLIT   as LANES, but in a multi-morphology batch whose parents
+ *                     all lie within 16 compartments every tree of 32 or more
+ *                     compartments runs on two lanes of its wavefront (the
+ *                     per-branch decomposition of section 4 inside a
+ *                     wavefront: the side branches hanging from the trunk,
+ *                     the path from the root into the largest subtrees, are
+ *                     eliminated on both lanes, the trunk on the first as
+ *                     its branches finish); a tree whose two-lane schedule
+ *                     does not shorten it stays on one lane.  Mono plans:
+ *                     as LANES;
  *   BPS_HINES_LEVELS  one wavefront per neuron: the tree cut into its
  *                     unbranched sections, grouped by level (the page's
  *                     per-branch / per-level decomposition of section 4),
@@ -372,10 +382,17 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     in LDS; for batches too small to fill the GPU with one
  *                     lane per neuron.  Trees of at most 4096 compartments;
  *   BPS_HINES_AUTO    LEVELS for batches of at most 786432 compartments in
- *                     all whose trees fit, else LANES (what hines_plan_create
+ *                     all whose trees fit, else LANES; when one lane per
+ *                     neuron would leave SIMDs of the GPU without a
+ *                     wavefront (fewer than 1024 blocks of 64 neurons), the
+ *                     largest trees go on two lanes as in SPLIT until the
+ *                     blocks nearly fill them (what hines_plan_create
  *                     chooses).
- * The solver layout and every other argument are the same for both. */
-enum { BPS_HINES_AUTO = 0, BPS_HINES_LANES = 1, BPS_HINES_LEVELS = 2 };
+ * Every schedule takes the same arguments; the solver layout is the plan's
+ * (elements per array: hines_plan_elems; convert with hines_pack and
+ * hines_unpack): a tree on two lanes has its compartments in the order its
+ * schedule visits them. */
+enum { BPS_HINES_AUTO = 0, BPS_HINES_LANES = 1, BPS_HINES_LEVELS = 2, BPS_HINES_SPLIT = 3 };
 
 /* hines_plan_create with an explicit schedule.  BPS_ENOTSUP for
  * BPS_HINES_LEVELS with a tree above 4096 compartments; BPS_EINVAL for an
@@ -386,6 +403,23 @@ BPS_API bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch,
 
 /* 1 if the plan solves with the level schedule, else 0. */
 BPS_API int hines_plan_uses_levels(const bps_hines_plan *plan);
+/* Number of trees the plan solves on two lanes (0 for a NULL plan). */
+BPS_API int64_t hines_plan_split(const bps_hines_plan *plan);
+
+/* The two-lane schedule BPS_HINES_SPLIT would give one tree (host only, no
+ * device needed; for inspection and host-side tests).
+ *   parent: host int32[n], p_i in [0, i) (parent[0] ignored).
+ *   node, code: host arrays of 2*cap entries; lane j's step t (first sweep
+ *   order, t < rows; the substitution takes the steps in reverse) is
+ *   node[j*cap + t], the compartment it eliminates (-1 while the lane
+ *   waits), and code[j*cap + t]: bits 0-5 the row's slot, bits 6-11 its
+ *   parent's slot (slot ids 0..15 the lane's ring of pending updates and
+ *   voltages, 16..31 the pair's trunk ring, 32 none), bit 12 live, bit 13
+ *   the parent is the lane's previous live row of the substitution.
+ * Returns the number of rows (steps), 0 if the tree stays on one lane, -1
+ * on invalid arguments or cap below the rows (message in bps_last_error). */
+BPS_API int32_t hines_split_schedule(int32_t n, const int32_t *parent, int32_t *node,
+                                     uint16_t *code, int32_t cap);
 
 /* Elements of one value array (u, l, d or rhs) in the plan's solver layout. */
 BPS_API int64_t hines_plan_elems(const bps_hines_plan *plan);
@@ -396,7 +430,8 @@ BPS_API int64_t hines_plan_unknowns(const bps_hines_plan *plan);
  * flat: device, the neurons' values one neuron after another (sum(sizes)
  * values; n*batch for mono, neuron-major).  packed: device,
  * hines_plan_elems values in the solver layout.  Padding entries of the
- * packed layout are written as 0 by hines_pack and never read by solves. */
+ * packed layout are written as 0 by hines_pack; no result depends on them,
+ * and a solve may leave any value in those of rhs. */
 BPS_API bps_status hines_pack(const bps_hines_plan *plan, int dtype, const void *flat,
                       void *packed, void *stream);
 BPS_API bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const void *packed,

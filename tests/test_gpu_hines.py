@@ -160,7 +160,7 @@ def test_mono_parent_distance_window_edge(dist, schedule):
     np.testing.assert_array_equal(info, rinfo)
 
 
-@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("schedule", SCHEDULES + [bps.BPS_HINES_SPLIT])
 @pytest.mark.parametrize("dist", [16, 17])
 def test_multi_parent_distance_window_edge(dist, schedule):
     """As the mono case, for blocks of different trees: every neuron with
@@ -186,10 +186,13 @@ def test_multi_parent_distance_window_edge(dist, schedule):
     np.testing.assert_array_equal(info, rinfo)
 
 
-def _run_multi(mm, schedule=bps.BPS_HINES_AUTO):
+def _run_multi(mm, schedule=bps.BPS_HINES_AUTO, min_split=0):
     plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=schedule)
     if schedule != bps.BPS_HINES_AUTO:
         assert plan.uses_levels == (schedule == bps.BPS_HINES_LEVELS)
+    if schedule in (bps.BPS_HINES_LANES, bps.BPS_HINES_LEVELS):
+        assert plan.split == 0
+    assert plan.split >= min_split
     E = plan.elems
     packed = [torch.empty(E, dtype=torch.float64, device="cuda:0") for _ in range(4)]
     for src, dst in zip((mm.u, mm.l, mm.d, mm.rhs), packed):
@@ -221,6 +224,112 @@ def test_multi_matches_oracle(batch, nmin, nmax, schedule):
     ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
     assert _rel_per_neuron(out, ref, mm.offsets) <= 1e-10
     np.testing.assert_array_equal(info, rinfo)
+
+
+# ---- trees on two lanes (BPS_HINES_SPLIT, and the automatic choice for
+# batches whose largest trees are twice the smallest) ----------------------------
+
+@pytest.mark.parametrize("batch,nmin,nmax", [(1, 600, 600), (5, 32, 40), (130, 20, 700),
+                                             (300, 256, 2048),
+                                             # more than one block per SIMD: the
+                                             # occupancy-first configuration
+                                             (70000, 30, 60)])
+def test_multi_split_matches_oracle(batch, nmin, nmax):
+    print(f"hines multi split batch={batch} n in [{nmin},{nmax}]", flush=True)
+    mm = W.hines_multi(batch, nmin, nmax, rng=np.random.default_rng(batch + 7 * nmax))
+    out, info = _run_multi(mm, bps.BPS_HINES_SPLIT, min_split=1)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    assert _rel_per_neuron(out, ref, mm.offsets) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+
+
+def test_multi_split_auto_choice():
+    """The automatic choice puts trees on two lanes, largest first, while one
+    lane per neuron leaves SIMDs without a wavefront (fewer than 1024 blocks
+    of 64), and none when the blocks fill them."""
+    print("hines multi split auto 2048 neurons of 256..2048", flush=True)
+    mm = W.hines_multi(2048, 256, 2048, rng=np.random.default_rng(41))
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
+    assert not plan.uses_levels
+    assert plan.split >= 0.95 * mm.batch
+    plan.close()
+    out, info = _run_multi(mm, bps.BPS_HINES_AUTO, min_split=1)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    assert _rel_per_neuron(out, ref, mm.offsets) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+    # 1025 blocks of one lane per neuron: nothing to fill
+    sizes = np.full(1025 * 64, 40, dtype=np.int32)
+    rng = np.random.default_rng(42)
+    par = np.concatenate([W.random_tree(40, rng) for _ in range(len(sizes))])
+    plan = bps.hines_plan_create(len(sizes), sizes, par, mono=False)
+    assert not plan.uses_levels and plan.split == 0
+    plan.close()
+    # 1000 blocks: as many trees as the free lanes of 1024 blocks take (less
+    # a margin of two blocks), the largest first
+    sizes = np.r_[np.full(1000 * 64 - 2000, 40), np.full(2000, 60)].astype(np.int32)
+    par = np.concatenate([W.random_tree(int(n), rng) for n in sizes])
+    plan = bps.hines_plan_create(len(sizes), sizes, par, mono=False)
+    assert plan.split == 1024 * 64 - len(sizes) - 128
+    assert plan.elems <= 1024 * 64 * 60
+    plan.close()
+
+
+def test_multi_split_breakdown_info():
+    """info of a tree on two lanes: 1 + the largest index with a bad pivot
+    (the first one Algorithm 1 meets), whichever lane meets it."""
+    rng = np.random.default_rng(12)
+    mm = W.hines_multi(40, 200, 400, rng=rng)
+    bad = {3: "zero_leaf", 8: "nan_mid", 21: "inf_root"}
+    for s, kind in bad.items():
+        o0, n = mm.offsets[s], int(mm.sizes[s])
+        if kind == "zero_leaf":
+            mm.d[o0 + n - 1] = 0.0
+        elif kind == "nan_mid":
+            mm.d[o0 + n // 3] = np.nan
+        else:
+            mm.d[o0] = np.inf
+    out, info = _run_multi(mm, bps.BPS_HINES_SPLIT, min_split=30)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    np.testing.assert_array_equal(info, rinfo)
+    assert info[3] == mm.sizes[3] and info[8] == mm.sizes[8] // 3 + 1 and info[21] == 1
+    ok = [s for s in range(mm.batch) if s not in bad]
+    offs = mm.offsets
+    errs = [np.linalg.norm(out[offs[s]:offs[s + 1]] - ref[offs[s]:offs[s + 1]]) /
+            np.linalg.norm(ref[offs[s]:offs[s + 1]]) for s in ok]
+    assert max(errs) <= 1e-10
+
+
+def test_multi_split_pack_contract():
+    """hines_pack of a split plan writes every compartment once and 0 to
+    every other element; hines_unpack inverts it exactly; solves repeat
+    bitwise."""
+    mm = W.hines_multi(150, 30, 500, rng=np.random.default_rng(13))
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False,
+                                 schedule=bps.BPS_HINES_SPLIT)
+    assert plan.split > 0
+    E = plan.elems
+    x = np.random.default_rng(1).uniform(1.0, 2.0, len(mm.u))
+    packed = torch.full((E,), -7.0, dtype=torch.float64, device="cuda:0")
+    bps.hines_pack(plan, dev(x), packed)
+    hp = host(packed)
+    assert np.count_nonzero(hp) == len(x)
+    assert np.array_equal(np.sort(hp[hp != 0]), np.sort(x))
+    back = torch.zeros(len(x), dtype=torch.float64, device="cuda:0")
+    bps.hines_unpack(plan, packed, back)
+    np.testing.assert_array_equal(host(back), x)
+    arrs = []
+    for v in (mm.u, mm.l, mm.d, mm.rhs):
+        t = torch.empty(E, dtype=torch.float64, device="cuda:0")
+        bps.hines_pack(plan, dev(v), t)
+        arrs.append(t)
+    work = buf(bps.hines_work_bytes(plan))
+    r0 = arrs[3].clone()
+    bps.hines_solve_batch(plan, *arrs, work)
+    first = host(arrs[3])
+    arrs[3].copy_(r0)
+    bps.hines_solve_batch(plan, *arrs, work)
+    np.testing.assert_array_equal(host(arrs[3]), first)
+    plan.close()
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
