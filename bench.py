@@ -575,19 +575,22 @@ def _hines_common(args, multi, which=None):
     import workloads as W
 
     cfg = W.WORKLOADS[which if which is not None else (4 if multi else 3)]
+    sched = {"auto": bps.BPS_HINES_AUTO, "lanes": bps.BPS_HINES_LANES, "split": bps.BPS_HINES_SPLIT,
+             "levels": bps.BPS_HINES_LEVELS}[args.hines_schedule]
     if multi:
         mm = W.hines_multi(cfg["batch"], cfg["nmin"], cfg["nmax"])
-        plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
+        plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=sched)
         arrs = []
         for v in (mm.u, mm.l, mm.d, mm.rhs):
             t = torch.empty(plan.elems, dtype=torch.float64, device="cuda:0")
             bps.hines_pack(plan, torch.as_tensor(v, device="cuda:0"), t)
             arrs.append(t)
         nsolve = cfg["nsteps"]
-        stats = {"mean_n": float(mm.sizes.mean()), "padded_elems": plan.elems}
+        stats = {"mean_n": float(mm.sizes.mean()), "padded_elems": plan.elems,
+                 "trees_on_two_lanes": plan.split}
     else:
         hm = W.hines_mono(cfg["n"], cfg["batch"], rng=W.rng_for(which if which is not None else 3))
-        plan = bps.hines_plan_create(cfg["batch"], [cfg["n"]], hm.parent, mono=True)
+        plan = bps.hines_plan_create(cfg["batch"], [cfg["n"]], hm.parent, mono=True, schedule=sched)
         arrs = [torch.as_tensor(v, device="cuda:0") for v in (hm.u, hm.l, hm.d, hm.rhs)]
         nsolve = 1
         stats = W.tree_stats(hm.parent)
@@ -606,8 +609,10 @@ def _hines_common(args, multi, which=None):
     kern_ms = _stats(per_solve)["median"]
     alg_bytes = per_unknown * plan.unknowns
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    kname = "k_hines_levels" if plan.uses_levels else ("k_hines_multi" if multi else "k_hines_mono_reg")
-    traffic = _traffic("hines_levels" if plan.uses_levels else ("hines_multi" if multi else "hines_mono"))
+    kname = ("k_hines_levels" if plan.uses_levels else
+             ("k_hines_split" if plan.split else "k_hines_multi") if multi else "k_hines_mono_reg")
+    traffic = _traffic("hines_levels" if plan.uses_levels else
+                       ("hines_split" if plan.split else "hines_multi") if multi else "hines_mono")
     line = {
         "metric": "unknowns solved/s (fp64), Hines " + ("multi" if multi else "mono"),
         "value": unknowns * args.steps / wall, "unit": "unknowns/s", "ms_per_step": ms_step,
@@ -617,7 +622,8 @@ def _hines_common(args, multi, which=None):
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "schedule": "levels" if plan.uses_levels else "one lane per neuron",
+                     "schedule": "levels" if plan.uses_levels else
+                                 "two lanes for the largest trees" if plan.split else "one lane per neuron",
                      "kernel_ms": kern_ms, "timed": "one solve call", "bytes_per_launch": alg_bytes,
                      "counter_gbs": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9},
     }
@@ -706,6 +712,8 @@ def main():
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
     ap.add_argument("--split", action="store_true",
                     help="workloads 2, 9: time the separate factor and solve calls instead")
+    ap.add_argument("--hines-schedule", default="auto", choices=["auto", "lanes", "split", "levels"],
+                    help="workloads 3, 4, 10: the plan's schedule (BPS_HINES_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
