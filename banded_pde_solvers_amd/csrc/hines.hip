@@ -3,7 +3,10 @@
 // Method: Algorithm 1 of "Simulating the behavior of the human brain on
 // GPUs" (section 2): eliminate from the leaves to the root (factor u_i/d_i,
 // update the parent's diagonal and right-hand side), divide at the root, then
-// substitute from the root to the leaves.  One lane per neuron (section 3).
+// substitute from the root to the leaves.  One lane per neuron (section 3);
+// in multi-morphology batches the largest trees may take two lanes of their
+// wavefront, split into trunk and side branches (section 4's per-branch
+// decomposition; k_hines_split, build_split).
 //
 // Layouts: mono-morphology uses the Full-Interleaved layout [n][ld] with one
 // parent vector shared by every lane (wave-uniform, scalar loads).
