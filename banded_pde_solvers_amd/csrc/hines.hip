@@ -76,7 +76,11 @@ constexpr int kLevelMaxN = 4096;        // tree size limit of the level schedule
 // Measured (one solve): trees of 512, 16 .. 1024 neurons: 77 .. 107 us with
 // levels, 147 us with one lane per neuron; 2048: 135 vs 151; 4096: 259 vs 158.
 // Trees of 256 .. 2048: 256 neurons 308 vs 513 us, 1024 neurons 584 vs 513.
+// Multi-morphology batches compare with two lanes per tree (levels / two
+// lanes): 256 trees of 512: 87 / 91 us, 1024 trees of 512: 99.5 / 93 us;
+// 256 trees of 256 .. 2048: 281 / 301 us, 512 such trees: 314 / 294 us.
 constexpr int64_t kLevelAutoUnknowns = 786432;
+constexpr int64_t kLevelAutoUnknownsMulti = 393216;
 constexpr int kHinesAhead = 8;  // rows of look-ahead for the streamed inputs
 constexpr int kSimds = 1024;    // SIMDs of the GPU (256 CUs x 4)
 constexpr int kSplitMin = 32;   // smallest tree put on two lanes
@@ -1275,7 +1279,8 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         BPS_FAIL(BPS_ENOTSUP, "level schedule needs trees of at most %d compartments", kLevelMaxN);
     }
     P->use_levels = sched == BPS_HINES_LEVELS ||
-                    (sched == BPS_HINES_AUTO && lv_fit && total <= kLevelAutoUnknowns);
+                    (sched == BPS_HINES_AUTO && lv_fit &&
+                     total <= (mono ? kLevelAutoUnknowns : kLevelAutoUnknownsMulti));
     bps_status st = BPS_OK;
     if (mono) {
         const int64_t n = sizes[0];

@@ -381,8 +381,9 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     one section per lane and level, with the neuron held
  *                     in LDS; for batches too small to fill the GPU with one
  *                     lane per neuron.  Trees of at most 4096 compartments;
- *   BPS_HINES_AUTO    LEVELS for batches of at most 786432 compartments in
- *                     all whose trees fit, else LANES; when one lane per
+ *   BPS_HINES_AUTO    LEVELS for batches whose trees fit and that hold at
+ *                     most 786432 compartments in all (mono) or 393216
+ *                     (multi-morphology), else LANES; when one lane per
  *                     neuron would leave SIMDs of the GPU without a
  *                     wavefront (fewer than 1024 blocks of 64 neurons), the
  *                     largest trees go on two lanes as in SPLIT until the

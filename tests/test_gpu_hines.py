@@ -465,6 +465,12 @@ def test_levels_auto_choice_and_limits():
     assert not bps.hines_plan_create(2622, [300], p, mono=True).uses_levels
     big = W.random_tree(5000, rng)
     assert not bps.hines_plan_create(10, [5000], big, mono=True).uses_levels
+    # multi-morphology: at most 393216 compartments
+    sizes = np.full(768, 512, dtype=np.int32)
+    par = np.concatenate([W.random_tree(512, rng) for _ in range(769)])
+    assert bps.hines_plan_create(768, sizes, par[:768 * 512], mono=False).uses_levels
+    plan = bps.hines_plan_create(769, np.full(769, 512, dtype=np.int32), par, mono=False)
+    assert not plan.uses_levels and plan.split == 769
     with pytest.raises(bps.BpsError):
         bps.hines_plan_create(10, [5000], big, mono=True, schedule=bps.BPS_HINES_LEVELS)
 

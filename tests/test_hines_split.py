@@ -154,5 +154,16 @@ def test_split_schedule_arguments():
     assert bps.hines_split_schedule(np.array([-1], dtype=np.int32)) is None
     # a chain (all trunk) gains nothing from a second lane
     assert bps.hines_split_schedule(np.r_[-1, np.arange(699)].astype(np.int32)) is None
+    # output arrays too short for the schedule: -1 and a message, nothing written past cap
+    import ctypes
+    L = bps.load_library()
+    p = W.random_tree(200, np.random.default_rng(2))
+    node = np.full(2 * 10 + 4, -5, dtype=np.int32)
+    code = np.zeros(2 * 10 + 4, dtype=np.uint16)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    m = L.hines_split_schedule(200, p.ctypes.data_as(i32p), node.ctypes.data_as(i32p),
+                               code.ctypes.data_as(ctypes.c_void_p), 10)
+    assert m == -1 and "cap" in bps.bps_last_error()
+    assert np.all(node == -5)
     with pytest.raises(bps.BpsError):
         bps.hines_split_schedule(np.array([-1, 0, 5], dtype=np.int32))
