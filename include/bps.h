@@ -441,13 +441,15 @@ BPS_API bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const voi
 /* Bytes of `work` hines_solve_batch needs for this plan. */
 BPS_API size_t hines_work_bytes(const bps_hines_plan *plan, int dtype);
 
-/* Solve every neuron ([H] Algorithm 1), one lane per neuron.
+/* Solve every neuron ([H] Algorithm 1) with the plan's schedule (one lane
+ * per neuron, two lanes for split trees, or one wavefront per neuron).
  * u, l, d: device, solver layout, not modified.  rhs: device, solver layout,
  * right-hand side on entry, voltages V on return (as in [H]).  work: device,
  * hines_work_bytes bytes.  info: device int32[batch] indexed by the ORIGINAL
  * neuron number, or NULL; a nonzero value is 1 + the first compartment, in
- * elimination order (n-1 down to 1, then the root 0), whose pivot is zero or
- * not finite.  dtype must be BPS_F64. */
+ * Algorithm 1's elimination order (n-1 down to 1, then the root 0), whose
+ * pivot is zero or not finite, whatever order the schedule eliminates in.
+ * dtype must be BPS_F64. */
 BPS_API bps_status hines_solve_batch(const bps_hines_plan *plan, int dtype,
                              const void *u, const void *l, const void *d,
                              void *rhs, void *work, int32_t *info, void *stream);
