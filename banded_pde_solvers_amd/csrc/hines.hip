@@ -27,6 +27,7 @@
 // per-lane accumulators in global memory (zeroed before each solve).
 #include <algorithm>
 #include <numeric>
+#include <thread>
 #include <vector>
 
 #include "common.h"
@@ -1172,13 +1173,32 @@ static bps_status build_split(bps_hines_plan *P, int64_t batch, const int32_t *s
     std::vector<int32_t> split_of(batch, -1), by_size(batch);
     std::iota(by_size.begin(), by_size.end(), 0);
     std::stable_sort(by_size.begin(), by_size.end(), [&](int32_t x, int32_t y) { return sizes[x] > sizes[y]; });
-    for (int32_t s : by_size) {
-        if (int64_t(lanes.size() / 2) >= want || sizes[s] < kSplitMin) break;
-        SplitLane two[2];
-        if (!split_schedule(sizes[s], parent + off[s], two)) continue;
-        split_of[s] = int32_t(lanes.size() / 2);
-        lanes.push_back(std::move(two[0]));
-        lanes.push_back(std::move(two[1]));
+    // schedules of the candidates (the largest trees, a few more than wanted
+    // in case some do not split), computed on all host threads; then taken
+    // in size order
+    int64_t ncand = 0;
+    while (ncand < batch && sizes[by_size[ncand]] >= kSplitMin) ++ncand;
+    ncand = std::min<int64_t>(ncand, want + want / 8 + 64);
+    std::vector<SplitLane> cand(2 * ncand);
+    std::vector<uint8_t> ok(ncand, 0);
+    {
+        const int64_t hw = std::min<int64_t>(16, std::thread::hardware_concurrency());
+        const int64_t nt = std::max<int64_t>(1, std::min<int64_t>(ncand / 64, hw));
+        std::vector<std::thread> pool;
+        for (int64_t t = 0; t < nt; ++t)
+            pool.emplace_back([&, t] {
+                for (int64_t c = t; c < ncand; c += nt) {
+                    const int32_t s = by_size[c];
+                    ok[c] = split_schedule(sizes[s], parent + off[s], &cand[2 * c]);
+                }
+            });
+        for (auto &th : pool) th.join();
+    }
+    for (int64_t c = 0; c < ncand && int64_t(lanes.size() / 2) < want; ++c) {
+        if (!ok[c]) continue;
+        split_of[by_size[c]] = int32_t(lanes.size() / 2);
+        lanes.push_back(std::move(cand[2 * c]));
+        lanes.push_back(std::move(cand[2 * c + 1]));
     }
     P->nsplit = int64_t(lanes.size() / 2);
     if (P->nsplit == 0) return BPS_OK;
