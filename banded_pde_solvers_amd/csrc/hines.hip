@@ -554,8 +554,8 @@ __global__ void __launch_bounds__(kWave) k_hines_split(HinesArgs A)
     const uint32_t kl = uint32_t(k);
 #pragma unroll
     for (int j = 0; j < kSlots; ++j) ring[j][k] = make_double2(0.0, 0.0);
-    // (the plan writes no slot id above 32; LDS accesses past the block's
-    // allocation would be dropped by the hardware in any case)
+    // (slot ids are at most 32: build_split writes them, split_check rejects
+    // a schedule with any other)
     auto own_slot = [&](uint32_t c) -> double2 & { return ring[c & 63u][kl]; };
     auto parent_slot = [&](uint32_t c) -> double2 & { return ring[(c >> 6) & 63u][kl & ~((c >> 14) & 1u)]; };
     int32_t bad = 0;
