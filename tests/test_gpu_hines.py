@@ -231,6 +231,8 @@ def test_multi_matches_oracle(batch, nmin, nmax, schedule):
 
 @pytest.mark.parametrize("batch,nmin,nmax", [(1, 600, 600), (5, 32, 40), (130, 20, 700),
                                              (300, 256, 2048),
+                                             # one- and two-compartment trees beside split ones
+                                             (200, 1, 100),
                                              # more than one block per SIMD: the
                                              # occupancy-first configuration
                                              (70000, 30, 60)])
