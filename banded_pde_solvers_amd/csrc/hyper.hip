@@ -176,7 +176,7 @@ __device__ __forceinline__ void setup_back_sweep(const double *__restrict__ src,
 // of the recurrence: the set-up is then bound by arithmetic latency rather
 // than by LDS round trips.
 template <int M, int P>
-__global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, double *__restrict__ coef)
+__device__ __forceinline__ void resident_setup(double sigma, double *__restrict__ coef)
 {
 #pragma clang fp contract(off)
     constexpr int m = M - 2, n2 = 2 * P, w = 4 * P;
@@ -452,6 +452,22 @@ __global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, doubl
         const double URc = e * ra[m - 1];
         h[5] = URa; h[6] = URb; h[7] = URc;
     }
+}
+
+template <int M, int P>
+__global__ void __launch_bounds__(64) k_hyper_resident_setup(double sigma, double *__restrict__ coef)
+{
+    resident_setup<M, P>(sigma, coef);
+}
+
+// The set-ups of two chunk lengths at once, one workgroup each (they run on
+// different CUs, so the call costs the longer of the two).
+template <int M1, int P1, int M2, int P2>
+__global__ void __launch_bounds__(64) k_hyper_resident_setup2(double sigma, double *__restrict__ coef1,
+                                                              double *__restrict__ coef2)
+{
+    if (blockIdx.x == 0) resident_setup<M1, P1>(sigma, coef1);
+    else resident_setup<M2, P2>(sigma, coef2);
 }
 
 // Right-hand side of each step, by the bits of EX:
@@ -765,19 +781,35 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
     }
 }
 
-// Chunk length for the resident path, 0 if the shape is not supported.
-int resident_chunk(int64_t n)
+// Chunk lengths of the resident path for n: M1 (0 if the shape is not
+// supported) with P1 chunks, and for n = 256 a second one (M2 = 16, P2 = 16)
+// for batches too small to give every SIMD a wavefront with 64-row chunks.
+// Sixteen chunks put one system in a 16-lane row (DPP exchanges, cyclic
+// reduction on the interface), which beats a dense interface step, so n =
+// 512 takes 32-row chunks.  Measured (100 steps, 64-row / 16-row chunks, n =
+// 256): 64 systems 0.168 / 0.069 ms, 4096 0.181 / 0.078, 16384 0.206 /
+// 0.189, 32768 0.331 / 0.361; n = 512 (64 / 32 rows): 8192 0.291 / 0.184,
+// 32768 0.69 / 0.62, 65536 1.18 / 1.12.
+struct ResChunks { int M1, P1, M2, P2; };
+static ResChunks resident_chunks(int64_t n)
 {
+    if (n == 256) return {64, 4, 16, 16};
+    if (n == 512) return {32, 16, 0, 0};
     constexpr int M = 64;
-    if (n % M != 0) return 0;
+    if (n % M != 0) return {0, 0, 0, 0};
     const int64_t P = n / M;
-    return ((P >= 2 && P <= kResMaxP) || P == 32 || P == 64) ? M : 0;
+    return ((P >= 2 && P <= kResMaxP) || P == 32 || P == 64) ? ResChunks{M, int(P), 0, 0}
+                                                            : ResChunks{0, 0, 0, 0};
 }
+
+int resident_chunk(int64_t n) { return resident_chunks(n).M1; }
 
 size_t resident_coef_bytes(int64_t n)
 {
-    const int M = resident_chunk(n);
-    return M ? size_t(res_coef_elems(M, int(n / M))) * sizeof(double) : 0;
+    const ResChunks rc = resident_chunks(n);
+    if (!rc.M1) return 0;
+    return (size_t(res_coef_elems(rc.M1, rc.P1)) + (rc.M2 ? size_t(res_coef_elems(rc.M2, rc.P2)) : 0)) *
+           sizeof(double);
 }
 
 template <int M, int P>
@@ -815,13 +847,33 @@ bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t n
                                  int mode, double e0, double e1, double e2, double rr, void *coef,
                                  void *C, hipStream_t st, int parts)
 {
-    constexpr int M = 64;
-    if (resident_chunk(n) != M || !(sigma >= 0.0))
+    const ResChunks rc = resident_chunks(n);
+    if (!rc.M1 || !(sigma >= 0.0))
         BPS_FAIL(BPS_ENOTSUP, "resident path needs n = 64*P, 2 <= P <= 16 or P = 32, 64, sigma >= 0");
     double *cf = (double *)coef, *x = (double *)C;
+    double *cf2 = cf + res_coef_elems(rc.M1, rc.P1);
+    if ((parts & kResSetup) && rc.M2) {
+        // both coefficient sets (n = 256 only), in one launch
+        hipLaunchKernelGGL((k_hyper_resident_setup2<64, 4, 16, 16>), dim3(2), dim3(64), 0, st, sigma, cf, cf2);
+        parts &= ~kResSetup;
+    }
+    // the second chunk length while 64-row chunks leave SIMDs without a
+    // wavefront (at most one wavefront per SIMD: 1024 of 64 / P1 systems)
+    const bool second = rc.M2 && batch <= int64_t(1024) * (kWave / rc.P1);
+    if (second) {
+        launch_res<16, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf2, x, parts, st);
+        BPS_LAUNCHED("k_hyper_resident");
+        return BPS_OK;
+    }
+    if (rc.M1 == 32) {
+        launch_res<32, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st);
+        BPS_LAUNCHED("k_hyper_resident");
+        return BPS_OK;
+    }
+    constexpr int M = 64;
 #define BPS_RES_CASE(PP) \
     case PP: launch_res<M, PP>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st); break;
-    switch (int(n / M)) {
+    switch (rc.P1) {
     BPS_RES_CASE(2) BPS_RES_CASE(3) BPS_RES_CASE(4) BPS_RES_CASE(5) BPS_RES_CASE(6)
     BPS_RES_CASE(7) BPS_RES_CASE(8) BPS_RES_CASE(9) BPS_RES_CASE(10) BPS_RES_CASE(11)
     BPS_RES_CASE(12) BPS_RES_CASE(13) BPS_RES_CASE(14) BPS_RES_CASE(15) BPS_RES_CASE(16)

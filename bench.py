@@ -109,6 +109,17 @@ def _time_loop(fn, steps, warmup):
     return wall, per[0]
 
 
+def _resident_kernel(n, batch, ex):
+    """Name of the resident step kernel the library launches for (n, batch):
+    16-row chunks for n = 256 up to 16384 systems, 32-row chunks for
+    n = 512, 64-row chunks otherwise."""
+    if n == 256 and batch <= 16384:
+        return f"k_hyper_resident<16,16,{ex}>"
+    if n == 512:
+        return f"k_hyper_resident<32,16,{ex}>"
+    return f"k_hyper_resident<64,{n // 64},{ex}>"
+
+
 def _source_hash(relpath):
     """Hash of a kernel source's code: comments and blank lines do not count
     (the sources hold no comment markers inside string literals)."""
@@ -329,7 +340,7 @@ def bench_hyperdiffusion(args, which=1):
     if kind == "hyperdiffusion":
         timing["factor_ms"] = _stats(per[0])
         timing["solve_kernel_ms"] = _stats(kern)
-        timed = f"k_hyper_resident<64,{n // 64},0> alone (HIP events around hyperdiffusion_solve)"
+        timed = f"{_resident_kernel(n, batch, 0)} alone (HIP events around hyperdiffusion_solve)"
     else:
         timed = "whole call (set-up kernel included)"
     line = {
@@ -340,9 +351,8 @@ def bench_hyperdiffusion(args, which=1):
         "dtype": "f64",
         "config": config,
         "timing": timing,
-        "roofline": {"bound": "alu", "kernel": f"k_hyper_resident<64,{n // 64}," +
-                     {"hyperdiffusion": "0", "hyperdiffusion_theta": "1",
-                      "cahn_hilliard": "2"}[kind] + ">",
+        "roofline": {"bound": "alu", "kernel": _resident_kernel(n, batch, {"hyperdiffusion": 0,
+                     "hyperdiffusion_theta": 1, "cahn_hilliard": 2}[kind]),
                      "achieved": achieved, "peak": FP64_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP64_VALU_PEAK_TFLOPS, "traffic": traffic,
                      "kernel_ms": kern_ms, "timed": timed,

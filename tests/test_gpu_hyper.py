@@ -74,6 +74,25 @@ def test_one_step_parity(n, batch):
     assert relerr_cols(_step(C0, dt, dx, 1), _oracle(C0, dt, dx, 1)) <= 1e-10
 
 
+def test_chunk_length_choice():
+    """n = 256 takes 16-row chunks up to 16384 systems and 64-row chunks
+    above; n = 512 32-row chunks at any batch.  Both sides of the switch
+    against the oracle (one step, sampled systems) and against each other
+    on the systems they share."""
+    for n, batches in ((256, (16384, 16385)), (512, (33, 8200))):
+        dt, dx = 1e-6, 1.0 / n
+        C0 = np.random.default_rng(n).uniform(-1, 1, (n, max(batches)))
+        outs = []
+        for batch in batches:
+            print(f"chunk choice n={n} batch={batch}", flush=True)
+            out = _step(C0[:, :batch], dt, dx, 1)
+            cols = np.unique(np.r_[0, batch - 1, np.random.default_rng(batch).integers(0, batch, 24)])
+            assert relerr_cols(out[:, cols], _oracle(C0[:, cols], dt, dx, 1)) <= 1e-10
+            outs.append(out)
+        k = min(batches)
+        assert relerr_cols(outs[0][:, :k], outs[1][:, :k]) <= 1e-10
+
+
 def test_workload1_trajectory_reduced_batch():
     """N = 1024, sigma ~ 1.1e6, 100 steps on 300 systems."""
     cfg = W.WORKLOADS[1]
