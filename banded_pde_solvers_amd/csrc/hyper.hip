@@ -786,15 +786,16 @@ k_hyper_resident(int64_t batch, int64_t ld, int64_t nsteps, const double *__rest
 // for batches too small to give every SIMD a wavefront with 64-row chunks.
 // Sixteen chunks put one system in a 16-lane row (DPP exchanges, cyclic
 // reduction on the interface), which beats a dense interface step, so n =
-// 512 takes 32-row chunks.  Measured (100 steps, 64-row / 16-row chunks, n =
-// 256): 64 systems 0.168 / 0.069 ms, 4096 0.181 / 0.078, 16384 0.206 /
-// 0.189, 32768 0.331 / 0.361; n = 512 (64 / 32 rows): 8192 0.291 / 0.184,
-// 32768 0.69 / 0.62, 65536 1.18 / 1.12.
+// 384 .. 896 in steps of 128 take 16 chunks of n/16 rows.  Measured (100
+// steps, 64-row / n/16-row chunks): n = 256: 64 systems 0.168 / 0.069 ms,
+// 4096 0.181 / 0.078, 16384 0.206 / 0.189, 32768 0.331 / 0.361; n = 512:
+// 8192 0.291 / 0.184, 65536 1.18 / 1.12; 65536 systems of n = 384, 640, 768,
+// 896: 0.94 / 0.91, 1.52 / 1.36, 1.78 / 1.58, 2.10 / 1.83 ms.
 struct ResChunks { int M1, P1, M2, P2; };
 static ResChunks resident_chunks(int64_t n)
 {
     if (n == 256) return {64, 4, 16, 16};
-    if (n == 512) return {32, 16, 0, 0};
+    if (n == 384 || n == 512 || n == 640 || n == 768 || n == 896) return {int(n / 16), 16, 0, 0};
     constexpr int M = 64;
     if (n % M != 0) return {0, 0, 0, 0};
     const int64_t P = n / M;
@@ -865,8 +866,14 @@ bps_status launch_hyper_resident(int64_t n, int64_t batch, int64_t ld, int64_t n
         BPS_LAUNCHED("k_hyper_resident");
         return BPS_OK;
     }
-    if (rc.M1 == 32) {
-        launch_res<32, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st);
+    if (rc.M1 != 64) {
+        switch (rc.M1) {
+        case 24: launch_res<24, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st); break;
+        case 32: launch_res<32, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st); break;
+        case 40: launch_res<40, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st); break;
+        case 48: launch_res<48, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st); break;
+        default: launch_res<56, 16>(batch, ld, nsteps, sigma, mode, e0, e1, e2, rr, cf, x, parts, st); break;
+        }
         BPS_LAUNCHED("k_hyper_resident");
         return BPS_OK;
     }

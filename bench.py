@@ -111,12 +111,12 @@ def _time_loop(fn, steps, warmup):
 
 def _resident_kernel(n, batch, ex):
     """Name of the resident step kernel the library launches for (n, batch):
-    16-row chunks for n = 256 up to 16384 systems, 32-row chunks for
-    n = 512, 64-row chunks otherwise."""
+    16-row chunks for n = 256 up to 16384 systems, 16 chunks for n = 384 ..
+    896 in steps of 128, 64-row chunks otherwise."""
     if n == 256 and batch <= 16384:
         return f"k_hyper_resident<16,16,{ex}>"
-    if n == 512:
-        return f"k_hyper_resident<32,16,{ex}>"
+    if n in (384, 512, 640, 768, 896):
+        return f"k_hyper_resident<{n // 16},16,{ex}>"
     return f"k_hyper_resident<64,{n // 64},{ex}>"
 
 

@@ -66,7 +66,7 @@ def _oracle(C0, dt, dx, theta, nsteps, dtype=torch.float64, gamma=GAMMA, mob=MOB
 
 
 @pytest.mark.parametrize("theta", [1.0, 0.5, 0.3])
-@pytest.mark.parametrize("n,batch", [(128, 37), (256, 17), (1024, 100), (832, 20), (2048, 24), (4096, 10),   # resident
+@pytest.mark.parametrize("n,batch", [(128, 37), (256, 17), (1024, 100), (832, 20), (2048, 24), (4096, 10), (512, 21), (768, 13),   # resident
                                      (96, 50), (100, 33)])                          # streaming
 def test_one_step_parity(n, batch, theta):
     print(f"theta={theta} n={n} batch={batch}", flush=True)

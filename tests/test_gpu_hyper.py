@@ -67,7 +67,9 @@ def test_workload0_modes_full():
 @pytest.mark.parametrize("n,batch", [(6, 1), (7, 65), (64, 130), (128, 37), (192, 50), (256, 17),
                                      (1024, 200), (2048, 40), (4096, 12),
                                      # chunk counts that do not divide a wavefront
-                                     (320, 33), (448, 20), (832, 40), (960, 17)])
+                                     (320, 33), (448, 20), (832, 40), (960, 17),
+                                     # 16 chunks of 24 .. 56 rows
+                                     (384, 33), (640, 20), (768, 17), (896, 9)])
 def test_one_step_parity(n, batch):
     dt, dx = _dt(n), 1.0 / n
     C0 = np.random.default_rng(n + batch).uniform(-1, 1, (n, batch))
@@ -102,7 +104,7 @@ def test_workload1_trajectory_reduced_batch():
     assert _traj_err(out, ref, C0) <= 2e-9
 
 
-@pytest.mark.parametrize("n,batch", [(128, 33), (1024, 70), (2048, 20), (4096, 8)])
+@pytest.mark.parametrize("n,batch", [(128, 33), (768, 40), (1024, 70), (2048, 20), (4096, 8)])
 def test_resident_and_streaming_paths_agree(n, batch):
     """The built-in operator (register-resident chunked kernel) against the
     same matrix given explicitly (one lane per system, streaming kernel)."""
