@@ -35,6 +35,7 @@ __all__ = [
     "hines_work_bytes", "hines_solve_batch", "BPS_HINES_AUTO", "BPS_HINES_LANES",
     "BPS_HINES_LEVELS", "BPS_HINES_SPLIT", "hines_plan_create_sched", "hines_plan_elems",
     "hines_plan_unknowns", "hines_plan_uses_levels", "hines_plan_split", "hines_split_schedule",
+    "BPS_HINES_SEP", "hines_plan_uses_sep", "hines_sep_schedule",
     "bps_version", "bps_init", "bps_status_str", "bps_last_error", "PentaDesc",
 ]
 
@@ -46,6 +47,7 @@ BPS_HINES_AUTO = 0
 BPS_HINES_LANES = 1
 BPS_HINES_LEVELS = 2
 BPS_HINES_SPLIT = 3
+BPS_HINES_SEP = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "libbps.so")
@@ -118,6 +120,8 @@ def load_library():
             "hines_plan_create_sched": ([ctypes.POINTER(vp), i64, i32p, i32p, st, i64, st], st),
             "hines_plan_uses_levels": ([vp], st),
             "hines_plan_split": ([vp], i64),
+            "hines_plan_uses_sep": ([vp], st),
+            "hines_sep_schedule": ([ctypes.c_int32, i32p, i32p, ctypes.c_int32], ctypes.c_int32),
             "hines_split_schedule": ([ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_int32],
                                      ctypes.c_int32),
             "hines_plan_destroy": ([vp], st),
@@ -439,6 +443,11 @@ class HinesPlan:
         """Number of trees solved on two lanes."""
         return int(load_library().hines_plan_split(self.handle))
 
+    @property
+    def uses_sep(self) -> bool:
+        """True when the plan solves with BPS_HINES_SEP (sixteen lanes per neuron)."""
+        return bool(load_library().hines_plan_uses_sep(self.handle))
+
     def close(self):
         if self._h is not None:
             _check("hines_plan_destroy", load_library().hines_plan_destroy(self._h))
@@ -505,6 +514,42 @@ def hines_split_schedule(parent):
 
 def hines_plan_uses_levels(plan: HinesPlan) -> bool:
     return plan.uses_levels
+
+
+def hines_plan_uses_sep(plan: HinesPlan) -> bool:
+    return plan.uses_sep
+
+
+def hines_sep_schedule(parent):
+    """Host-only BPS_HINES_SEP schedule of one tree (see bps.h), decoded:
+    a dict with R, ns, nc, npc, nh, codes (16, R) uint32, bases (16, 3),
+    septab (ns, 5), comptab (nc, 3), clist (nc,); None when the tree does
+    not qualify."""
+    import numpy as np
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
+    n = len(par)
+    cap = 8 + 16 * 32 + 48 + 5 * n + 4 * n + 64
+    out = np.zeros(cap, dtype=np.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L = load_library()
+    m = L.hines_sep_schedule(n, par.ctypes.data_as(i32p), out.ctypes.data_as(i32p), cap)
+    if m < 0:
+        raise BpsError("hines_sep_schedule", 1, (L.bps_last_error() or b"").decode())
+    if m == 0:
+        return None
+    R, ns, nc, npc, nh = (int(v) for v in out[:5])
+    o = 8
+    codes = out[o:o + 16 * R].view(np.uint32).reshape(16, R).copy()
+    o += 16 * R
+    bases = out[o:o + 48].reshape(16, 3).copy()
+    o += 48
+    septab = out[o:o + ns * 5].reshape(ns, 5).copy()
+    o += ns * 5
+    comptab = out[o:o + nc * 3].reshape(nc, 3).copy()
+    o += nc * 3
+    clist = out[o:o + nc].copy()
+    return {"R": R, "ns": ns, "nc": nc, "npc": npc, "nh": nh, "codes": codes, "bases": bases,
+            "septab": septab, "comptab": comptab, "clist": clist}
 
 
 def hines_plan_destroy(plan: HinesPlan):

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbps.so")
-SOURCES = ["api.cpp", "penta.hip", "penta_spike.hip", "hyper.hip", "hines.hip", "tri.hip"]
+SOURCES = ["api.cpp", "penta.hip", "penta_spike.hip", "hyper.hip", "hines.hip", "hines_sep.hip", "tri.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

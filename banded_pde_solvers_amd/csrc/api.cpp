@@ -81,6 +81,8 @@ int64_t hines_plan_unknowns_of(const bps_hines_plan *p);
 int64_t hines_plan_batch_of(const bps_hines_plan *p);
 int64_t hines_plan_split_of(const bps_hines_plan *p);
 int32_t hines_split_rows(int32_t n, const int32_t *parent, int32_t *node, uint16_t *code, int32_t cap);
+bool hines_plan_sep(const bps_hines_plan *p);
+int32_t hines_sep_blob(int32_t n, const int32_t *parent, int32_t *out, int32_t cap, std::string &why);
 
 static const int64_t kMaxDim = int64_t(1) << 40;
 
@@ -547,6 +549,34 @@ int hines_plan_uses_levels(const bps_hines_plan *plan) { return plan && hines_pl
 
 int64_t hines_plan_split(const bps_hines_plan *plan) { return plan ? hines_plan_split_of(plan) : 0; }
 
+int hines_plan_uses_sep(const bps_hines_plan *plan) { return plan && hines_plan_sep(plan); }
+
+int32_t hines_sep_schedule(int32_t n, const int32_t *parent, int32_t *out, int32_t cap)
+{
+    clear_error();
+    if (!parent || !out || cap < 0) {
+        set_error("hines_sep_schedule: NULL array or negative cap");
+        return -1;
+    }
+    if (n < 1) {
+        set_error("hines_sep_schedule: n = %d out of range", n);
+        return -1;
+    }
+    for (int32_t i = 1; i < n; ++i)
+        if (parent[i] < 0 || parent[i] >= i) {
+            set_error("hines_sep_schedule: parent[%d] = %d not in [0, %d)", i, parent[i], i);
+            return -1;
+        }
+    std::string why;
+    const int32_t m = hines_sep_blob(n, parent, out, cap, why);
+    if (m == 0) set_error("hines_sep_schedule: %s", why.c_str());
+    if (m < 0) {
+        set_error("hines_sep_schedule: %d words do not fit cap = %d", -m, cap);
+        return -1;
+    }
+    return m;
+}
+
 int32_t hines_split_schedule(int32_t n, const int32_t *parent, int32_t *node, uint16_t *code,
                              int32_t cap)
 {
@@ -604,7 +634,7 @@ bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch, const i
         }
     }
     if (schedule != BPS_HINES_AUTO && schedule != BPS_HINES_LANES && schedule != BPS_HINES_LEVELS &&
-        schedule != BPS_HINES_SPLIT)
+        schedule != BPS_HINES_SPLIT && schedule != BPS_HINES_SEP)
         BPS_FAIL(BPS_EINVAL, "unknown schedule %d", schedule);
     CHECK(prepare_device());
     return hines_plan_build(plan, batch, sizes, parent, mono, ld, schedule);

@@ -67,6 +67,10 @@ struct bps_hines_plan {
     int32_t *lv_spar = nullptr;    // per tree: parent (new index) of each section head, -1 root
     int32_t *lv_lev = nullptr;     // per tree: section ranges per level, nlev + 1 entries
     int64_t *lv_tree = nullptr;    // per tree: perm base, sec base, lev base, nlev, n, data base
+    // sixteen lanes per neuron (mono, k_hines_sep): the schedule, on the
+    // host and on the device, when the plan uses it
+    std::vector<int32_t> sep;
+    int32_t *sep_dev = nullptr;
 };
 
 namespace bps {
@@ -918,7 +922,7 @@ static void free_plan(bps_hines_plan *p)
     (void)hipFree(p->lane_n); (void)hipFree(p->lane_src); (void)hipFree(p->src_off);
     (void)hipFree(p->lv_perm); (void)hipFree(p->lv_sec); (void)hipFree(p->lv_spar);
     (void)hipFree(p->lv_lev); (void)hipFree(p->lv_tree);
-    (void)hipFree(p->code16); (void)hipFree(p->comp);
+    (void)hipFree(p->code16); (void)hipFree(p->comp); (void)hipFree(p->sep_dev);
     delete p;
 }
 
@@ -1294,6 +1298,10 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
     }
     if (mono) total *= batch;
     const bool lv_fit = nmax <= kLevelMaxN;
+    if (sched == BPS_HINES_SEP && !mono) {
+        delete P;
+        BPS_FAIL(BPS_ENOTSUP, "BPS_HINES_SEP takes mono plans only");
+    }
     if (sched == BPS_HINES_LEVELS && !lv_fit) {
         delete P;
         BPS_FAIL(BPS_ENOTSUP, "level schedule needs trees of at most %d compartments", kLevelMaxN);
@@ -1313,6 +1321,16 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         for (int64_t i = 1; i < n; ++i) P->max_dist = std::max<int32_t>(P->max_dist, int32_t(i - h[i]));
         st = upload(&P->parent, h);
         if (st == BPS_OK && P->use_levels) st = build_levels(P, 1, sizes, parent, {});
+        if (st == BPS_OK && sched == BPS_HINES_SEP) {
+            std::string why;
+            if (n > 2047 || n * ld * 8 > int64_t(0xFFFF0000u)) why = n > 2047 ? "tree size above 2047" : "n * ld * 8 bytes above 4 GiB";
+            else P->sep = sep_schedule(int32_t(n), parent, why);
+            if (P->sep.empty()) {
+                free_plan(P);
+                BPS_FAIL(BPS_ENOTSUP, "BPS_HINES_SEP: %s", why.c_str());
+            }
+            st = upload(&P->sep_dev, P->sep);
+        }
     } else {
         std::vector<int64_t> off(batch + 1, 0);
         for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];
@@ -1402,17 +1420,28 @@ bps_status hines_plan_free(bps_hines_plan *p)
 // the current device.
 hipError_t hines_prepare_device()
 {
-    return hipFuncSetAttribute((const void *)k_hines_levels,
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               int(4 * kLevelMaxN * sizeof(double)));
+    const hipError_t e = hipFuncSetAttribute((const void *)k_hines_levels,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             int(4 * kLevelMaxN * sizeof(double)));
+    return e != hipSuccess ? e : sep_prepare_device();
 }
 
 bool hines_plan_general(const bps_hines_plan *p) { return p->max_dist > kRing; }
 bool hines_plan_levels(const bps_hines_plan *p) { return p->use_levels; }
+bool hines_plan_sep(const bps_hines_plan *p) { return p->sep_dev != nullptr; }
 int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }
 int64_t hines_plan_unknowns_of(const bps_hines_plan *p) { return p->unknowns; }
 int64_t hines_plan_batch_of(const bps_hines_plan *p) { return p->batch; }
 int64_t hines_plan_split_of(const bps_hines_plan *p) { return p->nsplit; }
+
+int32_t hines_sep_blob(int32_t n, const int32_t *parent, int32_t *out, int32_t cap, std::string &why)
+{
+    const std::vector<int32_t> b = sep_schedule(n, parent, why);
+    if (b.empty()) return 0;
+    if (int64_t(b.size()) > cap) return -int32_t(b.size());
+    std::copy(b.begin(), b.end(), out);
+    return int32_t(b.size());
+}
 
 int32_t hines_split_rows(int32_t n, const int32_t *parent, int32_t *node, uint16_t *code, int32_t cap)
 {
@@ -1480,6 +1509,9 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
         BPS_LAUNCHED("k_hines_levels");
         return BPS_OK;
     }
+    if (P->sep_dev)
+        return launch_hines_sep(P->sep.data(), P->sep_dev, P->batch, P->ld, P->parent, u, l, d, rhs,
+                                work, info, st);
     const bool gen = hines_plan_general(P);
     HinesArgs A{};
     A.batch = P->batch; A.n = P->n; A.ld = P->ld;

@@ -1,6 +1,9 @@
 // kernels.h -- host launchers of the HIP kernels (internal to libbps).
 #pragma once
 
+#include <string>
+#include <vector>
+
 #include "common.h"
 
 namespace bps {
@@ -75,6 +78,16 @@ size_t tri_work_bytes_es(int64_t n, int64_t ld, size_t es);
 template <typename T>
 bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
                             const void *c, void *y, void *work, int32_t *info, hipStream_t st);
+
+// Hines systems of one shared tree on sixteen lanes per neuron
+// (hines_sep.hip): the schedule of a tree (empty, reason in why, when the
+// tree does not qualify), the kernel's dynamic LDS, and its launch.
+std::vector<int32_t> sep_schedule(int32_t n, const int32_t *parent, std::string &why);
+size_t sep_lds_bytes(const int32_t *blob);
+hipError_t sep_prepare_device();
+bps_status launch_hines_sep(const int32_t *blob_host, const int32_t *blob_dev, int64_t batch, int64_t ld,
+                            const int32_t *parent_dev, const void *u, const void *l, const void *d,
+                            void *rhs, void *work, int32_t *info, hipStream_t st);
 
 // Number of values of a factor buffer.
 inline int64_t penta_factor_elems(int64_t n, int64_t ldf, bool cyclic) {

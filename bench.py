@@ -586,7 +586,7 @@ def _hines_common(args, multi, which=None):
 
     cfg = W.WORKLOADS[which if which is not None else (4 if multi else 3)]
     sched = {"auto": bps.BPS_HINES_AUTO, "lanes": bps.BPS_HINES_LANES, "split": bps.BPS_HINES_SPLIT,
-             "levels": bps.BPS_HINES_LEVELS}[args.hines_schedule]
+             "levels": bps.BPS_HINES_LEVELS, "sep": bps.BPS_HINES_SEP}[args.hines_schedule]
     if multi:
         mm = W.hines_multi(cfg["batch"], cfg["nmin"], cfg["nmax"])
         plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=sched)
@@ -620,9 +620,11 @@ def _hines_common(args, multi, which=None):
     alg_bytes = per_unknown * plan.unknowns
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     kname = ("k_hines_levels" if plan.uses_levels else
-             ("k_hines_split" if plan.split else "k_hines_multi") if multi else "k_hines_mono_reg")
+             ("k_hines_split" if plan.split else "k_hines_multi") if multi else
+             "k_hines_sep" if plan.uses_sep else "k_hines_mono_reg")
     traffic = _traffic("hines_levels" if plan.uses_levels else
-                       ("hines_split" if plan.split else "hines_multi") if multi else "hines_mono")
+                       ("hines_split" if plan.split else "hines_multi") if multi else
+                       "hines_sep" if plan.uses_sep else "hines_mono")
     line = {
         "metric": "unknowns solved/s (fp64), Hines " + ("multi" if multi else "mono"),
         "value": unknowns * args.steps / wall, "unit": "unknowns/s", "ms_per_step": ms_step,
@@ -633,7 +635,8 @@ def _hines_common(args, multi, which=None):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "schedule": "levels" if plan.uses_levels else
-                                 "two lanes for the largest trees" if plan.split else "one lane per neuron",
+                                 "two lanes for the largest trees" if plan.split else
+                                 "sixteen lanes per neuron (separators)" if plan.uses_sep else "one lane per neuron",
                      "kernel_ms": kern_ms, "timed": "one solve call", "bytes_per_launch": alg_bytes,
                      "counter_gbs": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9},
     }
@@ -722,7 +725,7 @@ def main():
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
     ap.add_argument("--split", action="store_true",
                     help="workloads 2, 9: time the separate factor and solve calls instead")
-    ap.add_argument("--hines-schedule", default="auto", choices=["auto", "lanes", "split", "levels"],
+    ap.add_argument("--hines-schedule", default="auto", choices=["auto", "lanes", "split", "levels", "sep"],
                     help="workloads 3, 4, 10: the plan's schedule (BPS_HINES_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -375,6 +375,25 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     its branches finish); a tree whose two-lane schedule
  *                     does not shorten it stays on one lane.  Mono plans:
  *                     as LANES;
+ *   BPS_HINES_SEP     mono plans of trees of at most 2047 compartments whose
+ *                     parents all lie within 8 compartments: sixteen lanes
+ *                     per neuron.  Single compartments (separators) cut the
+ *                     tree into components with at most one separator below
+ *                     each; every lane eliminates whole components (Algorithm
+ *                     1 inside each, holding its rows' factors in registers),
+ *                     the components' Schur complements on the separators
+ *                     form a smaller tree system solved by Algorithm 1, then
+ *                     the lanes substitute their rows: the per-branch
+ *                     decomposition of section 4 with the pages' solve of
+ *                     the reduced system, each compartment's values read and
+ *                     written once.  The elimination order differs from
+ *                     Algorithm 1's on the separators and on the paths from
+ *                     them up to their components' roots, so results differ
+ *                     by rounding; a neuron any of whose pivots in this order
+ *                     is zero or not finite is solved again by Algorithm 1
+ *                     in the same call (its info is Algorithm 1's).
+ *                     BPS_ENOTSUP for other plans or when no partition fits
+ *                     sixteen lanes of 32 rows;
  *   BPS_HINES_LEVELS  one wavefront per neuron: the tree cut into its
  *                     unbranched sections, grouped by level (the page's
  *                     per-branch / per-level decomposition of section 4),
@@ -393,7 +412,8 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  * (elements per array: hines_plan_elems; convert with hines_pack and
  * hines_unpack): a tree on two lanes has its compartments in the order its
  * schedule visits them. */
-enum { BPS_HINES_AUTO = 0, BPS_HINES_LANES = 1, BPS_HINES_LEVELS = 2, BPS_HINES_SPLIT = 3 };
+enum { BPS_HINES_AUTO = 0, BPS_HINES_LANES = 1, BPS_HINES_LEVELS = 2, BPS_HINES_SPLIT = 3,
+       BPS_HINES_SEP = 4 };
 
 /* hines_plan_create with an explicit schedule.  BPS_ENOTSUP for
  * BPS_HINES_LEVELS with a tree above 4096 compartments; BPS_EINVAL for an
@@ -406,6 +426,34 @@ BPS_API bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch,
 BPS_API int hines_plan_uses_levels(const bps_hines_plan *plan);
 /* Number of trees the plan solves on two lanes (0 for a NULL plan). */
 BPS_API int64_t hines_plan_split(const bps_hines_plan *plan);
+/* 1 if the plan solves with BPS_HINES_SEP (sixteen lanes per neuron), else 0. */
+BPS_API int hines_plan_uses_sep(const bps_hines_plan *plan);
+
+/* The schedule BPS_HINES_SEP would give one tree (host only, no device
+ * needed; for inspection and host-side tests), as int32 words:
+ *   [0] R rows per lane, [1] ns separators, [2] nc components, [3] npc
+ *   components with a separator below, [4] nh compartments on those
+ *   components' paths, [5] n, [6] 16 lanes, [7] 0;
+ *   then codes [16][R]: lane k's step t of the first sweep (the second
+ *   takes the steps in reverse): bits 0-10 the compartment, 11-13 its slot
+ *   in the lane's ring of pending updates and voltages, 14-16 its parent's
+ *   slot, 17 live (else padding), 18 on a path, 19 first row of a path, 20
+ *   root of its component;
+ *   then [16][3] per lane the numbers of its first component, first path
+ *   row and first component with a path (each numbered in the order the
+ *   lanes visit them, lane by lane);
+ *   then ns x 5 words per separator (in descending compartment order): the
+ *   compartment, its parent in the separator tree (-1 none), the component
+ *   it hangs below (-1 when its parent is a separator or it is the root),
+ *   and the range [b, e) of its components in the list below;
+ *   then nc x 3 words per component: its parent separator (-1 for the
+ *   root's component), the separator below it (-1 none), its path index
+ *   (-1 none); then nc words: components listed by parent separator.
+ *   parent: host int32[n], p_i in [0, i) (parent[0] ignored).
+ * Returns the number of words written to out (at most cap), 0 if the tree
+ * does not qualify (reason in bps_last_error), -1 on invalid arguments or
+ * cap below the words needed. */
+BPS_API int32_t hines_sep_schedule(int32_t n, const int32_t *parent, int32_t *out, int32_t cap);
 
 /* The two-lane schedule BPS_HINES_SPLIT would give one tree (host only, no
  * device needed; for inspection and host-side tests).

@@ -1,0 +1,225 @@
+"""Host-side checks of the sixteen-lane Hines schedule (BPS_HINES_SEP).
+
+The library's schedule of one tree (hines_sep_schedule, host only) is run
+through a plain Python replay of what the kernel does with it: the first
+sweep of every lane (ring slots read, cleared and added, the path
+coefficients of the components with a separator below), the separators'
+tree system, and the second sweep; the voltages are compared with the
+oracle's Algorithm 1 on the same tree.  A schedule that sent an update to a
+wrong slot, missed a compartment, or paired a separator with the wrong
+component gives wrong voltages here.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+bps = pytest.importorskip("banded_pde_solvers_amd")
+
+LIVE, PATH, PATH0, TOP = 1 << 17, 1 << 18, 1 << 19, 1 << 20
+
+
+def _lib_or_skip():
+    try:
+        bps.load_library()
+    except bps.BpsLibraryMissing:
+        pytest.skip("libbps.so not built")
+
+
+def _replay(p, u, l, d, rhs, S):
+    """The kernel's arithmetic for one neuron, lane by lane."""
+    R, ns, nc, npc, nh = S["R"], S["ns"], S["nc"], S["npc"], S["nh"]
+    codes, st, ct, cl, bases = S["codes"], S["septab"], S["comptab"], S["clist"], S["bases"]
+    n = len(p)
+    q = np.zeros((16, R))
+    m = np.zeros((16, R))
+    red = np.zeros((nc, 2))
+    pdat = np.zeros((npc, 4))
+    hbuf = np.zeros(nh + 2)
+    bad = False
+    with np.errstate(all="ignore"):
+        ends = np.zeros((16, 2), dtype=int)
+        for k in range(16):
+            ring = np.zeros((8, 2))
+            g = P = al = ga = 0.0
+            ccomp, chidx, cpidx = (int(v) for v in bases[k])
+            for t in range(R):
+                w0 = int(codes[k, t])
+                x = w0 & 2047
+                own, par = (w0 >> 11) & 7, (w0 >> 14) & 7
+                pd = ring[own].copy()
+                ring[own] = 0.0
+                dd = d[x] - pd[0]
+                rr = rhs[x] - pd[1]
+                bad |= bool(w0 & LIVE) and not (dd != 0.0 and np.isfinite(dd))
+                rcp = 1.0 / dd
+                q[k, t], m[k, t] = rr * rcp, l[x] * rcp
+                fac = u[x] * rcp
+                if w0 & PATH0:
+                    g, P, al, ga = 1.0, 1.0, 0.0, 0.0
+                h = g * rcp
+                if w0 & PATH:
+                    hbuf[chidx] = h
+                    chidx += 1
+                    al += P * q[k, t]
+                    ga -= P * h
+                    P = -m[k, t] * P
+                    g = -fac * g
+                cb = np.array([fac * l[x], fac * rr])
+                if w0 & TOP:
+                    red[ccomp] = cb
+                    ccomp += 1
+                    if w0 & PATH:
+                        pdat[cpidx] = (g, al, P, ga)
+                        cpidx += 1
+                else:
+                    ring[par] += cb
+            ends[k] = ccomp, chidx
+        # separators' system, descending compartment order
+        qm = np.zeros((ns, 2))
+        spend = np.zeros((ns, 2))
+        for i in range(ns):
+            x, rp, pc, cb_, ce = (int(v) for v in st[i])
+            dh, rh, lh, uh = d[x], rhs[x], 0.0, 0.0
+            for c in cl[cb_:ce]:
+                dh -= red[c, 0]
+                rh -= red[c, 1]
+            if pc >= 0:
+                ut, a_, b_, gm = pdat[ct[pc, 2]]
+                dh += l[x] * u[x] * gm
+                rh -= l[x] * a_
+                lh, uh = l[x] * b_, u[x] * ut
+            elif rp >= 0:
+                lh, uh = l[x], u[x]
+            dd = dh - spend[i, 0]
+            rr = rh - spend[i, 1]
+            bad |= not (dd != 0.0 and np.isfinite(dd))
+            qm[i] = rr / dd, lh / dd
+            if rp >= 0:
+                spend[rp] += (uh / dd * lh, uh / dd * rr)
+        sx = np.zeros(ns)
+        for i in range(ns - 1, -1, -1):
+            rp = int(st[i, 1])
+            sx[i] = qm[i, 0] - qm[i, 1] * (sx[rp] if rp >= 0 else 0.0)
+        for c in range(nc):
+            pc, sc = int(ct[c, 0]), int(ct[c, 1])
+            red[c] = (sx[pc] if pc >= 0 else 0.0,
+                      u[st[sc, 0]] * sx[sc] if sc >= 0 else 0.0)
+        V = np.full(n, np.nan)
+        V[st[:, 0]] = sx
+        for k in range(16):
+            ring = np.zeros(8)
+            sg = 0.0
+            ccomp, chidx = ends[k]
+            for t in range(R - 1, -1, -1):
+                w0 = int(codes[k, t])
+                par, own = (w0 >> 14) & 7, (w0 >> 11) & 7
+                if w0 & TOP:
+                    ccomp -= 1
+                    xp, sg = red[ccomp]
+                else:
+                    xp = ring[par]
+                if w0 & PATH:
+                    chidx -= 1
+                h = hbuf[chidx] if w0 & PATH else 0.0
+                xv = q[k, t] - m[k, t] * xp - h * sg
+                ring[own] = xv
+                if w0 & LIVE:
+                    V[w0 & 2047] = xv
+    return V, bad
+
+
+def _values(p, rng):
+    n = len(p)
+    u = rng.uniform(-1.0, 0.0, n)
+    l = rng.uniform(-1.0, 0.0, n)
+    u[0] = l[0] = 0.0
+    d = 1.0 + np.abs(l) + rng.uniform(0.0, 1.0, n)
+    for i in range(1, n):
+        d[p[i]] += abs(u[i])
+    return u, l, d, rng.uniform(-1.0, 1.0, n)
+
+
+def _trees():
+    rng = np.random.default_rng(91)
+    out = [("one", np.array([-1], dtype=np.int32)), ("two", np.array([-1, 0], dtype=np.int32))]
+    for n in (7, 33, 100, 257, 384, 512, 530):
+        out.append((f"window8_{n}", W.random_tree(n, rng)))
+    for w in (2, 4):
+        out.append((f"window{w}_500", W.random_tree(500, rng, window=w)))
+    out.append(("chain", np.r_[-1, np.arange(499)].astype(np.int32)))
+    out.append(("far8", np.array([-1] + [max(0, i - 8) for i in range(1, 480)], dtype=np.int32)))
+    cat = [-1] + [i - 2 if i % 2 == 0 else i - 1 for i in range(1, 501)]
+    out.append(("caterpillar", np.array(cat, dtype=np.int32)))
+    # a broom of short brooms: runs of 8 children on one parent
+    out.append(("broom", np.array([-1] + [max(0, i - 1 - (i - 1) % 8) for i in range(1, 200)],
+                                  dtype=np.int32)))
+    return out
+
+
+@pytest.mark.parametrize("name,p", _trees(), ids=lambda v: v if isinstance(v, str) else "")
+def test_sep_schedule_replay_matches_oracle(name, p):
+    _lib_or_skip()
+    n = len(p)
+    S = bps.hines_sep_schedule(p)
+    assert S is not None, name
+    codes = S["codes"]
+    live = (codes & LIVE) != 0
+    rows = codes & 2047
+    seps = S["septab"][:, 0]
+    # every compartment exactly once: on a lane or as a separator
+    assert np.array_equal(np.sort(np.r_[rows[live], seps]), np.arange(n))
+    # each lane's live rows first, padding after; separators in descending order
+    for k in range(16):
+        nl = int(live[k].sum())
+        assert live[k, :nl].all() and not live[k, nl:].any()
+    assert np.all(np.diff(seps) < 0)
+    assert live.sum(1).max() <= S["R"]
+    assert int(((codes & PATH) != 0).sum()) == S["nh"]
+    # each lane's bases count the components, path rows and path components before it
+    tops = ((codes & TOP) != 0).sum(1)
+    paths = ((codes & PATH) != 0).sum(1)
+    tp = (((codes & TOP) != 0) & ((codes & PATH) != 0)).sum(1)
+    np.testing.assert_array_equal(S["bases"][:, 0], np.r_[0, np.cumsum(tops)[:-1]])
+    np.testing.assert_array_equal(S["bases"][:, 1], np.r_[0, np.cumsum(paths)[:-1]])
+    np.testing.assert_array_equal(S["bases"][:, 2], np.r_[0, np.cumsum(tp)[:-1]])
+    u, l, d, rhs = _values(p, np.random.default_rng(n))
+    V, bad = _replay(p, u, l, d, rhs, S)
+    assert not bad
+    ref, info = oracle.hines_solve(p, u, l, d, rhs)
+    assert info[0] == 0
+    err = np.linalg.norm(V - ref[0]) / np.linalg.norm(ref[0])
+    assert err <= 1e-13, (name, err)
+
+
+def test_sep_schedule_shapes():
+    """On the workloads' trees of 512: sixteen lanes of at most 32 rows, a
+    few separators, and a share of path rows."""
+    _lib_or_skip()
+    rng = np.random.default_rng(4)
+    for _ in range(10):
+        S = bps.hines_sep_schedule(W.random_tree(512, rng))
+        assert S is not None and S["R"] == 32
+        assert 4 <= S["ns"] <= 40 and S["nh"] <= 200
+    small = bps.hines_sep_schedule(W.random_tree(200, rng))
+    assert small is not None and small["R"] == 16
+
+
+def test_sep_schedule_refusals():
+    _lib_or_skip()
+    # a parent 9 compartments away, and a tree too large for 16 x 32 rows
+    p9 = np.array([-1] + [max(0, i - 9) for i in range(1, 50)], dtype=np.int32)
+    assert bps.hines_sep_schedule(p9) is None
+    assert "8 compartments" in bps.bps_last_error()
+    assert bps.hines_sep_schedule(W.random_tree(1200, np.random.default_rng(1))) is None
+    with pytest.raises(bps.BpsError):
+        bps.hines_sep_schedule(np.array([-1, 0, 5], dtype=np.int32))
+    import ctypes
+    L = bps.load_library()
+    p = W.random_tree(300, np.random.default_rng(2))
+    out = np.full(64, -5, dtype=np.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    m = L.hines_sep_schedule(300, p.ctypes.data_as(i32p), out.ctypes.data_as(i32p), 64)
+    assert m == -1 and "cap" in bps.bps_last_error()
+    assert np.all(out == -5)
