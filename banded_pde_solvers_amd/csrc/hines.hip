@@ -1320,17 +1320,29 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         h[0] = 0;   // never read; keep it a valid index
         for (int64_t i = 1; i < n; ++i) P->max_dist = std::max<int32_t>(P->max_dist, int32_t(i - h[i]));
         st = upload(&P->parent, h);
-        if (st == BPS_OK && P->use_levels) st = build_levels(P, 1, sizes, parent, {});
-        if (st == BPS_OK && sched == BPS_HINES_SEP) {
+        // sixteen lanes per neuron: when asked for, and by default for trees
+        // it takes, unless small trees in a batch large enough to fill the
+        // GPU with one lane per neuron (measured: 128 compartments, 16384
+        // neurons 39.8 vs 47.2 us, 32768 neurons 63.4 vs 53.5 us; 256 and
+        // above faster at every batch, e.g. 512 x 65536 346 vs 437 us and
+        // 512 x 256 29.8 us against 79.7 with levels)
+        const bool sep_try = sched == BPS_HINES_SEP ||
+                             (sched == BPS_HINES_AUTO && (n >= 256 || n * batch <= (int64_t(1) << 21)));
+        if (st == BPS_OK && sep_try) {
             std::string why;
-            if (n > 2047 || n * ld * 8 > int64_t(0xFFFF0000u)) why = n > 2047 ? "tree size above 2047" : "n * ld * 8 bytes above 4 GiB";
+            if (n > 2047 || n * ld * 8 > int64_t(0xFFFF0000u))
+                why = n > 2047 ? "tree size above 2047" : "n * ld * 8 bytes above 4 GiB";
             else P->sep = sep_schedule(int32_t(n), parent, why);
-            if (P->sep.empty()) {
+            if (P->sep.empty() && sched == BPS_HINES_SEP) {
                 free_plan(P);
                 BPS_FAIL(BPS_ENOTSUP, "BPS_HINES_SEP: %s", why.c_str());
             }
-            st = upload(&P->sep_dev, P->sep);
+            if (!P->sep.empty()) {
+                P->use_levels = false;
+                st = upload(&P->sep_dev, P->sep);
+            }
         }
+        if (st == BPS_OK && P->use_levels) st = build_levels(P, 1, sizes, parent, {});
     } else {
         std::vector<int64_t> off(batch + 1, 0);
         for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];

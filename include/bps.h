@@ -400,14 +400,17 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     one section per lane and level, with the neuron held
  *                     in LDS; for batches too small to fill the GPU with one
  *                     lane per neuron.  Trees of at most 4096 compartments;
- *   BPS_HINES_AUTO    LEVELS for batches whose trees fit and that hold at
- *                     most 786432 compartments in all (mono) or 393216
- *                     (multi-morphology), else LANES; when one lane per
- *                     neuron would leave SIMDs of the GPU without a
- *                     wavefront (fewer than 1024 blocks of 64 neurons), the
- *                     largest trees go on two lanes as in SPLIT until the
- *                     blocks nearly fill them (what hines_plan_create
- *                     chooses).
+ *   BPS_HINES_AUTO    mono plans: SEP for trees it takes, when the tree
+ *                     has at least 256 compartments or the batch at most
+ *                     2^21 compartments in all.  Otherwise, and for
+ *                     multi-morphology plans: LEVELS for batches whose trees
+ *                     fit and that hold at most 786432 compartments in all
+ *                     (mono) or 393216 (multi-morphology), else LANES; when
+ *                     one lane per neuron would leave SIMDs of the GPU
+ *                     without a wavefront (fewer than 1024 blocks of 64
+ *                     neurons), the largest trees go on two lanes as in
+ *                     SPLIT until the blocks nearly fill them (what
+ *                     hines_plan_create chooses).
  * Every schedule takes the same arguments; the solver layout is the plan's
  * (elements per array: hines_plan_elems; convert with hines_pack and
  * hines_unpack): a tree on two lanes has its compartments in the order its
@@ -490,7 +493,8 @@ BPS_API bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const voi
 BPS_API size_t hines_work_bytes(const bps_hines_plan *plan, int dtype);
 
 /* Solve every neuron ([H] Algorithm 1) with the plan's schedule (one lane
- * per neuron, two lanes for split trees, or one wavefront per neuron).
+ * per neuron, two lanes for split trees, sixteen lanes per neuron with
+ * separators, or one wavefront per neuron).
  * u, l, d: device, solver layout, not modified.  rhs: device, solver layout,
  * right-hand side on entry, voltages V on return (as in [H]).  work: device,
  * hines_work_bytes bytes.  info: device int32[batch] indexed by the ORIGINAL

@@ -38,12 +38,20 @@ class _Problems:
         self.y = self.y0.clone()
         self.wt = buf(bps.tri_work_bytes(2048, 50))
         hm = W.hines_mono(512, 64, rng=rng)                            # Hines, level schedule
-        self.plan = bps.hines_plan_create(64, [512], hm.parent, mono=True)
+        self.plan = bps.hines_plan_create(64, [512], hm.parent, mono=True,
+                                          schedule=bps.BPS_HINES_LEVELS)
         assert self.plan.uses_levels
         self.hu, self.hl, self.hd = (dev(v) for v in (hm.u, hm.l, hm.d))
         self.r0 = dev(hm.rhs)
         self.r = self.r0.clone()
         self.wr = buf(bps.hines_work_bytes(self.plan))
+        hs = W.hines_mono(300, 40, rng=rng)                            # Hines, sixteen lanes
+        self.splan = bps.hines_plan_create(40, [300], hs.parent, mono=True)
+        assert self.splan.uses_sep
+        self.su, self.sl, self.sd = (dev(v) for v in (hs.u, hs.l, hs.d))
+        self.s0 = dev(hs.rhs)
+        self.s = self.s0.clone()
+        self.ws = buf(bps.hines_work_bytes(self.splan))
         pb = W.penta_dominant(256, 70, cyclic=True, rng=rng)           # periodic fused penta
         self.pd = [dev(v) for v in pb.diagonals]
         self.x0 = dev(pb.f)
@@ -52,7 +60,7 @@ class _Problems:
 
     def reset(self):
         for dst, src in ((self.C, self.C0), (self.Q, self.Q0), (self.y, self.y0),
-                         (self.r, self.r0), (self.x, self.x0)):
+                         (self.r, self.r0), (self.x, self.x0), (self.s, self.s0)):
             dst.copy_(src)
 
     def run(self):
@@ -61,9 +69,10 @@ class _Problems:
         bps.tri_solve_batch(self.ta, self.tb, self.tc, self.y, self.wt)
         bps.hines_solve_batch(self.plan, self.hu, self.hl, self.hd, self.r, self.wr)
         bps.penta_factor_solve_batch(*self.pd, self.x, self.wp, cyclic=True)
+        bps.hines_solve_batch(self.splan, self.su, self.sl, self.sd, self.s, self.ws)
 
     def outputs(self):
-        return [host(t) for t in (self.C, self.Q, self.y, self.r, self.x)]
+        return [host(t) for t in (self.C, self.Q, self.y, self.r, self.x, self.s)]
 
 
 def test_graph_capture_replay_bitwise():

@@ -462,9 +462,18 @@ def test_levels_breakdown_info():
 def test_levels_auto_choice_and_limits():
     rng = np.random.default_rng(13)
     p = W.random_tree(300, rng)
-    # automatic choice: at most 786432 compartments in the batch
-    assert bps.hines_plan_create(2621, [300], p, mono=True).uses_levels
-    assert not bps.hines_plan_create(2622, [300], p, mono=True).uses_levels
+    # automatic choice for mono trees whose parents lie within 8: sixteen lanes
+    assert bps.hines_plan_create(2621, [300], p, mono=True).uses_sep
+    assert bps.hines_plan_create(30000, [300], p, mono=True).uses_sep
+    small = W.random_tree(128, rng)
+    assert bps.hines_plan_create(16384, [128], small, mono=True).uses_sep      # 2^21 compartments
+    plan = bps.hines_plan_create(16385, [128], small, mono=True)
+    assert not plan.uses_sep and not plan.uses_levels
+    # other mono trees: levels for at most 786432 compartments in the batch
+    p16 = W.random_tree(300, rng, window=16)
+    assert (np.arange(1, 300) - p16[1:]).max() > 8
+    assert bps.hines_plan_create(2621, [300], p16, mono=True).uses_levels
+    assert not bps.hines_plan_create(2622, [300], p16, mono=True).uses_levels
     big = W.random_tree(5000, rng)
     assert not bps.hines_plan_create(10, [5000], big, mono=True).uses_levels
     # multi-morphology: at most 393216 compartments
@@ -479,13 +488,15 @@ def test_levels_auto_choice_and_limits():
 
 def test_small_batch_workload_full():
     """The benchmarked small batch (512 compartments, 256 neurons): the
-    automatic choice is the level schedule; every neuron against the oracle."""
+    automatic choice is sixteen lanes per neuron; every neuron against the
+    oracle, with that schedule and with the level schedule."""
     cfg = W.WORKLOADS[10]
     hm = W.hines_mono(cfg["n"], cfg["batch"], rng=W.rng_for(10))
     plan = bps.hines_plan_create(cfg["batch"], [cfg["n"]], hm.parent, mono=True)
-    assert plan.uses_levels
+    assert plan.uses_sep
     plan.close()
-    out, info = _solve_mono(hm)
     ref, _ = _oracle_mono(hm)
-    assert _cols_err(out, ref) <= 1e-10
-    assert np.all(info == 0)
+    for sched in (bps.BPS_HINES_AUTO, bps.BPS_HINES_LEVELS):
+        out, info = _solve_mono(hm, schedule=sched)
+        assert _cols_err(out, ref) <= 1e-10
+        assert np.all(info == 0)
