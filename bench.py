@@ -624,7 +624,7 @@ def _hines_common(args, multi, which=None):
              "k_hines_sep" if plan.uses_sep else "k_hines_mono_reg")
     traffic = _traffic("hines_levels" if plan.uses_levels else
                        ("hines_split" if plan.split else "hines_multi") if multi else
-                       "hines_sep" if plan.uses_sep else "hines_mono")
+                       f"hines_sep_n{cfg['n']}_b{cfg['batch']}" if plan.uses_sep else "hines_mono")
     line = {
         "metric": "unknowns solved/s (fp64), Hines " + ("multi" if multi else "mono"),
         "value": unknowns * args.steps / wall, "unit": "unknowns/s", "ms_per_step": ms_step,
