@@ -35,7 +35,7 @@ __all__ = [
     "hines_work_bytes", "hines_solve_batch", "BPS_HINES_AUTO", "BPS_HINES_LANES",
     "BPS_HINES_LEVELS", "BPS_HINES_SPLIT", "hines_plan_create_sched", "hines_plan_elems",
     "hines_plan_unknowns", "hines_plan_uses_levels", "hines_plan_split", "hines_split_schedule",
-    "BPS_HINES_SEP", "hines_plan_uses_sep", "hines_sep_schedule",
+    "BPS_HINES_SEP", "hines_plan_uses_sep", "hines_sep_schedule", "hines_sep_multi_layout",
     "bps_version", "bps_init", "bps_status_str", "bps_last_error", "PentaDesc",
 ]
 
@@ -122,6 +122,7 @@ def load_library():
             "hines_plan_split": ([vp], i64),
             "hines_plan_uses_sep": ([vp], st),
             "hines_sep_schedule": ([ctypes.c_int32, i32p, i32p, ctypes.c_int32], ctypes.c_int32),
+            "hines_sep_multi_layout": ([i64, i32p, i32p, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int32),
             "hines_split_schedule": ([ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_int32],
                                      ctypes.c_int32),
             "hines_plan_destroy": ([vp], st),
@@ -518,6 +519,38 @@ def hines_plan_uses_levels(plan: HinesPlan) -> bool:
 
 def hines_plan_uses_sep(plan: HinesPlan) -> bool:
     return plan.uses_sep
+
+
+def hines_sep_multi_layout(sizes, parent):
+    """Host-only BPS_HINES_SEP layout of a multi-morphology batch (see bps.h):
+    a dict with nwg, elems, R, lds, K (lanes per workgroup), code, comp, pos,
+    lanetab (nwg*K, 5), wgoff, tabs; None when the batch does not qualify."""
+    import numpy as np
+    sz = np.ascontiguousarray(np.asarray(sizes, dtype=np.int32).reshape(-1))
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L = load_library()
+    dims = np.zeros(6, dtype=np.int64)
+    st = L.hines_sep_multi_layout(len(sz), sz.ctypes.data_as(i32p), par.ctypes.data_as(i32p),
+                                  dims.ctypes.data, None, None, None, None, None, None)
+    if st < 0:
+        raise BpsError("hines_sep_multi_layout", 1, (L.bps_last_error() or b"").decode())
+    if st == 0:
+        return None
+    nwg, elems, R, lds, ntab, K = (int(v) for v in dims)
+    code = np.zeros(elems, dtype=np.uint16)
+    comp = np.zeros(elems, dtype=np.int32)
+    pos = np.zeros(int(sz.sum()), dtype=np.int32)
+    lanetab = np.zeros(nwg * K * 5, dtype=np.int32)
+    wgoff = np.zeros(nwg + 1, dtype=np.int64)
+    tabs = np.zeros(max(ntab, 1), dtype=np.int32)
+    st = L.hines_sep_multi_layout(len(sz), sz.ctypes.data_as(i32p), par.ctypes.data_as(i32p),
+                                  dims.ctypes.data, code.ctypes.data, comp.ctypes.data, pos.ctypes.data,
+                                  lanetab.ctypes.data, wgoff.ctypes.data, tabs.ctypes.data)
+    if st != 1:
+        raise BpsError("hines_sep_multi_layout", 1, (L.bps_last_error() or b"").decode())
+    return {"nwg": nwg, "elems": elems, "R": R, "lds": lds, "K": K, "code": code, "comp": comp,
+            "pos": pos, "lanetab": lanetab.reshape(nwg * K, 5), "wgoff": wgoff, "tabs": tabs}
 
 
 def hines_sep_schedule(parent):

@@ -551,6 +551,50 @@ int64_t hines_plan_split(const bps_hines_plan *plan) { return plan ? hines_plan_
 
 int hines_plan_uses_sep(const bps_hines_plan *plan) { return plan && hines_plan_sep(plan); }
 
+int32_t hines_sep_multi_layout(int64_t batch, const int32_t *sizes, const int32_t *parent, int64_t *dims,
+                               uint16_t *code, int32_t *comp, int32_t *pos, int32_t *lanetab,
+                               int64_t *wgoff, int32_t *tabs)
+{
+    clear_error();
+    if (batch < 1 || !sizes || !parent || !dims) {
+        set_error("hines_sep_multi_layout: NULL array or batch < 1");
+        return -1;
+    }
+    std::vector<int64_t> off(size_t(batch) + 1, 0);
+    for (int64_t s = 0; s < batch; ++s) {
+        const int32_t n = sizes[s];
+        if (n < 1 || n > (1 << 30)) {
+            set_error("hines_sep_multi_layout: sizes[%lld] = %d out of range", (long long)s, n);
+            return -1;
+        }
+        for (int32_t i = 1; i < n; ++i)
+            if (parent[off[s] + i] < 0 || parent[off[s] + i] >= i) {
+                set_error("hines_sep_multi_layout: neuron %lld: parent[%d] = %d not in [0, %d)",
+                          (long long)s, i, parent[off[s] + i], i);
+                return -1;
+            }
+        off[s + 1] = off[s] + n;
+    }
+    SepMulti M;
+    std::string why;
+    if (!sep_build_multi(batch, sizes, parent, off.data(), M, why)) {
+        set_error("hines_sep_multi_layout: %s", why.c_str());
+        return 0;
+    }
+    dims[0] = M.nwg; dims[1] = M.elems; dims[2] = M.R; dims[3] = int64_t(M.lds);
+    dims[4] = int64_t(M.tabs.size());
+    dims[5] = M.lanes;
+    if (code && comp && pos && lanetab && wgoff && tabs) {
+        std::copy(M.code.begin(), M.code.end(), code);
+        std::copy(M.comp.begin(), M.comp.end(), comp);
+        std::copy(M.pos.begin(), M.pos.end(), pos);
+        std::copy(M.lanetab.begin(), M.lanetab.end(), lanetab);
+        std::copy(M.wgoff.begin(), M.wgoff.end(), wgoff);
+        std::copy(M.tabs.begin(), M.tabs.end(), tabs);
+    }
+    return 1;
+}
+
 int32_t hines_sep_schedule(int32_t n, const int32_t *parent, int32_t *out, int32_t cap)
 {
     clear_error();

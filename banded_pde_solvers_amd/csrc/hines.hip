@@ -71,11 +71,18 @@ struct bps_hines_plan {
     // host and on the device, when the plan uses it
     std::vector<int32_t> sep;
     int32_t *sep_dev = nullptr;
+    // multi-morphology trees on their own lanes (k_hines_sepm): code16 and
+    // comp hold the row codes and the element map; the flat parents serve
+    // Algorithm 1 on a tree that breaks down
+    bool use_sepm = false;
+    bps::SepMultiDev sepm;
+    int32_t *flat_parent = nullptr;
 };
 
 namespace bps {
 
 constexpr int kRing = 16;       // LDS ring slots per lane (power of two)
+constexpr int kSepSlotsHost = 8;    // parent window of the sixteen-lane schedules
 constexpr int kLevelMaxN = 4096;        // tree size limit of the level schedule (LDS)
 // auto: the level schedule up to this many compartments in the batch.
 // Measured (one solve): trees of 512, 16 .. 1024 neurons: 77 .. 107 us with
@@ -923,6 +930,9 @@ static void free_plan(bps_hines_plan *p)
     (void)hipFree(p->lv_perm); (void)hipFree(p->lv_sec); (void)hipFree(p->lv_spar);
     (void)hipFree(p->lv_lev); (void)hipFree(p->lv_tree);
     (void)hipFree(p->code16); (void)hipFree(p->comp); (void)hipFree(p->sep_dev);
+    (void)hipFree(const_cast<int32_t *>(p->sepm.lanetab)); (void)hipFree(const_cast<int32_t *>(p->sepm.tabs));
+    (void)hipFree(const_cast<int32_t *>(p->sepm.pos)); (void)hipFree(const_cast<int64_t *>(p->sepm.wgoff));
+    (void)hipFree(p->flat_parent);
     delete p;
 }
 
@@ -1298,10 +1308,6 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
     }
     if (mono) total *= batch;
     const bool lv_fit = nmax <= kLevelMaxN;
-    if (sched == BPS_HINES_SEP && !mono) {
-        delete P;
-        BPS_FAIL(BPS_ENOTSUP, "BPS_HINES_SEP takes mono plans only");
-    }
     if (sched == BPS_HINES_LEVELS && !lv_fit) {
         delete P;
         BPS_FAIL(BPS_ENOTSUP, "level schedule needs trees of at most %d compartments", kLevelMaxN);
@@ -1347,6 +1353,32 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         std::vector<int64_t> off(batch + 1, 0);
         for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];
         P->unknowns = off[batch];
+        if (sched == BPS_HINES_SEP) {
+            SepMulti M;
+            std::string why;
+            if (!sep_build_multi(batch, sizes, parent, off.data(), M, why)) {
+                free_plan(P);
+                BPS_FAIL(BPS_ENOTSUP, "BPS_HINES_SEP: %s", why.c_str());
+            }
+            P->use_levels = false;
+            P->use_sepm = true;
+            P->elems = M.elems;
+            P->max_dist = kSepSlotsHost;
+            std::vector<int32_t> fp(parent, parent + off[batch]);
+            int32_t *lt = nullptr, *tb = nullptr, *ps = nullptr;
+            int64_t *wo = nullptr;
+            if ((st = upload(&P->code16, M.code)) == BPS_OK && (st = upload(&P->comp, M.comp)) == BPS_OK &&
+                (st = upload(&ps, M.pos)) == BPS_OK && (st = upload(&lt, M.lanetab)) == BPS_OK &&
+                (st = upload(&tb, M.tabs)) == BPS_OK && (st = upload(&wo, M.wgoff)) == BPS_OK &&
+                (st = upload(&P->src_off, off)) == BPS_OK)
+                st = upload(&P->flat_parent, fp);
+            P->sepm.nwg = M.nwg; P->sepm.elems = M.elems; P->sepm.lds = M.lds;
+            P->sepm.code = P->code16; P->sepm.lanetab = lt; P->sepm.tabs = tb; P->sepm.pos = ps;
+            P->sepm.wgoff = wo;
+            if (st != BPS_OK) { free_plan(P); return st; }
+            *out = P;
+            return BPS_OK;
+        }
         if (!P->use_levels && sched != BPS_HINES_LANES) {
             int32_t dmax = 0;
             for (int64_t s = 0; s < batch; ++s)
@@ -1440,7 +1472,7 @@ hipError_t hines_prepare_device()
 
 bool hines_plan_general(const bps_hines_plan *p) { return p->max_dist > kRing; }
 bool hines_plan_levels(const bps_hines_plan *p) { return p->use_levels; }
-bool hines_plan_sep(const bps_hines_plan *p) { return p->sep_dev != nullptr; }
+bool hines_plan_sep(const bps_hines_plan *p) { return p->sep_dev != nullptr || p->use_sepm; }
 int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }
 int64_t hines_plan_unknowns_of(const bps_hines_plan *p) { return p->unknowns; }
 int64_t hines_plan_batch_of(const bps_hines_plan *p) { return p->batch; }
@@ -1472,6 +1504,10 @@ template <typename T>
 bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, void *dst,
                            hipStream_t st)
 {
+    if (P->use_sepm) {
+        BPS_HIP(sepm_pack(pack, sizeof(T) == 8, P->comp, P->elems, src, dst, st));
+        return BPS_OK;
+    }
     if (P->mono) {
         const int64_t total = P->n * (pack ? P->ld : P->batch);
         const unsigned grid = unsigned(std::min<int64_t>((total + 255) / 256, 65536));
@@ -1521,6 +1557,8 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
         BPS_LAUNCHED("k_hines_levels");
         return BPS_OK;
     }
+    if (P->use_sepm)
+        return launch_hines_sepm(P->sepm, P->flat_parent, P->src_off, u, l, d, rhs, work, info, st);
     if (P->sep_dev)
         return launch_hines_sep(P->sep.data(), P->sep_dev, P->batch, P->ld, P->parent, u, l, d, rhs,
                                 work, info, st);

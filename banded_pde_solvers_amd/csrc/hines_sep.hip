@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cstring>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "common.h"
@@ -223,25 +224,41 @@ k_hines_sep(SepArgs A)
     if (k == 0) {
         int anyb = 0;
         for (int kk = 0; kk < kSepLanes; ++kk) anyb |= badf[kk * kSepNeurons + j];
+        // the next separator's row is read one step ahead; an update for the
+        // next separator is carried in registers, others go through LDS
+        double cf = 0.0, cl = 0.0, cr = 0.0;
+        double2 ndr = make_double2(0.0, 0.0), nlu = ndr;
+        if (ns > 0) { ndr = sepv[j * 2]; nlu = sepv[j * 2 + 1]; }
         for (int i = 0; i < ns; ++i) {
             const int rp = septab[i * 5 + 1];
-            const double2 dr = sepv[(i * kSepNeurons + j) * 2];
-            const double2 lu = sepv[(i * kSepNeurons + j) * 2 + 1];
+            const double2 dr0 = ndr, lu = nlu;
+            if (i + 1 < ns) {
+                ndr = sepv[((i + 1) * kSepNeurons + j) * 2];
+                nlu = sepv[((i + 1) * kSepNeurons + j) * 2 + 1];
+            }
+            const double2 dr = make_double2(fma(-cf, cl, dr0.x), fma(-cf, cr, dr0.y));
             anyb |= int(bad_pivot(dr.x));
             const double rcp = recip(dr.x);
             sepv[(i * kSepNeurons + j) * 2 + 1] = make_double2(dr.y * rcp, lu.x * rcp);
+            cf = 0.0;
             if (rp >= 0) {
                 const double f = lu.y * rcp;
-                double2 &t = sepv[(rp * kSepNeurons + j) * 2];
-                const double2 o = t;
-                t = make_double2(fma(-f, lu.x, o.x), fma(-f, dr.y, o.y));
+                if (rp == i + 1) {
+                    cf = f; cl = lu.x; cr = dr.y;
+                } else {
+                    double2 &t = sepv[(rp * kSepNeurons + j) * 2];
+                    const double2 o = t;
+                    t = make_double2(fma(-f, lu.x, o.x), fma(-f, dr.y, o.y));
+                }
             }
         }
+        double xn = 0.0;
         for (int i = ns - 1; i >= 0; --i) {
             const int rp = septab[i * 5 + 1];
             const double2 qm = sepv[(i * kSepNeurons + j) * 2 + 1];
-            const double xp = rp >= 0 ? sepv[(rp * kSepNeurons + j) * 2].x : 0.0;
-            sepv[(i * kSepNeurons + j) * 2].x = qm.x - qm.y * xp;
+            const double xp = rp < 0 ? 0.0 : rp == i + 1 ? xn : sepv[(rp * kSepNeurons + j) * 2].x;
+            xn = qm.x - qm.y * xp;
+            sepv[(i * kSepNeurons + j) * 2].x = xn;
         }
         flag[j] = anyb;
         if (!anyb && act && A.info) A.info[s] = 0;
@@ -304,6 +321,310 @@ k_hines_sep(SepArgs A)
     }
 }
 
+// ---- multi-morphology: every tree its own schedule ----------------------
+//
+// Trees are packed into workgroups of 128 lanes, each tree on as many lanes
+// as its components need (at most R rows per lane), the separators' own
+// rows among them.  Values are stored in schedule order: element (w, t, k)
+// -- workgroup w, step t, lane k -- at ((w R + t) 128 + k), so every step
+// of a wavefront is one contiguous 512-byte access; the row codes (16 bits)
+// use the same order.  A workgroup's separator and component tables are
+// copied into LDS.
+
+// Row code bits of the multi-morphology layout.
+constexpr uint32_t kMOwn = 7u, kMLive = 1u << 6, kMPath = 1u << 7, kMPath0 = 1u << 8,
+                   kMTop = 1u << 9, kMSep = 1u << 10;
+constexpr int kMHeader = 8;     // words of a workgroup's table header
+constexpr int kMThreads = 128;  // lanes per workgroup (four workgroups per CU)
+constexpr int kMTree = 5;       // words per tree: separator range, lane range, tree number
+
+struct SepMArgs {
+    uint32_t bytes;             // elems * 8
+    const uint16_t *code;       // [elems]
+    const int32_t *lanetab;     // [nwg * 128][5]: tree slot, bases (components, path rows,
+                                // path components, separators)
+    const int64_t *wgoff;       // [nwg + 1] word offsets into tabs
+    const int32_t *tabs;        // per workgroup: header, trees, 16-bit tables
+    const int32_t *pos;         // flat compartment -> element (Algorithm 1 after a breakdown)
+    const int32_t *parent;      // flat parents (local indices)
+    const int64_t *src_off;     // [batch + 1]
+    const double *u, *l, *d;
+    double *rhs, *work;
+    int32_t *info;
+};
+
+template <int R>
+__global__ void __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_hines_sepm(SepMArgs A)
+{
+    extern __shared__ __align__(16) unsigned char sep_lds[];
+    const int tid = threadIdx.x;
+    const int64_t w = blockIdx.x;
+    const int32_t *wt = A.tabs + A.wgoff[w];
+    const int nt = wt[0], ns = wt[1], nc = wt[2], npc = wt[3], nh = wt[4], n16 = wt[5];
+    double2 *ring = reinterpret_cast<double2 *>(sep_lds);     // [8][256]
+    double2 *red = ring + kSepSlots * kMThreads;             // [nc]
+    double2 *pdat = red + nc;                                  // [npc][2]
+    double2 *sepv = pdat + 2 * npc;                            // [ns][2]
+    double *su = reinterpret_cast<double *>(sepv + 2 * ns);    // [ns]
+    double *hbuf = su + ns;                                    // [nh + 2]
+    int *badf = reinterpret_cast<int *>(hbuf + nh + 2);        // [256]
+    int *tflag = badf + kMThreads;                           // [nt]
+    int *trees = tflag + nt;                                   // [nt][5]
+    int16_t *t16 = reinterpret_cast<int16_t *>(trees + nt * kMTree);   // septab, comptab, clist
+    const int16_t *septab = t16, *comptab = t16 + ns * 4, *clist = comptab + nc * 3;
+    for (int i = tid; i < nt * kMTree; i += kMThreads) trees[i] = wt[kMHeader + i];
+    {
+        const int32_t *src = wt + kMHeader + nt * kMTree;
+        int32_t *dst = reinterpret_cast<int32_t *>(t16);
+        for (int i = tid; i < (n16 + 1) / 2; i += kMThreads) dst[i] = src[i];
+    }
+#pragma unroll
+    for (int q = 0; q < kSepSlots; ++q) ring[q * kMThreads + tid] = make_double2(0.0, 0.0);
+    if (tid == 0) hbuf[nh] = 0.0;
+    const int32_t *lt = A.lanetab + (w * kMThreads + tid) * 5;
+    const int tslot = lt[0];
+    int ccomp = lt[1], chidx = lt[2], cpidx = lt[3], csep = lt[4];
+    __syncthreads();
+
+    const SepBuf U(A.u, A.bytes), L(A.l, A.bytes), Dg(A.d, A.bytes), Rh(A.rhs, A.bytes);
+    const SepBuf C(A.code, A.bytes / 4);
+    const uint32_t lane8 = uint32_t(tid) * 8;
+    auto rowoff = [&](int t) { return uint32_t((w * R + t) * kMThreads) * 8u; };   // bytes
+    auto code_at = [&](int t) {
+        return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(C.r, uint32_t(tid) * 2, rowoff(t) / 4, 0));
+    };
+
+    // ---- first sweep ----
+    double q[R], m[R];
+    constexpr int D = 8, CD = 16;
+    double bu[D], bl[D], bd[D], br[D];
+    uint32_t cc[CD];
+#pragma unroll
+    for (int t = 0; t < CD; ++t) cc[t] = t < R ? code_at(t) : 0u;
+    auto load = [&](int t, double dep) {
+        const uint32_t c = cc[t % CD];
+        uint32_t o = (c & (kMLive | kMSep)) ? lane8 : kSepNoStore;
+        asm volatile("" : "+v"(o) : "v"(dep));
+        const uint32_t so = rowoff(t);
+        bu[t % D] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(U.r, o, so, 0));
+        bl[t % D] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(L.r, o, so, 0));
+        bd[t % D] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(Dg.r, o, so, 0));
+        br[t % D] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(Rh.r, o, so, 0));
+    };
+#pragma unroll
+    for (int t = 0; t < D; ++t) load(t, 0.0);
+    int bad = 0;
+    double g = 0.0, P = 0.0, al = 0.0, ga = 0.0;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const uint32_t c = cc[t % CD];
+        const double u_ = bu[t % D], l_ = bl[t % D], d_ = bd[t % D], r_ = br[t % D];
+        const bool live = c & kMLive, path = c & kMPath, top = c & kMTop;
+        const int own = int(c & kMOwn), par = int((c >> 3) & kMOwn);
+        if (c & kMSep) {
+            sepv[csep * 2] = make_double2(d_, r_);
+            sepv[csep * 2 + 1] = make_double2(l_, u_);
+            su[csep] = u_;
+            ++csep;
+        }
+        const double2 pd = ring[own * kMThreads + tid];
+        const double2 po = ring[par * kMThreads + tid];
+        ring[own * kMThreads + tid] = make_double2(0.0, 0.0);
+        const double dd = d_ - pd.x, rr = r_ - pd.y;
+        bad |= int(live) & int(bad_pivot(dd));
+        asm volatile("" : "+v"(bad));
+        const double rcp = recip(dd);
+        const double qq = rr * rcp, mm = l_ * rcp, fac = u_ * rcp;
+        q[t] = qq;
+        m[t] = mm;
+        if (c & kMPath0) { g = 1.0; P = 1.0; al = 0.0; ga = 0.0; }
+        const double h = g * rcp;
+        hbuf[path ? chidx : nh + 1] = h;
+        if (path) {
+            ++chidx;
+            al = fma(P, qq, al);
+            ga = fma(-P, h, ga);
+            P = -mm * P;
+            g = -fac * g;
+        }
+        const double2 cb = live ? make_double2(fac * l_, fac * rr) : make_double2(0.0, 0.0);
+        if (top) {
+            red[ccomp] = cb;
+            ++ccomp;
+            if (path) {
+                pdat[cpidx * 2] = make_double2(g, al);
+                pdat[cpidx * 2 + 1] = make_double2(P, ga);
+                ++cpidx;
+            }
+        } else {
+            const double2 o = par == own ? make_double2(0.0, 0.0) : po;
+            ring[par * kMThreads + tid] = make_double2(o.x + cb.x, o.y + cb.y);
+        }
+        if (t + CD < R) {
+            uint32_t so = rowoff(t + CD) / 4;
+            asm volatile("" : "+s"(so) : "v"(qq));
+            cc[t % CD] = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(C.r, uint32_t(tid) * 2, so, 0));
+        }
+        if (t + D < R) load(t + D, qq);
+    }
+    badf[tid] = bad;
+    __syncthreads();
+
+    // ---- the separators' tree systems ----
+    for (int i = tid; i < ns; i += kMThreads) {
+        const int rp = septab[i * 4], pcomp = septab[i * 4 + 1];
+        const int cb = septab[i * 4 + 2], ce = septab[i * 4 + 3];
+        const double2 dr = sepv[i * 2], lu = sepv[i * 2 + 1];
+        double dh = dr.x, rh = dr.y, lh = 0.0, uh = 0.0;
+        for (int c = cb; c < ce; ++c) {
+            const double2 v = red[clist[c]];
+            dh -= v.x;
+            rh -= v.y;
+        }
+        if (pcomp >= 0) {
+            const int pi = comptab[pcomp * 3 + 2];
+            const double2 a = pdat[pi * 2], b = pdat[pi * 2 + 1];
+            dh = fma(lu.x * lu.y, b.y, dh);
+            rh = fma(-lu.x, a.y, rh);
+            lh = lu.x * b.x;
+            uh = lu.y * a.x;
+        } else if (rp >= 0) {
+            lh = lu.x;
+            uh = lu.y;
+        }
+        sepv[i * 2] = make_double2(dh, rh);
+        sepv[i * 2 + 1] = make_double2(lh, uh);
+    }
+    __syncthreads();
+    if (tid < nt) {
+        const int *tr = trees + tid * kMTree;
+        int anyb = 0;
+        for (int k = tr[2]; k < tr[3]; ++k) anyb |= badf[k];
+        // the next separator's row is read one step ahead; an update for the
+        // next separator is carried in registers, others go through LDS
+        const int s0 = tr[0], s1 = tr[1];
+        double cf = 0.0, cl = 0.0, cr = 0.0;
+        double2 ndr = make_double2(0.0, 0.0), nlu = ndr;
+        int nrp = -1;
+        if (s0 < s1) { ndr = sepv[s0 * 2]; nlu = sepv[s0 * 2 + 1]; nrp = septab[s0 * 4]; }
+        for (int i = s0; i < s1; ++i) {
+            const double2 dr0 = ndr, lu = nlu;
+            const int rp = nrp;
+            if (i + 1 < s1) { ndr = sepv[(i + 1) * 2]; nlu = sepv[(i + 1) * 2 + 1]; nrp = septab[(i + 1) * 4]; }
+            const double2 dr = make_double2(fma(-cf, cl, dr0.x), fma(-cf, cr, dr0.y));
+            anyb |= int(bad_pivot(dr.x));
+            const double rcp = recip(dr.x);
+            sepv[i * 2 + 1] = make_double2(dr.y * rcp, lu.x * rcp);
+            cf = 0.0;
+            if (rp >= 0) {
+                const double f = lu.y * rcp;
+                if (rp == i + 1) {
+                    cf = f; cl = lu.x; cr = dr.y;
+                } else {
+                    const double2 o = sepv[rp * 2];
+                    sepv[rp * 2] = make_double2(fma(-f, lu.x, o.x), fma(-f, dr.y, o.y));
+                }
+            }
+        }
+        double xn = 0.0;
+        for (int i = s1 - 1; i >= s0; --i) {
+            const int rp = septab[i * 4];
+            const double2 qm = sepv[i * 2 + 1];
+            const double xp = rp < 0 ? 0.0 : rp == i + 1 ? xn : sepv[rp * 2].x;
+            xn = qm.x - qm.y * xp;
+            sepv[i * 2].x = xn;
+        }
+        tflag[tid] = anyb;
+        if (!anyb && A.info) A.info[tr[4]] = 0;
+    }
+    __syncthreads();
+    for (int c = tid; c < nc; c += kMThreads) {
+        const int pc = comptab[c * 3], sc = comptab[c * 3 + 1];
+        const double xp = pc >= 0 ? sepv[pc * 2].x : 0.0;
+        const double sg = sc >= 0 ? su[sc] * sepv[sc * 2].x : 0.0;
+        red[c] = make_double2(xp, sg);
+    }
+    __syncthreads();
+
+    // ---- second sweep ----
+    const bool ok = tslot < 0 || tflag[tslot] == 0;
+    const SepBuf V(A.rhs, ok ? A.bytes : 0u);
+    double sg = 0.0;
+#pragma unroll
+    for (int t = R - 1; t >= 0; --t) {
+        const int ci = (R - 1 - t) % CD;
+        if (t == R - 1) {
+#pragma unroll
+            for (int k = 0; k < CD; ++k) cc[k] = R - 1 - k >= 0 ? code_at(R - 1 - k) : 0u;
+        }
+        const uint32_t c = cc[ci];
+        const bool top = c & kMTop, path = c & kMPath, live = c & kMLive, sepr = c & kMSep;
+        const int own = int(c & kMOwn), par = int((c >> 3) & kMOwn);
+        if (top) --ccomp;
+        if (path) --chidx;
+        if (sepr) --csep;
+        const double2 v = top ? red[ccomp] : ring[par * kMThreads + tid];
+        sg = top ? v.y : sg;
+        const double h = hbuf[path ? chidx : nh];
+        double x = q[t] - m[t] * v.x - h * sg;
+        reinterpret_cast<double *>(ring)[(own * kMThreads + tid) * 2] = x;
+        if (sepr) x = sepv[csep * 2].x;
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, x), V.r,
+            (live || sepr) ? lane8 : kSepNoStore, rowoff(t), 0);
+        if (t - CD >= 0) {
+            uint32_t so = rowoff(t - CD) / 4;
+            asm volatile("" : "+s"(so) : "v"(x));
+            cc[ci] = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(C.r, uint32_t(tid) * 2, so, 0));
+        }
+    }
+
+    // ---- a tree whose partitioned elimination met a bad pivot: Algorithm 1
+    // on one lane through the element map (pivots in work), which sets info ----
+    if (tid < nt && tflag[tid]) {
+        const int64_t T = trees[tid * kMTree + 4];
+        const int64_t o = A.src_off[T];
+        const int64_t n = A.src_off[T + 1] - o;
+        const int32_t *pos = A.pos + o, *par = A.parent + o;
+        double *rh = A.rhs, *wk = A.work;
+        for (int64_t i = 0; i < n; ++i) wk[pos[i]] = 0.0;
+        int32_t b = 0;
+        for (int64_t i = n - 1; i >= 1; --i) {
+            const int64_t e = pos[i], pe = pos[par[i]];
+            const double dd = A.d[e] - wk[e];
+            const double rr = rh[e];
+            if (!b && bad_pivot(dd)) b = int32_t(i + 1);
+            const double fac = A.u[e] / dd;
+            wk[pe] += fac * A.l[e];
+            rh[pe] -= fac * rr;
+            wk[e] = dd;
+        }
+        const int64_t e0 = pos[0];
+        const double d0 = A.d[e0] - wk[e0];
+        if (!b && bad_pivot(d0)) b = 1;
+        rh[e0] = rh[e0] / d0;
+        for (int64_t i = 1; i < n; ++i) {
+            const int64_t e = pos[i];
+            rh[e] = (rh[e] - A.l[e] * rh[pos[par[i]]]) / wk[e];
+        }
+        if (A.info) A.info[T] = b;
+    }
+}
+
+// flat <-> schedule-ordered layout through the element map
+template <typename T, bool PACK>
+__global__ void k_sepm_pack(const int32_t *__restrict__ gcomp, int64_t elems, const T *__restrict__ src,
+                            T *__restrict__ dst)
+{
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < elems;
+         e += int64_t(gridDim.x) * blockDim.x) {
+        const int32_t c = gcomp[e];
+        if (PACK) dst[e] = c >= 0 ? src[c] : T(0);
+        else if (c >= 0) dst[c] = src[e];
+    }
+}
+
 // ---------------------------------------------------------------- host --
 
 struct SepPart {
@@ -349,6 +670,155 @@ SepPart sep_partition(int32_t n, const int32_t *p, int32_t target)
 
 size_t sep_lds_bytes(const int32_t *blob);
 
+// One tree's schedule over L lanes of at most R rows each (host): each
+// lane's rows in first-sweep order, components and path rows numbered in
+// the lanes' order (lane by lane, so that a lane counts from its bases),
+// the separators in descending compartment order.  With sep_rows the
+// separators' own rows are also given to lanes (contiguous numbers per
+// lane, at the start of its rows: the multi-morphology kernel reads all
+// values through the lanes).
+struct SepRow {
+    int32_t node;
+    uint32_t flags;     // kSepLive, kSepPath, kSepPath0, kSepTop, kSepSepRow
+    int own, par;       // ring slots
+};
+constexpr uint32_t kSepSepRow = 1u << 21;   // a separator's own row (multi-morphology)
+
+struct SepTree {
+    int L = 0, R = 0;
+    int32_t ns = 0, nc = 0, npc = 0, nh = 0;
+    std::vector<std::vector<SepRow>> lanes;
+    std::vector<int32_t> snode, rp, pcomp;           // per separator (pcomp: component number)
+    std::vector<std::vector<int32_t>> schild;         // per separator: components below it
+    std::vector<int32_t> cpar, clow, cpid;            // per component number
+    std::vector<int32_t> cbase, hbase, pbase, sbase;  // per lane
+};
+
+static bool sep_tree(int32_t n, const int32_t *p, int L, int R, bool sep_rows, SepTree &T)
+{
+    for (int32_t target = std::min(R, 32); target >= 6; target -= 2) {
+        SepPart S = sep_partition(n, p, target);
+        const int32_t nc = int32_t(S.csize.size());
+        std::vector<int32_t> sidx(n, -1), snode;
+        for (int32_t v = n - 1; v >= 0; --v)
+            if (S.sep[v]) { sidx[v] = int32_t(snode.size()); snode.push_back(v); }
+        const int32_t ns = int32_t(snode.size());
+        // lanes: largest component first onto the least loaded lane
+        std::vector<int32_t> order(nc), load(L, 0);
+        for (int32_t c = 0; c < nc; ++c) order[c] = c;
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t a, int32_t b) { return S.csize[a] > S.csize[b]; });
+        std::vector<std::vector<int32_t>> lane(L);
+        for (int32_t c : order) {
+            const int l = int(std::min_element(load.begin(), load.end()) - load.begin());
+            load[l] += S.csize[c];
+            lane[l].push_back(c);
+        }
+        // separators' rows: contiguous numbers, lane by lane, to the lanes
+        // with room (fewest rows first)
+        std::vector<int32_t> scnt(L, 0);
+        if (sep_rows) {
+            for (int32_t i = 0; i < ns; ++i) {
+                const int l = int(std::min_element(load.begin(), load.end()) - load.begin());
+                load[l] += 1;
+                scnt[l] += 1;
+            }
+        }
+        if (*std::max_element(load.begin(), load.end()) > R) continue;
+        // components: root, parent separator, lower separator, path
+        std::vector<int32_t> croot(nc, -1), cpar(nc, -1), clow(nc, -1), cpi(nc, -1);
+        for (int32_t v = 0; v < n; ++v)
+            if (S.comp[v] >= 0 && croot[S.comp[v]] < 0) croot[S.comp[v]] = v;
+        for (int32_t c = 0; c < nc; ++c) cpar[c] = croot[c] == 0 ? -1 : sidx[p[croot[c]]];
+        std::vector<char> onpath(n, 0), first(n, 0);
+        std::vector<int32_t> rp(ns, -1), pcomp(ns, -1);
+        bool okc = true;
+        for (int32_t i = 0; i < ns; ++i) {
+            const int32_t sv = snode[i];
+            if (sv == 0) continue;
+            const int32_t pv = p[sv];
+            if (S.sep[pv]) { rp[i] = sidx[pv]; continue; }
+            const int32_t c = S.comp[pv];
+            if (clow[c] >= 0) { okc = false; break; }   // cannot happen by construction
+            clow[c] = i;
+            cpi[c] = 1;
+            pcomp[i] = c;
+            rp[i] = cpar[c];
+            first[pv] = 1;
+            for (int32_t v = pv; v >= 0 && S.comp[v] == c; v = v > 0 ? p[v] : -1) onpath[v] = 1;
+        }
+        if (!okc) continue;
+        // numbering in the lanes' order
+        T = SepTree();
+        T.L = L; T.R = R; T.ns = ns; T.nc = nc;
+        T.lanes.assign(L, {});
+        T.cbase.assign(L, 0); T.hbase.assign(L, 0); T.pbase.assign(L, 0); T.sbase.assign(L, 0);
+        std::vector<int32_t> cid(nc, -1);
+        int32_t nh = 0, ncid = 0, npid = 0, nsid = 0;
+        for (int l = 0; l < L; ++l) {
+            T.cbase[l] = ncid; T.hbase[l] = nh; T.pbase[l] = npid; T.sbase[l] = nsid;
+            for (int32_t q = 0; q < scnt[l]; ++q, ++nsid)
+                T.lanes[l].push_back({snode[nsid], kSepSepRow, 0, 0});
+            for (int32_t c : lane[l]) {
+                cid[c] = ncid++;
+                if (cpi[c] >= 0) npid++;
+                for (int32_t v = n - 1; v >= 0; --v)
+                    if (S.comp[v] == c) {
+                        uint32_t f = kSepLive;
+                        if (v == croot[c]) f |= kSepTop;
+                        if (onpath[v]) { f |= kSepPath; ++nh; }
+                        if (first[v]) f |= kSepPath0;
+                        T.lanes[l].push_back({v, f, v & 7, v == croot[c] ? 0 : (p[v] & 7)});
+                    }
+            }
+        }
+        T.nh = nh;
+        T.npc = npid;
+        T.snode = snode;
+        T.rp = rp;
+        T.pcomp.assign(ns, -1);
+        T.schild.assign(ns, {});
+        T.cpar.assign(nc, -1); T.clow.assign(nc, -1); T.cpid.assign(nc, -1);
+        std::vector<int32_t> byid(nc);
+        for (int32_t c = 0; c < nc; ++c) byid[cid[c]] = c;
+        int32_t q = 0;
+        for (int32_t c2 = 0; c2 < nc; ++c2) {
+            const int32_t c = byid[c2];
+            T.cpar[c2] = cpar[c];
+            T.clow[c2] = clow[c];
+            if (cpi[c] >= 0) T.cpid[c2] = q++;
+            if (cpar[c] >= 0) T.schild[cpar[c]].push_back(c2);
+        }
+        for (int32_t i = 0; i < ns; ++i) T.pcomp[i] = pcomp[i] >= 0 ? cid[pcomp[i]] : -1;
+        // replay the ring traffic of both sweeps: every slot read holds
+        // exactly the updates (first sweep) or the voltage (second sweep) of
+        // the compartment that reads it
+        for (int l = 0; l < L; ++l) {
+            int32_t owner[kSepSlots];
+            std::fill(owner, owner + kSepSlots, -1);
+            for (const SepRow &r : T.lanes[l]) {
+                if (!(r.flags & kSepLive)) continue;
+                if (owner[r.own] >= 0 && owner[r.own] != r.node) return false;
+                owner[r.own] = -1;
+                if (!(r.flags & kSepTop)) {
+                    if (owner[r.par] < 0) owner[r.par] = p[r.node];
+                    else if (owner[r.par] != p[r.node]) return false;
+                }
+            }
+            for (int k = 0; k < kSepSlots; ++k)
+                if (owner[k] >= 0) return false;
+            std::fill(owner, owner + kSepSlots, -1);
+            for (auto it = T.lanes[l].rbegin(); it != T.lanes[l].rend(); ++it) {
+                if (!(it->flags & kSepLive)) continue;
+                if (!(it->flags & kSepTop) && owner[it->par] != p[it->node]) return false;
+                owner[it->own] = it->node;
+            }
+        }
+        return true;
+    }
+    return false;
+}
+
 // The schedule of one tree (host): empty, with the reason, when the tree
 // does not qualify (a parent more than 8 compartments away, more than 2047
 // compartments, or no partition whose lanes fit R rows).
@@ -358,155 +828,232 @@ std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
     for (int32_t i = 1; i < n; ++i)
         if (i - p[i] > kSepSlots) { why = "a parent more than 8 compartments away"; return {}; }
     for (int R : {16, 32}) {
-        for (int32_t target = std::min(R, 32); target >= 6; target -= 2) {
-            SepPart S = sep_partition(n, p, target);
-            const int32_t nc = int32_t(S.csize.size());
-            std::vector<int32_t> sidx(n, -1), snode;
-            for (int32_t v = n - 1; v >= 0; --v)
-                if (S.sep[v]) { sidx[v] = int32_t(snode.size()); snode.push_back(v); }
-            const int32_t ns = int32_t(snode.size());
-            if (nc > 255 || ns > 255) continue;
-            // lanes: largest component first onto the least loaded lane
-            std::vector<int32_t> order(nc), load(kSepLanes, 0);
-            for (int32_t c = 0; c < nc; ++c) order[c] = c;
-            std::stable_sort(order.begin(), order.end(),
-                             [&](int32_t a, int32_t b) { return S.csize[a] > S.csize[b]; });
-            std::vector<std::vector<int32_t>> lane(kSepLanes);
-            for (int32_t c : order) {
-                const int l = int(std::min_element(load.begin(), load.end()) - load.begin());
-                load[l] += S.csize[c];
-                lane[l].push_back(c);
-            }
-            if (*std::max_element(load.begin(), load.end()) > R) continue;
-            // components: root, parent separator, lower separator, path
-            std::vector<int32_t> croot(nc, -1), cpar(nc, -1), clow(nc, -1), cpi(nc, -1);
-            for (int32_t v = 0; v < n; ++v)
-                if (S.comp[v] >= 0 && croot[S.comp[v]] < 0) croot[S.comp[v]] = v;
-            for (int32_t c = 0; c < nc; ++c) cpar[c] = croot[c] == 0 ? -1 : sidx[p[croot[c]]];
-            std::vector<char> onpath(n, 0), first(n, 0);
-            std::vector<int32_t> rp(ns, -1), pcomp(ns, -1);
-            int32_t npc = 0;
-            bool okc = true;
-            for (int32_t i = 0; i < ns; ++i) {
-                const int32_t sv = snode[i];
-                if (sv == 0) continue;
-                const int32_t pv = p[sv];
-                if (S.sep[pv]) { rp[i] = sidx[pv]; continue; }
-                const int32_t c = S.comp[pv];
-                if (clow[c] >= 0) { okc = false; break; }   // cannot happen by construction
-                clow[c] = i;
-                cpi[c] = npc++;
-                pcomp[i] = c;
-                rp[i] = cpar[c];
-                first[pv] = 1;
-                for (int32_t v = pv; v >= 0 && S.comp[v] == c; v = v > 0 ? p[v] : -1) onpath[v] = 1;
-            }
-            if (!okc) continue;
-            // numbering in the lanes' order: components, path rows, components
-            // with a path; each lane's first numbers are its bases
-            std::vector<int32_t> cid(nc, -1);
-            std::vector<int32_t> base(kSepLanes * 3, 0);
-            int32_t nh = 0, ncid = 0, npid = 0;
-            std::vector<std::vector<int32_t>> rows(kSepLanes);
-            for (int l = 0; l < kSepLanes; ++l) {
-                base[l * 3] = ncid; base[l * 3 + 1] = nh; base[l * 3 + 2] = npid;
-                for (int32_t c : lane[l]) {
-                    cid[c] = ncid++;
-                    if (cpi[c] >= 0) npid++;
-                    for (int32_t v = n - 1; v >= 0; --v)
-                        if (S.comp[v] == c) {
-                            rows[l].push_back(v);
-                            if (onpath[v]) ++nh;
-                        }
-                }
-            }
-            if (nh > 1000) continue;
-            // path data index in the lanes' order
-            std::vector<int32_t> pid(nc, -1);
-            {
-                int32_t q = 0;
-                for (int l = 0; l < kSepLanes; ++l)
-                    for (int32_t c : lane[l])
-                        if (cpi[c] >= 0) pid[c] = q++;
-            }
-            // blob
-            std::vector<int32_t> blob(kSepHeader + sep_tab_words(R, ns, nc), 0);
-            blob[0] = R; blob[1] = ns; blob[2] = nc; blob[3] = npc; blob[4] = nh; blob[5] = n;
-            blob[6] = kSepLanes;
-            int32_t *codes = blob.data() + kSepHeader;
-            for (int l = 0; l < kSepLanes; ++l) {
-                int t = 0;
-                for (int32_t v : rows[l]) {
-                    const int32_t c = S.comp[v];
-                    uint32_t w0 = uint32_t(v) | (uint32_t(v & 7) << 11) | kSepLive;
-                    if (v != croot[c]) w0 |= uint32_t(p[v] & 7) << 14;
-                    else w0 |= kSepTop;
-                    if (onpath[v]) w0 |= kSepPath;
-                    if (first[v]) w0 |= kSepPath0;
-                    codes[l * R + t] = int32_t(w0);
-                    ++t;
-                }
-            }
-            int32_t *bt = codes + kSepLanes * R;
-            std::copy(base.begin(), base.end(), bt);
-            int32_t *st = bt + kSepLanes * 3;
-            int32_t *ct = st + ns * 5;
-            int32_t *cl = ct + nc * 3;
-            int32_t ncl = 0;
-            std::vector<int32_t> byid(nc);
-            for (int32_t c = 0; c < nc; ++c) byid[cid[c]] = c;
-            for (int32_t i = 0; i < ns; ++i) {
-                st[i * 5] = snode[i];
-                st[i * 5 + 1] = rp[i];
-                st[i * 5 + 2] = pcomp[i] >= 0 ? cid[pcomp[i]] : -1;
-                st[i * 5 + 3] = ncl;
-                for (int32_t c2 = 0; c2 < nc; ++c2)
-                    if (cpar[byid[c2]] == i) cl[ncl++] = c2;
-                st[i * 5 + 4] = ncl;
-            }
-            for (int32_t c2 = 0; c2 < nc; ++c2) {
-                const int32_t c = byid[c2];
-                ct[c2 * 3] = cpar[c];
-                ct[c2 * 3 + 1] = clow[c];
-                ct[c2 * 3 + 2] = pid[c];
-            }
-            // replay the ring traffic of both sweeps: every slot read holds
-            // exactly the updates (first sweep) or the voltage (second sweep)
-            // of the compartment that reads it
-            bool good = true;
-            for (int l = 0; l < kSepLanes && good; ++l) {
-                int32_t owner[kSepSlots];
-                std::fill(owner, owner + kSepSlots, -1);
-                for (int t = 0; t < R && good; ++t) {
-                    const uint32_t w0 = uint32_t(codes[l * R + t]);
-                    if (!(w0 & kSepLive)) break;
-                    const int32_t v = int32_t(w0 & 2047);
-                    const int own = (w0 >> 11) & 7, par = (w0 >> 14) & 7;
-                    if (owner[own] >= 0 && owner[own] != v) good = false;
-                    owner[own] = -1;
-                    if (!(w0 & kSepTop)) {
-                        if (owner[par] < 0) owner[par] = p[v];
-                        else if (owner[par] != p[v]) good = false;
-                    }
-                }
-                for (int q = 0; q < kSepSlots; ++q) good = good && owner[q] < 0;
-                std::fill(owner, owner + kSepSlots, -1);
-                for (int t = R - 1; t >= 0 && good; --t) {
-                    const uint32_t w0 = uint32_t(codes[l * R + t]);
-                    if (!(w0 & kSepLive)) continue;
-                    const int32_t v = int32_t(w0 & 2047);
-                    const int own = (w0 >> 11) & 7, par = (w0 >> 14) & 7;
-                    if (!(w0 & kSepTop) && owner[par] != p[v]) good = false;
-                    owner[own] = v;
-                }
-            }
-            if (!good) { why = "internal: slot replay failed"; return {}; }
-            if (sep_lds_bytes(blob.data()) > 160 * 1024) continue;
-            return blob;
+        SepTree T;
+        if (!sep_tree(n, p, kSepLanes, R, false, T)) continue;
+        const int32_t ns = T.ns, nc = T.nc;
+        if (nc > 255 || ns > 255 || T.nh > 1000) continue;
+        std::vector<int32_t> blob(kSepHeader + sep_tab_words(R, ns, nc), 0);
+        blob[0] = R; blob[1] = ns; blob[2] = nc; blob[3] = T.npc; blob[4] = T.nh; blob[5] = n;
+        blob[6] = kSepLanes;
+        int32_t *codes = blob.data() + kSepHeader;
+        for (int l = 0; l < kSepLanes; ++l) {
+            int t = 0;
+            for (const SepRow &r : T.lanes[l])
+                codes[l * R + t++] = int32_t(uint32_t(r.node) | (uint32_t(r.own) << 11) |
+                                             (uint32_t(r.par) << 14) | r.flags);
         }
+        int32_t *bt = codes + kSepLanes * R;
+        for (int l = 0; l < kSepLanes; ++l) {
+            bt[l * 3] = T.cbase[l]; bt[l * 3 + 1] = T.hbase[l]; bt[l * 3 + 2] = T.pbase[l];
+        }
+        int32_t *st = bt + kSepLanes * 3;
+        int32_t *ct = st + ns * 5;
+        int32_t *cl = ct + nc * 3;
+        int32_t ncl = 0;
+        for (int32_t i = 0; i < ns; ++i) {
+            st[i * 5] = T.snode[i];
+            st[i * 5 + 1] = T.rp[i];
+            st[i * 5 + 2] = T.pcomp[i];
+            st[i * 5 + 3] = ncl;
+            for (int32_t c : T.schild[i]) cl[ncl++] = c;
+            st[i * 5 + 4] = ncl;
+        }
+        for (int32_t c = 0; c < nc; ++c) {
+            ct[c * 3] = T.cpar[c];
+            ct[c * 3 + 1] = T.clow[c];
+            ct[c * 3 + 2] = T.cpid[c];
+        }
+        if (sep_lds_bytes(blob.data()) > 160 * 1024) continue;
+        return blob;
     }
     why = "no partition fits 16 lanes of 32 rows";
     return {};
+}
+
+// Multi-morphology schedule (host): every tree its schedule (the fewest
+// lanes of at most 32 rows, separators' rows included), trees packed first
+// fit, largest first, into workgroups of 128 lanes whose LDS stays within
+// 40 KB (four workgroups per CU).  Fails, with the reason, when a tree does
+// not qualify.
+constexpr int kSepMR = 32;
+constexpr size_t kSepMLds = 40 * 1024;
+
+static size_t sepm_tree_lds(const SepTree &T)
+{
+    return size_t(T.nc) * 16 + size_t(T.npc) * 32 + size_t(T.ns) * 40 + size_t(T.nh) * 8 +
+           size_t(T.ns + T.nc) * 8 + 4 + 4 * kMTree;
+}
+static size_t sepm_fixed_lds() { return size_t(kSepSlots) * kMThreads * 16 + 16 + kMThreads * 4 + 8; }
+
+bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent, const int64_t *off,
+                     SepMulti &M, std::string &why)
+{
+    const int R = kSepMR;
+    std::vector<SepTree> tr(static_cast<size_t>(batch));
+    std::vector<int> fail(static_cast<size_t>(batch), 0);
+    const int nth = int(std::max<int64_t>(1, std::min<int64_t>(16, (batch + 255) / 256)));
+    std::vector<std::thread> th;
+    for (int k = 0; k < nth; ++k)
+        th.emplace_back([&, k] {
+            for (int64_t s = k; s < batch; s += nth) {
+                const int32_t n = sizes[s];
+                const int32_t *p = parent + off[s];
+                if (n > 8191) { fail[s] = 1; continue; }
+                bool ok = true;
+                for (int32_t i = 1; i < n && ok; ++i) ok = i - p[i] <= kSepSlots;
+                if (!ok) { fail[s] = 2; continue; }
+                int L = std::max(1, (n + 29) / 30);
+                while (L <= kMThreads && !sep_tree(n, p, L, R, true, tr[s])) ++L;
+                if (L > kMThreads || sepm_tree_lds(tr[s]) + sepm_fixed_lds() > kSepMLds) fail[s] = 3;
+            }
+        });
+    for (auto &t : th) t.join();
+    for (int64_t s = 0; s < batch; ++s)
+        if (fail[s]) {
+            why = fail[s] == 2 ? "a parent more than 8 compartments away" : "a tree too large for 128 lanes of 32 rows";
+            return false;
+        }
+    // best fit, largest first: each tree into the workgroup with the fewest
+    // free lanes that still holds it (and its LDS), workgroups bucketed by
+    // free lanes
+    std::vector<int64_t> order(static_cast<size_t>(batch));
+    for (int64_t s = 0; s < batch; ++s) order[s] = s;
+    std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) { return tr[a].L > tr[b].L; });
+    struct Bin { int lanes = 0; size_t lds = 0; std::vector<int64_t> trees; };
+    std::vector<Bin> bins;
+    std::vector<std::vector<int32_t>> bucket(kMThreads + 1);   // by free lanes
+    for (int64_t s : order) {
+        const int L = tr[s].L;
+        const size_t ld = sepm_tree_lds(tr[s]);
+        int32_t b = -1;
+        for (int f = L; f <= kMThreads && b < 0; ++f) {
+            auto &bk = bucket[f];
+            for (size_t q = 0; q < bk.size(); ++q)
+                if (sepm_fixed_lds() + bins[bk[q]].lds + ld <= kSepMLds) {
+                    b = bk[q];
+                    bk[q] = bk.back();
+                    bk.pop_back();
+                    break;
+                }
+        }
+        if (b < 0) {
+            b = int32_t(bins.size());
+            bins.emplace_back();
+        }
+        bins[b].lanes += L;
+        bins[b].lds += ld;
+        bins[b].trees.push_back(s);
+        bucket[kMThreads - bins[b].lanes].push_back(b);
+    }
+    const int64_t nwg = int64_t(bins.size());
+    const int64_t elems = nwg * R * kMThreads;
+    int64_t total = 0;
+    for (int64_t s = 0; s < batch; ++s) total += sizes[s];
+    if (elems * 8 > int64_t(0xFFFF0000u)) { why = "more than 4 GiB per array in the schedule-ordered layout"; return false; }
+    M = SepMulti();
+    M.R = R;
+    M.lanes = kMThreads;
+    M.nwg = nwg;
+    M.elems = elems;
+    M.code.assign(size_t(elems), 0);
+    M.comp.assign(size_t(elems), -1);
+    M.pos.assign(size_t(total), -1);
+    M.lanetab.assign(size_t(nwg) * kMThreads * 5, 0);
+    M.wgoff.assign(size_t(nwg) + 1, 0);
+    M.lds = 0;
+    for (int64_t wgi = 0; wgi < nwg; ++wgi) {
+        const Bin &B = bins[size_t(wgi)];
+        const int nt = int(B.trees.size());
+        int32_t ns = 0, nc = 0, npc = 0, nh = 0;
+        for (int64_t s : B.trees) { ns += tr[s].ns; nc += tr[s].nc; npc += tr[s].npc; nh += tr[s].nh; }
+        const int32_t n16 = ns * 4 + nc * 4;
+        std::vector<int32_t> tab(size_t(kMHeader + nt * kMTree + (n16 + 1) / 2), 0);
+        tab[0] = nt; tab[1] = ns; tab[2] = nc; tab[3] = npc; tab[4] = nh; tab[5] = n16;
+        int16_t *t16 = reinterpret_cast<int16_t *>(tab.data() + kMHeader + nt * kMTree);
+        int16_t *septab = t16, *comptab = t16 + ns * 4, *clist = comptab + nc * 3;
+        int32_t sb = 0, cb = 0, pb = 0, hb = 0, lane0 = 0, ncl = 0;
+        for (int ti = 0; ti < nt; ++ti) {
+            const int64_t s = B.trees[size_t(ti)];
+            const SepTree &T = tr[size_t(s)];
+            const int32_t *p = parent + off[s];
+            int32_t *trow = tab.data() + kMHeader + ti * kMTree;
+            trow[0] = sb; trow[1] = sb + T.ns; trow[2] = lane0; trow[3] = lane0 + T.L; trow[4] = int32_t(s);
+            for (int32_t i = 0; i < T.ns; ++i) {
+                septab[(sb + i) * 4] = int16_t(T.rp[i] >= 0 ? sb + T.rp[i] : -1);
+                septab[(sb + i) * 4 + 1] = int16_t(T.pcomp[i] >= 0 ? cb + T.pcomp[i] : -1);
+                septab[(sb + i) * 4 + 2] = int16_t(ncl);
+                for (int32_t c : T.schild[i]) clist[ncl++] = int16_t(cb + c);
+                septab[(sb + i) * 4 + 3] = int16_t(ncl);
+            }
+            for (int32_t c = 0; c < T.nc; ++c) {
+                comptab[(cb + c) * 3] = int16_t(T.cpar[c] >= 0 ? sb + T.cpar[c] : -1);
+                comptab[(cb + c) * 3 + 1] = int16_t(T.clow[c] >= 0 ? sb + T.clow[c] : -1);
+                comptab[(cb + c) * 3 + 2] = int16_t(T.cpid[c] >= 0 ? pb + T.cpid[c] : -1);
+            }
+            for (int l = 0; l < T.L; ++l) {
+                const int lane = lane0 + l;
+                int32_t *lt = M.lanetab.data() + (wgi * kMThreads + lane) * 5;
+                lt[0] = ti; lt[1] = cb + T.cbase[l]; lt[2] = hb + T.hbase[l]; lt[3] = pb + T.pbase[l];
+                lt[4] = sb + T.sbase[l];
+                int t = 0;
+                for (const SepRow &r : T.lanes[l]) {
+                    const int64_t e = (wgi * R + t) * kMThreads + lane;
+                    uint32_t c = uint32_t(r.own) | (uint32_t(r.par) << 3);
+                    if (r.flags & kSepLive) c |= kMLive;
+                    if (r.flags & kSepPath) c |= kMPath;
+                    if (r.flags & kSepPath0) c |= kMPath0;
+                    if (r.flags & kSepTop) c |= kMTop;
+                    if (r.flags & kSepSepRow) c |= kMSep;
+                    M.code[size_t(e)] = uint16_t(c);
+                    M.comp[size_t(e)] = int32_t(off[s] + r.node);
+                    M.pos[size_t(off[s] + r.node)] = int32_t(e);
+                    ++t;
+                }
+            }
+            (void)p;
+            sb += T.ns; cb += T.nc; pb += T.npc; hb += T.nh; lane0 += T.L;
+        }
+        for (int lane = lane0; lane < kMThreads; ++lane) M.lanetab[size_t((wgi * kMThreads + lane) * 5)] = -1;
+        M.wgoff[size_t(wgi) + 1] = M.wgoff[size_t(wgi)] + int64_t(tab.size());
+        M.tabs.insert(M.tabs.end(), tab.begin(), tab.end());
+        const size_t lds = sepm_fixed_lds() + size_t(nc) * 16 + size_t(npc) * 32 + size_t(ns) * 40 +
+                           size_t(nh + 2) * 8 + size_t(nt) * (4 + 4 * kMTree) + size_t(n16 + 2) * 2;
+        M.lds = std::max(M.lds, lds);
+    }
+    return true;
+}
+
+hipError_t sepm_pack(bool pack, bool f64, const int32_t *gcomp, int64_t elems, const void *src, void *dst,
+                     hipStream_t st)
+{
+    const unsigned grid = unsigned(std::min<int64_t>((elems + 255) / 256, 65536));
+    if (f64) {
+        if (pack) hipLaunchKernelGGL((k_sepm_pack<double, true>), dim3(grid), dim3(256), 0, st, gcomp, elems,
+                                     (const double *)src, (double *)dst);
+        else hipLaunchKernelGGL((k_sepm_pack<double, false>), dim3(grid), dim3(256), 0, st, gcomp, elems,
+                                (const double *)src, (double *)dst);
+    } else {
+        if (pack) hipLaunchKernelGGL((k_sepm_pack<float, true>), dim3(grid), dim3(256), 0, st, gcomp, elems,
+                                     (const float *)src, (float *)dst);
+        else hipLaunchKernelGGL((k_sepm_pack<float, false>), dim3(grid), dim3(256), 0, st, gcomp, elems,
+                                (const float *)src, (float *)dst);
+    }
+    return hipGetLastError();
+}
+
+bps_status launch_hines_sepm(const SepMultiDev &S, const int32_t *parent_dev, const int64_t *src_off,
+                             const void *u, const void *l, const void *d, void *rhs, void *work,
+                             int32_t *info, hipStream_t st)
+{
+    SepMArgs A{};
+    A.bytes = uint32_t(S.elems * 8);
+    A.code = S.code; A.lanetab = S.lanetab; A.wgoff = S.wgoff; A.tabs = S.tabs; A.pos = S.pos;
+    A.parent = parent_dev; A.src_off = src_off;
+    A.u = (const double *)u; A.l = (const double *)l; A.d = (const double *)d;
+    A.rhs = (double *)rhs; A.work = (double *)work; A.info = info;
+    hipLaunchKernelGGL(k_hines_sepm<kSepMR>, dim3(unsigned(S.nwg)), dim3(kMThreads), S.lds, st, A);
+    BPS_LAUNCHED("k_hines_sepm");
+    return BPS_OK;
 }
 
 size_t sep_lds_bytes(const int32_t *blob)
@@ -522,6 +1069,9 @@ hipError_t sep_prepare_device()
 {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_hines_sep<16>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_hines_sepm<kSepMR>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_hines_sep<32>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);

@@ -89,6 +89,35 @@ bps_status launch_hines_sep(const int32_t *blob_host, const int32_t *blob_dev, i
                             const int32_t *parent_dev, const void *u, const void *l, const void *d,
                             void *rhs, void *work, int32_t *info, hipStream_t st);
 
+// Multi-morphology trees, each its own sixteen-lane-style schedule, in a
+// schedule-ordered layout (hines_sep.hip): the host plan, its device copy,
+// the layout transform and the launch.
+struct SepMulti {
+    int R = 0, lanes = 0;           // rows per lane, lanes per workgroup
+    int64_t nwg = 0, elems = 0;
+    size_t lds = 0;
+    std::vector<uint16_t> code;      // [elems] row codes
+    std::vector<int32_t> comp;       // [elems] flat compartment, -1 padding
+    std::vector<int32_t> pos;        // [compartments] element of each flat compartment
+    std::vector<int32_t> lanetab;    // [nwg * lanes][5]
+    std::vector<int64_t> wgoff;      // [nwg + 1]
+    std::vector<int32_t> tabs;
+};
+struct SepMultiDev {
+    int64_t nwg = 0, elems = 0;
+    size_t lds = 0;
+    const uint16_t *code = nullptr;
+    const int32_t *lanetab = nullptr, *tabs = nullptr, *pos = nullptr;
+    const int64_t *wgoff = nullptr;
+};
+bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent, const int64_t *off,
+                     SepMulti &M, std::string &why);
+hipError_t sepm_pack(bool pack, bool f64, const int32_t *gcomp, int64_t elems, const void *src, void *dst,
+                     hipStream_t st);
+bps_status launch_hines_sepm(const SepMultiDev &S, const int32_t *parent_dev, const int64_t *src_off,
+                             const void *u, const void *l, const void *d, void *rhs, void *work,
+                             int32_t *info, hipStream_t st);
+
 // Number of values of a factor buffer.
 inline int64_t penta_factor_elems(int64_t n, int64_t ldf, bool cyclic) {
     return cyclic ? (9 * (n - 2) + 4) * ldf : 5 * n * ldf;

@@ -620,10 +620,11 @@ def _hines_common(args, multi, which=None):
     alg_bytes = per_unknown * plan.unknowns
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     kname = ("k_hines_levels" if plan.uses_levels else
-             ("k_hines_split" if plan.split else "k_hines_multi") if multi else
-             "k_hines_sep" if plan.uses_sep else "k_hines_mono_reg")
+             ("k_hines_sepm" if plan.uses_sep else "k_hines_split" if plan.split else "k_hines_multi")
+             if multi else "k_hines_sep" if plan.uses_sep else "k_hines_mono_reg")
     traffic = _traffic("hines_levels" if plan.uses_levels else
-                       ("hines_split" if plan.split else "hines_multi") if multi else
+                       ("hines_sepm" if plan.uses_sep else "hines_split" if plan.split else "hines_multi")
+                       if multi else
                        f"hines_sep_n{cfg['n']}_b{cfg['batch']}" if plan.uses_sep else "hines_mono")
     line = {
         "metric": "unknowns solved/s (fp64), Hines " + ("multi" if multi else "mono"),

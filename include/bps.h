@@ -473,6 +473,34 @@ BPS_API int32_t hines_sep_schedule(int32_t n, const int32_t *parent, int32_t *ou
 BPS_API int32_t hines_split_schedule(int32_t n, const int32_t *parent, int32_t *node,
                                      uint16_t *code, int32_t cap);
 
+/* The schedule BPS_HINES_SEP gives a multi-morphology batch (host only, no
+ * device needed; for inspection and host-side tests).  sizes, parent as
+ * for hines_plan_create with mono == 0.  dims: host int64[6], set to the
+ * number of workgroups, the elements per value array of the
+ * schedule-ordered layout (element (w, t, k) = workgroup w, step t < R,
+ * lane k < K at ((w R + t) K + k)), R, the kernel's LDS bytes per
+ * workgroup, the words of the workgroups' tables, and K, the lanes per
+ * workgroup.  When every other pointer is non-NULL they receive (sized
+ * from a first call with NULL arrays): code[elems] the row codes (bits 0-2
+ * the row's ring slot, 3-5 its parent's, 6 live, 7 on a path, 8 first row
+ * of a path, 9 root of its component, 10 a separator's own row),
+ * comp[elems] the flat compartment of each element (-1 padding),
+ * pos[sum(sizes)] the element of each flat compartment,
+ * lanetab[workgroups * K][5] per lane its tree's slot in the workgroup (-1
+ * unused) and its first component, path row, path component and separator
+ * numbers, wgoff[workgroups + 1] and tabs: per workgroup 8 header words
+ * (trees, separators, components, path components, path rows, 16-bit
+ * table entries), 5 words per tree (separator range, lane range, tree
+ * number) and 16-bit tables (per separator: its parent separator, the
+ * component it hangs below, its range of components below; per component:
+ * parent separator, lower separator, path index; the component list), all
+ * numbered within the workgroup.
+ * Returns 1, 0 if the batch does not qualify (reason in bps_last_error),
+ * -1 on invalid arguments. */
+BPS_API int32_t hines_sep_multi_layout(int64_t batch, const int32_t *sizes, const int32_t *parent,
+                                       int64_t *dims, uint16_t *code, int32_t *comp, int32_t *pos,
+                                       int32_t *lanetab, int64_t *wgoff, int32_t *tabs);
+
 /* Elements of one value array (u, l, d or rhs) in the plan's solver layout. */
 BPS_API int64_t hines_plan_elems(const bps_hines_plan *plan);
 /* Real compartments (sum of sizes, or n*batch for mono). */

@@ -1,13 +1,16 @@
-"""GPU parity: the sixteen-lane Hines schedule (BPS_HINES_SEP) against the oracle.
+"""GPU parity: the separator Hines schedules (BPS_HINES_SEP) against the oracle.
 
 Per-neuron normwise relative error <= 1e-10 through the C-ABI, on ragged
 batches (not a multiple of the 16 neurons of a workgroup), ld > batch, both
 row counts per lane (16 and 32), chains (every component a path), the
 largest trees the schedule takes, breakdowns (info equals Algorithm 1's and
 the other neurons are unaffected), repeatability, and sampled neurons of
-the full 100000 x 512 workload."""
+the full 100000 x 512 workload; multi-morphology batches (every tree its own
+schedule, the schedule-ordered layout) likewise, with the pack contract and
+the full 32768-neuron workload sampled."""
 import numpy as np
 import pytest
+import torch
 
 import banded_pde_solvers_amd as bps
 import oracle
@@ -126,8 +129,9 @@ def test_sep_refusals_and_auto():
     with pytest.raises(bps.BpsError):
         bps.hines_plan_create(64, [1500], W.random_tree(1500, rng), mono=True, schedule=SEP)
     sizes = np.full(4, 50, dtype=np.int32)
+    p9 = np.array([-1] + [max(0, i - 9) for i in range(1, 50)], dtype=np.int32)
     with pytest.raises(bps.BpsError):
-        bps.hines_plan_create(4, sizes, np.concatenate([W.random_tree(50, rng)] * 4), mono=False,
+        bps.hines_plan_create(4, sizes, np.concatenate([W.random_tree(50, rng)] * 3 + [p9]), mono=False,
                               schedule=SEP)
 
 
@@ -143,3 +147,98 @@ def test_sep_full_workload_sampled():
     ref, _ = _oracle(sub)
     assert _cols_err(out[:, cols], ref) <= 1e-10
     assert np.all(info == 0)
+
+
+# ---- multi-morphology: every tree its own schedule -------------------------------
+
+def _run_multi(mm, schedule=SEP, twice=False):
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=schedule)
+    if schedule == SEP:
+        assert plan.uses_sep and not plan.uses_levels and plan.split == 0
+    E = plan.elems
+    packed = [torch.empty(E, dtype=torch.float64, device="cuda:0") for _ in range(4)]
+    for src, dst in zip((mm.u, mm.l, mm.d, mm.rhs), packed):
+        bps.hines_pack(plan, dev(src), dst)
+    r0 = packed[3].clone()
+    work = buf(bps.hines_work_bytes(plan))
+    info = info_buf(mm.batch)
+    bps.hines_solve_batch(plan, *packed, work, info)
+    if twice:
+        bps.hines_solve_batch(plan, *packed[:3], r0, work, info)
+        np.testing.assert_array_equal(host(r0), host(packed[3]))          # bitwise repeatable
+    flat = torch.empty(len(mm.u), dtype=torch.float64, device="cuda:0")
+    bps.hines_unpack(plan, packed[3], flat)
+    out = host(flat)
+    dflat = torch.empty_like(flat)
+    bps.hines_unpack(plan, packed[2], dflat)
+    np.testing.assert_array_equal(host(dflat), mm.d)
+    plan.close()
+    return out, host(info).astype(int)
+
+
+def _multi_err(mm, out, ref, skip=()):
+    o = mm.offsets
+    return max(np.linalg.norm(out[o[s]:o[s + 1]] - ref[o[s]:o[s + 1]]) / np.linalg.norm(ref[o[s]:o[s + 1]])
+               for s in range(mm.batch) if s not in skip)
+
+
+@pytest.mark.parametrize("batch,nmin,nmax", [(1, 1, 1), (3, 2, 40), (40, 30, 300), (300, 256, 2048),
+                                             (5000, 1, 100), (70000, 30, 60)])
+def test_sep_multi_matches_oracle(batch, nmin, nmax):
+    print(f"hines sep multi batch={batch} n={nmin}..{nmax}", flush=True)
+    mm = W.hines_multi(batch, nmin, nmax, rng=np.random.default_rng(batch + nmax))
+    out, info = _run_multi(mm, twice=(batch == 300))
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    assert _multi_err(mm, out, ref) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+
+
+def test_sep_multi_breakdown_info():
+    rng = np.random.default_rng(12)
+    mm = W.hines_multi(40, 200, 400, rng=rng)
+    bad = {3: "zero_leaf", 8: "nan_mid", 21: "inf_root"}
+    for s, kind in bad.items():
+        o0, n = mm.offsets[s], int(mm.sizes[s])
+        if kind == "zero_leaf":
+            mm.d[o0 + n - 1] = 0.0
+        elif kind == "nan_mid":
+            mm.d[o0 + n // 3] = np.nan
+        else:
+            mm.d[o0] = np.inf
+    print("hines sep multi breakdown", flush=True)
+    out, info = _run_multi(mm)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    np.testing.assert_array_equal(info, rinfo)
+    assert info[3] == mm.sizes[3] and info[8] == mm.sizes[8] // 3 + 1 and info[21] == 1
+    assert _multi_err(mm, out, ref, skip=bad) <= 1e-10
+
+
+def test_sep_multi_pack_contract():
+    """hines_pack writes every compartment once and 0 to every other element;
+    hines_unpack inverts it exactly."""
+    mm = W.hines_multi(150, 30, 500, rng=np.random.default_rng(13))
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=SEP)
+    packed = torch.empty(plan.elems, dtype=torch.float64, device="cuda:0")
+    x = np.arange(1, len(mm.u) + 1, dtype=np.float64)
+    bps.hines_pack(plan, dev(x), packed)
+    pk = host(packed)
+    assert np.count_nonzero(pk) == len(x) and np.array_equal(np.sort(pk[pk != 0]), x)
+    back = torch.empty(len(x), dtype=torch.float64, device="cuda:0")
+    bps.hines_unpack(plan, packed, back)
+    np.testing.assert_array_equal(host(back), x)
+    plan.close()
+
+
+@pytest.mark.slow
+def test_sep_multi_full_workload_sampled():
+    cfg = W.WORKLOADS[4]
+    print(f"full hines multi {cfg['batch']} neurons sep", flush=True)
+    mm = W.hines_multi(cfg["batch"], cfg["nmin"], cfg["nmax"])
+    out, info = _run_multi(mm)
+    assert np.all(info == 0)
+    pick = np.unique(np.r_[0, cfg["batch"] - 1, np.random.default_rng(4).integers(0, cfg["batch"], 150)])
+    for s in pick:
+        p, u, l, d, r = mm.neuron(s)
+        V, _ = oracle.hines_solve(p, u, l, d, r)
+        got = out[mm.offsets[s]:mm.offsets[s + 1]]
+        assert np.linalg.norm(got - V[0]) / np.linalg.norm(V[0]) <= 1e-10
