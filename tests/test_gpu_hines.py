@@ -249,8 +249,9 @@ def test_multi_split_auto_choice():
     """The automatic choice puts trees on two lanes, largest first, while one
     lane per neuron leaves SIMDs without a wavefront (fewer than 1024 blocks
     of 64), and none when the blocks fill them."""
-    print("hines multi split auto 2048 neurons of 256..2048", flush=True)
-    mm = W.hines_multi(2048, 256, 2048, rng=np.random.default_rng(41))
+    print("hines multi split auto 2048 neurons of 256..2048 (parents within 16)", flush=True)
+    mm = W.hines_multi(2048, 256, 2048, rng=np.random.default_rng(41), window=16)
+    assert max(np.max(np.arange(1, n) - mm.neuron(s)[0][1:]) for s, n in enumerate(mm.sizes)) > 8
     plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
     assert not plan.uses_levels
     assert plan.split >= 0.95 * mm.batch
@@ -476,9 +477,10 @@ def test_levels_auto_choice_and_limits():
     assert not bps.hines_plan_create(2622, [300], p16, mono=True).uses_levels
     big = W.random_tree(5000, rng)
     assert not bps.hines_plan_create(10, [5000], big, mono=True).uses_levels
-    # multi-morphology: at most 393216 compartments
+    # multi-morphology trees the separator schedules do not take (parents up
+    # to 16 away): at most 393216 compartments
     sizes = np.full(768, 512, dtype=np.int32)
-    par = np.concatenate([W.random_tree(512, rng) for _ in range(769)])
+    par = np.concatenate([W.random_tree(512, rng, window=16) for _ in range(769)])
     assert bps.hines_plan_create(768, sizes, par[:768 * 512], mono=False).uses_levels
     plan = bps.hines_plan_create(769, np.full(769, 512, dtype=np.int32), par, mono=False)
     assert not plan.uses_levels and plan.split == 769

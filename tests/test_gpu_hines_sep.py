@@ -242,3 +242,30 @@ def test_sep_multi_full_workload_sampled():
         V, _ = oracle.hines_solve(p, u, l, d, r)
         got = out[mm.offsets[s]:mm.offsets[s + 1]]
         assert np.linalg.norm(got - V[0]) / np.linalg.norm(V[0]) <= 1e-10
+
+
+def test_sep_multi_auto_choice():
+    """The automatic choice for multi-morphology batches: separator schedules
+    when every tree has its parents within 8 and the trees average at least
+    128 compartments; otherwise the other schedules."""
+    rng = np.random.default_rng(23)
+    mm = W.hines_multi(300, 100, 160, rng=rng)
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
+    assert plan.uses_sep == (mm.sizes.mean() >= 128)
+    plan.close()
+    big = W.hines_multi(64, 256, 2048, rng=rng)
+    plan = bps.hines_plan_create(big.batch, big.sizes, big.parent, mono=False)
+    assert plan.uses_sep and not plan.uses_levels and plan.split == 0
+    plan.close()
+    small = W.hines_multi(64, 30, 60, rng=rng)
+    plan = bps.hines_plan_create(small.batch, small.sizes, small.parent, mono=False)
+    assert not plan.uses_sep
+    plan.close()
+    w16 = W.hines_multi(64, 256, 2048, rng=rng, window=16)
+    plan = bps.hines_plan_create(w16.batch, w16.sizes, w16.parent, mono=False)
+    assert not plan.uses_sep
+    plan.close()
+    out, info = _run_multi(big, schedule=bps.BPS_HINES_AUTO)
+    ref, rinfo = oracle.hines_multi_solve(big.offsets, big.parent, big.u, big.l, big.d, big.rhs)
+    assert _multi_err(big, out, ref) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)

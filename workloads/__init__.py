@@ -292,8 +292,9 @@ class HinesMulti:
 
 
 def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
-                rng: np.random.Generator | None = None) -> HinesMulti:
-    """One seeded tree per neuron, compartment count uniform in [nmin, nmax].
+                rng: np.random.Generator | None = None, window: int = 8) -> HinesMulti:
+    """One seeded tree per neuron, compartment count uniform in [nmin, nmax]
+    (parents drawn as in ``random_tree`` with this window).
 
     The sizes are drawn first (one block), then neuron by neuron: its tree,
     then its u, l, d, rhs exactly as ``hines_mono`` draws them for batch 1.
@@ -308,7 +309,7 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
     u = np.empty(total); l = np.empty(total); d = np.empty(total); rhs = np.empty(total)
     for s in range(batch):
         o0, o1 = offsets[s], offsets[s + 1]
-        p = random_tree(int(sizes[s]), rng)
+        p = random_tree(int(sizes[s]), rng, window=window)
         us, ls, ds, rs = _hines_values(p, (int(sizes[s]),), rng)
         parent[o0:o1] = p
         u[o0:o1] = us; l[o0:o1] = ls; d[o0:o1] = ds; rhs[o0:o1] = rs
