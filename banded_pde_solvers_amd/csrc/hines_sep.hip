@@ -222,6 +222,9 @@ k_hines_sep(SepArgs A)
     __syncthreads();
     // (b) Algorithm 1 on the separators (one lane per neuron), in place
     if (k == 0) {
+        // one lane per neuron runs a serial chain while the other waves of
+        // the CU run their sweeps: it takes the issue slots first
+        __builtin_amdgcn_s_setprio(3);
         int anyb = 0;
         for (int kk = 0; kk < kSepLanes; ++kk) anyb |= badf[kk * kSepNeurons + j];
         // the next separator's row is read one step ahead; an update for the
@@ -262,6 +265,7 @@ k_hines_sep(SepArgs A)
         }
         flag[j] = anyb;
         if (!anyb && act && A.info) A.info[s] = 0;
+        __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
     // (c) each component's parent voltage and u x of its lower separator
@@ -374,6 +378,7 @@ k_hines_sepm(SepMArgs A)
     int16_t *t16 = reinterpret_cast<int16_t *>(trees + nt * kMTree);   // septab, comptab, clist
     const int16_t *septab = t16, *comptab = t16 + ns * 4, *clist = comptab + nc * 3;
     for (int i = tid; i < nt * kMTree; i += kMThreads) trees[i] = wt[kMHeader + i];
+    for (int i = tid; i < nt; i += kMThreads) tflag[i] = 0;
     {
         const int32_t *src = wt + kMHeader + nt * kMTree;
         int32_t *dst = reinterpret_cast<int32_t *>(t16);
@@ -468,7 +473,7 @@ k_hines_sepm(SepMArgs A)
         }
         if (t + D < R) load(t + D, qq);
     }
-    badf[tid] = bad;
+    if (bad && tslot >= 0) atomicOr(&tflag[tslot], 1);
     __syncthreads();
 
     // ---- the separators' tree systems ----
@@ -498,9 +503,11 @@ k_hines_sepm(SepMArgs A)
     }
     __syncthreads();
     if (tid < nt) {
+        // one lane per tree runs a serial chain while the other waves of the
+        // CU run their sweeps: it takes the issue slots first
+        __builtin_amdgcn_s_setprio(3);
         const int *tr = trees + tid * kMTree;
-        int anyb = 0;
-        for (int k = tr[2]; k < tr[3]; ++k) anyb |= badf[k];
+        int anyb = tflag[tid];
         // the next separator's row is read one step ahead; an update for the
         // next separator is carried in registers, others go through LDS
         const int s0 = tr[0], s1 = tr[1];
@@ -537,6 +544,7 @@ k_hines_sepm(SepMArgs A)
         }
         tflag[tid] = anyb;
         if (!anyb && A.info) A.info[tr[4]] = 0;
+        __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
     for (int c = tid; c < nc; c += kMThreads) {
