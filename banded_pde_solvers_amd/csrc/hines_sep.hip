@@ -508,17 +508,19 @@ k_hines_sepm(SepMArgs A)
         __builtin_amdgcn_s_setprio(3);
         const int *tr = trees + tid * kMTree;
         int anyb = tflag[tid];
-        // the next separator's row is read one step ahead; an update for the
-        // next separator is carried in registers, others go through LDS
+        // the next separator's row is read one step ahead (two register sets
+        // in turn); an update for the next separator is carried in registers,
+        // others go through LDS (they reach two or more rows ahead, which
+        // have not been read yet)
         const int s0 = tr[0], s1 = tr[1];
         double cf = 0.0, cl = 0.0, cr = 0.0;
-        double2 ndr = make_double2(0.0, 0.0), nlu = ndr;
-        int nrp = -1;
-        if (s0 < s1) { ndr = sepv[s0 * 2]; nlu = sepv[s0 * 2 + 1]; nrp = septab[s0 * 4]; }
-        for (int i = s0; i < s1; ++i) {
-            const double2 dr0 = ndr, lu = nlu;
-            const int rp = nrp;
-            if (i + 1 < s1) { ndr = sepv[(i + 1) * 2]; nlu = sepv[(i + 1) * 2 + 1]; nrp = septab[(i + 1) * 4]; }
+        auto rd = [&](int i, double2 &a, double2 &b, int &r) {
+            const int ii = i < s1 ? i : s1 - 1;
+            a = sepv[ii * 2];
+            b = sepv[ii * 2 + 1];
+            r = septab[ii * 4];
+        };
+        auto elim = [&](int i, const double2 dr0, const double2 lu, const int rp) {
             const double2 dr = make_double2(fma(-cf, cl, dr0.x), fma(-cf, cr, dr0.y));
             anyb |= int(bad_pivot(dr.x));
             const double rcp = recip(dr.x);
@@ -533,14 +535,44 @@ k_hines_sepm(SepMArgs A)
                     sepv[rp * 2] = make_double2(fma(-f, lu.x, o.x), fma(-f, dr.y, o.y));
                 }
             }
+        };
+        if (s0 < s1) {
+            double2 a0, b0, a1, b1;
+            int r0, r1;
+            rd(s0, a0, b0, r0);
+            for (int i = s0; i < s1; i += 2) {
+                rd(i + 1, a1, b1, r1);
+                elim(i, a0, b0, r0);
+                if (i + 1 >= s1) break;
+                rd(i + 2, a0, b0, r0);
+                elim(i + 1, a1, b1, r1);
+            }
         }
+        // substitution from the top: the next row read one step ahead, the
+        // parent's voltage from registers when it is the previous row
         double xn = 0.0;
-        for (int i = s1 - 1; i >= s0; --i) {
-            const int rp = septab[i * 4];
-            const double2 qm = sepv[i * 2 + 1];
-            const double xp = rp < 0 ? 0.0 : rp == i + 1 ? xn : sepv[rp * 2].x;
-            xn = qm.x - qm.y * xp;
-            sepv[i * 2].x = xn;
+        if (s0 < s1) {
+            auto rq = [&](int i, double2 &q, int &r) {
+                const int ii = i >= s0 ? i : s0;
+                q = sepv[ii * 2 + 1];
+                r = septab[ii * 4];
+            };
+            auto sub = [&](int i, const double2 qm, const int rp) {
+                double xp = xn;
+                if (rp != i + 1) xp = rp >= 0 ? sepv[rp * 2].x : 0.0;
+                xn = fma(-qm.y, xp, qm.x);
+                sepv[i * 2].x = xn;
+            };
+            double2 q0, q1;
+            int r0, r1;
+            rq(s1 - 1, q0, r0);
+            for (int i = s1 - 1; i >= s0; i -= 2) {
+                rq(i - 1, q1, r1);
+                sub(i, q0, r0);
+                if (i - 1 < s0) break;
+                rq(i - 2, q0, r0);
+                sub(i - 1, q1, r1);
+            }
         }
         tflag[tid] = anyb;
         if (!anyb && A.info) A.info[tr[4]] = 0;
