@@ -227,41 +227,68 @@ k_hines_sep(SepArgs A)
         __builtin_amdgcn_s_setprio(3);
         int anyb = 0;
         for (int kk = 0; kk < kSepLanes; ++kk) anyb |= badf[kk * kSepNeurons + j];
-        // the next separator's row is read one step ahead; an update for the
-        // next separator is carried in registers, others go through LDS
+        // the next separator's row is read one step ahead (two register sets
+        // in turn); an update for the next separator is carried in registers,
+        // others go through LDS (they reach two or more rows ahead, which
+        // have not been read yet)
         double cf = 0.0, cl = 0.0, cr = 0.0;
-        double2 ndr = make_double2(0.0, 0.0), nlu = ndr;
-        if (ns > 0) { ndr = sepv[j * 2]; nlu = sepv[j * 2 + 1]; }
-        for (int i = 0; i < ns; ++i) {
-            const int rp = septab[i * 5 + 1];
-            const double2 dr0 = ndr, lu = nlu;
-            if (i + 1 < ns) {
-                ndr = sepv[((i + 1) * kSepNeurons + j) * 2];
-                nlu = sepv[((i + 1) * kSepNeurons + j) * 2 + 1];
-            }
+        auto at = [&](int i) { return (i * kSepNeurons + j) * 2; };
+        auto rd = [&](int i, double2 &a, double2 &b, int &r) {
+            const int ii = i < ns ? i : ns - 1;
+            a = sepv[at(ii)];
+            b = sepv[at(ii) + 1];
+            r = septab[ii * 5 + 1];
+        };
+        auto elim = [&](int i, const double2 dr0, const double2 lu, const int rp) {
             const double2 dr = make_double2(fma(-cf, cl, dr0.x), fma(-cf, cr, dr0.y));
             anyb |= int(bad_pivot(dr.x));
             const double rcp = recip(dr.x);
-            sepv[(i * kSepNeurons + j) * 2 + 1] = make_double2(dr.y * rcp, lu.x * rcp);
+            sepv[at(i) + 1] = make_double2(dr.y * rcp, lu.x * rcp);
             cf = 0.0;
             if (rp >= 0) {
                 const double f = lu.y * rcp;
                 if (rp == i + 1) {
                     cf = f; cl = lu.x; cr = dr.y;
                 } else {
-                    double2 &t = sepv[(rp * kSepNeurons + j) * 2];
-                    const double2 o = t;
-                    t = make_double2(fma(-f, lu.x, o.x), fma(-f, dr.y, o.y));
+                    const double2 o = sepv[at(rp)];
+                    sepv[at(rp)] = make_double2(fma(-f, lu.x, o.x), fma(-f, dr.y, o.y));
                 }
             }
-        }
+        };
         double xn = 0.0;
-        for (int i = ns - 1; i >= 0; --i) {
-            const int rp = septab[i * 5 + 1];
-            const double2 qm = sepv[(i * kSepNeurons + j) * 2 + 1];
-            const double xp = rp < 0 ? 0.0 : rp == i + 1 ? xn : sepv[(rp * kSepNeurons + j) * 2].x;
-            xn = qm.x - qm.y * xp;
-            sepv[(i * kSepNeurons + j) * 2].x = xn;
+        if (ns > 0) {
+            double2 a0, b0, a1, b1;
+            int r0, r1;
+            rd(0, a0, b0, r0);
+            for (int i = 0; i < ns; i += 2) {
+                rd(i + 1, a1, b1, r1);
+                elim(i, a0, b0, r0);
+                if (i + 1 >= ns) break;
+                rd(i + 2, a0, b0, r0);
+                elim(i + 1, a1, b1, r1);
+            }
+            // substitution from the top: the next row read one step ahead, the
+            // parent's voltage from registers when it is the previous row
+            auto rq = [&](int i, double2 &q, int &r) {
+                const int ii = i >= 0 ? i : 0;
+                q = sepv[at(ii) + 1];
+                r = septab[ii * 5 + 1];
+            };
+            auto sub = [&](int i, const double2 qm, const int rp) {
+                double xp = xn;
+                if (rp != i + 1) xp = rp >= 0 ? sepv[at(rp)].x : 0.0;
+                xn = fma(-qm.y, xp, qm.x);
+                sepv[at(i)].x = xn;
+            };
+            double2 q0, q1;
+            rq(ns - 1, q0, r0);
+            for (int i = ns - 1; i >= 0; i -= 2) {
+                rq(i - 1, q1, r1);
+                sub(i, q0, r0);
+                if (i - 1 < 0) break;
+                rq(i - 2, q0, r0);
+                sub(i - 1, q1, r1);
+            }
         }
         flag[j] = anyb;
         if (!anyb && act && A.info) A.info[s] = 0;
