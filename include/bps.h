@@ -375,42 +375,50 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     its branches finish); a tree whose two-lane schedule
  *                     does not shorten it stays on one lane.  Mono plans:
  *                     as LANES;
- *   BPS_HINES_SEP     mono plans of trees of at most 2047 compartments whose
- *                     parents all lie within 8 compartments: sixteen lanes
- *                     per neuron.  Single compartments (separators) cut the
- *                     tree into components with at most one separator below
- *                     each; every lane eliminates whole components (Algorithm
- *                     1 inside each, holding its rows' factors in registers),
- *                     the components' Schur complements on the separators
- *                     form a smaller tree system solved by Algorithm 1, then
- *                     the lanes substitute their rows: the per-branch
+ *   BPS_HINES_SEP     trees whose parents all lie within 8 compartments:
+ *                     single compartments (separators) cut each tree into
+ *                     components with at most one separator below each;
+ *                     lanes eliminate whole components (Algorithm 1 inside
+ *                     each, holding their rows' factors in registers), the
+ *                     components' Schur complements on the separators form a
+ *                     smaller tree system solved by Algorithm 1, then the
+ *                     lanes substitute their rows: the per-branch
  *                     decomposition of section 4 with the pages' solve of
  *                     the reduced system, each compartment's values read and
- *                     written once.  The elimination order differs from
- *                     Algorithm 1's on the separators and on the paths from
- *                     them up to their components' roots, so results differ
- *                     by rounding; a neuron any of whose pivots in this order
- *                     is zero or not finite is solved again by Algorithm 1
- *                     in the same call (its info is Algorithm 1's).
- *                     BPS_ENOTSUP for other plans or when no partition fits
- *                     sixteen lanes of 32 rows;
+ *                     written once.  Mono plans (trees of at most 2047
+ *                     compartments): sixteen lanes per neuron in the
+ *                     Full-Interleaved layout.  Multi-morphology plans (trees
+ *                     of at most 8191 compartments): every tree on as many
+ *                     lanes as it needs, trees packed into workgroups of 128
+ *                     lanes, the plan's layout in schedule order (element
+ *                     (w, t, k) = workgroup w, step t, lane k; the
+ *                     separators' own rows among the lanes' rows; see
+ *                     hines_sep_multi_layout).  The elimination order differs
+ *                     from Algorithm 1's on the separators and on the paths
+ *                     from them up to their components' roots, so results
+ *                     differ by rounding; a neuron any of whose pivots in
+ *                     this order is zero or not finite is solved again by
+ *                     Algorithm 1 in the same call (its info is Algorithm
+ *                     1's).  BPS_ENOTSUP for other trees or when no
+ *                     partition fits the lanes (32 rows each);
  *   BPS_HINES_LEVELS  one wavefront per neuron: the tree cut into its
  *                     unbranched sections, grouped by level (the page's
  *                     per-branch / per-level decomposition of section 4),
  *                     one section per lane and level, with the neuron held
  *                     in LDS; for batches too small to fill the GPU with one
  *                     lane per neuron.  Trees of at most 4096 compartments;
- *   BPS_HINES_AUTO    mono plans: SEP for trees it takes, when the tree
- *                     has at least 256 compartments or the batch at most
- *                     2^21 compartments in all.  Otherwise, and for
- *                     multi-morphology plans: LEVELS for batches whose trees
- *                     fit and that hold at most 786432 compartments in all
- *                     (mono) or 393216 (multi-morphology), else LANES; when
- *                     one lane per neuron would leave SIMDs of the GPU
- *                     without a wavefront (fewer than 1024 blocks of 64
- *                     neurons), the largest trees go on two lanes as in
- *                     SPLIT until the blocks nearly fill them (what
- *                     hines_plan_create chooses).
+ *   BPS_HINES_AUTO    SEP for trees it takes: mono plans whose tree has at
+ *                     least 256 compartments or whose batch has at most
+ *                     2^21 compartments in all; multi-morphology plans whose
+ *                     trees average at least 128 compartments.  Otherwise:
+ *                     LEVELS for batches whose trees fit and that hold at
+ *                     most 786432 compartments in all (mono) or 393216
+ *                     (multi-morphology), else LANES; when one lane per
+ *                     neuron would leave SIMDs of the GPU without a
+ *                     wavefront (fewer than 1024 blocks of 64 neurons), the
+ *                     largest trees go on two lanes as in SPLIT until the
+ *                     blocks nearly fill them (what hines_plan_create
+ *                     chooses).
  * Every schedule takes the same arguments; the solver layout is the plan's
  * (elements per array: hines_plan_elems; convert with hines_pack and
  * hines_unpack): a tree on two lanes has its compartments in the order its
