@@ -52,6 +52,17 @@ class _Problems:
         self.s0 = dev(hs.rhs)
         self.s = self.s0.clone()
         self.ws = buf(bps.hines_work_bytes(self.splan))
+        mm = W.hines_multi(40, 200, 900, rng=rng)                      # multi-morphology, separators
+        self.mplan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
+        assert self.mplan.uses_sep
+        mp = []
+        for v in (mm.u, mm.l, mm.d, mm.rhs):
+            t = torch.empty(self.mplan.elems, dtype=torch.float64, device="cuda:0")
+            bps.hines_pack(self.mplan, dev(v), t)
+            mp.append(t)
+        self.mu, self.ml, self.md, self.m0 = mp
+        self.m = self.m0.clone()
+        self.wm = buf(bps.hines_work_bytes(self.mplan))
         pb = W.penta_dominant(256, 70, cyclic=True, rng=rng)           # periodic fused penta
         self.pd = [dev(v) for v in pb.diagonals]
         self.x0 = dev(pb.f)
@@ -60,7 +71,7 @@ class _Problems:
 
     def reset(self):
         for dst, src in ((self.C, self.C0), (self.Q, self.Q0), (self.y, self.y0),
-                         (self.r, self.r0), (self.x, self.x0), (self.s, self.s0)):
+                         (self.r, self.r0), (self.x, self.x0), (self.s, self.s0), (self.m, self.m0)):
             dst.copy_(src)
 
     def run(self):
@@ -70,9 +81,10 @@ class _Problems:
         bps.hines_solve_batch(self.plan, self.hu, self.hl, self.hd, self.r, self.wr)
         bps.penta_factor_solve_batch(*self.pd, self.x, self.wp, cyclic=True)
         bps.hines_solve_batch(self.splan, self.su, self.sl, self.sd, self.s, self.ws)
+        bps.hines_solve_batch(self.mplan, self.mu, self.ml, self.md, self.m, self.wm)
 
     def outputs(self):
-        return [host(t) for t in (self.C, self.Q, self.y, self.r, self.x, self.s)]
+        return [host(t) for t in (self.C, self.Q, self.y, self.r, self.x, self.s, self.m)]
 
 
 def test_graph_capture_replay_bitwise():
