@@ -368,6 +368,7 @@ constexpr uint32_t kMOwn = 7u, kMLive = 1u << 6, kMPath = 1u << 7, kMPath0 = 1u 
 constexpr int kMHeader = 8;     // words of a workgroup's table header
 constexpr int kMThreads = 128;  // lanes per workgroup (four workgroups per CU)
 constexpr int kMTree = 5;       // words per tree: separator range, lane range, tree number
+constexpr int kMJump = 4;       // separators per lane in the substitution (at most 512 per workgroup)
 
 struct SepMArgs {
     uint32_t bytes;             // elems * 8
@@ -537,30 +538,32 @@ k_hines_sepm(SepMArgs A)
         int anyb = tflag[tid];
         // the next separator's row is read one step ahead (two register sets
         // in turn); an update for the next separator is carried in registers,
-        // others go through LDS (they reach two or more rows ahead, which
-        // have not been read yet)
+        // others are added in LDS by atomics that return nothing (they reach
+        // two or more rows ahead, which have not been read yet, and one lane's
+        // LDS operations complete in order), so no step waits on them
         const int s0 = tr[0], s1 = tr[1];
         double cf = 0.0, cl = 0.0, cr = 0.0;
         auto rd = [&](int i, double2 &a, double2 &b, int &r) {
             const int ii = i < s1 ? i : s1 - 1;
+            r = septab[ii * 4];         // first: the oldest of the three reads
             a = sepv[ii * 2];
             b = sepv[ii * 2 + 1];
-            r = septab[ii * 4];
         };
         auto elim = [&](int i, const double2 dr0, const double2 lu, const int rp) {
             const double2 dr = make_double2(fma(-cf, cl, dr0.x), fma(-cf, cr, dr0.y));
             anyb |= int(bad_pivot(dr.x));
             const double rcp = recip(dr.x);
-            sepv[i * 2 + 1] = make_double2(dr.y * rcp, lu.x * rcp);
-            cf = 0.0;
-            if (rp >= 0) {
-                const double f = lu.y * rcp;
-                if (rp == i + 1) {
-                    cf = f; cl = lu.x; cr = dr.y;
-                } else {
-                    const double2 o = sepv[rp * 2];
-                    sepv[rp * 2] = make_double2(fma(-f, lu.x, o.x), fma(-f, dr.y, o.y));
-                }
+            // x_i = q_i + (-m_i) x_rp: the substitution's affine map
+            sepv[i * 2 + 1] = make_double2(dr.y * rcp, -(lu.x * rcp));
+            const double f = lu.y * rcp;
+            const bool next = rp == i + 1;
+            cf = next ? f : 0.0;
+            cl = next ? lu.x : 0.0;
+            cr = next ? dr.y : 0.0;
+            if (rp > i + 1) {
+                double *o = reinterpret_cast<double *>(sepv + rp * 2);
+                __hip_atomic_fetch_add(o, -(f * lu.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(o + 1, -(f * dr.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         };
         if (s0 < s1) {
@@ -575,35 +578,59 @@ k_hines_sepm(SepMArgs A)
                 elim(i + 1, a1, b1, r1);
             }
         }
-        // substitution from the top: the next row read one step ahead, the
-        // parent's voltage from registers when it is the previous row
-        double xn = 0.0;
-        if (s0 < s1) {
-            auto rq = [&](int i, double2 &q, int &r) {
-                const int ii = i >= s0 ? i : s0;
-                q = sepv[ii * 2 + 1];
-                r = septab[ii * 4];
-            };
-            auto sub = [&](int i, const double2 qm, const int rp) {
-                double xp = xn;
-                if (rp != i + 1) xp = rp >= 0 ? sepv[rp * 2].x : 0.0;
-                xn = fma(-qm.y, xp, qm.x);
-                sepv[i * 2].x = xn;
-            };
-            double2 q0, q1;
-            int r0, r1;
-            rq(s1 - 1, q0, r0);
-            for (int i = s1 - 1; i >= s0; i -= 2) {
-                rq(i - 1, q1, r1);
-                sub(i, q0, r0);
-                if (i - 1 < s0) break;
-                rq(i - 2, q0, r0);
-                sub(i - 1, q1, r1);
-            }
-        }
         tflag[tid] = anyb;
         if (!anyb && A.info) A.info[tr[4]] = 0;
         __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();
+    // substitution over the separators' forest by pointer jumping, every lane
+    // holding up to kMJump separators in registers: x_i = a_i + b_i x_p(i)
+    // becomes x_i = (a_i + b_i a_p) + (b_i b_p) x_p(p) each round, until no
+    // pointer is left (the table header holds the rounds, from the deepest
+    // separator of the workgroup). A round reads the parents' entries from
+    // one buffer and publishes its own to the other: (a, b) in the
+    // separator's second and first value pairs, p in columns 0 and 2 of its
+    // table row (column 2 is read no more by then)
+    {
+        int16_t *sp = t16;
+        const int rounds = wt[6];
+        double ja[kMJump], jb[kMJump];
+        int jp[kMJump];
+#pragma unroll
+        for (int j = 0; j < kMJump; ++j) {
+            const int i = tid + j * kMThreads;
+            if (i < ns) {
+                const double2 v = sepv[i * 2 + 1];
+                ja[j] = v.x;
+                jb[j] = v.y;
+                jp[j] = septab[i * 4];
+            }
+        }
+        for (int k = 0; k < rounds; ++k) {
+            const int ci = (k & 1) ? 0 : 1, ni = (k & 1) ? 1 : 0;
+            const int cp = (k & 1) ? 2 : 0, np = (k & 1) ? 0 : 2;
+#pragma unroll
+            for (int j = 0; j < kMJump; ++j) {
+                const int i = tid + j * kMThreads;
+                if (i < ns) {
+                    const int p = jp[j];
+                    if (p >= 0) {
+                        const double2 vp = sepv[p * 2 + ci];
+                        jp[j] = sp[p * 4 + cp];
+                        ja[j] = fma(jb[j], vp.x, ja[j]);
+                        jb[j] *= vp.y;
+                    }
+                    sepv[i * 2 + ni] = make_double2(ja[j], jb[j]);
+                    sp[i * 4 + np] = int16_t(jp[j]);
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < kMJump; ++j) {
+            const int i = tid + j * kMThreads;
+            if (i < ns) sepv[i * 2].x = ja[j];
+        }
     }
     __syncthreads();
     for (int c = tid; c < nc; c += kMThreads) {
@@ -950,7 +977,10 @@ static size_t sepm_tree_lds(const SepTree &T)
     return size_t(T.nc) * 16 + size_t(T.npc) * 32 + size_t(T.ns) * 40 + size_t(T.nh) * 8 +
            size_t(T.ns + T.nc) * 8 + 4 + 4 * kMTree;
 }
-static size_t sepm_fixed_lds() { return size_t(kSepSlots) * kMThreads * 16 + 16 + kMThreads * 4 + 8; }
+// the kernel's carve-up: the ring, 16 bytes of alignment, the lanes' flags, 8
+// bytes of alignment, two spare path entries (16 bytes) and the 16-bit tables'
+// rounding (4 bytes); a workgroup needs this plus sepm_tree_lds of its trees
+static size_t sepm_fixed_lds() { return size_t(kSepSlots) * kMThreads * 16 + 16 + kMThreads * 4 + 8 + 16 + 4; }
 
 bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent, const int64_t *off,
                      SepMulti &M, std::string &why)
@@ -1036,6 +1066,18 @@ bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent,
         const int32_t n16 = ns * 4 + nc * 4;
         std::vector<int32_t> tab(size_t(kMHeader + nt * kMTree + (n16 + 1) / 2), 0);
         tab[0] = nt; tab[1] = ns; tab[2] = nc; tab[3] = npc; tab[4] = nh; tab[5] = n16;
+        int32_t depth = 0;                       // most ancestors of a separator
+        for (int64_t s : B.trees) {
+            const SepTree &T = tr[size_t(s)];
+            std::vector<int32_t> dp(size_t(T.ns), 0);
+            for (int32_t i = T.ns - 1; i >= 0; --i) {
+                dp[size_t(i)] = T.rp[size_t(i)] >= 0 ? dp[size_t(T.rp[size_t(i)])] + 1 : 0;
+                depth = std::max(depth, dp[size_t(i)]);
+            }
+        }
+        int32_t rounds = 0;                      // 2^rounds > depth
+        while ((int64_t(1) << rounds) <= depth) ++rounds;
+        tab[6] = rounds;
         int16_t *t16 = reinterpret_cast<int16_t *>(tab.data() + kMHeader + nt * kMTree);
         int16_t *septab = t16, *comptab = t16 + ns * 4, *clist = comptab + nc * 3;
         int32_t sb = 0, cb = 0, pb = 0, hb = 0, lane0 = 0, ncl = 0;
@@ -1084,7 +1126,11 @@ bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent,
         M.wgoff[size_t(wgi) + 1] = M.wgoff[size_t(wgi)] + int64_t(tab.size());
         M.tabs.insert(M.tabs.end(), tab.begin(), tab.end());
         const size_t lds = sepm_fixed_lds() + size_t(nc) * 16 + size_t(npc) * 32 + size_t(ns) * 40 +
-                           size_t(nh + 2) * 8 + size_t(nt) * (4 + 4 * kMTree) + size_t(n16 + 2) * 2;
+                           size_t(nh) * 8 + size_t(nt) * (4 + 4 * kMTree) + size_t(n16) * 2;
+        if (lds != sepm_fixed_lds() + B.lds || lds > kSepMLds || ns > kMJump * kMThreads) {
+            why = "internal: a workgroup's LDS outside its budget";
+            return false;
+        }
         M.lds = std::max(M.lds, lds);
     }
     return true;

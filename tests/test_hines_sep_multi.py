@@ -168,12 +168,22 @@ def _replay(Lo, sizes, u, l, d, rhs):
                         f = uh / dh
                         sepv[rp, 0] -= f * lh
                         sepv[rp, 1] -= f * rh
-                for i in range(s1 - 1, s0 - 1, -1):
-                    rp = int(septab[i, 0])
-                    sepv[i, 0] = sepv[i, 2] - sepv[i, 3] * (sepv[rp, 0] if rp >= 0 else 0.0)
                 tflag[tt] = anyb
                 if anyb:
                     bad_trees.add(T)
+            # substitution by pointer jumping over the workgroup's separators:
+            # x_i = a_i + b_i x_p(i), the header's number of rounds
+            rounds = int(Lo["tabs"][Lo["wgoff"][w] + 6])
+            a, b, ptr = sepv[:, 2].copy(), -sepv[:, 3], septab[:, 0].copy()
+            for k in range(rounds):
+                assert k == 0 or np.any(ptr >= 0)           # no round more than needed
+                has = ptr >= 0
+                pp = np.where(has, ptr, 0)
+                a = np.where(has, b * a[pp] + a, a)
+                b = np.where(has, b * b[pp], b)
+                ptr = np.where(has, ptr[pp], ptr)
+            assert np.all(ptr < 0)                          # enough rounds
+            sepv[:, 0] = a
             for c in range(nc):
                 pc, sc = int(comptab[c, 0]), int(comptab[c, 1])
                 red[c] = (sepv[pc, 0] if pc >= 0 else 0.0, su[sc] * sepv[sc, 0] if sc >= 0 else 0.0)
@@ -222,6 +232,20 @@ def test_sep_multi_replay_matches_oracle(batch, nmin, nmax, seed):
     err = max(np.linalg.norm(V[o[s]:o[s + 1]] - ref[o[s]:o[s + 1]]) / np.linalg.norm(ref[o[s]:o[s + 1]])
               for s in range(batch))
     assert err <= 1e-13
+
+
+@pytest.mark.parametrize("batch,nmin,nmax,window", [(2000, 100, 300, 2), (2000, 30, 2047, 1),
+                                                     (3000, 20, 200, 8)])
+def test_sep_multi_layout_lds_budget(batch, nmin, nmax, window):
+    """Batches whose workgroups fill the LDS budget (many path rows): every
+    workgroup within 40 KB, so that four fit in a CU's 160 KB, and every table
+    index in range."""
+    _lib_or_skip()
+    mm = W.hines_multi(batch, nmin, nmax, rng=np.random.default_rng(5), window=window)
+    Lo = bps.hines_sep_multi_layout(mm.sizes, mm.parent)
+    assert Lo is not None
+    assert 4 * Lo["lds"] <= 160 * 1024
+    _check_ranges(Lo, mm.sizes)
 
 
 def test_sep_multi_layout_refusals():
