@@ -193,6 +193,22 @@ def test_sep_multi_matches_oracle(batch, nmin, nmax):
     np.testing.assert_array_equal(info, rinfo)
 
 
+def test_sep_multi_many_separators():
+    """Trees of doubling chains put more separators than lanes in a workgroup
+    (each substitution lane then holds a second one), mixed with random trees."""
+    print("hines sep multi: doubling-chain trees", flush=True)
+    rng = np.random.default_rng(23)
+    trees = [W.doubling_tree(34)] * 40 + [W.doubling_tree(30)] * 9 + \
+            [W.random_tree(int(n), rng) for n in rng.integers(200, 900, size=25)]
+    mm = W.hines_multi_trees(trees, rng)
+    Lo = bps.hines_sep_multi_layout(mm.sizes, mm.parent)
+    assert max(int(Lo["tabs"][Lo["wgoff"][w] + 1]) for w in range(Lo["nwg"])) > Lo["K"]
+    out, info = _run_multi(mm, twice=True)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    assert _multi_err(mm, out, ref) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+
+
 def test_sep_multi_breakdown_info():
     rng = np.random.default_rng(12)
     mm = W.hines_multi(40, 200, 400, rng=rng)

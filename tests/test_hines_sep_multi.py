@@ -234,6 +234,25 @@ def test_sep_multi_replay_matches_oracle(batch, nmin, nmax, seed):
     assert err <= 1e-13
 
 
+def test_sep_multi_replay_many_separators():
+    """Trees of doubling chains give workgroups of more separators than lanes
+    (the substitution's lanes then hold a second separator each)."""
+    _lib_or_skip()
+    mm = W.hines_multi_trees([W.doubling_tree(34)] * 8 + [W.doubling_tree(30)] * 2,
+                             np.random.default_rng(17))
+    Lo = bps.hines_sep_multi_layout(mm.sizes, mm.parent)
+    assert Lo is not None
+    assert max(int(Lo["tabs"][Lo["wgoff"][w] + 1]) for w in range(Lo["nwg"])) > Lo["K"]
+    _check_ranges(Lo, mm.sizes)
+    V, bad = _replay(Lo, mm.sizes, mm.u, mm.l, mm.d, mm.rhs)
+    assert not bad
+    ref, info = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    o = mm.offsets
+    err = max(np.linalg.norm(V[o[s]:o[s + 1]] - ref[o[s]:o[s + 1]]) / np.linalg.norm(ref[o[s]:o[s + 1]])
+              for s in range(mm.batch))
+    assert err <= 1e-13
+
+
 @pytest.mark.parametrize("batch,nmin,nmax,window", [(2000, 100, 300, 2), (2000, 30, 2047, 1),
                                                      (3000, 20, 200, 8)])
 def test_sep_multi_layout_lds_budget(batch, nmin, nmax, window):

@@ -316,6 +316,35 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
     return HinesMulti(sizes, offsets, parent, u, l, d, rhs)
 
 
+def hines_multi_trees(trees, rng: np.random.Generator) -> HinesMulti:
+    """A multi-morphology batch of the given trees (parent arrays), values
+    drawn tree by tree as ``hines_multi`` draws them."""
+    sizes = np.array([len(p) for p in trees], dtype=np.int32)
+    offsets = np.zeros(len(trees) + 1, dtype=np.int64)
+    np.cumsum(sizes, out=offsets[1:])
+    parent = np.concatenate([np.asarray(p, dtype=np.int32) for p in trees])
+    vals = [_hines_values(np.asarray(p, dtype=np.int32), (len(p),), rng) for p in trees]
+    u, l, d, rhs = (np.concatenate([v[k] for v in vals]) for k in range(4))
+    return HinesMulti(sizes, offsets, parent, u, l, d, rhs)
+
+
+def doubling_tree(T: int) -> np.ndarray:
+    """A tree of chains that double level by level: one chain of T
+    compartments, then 2, 4 and 8 interleaved chains of T each (chain j of a
+    level starts below the last compartment of chain j mod c of the level
+    before, c its chain count), so every parent lies within 8 and every
+    branch point has two long subtrees below it."""
+    par = [-1] + list(range(T - 1))
+    last = [T - 1]
+    for c in (2, 4, 8):
+        base = len(par)
+        for t in range(T):
+            for j in range(c):
+                par.append(last[j % (c // 2)] if t == 0 else base + (t - 1) * c + j)
+        last = [base + (T - 1) * c + j for j in range(c)]
+    return np.array(par, dtype=np.int32)
+
+
 # ----------------------------------------------------------------------------
 # The named workloads at their full sizes (5: the headline shape time-stepped
 # with Crank-Nicolson instead of backward Euler; 6: the same grid and batch
