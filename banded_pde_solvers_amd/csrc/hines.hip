@@ -82,7 +82,6 @@ struct bps_hines_plan {
 namespace bps {
 
 constexpr int kRing = 16;       // LDS ring slots per lane (power of two)
-constexpr int kSepSlotsHost = 8;    // parent window of the sixteen-lane schedules
 constexpr int kLevelMaxN = 4096;        // tree size limit of the level schedule (LDS)
 // auto: the level schedule up to this many compartments in the batch.
 // Measured (one solve): trees of 512, 16 .. 1024 neurons: 77 .. 107 us with
@@ -1354,18 +1353,11 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];
         P->unknowns = off[batch];
         // separator schedules: when asked for, and by default for batches
-        // whose trees all have their parents within 8 compartments and
-        // average at least 128 compartments (measured: trees of 256..2048,
-        // 64 of them 44 us vs 270 with levels, 32768 451 vs 613 on two
-        // lanes; 512 x 32768 205 vs 230 on one lane; trees of 1..100 and
+        // whose trees average at least 128 compartments (measured: trees of
+        // 256..2048, 64 of them 44 us vs 270 with levels, 32768 451 vs 613 on
+        // two lanes; 512 x 32768 205 vs 230 on one lane; trees of 1..100 and
         // 30..60 within 30% either way, in favour of the others)
-        bool sep_auto = false;
-        if (sched == BPS_HINES_AUTO && off[batch] >= 128 * batch) {
-            sep_auto = true;
-            for (int64_t s = 0; s < batch && sep_auto; ++s)
-                for (int32_t i = 1; i < sizes[s] && sep_auto; ++i)
-                    sep_auto = i - parent[off[s] + i] <= kSepSlotsHost;
-        }
+        const bool sep_auto = sched == BPS_HINES_AUTO && off[batch] >= 128 * batch;
         SepMulti M;
         std::string why;
         const bool sep_ok = (sched == BPS_HINES_SEP || sep_auto) &&
@@ -1378,7 +1370,6 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
             P->use_levels = false;
             P->use_sepm = true;
             P->elems = M.elems;
-            P->max_dist = kSepSlotsHost;
             std::vector<int32_t> fp(parent, parent + off[batch]);
             int32_t *lt = nullptr, *tb = nullptr, *ps = nullptr;
             int64_t *wo = nullptr;
@@ -1485,7 +1476,10 @@ hipError_t hines_prepare_device()
     return e != hipSuccess ? e : sep_prepare_device();
 }
 
-bool hines_plan_general(const bps_hines_plan *p) { return p->max_dist > kRing; }
+bool hines_plan_general(const bps_hines_plan *p)
+{
+    return !p->sep_dev && !p->use_sepm && p->max_dist > kRing;
+}
 bool hines_plan_levels(const bps_hines_plan *p) { return p->use_levels; }
 bool hines_plan_sep(const bps_hines_plan *p) { return p->sep_dev != nullptr || p->use_sepm; }
 int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }

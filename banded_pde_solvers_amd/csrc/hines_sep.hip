@@ -862,10 +862,35 @@ static bool sep_tree(int32_t n, const int32_t *p, int L, int R, bool sep_rows, S
                         if (v == croot[c]) f |= kSepTop;
                         if (onpath[v]) { f |= kSepPath; ++nh; }
                         if (first[v]) f |= kSepPath0;
-                        T.lanes[l].push_back({v, f, v & 7, v == croot[c] ? 0 : (p[v] & 7)});
+                        T.lanes[l].push_back({v, f, 0, 0});
                     }
             }
         }
+        // ring slots, lane by lane in stream order: a compartment's slot holds
+        // its children's pending updates (first sweep) and then its voltage for
+        // them (second sweep), from its first child's row to its own; the
+        // parent's slot opens at its first child's row in the slot that row
+        // frees, a leaf takes any free slot for its own row
+        bool fits = true;
+        std::vector<int8_t> slot(size_t(n), -1);
+        for (int l = 0; l < L && fits; ++l) {
+            uint32_t busy = 0;
+            for (SepRow &r : T.lanes[l]) {
+                if (!(r.flags & kSepLive)) continue;
+                int sv = slot[size_t(r.node)];
+                if (sv < 0) {
+                    if (busy == (1u << kSepSlots) - 1) { fits = false; break; }
+                    sv = __builtin_ctz(~busy);
+                }
+                r.own = sv;
+                busy &= ~(1u << sv);
+                if (r.flags & kSepTop) continue;
+                int8_t &sp = slot[size_t(p[r.node])];
+                if (sp < 0) { sp = int8_t(sv); busy |= 1u << sv; }
+                r.par = sp;
+            }
+        }
+        if (!fits) continue;      // more than 8 pending at once: smaller components
         T.nh = nh;
         T.npc = npid;
         T.snode = snode;
@@ -914,13 +939,11 @@ static bool sep_tree(int32_t n, const int32_t *p, int L, int R, bool sep_rows, S
 }
 
 // The schedule of one tree (host): empty, with the reason, when the tree
-// does not qualify (a parent more than 8 compartments away, more than 2047
-// compartments, or no partition whose lanes fit R rows).
+// does not qualify (more than 2047 compartments, or no partition whose lanes
+// fit R rows with at most 8 compartments pending at once in a lane).
 std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
 {
     if (n < 1 || n > 2047) { why = "tree size outside [1, 2047]"; return {}; }
-    for (int32_t i = 1; i < n; ++i)
-        if (i - p[i] > kSepSlots) { why = "a parent more than 8 compartments away"; return {}; }
     for (int R : {16, 32}) {
         SepTree T;
         if (!sep_tree(n, p, kSepLanes, R, false, T)) continue;
@@ -996,9 +1019,6 @@ bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent,
                 const int32_t n = sizes[s];
                 const int32_t *p = parent + off[s];
                 if (n > 8191) { fail[s] = 1; continue; }
-                bool ok = true;
-                for (int32_t i = 1; i < n && ok; ++i) ok = i - p[i] <= kSepSlots;
-                if (!ok) { fail[s] = 2; continue; }
                 int L = std::max(1, (n + 29) / 30);
                 while (L <= kMThreads && !sep_tree(n, p, L, R, true, tr[s])) ++L;
                 if (L > kMThreads || sepm_tree_lds(tr[s]) + sepm_fixed_lds() > kSepMLds) fail[s] = 3;
@@ -1007,7 +1027,7 @@ bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent,
     for (auto &t : th) t.join();
     for (int64_t s = 0; s < batch; ++s)
         if (fail[s]) {
-            why = fail[s] == 2 ? "a parent more than 8 compartments away" : "a tree too large for 128 lanes of 32 rows";
+            why = "a tree too large for 128 lanes of 32 rows";
             return false;
         }
     // best fit, largest first: each tree into the workgroup with the fewest

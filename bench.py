@@ -30,7 +30,7 @@ oracle, built with gcc -O3 -march=native -fopenmp on this host, timed on a
 bounded sample of the same workload with all of this host's cores and with
 one thread, median of 5 runs each, CPU model and core counts stated).
 
-    python bench.py [--steps K] [--warmup W] [--workload {0,...,10}]
+    python bench.py [--steps K] [--warmup W] [--workload {0,...,12}]
 
 --workload selects another workload for manual measurements
 (0: the small periodic case, N = 256, 64 systems, 10 steps from seeded Fourier
@@ -42,7 +42,9 @@ and batch for the Cahn-Hilliard equation, semi-implicit, 25 flops; 7, 8:
 batched tridiagonal solves, 512 x 256000 and 8192 x 20000, --dtype f64|f32;
 9: periodic pentadiagonal 512 x 65536 with per-system coefficients, fused
 factor+solve, --dtype f64|f32; 10: Hines mono 512 x 256, a batch too small
-for one lane per neuron, solved with the per-level section schedule).
+for one lane per neuron, solved with the per-level section schedule; 11, 12:
+workloads 3 and 4 with their trees numbered depth first, parents arbitrarily
+far back).
 HBM-bound workloads also report the measured bandwidth of a plain 1 GiB
 device copy (copy_gbs) and the kernel's fraction of it (frac_of_copy): a
 stream that writes cannot exceed it.  Only one GPU is used; --gpus above 1
@@ -588,7 +590,8 @@ def _hines_common(args, multi, which=None):
     sched = {"auto": bps.BPS_HINES_AUTO, "lanes": bps.BPS_HINES_LANES, "split": bps.BPS_HINES_SPLIT,
              "levels": bps.BPS_HINES_LEVELS, "sep": bps.BPS_HINES_SEP}[args.hines_schedule]
     if multi:
-        mm = W.hines_multi(cfg["batch"], cfg["nmin"], cfg["nmax"])
+        mm = W.hines_multi(cfg["batch"], cfg["nmin"], cfg["nmax"],
+                           rng=W.rng_for(which) if which is not None else None, dfs=cfg.get("dfs", False))
         plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=sched)
         arrs = []
         for v in (mm.u, mm.l, mm.d, mm.rhs):
@@ -599,7 +602,8 @@ def _hines_common(args, multi, which=None):
         stats = {"mean_n": float(mm.sizes.mean()), "padded_elems": plan.elems,
                  "trees_on_two_lanes": plan.split}
     else:
-        hm = W.hines_mono(cfg["n"], cfg["batch"], rng=W.rng_for(which if which is not None else 3))
+        hm = W.hines_mono(cfg["n"], cfg["batch"], rng=W.rng_for(which if which is not None else 3),
+                          dfs=cfg.get("dfs", False))
         plan = bps.hines_plan_create(cfg["batch"], [cfg["n"]], hm.parent, mono=True, schedule=sched)
         arrs = [torch.as_tensor(v, device="cuda:0") for v in (hm.u, hm.l, hm.d, hm.rhs)]
         nsolve = 1
@@ -619,13 +623,21 @@ def _hines_common(args, multi, which=None):
     kern_ms = _stats(per_solve)["median"]
     alg_bytes = per_unknown * plan.unknowns
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    if multi:
+        loc = np.arange(len(mm.parent)) - np.repeat(mm.offsets[:-1], mm.sizes)
+        maxd = int(np.max(np.where(loc > 0, loc - mm.parent, 0)))
+    else:
+        maxd = int(stats["max_parent_distance"])
+    general = not plan.uses_levels and not plan.uses_sep and maxd > 16      # beyond the 16-slot ring
     kname = ("k_hines_levels" if plan.uses_levels else
+             "k_hines<general>" if general else
              ("k_hines_sepm" if plan.uses_sep else "k_hines_split" if plan.split else "k_hines_multi")
              if multi else "k_hines_sep" if plan.uses_sep else "k_hines_mono_reg")
-    traffic = _traffic("hines_levels" if plan.uses_levels else
-                       ("hines_sepm" if plan.uses_sep else "hines_split" if plan.split else "hines_multi")
-                       if multi else
-                       f"hines_sep_n{cfg['n']}_b{cfg['batch']}" if plan.uses_sep else "hines_mono")
+    tkey = ("hines_levels" if plan.uses_levels else "hines_general" if general else
+            ("hines_sepm" if plan.uses_sep else "hines_split" if plan.split else "hines_multi")
+            if multi else
+            f"hines_sep_n{cfg['n']}_b{cfg['batch']}" if plan.uses_sep else "hines_mono")
+    traffic = _traffic(tkey + ("_dfs" if cfg.get("dfs") else ""))
     line = {
         "metric": "unknowns solved/s (fp64), Hines " + ("multi" if multi else "mono"),
         "value": unknowns * args.steps / wall, "unit": "unknowns/s", "ms_per_step": ms_step,
@@ -637,7 +649,10 @@ def _hines_common(args, multi, which=None):
                      "traffic": traffic,
                      "schedule": "levels" if plan.uses_levels else
                                  "two lanes for the largest trees" if plan.split else
-                                 "sixteen lanes per neuron (separators)" if plan.uses_sep else "one lane per neuron",
+                                 ("separators, every tree on its own lanes" if multi else
+                                  "sixteen lanes per neuron (separators)") if plan.uses_sep else
+                                 "one lane per neuron, general variant (parents beyond 16)" if general else
+                                 "one lane per neuron",
                      "kernel_ms": kern_ms, "timed": "one solve call", "bytes_per_launch": alg_bytes,
                      "counter_gbs": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9},
     }
@@ -667,7 +682,8 @@ def _hines_common(args, multi, which=None):
                       "norm": "||V_gpu - V_oracle|| / ||V_oracle|| per neuron, one solve"}
     if not args.no_cpu_baseline:
         if multi:
-            small = W.hines_multi(2048, cfg["nmin"], cfg["nmax"], rng=np.random.default_rng(9))
+            small = W.hines_multi(2048, cfg["nmin"], cfg["nmax"], rng=np.random.default_rng(9),
+                                  dfs=cfg.get("dfs", False))
 
             def sample(k):
                 for r in range((k + 2047) // 2048):
@@ -679,7 +695,7 @@ def _hines_common(args, multi, which=None):
             line["cpu_baseline"] = _cpu_baseline(sample, float(small.sizes.mean()), "neurons",
                                                  args.cpu_seconds)
         else:
-            small = W.hines_mono(cfg["n"], 4096, rng=np.random.default_rng(9))
+            small = W.hines_mono(cfg["n"], 4096, rng=np.random.default_rng(9), dfs=cfg.get("dfs", False))
             fl = [W.to_flat(v) for v in (small.u, small.l, small.d, small.rhs)]
 
             def sample(k):
@@ -722,12 +738,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=list(range(0, 11)))
+    ap.add_argument("--workload", type=int, default=1, choices=list(range(0, 13)))
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
     ap.add_argument("--split", action="store_true",
                     help="workloads 2, 9: time the separate factor and solve calls instead")
     ap.add_argument("--hines-schedule", default="auto", choices=["auto", "lanes", "split", "levels", "sep"],
-                    help="workloads 3, 4, 10: the plan's schedule (BPS_HINES_*)")
+                    help="workloads 3, 4, 10, 11, 12: the plan's schedule (BPS_HINES_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -764,7 +780,8 @@ def main():
           4: lambda a: _hines_common(a, True), 5: lambda a: bench_hyperdiffusion(a, 5),
           6: lambda a: bench_hyperdiffusion(a, 6), 7: lambda a: bench_tri(a, 7),
           8: lambda a: bench_tri(a, 8), 9: lambda a: bench_penta(a, 9),
-          10: lambda a: _hines_common(a, False, 10)}[args.workload]
+          10: lambda a: _hines_common(a, False, 10), 11: lambda a: _hines_common(a, False, 11),
+          12: lambda a: _hines_common(a, True, 12)}[args.workload]
     line = fn(args)
     roof = line.get("roofline")
     if roof and roof.get("bound") == "hbm":

@@ -375,8 +375,7 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     its branches finish); a tree whose two-lane schedule
  *                     does not shorten it stays on one lane.  Mono plans:
  *                     as LANES;
- *   BPS_HINES_SEP     trees whose parents all lie within 8 compartments:
- *                     single compartments (separators) cut each tree into
+ *   BPS_HINES_SEP     single compartments (separators) cut each tree into
  *                     components with at most one separator below each;
  *                     lanes eliminate whole components (Algorithm 1 inside
  *                     each, holding their rows' factors in registers), the
@@ -399,8 +398,13 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     differ by rounding; a neuron any of whose pivots in
  *                     this order is zero or not finite is solved again by
  *                     Algorithm 1 in the same call (its info is Algorithm
- *                     1's).  BPS_ENOTSUP for other trees or when no
- *                     partition fits the lanes (32 rows each);
+ *                     1's).  A lane keeps its pending updates and
+ *                     voltages in eight slots, given per lane from the
+ *                     tree's own order (parents may lie anywhere before
+ *                     their children): components are made small enough
+ *                     that no lane holds more than eight at once.
+ *                     BPS_ENOTSUP for larger trees or when no partition
+ *                     fits the lanes (32 rows each);
  *   BPS_HINES_LEVELS  one wavefront per neuron: the tree cut into its
  *                     unbranched sections, grouped by level (the page's
  *                     per-branch / per-level decomposition of section 4),

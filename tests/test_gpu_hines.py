@@ -249,8 +249,11 @@ def test_multi_split_auto_choice():
     """The automatic choice puts trees on two lanes, largest first, while one
     lane per neuron leaves SIMDs without a wavefront (fewer than 1024 blocks
     of 64), and none when the blocks fill them."""
-    print("hines multi split auto 2048 neurons of 256..2048 (parents within 16)", flush=True)
-    mm = W.hines_multi(2048, 256, 2048, rng=np.random.default_rng(41), window=16)
+    print("hines multi split auto 4096 neurons of 40..210 (parents within 16)", flush=True)
+    # trees averaging under 128 compartments (not the separator schedules),
+    # more than the level schedule's 393216 compartments in all
+    mm = W.hines_multi(4096, 40, 210, rng=np.random.default_rng(41), window=16)
+    assert mm.sizes.mean() < 128 and mm.sizes.sum() > 393216
     assert max(np.max(np.arange(1, n) - mm.neuron(s)[0][1:]) for s, n in enumerate(mm.sizes)) > 8
     plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
     assert not plan.uses_levels
@@ -463,27 +466,29 @@ def test_levels_breakdown_info():
 def test_levels_auto_choice_and_limits():
     rng = np.random.default_rng(13)
     p = W.random_tree(300, rng)
-    # automatic choice for mono trees whose parents lie within 8: sixteen lanes
+    # automatic choice for mono trees the sixteen-lane schedule takes
     assert bps.hines_plan_create(2621, [300], p, mono=True).uses_sep
     assert bps.hines_plan_create(30000, [300], p, mono=True).uses_sep
     small = W.random_tree(128, rng)
     assert bps.hines_plan_create(16384, [128], small, mono=True).uses_sep      # 2^21 compartments
     plan = bps.hines_plan_create(16385, [128], small, mono=True)
     assert not plan.uses_sep and not plan.uses_levels
-    # other mono trees: levels for at most 786432 compartments in the batch
-    p16 = W.random_tree(300, rng, window=16)
-    assert (np.arange(1, 300) - p16[1:]).max() > 8
-    assert bps.hines_plan_create(2621, [300], p16, mono=True).uses_levels
-    assert not bps.hines_plan_create(2622, [300], p16, mono=True).uses_levels
+    # mono trees the sixteen-lane schedule does not take (a star: 299
+    # one-compartment components): levels for at most 786432 compartments
+    star = np.array([-1] + [0] * 299, dtype=np.int32)
+    assert not bps.hines_plan_create(2621, [300], star, mono=True).uses_sep
+    assert bps.hines_plan_create(2621, [300], star, mono=True).uses_levels
+    assert not bps.hines_plan_create(2622, [300], star, mono=True).uses_levels
     big = W.random_tree(5000, rng)
     assert not bps.hines_plan_create(10, [5000], big, mono=True).uses_levels
-    # multi-morphology trees the separator schedules do not take (parents up
-    # to 16 away): at most 393216 compartments
-    sizes = np.full(768, 512, dtype=np.int32)
-    par = np.concatenate([W.random_tree(512, rng, window=16) for _ in range(769)])
-    assert bps.hines_plan_create(768, sizes, par[:768 * 512], mono=False).uses_levels
-    plan = bps.hines_plan_create(769, np.full(769, 512, dtype=np.int32), par, mono=False)
-    assert not plan.uses_levels and plan.split == 769
+    # multi-morphology batches the separator schedules are not chosen for
+    # (trees averaging under 128 compartments): at most 393216 compartments
+    sizes = np.full(3096, 127, dtype=np.int32)
+    par = np.concatenate([W.random_tree(127, rng, window=16) for _ in range(3097)])
+    plan = bps.hines_plan_create(3096, sizes, par[:3096 * 127], mono=False)
+    assert plan.uses_levels and not plan.uses_sep
+    plan = bps.hines_plan_create(3097, np.full(3097, 127, dtype=np.int32), par, mono=False)
+    assert not plan.uses_levels and not plan.uses_sep and plan.split == 3097
     with pytest.raises(bps.BpsError):
         bps.hines_plan_create(10, [5000], big, mono=True, schedule=bps.BPS_HINES_LEVELS)
 

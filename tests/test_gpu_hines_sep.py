@@ -4,8 +4,9 @@ Per-neuron normwise relative error <= 1e-10 through the C-ABI, on ragged
 batches (not a multiple of the 16 neurons of a workgroup), ld > batch, both
 row counts per lane (16 and 32), chains (every component a path), the
 largest trees the schedule takes, breakdowns (info equals Algorithm 1's and
-the other neurons are unaffected), repeatability, and sampled neurons of
-the full 100000 x 512 workload; multi-morphology batches (every tree its own
+the other neurons are unaffected), repeatability, trees with parents far
+back (depth-first numbering, wide windows: ring slots given per lane), and
+sampled neurons of the full 100000 x 512 workload; multi-morphology batches (every tree its own
 schedule, the schedule-ordered layout) likewise, with the pack contract and
 the full 32768-neuron workload sampled."""
 import numpy as np
@@ -77,7 +78,8 @@ def test_sep_matches_oracle(n, batch, ld):
     assert np.all(info == 0)
 
 
-@pytest.mark.parametrize("shape", ["chain", "far8", "caterpillar", "window2", "broom"])
+@pytest.mark.parametrize("shape", ["chain", "far8", "caterpillar", "window2", "broom",
+                                   "far9", "window64", "dfs", "comb_reversed"])
 def test_sep_tree_shapes(shape):
     rng = np.random.default_rng(5)
     n = 480
@@ -89,6 +91,15 @@ def test_sep_tree_shapes(shape):
         p = np.array([-1] + [i - 2 if i % 2 == 0 else i - 1 for i in range(1, n)])
     elif shape == "window2":
         p = W.random_tree(n, rng, window=2)
+    elif shape == "far9":
+        p = np.array([-1] + [max(0, i - 9) for i in range(1, n)])
+    elif shape == "window64":
+        p = W.random_tree(n, rng, window=64)
+    elif shape == "dfs":
+        p = W.dfs_tree(n, rng)
+    elif shape == "comb_reversed":
+        # spine 0..k, then its leaves from the last spine compartment back
+        p = np.array([-1] + list(range(119)) + list(range(119, -1, -1)))
     else:
         p = np.array([-1] + [max(0, i - 1 - (i - 1) % 8) for i in range(1, n)])
     print(f"hines sep shape={shape}", flush=True)
@@ -122,17 +133,25 @@ def test_sep_breakdown_info():
 
 def test_sep_refusals_and_auto():
     rng = np.random.default_rng(3)
-    p16 = W.random_tree(300, rng, window=16)
-    if (np.arange(1, 300) - p16[1:]).max() > 8:
-        with pytest.raises(bps.BpsError):
-            bps.hines_plan_create(64, [300], p16, mono=True, schedule=SEP)
+    # trees with parents far back are taken (ring slots per lane), also by
+    # the automatic choice
+    for p in (W.random_tree(300, rng, window=16), W.dfs_tree(300, rng)):
+        assert (np.arange(1, 300) - p[1:]).max() > 8
+        bps.hines_plan_create(64, [300], p, mono=True, schedule=SEP).close()
+        plan = bps.hines_plan_create(64, [300], p, mono=True)
+        assert plan.uses_sep
+        plan.close()
+    # too large for sixteen lanes of 32 rows; a star of 1499 components
     with pytest.raises(bps.BpsError):
         bps.hines_plan_create(64, [1500], W.random_tree(1500, rng), mono=True, schedule=SEP)
-    sizes = np.full(4, 50, dtype=np.int32)
-    p9 = np.array([-1] + [max(0, i - 9) for i in range(1, 50)], dtype=np.int32)
     with pytest.raises(bps.BpsError):
-        bps.hines_plan_create(4, sizes, np.concatenate([W.random_tree(50, rng)] * 3 + [p9]), mono=False,
+        bps.hines_plan_create(64, [1500], np.array([-1] + [0] * 1499, dtype=np.int32), mono=True,
                               schedule=SEP)
+    # a multi-morphology tree too large for 128 lanes of 32 rows
+    sizes = np.array([50, 50, 9000], dtype=np.int32)
+    with pytest.raises(bps.BpsError):
+        bps.hines_plan_create(3, sizes, np.concatenate([W.random_tree(50, rng)] * 2 +
+                                                       [W.random_tree(9000, rng)]), mono=False, schedule=SEP)
 
 
 @pytest.mark.slow
@@ -260,10 +279,27 @@ def test_sep_multi_full_workload_sampled():
         assert np.linalg.norm(got - V[0]) / np.linalg.norm(V[0]) <= 1e-10
 
 
+def test_sep_multi_far_parents():
+    """Depth-first numbered trees of 256..2048 compartments (parents far
+    back), on the automatic choice: separator schedules, against the oracle."""
+    print("hines sep multi: depth-first numbered trees", flush=True)
+    rng = np.random.default_rng(31)
+    trees = [W.dfs_tree(int(n), rng) for n in rng.integers(256, 2049, size=600)] + \
+            [W.random_tree(int(n), rng, window=32) for n in rng.integers(256, 2049, size=100)]
+    mm = W.hines_multi_trees(trees, rng)
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
+    assert plan.uses_sep and not plan.uses_levels and plan.split == 0
+    plan.close()
+    out, info = _run_multi(mm, twice=True)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    assert _multi_err(mm, out, ref) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+
+
 def test_sep_multi_auto_choice():
     """The automatic choice for multi-morphology batches: separator schedules
-    when every tree has its parents within 8 and the trees average at least
-    128 compartments; otherwise the other schedules."""
+    when the trees average at least 128 compartments (wherever their parents
+    lie); otherwise the other schedules."""
     rng = np.random.default_rng(23)
     mm = W.hines_multi(300, 100, 160, rng=rng)
     plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
@@ -279,7 +315,7 @@ def test_sep_multi_auto_choice():
     plan.close()
     w16 = W.hines_multi(64, 256, 2048, rng=rng, window=16)
     plan = bps.hines_plan_create(w16.batch, w16.sizes, w16.parent, mono=False)
-    assert not plan.uses_sep
+    assert plan.uses_sep
     plan.close()
     out, info = _run_multi(big, schedule=bps.BPS_HINES_AUTO)
     ref, rinfo = oracle.hines_multi_solve(big.offsets, big.parent, big.u, big.l, big.d, big.rhs)

@@ -155,7 +155,22 @@ def _trees():
     # a broom of short brooms: runs of 8 children on one parent
     out.append(("broom", np.array([-1] + [max(0, i - 1 - (i - 1) % 8) for i in range(1, 200)],
                                   dtype=np.int32)))
+    # parents far back: every parent 9 away, wider windows, depth-first
+    # numbering, and a comb whose leaves come after the whole spine in
+    # reverse (every spine compartment pending at once in descending order)
+    out.append(("far9", np.array([-1] + [max(0, i - 9) for i in range(1, 300)], dtype=np.int32)))
+    for w in (16, 64):
+        out.append((f"window{w}_400", W.random_tree(400, rng, window=w)))
+    for n in (60, 300, 512):
+        out.append((f"dfs_{n}", W.dfs_tree(n, rng)))
+    out.append(("comb_reversed", _comb(100)))
     return out
+
+
+def _comb(k):
+    """Spine 0..k, then one leaf per spine compartment, numbered from the
+    last spine compartment back to the first."""
+    return np.array([-1] + list(range(k)) + list(range(k, -1, -1)), dtype=np.int32)
 
 
 @pytest.mark.parametrize("name,p", _trees(), ids=lambda v: v if isinstance(v, str) else "")
@@ -206,12 +221,26 @@ def test_sep_schedule_shapes():
     assert small is not None and small["R"] == 16
 
 
+def test_sep_schedule_slots_beyond_window():
+    """Ring slots are given per lane, not by compartment number: a parent far
+    back costs a slot only while its children's updates are pending, and the
+    reversed comb (up to 100 pending at once with one slot per compartment)
+    is cut into components small enough for the eight slots."""
+    _lib_or_skip()
+    S = bps.hines_sep_schedule(_comb(100))
+    assert S is not None and S["ns"] >= 2
+    own, par = (S["codes"] >> 11) & 7, (S["codes"] >> 14) & 7
+    live = (S["codes"] & LIVE) != 0
+    assert own[live].max() <= 7 and par[live].max() <= 7
+
+
 def test_sep_schedule_refusals():
     _lib_or_skip()
-    # a parent 9 compartments away, and a tree too large for 16 x 32 rows
-    p9 = np.array([-1] + [max(0, i - 9) for i in range(1, 50)], dtype=np.int32)
-    assert bps.hines_sep_schedule(p9) is None
-    assert "8 compartments" in bps.bps_last_error()
+    # a star (1499 one-compartment components, more than 255), and a tree
+    # too large for 16 x 32 rows
+    star = np.array([-1] + [0] * 1499, dtype=np.int32)
+    assert bps.hines_sep_schedule(star) is None
+    assert "no partition" in bps.bps_last_error()
     assert bps.hines_sep_schedule(W.random_tree(1200, np.random.default_rng(1))) is None
     with pytest.raises(bps.BpsError):
         bps.hines_sep_schedule(np.array([-1, 0, 5], dtype=np.int32))

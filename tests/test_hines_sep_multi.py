@@ -234,6 +234,26 @@ def test_sep_multi_replay_matches_oracle(batch, nmin, nmax, seed):
     assert err <= 1e-13
 
 
+def test_sep_multi_replay_far_parents():
+    """Depth-first numbered trees and wide windows: parents far back."""
+    _lib_or_skip()
+    rng = np.random.default_rng(29)
+    trees = [W.dfs_tree(int(n), rng) for n in rng.integers(100, 1500, size=30)] + \
+            [W.random_tree(int(n), rng, window=40) for n in rng.integers(100, 800, size=10)]
+    mm = W.hines_multi_trees(trees, rng)
+    assert max(int(np.max(np.arange(1, n) - mm.neuron(s)[0][1:])) for s, n in enumerate(mm.sizes)) > 100
+    Lo = bps.hines_sep_multi_layout(mm.sizes, mm.parent)
+    assert Lo is not None
+    _check_ranges(Lo, mm.sizes)
+    V, bad = _replay(Lo, mm.sizes, mm.u, mm.l, mm.d, mm.rhs)
+    assert not bad
+    ref, info = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    o = mm.offsets
+    err = max(np.linalg.norm(V[o[s]:o[s + 1]] - ref[o[s]:o[s + 1]]) / np.linalg.norm(ref[o[s]:o[s + 1]])
+              for s in range(mm.batch))
+    assert err <= 1e-13
+
+
 def test_sep_multi_replay_many_separators():
     """Trees of doubling chains give workgroups of more separators than lanes
     (the substitution's lanes then hold a second separator each)."""
@@ -269,9 +289,9 @@ def test_sep_multi_layout_lds_budget(batch, nmin, nmax, window):
 
 def test_sep_multi_layout_refusals():
     _lib_or_skip()
-    p9 = np.array([-1] + [max(0, i - 9) for i in range(1, 40)], dtype=np.int32)
+    big = W.random_tree(9000, np.random.default_rng(1))
     good = W.random_tree(40, np.random.default_rng(1))
-    assert bps.hines_sep_multi_layout([40, 40], np.r_[good, p9]) is None
-    assert "8 compartments" in bps.bps_last_error()
+    assert bps.hines_sep_multi_layout([40, 9000], np.r_[good, big]) is None
+    assert "too large" in bps.bps_last_error()
     with pytest.raises(bps.BpsError):
         bps.hines_sep_multi_layout([3], [-1, 0, 5])

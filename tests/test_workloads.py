@@ -66,3 +66,30 @@ def test_tri_dominance_and_outside_zeros():
     assert np.all(tb.b < np.abs(tb.a) + np.abs(tb.c) + 2)
     again = W.tri_dominant(33, 20, rng=np.random.default_rng(1), chunk=8)
     np.testing.assert_array_equal(tb.y, again.y)
+
+
+def test_dfs_tree_is_a_preorder_of_the_drawn_tree():
+    """Depth-first numbering: each compartment's parent is the one before it
+    or an ancestor of it; the same tree as random_tree's draw up to the
+    numbering (children counts agree); parents far back occur."""
+    rng = np.random.default_rng(4)
+    far = 0
+    for n in (1, 2, 3, 17, 300, 2048):
+        p = W.dfs_tree(n, np.random.default_rng(n))
+        p0 = W.random_tree(n, np.random.default_rng(n))
+        assert p[0] == -1 and np.all(p[1:] < np.arange(1, n))
+        for i in range(1, n):
+            a = i - 1
+            while a != p[i] and a > 0:
+                a = p[a]
+            assert a == p[i]
+        kids = lambda q: np.sort(np.bincount(q[1:], minlength=n)) if n > 1 else q
+        np.testing.assert_array_equal(kids(p), kids(p0))
+        far = max(far, int(np.max(np.arange(1, n) - p[1:], initial=0)))
+    assert far > 100
+    hm = W.hines_mono(300, 4, rng=rng, dfs=True)
+    acc = np.abs(hm.l).copy()
+    for i in range(1, 300):
+        acc[hm.parent[i]] += np.abs(hm.u[i])
+    assert np.all(hm.d - acc >= 1.0)
+    assert W.WORKLOADS[11]["dfs"] and W.WORKLOADS[12]["dfs"]

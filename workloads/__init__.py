@@ -252,21 +252,21 @@ def _hines_values(parent: np.ndarray, shape, rng: np.random.Generator):
     u[0] = 0.0
     l[0] = 0.0
     d = 1.0 + np.abs(l) + rng.uniform(0.0, 1.0, size=shape)
-    for i in range(1, n):
-        d[parent[i]] += np.abs(u[i])
+    # children in index order, as a loop over i = 1 .. n-1 would add them
+    np.add.at(d, np.asarray(parent[1:n], dtype=np.int64), np.abs(u[1:n]))
     rhs = rng.uniform(-1.0, 1.0, size=shape)
     return u, l, d, rhs
 
 
 def hines_mono(n: int = 512, batch: int = 100000,
-               rng: np.random.Generator | None = None) -> HinesMono:
+               rng: np.random.Generator | None = None, dfs: bool = False) -> HinesMono:
     """One seeded tree shared by all neurons; per-neuron values.
 
-    Draw order: the tree, then u, l, the U(0,1) part of d, rhs, each as one
-    (n, batch) block.
+    Draw order: the tree (``dfs_tree`` when dfs, else ``random_tree``), then
+    u, l, the U(0,1) part of d, rhs, each as one (n, batch) block.
     """
     rng = rng if rng is not None else rng_for(3)
-    p = random_tree(n, rng)
+    p = dfs_tree(n, rng) if dfs else random_tree(n, rng)
     u, l, d, rhs = _hines_values(p, (n, batch), rng)
     return HinesMono(p, u, l, d, rhs)
 
@@ -292,9 +292,11 @@ class HinesMulti:
 
 
 def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
-                rng: np.random.Generator | None = None, window: int = 8) -> HinesMulti:
+                rng: np.random.Generator | None = None, window: int = 8,
+                dfs: bool = False) -> HinesMulti:
     """One seeded tree per neuron, compartment count uniform in [nmin, nmax]
-    (parents drawn as in ``random_tree`` with this window).
+    (parents drawn as in ``random_tree`` with this window; renumbered depth
+    first as ``dfs_tree`` does when dfs).
 
     The sizes are drawn first (one block), then neuron by neuron: its tree,
     then its u, l, d, rhs exactly as ``hines_mono`` draws them for batch 1.
@@ -309,11 +311,46 @@ def hines_multi(batch: int = 32768, nmin: int = 256, nmax: int = 2048,
     u = np.empty(total); l = np.empty(total); d = np.empty(total); rhs = np.empty(total)
     for s in range(batch):
         o0, o1 = offsets[s], offsets[s + 1]
-        p = random_tree(int(sizes[s]), rng, window=window)
+        p = (dfs_tree if dfs else random_tree)(int(sizes[s]), rng, window=window)
         us, ls, ds, rs = _hines_values(p, (int(sizes[s]),), rng)
         parent[o0:o1] = p
         u[o0:o1] = us; l[o0:o1] = ls; d[o0:o1] = ds; rhs[o0:o1] = rs
     return HinesMulti(sizes, offsets, parent, u, l, d, rhs)
+
+
+def dfs_tree(n: int, rng: np.random.Generator, window: int = 8) -> np.ndarray:
+    """A tree drawn as ``random_tree`` draws it, renumbered in depth-first
+    preorder with each compartment's children visited in random order (the
+    usual numbering of reconstructed morphologies): a branch's second
+    subtree starts after the whole first one, so parents lie arbitrarily far
+    back."""
+    p0 = random_tree(n, rng, window=window)
+    keys = rng.random(n)
+    if n == 1:
+        return p0
+    par = p0.tolist()
+    size = [1] * n
+    for i in range(n - 1, 0, -1):
+        size[par[i]] += size[i]
+    # children grouped by parent, in random order; each one's offset after
+    # its parent: 1 + the subtrees of the siblings before it
+    kids = np.lexsort((keys[1:], p0[1:])) + 1
+    sz = np.asarray(size, dtype=np.int64)[kids]
+    grp = p0[kids]
+    csum = np.cumsum(sz) - sz
+    first = np.r_[True, grp[1:] != grp[:-1]]
+    start = np.maximum.accumulate(np.where(first, csum, 0))
+    off = np.empty(n, dtype=np.int64)
+    off[kids] = 1 + csum - start
+    offl = off.tolist()
+    pre = [0] * n
+    for c in range(1, n):
+        pre[c] = pre[par[c]] + offl[c]
+    pre = np.asarray(pre, dtype=np.int64)
+    p = np.empty(n, dtype=np.int32)
+    p[0] = -1
+    p[pre[1:]] = pre[p0[1:]]
+    return p
 
 
 def hines_multi_trees(trees, rng: np.random.Generator) -> HinesMulti:
@@ -378,4 +415,9 @@ WORKLOADS = {
     # Hines mono with few neurons (the page measures batches from 256): the
     # level schedule's regime
     10: dict(name="hines_mono_n512_b256", kind="hines_mono", n=512, batch=256),
+    # workloads 3 and 4 with their trees numbered depth first (the numbering
+    # of reconstructed morphologies: parents arbitrarily far back)
+    11: dict(name="hines_mono_dfs_n512_b100000", kind="hines_mono", n=512, batch=100000, dfs=True),
+    12: dict(name="hines_multi_dfs_b32768_n256to2048_20steps", kind="hines_multi",
+             batch=32768, nmin=256, nmax=2048, nsteps=20, dfs=True),
 }
