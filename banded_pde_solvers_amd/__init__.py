@@ -555,13 +555,13 @@ def hines_sep_multi_layout(sizes, parent):
 
 def hines_sep_schedule(parent):
     """Host-only BPS_HINES_SEP schedule of one tree (see bps.h), decoded:
-    a dict with R, ns, nc, npc, nh, codes (16, R) uint32, bases (16, 3),
-    septab (ns, 5), comptab (nc, 3), clist (nc,); None when the tree does
-    not qualify."""
+    a dict with R, lanes (16 or 32), ns, nc, npc, nh, codes (lanes, R)
+    uint32, bases (lanes, 3), septab (ns, 5), comptab (nc, 3), clist (nc,);
+    None when the tree does not qualify."""
     import numpy as np
     par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
     n = len(par)
-    cap = 8 + 16 * 32 + 48 + 5 * n + 4 * n + 64
+    cap = 8 + 32 * 32 + 96 + 5 * n + 4 * n + 64
     out = np.zeros(cap, dtype=np.int32)
     i32p = ctypes.POINTER(ctypes.c_int32)
     L = load_library()
@@ -571,17 +571,18 @@ def hines_sep_schedule(parent):
     if m == 0:
         return None
     R, ns, nc, npc, nh = (int(v) for v in out[:5])
+    K = int(out[6])
     o = 8
-    codes = out[o:o + 16 * R].view(np.uint32).reshape(16, R).copy()
-    o += 16 * R
-    bases = out[o:o + 48].reshape(16, 3).copy()
-    o += 48
+    codes = out[o:o + K * R].view(np.uint32).reshape(K, R).copy()
+    o += K * R
+    bases = out[o:o + 3 * K].reshape(K, 3).copy()
+    o += 3 * K
     septab = out[o:o + ns * 5].reshape(ns, 5).copy()
     o += ns * 5
     comptab = out[o:o + nc * 3].reshape(nc, 3).copy()
     o += nc * 3
     clist = out[o:o + nc].copy()
-    return {"R": R, "ns": ns, "nc": nc, "npc": npc, "nh": nh, "codes": codes, "bases": bases,
+    return {"R": R, "lanes": K, "ns": ns, "nc": nc, "npc": npc, "nh": nh, "codes": codes, "bases": bases,
             "septab": septab, "comptab": comptab, "clist": clist}
 
 

@@ -23,6 +23,8 @@
 #include <cstring>
 #include <string>
 #include <thread>
+#include <tuple>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -32,9 +34,7 @@ namespace bps {
 
 namespace {
 
-constexpr int kSepLanes = 16;       // lanes per neuron
-constexpr int kSepNeurons = 16;     // neurons per workgroup
-constexpr int kSepThreads = kSepLanes * kSepNeurons;
+constexpr int kSepNeurons = 16;     // neurons per workgroup (16 or 32 lanes each)
 constexpr int kSepSlots = 8;        // ring of pending updates / voltages per lane
 constexpr int kSepHeader = 8;
 
@@ -84,16 +84,17 @@ __device__ __forceinline__ double recip(double x)
     return fma(fma(-x, r, 1.0), r, r);
 }
 
-// Words of the schedule's tables after the header.
-__host__ __device__ inline int sep_tab_words(int R, int ns, int nc)
+// Words of the schedule's tables after the header (lanes per neuron: 16 or 32).
+__host__ __device__ inline int sep_tab_words(int R, int ns, int nc, int lanes)
 {
-    return kSepLanes * R + kSepLanes * 3 + ns * 5 + nc * 4;
+    return lanes * R + lanes * 3 + ns * 5 + nc * 4;
 }
 
-template <int R>
-__global__ void __launch_bounds__(kSepThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int R, int LANES>
+__global__ void __launch_bounds__(LANES * kSepNeurons) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_hines_sep(SepArgs A)
 {
+    constexpr int NT = LANES * kSepNeurons;   // threads: lane k = tid / 16 of neuron j = tid % 16
     extern __shared__ __align__(16) unsigned char sep_lds[];
     const int tid = threadIdx.x, k = tid >> 4, j = tid & 15;
     const int64_t s = int64_t(blockIdx.x) * kSepNeurons + j;
@@ -101,28 +102,28 @@ k_hines_sep(SepArgs A)
     // lanes past the batch shadow the last neuron (loads only)
     const uint32_t s8 = uint32_t(uint64_t(act ? s : A.batch - 1) * 8);
     const int ns = A.ns, nc = A.nc, npc = A.npc, nh = A.nh;
-    double2 *ring = reinterpret_cast<double2 *>(sep_lds);     // [8][256]
-    double2 *red = ring + kSepSlots * kSepThreads;             // [nc][16]
+    double2 *ring = reinterpret_cast<double2 *>(sep_lds);     // [8][NT]
+    double2 *red = ring + kSepSlots * NT;             // [nc][16]
     double2 *pdat = red + nc * kSepNeurons;                    // [npc][16][2]
     double2 *sepv = pdat + npc * 2 * kSepNeurons;              // [ns][16][2]
     double *su = reinterpret_cast<double *>(sepv + ns * 2 * kSepNeurons);   // [ns][16]
     double *hbuf = su + ns * kSepNeurons;                      // [nh + 2][16]
-    int *badf = reinterpret_cast<int *>(hbuf + (nh + 2) * kSepNeurons);  // [256]
-    int *flag = badf + kSepThreads;                            // [16]
+    int *badf = reinterpret_cast<int *>(hbuf + (nh + 2) * kSepNeurons);  // [NT]
+    int *flag = badf + NT;                            // [16]
     int *tab = flag + kSepNeurons;                             // the schedule's tables
-    const int *codes = tab, *bases = tab + kSepLanes * R, *septab = bases + kSepLanes * 3;
+    const int *codes = tab, *bases = tab + LANES * R, *septab = bases + LANES * 3;
     const int *comptab = septab + ns * 5, *clist = comptab + nc * 3;
 
     const SepBuf U(A.u, A.bytes), L(A.l, A.bytes), Dg(A.d, A.bytes), Rh(A.rhs, A.bytes);
     const uint32_t ld8 = A.ld8;
-    const int ntab = sep_tab_words(R, ns, nc);
-    for (int i = tid; i < ntab; i += kSepThreads) tab[i] = A.tab[i];
+    const int ntab = sep_tab_words(R, ns, nc, LANES);
+    for (int i = tid; i < ntab; i += NT) tab[i] = A.tab[i];
 #pragma unroll
-    for (int q = 0; q < kSepSlots; ++q) ring[q * kSepThreads + tid] = make_double2(0.0, 0.0);
+    for (int q = 0; q < kSepSlots; ++q) ring[q * NT + tid] = make_double2(0.0, 0.0);
     if (k == 0) hbuf[nh * kSepNeurons + j] = 0.0;              // read by rows off the paths
     // the separators' own rows
-    for (int i = k; i < ns; i += kSepLanes) {
-        const uint32_t o = uint32_t(A.tab[kSepLanes * R + kSepLanes * 3 + i * 5]) * ld8 + s8;
+    for (int i = k; i < ns; i += LANES) {
+        const uint32_t o = uint32_t(A.tab[LANES * R + LANES * 3 + i * 5]) * ld8 + s8;
         const double uu = U.ld(o), ll = L.ld(o), dd = Dg.ld(o), rr = Rh.ld(o);
         su[i * kSepNeurons + j] = uu;
         sepv[(i * kSepNeurons + j) * 2] = make_double2(dd, rr);
@@ -151,9 +152,9 @@ k_hines_sep(SepArgs A)
         const double u_ = bu[t % D], l_ = bl[t % D], d_ = bd[t % D], r_ = br[t % D];
         const bool live = w0 & kSepLive, path = w0 & kSepPath, top = w0 & kSepTop;
         const int own = (w0 >> 11) & 7, par = (w0 >> 14) & 7;
-        const double2 pd = ring[own * kSepThreads + tid];
-        const double2 po = ring[par * kSepThreads + tid];
-        ring[own * kSepThreads + tid] = make_double2(0.0, 0.0);
+        const double2 pd = ring[own * NT + tid];
+        const double2 po = ring[par * NT + tid];
+        ring[own * NT + tid] = make_double2(0.0, 0.0);
         const double dd = d_ - pd.x, rr = r_ - pd.y;
         bad |= int(live) & int(bad_pivot(dd));
         asm volatile("" : "+v"(bad));   // test each pivot now, not all of them at the end
@@ -182,7 +183,7 @@ k_hines_sep(SepArgs A)
             }
         } else {
             const double2 o = par == own ? make_double2(0.0, 0.0) : po;
-            ring[par * kSepThreads + tid] = make_double2(o.x + cb.x, o.y + cb.y);
+            ring[par * NT + tid] = make_double2(o.x + cb.x, o.y + cb.y);
         }
         if (t + D < R) load(t + D, qq);
     }
@@ -191,7 +192,7 @@ k_hines_sep(SepArgs A)
 
     // ---- the separators' tree system ----
     // (a) every separator's row with its components' terms (all lanes)
-    for (int i = k; i < ns; i += kSepLanes) {
+    for (int i = k; i < ns; i += LANES) {
         const int rp = septab[i * 5 + 1], pcomp = septab[i * 5 + 2];
         const int cb = septab[i * 5 + 3], ce = septab[i * 5 + 4];
         const double2 dr = sepv[(i * kSepNeurons + j) * 2];
@@ -226,7 +227,7 @@ k_hines_sep(SepArgs A)
         // the CU run their sweeps: it takes the issue slots first
         __builtin_amdgcn_s_setprio(3);
         int anyb = 0;
-        for (int kk = 0; kk < kSepLanes; ++kk) anyb |= badf[kk * kSepNeurons + j];
+        for (int kk = 0; kk < LANES; ++kk) anyb |= badf[kk * kSepNeurons + j];
         // the next separator's row is read one step ahead (two register sets
         // in turn); an update for the next separator is carried in registers,
         // others go through LDS (they reach two or more rows ahead, which
@@ -296,7 +297,7 @@ k_hines_sep(SepArgs A)
     }
     __syncthreads();
     // (c) each component's parent voltage and u x of its lower separator
-    for (int c = k; c < nc; c += kSepLanes) {
+    for (int c = k; c < nc; c += LANES) {
         const int pc = comptab[c * 3], sc = comptab[c * 3 + 1];
         const double xp = pc >= 0 ? sepv[(pc * kSepNeurons + j) * 2].x : 0.0;
         const double sg = sc >= 0 ? su[sc * kSepNeurons + j] * sepv[(sc * kSepNeurons + j) * 2].x : 0.0;
@@ -307,7 +308,7 @@ k_hines_sep(SepArgs A)
     // ---- second sweep: each component from its root down ----
     const bool ok = flag[j] == 0;
     const SepBuf V(A.rhs, act && ok ? A.bytes : 0u);
-    for (int i = k; i < ns; i += kSepLanes)
+    for (int i = k; i < ns; i += LANES)
         V.st(sepv[(i * kSepNeurons + j) * 2].x, uint32_t(septab[i * 5]) * ld8 + s8);
     double sg = 0.0;
 #pragma unroll
@@ -317,11 +318,11 @@ k_hines_sep(SepArgs A)
         const int own = (w0 >> 11) & 7, par = (w0 >> 14) & 7;
         if (top) --ccomp;
         if (path) --chidx;
-        const double2 v = top ? red[ccomp * kSepNeurons + j] : ring[par * kSepThreads + tid];
+        const double2 v = top ? red[ccomp * kSepNeurons + j] : ring[par * NT + tid];
         sg = top ? v.y : sg;
         const double h = hbuf[(path ? chidx : nh) * kSepNeurons + j];
         const double x = q[t] - m[t] * v.x - h * sg;
-        reinterpret_cast<double *>(ring)[(own * kSepThreads + tid) * 2] = x;
+        reinterpret_cast<double *>(ring)[(own * NT + tid) * 2] = x;
         V.st(x, (w0 & kSepLive) ? uint32_t(w0 & 2047) * ld8 + s8 : kSepNoStore);
     }
 
@@ -788,9 +789,10 @@ struct SepTree {
     std::vector<int32_t> cbase, hbase, pbase, sbase;  // per lane
 };
 
-static bool sep_tree(int32_t n, const int32_t *p, int L, int R, bool sep_rows, SepTree &T)
+static bool sep_tree(int32_t n, const int32_t *p, int L, int R, bool sep_rows, SepTree &T,
+                     int32_t min_target = 6)
 {
-    for (int32_t target = std::min(R, 32); target >= 6; target -= 2) {
+    for (int32_t target = std::min(R, 32); target >= min_target; target -= 2) {
         SepPart S = sep_partition(n, p, target);
         const int32_t nc = int32_t(S.csize.size());
         std::vector<int32_t> sidx(n, -1), snode;
@@ -944,26 +946,32 @@ static bool sep_tree(int32_t n, const int32_t *p, int L, int R, bool sep_rows, S
 std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
 {
     if (n < 1 || n > 2047) { why = "tree size outside [1, 2047]"; return {}; }
-    for (int R : {16, 32}) {
+    // sixteen lanes of 16 or 32 rows, else thirty-two lanes of 24 or 32 rows;
+    // sixteen lanes of 32 rows only with components of at least 16 rows
+    // (measured: a tree of 560 squeezed into them by components of ~10
+    // rows, 57 separators, took 0.89 ms for 91424 neurons where one lane per
+    // neuron takes 0.72)
+    for (const auto [lanes, R, tmin] :
+         {std::tuple<int, int, int>{16, 16, 6}, {16, 32, 16}, {32, 24, 12}, {32, 32, 6}}) {
         SepTree T;
-        if (!sep_tree(n, p, kSepLanes, R, false, T)) continue;
+        if (!sep_tree(n, p, lanes, R, false, T, tmin)) continue;
         const int32_t ns = T.ns, nc = T.nc;
         if (nc > 255 || ns > 255 || T.nh > 1000) continue;
-        std::vector<int32_t> blob(kSepHeader + sep_tab_words(R, ns, nc), 0);
+        std::vector<int32_t> blob(kSepHeader + sep_tab_words(R, ns, nc, lanes), 0);
         blob[0] = R; blob[1] = ns; blob[2] = nc; blob[3] = T.npc; blob[4] = T.nh; blob[5] = n;
-        blob[6] = kSepLanes;
+        blob[6] = lanes;
         int32_t *codes = blob.data() + kSepHeader;
-        for (int l = 0; l < kSepLanes; ++l) {
+        for (int l = 0; l < lanes; ++l) {
             int t = 0;
             for (const SepRow &r : T.lanes[l])
                 codes[l * R + t++] = int32_t(uint32_t(r.node) | (uint32_t(r.own) << 11) |
                                              (uint32_t(r.par) << 14) | r.flags);
         }
-        int32_t *bt = codes + kSepLanes * R;
-        for (int l = 0; l < kSepLanes; ++l) {
+        int32_t *bt = codes + lanes * R;
+        for (int l = 0; l < lanes; ++l) {
             bt[l * 3] = T.cbase[l]; bt[l * 3 + 1] = T.hbase[l]; bt[l * 3 + 2] = T.pbase[l];
         }
-        int32_t *st = bt + kSepLanes * 3;
+        int32_t *st = bt + lanes * 3;
         int32_t *ct = st + ns * 5;
         int32_t *cl = ct + nc * 3;
         int32_t ncl = 0;
@@ -983,7 +991,7 @@ std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
         if (sep_lds_bytes(blob.data()) > 160 * 1024) continue;
         return blob;
     }
-    why = "no partition fits 16 lanes of 32 rows";
+    why = "no partition fits 32 lanes of 32 rows";
     return {};
 }
 
@@ -1192,22 +1200,23 @@ bps_status launch_hines_sepm(const SepMultiDev &S, const int32_t *parent_dev, co
 size_t sep_lds_bytes(const int32_t *blob)
 {
     const size_t R = size_t(blob[0]), ns = size_t(blob[1]), nc = size_t(blob[2]);
-    const size_t npc = size_t(blob[3]), nh = size_t(blob[4]);
-    return size_t(kSepSlots) * kSepThreads * 16 + nc * kSepNeurons * 16 + npc * kSepNeurons * 32 +
+    const size_t npc = size_t(blob[3]), nh = size_t(blob[4]), nt = size_t(blob[6]) * kSepNeurons;
+    return size_t(kSepSlots) * nt * 16 + nc * kSepNeurons * 16 + npc * kSepNeurons * 32 +
            ns * kSepNeurons * 32 + ns * kSepNeurons * 8 + (nh + 2) * kSepNeurons * 8 +
-           size_t(kSepThreads + kSepNeurons) * 4 + size_t(sep_tab_words(int(R), int(ns), int(nc))) * 4;
+           size_t(nt + kSepNeurons) * 4 + size_t(sep_tab_words(int(R), int(ns), int(nc), blob[6])) * 4;
 }
 
 hipError_t sep_prepare_device()
 {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_hines_sep<16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_hines_sepm<kSepMR>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_hines_sep<32>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    for (const void *f : {reinterpret_cast<const void *>(&k_hines_sep<16, 16>),
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 16>),
+                          reinterpret_cast<const void *>(&k_hines_sep<24, 32>),
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 32>)}) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+    }
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_hines_sepm<kSepMR>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
 }
 
 bps_status launch_hines_sep(const int32_t *blob_host, const int32_t *blob_dev, int64_t batch, int64_t ld,
@@ -1226,9 +1235,12 @@ bps_status launch_hines_sep(const int32_t *blob_host, const int32_t *blob_dev, i
     A.u = (const double *)u; A.l = (const double *)l; A.d = (const double *)d;
     A.rhs = (double *)rhs; A.work = (double *)work; A.info = info;
     const size_t lds = sep_lds_bytes(blob_host);
-    const dim3 grid(unsigned((batch + kSepNeurons - 1) / kSepNeurons));
-    if (R == 16) hipLaunchKernelGGL(k_hines_sep<16>, grid, dim3(kSepThreads), lds, st, A);
-    else hipLaunchKernelGGL(k_hines_sep<32>, grid, dim3(kSepThreads), lds, st, A);
+    const int lanes = blob_host[6];
+    const dim3 grid(unsigned((batch + kSepNeurons - 1) / kSepNeurons)), block(unsigned(lanes * kSepNeurons));
+    if (lanes == 32 && R == 24) hipLaunchKernelGGL((k_hines_sep<24, 32>), grid, block, lds, st, A);
+    else if (lanes == 32) hipLaunchKernelGGL((k_hines_sep<32, 32>), grid, block, lds, st, A);
+    else if (R == 16) hipLaunchKernelGGL((k_hines_sep<16, 16>), grid, block, lds, st, A);
+    else hipLaunchKernelGGL((k_hines_sep<32, 16>), grid, block, lds, st, A);
     BPS_LAUNCHED("k_hines_sep");
     return BPS_OK;
 }

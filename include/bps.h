@@ -385,8 +385,10 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     decomposition of section 4 with the pages' solve of
  *                     the reduced system, each compartment's values read and
  *                     written once.  Mono plans (trees of at most 2047
- *                     compartments): sixteen lanes per neuron in the
- *                     Full-Interleaved layout.  Multi-morphology plans (trees
+ *                     compartments whose components fit 16 lanes of 32
+ *                     rows or 32 lanes of 32 rows, about 1000 compartments
+ *                     at most): sixteen or thirty-two lanes per neuron in
+ *                     the Full-Interleaved layout.  Multi-morphology plans (trees
  *                     of at most 8191 compartments): every tree on as many
  *                     lanes as it needs, trees packed into workgroups of 128
  *                     lanes, the plan's layout in schedule order (element
@@ -441,7 +443,7 @@ BPS_API bps_status hines_plan_create_sched(bps_hines_plan **plan, int64_t batch,
 BPS_API int hines_plan_uses_levels(const bps_hines_plan *plan);
 /* Number of trees the plan solves on two lanes (0 for a NULL plan). */
 BPS_API int64_t hines_plan_split(const bps_hines_plan *plan);
-/* 1 if the plan solves with BPS_HINES_SEP (sixteen lanes per neuron), else 0. */
+/* 1 if the plan solves with BPS_HINES_SEP (separator schedules), else 0. */
 BPS_API int hines_plan_uses_sep(const bps_hines_plan *plan);
 
 /* The schedule BPS_HINES_SEP would give one tree (host only, no device
@@ -533,8 +535,9 @@ BPS_API bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const voi
 BPS_API size_t hines_work_bytes(const bps_hines_plan *plan, int dtype);
 
 /* Solve every neuron ([H] Algorithm 1) with the plan's schedule (one lane
- * per neuron, two lanes for split trees, sixteen lanes per neuron with
- * separators, or one wavefront per neuron).
+ * per neuron, two lanes for split trees, separator schedules (sixteen or
+ * thirty-two lanes per neuron, or every tree on its own lanes), or one
+ * wavefront per neuron).
  * u, l, d: device, solver layout, not modified.  rhs: device, solver layout,
  * right-hand side on entry, voltages V on return (as in [H]).  work: device,
  * hines_work_bytes bytes.  info: device int32[batch] indexed by the ORIGINAL

@@ -67,11 +67,12 @@ def _values(p, batch, rng):
 
 @pytest.mark.parametrize("n,batch,ld", [(1, 3, 0), (2, 17, 0), (33, 16, 0), (100, 15, 20),
                                         (200, 33, 0), (257, 100, 104), (512, 1000, 0),
-                                        (512, 4099, 4160), (530, 77, 0)])
+                                        (512, 4099, 4160), (530, 77, 0), (600, 33, 40),
+                                        (700, 130, 0), (800, 1000, 0), (960, 257, 260)])
 def test_sep_matches_oracle(n, batch, ld):
     print(f"hines sep n={n} batch={batch} ld={ld}", flush=True)
     hm = W.hines_mono(n, batch, rng=np.random.default_rng(n + 31 * batch))
-    out, info = _solve(hm, ld=ld, twice=(n == 512))
+    out, info = _solve(hm, ld=ld, twice=(n in (512, 800)))
     ref, rinfo = _oracle(hm)
     assert _cols_err(out, ref) <= 1e-10
     np.testing.assert_array_equal(info, rinfo)
@@ -128,6 +129,24 @@ def test_sep_breakdown_info():
     np.testing.assert_array_equal(info, rinfo)
     assert info[1] == 300 and info[5] == 151 and info[9] == 1 and info[20] == 1 and info[33] == 41
     ok = [s for s in range(hm.u.shape[1]) if s not in (1, 5, 9, 20, 33)]
+    assert _cols_err(out[:, ok], ref[:, ok]) <= 1e-10
+
+
+@pytest.mark.parametrize("n", [600, 1000])
+def test_sep_thirty_two_lanes_depth_first(n):
+    """Thirty-two lanes per neuron on depth-first numbered trees, a ragged
+    batch, with a breakdown in one neuron."""
+    print(f"hines sep 32 lanes dfs n={n}", flush=True)
+    rng = np.random.default_rng(n)
+    hm = _values(W.dfs_tree(n, rng), 70, rng)
+    assert bps.hines_sep_schedule(hm.parent)["lanes"] == 32
+    hm.d[n // 2, 9] = 0.0
+    hm.u[:, 9] = 0.0                      # decoupled: every pivot is d itself
+    out, info = _solve(hm)
+    ref, rinfo = _oracle(hm)
+    np.testing.assert_array_equal(info, rinfo)
+    assert info[9] == n // 2 + 1
+    ok = [s for s in range(70) if s != 9]
     assert _cols_err(out[:, ok], ref[:, ok]) <= 1e-10
 
 

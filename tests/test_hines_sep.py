@@ -29,18 +29,18 @@ def _lib_or_skip():
 
 def _replay(p, u, l, d, rhs, S):
     """The kernel's arithmetic for one neuron, lane by lane."""
-    R, ns, nc, npc, nh = S["R"], S["ns"], S["nc"], S["npc"], S["nh"]
+    R, ns, nc, npc, nh, K = S["R"], S["ns"], S["nc"], S["npc"], S["nh"], S["lanes"]
     codes, st, ct, cl, bases = S["codes"], S["septab"], S["comptab"], S["clist"], S["bases"]
     n = len(p)
-    q = np.zeros((16, R))
-    m = np.zeros((16, R))
+    q = np.zeros((K, R))
+    m = np.zeros((K, R))
     red = np.zeros((nc, 2))
     pdat = np.zeros((npc, 4))
     hbuf = np.zeros(nh + 2)
     bad = False
     with np.errstate(all="ignore"):
-        ends = np.zeros((16, 2), dtype=int)
-        for k in range(16):
+        ends = np.zeros((K, 2), dtype=int)
+        for k in range(K):
             ring = np.zeros((8, 2))
             g = P = al = ga = 0.0
             ccomp, chidx, cpidx = (int(v) for v in bases[k])
@@ -108,7 +108,7 @@ def _replay(p, u, l, d, rhs, S):
                       u[st[sc, 0]] * sx[sc] if sc >= 0 else 0.0)
         V = np.full(n, np.nan)
         V[st[:, 0]] = sx
-        for k in range(16):
+        for k in range(K):
             ring = np.zeros(8)
             sg = 0.0
             ccomp, chidx = ends[k]
@@ -164,6 +164,10 @@ def _trees():
     for n in (60, 300, 512):
         out.append((f"dfs_{n}", W.dfs_tree(n, rng)))
     out.append(("comb_reversed", _comb(100)))
+    # thirty-two lanes per neuron
+    for n in (600, 700, 1000):
+        out.append((f"window8_{n}", W.random_tree(n, rng)))
+        out.append((f"dfs_{n}", W.dfs_tree(n, rng)))
     return out
 
 
@@ -186,7 +190,7 @@ def test_sep_schedule_replay_matches_oracle(name, p):
     # every compartment exactly once: on a lane or as a separator
     assert np.array_equal(np.sort(np.r_[rows[live], seps]), np.arange(n))
     # each lane's live rows first, padding after; separators in descending order
-    for k in range(16):
+    for k in range(S["lanes"]):
         nl = int(live[k].sum())
         assert live[k, :nl].all() and not live[k, nl:].any()
     assert np.all(np.diff(seps) < 0)
@@ -210,7 +214,8 @@ def test_sep_schedule_replay_matches_oracle(name, p):
 
 def test_sep_schedule_shapes():
     """On the workloads' trees of 512: sixteen lanes of at most 32 rows, a
-    few separators, and a share of path rows."""
+    few separators, and a share of path rows; trees of 600..960: thirty-two
+    lanes of 24 rows, then of 32."""
     _lib_or_skip()
     rng = np.random.default_rng(4)
     for _ in range(10):
@@ -218,7 +223,10 @@ def test_sep_schedule_shapes():
         assert S is not None and S["R"] == 32
         assert 4 <= S["ns"] <= 40 and S["nh"] <= 200
     small = bps.hines_sep_schedule(W.random_tree(200, rng))
-    assert small is not None and small["R"] == 16
+    assert small is not None and small["R"] == 16 and small["lanes"] == 16
+    for n, R in ((600, 24), (700, 24), (960, 32)):
+        S = bps.hines_sep_schedule(W.random_tree(n, rng))
+        assert S is not None and S["lanes"] == 32 and S["R"] == R
 
 
 def test_sep_schedule_slots_beyond_window():
@@ -237,7 +245,7 @@ def test_sep_schedule_slots_beyond_window():
 def test_sep_schedule_refusals():
     _lib_or_skip()
     # a star (1499 one-compartment components, more than 255), and a tree
-    # too large for 16 x 32 rows
+    # too large for 32 x 32 rows
     star = np.array([-1] + [0] * 1499, dtype=np.int32)
     assert bps.hines_sep_schedule(star) is None
     assert "no partition" in bps.bps_last_error()
