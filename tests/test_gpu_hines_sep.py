@@ -150,6 +150,46 @@ def test_sep_thirty_two_lanes_depth_first(n):
     assert _cols_err(out[:, ok], ref[:, ok]) <= 1e-10
 
 
+def _kind_tree(kind, n, rng):
+    if kind == 0:
+        return W.random_tree(n, rng, window=int(rng.integers(1, 65)))
+    if kind == 1:
+        return W.dfs_tree(n, rng, window=int(rng.integers(1, 17)))
+    p = np.empty(n, dtype=np.int32)           # bushy: parent uniform over all before
+    p[0] = -1
+    for i in range(1, n):
+        p[i] = rng.integers(0, i)
+    return p
+
+
+def test_sep_fuzz_mono_and_multi():
+    """Seeded trees of every kind (windows 1..64, depth-first, bushy), mono
+    plans the schedule takes and one multi-morphology batch of them all,
+    against the oracle."""
+    rng = np.random.default_rng(4242)
+    done = 0
+    for it in range(12):
+        n = int(rng.integers(2, 1000))
+        p = _kind_tree(it % 3, n, rng)
+        if bps.hines_sep_schedule(p) is None:
+            continue
+        print(f"hines sep fuzz mono it={it} n={n}", flush=True)
+        hm = _values(p, 37, rng)
+        out, info = _solve(hm)
+        ref, rinfo = _oracle(hm)
+        assert _cols_err(out, ref) <= 1e-10, (it, n)
+        np.testing.assert_array_equal(info, rinfo)
+        done += 1
+    assert done >= 6
+    print("hines sep fuzz multi", flush=True)
+    trees = [_kind_tree(k % 3, int(rng.integers(1, 1500)), rng) for k in range(300)]
+    mm = W.hines_multi_trees(trees, rng)
+    out, info = _run_multi(mm)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    assert _multi_err(mm, out, ref) <= 1e-10
+    np.testing.assert_array_equal(info, rinfo)
+
+
 def test_sep_refusals_and_auto():
     rng = np.random.default_rng(3)
     # trees with parents far back are taken (ring slots per lane), also by

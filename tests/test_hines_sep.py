@@ -260,3 +260,60 @@ def test_sep_schedule_refusals():
     m = L.hines_sep_schedule(300, p.ctypes.data_as(i32p), out.ctypes.data_as(i32p), 64)
     assert m == -1 and "cap" in bps.bps_last_error()
     assert np.all(out == -5)
+
+
+def _random_recursive(n, rng, bushy):
+    """Each compartment below a uniformly chosen earlier one (bushy) or
+    below one of the last few (stringy), then renumbered depth first."""
+    p = np.empty(n, dtype=np.int32)
+    p[0] = -1
+    for i in range(1, n):
+        p[i] = rng.integers(0, i) if bushy else max(0, i - 1 - int(rng.geometric(0.5)) + 1)
+    if n > 1 and rng.random() < 0.5:
+        # depth-first renumbering of the same tree
+        kids = [[] for _ in range(n)]
+        for i in range(1, n):
+            kids[p[i]].append(i)
+        order, stack = [], [0]
+        while stack:
+            v = stack.pop()
+            order.append(v)
+            ch = kids[v][:]
+            rng.shuffle(ch)
+            stack.extend(ch)
+        new = np.empty(n, dtype=np.int64)
+        new[np.array(order)] = np.arange(n)
+        q = np.empty(n, dtype=np.int32)
+        q[0] = -1
+        q[new[1:]] = new[p[1:]]
+        p = q
+    return p
+
+
+def test_sep_schedule_fuzz():
+    """Many seeded trees of every kind (windows 1..64, depth-first, bushy
+    and stringy random recursive trees, 1..1000 compartments): every
+    schedule the library gives replays to the oracle's voltages."""
+    _lib_or_skip()
+    rng = np.random.default_rng(2024)
+    taken = 0
+    for it in range(300):
+        n = int(rng.integers(1, 1000))
+        kind = it % 4
+        if kind == 0:
+            p = W.random_tree(n, rng, window=int(rng.integers(1, 65)))
+        elif kind == 1:
+            p = W.dfs_tree(n, rng, window=int(rng.integers(1, 17)))
+        else:
+            p = _random_recursive(n, rng, bushy=(kind == 2))
+        S = bps.hines_sep_schedule(p)
+        if S is None:
+            continue
+        taken += 1
+        u, l, d, rhs = _values(p, rng)
+        V, bad = _replay(p, u, l, d, rhs, S)
+        assert not bad
+        ref, info = oracle.hines_solve(p, u, l, d, rhs)
+        err = np.linalg.norm(V - ref[0]) / np.linalg.norm(ref[0])
+        assert err <= 1e-13, (it, n, kind, err)
+    assert taken >= 200

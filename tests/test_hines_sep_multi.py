@@ -295,3 +295,34 @@ def test_sep_multi_layout_refusals():
     assert "too large" in bps.bps_last_error()
     with pytest.raises(bps.BpsError):
         bps.hines_sep_multi_layout([3], [-1, 0, 5])
+
+
+def test_sep_multi_replay_fuzz():
+    """A batch of trees of every kind (windows 1..64, depth-first, bushy
+    random recursive trees): the layout replays to the oracle's voltages."""
+    _lib_or_skip()
+    rng = np.random.default_rng(77)
+    trees = []
+    for it in range(60):
+        n = int(rng.integers(1, 1500))
+        if it % 3 == 0:
+            trees.append(W.random_tree(n, rng, window=int(rng.integers(1, 65))))
+        elif it % 3 == 1:
+            trees.append(W.dfs_tree(n, rng, window=int(rng.integers(1, 17))))
+        else:
+            p = np.empty(n, dtype=np.int32)
+            p[0] = -1
+            for i in range(1, n):
+                p[i] = rng.integers(0, i)
+            trees.append(p)
+    mm = W.hines_multi_trees(trees, rng)
+    Lo = bps.hines_sep_multi_layout(mm.sizes, mm.parent)
+    assert Lo is not None
+    _check_ranges(Lo, mm.sizes)
+    V, bad = _replay(Lo, mm.sizes, mm.u, mm.l, mm.d, mm.rhs)
+    assert not bad
+    ref, info = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    o = mm.offsets
+    err = max(np.linalg.norm(V[o[s]:o[s + 1]] - ref[o[s]:o[s + 1]]) / np.linalg.norm(ref[o[s]:o[s + 1]])
+              for s in range(mm.batch))
+    assert err <= 1e-13
