@@ -34,7 +34,7 @@ namespace bps {
 
 namespace {
 
-constexpr int kSepNeurons = 16;     // neurons per workgroup (16 or 32 lanes each)
+constexpr int kSepNeurons = 16;     // neurons per workgroup with 16 lanes each (8 with 32)
 constexpr int kSepSlots = 8;        // ring of pending updates / voltages per lane
 constexpr int kSepHeader = 8;
 
@@ -90,27 +90,40 @@ __host__ __device__ inline int sep_tab_words(int R, int ns, int nc, int lanes)
     return lanes * R + lanes * 3 + ns * 5 + nc * 4;
 }
 
-template <int R, int LANES>
-__global__ void __launch_bounds__(LANES * kSepNeurons) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Neuron group of a workgroup.  With 8 neurons per workgroup a 128-byte row
+// segment holds two groups' values; workgroups are handed to the 8 XCDs in
+// turn (block b to XCD b mod 8), so within each run of 16 blocks b and b + 8
+// take groups 2m and 2m + 1: the two halves of each segment are read by one
+// XCD's L2 at about the same time.  A last partial run keeps its order.
+template <int NEU>
+__device__ __forceinline__ int64_t sep_group(int64_t b, int64_t nblk)
+{
+    if (NEU == 16 || b >= nblk / 16 * 16) return b;
+    const int64_t r = b % 16;
+    return b - r + 2 * (r % 8) + r / 8;
+}
+
+template <int R, int LANES, int NEU>
+__global__ void __launch_bounds__(LANES * NEU) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_hines_sep(SepArgs A)
 {
-    constexpr int NT = LANES * kSepNeurons;   // threads: lane k = tid / 16 of neuron j = tid % 16
+    constexpr int NT = LANES * NEU;   // threads: lane k = tid / NEU of neuron j = tid % NEU
     extern __shared__ __align__(16) unsigned char sep_lds[];
-    const int tid = threadIdx.x, k = tid >> 4, j = tid & 15;
-    const int64_t s = int64_t(blockIdx.x) * kSepNeurons + j;
+    const int tid = threadIdx.x, k = tid / NEU, j = tid % NEU;
+    const int64_t s = sep_group<NEU>(blockIdx.x, gridDim.x) * NEU + j;
     const bool act = s < A.batch;
     // lanes past the batch shadow the last neuron (loads only)
     const uint32_t s8 = uint32_t(uint64_t(act ? s : A.batch - 1) * 8);
     const int ns = A.ns, nc = A.nc, npc = A.npc, nh = A.nh;
     double2 *ring = reinterpret_cast<double2 *>(sep_lds);     // [8][NT]
-    double2 *red = ring + kSepSlots * NT;             // [nc][16]
-    double2 *pdat = red + nc * kSepNeurons;                    // [npc][16][2]
-    double2 *sepv = pdat + npc * 2 * kSepNeurons;              // [ns][16][2]
-    double *su = reinterpret_cast<double *>(sepv + ns * 2 * kSepNeurons);   // [ns][16]
-    double *hbuf = su + ns * kSepNeurons;                      // [nh + 2][16]
-    int *badf = reinterpret_cast<int *>(hbuf + (nh + 2) * kSepNeurons);  // [NT]
-    int *flag = badf + NT;                            // [16]
-    int *tab = flag + kSepNeurons;                             // the schedule's tables
+    double2 *red = ring + kSepSlots * NT;             // [nc][NEU]
+    double2 *pdat = red + nc * NEU;                    // [npc][NEU][2]
+    double2 *sepv = pdat + npc * 2 * NEU;              // [ns][NEU][2]
+    double *su = reinterpret_cast<double *>(sepv + ns * 2 * NEU);   // [ns][NEU]
+    double *hbuf = su + ns * NEU;                      // [nh + 2][NEU]
+    int *badf = reinterpret_cast<int *>(hbuf + (nh + 2) * NEU);  // [NT]
+    int *flag = badf + NT;                            // [NEU]
+    int *tab = flag + NEU;                             // the schedule's tables
     const int *codes = tab, *bases = tab + LANES * R, *septab = bases + LANES * 3;
     const int *comptab = septab + ns * 5, *clist = comptab + nc * 3;
 
@@ -120,14 +133,14 @@ k_hines_sep(SepArgs A)
     for (int i = tid; i < ntab; i += NT) tab[i] = A.tab[i];
 #pragma unroll
     for (int q = 0; q < kSepSlots; ++q) ring[q * NT + tid] = make_double2(0.0, 0.0);
-    if (k == 0) hbuf[nh * kSepNeurons + j] = 0.0;              // read by rows off the paths
+    if (k == 0) hbuf[nh * NEU + j] = 0.0;              // read by rows off the paths
     // the separators' own rows
     for (int i = k; i < ns; i += LANES) {
         const uint32_t o = uint32_t(A.tab[LANES * R + LANES * 3 + i * 5]) * ld8 + s8;
         const double uu = U.ld(o), ll = L.ld(o), dd = Dg.ld(o), rr = Rh.ld(o);
-        su[i * kSepNeurons + j] = uu;
-        sepv[(i * kSepNeurons + j) * 2] = make_double2(dd, rr);
-        sepv[(i * kSepNeurons + j) * 2 + 1] = make_double2(ll, uu);
+        su[i * NEU + j] = uu;
+        sepv[(i * NEU + j) * 2] = make_double2(dd, rr);
+        sepv[(i * NEU + j) * 2 + 1] = make_double2(ll, uu);
     }
     __syncthreads();
 
@@ -164,7 +177,7 @@ k_hines_sep(SepArgs A)
         m[t] = mm;
         if (w0 & kSepPath0) { g = 1.0; P = 1.0; al = 0.0; ga = 0.0; }
         const double h = g * rcp;
-        hbuf[(path ? chidx : nh + 1) * kSepNeurons + j] = h;
+        hbuf[(path ? chidx : nh + 1) * NEU + j] = h;
         if (path) {
             ++chidx;
             al = fma(P, qq, al);
@@ -174,11 +187,11 @@ k_hines_sep(SepArgs A)
         }
         const double2 cb = make_double2(fac * l_, fac * rr);
         if (top) {
-            red[ccomp * kSepNeurons + j] = cb;
+            red[ccomp * NEU + j] = cb;
             ++ccomp;
             if (path) {
-                pdat[(cpidx * kSepNeurons + j) * 2] = make_double2(g, al);
-                pdat[(cpidx * kSepNeurons + j) * 2 + 1] = make_double2(P, ga);
+                pdat[(cpidx * NEU + j) * 2] = make_double2(g, al);
+                pdat[(cpidx * NEU + j) * 2 + 1] = make_double2(P, ga);
                 ++cpidx;
             }
         } else {
@@ -195,11 +208,11 @@ k_hines_sep(SepArgs A)
     for (int i = k; i < ns; i += LANES) {
         const int rp = septab[i * 5 + 1], pcomp = septab[i * 5 + 2];
         const int cb = septab[i * 5 + 3], ce = septab[i * 5 + 4];
-        const double2 dr = sepv[(i * kSepNeurons + j) * 2];
-        const double2 lu = sepv[(i * kSepNeurons + j) * 2 + 1];
+        const double2 dr = sepv[(i * NEU + j) * 2];
+        const double2 lu = sepv[(i * NEU + j) * 2 + 1];
         double dh = dr.x, rh = dr.y, lh = 0.0, uh = 0.0;
         for (int c = cb; c < ce; ++c) {
-            const double2 v = red[clist[c] * kSepNeurons + j];
+            const double2 v = red[clist[c] * NEU + j];
             dh -= v.x;
             rh -= v.y;
         }
@@ -207,8 +220,8 @@ k_hines_sep(SepArgs A)
             // the separator meets its parent component through the path: the
             // parent compartment's voltage is al + P x_top + ga (u x_sep)
             const int pi = comptab[pcomp * 3 + 2];
-            const double2 a = pdat[(pi * kSepNeurons + j) * 2];
-            const double2 b = pdat[(pi * kSepNeurons + j) * 2 + 1];
+            const double2 a = pdat[(pi * NEU + j) * 2];
+            const double2 b = pdat[(pi * NEU + j) * 2 + 1];
             dh = fma(lu.x * lu.y, b.y, dh);
             rh = fma(-lu.x, a.y, rh);
             lh = lu.x * b.x;
@@ -217,8 +230,8 @@ k_hines_sep(SepArgs A)
             lh = lu.x;
             uh = lu.y;
         }
-        sepv[(i * kSepNeurons + j) * 2] = make_double2(dh, rh);
-        sepv[(i * kSepNeurons + j) * 2 + 1] = make_double2(lh, uh);
+        sepv[(i * NEU + j) * 2] = make_double2(dh, rh);
+        sepv[(i * NEU + j) * 2 + 1] = make_double2(lh, uh);
     }
     __syncthreads();
     // (b) Algorithm 1 on the separators (one lane per neuron), in place
@@ -227,13 +240,13 @@ k_hines_sep(SepArgs A)
         // the CU run their sweeps: it takes the issue slots first
         __builtin_amdgcn_s_setprio(3);
         int anyb = 0;
-        for (int kk = 0; kk < LANES; ++kk) anyb |= badf[kk * kSepNeurons + j];
+        for (int kk = 0; kk < LANES; ++kk) anyb |= badf[kk * NEU + j];
         // the next separator's row is read one step ahead (two register sets
         // in turn); an update for the next separator is carried in registers,
         // others go through LDS (they reach two or more rows ahead, which
         // have not been read yet)
         double cf = 0.0, cl = 0.0, cr = 0.0;
-        auto at = [&](int i) { return (i * kSepNeurons + j) * 2; };
+        auto at = [&](int i) { return (i * NEU + j) * 2; };
         auto rd = [&](int i, double2 &a, double2 &b, int &r) {
             const int ii = i < ns ? i : ns - 1;
             a = sepv[at(ii)];
@@ -299,9 +312,9 @@ k_hines_sep(SepArgs A)
     // (c) each component's parent voltage and u x of its lower separator
     for (int c = k; c < nc; c += LANES) {
         const int pc = comptab[c * 3], sc = comptab[c * 3 + 1];
-        const double xp = pc >= 0 ? sepv[(pc * kSepNeurons + j) * 2].x : 0.0;
-        const double sg = sc >= 0 ? su[sc * kSepNeurons + j] * sepv[(sc * kSepNeurons + j) * 2].x : 0.0;
-        red[c * kSepNeurons + j] = make_double2(xp, sg);
+        const double xp = pc >= 0 ? sepv[(pc * NEU + j) * 2].x : 0.0;
+        const double sg = sc >= 0 ? su[sc * NEU + j] * sepv[(sc * NEU + j) * 2].x : 0.0;
+        red[c * NEU + j] = make_double2(xp, sg);
     }
     __syncthreads();
 
@@ -309,7 +322,7 @@ k_hines_sep(SepArgs A)
     const bool ok = flag[j] == 0;
     const SepBuf V(A.rhs, act && ok ? A.bytes : 0u);
     for (int i = k; i < ns; i += LANES)
-        V.st(sepv[(i * kSepNeurons + j) * 2].x, uint32_t(septab[i * 5]) * ld8 + s8);
+        V.st(sepv[(i * NEU + j) * 2].x, uint32_t(septab[i * 5]) * ld8 + s8);
     double sg = 0.0;
 #pragma unroll
     for (int t = R - 1; t >= 0; --t) {
@@ -318,9 +331,9 @@ k_hines_sep(SepArgs A)
         const int own = (w0 >> 11) & 7, par = (w0 >> 14) & 7;
         if (top) --ccomp;
         if (path) --chidx;
-        const double2 v = top ? red[ccomp * kSepNeurons + j] : ring[par * NT + tid];
+        const double2 v = top ? red[ccomp * NEU + j] : ring[par * NT + tid];
         sg = top ? v.y : sg;
-        const double h = hbuf[(path ? chidx : nh) * kSepNeurons + j];
+        const double h = hbuf[(path ? chidx : nh) * NEU + j];
         const double x = q[t] - m[t] * v.x - h * sg;
         reinterpret_cast<double *>(ring)[(own * NT + tid) * 2] = x;
         V.st(x, (w0 & kSepLive) ? uint32_t(w0 & 2047) * ld8 + s8 : kSepNoStore);
@@ -960,6 +973,7 @@ std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
         std::vector<int32_t> blob(kSepHeader + sep_tab_words(R, ns, nc, lanes), 0);
         blob[0] = R; blob[1] = ns; blob[2] = nc; blob[3] = T.npc; blob[4] = T.nh; blob[5] = n;
         blob[6] = lanes;
+        blob[7] = lanes == 32 ? 8 : kSepNeurons;     // neurons per workgroup
         int32_t *codes = blob.data() + kSepHeader;
         for (int l = 0; l < lanes; ++l) {
             int t = 0;
@@ -1200,18 +1214,17 @@ bps_status launch_hines_sepm(const SepMultiDev &S, const int32_t *parent_dev, co
 size_t sep_lds_bytes(const int32_t *blob)
 {
     const size_t R = size_t(blob[0]), ns = size_t(blob[1]), nc = size_t(blob[2]);
-    const size_t npc = size_t(blob[3]), nh = size_t(blob[4]), nt = size_t(blob[6]) * kSepNeurons;
-    return size_t(kSepSlots) * nt * 16 + nc * kSepNeurons * 16 + npc * kSepNeurons * 32 +
-           ns * kSepNeurons * 32 + ns * kSepNeurons * 8 + (nh + 2) * kSepNeurons * 8 +
-           size_t(nt + kSepNeurons) * 4 + size_t(sep_tab_words(int(R), int(ns), int(nc), blob[6])) * 4;
+    const size_t npc = size_t(blob[3]), nh = size_t(blob[4]), neu = size_t(blob[7]), nt = size_t(blob[6]) * neu;
+    return size_t(kSepSlots) * nt * 16 + nc * neu * 16 + npc * neu * 32 + ns * neu * 32 + ns * neu * 8 +
+           (nh + 2) * neu * 8 + size_t(nt + neu) * 4 + size_t(sep_tab_words(int(R), int(ns), int(nc), blob[6])) * 4;
 }
 
 hipError_t sep_prepare_device()
 {
-    for (const void *f : {reinterpret_cast<const void *>(&k_hines_sep<16, 16>),
-                          reinterpret_cast<const void *>(&k_hines_sep<32, 16>),
-                          reinterpret_cast<const void *>(&k_hines_sep<24, 32>),
-                          reinterpret_cast<const void *>(&k_hines_sep<32, 32>)}) {
+    for (const void *f : {reinterpret_cast<const void *>(&k_hines_sep<16, 16, 16>),
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 16, 16>),
+                          reinterpret_cast<const void *>(&k_hines_sep<24, 32, 8>),
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 32, 8>)}) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
     }
@@ -1235,12 +1248,12 @@ bps_status launch_hines_sep(const int32_t *blob_host, const int32_t *blob_dev, i
     A.u = (const double *)u; A.l = (const double *)l; A.d = (const double *)d;
     A.rhs = (double *)rhs; A.work = (double *)work; A.info = info;
     const size_t lds = sep_lds_bytes(blob_host);
-    const int lanes = blob_host[6];
-    const dim3 grid(unsigned((batch + kSepNeurons - 1) / kSepNeurons)), block(unsigned(lanes * kSepNeurons));
-    if (lanes == 32 && R == 24) hipLaunchKernelGGL((k_hines_sep<24, 32>), grid, block, lds, st, A);
-    else if (lanes == 32) hipLaunchKernelGGL((k_hines_sep<32, 32>), grid, block, lds, st, A);
-    else if (R == 16) hipLaunchKernelGGL((k_hines_sep<16, 16>), grid, block, lds, st, A);
-    else hipLaunchKernelGGL((k_hines_sep<32, 16>), grid, block, lds, st, A);
+    const int lanes = blob_host[6], neu = blob_host[7];
+    const dim3 grid(unsigned((batch + neu - 1) / neu)), block(unsigned(lanes * neu));
+    if (lanes == 32 && R == 24) hipLaunchKernelGGL((k_hines_sep<24, 32, 8>), grid, block, lds, st, A);
+    else if (lanes == 32) hipLaunchKernelGGL((k_hines_sep<32, 32, 8>), grid, block, lds, st, A);
+    else if (R == 16) hipLaunchKernelGGL((k_hines_sep<16, 16, 16>), grid, block, lds, st, A);
+    else hipLaunchKernelGGL((k_hines_sep<32, 16, 16>), grid, block, lds, st, A);
     BPS_LAUNCHED("k_hines_sep");
     return BPS_OK;
 }

@@ -450,13 +450,14 @@ BPS_API int hines_plan_uses_sep(const bps_hines_plan *plan);
  * needed; for inspection and host-side tests), as int32 words:
  *   [0] R rows per lane, [1] ns separators, [2] nc components, [3] npc
  *   components with a separator below, [4] nh compartments on those
- *   components' paths, [5] n, [6] 16 lanes, [7] 0;
- *   then codes [16][R]: lane k's step t of the first sweep (the second
+ *   components' paths, [5] n, [6] lanes per neuron (16 or 32), [7]
+ *   neurons per workgroup (16, or 8 with 32 lanes);
+ *   then codes [lanes][R]: lane k's step t of the first sweep (the second
  *   takes the steps in reverse): bits 0-10 the compartment, 11-13 its slot
  *   in the lane's ring of pending updates and voltages, 14-16 its parent's
  *   slot, 17 live (else padding), 18 on a path, 19 first row of a path, 20
  *   root of its component;
- *   then [16][3] per lane the numbers of its first component, first path
+ *   then [lanes][3] per lane the numbers of its first component, first path
  *   row and first component with a path (each numbered in the order the
  *   lanes visit them, lane by lane);
  *   then ns x 5 words per separator (in descending compartment order): the
