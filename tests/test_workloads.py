@@ -92,4 +92,4 @@ def test_dfs_tree_is_a_preorder_of_the_drawn_tree():
     for i in range(1, 300):
         acc[hm.parent[i]] += np.abs(hm.u[i])
     assert np.all(hm.d - acc >= 1.0)
-    assert W.WORKLOADS[11]["dfs"] and W.WORKLOADS[12]["dfs"]
+    assert W.WORKLOADS[11]["dfs"] and W.WORKLOADS[12]["dfs"] and W.WORKLOADS[13]["n"] == 960

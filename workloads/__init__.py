@@ -420,4 +420,7 @@ WORKLOADS = {
     11: dict(name="hines_mono_dfs_n512_b100000", kind="hines_mono", n=512, batch=100000, dfs=True),
     12: dict(name="hines_multi_dfs_b32768_n256to2048_20steps", kind="hines_multi",
              batch=32768, nmin=256, nmax=2048, nsteps=20, dfs=True),
+    # a larger shared tree, about as many compartments as workload 3: the
+    # thirty-two-lane separator schedule
+    13: dict(name="hines_mono_n960_b53328", kind="hines_mono", n=960, batch=53328),
 }
