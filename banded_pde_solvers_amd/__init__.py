@@ -446,7 +446,7 @@ class HinesPlan:
 
     @property
     def uses_sep(self) -> bool:
-        """True when the plan solves with BPS_HINES_SEP (sixteen lanes per neuron)."""
+        """True when the plan solves with BPS_HINES_SEP (separator schedules)."""
         return bool(load_library().hines_plan_uses_sep(self.handle))
 
     def close(self):

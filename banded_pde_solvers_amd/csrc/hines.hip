@@ -67,7 +67,7 @@ struct bps_hines_plan {
     int32_t *lv_spar = nullptr;    // per tree: parent (new index) of each section head, -1 root
     int32_t *lv_lev = nullptr;     // per tree: section ranges per level, nlev + 1 entries
     int64_t *lv_tree = nullptr;    // per tree: perm base, sec base, lev base, nlev, n, data base
-    // sixteen lanes per neuron (mono, k_hines_sep): the schedule, on the
+    // separator schedule of a shared tree (mono, k_hines_sep): on the
     // host and on the device, when the plan uses it
     std::vector<int32_t> sep;
     int32_t *sep_dev = nullptr;
@@ -1325,7 +1325,7 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         h[0] = 0;   // never read; keep it a valid index
         for (int64_t i = 1; i < n; ++i) P->max_dist = std::max<int32_t>(P->max_dist, int32_t(i - h[i]));
         st = upload(&P->parent, h);
-        // sixteen lanes per neuron: when asked for, and by default for trees
+        // separator schedules: when asked for, and by default for trees
         // it takes, unless small trees in a batch large enough to fill the
         // GPU with one lane per neuron (measured: 128 compartments, 16384
         // neurons 39.8 vs 47.2 us, 32768 neurons 63.4 vs 53.5 us; 256 and

@@ -1,6 +1,7 @@
 // hines_sep.hip -- Hines systems of one shared morphology, each neuron
-// solved by sixteen lanes ([H] section 2, Algorithm 1, and the per-branch
-// decomposition of section 4).
+// solved by sixteen or thirty-two lanes, and multi-morphology batches with
+// every tree on its own lanes ([H] section 2, Algorithm 1, and the
+// per-branch decomposition of section 4).
 //
 // A set S of single compartments ("separators") cuts the tree into
 // components, each with at most one separator below it.  Given the voltages
@@ -16,9 +17,12 @@
 // kernel reads u, l, d, rhs and writes V once: 40 bytes, where one lane per
 // neuron also writes and reads q, m.
 //
-// Workgroup: 16 neurons x 16 lanes.  Thread (k, j) = lane k of neuron j;
-// a wavefront holds 4 lanes of 16 neighbouring neurons, so every access is
-// four 128-byte row segments of the interleaved layout.
+// Workgroup: 16 neurons x 16 lanes, or 8 neurons x 32 lanes.  Thread
+// (k, j) = lane k of neuron j; a wavefront holds 4 lanes of 16 neighbouring
+// neurons (every access four 128-byte row segments of the interleaved
+// layout) or 8 lanes of 8 (eight 64-byte halves, the other halves read by a
+// workgroup on the same XCD).  A lane keeps its compartments' pending
+// updates and voltages in 8 ring slots that the schedule assigns.
 #include <algorithm>
 #include <cstring>
 #include <string>
@@ -52,7 +56,7 @@ struct SepArgs {
     uint32_t ld8;       // ld * 8
     uint32_t bytes;     // n * ld * 8
     int32_t n, ns, nc, npc, nh;
-    const int32_t *tab;         // codes [16][R], bases [16][3], separators [ns][5],
+    const int32_t *tab;         // codes [lanes][R], bases [lanes][3], separators [ns][5],
                                 // components [nc][3], component list [nc]
     const int32_t *parent;      // [n] for Algorithm 1 on a neuron that breaks down
     const double *u, *l, *d;
