@@ -69,6 +69,7 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
 bps_status hines_plan_free(bps_hines_plan *p);
 bool hines_plan_general(const bps_hines_plan *p);
 bool hines_plan_levels(const bps_hines_plan *p);
+size_t hines_plan_work_bytes(const bps_hines_plan *p);
 template <typename T>
 bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, void *dst,
                            hipStream_t st);
@@ -721,7 +722,7 @@ bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const void *packe
 size_t hines_work_bytes(const bps_hines_plan *plan, int dtype)
 {
     if (!plan || dtype != BPS_F64) return 0;
-    return size_t(hines_plan_elems_of(plan)) * 8 * (hines_plan_general(plan) ? 3 : 1);
+    return hines_plan_work_bytes(plan);
 }
 
 bps_status hines_solve_batch(const bps_hines_plan *plan, int dtype, const void *u, const void *l,

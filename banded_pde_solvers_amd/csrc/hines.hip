@@ -77,6 +77,11 @@ struct bps_hines_plan {
     bool use_sepm = false;
     bps::SepMultiDev sepm;
     int32_t *flat_parent = nullptr;
+    // trees the separator schedules do not take (too large for one
+    // workgroup), in a plan of their own (one lane per tree, original tree
+    // numbers and flat offsets) whose elements follow the separators' ones
+    int64_t sep_elems = 0;
+    bps_hines_plan *rest = nullptr;
 };
 
 namespace bps {
@@ -932,6 +937,7 @@ static void free_plan(bps_hines_plan *p)
     (void)hipFree(const_cast<int32_t *>(p->sepm.lanetab)); (void)hipFree(const_cast<int32_t *>(p->sepm.tabs));
     (void)hipFree(const_cast<int32_t *>(p->sepm.pos)); (void)hipFree(const_cast<int64_t *>(p->sepm.wgoff));
     (void)hipFree(p->flat_parent);
+    free_plan(p->rest);
     delete p;
 }
 
@@ -1293,6 +1299,41 @@ static bps_status build_split(bps_hines_plan *P, int64_t batch, const int32_t *s
 }
 
 bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,
+                            const int32_t *parent, int mono, int64_t ld, int sched);
+
+// The trees a multi-morphology separator plan leaves out (skip): a one-lane
+// plan of their own, retargeted to the original tree numbers (lane_src) and
+// flat offsets (src_off), so that its kernels and layout transform address
+// the caller's arrays and info directly; its elements follow P's.
+static bps_status build_rest(bps_hines_plan *P, int64_t batch, const int32_t *sizes, const int32_t *parent,
+                             const std::vector<int64_t> &off, const std::vector<char> &skip)
+{
+    std::vector<int32_t> ids, sz, par;
+    for (int64_t s = 0; s < int64_t(skip.size()); ++s)
+        if (skip[size_t(s)]) {
+            ids.push_back(int32_t(s));
+            sz.push_back(sizes[s]);
+            par.insert(par.end(), parent + off[s], parent + off[s] + sizes[s]);
+        }
+    if (ids.empty()) return BPS_OK;
+    bps_hines_plan *R = nullptr;
+    bps_status st = hines_plan_build(&R, int64_t(ids.size()), sz.data(), par.data(), 0, 0, BPS_HINES_LANES);
+    if (st != BPS_OK) return st;
+    P->rest = R;
+    std::vector<int32_t> ls(size_t(R->nblocks) * kWave);
+    if (hipMemcpy(ls.data(), R->lane_src, ls.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        BPS_FAIL(BPS_EHIP, "hines plan: reading the lanes of the trees left out");
+    for (int32_t &v : ls)
+        if (v >= 0) v = ids[size_t(v)];
+    (void)hipFree(R->lane_src); R->lane_src = nullptr;
+    (void)hipFree(R->src_off); R->src_off = nullptr;
+    if ((st = upload(&R->lane_src, ls)) != BPS_OK || (st = upload(&R->src_off, off)) != BPS_OK) return st;
+    P->elems = P->sep_elems + R->elems;
+    (void)batch;
+    return BPS_OK;
+}
+
+bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *sizes,
                             const int32_t *parent, int mono, int64_t ld, int sched)
 {
     auto *P = new bps_hines_plan();
@@ -1360,8 +1401,9 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         const bool sep_auto = sched == BPS_HINES_AUTO && off[batch] >= 128 * batch;
         SepMulti M;
         std::string why;
+        std::vector<char> skip;
         const bool sep_ok = (sched == BPS_HINES_SEP || sep_auto) &&
-                            sep_build_multi(batch, sizes, parent, off.data(), M, why);
+                            sep_build_multi(batch, sizes, parent, off.data(), M, why, sep_auto ? &skip : nullptr);
         if (sched == BPS_HINES_SEP && !sep_ok) {
             free_plan(P);
             BPS_FAIL(BPS_ENOTSUP, "BPS_HINES_SEP: %s", why.c_str());
@@ -1381,6 +1423,8 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
             P->sepm.nwg = M.nwg; P->sepm.elems = M.elems; P->sepm.lds = M.lds;
             P->sepm.code = P->code16; P->sepm.lanetab = lt; P->sepm.tabs = tb; P->sepm.pos = ps;
             P->sepm.wgoff = wo;
+            P->sep_elems = M.elems;
+            if (st == BPS_OK) st = build_rest(P, batch, sizes, parent, off, skip);
             if (st != BPS_OK) { free_plan(P); return st; }
             *out = P;
             return BPS_OK;
@@ -1481,6 +1525,12 @@ bool hines_plan_general(const bps_hines_plan *p)
     return !p->sep_dev && !p->use_sepm && p->max_dist > kRing;
 }
 bool hines_plan_levels(const bps_hines_plan *p) { return p->use_levels; }
+size_t hines_plan_work_bytes(const bps_hines_plan *p)
+{
+    if (p->use_sepm)
+        return size_t(p->sep_elems) * 8 + (p->rest ? hines_plan_work_bytes(p->rest) : 0);
+    return size_t(p->elems) * 8 * (hines_plan_general(p) ? 3 : 1);
+}
 bool hines_plan_sep(const bps_hines_plan *p) { return p->sep_dev != nullptr || p->use_sepm; }
 int64_t hines_plan_elems_of(const bps_hines_plan *p) { return p->elems; }
 int64_t hines_plan_unknowns_of(const bps_hines_plan *p) { return p->unknowns; }
@@ -1514,8 +1564,11 @@ bps_status hines_transform(const bps_hines_plan *P, bool pack, const void *src, 
                            hipStream_t st)
 {
     if (P->use_sepm) {
-        BPS_HIP(sepm_pack(pack, sizeof(T) == 8, P->comp, P->elems, src, dst, st));
-        return BPS_OK;
+        BPS_HIP(sepm_pack(pack, sizeof(T) == 8, P->comp, P->sep_elems, src, dst, st));
+        if (!P->rest) return BPS_OK;
+        // the trees left out: their own transform, after the separators' elements
+        return pack ? hines_transform<T>(P->rest, true, src, static_cast<T *>(dst) + P->sep_elems, st)
+                    : hines_transform<T>(P->rest, false, static_cast<const T *>(src) + P->sep_elems, dst, st);
     }
     if (P->mono) {
         const int64_t total = P->n * (pack ? P->ld : P->batch);
@@ -1566,8 +1619,15 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
         BPS_LAUNCHED("k_hines_levels");
         return BPS_OK;
     }
-    if (P->use_sepm)
-        return launch_hines_sepm(P->sepm, P->flat_parent, P->src_off, u, l, d, rhs, work, info, st);
+    if (P->use_sepm) {
+        const bps_status s0 = launch_hines_sepm(P->sepm, P->flat_parent, P->src_off, u, l, d, rhs, work, info, st);
+        if (s0 != BPS_OK || !P->rest) return s0;
+        // the trees left out, on their own elements and work
+        const int64_t e = P->sep_elems;
+        return hines_launch(P->rest, static_cast<const double *>(u) + e, static_cast<const double *>(l) + e,
+                            static_cast<const double *>(d) + e, static_cast<double *>(rhs) + e,
+                            static_cast<unsigned char *>(work) + size_t(e) * 8, info, st);
+    }
     if (P->sep_dev)
         return launch_hines_sep(P->sep.data(), P->sep_dev, P->batch, P->ld, P->parent, u, l, d, rhs,
                                 work, info, st);

@@ -1032,7 +1032,7 @@ static size_t sepm_tree_lds(const SepTree &T)
 static size_t sepm_fixed_lds() { return size_t(kSepSlots) * kMThreads * 16 + 16 + kMThreads * 4 + 8 + 16 + 4; }
 
 bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent, const int64_t *off,
-                     SepMulti &M, std::string &why)
+                     SepMulti &M, std::string &why, std::vector<char> *skip)
 {
     const int R = kSepMR;
     std::vector<SepTree> tr(static_cast<size_t>(batch));
@@ -1051,16 +1051,26 @@ bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent,
             }
         });
     for (auto &t : th) t.join();
-    for (int64_t s = 0; s < batch; ++s)
-        if (fail[s]) {
+    // a tree that does not fit fails the batch, or with `skip` is left out
+    // (marked) for the caller to solve otherwise
+    int64_t nfit = 0;
+    if (skip) skip->assign(size_t(batch), 0);
+    for (int64_t s = 0; s < batch; ++s) {
+        if (!fail[s]) { ++nfit; continue; }
+        if (!skip) {
             why = "a tree too large for 128 lanes of 32 rows";
             return false;
         }
+        (*skip)[size_t(s)] = 1;
+    }
+    if (nfit == 0) { why = "no tree fits 128 lanes of 32 rows"; return false; }
     // best fit, largest first: each tree into the workgroup with the fewest
     // free lanes that still holds it (and its LDS), workgroups bucketed by
     // free lanes
-    std::vector<int64_t> order(static_cast<size_t>(batch));
-    for (int64_t s = 0; s < batch; ++s) order[s] = s;
+    std::vector<int64_t> order;
+    order.reserve(size_t(nfit));
+    for (int64_t s = 0; s < batch; ++s)
+        if (!fail[s]) order.push_back(s);
     std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) { return tr[a].L > tr[b].L; });
     struct Bin { int lanes = 0; size_t lds = 0; std::vector<int64_t> trees; };
     std::vector<Bin> bins;

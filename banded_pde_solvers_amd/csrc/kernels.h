@@ -110,8 +110,10 @@ struct SepMultiDev {
     const int32_t *lanetab = nullptr, *tabs = nullptr, *pos = nullptr;
     const int64_t *wgoff = nullptr;
 };
+// With skip, trees that do not fit are marked there and left out (the
+// schedule holds the others); without, such a tree fails the batch.
 bool sep_build_multi(int64_t batch, const int32_t *sizes, const int32_t *parent, const int64_t *off,
-                     SepMulti &M, std::string &why);
+                     SepMulti &M, std::string &why, std::vector<char> *skip = nullptr);
 hipError_t sepm_pack(bool pack, bool f64, const int32_t *gcomp, int64_t elems, const void *src, void *dst,
                      hipStream_t st);
 bps_status launch_hines_sepm(const SepMultiDev &S, const int32_t *parent_dev, const int64_t *src_off,

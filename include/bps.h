@@ -416,7 +416,11 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *   BPS_HINES_AUTO    SEP for trees it takes: mono plans whose tree has at
  *                     least 256 compartments or whose batch has at most
  *                     2^21 compartments in all; multi-morphology plans whose
- *                     trees average at least 128 compartments.  Otherwise:
+ *                     trees average at least 128 compartments (trees too
+ *                     large for one workgroup of SEP's layout, if any, are
+ *                     solved one lane each, their elements after the
+ *                     others'; asked for explicitly, SEP takes every tree
+ *                     or gives BPS_ENOTSUP).  Otherwise:
  *                     LEVELS for batches whose trees fit and that hold at
  *                     most 786432 compartments in all (mono) or 393216
  *                     (multi-morphology), else LANES; when one lane per

@@ -355,6 +355,36 @@ def test_sep_multi_far_parents():
     np.testing.assert_array_equal(info, rinfo)
 
 
+def test_sep_multi_hybrid_trees_too_large():
+    """A batch whose few trees do not fit a workgroup (6000 and 9000
+    compartments, one of 5000 numbered depth first): the automatic choice
+    keeps the others on separator schedules and solves those on one lane
+    each (after the separators' elements of the layout); pack, solve,
+    unpack and info against the oracle, with a breakdown in a large tree and
+    in a separator-scheduled one."""
+    print("hines sep multi: hybrid with trees too large for a workgroup", flush=True)
+    rng = np.random.default_rng(77)
+    trees = [W.dfs_tree(int(n), rng) for n in rng.integers(256, 2049, size=300)]
+    trees[17] = W.random_tree(6000, rng)
+    trees[150] = W.random_tree(9000, rng)
+    trees[299] = W.dfs_tree(5000, rng)
+    mm = W.hines_multi_trees(trees, rng)
+    o = mm.offsets
+    for s_, i_ in ((150, 4000), (40, 100)):       # zero pivots, the tree's rows decoupled
+        mm.u[o[s_]:o[s_ + 1]] = 0.0
+        mm.d[o[s_] + i_] = 0.0
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
+    assert plan.uses_sep and plan.elems > 0
+    plan.close()
+    out, info = _run_multi(mm, schedule=bps.BPS_HINES_AUTO, twice=True)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    np.testing.assert_array_equal(info, rinfo)
+    assert info[150] == 4001 and info[40] == 101
+    assert _multi_err(mm, out, ref, skip=(150, 40)) <= 1e-10
+    with pytest.raises(bps.BpsError):                 # asked for explicitly: all trees or none
+        bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=SEP)
+
+
 def test_sep_multi_auto_choice():
     """The automatic choice for multi-morphology batches: separator schedules
     when the trees average at least 128 compartments (wherever their parents
