@@ -1367,13 +1367,15 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         for (int64_t i = 1; i < n; ++i) P->max_dist = std::max<int32_t>(P->max_dist, int32_t(i - h[i]));
         st = upload(&P->parent, h);
         // separator schedules: when asked for, and by default for trees
-        // it takes, unless small trees in a batch large enough to fill the
-        // GPU with one lane per neuron (measured: 128 compartments, 16384
-        // neurons 39.8 vs 47.2 us, 32768 neurons 63.4 vs 53.5 us; 256 and
-        // above faster at every batch, e.g. 512 x 65536 346 vs 437 us and
-        // 512 x 256 29.8 us against 79.7 with levels)
+        // it takes, unless small trees with parents within 16 in a batch
+        // large enough to fill the GPU with one lane per neuron (measured:
+        // 128 compartments, 16384 neurons 39.8 vs 47.2 us, 32768 neurons 63.4
+        // vs 53.5 us; 256 and above faster at every batch, e.g. 512 x 65536
+        // 346 vs 437 us and 512 x 256 29.8 us against 79.7 with levels;
+        // parents further back leave the others the general variant)
         const bool sep_try = sched == BPS_HINES_SEP ||
-                             (sched == BPS_HINES_AUTO && (n >= 256 || n * batch <= (int64_t(1) << 21)));
+                             (sched == BPS_HINES_AUTO && (n >= 256 || n * batch <= (int64_t(1) << 21) ||
+                                                          P->max_dist > kRing));
         if (st == BPS_OK && sep_try) {
             std::string why;
             if (n > 2047 || n * ld * 8 > int64_t(0xFFFF0000u))
@@ -1393,12 +1395,19 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
         std::vector<int64_t> off(batch + 1, 0);
         for (int64_t s = 0; s < batch; ++s) off[s + 1] = off[s] + sizes[s];
         P->unknowns = off[batch];
-        // separator schedules: when asked for, and by default for batches
-        // whose trees average at least 128 compartments (measured: trees of
-        // 256..2048, 64 of them 44 us vs 270 with levels, 32768 451 vs 613 on
-        // two lanes; 512 x 32768 205 vs 230 on one lane; trees of 1..100 and
-        // 30..60 within 30% either way, in favour of the others)
-        const bool sep_auto = sched == BPS_HINES_AUTO && off[batch] >= 128 * batch;
+        // separator schedules: when asked for, and by default unless the
+        // trees average under 128 compartments, lie within 16 of their
+        // parents and are enough for one lane per tree to fill every SIMD
+        // (measured, us per solve, separators / the other choice: 70000
+        // trees of 30..60 56 / 37 on one lane; depth-first numbered, whose
+        // one-lane kernel is the general one, 56 / 106; 5000 of 1..100 24 / 37
+        // with levels; 20000 of 60..190 36 / 51 on two lanes; 64 of 256..2048
+        // 44 / 270 with levels; 32768 of 256..2048 0.38 / 0.61 ms two lanes)
+        int32_t dfar = 0;
+        for (int64_t s = 0; s < batch && dfar <= kRing; ++s)
+            for (int32_t i = 1; i < sizes[s]; ++i) dfar = std::max(dfar, i - parent[off[s] + i]);
+        const bool fills = (batch + kWave - 1) / kWave >= kSimds;
+        const bool sep_auto = sched == BPS_HINES_AUTO && (off[batch] >= 128 * batch || dfar > kRing || !fills);
         SepMulti M;
         std::string why;
         std::vector<char> skip;

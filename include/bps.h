@@ -414,12 +414,15 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     in LDS; for batches too small to fill the GPU with one
  *                     lane per neuron.  Trees of at most 4096 compartments;
  *   BPS_HINES_AUTO    SEP for trees it takes: mono plans whose tree has at
- *                     least 256 compartments or whose batch has at most
- *                     2^21 compartments in all; multi-morphology plans whose
- *                     trees average at least 128 compartments (trees too
+ *                     least 256 compartments, or a parent more than 16
+ *                     compartments back, or whose batch has at most 2^21
+ *                     compartments in all; multi-morphology plans unless
+ *                     the trees average under 128 compartments, have all
+ *                     their parents within 16 and fill the GPU with one
+ *                     lane each (at least 1024 blocks of 64); trees too
  *                     large for one workgroup of SEP's layout, if any, are
  *                     solved one lane each, their elements after the
- *                     others'; asked for explicitly, SEP takes every tree
+ *                     others' (asked for explicitly, SEP takes every tree
  *                     or gives BPS_ENOTSUP).  Otherwise:
  *                     LEVELS for batches whose trees fit and that hold at
  *                     most 786432 compartments in all (mono) or 393216

@@ -246,20 +246,18 @@ def test_multi_split_matches_oracle(batch, nmin, nmax):
 
 
 def test_multi_split_auto_choice():
-    """The automatic choice puts trees on two lanes, largest first, while one
-    lane per neuron leaves SIMDs without a wavefront (fewer than 1024 blocks
-    of 64), and none when the blocks fill them."""
-    print("hines multi split auto 4096 neurons of 40..210 (parents within 16)", flush=True)
-    # trees averaging under 128 compartments (not the separator schedules),
-    # more than the level schedule's 393216 compartments in all
+    """Two lanes per tree when asked for (every tree whose two-lane schedule
+    is shorter); by default, small trees with parents within 16 that fill
+    every SIMD with one lane each stay on one lane, and fewer go to the
+    separator schedules (which replaced two lanes as the choice there)."""
+    print("hines multi split 4096 neurons of 40..210 (parents within 16)", flush=True)
     mm = W.hines_multi(4096, 40, 210, rng=np.random.default_rng(41), window=16)
-    assert mm.sizes.mean() < 128 and mm.sizes.sum() > 393216
     assert max(np.max(np.arange(1, n) - mm.neuron(s)[0][1:]) for s, n in enumerate(mm.sizes)) > 8
-    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
-    assert not plan.uses_levels
+    plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False, schedule=bps.BPS_HINES_SPLIT)
+    assert not plan.uses_levels and not plan.uses_sep
     assert plan.split >= 0.95 * mm.batch
     plan.close()
-    out, info = _run_multi(mm, bps.BPS_HINES_AUTO, min_split=1)
+    out, info = _run_multi(mm, bps.BPS_HINES_SPLIT, min_split=1)
     ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
     assert _rel_per_neuron(out, ref, mm.offsets) <= 1e-10
     np.testing.assert_array_equal(info, rinfo)
@@ -270,13 +268,11 @@ def test_multi_split_auto_choice():
     plan = bps.hines_plan_create(len(sizes), sizes, par, mono=False)
     assert not plan.uses_levels and plan.split == 0
     plan.close()
-    # 1000 blocks: as many trees as the free lanes of 1024 blocks take (less
-    # a margin of two blocks), the largest first
+    # 1000 blocks: one lane per tree would leave SIMDs idle: separator schedules
     sizes = np.r_[np.full(1000 * 64 - 2000, 40), np.full(2000, 60)].astype(np.int32)
     par = np.concatenate([W.random_tree(int(n), rng) for n in sizes])
     plan = bps.hines_plan_create(len(sizes), sizes, par, mono=False)
-    assert plan.split == 1024 * 64 - len(sizes) - 128
-    assert plan.elems <= 1024 * 64 * 60
+    assert plan.uses_sep and plan.split == 0
     plan.close()
 
 
@@ -482,13 +478,15 @@ def test_levels_auto_choice_and_limits():
     big = W.random_tree(5000, rng)
     assert not bps.hines_plan_create(10, [5000], big, mono=True).uses_levels
     # multi-morphology batches the separator schedules are not chosen for
-    # (trees averaging under 128 compartments): at most 393216 compartments
-    sizes = np.full(3096, 127, dtype=np.int32)
-    par = np.concatenate([W.random_tree(127, rng, window=16) for _ in range(3097)])
-    plan = bps.hines_plan_create(3096, sizes, par[:3096 * 127], mono=False)
+    # (small trees, parents within 16, enough to fill every SIMD with one
+    # lane each): levels for at most 393216 compartments
+    nb = 1024 * 64
+    par6 = np.concatenate([W.random_tree(6, rng, window=16) for _ in range(nb)])
+    plan = bps.hines_plan_create(nb, np.full(nb, 6, dtype=np.int32), par6, mono=False)
     assert plan.uses_levels and not plan.uses_sep
-    plan = bps.hines_plan_create(3097, np.full(3097, 127, dtype=np.int32), par, mono=False)
-    assert not plan.uses_levels and not plan.uses_sep and plan.split == 3097
+    par7 = np.concatenate([W.random_tree(7, rng, window=16) for _ in range(nb)])
+    plan = bps.hines_plan_create(nb, np.full(nb, 7, dtype=np.int32), par7, mono=False)
+    assert not plan.uses_levels and not plan.uses_sep and plan.split == 0
     with pytest.raises(bps.BpsError):
         bps.hines_plan_create(10, [5000], big, mono=True, schedule=bps.BPS_HINES_LEVELS)
 

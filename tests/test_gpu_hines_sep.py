@@ -387,12 +387,13 @@ def test_sep_multi_hybrid_trees_too_large():
 
 def test_sep_multi_auto_choice():
     """The automatic choice for multi-morphology batches: separator schedules
-    when the trees average at least 128 compartments (wherever their parents
-    lie); otherwise the other schedules."""
+    unless the trees average under 128 compartments, have their parents
+    within 16 and are enough (1024 blocks of 64) to fill every SIMD with one
+    lane per tree; then one lane per tree."""
     rng = np.random.default_rng(23)
     mm = W.hines_multi(300, 100, 160, rng=rng)
     plan = bps.hines_plan_create(mm.batch, mm.sizes, mm.parent, mono=False)
-    assert plan.uses_sep == (mm.sizes.mean() >= 128)
+    assert plan.uses_sep                              # 5 blocks: one lane per tree would not fill
     plan.close()
     big = W.hines_multi(64, 256, 2048, rng=rng)
     plan = bps.hines_plan_create(big.batch, big.sizes, big.parent, mono=False)
@@ -400,7 +401,15 @@ def test_sep_multi_auto_choice():
     plan.close()
     small = W.hines_multi(64, 30, 60, rng=rng)
     plan = bps.hines_plan_create(small.batch, small.sizes, small.parent, mono=False)
-    assert not plan.uses_sep
+    assert plan.uses_sep
+    plan.close()
+    many = W.hines_multi(1024 * 64, 30, 60, rng=rng)  # fills every SIMD, parents within 8
+    plan = bps.hines_plan_create(many.batch, many.sizes, many.parent, mono=False)
+    assert not plan.uses_sep and not plan.uses_levels and plan.split == 0
+    plan.close()
+    far = W.hines_multi_trees([W.dfs_tree(int(n), rng) for n in rng.integers(30, 61, size=1024 * 64)], rng)
+    plan = bps.hines_plan_create(far.batch, far.sizes, far.parent, mono=False)
+    assert plan.uses_sep                              # the other kernels' general variant otherwise
     plan.close()
     w16 = W.hines_multi(64, 256, 2048, rng=rng, window=16)
     plan = bps.hines_plan_create(w16.batch, w16.sizes, w16.parent, mono=False)
