@@ -165,14 +165,20 @@ __global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
     // parent updates are accumulated with LDS atomic adds on the lane's own
     // column (no read on the elimination chain); only the row's own pending
     // value is read back.
-    double qu[D], ql[D], qd[D], qr[D];
+    // The general variant's accumulators of far children come in with the
+    // row's inputs, D (< kRing) rows ahead: a child more than kRing rows away
+    // has been eliminated by then, and its update (a global atomic add that
+    // returns nothing) precedes the load in this lane's order.
+    double qu[D], ql[D], qd[D], qr[D], qgd[D], qgr[D];
     int32_t qp[D];
+    static_assert(D < kRing, "far-child accumulators are read D rows ahead");
     auto load_b = [&](int j, int32_t r) {
         const bool live = r >= 1 && r < my_n;
         const int64_t o = int64_t(live ? r : 0) * ld;
         qu[j] = live ? u[o] : 0.0; ql[j] = live ? l[o] : 0.0;
         qd[j] = live ? d[o] : 1.0; qr[j] = live ? rhs[o] : 0.0;
         if (!MONO) qp[j] = live ? par[o] : 0;
+        if (GEN) { qgd[j] = live ? gd[o] : 0.0; qgr[j] = live ? gr[o] : 0.0; }
     };
 #pragma unroll
     for (int j = 0; j < D; ++j) load_b(j, rows - 1 - j);
@@ -182,6 +188,7 @@ __global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
             const int32_t i = i0 - j;
             if (i < 1) break;
             const double ui = qu[j], li = ql[j], di = qd[j], ri = qr[j];
+            const double gdi = GEN ? qgd[j] : 0.0, gri = GEN ? qgr[j] : 0.0;
             const int32_t pi = MONO ? parent_of(i) : qp[j];
             load_b(j, i - D);
             if (i >= my_n) continue;
@@ -189,7 +196,7 @@ __global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
             const int slot = i & (kRing - 1);
             double pd = ring_d[slot][k], pr = ring_r[slot][k];
             ring_d[slot][k] = 0.0; ring_r[slot][k] = 0.0;
-            if (GEN) { pd += gd[o]; pr += gr[o]; }
+            if (GEN) { pd += gdi; pr += gri; }
             const double dd = di - pd;               // d'_i
             const double rr = ri - pr;               // rhs'_i
             if (!bad && bad_pivot(dd)) bad = i + 1;
@@ -202,8 +209,8 @@ __global__ void __launch_bounds__(kWave) k_hines(HinesArgs A)
                 unsafeAtomicAdd(&ring_d[ps][k], fac * li);
                 unsafeAtomicAdd(&ring_r[ps][k], fac * rr);
             } else {
-                gd[int64_t(pi) * ld] += fac * li;
-                gr[int64_t(pi) * ld] += fac * rr;
+                unsafeAtomicAdd(&gd[int64_t(pi) * ld], fac * li);
+                unsafeAtomicAdd(&gr[int64_t(pi) * ld], fac * rr);
             }
         }
     }
