@@ -45,8 +45,8 @@ struct bps_hines_plan {
     int32_t max_rows = 0;    // multi: largest block row count
     // device arrays
     int32_t *parent = nullptr;     // mono [n]; multi packed [elems]
-    uint8_t *dist8 = nullptr;      // multi packed [elems]: i - p_i (0 for roots and padding),
-                                   // when every parent is within kRing rows
+    uint8_t *dist8 = nullptr;      // multi packed [elems]: i - p_i (0 for roots and padding,
+                                   // kFar for a parent more than kRing rows up)
     int64_t *blk_off = nullptr;    // multi [nblocks]
     int32_t *blk_rows = nullptr;   // multi [nblocks]
     int32_t *lane_n = nullptr;     // multi [nblocks*64]
@@ -87,6 +87,7 @@ struct bps_hines_plan {
 namespace bps {
 
 constexpr int kRing = 16;       // LDS ring slots per lane (power of two)
+constexpr int kFar = 255;       // distance byte of a parent more than kRing rows up
 constexpr int kLevelMaxN = 4096;        // tree size limit of the level schedule (LDS)
 // auto: the level schedule up to this many compartments in the batch.
 // Measured (one solve): trees of 512, 16 .. 1024 neurons: 77 .. 107 us with
@@ -412,7 +413,7 @@ struct BlockBuf {
 // through buffer descriptors (one instruction per access), the look-ahead
 // alternates between two sets of registers (no copies), and the pending
 // (d, rhs) updates of a row share one 16-byte LDS slot.
-template <int D>
+template <int D, bool GEN = false>
 __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
 {
     __shared__ double2 ring[kRing][kWave];
@@ -430,6 +431,16 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     // parents as one-byte distances i - p_i (the window holds them): a
     // quarter of the bytes of int32 indices in both sweeps
     const BlockBuf PD(A.dist8 + off, nbytes / 8);
+    // GEN: a distance byte of kFar marks a parent more than kRing rows up;
+    // its index comes from the packed parents, and its pending updates go
+    // to the lane's global accumulators (atomic adds that return nothing),
+    // which a row reads with its inputs, D (< kRing) rows ahead: every child
+    // more than kRing rows away has added to them by then, in this lane's
+    // order
+    static_assert(!GEN || D < kRing, "far-child accumulators are read D rows ahead");
+    const BlockBuf PI(GEN ? static_cast<const void *>(A.parent + off) : A.u, GEN ? nbytes / 2 : 8u);
+    const BlockBuf GD(GEN ? static_cast<const void *>(A.gd + off) : A.u, GEN ? nbytes : 8u);
+    const BlockBuf GR(GEN ? static_cast<const void *>(A.gr + off) : A.u, GEN ? nbytes : 8u);
     const uint32_t lo8 = uint32_t(k) * 8u, lo1 = uint32_t(k);   // lane byte offsets
     // row byte offsets (scalar: a buffer access takes its row offset from an SGPR)
     auto rb8 = [](int32_t r) { return __builtin_amdgcn_readfirstlane(uint32_t(r) * (kWave * 8u)); };
@@ -439,17 +450,22 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     int32_t bad = 0;
 
     // ---- leaves -> root ----
-    struct BRow { double u, l, d, r; int32_t p; };   // p: distance to the parent
+    struct BRow { double u, l, d, r, gd, gr; int32_t p, pi; };   // p: distance to the parent
     auto load_b = [&](BRow &q, int32_t r) {
         const int32_t rc = r >= 1 ? r : 1 < rows ? 1 : 0;
         q.u = U.ld(lo8, rb8(rc)); q.l = L.ld(lo8, rb8(rc)); q.d = Dg.ld(lo8, rb8(rc));
         q.r = R.ld(lo8, rb8(rc)); q.p = PD.ldb(lo1, rb1(rc));
+        if (GEN) {
+            q.gd = GD.ld(lo8, rb8(rc)); q.gr = GR.ld(lo8, rb8(rc));
+            q.pi = PI.ldi(lo8 / 2, rb8(rc) / 2);
+        }
     };
     auto elim = [&](int32_t i, const BRow &q) {
         const bool live = i < my_n;
         const int slot = i & (kRing - 1);
-        const double2 pp = ring[slot][k];
+        double2 pp = ring[slot][k];
         ring[slot][k] = make_double2(0.0, 0.0);
+        if (GEN) { pp.x += q.gd; pp.y += q.gr; }
         const double dd = q.d - pp.x;            // d'_i
         const double rr = q.r - pp.y;            // rhs'_i
         if (live && !bad && bad_pivot(dd)) bad = i + 1;
@@ -457,9 +473,15 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
         const double fac = live ? q.u * rcp : 0.0;  // factor of Algorithm 1
         R.st(live ? rr * rcp : q.r, lo8, rb8(i));   // q_i (padding unchanged)
         MW.st(live ? q.l * rcp : 0.0, lo8, rb8(i)); // m_i
-        const int ps = (i - q.p) & (kRing - 1);
-        unsafeAtomicAdd(&ring[ps][k].x, fac * q.l);
-        unsafeAtomicAdd(&ring[ps][k].y, fac * rr);
+        if (GEN && q.p == kFar) {
+            const int64_t pe = off + int64_t(q.pi) * kWave + k;
+            unsafeAtomicAdd(&A.gd[pe], fac * q.l);
+            unsafeAtomicAdd(&A.gr[pe], fac * rr);
+        } else {
+            const int ps = (i - q.p) & (kRing - 1);
+            unsafeAtomicAdd(&ring[ps][k].x, fac * q.l);
+            unsafeAtomicAdd(&ring[ps][k].y, fac * rr);
+        }
     };
     BRow qa[D], qb[D];
 #pragma unroll
@@ -492,7 +514,8 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
             if (i0 - j >= 1) elim(i0 - j, qa[j]);
     }
     const bool root = my_n > 0;
-    const double2 p0 = ring[0][k];
+    double2 p0 = ring[0][k];
+    if (GEN) { p0.x += GD.ld(lo8, 0); p0.y += GR.ld(lo8, 0); }
     const double dd0 = Dg.ld(lo8, 0) - p0.x;
     if (root && !bad && bad_pivot(dd0)) bad = 1;
     const double r0 = R.ld(lo8, 0);
@@ -504,14 +527,17 @@ __global__ void __launch_bounds__(kWave) k_hines_multi(HinesArgs A)
     // parent one row up comes from a register ----
     ring[0][k].x = v0;
     double vprev = v0;
-    struct FRow { double q, m; int32_t p; };         // p: distance to the parent
+    struct FRow { double q, m; int32_t p, pi; };     // p: distance to the parent
     auto load_f = [&](FRow &f, int32_t r) {
         const int32_t rc = r < rows ? r : rows - 1;
         f.q = R.ld(lo8, rb8(rc)); f.m = MW.ld(lo8, rb8(rc)); f.p = PD.ldb(lo1, rb1(rc));
+        if (GEN) f.pi = PI.ldi(lo8 / 2, rb8(rc) / 2);
     };
     auto subst = [&](int32_t i, const FRow &f) {
         const bool live = i < my_n;
-        const double vr = ring[(i - f.p) & (kRing - 1)][k].x;
+        double vr = ring[(i - f.p) & (kRing - 1)][k].x;
+        // a far parent's voltage, written long before (its row differs by lane)
+        if (GEN && f.p == kFar) vr = R.ld(lo8 + uint32_t(f.pi) * (kWave * 8u), 0);
         const double vp = (f.p == 1) ? vprev : vr;
         const double v = f.q - f.m * vp;
         R.st(live ? v : f.q, lo8, rb8(i));
@@ -1496,11 +1522,11 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
                 for (int32_t i = 1; i < sizes[s]; ++i) {
                     const int32_t p = parent[off[s] + i];
                     pk[boff[b] + int64_t(i) * kWave + k] = p;
-                    d8[boff[b] + int64_t(i) * kWave + k] = uint8_t(std::min(i - p, 255));
+                    d8[boff[b] + int64_t(i) * kWave + k] = uint8_t(i - p <= kRing ? i - p : kFar);
                     P->max_dist = std::max<int32_t>(P->max_dist, i - p);
                 }
             }
-        if (P->max_dist <= kRing) st = upload(&P->dist8, d8);
+        st = upload(&P->dist8, d8);
         if (st == BPS_OK && (st = upload(&P->parent, pk)) == BPS_OK && (st = upload(&P->blk_off, boff)) == BPS_OK &&
             (st = upload(&P->blk_rows, brows)) == BPS_OK && (st = upload(&P->lane_n, ln)) == BPS_OK &&
             (st = upload(&P->lane_src, lsrc)) == BPS_OK)
@@ -1674,7 +1700,7 @@ bps_status hines_launch(const bps_hines_plan *P, const void *u, const void *l, c
         if (gen) hipLaunchKernelGGL((k_hines<true, true, D>), grid, dim3(kWave), 0, st, A);
         else hipLaunchKernelGGL((k_hines_mono_reg<D>), grid, dim3(kWave), 0, st, A);
     } else {
-        if (gen) hipLaunchKernelGGL((k_hines<false, true, D>), grid, dim3(kWave), 0, st, A);
+        if (gen) hipLaunchKernelGGL((k_hines_multi<D, true>), grid, dim3(kWave), 0, st, A);
         else if (P->nsplit > 0 && P->nblocks <= kSimds)
             hipLaunchKernelGGL((k_hines_split<16>), grid, dim3(kWave), 0, st, A);
         else if (P->nsplit > 0) hipLaunchKernelGGL((k_hines_split<D>), grid, dim3(kWave), 0, st, A);

@@ -19,9 +19,11 @@ from gpu_util import buf, dev, host, info_buf
 pytestmark = pytest.mark.gpu
 
 
-def _rel_per_neuron(x, y, off):
+def _rel_per_neuron(x, y, off, skip=()):
     errs = []
     for s in range(len(off) - 1):
+        if s in skip:
+            continue
         a, b = x[off[s]:off[s + 1]], y[off[s]:off[s + 1]]
         errs.append(np.linalg.norm(a - b) / np.linalg.norm(b))
     return float(np.max(errs))
@@ -243,6 +245,33 @@ def test_multi_split_matches_oracle(batch, nmin, nmax):
     ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
     assert _rel_per_neuron(out, ref, mm.offsets) <= 1e-10
     np.testing.assert_array_equal(info, rinfo)
+
+
+def test_multi_one_lane_far_parents():
+    """One lane per tree (BPS_HINES_LANES) on depth-first numbered trees,
+    parents up to thousands of compartments back: far children's updates go
+    through the lane's global accumulators; breakdowns near a far parent and
+    in a chain, info as Algorithm 1's."""
+    print("hines multi one lane, depth-first trees", flush=True)
+    rng = np.random.default_rng(61)
+    trees = [W.dfs_tree(int(n), rng) for n in rng.integers(20, 3000, size=200)]
+    mm = W.hines_multi_trees(trees, rng)
+    far = [s for s in range(mm.batch)
+           if np.max(np.arange(1, mm.sizes[s]) - mm.neuron(s)[0][1:], initial=0) > 100]
+    assert len(far) > 50
+    o = mm.offsets
+    s1, s2 = far[0], far[1]
+    p1 = mm.neuron(s1)[0]
+    i1 = int(np.argmax(np.arange(len(p1)) - np.r_[0, p1[1:]]))    # the row with the farthest parent
+    mm.u[o[s1]:o[s1 + 1]] = 0.0
+    mm.d[o[s1] + int(p1[i1])] = 0.0
+    mm.u[o[s2]:o[s2 + 1]] = 0.0
+    mm.d[o[s2] + 5] = 0.0
+    out, info = _run_multi(mm, bps.BPS_HINES_LANES)
+    ref, rinfo = oracle.hines_multi_solve(mm.offsets, mm.parent, mm.u, mm.l, mm.d, mm.rhs)
+    np.testing.assert_array_equal(info, rinfo)
+    assert info[s1] == int(p1[i1]) + 1 and info[s2] == 6
+    assert _rel_per_neuron(out, ref, mm.offsets, skip=(s1, s2)) <= 1e-10
 
 
 def test_multi_split_auto_choice():
