@@ -555,13 +555,13 @@ def hines_sep_multi_layout(sizes, parent):
 
 def hines_sep_schedule(parent):
     """Host-only BPS_HINES_SEP schedule of one tree (see bps.h), decoded:
-    a dict with R, lanes (16 or 32), ns, nc, npc, nh, codes (lanes, R)
+    a dict with R, lanes (16, 32 or 64), ns, nc, npc, nh, codes (lanes, R)
     uint32, bases (lanes, 3), septab (ns, 5), comptab (nc, 3), clist (nc,);
     None when the tree does not qualify."""
     import numpy as np
     par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
     n = len(par)
-    cap = 8 + 32 * 32 + 96 + 5 * n + 4 * n + 64
+    cap = 8 + 64 * 32 + 64 * 3 + 5 * n + 4 * n + 64
     out = np.zeros(cap, dtype=np.int32)
     i32p = ctypes.POINTER(ctypes.c_int32)
     L = load_library()

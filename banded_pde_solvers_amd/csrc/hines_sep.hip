@@ -1,5 +1,5 @@
 // hines_sep.hip -- Hines systems of one shared morphology, each neuron
-// solved by sixteen or thirty-two lanes, and multi-morphology batches with
+// solved by sixteen, thirty-two or sixty-four lanes, and multi-morphology batches with
 // every tree on its own lanes ([H] section 2, Algorithm 1, and the
 // per-branch decomposition of section 4).
 //
@@ -17,11 +17,12 @@
 // kernel reads u, l, d, rhs and writes V once: 40 bytes, where one lane per
 // neuron also writes and reads q, m.
 //
-// Workgroup: 16 neurons x 16 lanes, or 8 neurons x 32 lanes.  Thread
-// (k, j) = lane k of neuron j; a wavefront holds 4 lanes of 16 neighbouring
-// neurons (every access four 128-byte row segments of the interleaved
-// layout) or 8 lanes of 8 (eight 64-byte halves, the other halves read by a
-// workgroup on the same XCD).  A lane keeps its compartments' pending
+// Workgroup: 16 neurons x 16 lanes, 8 neurons x 32 lanes or 4 neurons x 64
+// lanes.  Thread (k, j) = lane k of neuron j; a wavefront holds 4 lanes of
+// 16 neighbouring neurons (every access four 128-byte row segments of the
+// interleaved layout), 8 lanes of 8 (eight 64-byte halves, the other halves
+// read by a workgroup on the same XCD) or 16 lanes of 4 (32-byte quarters,
+// the others read by three workgroups on the same XCD).  A lane keeps its compartments' pending
 // updates and voltages in 8 ring slots that the schedule assigns.
 #include <algorithm>
 #include <cstring>
@@ -38,7 +39,7 @@ namespace bps {
 
 namespace {
 
-constexpr int kSepNeurons = 16;     // neurons per workgroup with 16 lanes each (8 with 32)
+constexpr int kSepNeurons = 16;     // neurons per workgroup with 16 lanes each (8 with 32, 4 with 64)
 constexpr int kSepSlots = 8;        // ring of pending updates / voltages per lane
 constexpr int kSepHeader = 8;
 
@@ -94,17 +95,19 @@ __host__ __device__ inline int sep_tab_words(int R, int ns, int nc, int lanes)
     return lanes * R + lanes * 3 + ns * 5 + nc * 4;
 }
 
-// Neuron group of a workgroup.  With 8 neurons per workgroup a 128-byte row
-// segment holds two groups' values; workgroups are handed to the 8 XCDs in
-// turn (block b to XCD b mod 8), so within each run of 16 blocks b and b + 8
-// take groups 2m and 2m + 1: the two halves of each segment are read by one
-// XCD's L2 at about the same time.  A last partial run keeps its order.
+// Neuron group of a workgroup.  With NEU < 16 neurons per workgroup a
+// 128-byte row segment holds G = 16 / NEU groups' values; workgroups are
+// handed to the 8 XCDs in turn (block b to XCD b mod 8), so within each run
+// of 8 G blocks, blocks b, b + 8, ..., b + 8 (G - 1) take groups G m, ...,
+// G m + G - 1: the parts of each segment are read by one XCD's L2 at about
+// the same time.  A last partial run keeps its order.
 template <int NEU>
 __device__ __forceinline__ int64_t sep_group(int64_t b, int64_t nblk)
 {
-    if (NEU == 16 || b >= nblk / 16 * 16) return b;
-    const int64_t r = b % 16;
-    return b - r + 2 * (r % 8) + r / 8;
+    constexpr int G = 16 / NEU, RUN = 8 * G;
+    if (G == 1 || b >= nblk / RUN * RUN) return b;
+    const int64_t r = b % RUN;
+    return b - r + G * (r % 8) + r / 8;
 }
 
 template <int R, int LANES, int NEU>
@@ -963,13 +966,14 @@ static bool sep_tree(int32_t n, const int32_t *p, int L, int R, bool sep_rows, S
 std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
 {
     if (n < 1 || n > 2047) { why = "tree size outside [1, 2047]"; return {}; }
-    // sixteen lanes of 16 or 32 rows, else thirty-two lanes of 24 or 32 rows;
-    // sixteen lanes of 32 rows only with components of at least 16 rows
+    // sixteen lanes of 16 or 32 rows, else thirty-two lanes of 24 or 32 rows,
+    // else sixty-four of 32; sixteen lanes of 32 rows only with components of
+    // at least 16 rows
     // (measured: a tree of 560 squeezed into them by components of ~10
     // rows, 57 separators, took 0.89 ms for 91424 neurons where one lane per
     // neuron takes 0.72)
     for (const auto [lanes, R, tmin] :
-         {std::tuple<int, int, int>{16, 16, 6}, {16, 32, 16}, {32, 24, 12}, {32, 32, 6}}) {
+         {std::tuple<int, int, int>{16, 16, 6}, {16, 32, 16}, {32, 24, 12}, {32, 32, 6}, {64, 32, 6}}) {
         SepTree T;
         if (!sep_tree(n, p, lanes, R, false, T, tmin)) continue;
         const int32_t ns = T.ns, nc = T.nc;
@@ -977,7 +981,7 @@ std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
         std::vector<int32_t> blob(kSepHeader + sep_tab_words(R, ns, nc, lanes), 0);
         blob[0] = R; blob[1] = ns; blob[2] = nc; blob[3] = T.npc; blob[4] = T.nh; blob[5] = n;
         blob[6] = lanes;
-        blob[7] = lanes == 32 ? 8 : kSepNeurons;     // neurons per workgroup
+        blob[7] = kSepNeurons * 16 / lanes;          // neurons per workgroup
         int32_t *codes = blob.data() + kSepHeader;
         for (int l = 0; l < lanes; ++l) {
             int t = 0;
@@ -1009,7 +1013,7 @@ std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
         if (sep_lds_bytes(blob.data()) > 160 * 1024) continue;
         return blob;
     }
-    why = "no partition fits 32 lanes of 32 rows";
+    why = "no partition fits 64 lanes of 32 rows";
     return {};
 }
 
@@ -1238,7 +1242,8 @@ hipError_t sep_prepare_device()
     for (const void *f : {reinterpret_cast<const void *>(&k_hines_sep<16, 16, 16>),
                           reinterpret_cast<const void *>(&k_hines_sep<32, 16, 16>),
                           reinterpret_cast<const void *>(&k_hines_sep<24, 32, 8>),
-                          reinterpret_cast<const void *>(&k_hines_sep<32, 32, 8>)}) {
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 32, 8>),
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 64, 4>)}) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
     }
@@ -1264,7 +1269,8 @@ bps_status launch_hines_sep(const int32_t *blob_host, const int32_t *blob_dev, i
     const size_t lds = sep_lds_bytes(blob_host);
     const int lanes = blob_host[6], neu = blob_host[7];
     const dim3 grid(unsigned((batch + neu - 1) / neu)), block(unsigned(lanes * neu));
-    if (lanes == 32 && R == 24) hipLaunchKernelGGL((k_hines_sep<24, 32, 8>), grid, block, lds, st, A);
+    if (lanes == 64) hipLaunchKernelGGL((k_hines_sep<32, 64, 4>), grid, block, lds, st, A);
+    else if (lanes == 32 && R == 24) hipLaunchKernelGGL((k_hines_sep<24, 32, 8>), grid, block, lds, st, A);
     else if (lanes == 32) hipLaunchKernelGGL((k_hines_sep<32, 32, 8>), grid, block, lds, st, A);
     else if (R == 16) hipLaunchKernelGGL((k_hines_sep<16, 16, 16>), grid, block, lds, st, A);
     else hipLaunchKernelGGL((k_hines_sep<32, 16, 16>), grid, block, lds, st, A);

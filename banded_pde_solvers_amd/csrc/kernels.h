@@ -79,7 +79,7 @@ template <typename T>
 bps_status launch_tri_solve(int64_t n, int64_t batch, int64_t ld, const void *a, const void *b,
                             const void *c, void *y, void *work, int32_t *info, hipStream_t st);
 
-// Hines systems of one shared tree on sixteen or thirty-two lanes per neuron
+// Hines systems of one shared tree on sixteen, thirty-two or sixty-four lanes per neuron
 // (hines_sep.hip): the schedule of a tree (empty, reason in why, when the
 // tree does not qualify), the kernel's dynamic LDS, and its launch.
 std::vector<int32_t> sep_schedule(int32_t n, const int32_t *parent, std::string &why);

@@ -31,7 +31,7 @@ oracle, built with gcc -O3 -march=native -fopenmp on this host, timed on a
 bounded sample of the same workload with all of this host's cores and with
 one thread, median of 5 runs each, CPU model and core counts stated).
 
-    python bench.py [--steps K] [--warmup W] [--workload {0,...,13}]
+    python bench.py [--steps K] [--warmup W] [--workload {0,...,14}]
 
 --workload selects another workload for manual measurements
 (0: the small periodic case, N = 256, 64 systems, 10 steps from seeded Fourier
@@ -46,7 +46,9 @@ factor+solve, --dtype f64|f32; 10: Hines mono 512 x 256, a batch too small
 for one lane per neuron, solved with the per-level section schedule; 11, 12:
 workloads 3 and 4 with their trees numbered depth first, parents arbitrarily
 far back; 13: Hines mono, one tree of 960 compartments x 53328 neurons, the
-thirty-two-lane separator schedule).
+thirty-two-lane separator schedule; 14: Hines mono, one tree of 2000
+compartments numbered depth first x 25600 neurons, the sixty-four-lane
+separator schedule).
 HBM-bound workloads also report the measured bandwidth of a plain 1 GiB
 device copy (copy_gbs) and the kernel's fraction of it (frac_of_copy): a
 stream that writes cannot exceed it.  Only one GPU is used; --gpus above 1
@@ -742,12 +744,12 @@ def main():
     # median of 50 timed calls (the SpEC page's benchmarking section)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=list(range(0, 14)))
+    ap.add_argument("--workload", type=int, default=1, choices=list(range(0, 15)))
     ap.add_argument("--dtype", default="f64", choices=["f64", "f32"], help="workloads 2, 7, 8, 9")
     ap.add_argument("--split", action="store_true",
                     help="workloads 2, 9: time the separate factor and solve calls instead")
     ap.add_argument("--hines-schedule", default="auto", choices=["auto", "lanes", "split", "levels", "sep"],
-                    help="workloads 3, 4, 10-13: the plan's schedule (BPS_HINES_*)")
+                    help="workloads 3, 4, 10-14: the plan's schedule (BPS_HINES_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -785,7 +787,8 @@ def main():
           6: lambda a: bench_hyperdiffusion(a, 6), 7: lambda a: bench_tri(a, 7),
           8: lambda a: bench_tri(a, 8), 9: lambda a: bench_penta(a, 9),
           10: lambda a: _hines_common(a, False, 10), 11: lambda a: _hines_common(a, False, 11),
-          12: lambda a: _hines_common(a, True, 12), 13: lambda a: _hines_common(a, False, 13)}[args.workload]
+          12: lambda a: _hines_common(a, True, 12), 13: lambda a: _hines_common(a, False, 13),
+          14: lambda a: _hines_common(a, False, 14)}[args.workload]
     line = fn(args)
     roof = line.get("roofline")
     if roof and roof.get("bound") == "hbm":

@@ -385,10 +385,9 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     decomposition of section 4 with the pages' solve of
  *                     the reduced system, each compartment's values read and
  *                     written once.  Mono plans (trees of at most 2047
- *                     compartments whose components fit 16 lanes of 32
- *                     rows or 32 lanes of 32 rows, about 1000 compartments
- *                     at most): sixteen or thirty-two lanes per neuron in
- *                     the Full-Interleaved layout.  Multi-morphology plans (trees
+ *                     compartments whose components fit 16, 32 or 64
+ *                     lanes of 32 rows): sixteen, thirty-two or sixty-four
+ *                     lanes per neuron in the Full-Interleaved layout.  Multi-morphology plans (trees
  *                     of at most 8191 compartments): every tree on as many
  *                     lanes as it needs, trees packed into workgroups of 128
  *                     lanes, the plan's layout in schedule order (element
@@ -413,11 +412,13 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *                     one section per lane and level, with the neuron held
  *                     in LDS; for batches too small to fill the GPU with one
  *                     lane per neuron.  Trees of at most 4096 compartments;
- *   BPS_HINES_AUTO    SEP for trees it takes: mono plans whose tree has at
- *                     least 256 compartments, or a parent more than 16
- *                     compartments back, or whose batch has at most 2^21
- *                     compartments in all; multi-morphology plans unless
- *                     the trees average under 128 compartments, have all
+ *   BPS_HINES_AUTO    SEP for trees it takes: mono plans whose tree has a
+ *                     parent more than 16 compartments back, or has at
+ *                     least 256 compartments or a batch of at most 2^21
+ *                     compartments in all, unless (parents within 16) its
+ *                     schedule takes 64 lanes, or 32 lanes of 32 rows with
+ *                     more than 32 separators; multi-morphology plans
+ *                     unless the trees average under 128 compartments, have all
  *                     their parents within 16 and fill the GPU with one
  *                     lane each (at least 1024 blocks of 64); trees too
  *                     large for one workgroup of SEP's layout, if any, are
@@ -457,8 +458,8 @@ BPS_API int hines_plan_uses_sep(const bps_hines_plan *plan);
  * needed; for inspection and host-side tests), as int32 words:
  *   [0] R rows per lane, [1] ns separators, [2] nc components, [3] npc
  *   components with a separator below, [4] nh compartments on those
- *   components' paths, [5] n, [6] lanes per neuron (16 or 32), [7]
- *   neurons per workgroup (16, or 8 with 32 lanes);
+ *   components' paths, [5] n, [6] lanes per neuron (16, 32 or 64), [7]
+ *   neurons per workgroup (16, 8 with 32 lanes, 4 with 64);
  *   then codes [lanes][R]: lane k's step t of the first sweep (the second
  *   takes the steps in reverse): bits 0-10 the compartment, 11-13 its slot
  *   in the lane's ring of pending updates and voltages, 14-16 its parent's
@@ -543,8 +544,9 @@ BPS_API bps_status hines_unpack(const bps_hines_plan *plan, int dtype, const voi
 BPS_API size_t hines_work_bytes(const bps_hines_plan *plan, int dtype);
 
 /* Solve every neuron ([H] Algorithm 1) with the plan's schedule (one lane
- * per neuron, two lanes for split trees, separator schedules (sixteen or
- * thirty-two lanes per neuron, or every tree on its own lanes), or one
+ * per neuron, two lanes for split trees, separator schedules (sixteen,
+ * thirty-two or sixty-four lanes per neuron, or every tree on its own
+ * lanes), or one
  * wavefront per neuron).
  * u, l, d: device, solver layout, not modified.  rhs: device, solver layout,
  * right-hand side on entry, voltages V on return (as in [H]).  work: device,

@@ -150,6 +150,26 @@ def test_sep_thirty_two_lanes_depth_first(n):
     assert _cols_err(out[:, ok], ref[:, ok]) <= 1e-10
 
 
+@pytest.mark.parametrize("n,batch,ld,dfs", [(1300, 70, 0, False), (1500, 1003, 1010, True),
+                                            (2047, 261, 0, False), (2047, 130, 0, True)])
+def test_sep_sixty_four_lanes(n, batch, ld, dfs):
+    """Sixty-four lanes per neuron (four neurons per workgroup, the
+    workgroups of a run of 32 grouped by XCD, a ragged last run), window
+    and depth-first numbered trees, with a breakdown in one neuron."""
+    print(f"hines sep 64 lanes n={n} batch={batch} ld={ld} dfs={dfs}", flush=True)
+    rng = np.random.default_rng(n + batch)
+    hm = _values(W.dfs_tree(n, rng) if dfs else W.random_tree(n, rng), batch, rng)
+    assert bps.hines_sep_schedule(hm.parent)["lanes"] == 64
+    hm.d[n // 3, 5] = 0.0
+    hm.u[:, 5] = 0.0                      # decoupled: every pivot is d itself
+    out, info = _solve(hm, ld=ld, twice=(batch == 130))
+    ref, rinfo = _oracle(hm)
+    np.testing.assert_array_equal(info, rinfo)
+    assert info[5] == n // 3 + 1
+    ok = [s for s in range(batch) if s != 5]
+    assert _cols_err(out[:, ok], ref[:, ok]) <= 1e-10
+
+
 def _kind_tree(kind, n, rng):
     if kind == 0:
         return W.random_tree(n, rng, window=int(rng.integers(1, 65)))
@@ -169,7 +189,7 @@ def test_sep_fuzz_mono_and_multi():
     rng = np.random.default_rng(4242)
     done = 0
     for it in range(12):
-        n = int(rng.integers(2, 1000))
+        n = int(rng.integers(2, 2048))
         p = _kind_tree(it % 3, n, rng)
         if bps.hines_sep_schedule(p) is None:
             continue
@@ -200,9 +220,32 @@ def test_sep_refusals_and_auto():
         plan = bps.hines_plan_create(64, [300], p, mono=True)
         assert plan.uses_sep
         plan.close()
-    # too large for sixteen lanes of 32 rows; a star of 1499 components
+    # trees of 1300..2047 on sixty-four lanes; by the automatic choice only
+    # with parents far back (one lane per neuron is faster otherwise)
+    for p, far in ((W.random_tree(1500, rng), False), (W.dfs_tree(1500, rng), True)):
+        bps.hines_plan_create(64, [1500], p, mono=True, schedule=SEP).close()
+        plan = bps.hines_plan_create(4096, [1500], p, mono=True)
+        assert plan.uses_sep == far and not plan.uses_levels
+        plan.close()
+    # 32 lanes of 32 rows: taken with at most 32 separators, left to one lane
+    # per neuron beyond (parents within 16)
+    seen = set()
+    for seed in range(40):
+        p = W.random_tree(1024, np.random.default_rng(seed))
+        S = bps.hines_sep_schedule(p)
+        if S is None or S["lanes"] != 32 or S["R"] != 32:
+            continue
+        squeezed = S["ns"] > 32
+        plan = bps.hines_plan_create(4096, [1024], p, mono=True)
+        assert plan.uses_sep == (not squeezed), (seed, S["ns"])
+        plan.close()
+        seen.add(squeezed)
+        if len(seen) == 2:
+            break
+    assert seen == {True, False}
+    # above the 2047 compartments of the row codes; a star of 1499 components
     with pytest.raises(bps.BpsError):
-        bps.hines_plan_create(64, [1500], W.random_tree(1500, rng), mono=True, schedule=SEP)
+        bps.hines_plan_create(64, [2048], W.random_tree(2048, rng), mono=True, schedule=SEP)
     with pytest.raises(bps.BpsError):
         bps.hines_plan_create(64, [1500], np.array([-1] + [0] * 1499, dtype=np.int32), mono=True,
                               schedule=SEP)

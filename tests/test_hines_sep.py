@@ -168,6 +168,10 @@ def _trees():
     for n in (600, 700, 1000):
         out.append((f"window8_{n}", W.random_tree(n, rng)))
         out.append((f"dfs_{n}", W.dfs_tree(n, rng)))
+    # sixty-four lanes per neuron, up to the largest tree the codes hold
+    for n in (1500, 2047):
+        out.append((f"window8_{n}", W.random_tree(n, rng)))
+        out.append((f"dfs_{n}", W.dfs_tree(n, rng)))
     return out
 
 
@@ -215,7 +219,8 @@ def test_sep_schedule_replay_matches_oracle(name, p):
 def test_sep_schedule_shapes():
     """On the workloads' trees of 512: sixteen lanes of at most 32 rows, a
     few separators, and a share of path rows; trees of 600..960: thirty-two
-    lanes of 24 rows, then of 32."""
+    lanes of 24 rows, then of 32; trees of 1300..2047: sixty-four lanes of
+    32 rows."""
     _lib_or_skip()
     rng = np.random.default_rng(4)
     for _ in range(10):
@@ -227,6 +232,11 @@ def test_sep_schedule_shapes():
     for n, R in ((600, 24), (700, 24), (960, 32)):
         S = bps.hines_sep_schedule(W.random_tree(n, rng))
         assert S is not None and S["lanes"] == 32 and S["R"] == R
+    for n in (1300, 1700, 2047):
+        for tree in (W.random_tree(n, rng), W.dfs_tree(n, rng)):
+            S = bps.hines_sep_schedule(tree)
+            assert S is not None and S["lanes"] == 64 and S["R"] == 32
+            assert S["ns"] <= 255 and S["nc"] <= 255
 
 
 def test_sep_schedule_slots_beyond_window():
@@ -245,11 +255,12 @@ def test_sep_schedule_slots_beyond_window():
 def test_sep_schedule_refusals():
     _lib_or_skip()
     # a star (1499 one-compartment components, more than 255), and a tree
-    # too large for 32 x 32 rows
+    # beyond the 2047 compartments of the row codes
     star = np.array([-1] + [0] * 1499, dtype=np.int32)
     assert bps.hines_sep_schedule(star) is None
     assert "no partition" in bps.bps_last_error()
-    assert bps.hines_sep_schedule(W.random_tree(1200, np.random.default_rng(1))) is None
+    assert bps.hines_sep_schedule(W.random_tree(2048, np.random.default_rng(1))) is None
+    assert "2047" in bps.bps_last_error()
     with pytest.raises(bps.BpsError):
         bps.hines_sep_schedule(np.array([-1, 0, 5], dtype=np.int32))
     import ctypes
@@ -292,13 +303,13 @@ def _random_recursive(n, rng, bushy):
 
 def test_sep_schedule_fuzz():
     """Many seeded trees of every kind (windows 1..64, depth-first, bushy
-    and stringy random recursive trees, 1..1000 compartments): every
+    and stringy random recursive trees, 1..2047 compartments): every
     schedule the library gives replays to the oracle's voltages."""
     _lib_or_skip()
     rng = np.random.default_rng(2024)
     taken = 0
     for it in range(300):
-        n = int(rng.integers(1, 1000))
+        n = int(rng.integers(1, 2048))
         kind = it % 4
         if kind == 0:
             p = W.random_tree(n, rng, window=int(rng.integers(1, 65)))

@@ -423,4 +423,7 @@ WORKLOADS = {
     # a larger shared tree, about as many compartments as workload 3: the
     # thirty-two-lane separator schedule
     13: dict(name="hines_mono_n960_b53328", kind="hines_mono", n=960, batch=53328),
+    # a shared tree of 2000 compartments numbered depth first, about as many
+    # compartments as workload 3: the sixty-four-lane separator schedule
+    14: dict(name="hines_mono_dfs_n2000_b25600", kind="hines_mono", n=2000, batch=25600, dfs=True),
 }
