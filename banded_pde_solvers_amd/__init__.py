@@ -555,7 +555,8 @@ def hines_sep_multi_layout(sizes, parent):
 
 def hines_sep_schedule(parent):
     """Host-only BPS_HINES_SEP schedule of one tree (see bps.h), decoded:
-    a dict with R, lanes (16, 32 or 64), ns, nc, npc, nh, codes (lanes, R)
+    a dict with R, lanes (16, 32 or 64), neurons (per workgroup), ns, nc,
+    npc, nh, codes (lanes, R)
     uint32, bases (lanes, 3), septab (ns, 5), comptab (nc, 3), clist (nc,);
     None when the tree does not qualify."""
     import numpy as np
@@ -582,7 +583,8 @@ def hines_sep_schedule(parent):
     comptab = out[o:o + nc * 3].reshape(nc, 3).copy()
     o += nc * 3
     clist = out[o:o + nc].copy()
-    return {"R": R, "lanes": K, "ns": ns, "nc": nc, "npc": npc, "nh": nh, "codes": codes, "bases": bases,
+    return {"R": R, "lanes": K, "neurons": int(out[7]), "ns": ns, "nc": nc, "npc": npc, "nh": nh,
+            "codes": codes, "bases": bases,
             "septab": septab, "comptab": comptab, "clist": clist}
 
 

@@ -17,12 +17,12 @@
 // kernel reads u, l, d, rhs and writes V once: 40 bytes, where one lane per
 // neuron also writes and reads q, m.
 //
-// Workgroup: 16 neurons x 16 lanes, 8 neurons x 32 lanes or 4 neurons x 64
-// lanes.  Thread (k, j) = lane k of neuron j; a wavefront holds 4 lanes of
-// 16 neighbouring neurons (every access four 128-byte row segments of the
-// interleaved layout), 8 lanes of 8 (eight 64-byte halves, the other halves
-// read by a workgroup on the same XCD) or 16 lanes of 4 (32-byte quarters,
-// the others read by three workgroups on the same XCD).  A lane keeps its compartments' pending
+// Workgroup: 16 neurons x 16 lanes, 8 neurons x 32 or 64 lanes, or 4
+// neurons x 64 lanes.  Thread (k, j) = lane k of neuron j; a wavefront holds
+// 4 lanes of 16 neighbouring neurons (every access four 128-byte row
+// segments of the interleaved layout), 8 lanes of 8 (eight 64-byte halves,
+// the other halves read by a workgroup on the same XCD) or 16 lanes of 4
+// (32-byte quarters, the others read by three workgroups on the same XCD).  A lane keeps its compartments' pending
 // updates and voltages in 8 ring slots that the schedule assigns.
 #include <algorithm>
 #include <cstring>
@@ -982,6 +982,12 @@ std::vector<int32_t> sep_schedule(int32_t n, const int32_t *p, std::string &why)
         blob[0] = R; blob[1] = ns; blob[2] = nc; blob[3] = T.npc; blob[4] = T.nh; blob[5] = n;
         blob[6] = lanes;
         blob[7] = kSepNeurons * 16 / lanes;          // neurons per workgroup
+        // 64 lanes: 8 neurons per workgroup (one per CU, 64-byte halves of
+        // the row segments per access) when its LDS fits, else 4
+        if (lanes == 64) {
+            blob[7] = 8;
+            if (sep_lds_bytes(blob.data()) > 160 * 1024) blob[7] = 4;
+        }
         int32_t *codes = blob.data() + kSepHeader;
         for (int l = 0; l < lanes; ++l) {
             int t = 0;
@@ -1243,7 +1249,8 @@ hipError_t sep_prepare_device()
                           reinterpret_cast<const void *>(&k_hines_sep<32, 16, 16>),
                           reinterpret_cast<const void *>(&k_hines_sep<24, 32, 8>),
                           reinterpret_cast<const void *>(&k_hines_sep<32, 32, 8>),
-                          reinterpret_cast<const void *>(&k_hines_sep<32, 64, 4>)}) {
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 64, 4>),
+                          reinterpret_cast<const void *>(&k_hines_sep<32, 64, 8>)}) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
     }
@@ -1269,7 +1276,8 @@ bps_status launch_hines_sep(const int32_t *blob_host, const int32_t *blob_dev, i
     const size_t lds = sep_lds_bytes(blob_host);
     const int lanes = blob_host[6], neu = blob_host[7];
     const dim3 grid(unsigned((batch + neu - 1) / neu)), block(unsigned(lanes * neu));
-    if (lanes == 64) hipLaunchKernelGGL((k_hines_sep<32, 64, 4>), grid, block, lds, st, A);
+    if (lanes == 64 && neu == 8) hipLaunchKernelGGL((k_hines_sep<32, 64, 8>), grid, block, lds, st, A);
+    else if (lanes == 64) hipLaunchKernelGGL((k_hines_sep<32, 64, 4>), grid, block, lds, st, A);
     else if (lanes == 32 && R == 24) hipLaunchKernelGGL((k_hines_sep<24, 32, 8>), grid, block, lds, st, A);
     else if (lanes == 32) hipLaunchKernelGGL((k_hines_sep<32, 32, 8>), grid, block, lds, st, A);
     else if (R == 16) hipLaunchKernelGGL((k_hines_sep<16, 16, 16>), grid, block, lds, st, A);

@@ -459,7 +459,7 @@ BPS_API int hines_plan_uses_sep(const bps_hines_plan *plan);
  *   [0] R rows per lane, [1] ns separators, [2] nc components, [3] npc
  *   components with a separator below, [4] nh compartments on those
  *   components' paths, [5] n, [6] lanes per neuron (16, 32 or 64), [7]
- *   neurons per workgroup (16, 8 with 32 lanes, 4 with 64);
+ *   neurons per workgroup (16, 8 with 32 lanes, 8 or 4 with 64);
  *   then codes [lanes][R]: lane k's step t of the first sweep (the second
  *   takes the steps in reverse): bits 0-10 the compartment, 11-13 its slot
  *   in the lane's ring of pending updates and voltages, 14-16 its parent's

@@ -150,16 +150,24 @@ def test_sep_thirty_two_lanes_depth_first(n):
     assert _cols_err(out[:, ok], ref[:, ok]) <= 1e-10
 
 
-@pytest.mark.parametrize("n,batch,ld,dfs", [(1300, 70, 0, False), (1500, 1003, 1010, True),
-                                            (2047, 261, 0, False), (2047, 130, 0, True)])
-def test_sep_sixty_four_lanes(n, batch, ld, dfs):
-    """Sixty-four lanes per neuron (four neurons per workgroup, the
-    workgroups of a run of 32 grouped by XCD, a ragged last run), window
-    and depth-first numbered trees, with a breakdown in one neuron."""
-    print(f"hines sep 64 lanes n={n} batch={batch} ld={ld} dfs={dfs}", flush=True)
-    rng = np.random.default_rng(n + batch)
-    hm = _values(W.dfs_tree(n, rng) if dfs else W.random_tree(n, rng), batch, rng)
-    assert bps.hines_sep_schedule(hm.parent)["lanes"] == 64
+@pytest.mark.parametrize("n,batch,ld,kind,neu", [(1300, 70, 0, "win8", 8), (1500, 1003, 1010, "dfs", 8),
+                                                 (2047, 261, 0, "win8", 8), (2047, 130, 0, "dfs", 8),
+                                                 (2047, 517, 0, "win16", 4)])
+def test_sep_sixty_four_lanes(n, batch, ld, kind, neu):
+    """Sixty-four lanes per neuron: 8 neurons per workgroup, or 4 when the
+    LDS of 8 does not fit (the workgroups sharing a row segment grouped by
+    XCD, a ragged last run), window and depth-first numbered trees, with a
+    breakdown in one neuron."""
+    print(f"hines sep 64 lanes n={n} batch={batch} ld={ld} {kind}", flush=True)
+    if kind == "win16":
+        p = W.random_tree(n, np.random.default_rng(10), window=16)
+        rng = np.random.default_rng(n + batch)
+    else:
+        rng = np.random.default_rng(n + batch)
+        p = W.dfs_tree(n, rng) if kind == "dfs" else W.random_tree(n, rng)
+    hm = _values(p, batch, rng)
+    S = bps.hines_sep_schedule(hm.parent)
+    assert S["lanes"] == 64 and S["neurons"] == neu
     hm.d[n // 3, 5] = 0.0
     hm.u[:, 5] = 0.0                      # decoupled: every pivot is d itself
     out, info = _solve(hm, ld=ld, twice=(batch == 130))

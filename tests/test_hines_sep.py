@@ -235,7 +235,7 @@ def test_sep_schedule_shapes():
     for n in (1300, 1700, 2047):
         for tree in (W.random_tree(n, rng), W.dfs_tree(n, rng)):
             S = bps.hines_sep_schedule(tree)
-            assert S is not None and S["lanes"] == 64 and S["R"] == 32
+            assert S is not None and S["lanes"] == 64 and S["R"] == 32 and S["neurons"] in (4, 8)
             assert S["ns"] <= 255 and S["nc"] <= 255
 
 
