@@ -1418,10 +1418,10 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
             // rows squeezed to more than 32 separators: one lane per neuron
             // is faster there (51.2M compartments per batch, separators /
             // one lane: n = 1024 with 40 separators 0.870 / 0.736 ms, 1100
-            // with 79 1.06 / 0.674, 64 lanes for 1300 .. 2047 0.89 .. 1.26 /
-            // 0.71 .. 0.84; but 1000 with 25 0.644 / 0.756, and 800 on 24 rows
+            // with 79 1.06 / 0.674, 64 lanes for 1300 .. 2000 0.80 .. 0.85 /
+            // 0.71 .. 0.82; but 1000 with 25 0.644 / 0.756, and 800 on 24 rows
             // with 39 .. 56 0.619 / 0.662), while its general variant takes
-            // 2.1 .. 3.4 ms for such trees numbered depth first
+            // 2.1 .. 3.5 ms for such trees numbered depth first
             if (sched == BPS_HINES_AUTO && P->max_dist <= kRing && !P->sep.empty() &&
                 (P->sep[6] == 64 || (P->sep[6] == 32 && P->sep[0] == 32 && P->sep[1] > 32)))
                 P->sep.clear();
