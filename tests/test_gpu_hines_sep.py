@@ -5,8 +5,10 @@ batches (not a multiple of the 16 neurons of a workgroup), ld > batch, both
 row counts per lane (16 and 32), chains (every component a path), the
 largest trees the schedule takes, breakdowns (info equals Algorithm 1's and
 the other neurons are unaffected), repeatability, trees with parents far
-back (depth-first numbering, wide windows: ring slots given per lane), and
-sampled neurons of the full 100000 x 512 workload; multi-morphology batches (every tree its own
+back (depth-first numbering, wide windows: ring slots given per lane),
+sixty-four lanes per neuron (8 or 4 neurons per workgroup), and sampled
+neurons of the full 100000 x 512, 53328 x 960 and depth-first 25600 x 2000
+workloads; multi-morphology batches (every tree its own
 schedule, the schedule-ordered layout) likewise, with the pack contract and
 the full 32768-neuron workload sampled."""
 import numpy as np
@@ -265,13 +267,19 @@ def test_sep_refusals_and_auto():
 
 
 @pytest.mark.slow
-def test_sep_full_workload_sampled():
-    cfg = W.WORKLOADS[3]
-    print(f"full hines mono {cfg['n']}x{cfg['batch']} sep", flush=True)
-    hm = W.hines_mono(cfg["n"], cfg["batch"])
+@pytest.mark.parametrize("which", [3, 13, 14])
+def test_sep_full_workload_sampled(which):
+    """The full mono workloads on sixteen, thirty-two and sixty-four lanes
+    per neuron (the benchmark's inputs and launch), sampled neurons against
+    the oracle."""
+    cfg = W.WORKLOADS[which]
+    print(f"full hines mono {cfg['n']}x{cfg['batch']} sep (workload {which})", flush=True)
+    hm = W.hines_mono(cfg["n"], cfg["batch"], rng=W.rng_for(which), dfs=cfg.get("dfs", False))
+    S = bps.hines_sep_schedule(hm.parent)
+    assert S["lanes"] == {3: 16, 13: 32, 14: 64}[which]
     out, info = _solve(hm)
-    cols = np.unique(np.r_[0, 15, 16, cfg["batch"] - 1,
-                           np.random.default_rng(3).integers(0, cfg["batch"], 200)])
+    cols = np.unique(np.r_[0, 7, 8, 15, 16, cfg["batch"] - 1,
+                           np.random.default_rng(which).integers(0, cfg["batch"], 200)])
     sub = W.HinesMono(hm.parent, *(v[:, cols] for v in (hm.u, hm.l, hm.d, hm.rhs)))
     ref, _ = _oracle(sub)
     assert _cols_err(out[:, cols], ref) <= 1e-10
