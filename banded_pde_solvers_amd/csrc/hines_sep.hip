@@ -1,6 +1,6 @@
 // hines_sep.hip -- Hines systems of one shared morphology, each neuron
-// solved by sixteen, thirty-two or sixty-four lanes, and multi-morphology batches with
-// every tree on its own lanes ([H] section 2, Algorithm 1, and the
+// solved by sixteen, thirty-two or sixty-four lanes, and multi-morphology
+// batches with every tree on its own lanes ([H] section 2, Algorithm 1, and the
 // per-branch decomposition of section 4).
 //
 // A set S of single compartments ("separators") cuts the tree into
@@ -22,8 +22,9 @@
 // 4 lanes of 16 neighbouring neurons (every access four 128-byte row
 // segments of the interleaved layout), 8 lanes of 8 (eight 64-byte halves,
 // the other halves read by a workgroup on the same XCD) or 16 lanes of 4
-// (32-byte quarters, the others read by three workgroups on the same XCD).  A lane keeps its compartments' pending
-// updates and voltages in 8 ring slots that the schedule assigns.
+// (32-byte quarters, the others read by three workgroups on the same XCD).
+// A lane keeps its compartments' pending updates and voltages in 8 ring
+// slots that the schedule assigns.
 #include <algorithm>
 #include <cstring>
 #include <string>
@@ -39,7 +40,7 @@ namespace bps {
 
 namespace {
 
-constexpr int kSepNeurons = 16;     // neurons per workgroup with 16 lanes each (8 with 32, 4 with 64)
+constexpr int kSepNeurons = 16;     // neurons per workgroup with 16 lanes each (8 with 32, 8 or 4 with 64)
 constexpr int kSepSlots = 8;        // ring of pending updates / voltages per lane
 constexpr int kSepHeader = 8;
 
