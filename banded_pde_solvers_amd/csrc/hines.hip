@@ -1414,15 +1414,20 @@ bps_status hines_plan_build(bps_hines_plan **out, int64_t batch, const int32_t *
             if (n > 2047 || n * ld * 8 > int64_t(0xFFFF0000u))
                 why = n > 2047 ? "tree size above 2047" : "n * ld * 8 bytes above 4 GiB";
             else P->sep = sep_schedule(int32_t(n), parent, why);
-            // with parents within 16, not on 64 lanes nor on 32 lanes of 32
-            // rows squeezed to more than 32 separators: one lane per neuron
-            // is faster there (51.2M compartments per batch, separators /
-            // one lane: n = 1024 with 40 separators 0.870 / 0.736 ms, 1100
-            // with 79 1.06 / 0.674, 64 lanes for 1300 .. 2000 0.80 .. 0.85 /
-            // 0.71 .. 0.82; but 1000 with 25 0.644 / 0.756, and 800 on 24 rows
-            // with 39 .. 56 0.619 / 0.662), while its general variant takes
-            // 2.1 .. 3.5 ms for such trees numbered depth first
-            if (sched == BPS_HINES_AUTO && P->max_dist <= kRing && !P->sep.empty() &&
+            // with parents within 16 and at least 24576 neurons, not on 64
+            // lanes nor on 32 lanes of 32 rows squeezed to more than 32
+            // separators: one lane per neuron is faster there (51.2M
+            // compartments per batch, separators / one lane: n = 1024 with 40
+            // separators 0.870 / 0.736 ms, 1100 with 79 1.06 / 0.674, 64 lanes
+            // for 1300 .. 2000 0.80 .. 0.85 / 0.71 .. 0.82; but 1000 with 25
+            // 0.644 / 0.756, and 800 on 24 rows with 39 .. 56 0.619 / 0.662),
+            // while its general variant takes 2.1 .. 3.5 ms for such trees
+            // numbered depth first.  Smaller batches leave one lane per neuron
+            // latency-bound: n = 1500 (64 lanes), 2048 .. 32768 neurons 0.046,
+            // 0.087, 0.204, 0.416, 0.814 ms against 0.429, 0.431, 0.482, 0.526,
+            // 0.665; n = 1024 (40 separators) 0.036, 0.069, 0.132, 0.316, 0.616
+            // against 0.293, 0.297, 0.317, 0.356, 0.451
+            if (sched == BPS_HINES_AUTO && P->max_dist <= kRing && batch >= 24576 && !P->sep.empty() &&
                 (P->sep[6] == 64 || (P->sep[6] == 32 && P->sep[0] == 32 && P->sep[1] > 32)))
                 P->sep.clear();
             if (P->sep.empty() && sched == BPS_HINES_SEP) {

@@ -415,9 +415,10 @@ BPS_API bps_status hines_plan_destroy(bps_hines_plan *plan);
  *   BPS_HINES_AUTO    SEP for trees it takes: mono plans whose tree has a
  *                     parent more than 16 compartments back, or has at
  *                     least 256 compartments or a batch of at most 2^21
- *                     compartments in all, unless (parents within 16) its
- *                     schedule takes 64 lanes, or 32 lanes of 32 rows with
- *                     more than 32 separators; multi-morphology plans
+ *                     compartments in all, unless (parents within 16, at
+ *                     least 24576 neurons) its schedule takes 64 lanes, or
+ *                     32 lanes of 32 rows with more than 32 separators;
+ *                     multi-morphology plans
  *                     unless the trees average under 128 compartments, have all
  *                     their parents within 16 and fill the GPU with one
  *                     lane each (at least 1024 blocks of 64); trees too

@@ -230,15 +230,17 @@ def test_sep_refusals_and_auto():
         plan = bps.hines_plan_create(64, [300], p, mono=True)
         assert plan.uses_sep
         plan.close()
-    # trees of 1300..2047 on sixty-four lanes; by the automatic choice only
-    # with parents far back (one lane per neuron is faster otherwise)
+    # trees of 1300..2047 on sixty-four lanes; by the automatic choice with
+    # parents far back, or in batches below 24576 neurons (one lane per
+    # neuron is faster for larger batches of trees with parents within 16)
     for p, far in ((W.random_tree(1500, rng), False), (W.dfs_tree(1500, rng), True)):
         bps.hines_plan_create(64, [1500], p, mono=True, schedule=SEP).close()
-        plan = bps.hines_plan_create(4096, [1500], p, mono=True)
-        assert plan.uses_sep == far and not plan.uses_levels
-        plan.close()
+        for batch in (4096, 24575, 24576, 32768):
+            plan = bps.hines_plan_create(batch, [1500], p, mono=True)
+            assert plan.uses_sep == (far or batch < 24576) and not plan.uses_levels, batch
+            plan.close()
     # 32 lanes of 32 rows: taken with at most 32 separators, left to one lane
-    # per neuron beyond (parents within 16)
+    # per neuron beyond (parents within 16, 24576 neurons or more)
     seen = set()
     for seed in range(40):
         p = W.random_tree(1024, np.random.default_rng(seed))
@@ -246,8 +248,11 @@ def test_sep_refusals_and_auto():
         if S is None or S["lanes"] != 32 or S["R"] != 32:
             continue
         squeezed = S["ns"] > 32
-        plan = bps.hines_plan_create(4096, [1024], p, mono=True)
+        plan = bps.hines_plan_create(32768, [1024], p, mono=True)
         assert plan.uses_sep == (not squeezed), (seed, S["ns"])
+        plan.close()
+        plan = bps.hines_plan_create(4096, [1024], p, mono=True)
+        assert plan.uses_sep, (seed, S["ns"])
         plan.close()
         seen.add(squeezed)
         if len(seen) == 2:
